@@ -1,0 +1,742 @@
+/*
+ * bs_oracle.c -- plain, slow, scalar CPU oracle for the BF16 rANS container.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product decode path
+ * never calls it, and it shares no code, header, table or helper with the HIP
+ * library: everything here is written out again from the format definition.
+ *
+ * What is computed, and where it comes from:
+ *   - Each BF16 word is split into its exact fields [sign:1 | exponent:8 |
+ *     fraction:7]; the joint (sign, exponent) symbol is coded with a per-tensor
+ *     rANS model; once decoded it selects the distribution used for the 7-bit
+ *     fraction; the decoder recombines the fields bitwise.  Non-BF16 spans are
+ *     kept verbatim in a residual.
+ *     [Qwen3.8-27B-BF16-NVLC-Lossless model card, codec paragraph after the
+ *      metrics table]
+ *   - Every tensor carries a hash checked at decompression (sha256 here).
+ *     [Gemma 2 9B Instruct -- Lossless Compressed card, "What lossless means";
+ *      NVLC card, SHA256SUMS verification block]
+ *   - Everything else (state width, renormalisation unit, table precisions,
+ *     the quantisation rule, the choice of coded fraction contexts, the
+ *     lane/chunk interleave and the byte layout) is not given by the pages.
+ *     It is this container's own definition; the readings are listed in the
+ *     design notes of the repository.
+ *
+ * The rANS coder follows Duda's range variant of asymmetric numeral systems:
+ *   encode  x' = floor(x / q) * 2^M + (x mod q) + cum
+ *   decode  slot = x mod 2^M, sym = the symbol with cum <= slot < cum + q,
+ *           x = q * floor(x / 2^M) + slot - cum
+ * with a 32-bit state kept in [2^16, 2^32) by 16-bit renormalisation words.
+ *
+ * Parity pins live in tests/test_oracle_*.py (hand-computed coder states,
+ * a bit-stack reduction, brute force, normaliser invariants, round trips).
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define BSO_L          65536u          /* lower end of the state interval */
+#define BSO_MAGIC      "BF16RANS"
+#define BSO_VERSION    1u
+#define BSO_HDR_BYTES  64u
+#define BSO_DIR_BYTES  96u
+#define BSO_KIND_BF16  1u
+#define BSO_KIND_RAW   2u
+#define BSO_MAX_TABLES 6u
+#define BSO_MAX_SYMS   256u            /* more occupied (sign,exp) symbols -> stored RAW */
+#define BSO_CANDIDATES 64u
+#define BSO_OUT_ALIGN  256u
+
+/* error codes (negative), same meaning as the names say */
+#define BSO_OK       0
+#define BSO_EINVAL  -1
+#define BSO_EFORMAT -2
+#define BSO_EVERSION -3
+#define BSO_ENOSPACE -4
+#define BSO_ENOMEM  -5
+#define BSO_ECORRUPT -7
+
+/* ------------------------------------------------------------------------ */
+/* little-endian helpers (explicit byte order, no type punning)              */
+/* ------------------------------------------------------------------------ */
+static void put16(uint8_t* p, uint32_t v) { p[0] = (uint8_t)v; p[1] = (uint8_t)(v >> 8); }
+static void put32(uint8_t* p, uint32_t v) { for (int i = 0; i < 4; i++) p[i] = (uint8_t)(v >> (8 * i)); }
+static void put64(uint8_t* p, uint64_t v) { for (int i = 0; i < 8; i++) p[i] = (uint8_t)(v >> (8 * i)); }
+static uint32_t get16(const uint8_t* p) { return (uint32_t)p[0] | ((uint32_t)p[1] << 8); }
+static uint32_t get32(const uint8_t* p) { uint32_t v = 0; for (int i = 0; i < 4; i++) v |= (uint32_t)p[i] << (8 * i); return v; }
+static uint64_t get64(const uint8_t* p) { uint64_t v = 0; for (int i = 0; i < 8; i++) v |= (uint64_t)p[i] << (8 * i); return v; }
+static uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+/* ------------------------------------------------------------------------ */
+/* Field split and recombination                                             */
+/* [NVLC card, codec paragraph: sign:1 | exponent:8 | fraction:7]            */
+/* The joint symbol is s = sign*256 + exponent, i.e. the top 9 bits.         */
+/* ------------------------------------------------------------------------ */
+uint32_t bso_symbol_s(uint16_t w) { return ((uint32_t)w >> 15) * 256u + (((uint32_t)w >> 7) & 0xFFu); }
+uint32_t bso_symbol_f(uint16_t w) { return (uint32_t)w & 0x7Fu; }
+uint16_t bso_combine(uint32_t s, uint32_t f) {
+    uint32_t sign = s / 256u, expo = s % 256u;
+    return (uint16_t)((sign << 15) | (expo << 7) | f);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Histogram of the two fields: cs[s] and cf[s][f] (512 x 128, row major).    */
+/* [NVLC card, codec paragraph: the model is per tensor]                      */
+/* ------------------------------------------------------------------------ */
+void bso_histogram(const uint16_t* w, uint64_t n, uint64_t* cs, uint64_t* cf) {
+    memset(cs, 0, 512 * sizeof(uint64_t));
+    memset(cf, 0, 512 * 128 * sizeof(uint64_t));
+    for (uint64_t i = 0; i < n; i++) {
+        uint32_t s = bso_symbol_s(w[i]);
+        uint32_t f = bso_symbol_f(w[i]);
+        cs[s] += 1;
+        cf[s * 128 + f] += 1;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantise counts c[0..A) to frequencies q summing to 2^M (integer only).   */
+/* Container rule (the pages give none):                                     */
+/*   q_i = 0 if c_i = 0, else max(1, floor(c_i 2^M / n));                    */
+/*   while the sum is short, add 1 to occupied symbols in order of the       */
+/*   remainder (c_i 2^M mod n) descending, lower index first on ties,        */
+/*   cycling through that order;                                             */
+/*   while the sum is over, take 1 from the symbol with the largest q (>1),  */
+/*   lower index first on ties.                                              */
+/* Returns 0, or BSO_EINVAL when nothing is occupied or 2^M is too small.    */
+/* ------------------------------------------------------------------------ */
+int bso_normalise(const uint64_t* c, uint32_t A, uint32_t M, uint32_t* q) {
+    uint64_t n = 0, occupied = 0;
+    for (uint32_t i = 0; i < A; i++) { n += c[i]; if (c[i]) occupied++; }
+    if (n == 0 || occupied > ((uint64_t)1 << M)) return BSO_EINVAL;
+    const unsigned __int128 total = (unsigned __int128)1 << M;
+    int64_t sum = 0;
+    for (uint32_t i = 0; i < A; i++) {
+        if (c[i] == 0) { q[i] = 0; continue; }
+        uint64_t v = (uint64_t)(((unsigned __int128)c[i] * total) / n);
+        q[i] = (uint32_t)(v < 1 ? 1 : v);
+        sum += q[i];
+    }
+    int64_t d = ((int64_t)1 << M) - sum;
+    if (d > 0) {
+        /* order occupied symbols by remainder descending, index ascending:
+           a plain selection sort, written for clarity, not speed */
+        uint32_t* order = (uint32_t*)malloc(sizeof(uint32_t) * occupied);
+        uint64_t* rem = (uint64_t*)malloc(sizeof(uint64_t) * A);
+        if (!order || !rem) { free(order); free(rem); return BSO_ENOMEM; }
+        uint64_t k = 0;
+        for (uint32_t i = 0; i < A; i++) {
+            if (!c[i]) continue;
+            rem[i] = (uint64_t)(((unsigned __int128)c[i] * total) % n);
+            order[k++] = i;
+        }
+        for (uint64_t a = 0; a < k; a++) {
+            uint64_t best = a;
+            for (uint64_t b = a + 1; b < k; b++) {
+                uint32_t ib = order[b], ibest = order[best];
+                if (rem[ib] > rem[ibest] || (rem[ib] == rem[ibest] && ib < ibest)) best = b;
+            }
+            uint32_t t = order[a]; order[a] = order[best]; order[best] = t;
+        }
+        for (int64_t j = 0; j < d; j++) q[order[(uint64_t)j % k]] += 1;
+        free(order); free(rem);
+    }
+    while (d < 0) {
+        uint32_t best = A;
+        for (uint32_t i = 0; i < A; i++) {
+            if (q[i] > 1 && (best == A || q[i] > q[best])) best = i;
+        }
+        if (best == A) return BSO_EINVAL; /* unreachable when occupied <= 2^M */
+        q[best] -= 1;
+        d += 1;
+    }
+    return BSO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Choice of the coded fraction contexts (container rule, integer only).     */
+/* [NVLC card, codec paragraph: the decoded sign/exponent symbol selects the */
+/*  fraction distribution]                                                   */
+/* Both signs of one exponent e share a context, with merged counts          */
+/*   n_e = cs[e] + cs[256+e],  m_e[f] = cf[e][f] + cf[256+e][f].             */
+/* Candidates: the 64 exponents with the largest n_e > 0 (lower e on ties).  */
+/* Excess  E_e = 128 sum_f m_e[f]^2 - n_e^2  (n_e * E_e / n_e^2 is the       */
+/* chi-square distance from the flat fraction distribution).                 */
+/* Eligible iff 256 E_e > n_e^2 + 726784 n_e; score = floor(E_e / n_e).      */
+/* Selected: up to cmax eligible candidates with the highest score (lower e  */
+/* on ties); table ids 1..k are given in ascending e.  route[s] = id of      */
+/* s mod 256 when selected, else 0 (the flat table).                         */
+/* qf[(id-1)*128 + f] = normalise(m_e, M_f).                                 */
+/* ------------------------------------------------------------------------ */
+int bso_select_tables(const uint64_t* cs, const uint64_t* cf, uint32_t M_f, uint32_t cmax,
+                      uint32_t* route /*512*/, uint32_t* n_tables, uint32_t* qf /*cmax*128*/) {
+    if (cmax > BSO_MAX_TABLES) return BSO_EINVAL;
+    uint64_t ne[256];
+    int used[256];
+    for (uint32_t e = 0; e < 256; e++) { ne[e] = cs[e] + cs[256 + e]; used[e] = 0; }
+    /* candidates by count */
+    uint32_t cand[BSO_CANDIDATES];
+    uint32_t nc = 0;
+    while (nc < BSO_CANDIDATES) {
+        uint32_t best = 256;
+        for (uint32_t e = 0; e < 256; e++) {
+            if (used[e] || ne[e] == 0) continue;
+            if (best == 256 || ne[e] > ne[best]) best = e;
+        }
+        if (best == 256) break;
+        used[best] = 1;
+        cand[nc++] = best;
+    }
+    /* score eligible candidates */
+    uint64_t score[BSO_CANDIDATES];
+    int eligible[BSO_CANDIDATES];
+    for (uint32_t k = 0; k < nc; k++) {
+        uint32_t e = cand[k];
+        unsigned __int128 n = ne[e];
+        unsigned __int128 sq = 0;
+        for (uint32_t f = 0; f < 128; f++) {
+            unsigned __int128 m = (unsigned __int128)cf[e * 128 + f] + cf[(256 + e) * 128 + f];
+            sq += m * m;
+        }
+        unsigned __int128 E = 128 * sq - n * n;
+        eligible[k] = (256 * E > n * n + (unsigned __int128)726784 * n);
+        score[k] = (uint64_t)(E / n);
+    }
+    /* pick the top cmax by score */
+    int picked[256];
+    for (uint32_t e = 0; e < 256; e++) picked[e] = 0;
+    uint32_t k_sel = 0;
+    int taken[BSO_CANDIDATES];
+    for (uint32_t k = 0; k < nc; k++) taken[k] = 0;
+    while (k_sel < cmax) {
+        int best = -1;
+        for (uint32_t k = 0; k < nc; k++) {
+            if (!eligible[k] || taken[k]) continue;
+            if (best < 0 || score[k] > score[best] ||
+                (score[k] == score[best] && cand[k] < cand[best])) best = (int)k;
+        }
+        if (best < 0) break;
+        taken[best] = 1;
+        picked[cand[best]] = 1;
+        k_sel++;
+    }
+    /* ids in ascending exponent order, tables normalised from merged counts */
+    uint32_t id_of[256];
+    uint32_t id = 0;
+    for (uint32_t e = 0; e < 256; e++) {
+        id_of[e] = 0;
+        if (!picked[e]) continue;
+        id++;
+        id_of[e] = id;
+        uint64_t m[128];
+        for (uint32_t f = 0; f < 128; f++) m[f] = cf[e * 128 + f] + cf[(256 + e) * 128 + f];
+        int rc = bso_normalise(m, 128, M_f, qf + (id - 1) * 128);
+        if (rc) return rc;
+    }
+    for (uint32_t s = 0; s < 512; s++) route[s] = cs[s] ? id_of[s % 256] : 0;
+    *n_tables = id;
+    return BSO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Lane/chunk shape of a record (container rule).                            */
+/* Records of n >= Wmax weights use W = Wmax, K = Kmax.  A smaller record is */
+/* one chunk whose lane count is the smallest power of two that keeps the   */
+/* weights per lane at or below Wmax/Kmax (at most Kmax), with W = n rounded */
+/* up to a multiple of 8K.                                                   */
+/* ------------------------------------------------------------------------ */
+int bso_record_shape(uint64_t n, uint32_t Wmax, uint32_t Kmax, uint32_t* W, uint32_t* K) {
+    if (Kmax == 0 || Wmax == 0 || Wmax % (8 * Kmax)) return BSO_EINVAL;
+    if (n >= Wmax) { *W = Wmax; *K = Kmax; return BSO_OK; }
+    uint64_t per_lane = Wmax / Kmax;
+    uint64_t need = (n + per_lane - 1) / per_lane;
+    uint32_t k = 1;
+    while (k < need && k < Kmax) k *= 2;
+    if (n == 0) k = 1;
+    *K = k;
+    *W = (uint32_t)round_up(n ? n : 1, 8 * (uint64_t)k);
+    return BSO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The rANS coder, one symbol at a time.                                     */
+/* A table is (M, A, q[0..A)); cum is the running sum in symbol order.       */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    uint32_t M;
+    uint32_t A;
+    const uint32_t* q;
+} bso_table;
+
+static uint32_t table_cum(const bso_table* t, uint32_t sym) {
+    uint32_t c = 0;
+    for (uint32_t i = 0; i < sym; i++) c += t->q[i];
+    return c;
+}
+
+/* Encode one symbol into state *x; flushed 16-bit words are appended to a   */
+/* growable list (in emission order, reversed later).                        */
+typedef struct { uint16_t* w; uint64_t n, cap; } wordlist;
+
+static int wl_push(wordlist* wl, uint16_t v) {
+    if (wl->n == wl->cap) {
+        uint64_t nc = wl->cap ? wl->cap * 2 : 1024;
+        uint16_t* p = (uint16_t*)realloc(wl->w, nc * sizeof(uint16_t));
+        if (!p) return BSO_ENOMEM;
+        wl->w = p; wl->cap = nc;
+    }
+    wl->w[wl->n++] = v;
+    return BSO_OK;
+}
+
+static int enc_symbol(uint32_t* x, const bso_table* t, uint32_t sym, wordlist* out) {
+    uint32_t q = t->q[sym];
+    if (q == 0) return BSO_EINVAL;
+    uint32_t cum = table_cum(t, sym);
+    uint64_t x_max = (uint64_t)q << (32 - t->M);
+    if ((uint64_t)*x >= x_max) {
+        int rc = wl_push(out, (uint16_t)(*x & 0xFFFFu));
+        if (rc) return rc;
+        *x >>= 16;
+    }
+    *x = (*x / q) * (1u << t->M) + (*x % q) + cum;
+    return BSO_OK;
+}
+
+/* Decode one symbol from state *x, then refill from words[*pos] if needed. */
+static int dec_symbol(uint32_t* x, const bso_table* t, const uint16_t* words, uint64_t nw,
+                      uint64_t* pos, uint32_t* sym) {
+    uint32_t slot = *x & ((1u << t->M) - 1u);
+    uint32_t cum = 0, s = 0;
+    while (s < t->A && !(cum <= slot && slot < cum + t->q[s])) { cum += t->q[s]; s++; }
+    if (s == t->A) return BSO_ECORRUPT;
+    *sym = s;
+    *x = t->q[s] * (*x >> t->M) + slot - cum;
+    if (*x < BSO_L) {
+        if (*pos >= nw) return BSO_ECORRUPT;
+        *x = (*x << 16) | words[*pos];
+        *pos += 1;
+    }
+    return BSO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Generic interleaved coder over an explicit schedule (used by the pins):   */
+/* nsteps sub-steps x K lanes; syms[step*K+l] = -1 where a lane is idle;     */
+/* tab_of[step*K+l] picks the table.  Encoding walks the sub-steps from last */
+/* to first and, inside one, the lanes from K-1 down to 0; the emitted words */
+/* are then reversed, so decoding walks everything forwards.                 */
+/* ------------------------------------------------------------------------ */
+int bso_sched_encode(uint32_t K, uint32_t nsteps, const int32_t* syms, const uint32_t* tab_of,
+                     const uint32_t* tabM, const uint32_t* tabA, const uint32_t* tabq, uint32_t ntab,
+                     uint32_t* states, uint16_t* words, uint64_t cap, uint64_t* nw) {
+    bso_table* tabs = (bso_table*)malloc(sizeof(bso_table) * (ntab ? ntab : 1));
+    if (!tabs) return BSO_ENOMEM;
+    uint64_t off = 0;
+    for (uint32_t i = 0; i < ntab; i++) { tabs[i].M = tabM[i]; tabs[i].A = tabA[i]; tabs[i].q = tabq + off; off += tabA[i]; }
+    wordlist wl = {0, 0, 0};
+    for (uint32_t l = 0; l < K; l++) states[l] = BSO_L;
+    int rc = BSO_OK;
+    for (int64_t st = (int64_t)nsteps - 1; st >= 0 && !rc; st--) {
+        for (int64_t l = (int64_t)K - 1; l >= 0 && !rc; l--) {
+            int32_t s = syms[(uint64_t)st * K + (uint64_t)l];
+            if (s < 0) continue;
+            rc = enc_symbol(&states[l], &tabs[tab_of[(uint64_t)st * K + (uint64_t)l]], (uint32_t)s, &wl);
+        }
+    }
+    if (!rc) {
+        if (wl.n > cap) rc = BSO_ENOSPACE;
+        else for (uint64_t i = 0; i < wl.n; i++) words[i] = wl.w[wl.n - 1 - i];
+        *nw = wl.n;
+    }
+    free(wl.w); free(tabs);
+    return rc;
+}
+
+int bso_sched_decode(uint32_t K, uint32_t nsteps, const int32_t* active, const uint32_t* tab_of,
+                     const uint32_t* tabM, const uint32_t* tabA, const uint32_t* tabq, uint32_t ntab,
+                     const uint32_t* states_in, const uint16_t* words, uint64_t nw,
+                     int32_t* syms_out, uint32_t* states_out) {
+    bso_table* tabs = (bso_table*)malloc(sizeof(bso_table) * (ntab ? ntab : 1));
+    if (!tabs) return BSO_ENOMEM;
+    uint64_t off = 0;
+    for (uint32_t i = 0; i < ntab; i++) { tabs[i].M = tabM[i]; tabs[i].A = tabA[i]; tabs[i].q = tabq + off; off += tabA[i]; }
+    for (uint32_t l = 0; l < K; l++) states_out[l] = states_in[l];
+    uint64_t pos = 0;
+    int rc = BSO_OK;
+    for (uint64_t st = 0; st < nsteps && !rc; st++) {
+        for (uint32_t l = 0; l < K && !rc; l++) {
+            uint64_t i = st * K + l;
+            syms_out[i] = -1;
+            if (!active[i]) continue;
+            uint32_t sym;
+            rc = dec_symbol(&states_out[l], &tabs[tab_of[i]], words, nw, &pos, &sym);
+            if (!rc) syms_out[i] = (int32_t)sym;
+        }
+    }
+    free(tabs);
+    if (!rc && pos != nw) rc = BSO_ECORRUPT;
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One chunk of a BF16 record.                                               */
+/* Weight j of the chunk: group g = j / 8, position p = j mod 8, lane        */
+/* l = g mod K, macro-step t = g / K.  A lane's symbols are, for t then p    */
+/* ascending, the s symbol of the weight followed by its f symbol.  The      */
+/* sub-step is (t, p, phase); lane l takes part iff 8(tK + l) + p < n_c.     */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    uint32_t M_s, M_f;
+    uint32_t qs[512];
+    uint32_t route[512];
+    uint32_t n_tables;
+    uint32_t qf[1 + BSO_MAX_TABLES][128]; /* [0] is the flat table */
+} bso_model;
+
+static int chunk_encode(const bso_model* md, const uint16_t* w, uint32_t n_c, uint32_t K,
+                        uint32_t* states, wordlist* wl) {
+    bso_table ts = { md->M_s, 512, md->qs };
+    uint32_t groups = (n_c + 7) / 8;
+    uint32_t T = (groups + K - 1) / K;
+    for (uint32_t l = 0; l < K; l++) states[l] = BSO_L;
+    for (int64_t t = (int64_t)T - 1; t >= 0; t--) {
+        for (int p = 7; p >= 0; p--) {
+            for (int phase = 1; phase >= 0; phase--) {
+                for (int64_t l = (int64_t)K - 1; l >= 0; l--) {
+                    uint64_t j = 8 * ((uint64_t)t * K + (uint64_t)l) + (uint64_t)p;
+                    if (j >= n_c) continue;
+                    uint32_t s = bso_symbol_s(w[j]);
+                    int rc;
+                    if (phase == 0) {
+                        rc = enc_symbol(&states[l], &ts, s, wl);
+                    } else {
+                        bso_table tf = { md->M_f, 128, md->qf[md->route[s]] };
+                        rc = enc_symbol(&states[l], &tf, bso_symbol_f(w[j]), wl);
+                    }
+                    if (rc) return rc;
+                }
+            }
+        }
+    }
+    return BSO_OK;
+}
+
+static int chunk_decode(const bso_model* md, const uint32_t* states_in, const uint16_t* words,
+                        uint64_t nw, uint32_t n_c, uint32_t K, uint16_t* out) {
+    bso_table ts = { md->M_s, 512, md->qs };
+    uint32_t groups = (n_c + 7) / 8;
+    uint32_t T = (groups + K - 1) / K;
+    uint32_t* x = (uint32_t*)malloc(sizeof(uint32_t) * K);
+    uint32_t* s_now = (uint32_t*)malloc(sizeof(uint32_t) * K);
+    if (!x || !s_now) { free(x); free(s_now); return BSO_ENOMEM; }
+    for (uint32_t l = 0; l < K; l++) x[l] = states_in[l];
+    uint64_t pos = 0;
+    int rc = BSO_OK;
+    for (uint32_t t = 0; t < T && !rc; t++) {
+        for (uint32_t p = 0; p < 8 && !rc; p++) {
+            for (int phase = 0; phase < 2 && !rc; phase++) {
+                for (uint32_t l = 0; l < K && !rc; l++) {
+                    uint64_t j = 8 * ((uint64_t)t * K + l) + p;
+                    if (j >= n_c) continue;
+                    uint32_t sym;
+                    if (phase == 0) {
+                        rc = dec_symbol(&x[l], &ts, words, nw, &pos, &sym);
+                        s_now[l] = sym;
+                    } else {
+                        bso_table tf = { md->M_f, 128, md->qf[md->route[s_now[l]]] };
+                        rc = dec_symbol(&x[l], &tf, words, nw, &pos, &sym);
+                        if (!rc) out[j] = bso_combine(s_now[l], sym);
+                    }
+                }
+            }
+        }
+    }
+    /* the encoder started every lane at L, so a whole chunk must end there */
+    for (uint32_t l = 0; l < K && !rc; l++) if (x[l] != BSO_L) rc = BSO_ECORRUPT;
+    if (!rc && pos != nw) rc = BSO_ECORRUPT;
+    free(x); free(s_now);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Byte buffer for the container                                             */
+/* ------------------------------------------------------------------------ */
+typedef struct { uint8_t* p; uint64_t n, cap; } bytebuf;
+
+static int bb_reserve(bytebuf* b, uint64_t need) {
+    if (need <= b->cap) return BSO_OK;
+    uint64_t nc = b->cap ? b->cap : 4096;
+    while (nc < need) nc *= 2;
+    uint8_t* p = (uint8_t*)realloc(b->p, nc);
+    if (!p) return BSO_ENOMEM;
+    memset(p + b->cap, 0, nc - b->cap);
+    b->p = p; b->cap = nc;
+    return BSO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Encode one BF16 record body.                                              */
+/* ------------------------------------------------------------------------ */
+static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32_t Kmax,
+                            uint32_t M_s, uint32_t M_f, uint32_t cmax, bytebuf* body) {
+    uint32_t W, K;
+    int rc = bso_record_shape(n, Wmax, Kmax, &W, &K);
+    if (rc) return rc;
+    bso_model* md = (bso_model*)calloc(1, sizeof(bso_model));
+    uint64_t* cs = (uint64_t*)calloc(512, sizeof(uint64_t));
+    uint64_t* cf = (uint64_t*)calloc(512 * 128, sizeof(uint64_t));
+    if (!md || !cs || !cf) { free(md); free(cs); free(cf); return BSO_ENOMEM; }
+    md->M_s = M_s; md->M_f = M_f;
+    uint32_t n_sym = 0;
+    uint64_t n_chunks = n ? (n + W - 1) / W : 0;
+    if (n) {
+        bso_histogram(w, n, cs, cf);
+        rc = bso_normalise(cs, 512, M_s, md->qs);
+        if (!rc) rc = bso_select_tables(cs, cf, M_f, cmax, md->route, &md->n_tables, &md->qf[1][0]);
+        for (uint32_t s = 0; s < 512; s++) if (cs[s]) n_sym++;
+    }
+    for (uint32_t f = 0; f < 128; f++) md->qf[0][f] = 1u << (M_f - 7);
+    if (rc) goto done;
+
+    /* fixed part and tables */
+    uint64_t off = 24;
+    uint64_t tables_end = off + 4ull * n_sym;
+    tables_end = round_up(tables_end + n_sym, 4);
+    tables_end += 256ull * md->n_tables;
+    uint64_t index_off = round_up(tables_end, 16);
+    uint64_t payload_off = index_off + 16 * n_chunks;
+    rc = bb_reserve(body, payload_off);
+    if (rc) goto done;
+    body->n = payload_off;
+    uint8_t* b = body->p;
+    put32(b + 0, W); put32(b + 4, K); put32(b + 8, (uint32_t)n_chunks);
+    b[12] = (uint8_t)M_s; b[13] = (uint8_t)M_f; b[14] = (uint8_t)md->n_tables; b[15] = 0;
+    put32(b + 16, n_sym); put32(b + 20, 0);
+    uint64_t k = 0;
+    for (uint32_t s = 0; s < 512; s++) {
+        if (!cs[s]) continue;
+        put16(b + off + 4 * k, s);
+        put16(b + off + 4 * k + 2, md->qs[s]);
+        b[off + 4ull * n_sym + k] = (uint8_t)md->route[s];
+        k++;
+    }
+    uint64_t ft = round_up(off + 4ull * n_sym + n_sym, 4);
+    for (uint32_t t = 1; t <= md->n_tables; t++)
+        for (uint32_t f = 0; f < 128; f++) put16(b + ft + 256ull * (t - 1) + 2 * f, md->qf[t][f]);
+
+    /* chunks */
+    uint32_t* states = (uint32_t*)malloc(sizeof(uint32_t) * K);
+    if (!states) { rc = BSO_ENOMEM; goto done; }
+    for (uint64_t c = 0; c < n_chunks && !rc; c++) {
+        uint32_t n_c = (uint32_t)((n - c * W) < W ? (n - c * W) : W);
+        wordlist wl = {0, 0, 0};
+        rc = chunk_encode(md, w + c * W, n_c, K, states, &wl);
+        if (rc) { free(wl.w); break; }
+        uint64_t start = body->n;
+        uint64_t states_bytes = round_up(4ull * K, 16);
+        uint64_t end = start + states_bytes + round_up(2 * wl.n, 16);
+        rc = bb_reserve(body, end);
+        if (rc) { free(wl.w); break; }
+        b = body->p;
+        put64(b + index_off + 16 * c, start);
+        put32(b + index_off + 16 * c + 8, (uint32_t)wl.n);
+        put32(b + index_off + 16 * c + 12, 0);
+        for (uint32_t l = 0; l < K; l++) put32(b + start + 4ull * l, states[l]);
+        for (uint64_t i = 0; i < wl.n; i++) put16(b + start + states_bytes + 2 * i, wl.w[wl.n - 1 - i]);
+        body->n = end;
+        free(wl.w);
+    }
+    free(states);
+done:
+    free(md); free(cs); free(cf);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole container.                                                          */
+/* kinds[i]: 1 = BF16 (n[i] weights at data[i]), 2 = RAW (n[i] bytes).       */
+/* sha[i*32..]: sha256 of the tensor's bytes, computed by the caller.        */
+/* A BF16 tensor with more than 256 occupied (sign,exp) symbols is stored    */
+/* as a RAW record of its 2n bytes.                                          */
+/* On success *out points to malloc'ed bytes (free with bso_free).          */
+/* ------------------------------------------------------------------------ */
+int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* const* data,
+                         const uint64_t* n, const uint8_t* sha,
+                         uint32_t Wmax, uint32_t Kmax, uint32_t M_s, uint32_t M_f, uint32_t cmax,
+                         uint8_t** out, uint64_t* out_len) {
+    if (M_s < 9 || M_s > 12 || M_f < 7 || M_f > 10 || cmax > BSO_MAX_TABLES) return BSO_EINVAL;
+    if (!(Kmax <= 64 || Kmax == 128 || Kmax == 256) || Kmax == 0) return BSO_EINVAL;
+    if ((Kmax & (Kmax - 1)) != 0) return BSO_EINVAL;
+    bytebuf c = {0, 0, 0};
+    uint64_t dir = BSO_HDR_BYTES;
+    uint64_t pos = round_up(dir + (uint64_t)BSO_DIR_BYTES * n_tensors, 16);
+    int rc = bb_reserve(&c, pos);
+    if (rc) return rc;
+    c.n = pos;
+    uint64_t out_pos = 0;
+    for (uint32_t i = 0; i < n_tensors && !rc; i++) {
+        uint32_t kind = kinds[i];
+        uint64_t bytes = kind == BSO_KIND_BF16 ? 2 * n[i] : n[i];
+        uint64_t count = n[i];
+        bytebuf body = {0, 0, 0};
+        if (kind == BSO_KIND_BF16) {
+            /* count occupied symbols first: too many -> verbatim */
+            const uint16_t* w = (const uint16_t*)data[i];
+            int seen[512];
+            uint32_t occ = 0;
+            for (int s = 0; s < 512; s++) seen[s] = 0;
+            for (uint64_t j = 0; j < n[i]; j++) {
+                uint32_t s = bso_symbol_s(w[j]);
+                if (!seen[s]) { seen[s] = 1; occ++; }
+            }
+            if (occ > BSO_MAX_SYMS) { kind = BSO_KIND_RAW; count = bytes; }
+        }
+        if (kind == BSO_KIND_BF16) {
+            rc = encode_bf16_body((const uint16_t*)data[i], n[i], Wmax, Kmax, M_s, M_f, cmax, &body);
+        } else if (kind == BSO_KIND_RAW) {
+            rc = bb_reserve(&body, bytes ? bytes : 1);
+            if (!rc) { if (bytes) memcpy(body.p, data[i], bytes); body.n = bytes; }
+        } else {
+            rc = BSO_EINVAL;
+        }
+        if (rc) { free(body.p); break; }
+        uint64_t rec_off = round_up(c.n, 16);
+        rc = bb_reserve(&c, rec_off + body.n);
+        if (rc) { free(body.p); break; }
+        if (body.n) memcpy(c.p + rec_off, body.p, body.n);
+        c.n = rec_off + body.n;
+        free(body.p);
+        uint8_t* d = c.p + dir + (uint64_t)BSO_DIR_BYTES * i;
+        put32(d + 0, kind); put32(d + 4, 0);
+        put64(d + 8, count);
+        put64(d + 16, out_pos);
+        put64(d + 24, rec_off);
+        put64(d + 32, c.n - rec_off);
+        memcpy(d + 40, sha + 32ull * i, 32);
+        out_pos = round_up(out_pos + bytes, BSO_OUT_ALIGN);
+    }
+    if (rc) { free(c.p); return rc; }
+    uint64_t total = round_up(c.n, 16);
+    rc = bb_reserve(&c, total);
+    if (rc) { free(c.p); return rc; }
+    c.n = total;
+    /* the decoded extent ends with the last record's bytes (no trailing pad) */
+    uint64_t out_len_bytes = 0;
+    for (uint32_t i = 0; i < n_tensors; i++) {
+        const uint8_t* d = c.p + dir + (uint64_t)BSO_DIR_BYTES * i;
+        uint64_t kind = get32(d), cnt = get64(d + 8), oo = get64(d + 16);
+        uint64_t e = oo + (kind == BSO_KIND_BF16 ? 2 * cnt : cnt);
+        if (e > out_len_bytes) out_len_bytes = e;
+    }
+    memcpy(c.p, BSO_MAGIC, 8);
+    put32(c.p + 8, BSO_VERSION);
+    put32(c.p + 12, n_tensors);
+    put64(c.p + 16, dir);
+    put64(c.p + 24, total);
+    put64(c.p + 32, out_len_bytes);
+    *out = c.p;
+    *out_len = total;
+    return BSO_OK;
+}
+
+void bso_free(void* p) { free(p); }
+
+/* ------------------------------------------------------------------------ */
+/* Decode a container into out (out_cap bytes, zero-filled gaps untouched).  */
+/* rec_status[i] (may be NULL) receives 0 or the error of record i.          */
+/* Returns the first error, or 0.                                            */
+/* ------------------------------------------------------------------------ */
+static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md,
+                       uint32_t* W, uint32_t* K, uint64_t* n_chunks, uint64_t* index_off) {
+    if (len < 24) return BSO_EFORMAT;
+    *W = get32(b); *K = get32(b + 4);
+    *n_chunks = get32(b + 8);
+    md->M_s = b[12]; md->M_f = b[13]; md->n_tables = b[14];
+    uint32_t n_sym = get32(b + 16);
+    if (md->M_s < 9 || md->M_s > 12 || md->M_f < 7 || md->M_f > 10 || md->n_tables > BSO_MAX_TABLES)
+        return BSO_EFORMAT;
+    if (*K == 0 || *W == 0 || *W % (8 * *K)) return BSO_EFORMAT;
+    if (!(*K <= 64 || *K == 128 || *K == 256)) return BSO_EFORMAT;
+    if (*n_chunks != (n + *W - 1) / *W) return BSO_EFORMAT;
+    if (n_sym > BSO_MAX_SYMS || (n_sym == 0) != (n == 0)) return BSO_EFORMAT;
+    uint64_t off = 24;
+    uint64_t ft = round_up(off + 4ull * n_sym + n_sym, 4);
+    uint64_t tab_end = ft + 256ull * md->n_tables;
+    *index_off = round_up(tab_end, 16);
+    if (*index_off + 16 * *n_chunks > len) return BSO_EFORMAT;
+    memset(md->qs, 0, sizeof(md->qs));
+    memset(md->route, 0, sizeof(md->route));
+    uint64_t sum = 0;
+    int last = -1;
+    for (uint32_t k = 0; k < n_sym; k++) {
+        uint32_t s = get16(b + off + 4ull * k), q = get16(b + off + 4ull * k + 2);
+        if ((int)s <= last || s >= 512 || q == 0) return BSO_EFORMAT;
+        last = (int)s;
+        md->qs[s] = q;
+        md->route[s] = b[off + 4ull * n_sym + k];
+        if (md->route[s] > md->n_tables) return BSO_EFORMAT;
+        sum += q;
+    }
+    if (n_sym && sum != (1ull << md->M_s)) return BSO_EFORMAT;
+    for (uint32_t f = 0; f < 128; f++) md->qf[0][f] = 1u << (md->M_f - 7);
+    for (uint32_t t = 1; t <= md->n_tables; t++) {
+        uint64_t tsum = 0;
+        for (uint32_t f = 0; f < 128; f++) { md->qf[t][f] = get16(b + ft + 256ull * (t - 1) + 2 * f); tsum += md->qf[t][f]; }
+        if (tsum != (1ull << md->M_f)) return BSO_EFORMAT;
+    }
+    return BSO_OK;
+}
+
+int bso_decode_container(const uint8_t* c, uint64_t len, uint8_t* out, uint64_t out_cap, int32_t* rec_status) {
+    if (len < BSO_HDR_BYTES || memcmp(c, BSO_MAGIC, 8) != 0) return BSO_EFORMAT;
+    if (get32(c + 8) != BSO_VERSION) return BSO_EVERSION;
+    uint32_t n_rec = get32(c + 12);
+    uint64_t dir = get64(c + 16);
+    if (get64(c + 24) != len) return BSO_EFORMAT;
+    if (dir + (uint64_t)BSO_DIR_BYTES * n_rec > len) return BSO_EFORMAT;
+    if (get64(c + 32) > out_cap) return BSO_ENOSPACE;
+    int first_err = BSO_OK;
+    for (uint32_t i = 0; i < n_rec; i++) {
+        const uint8_t* d = c + dir + (uint64_t)BSO_DIR_BYTES * i;
+        uint32_t kind = get32(d);
+        uint64_t n = get64(d + 8), oo = get64(d + 16), ro = get64(d + 24), rl = get64(d + 32);
+        int rc = BSO_OK;
+        if (ro + rl > len || ro + rl < ro) rc = BSO_EFORMAT;
+        else if (kind == BSO_KIND_RAW) {
+            if (oo + n > out_cap || rl < n) rc = BSO_EFORMAT;
+            else if (n) memcpy(out + oo, c + ro, n);
+        } else if (kind == BSO_KIND_BF16) {
+            bso_model* md = (bso_model*)calloc(1, sizeof(bso_model));
+            uint32_t W, K; uint64_t nch, io;
+            if (!md) rc = BSO_ENOMEM;
+            if (!rc) rc = parse_model(c + ro, rl, n, md, &W, &K, &nch, &io);
+            if (!rc && (oo + 2 * n > out_cap || oo % 16)) rc = BSO_EFORMAT;
+            uint16_t* tmp = NULL;
+            if (!rc && n) { tmp = (uint16_t*)malloc(sizeof(uint16_t) * W); if (!tmp) rc = BSO_ENOMEM; }
+            for (uint64_t ch = 0; ch < nch && !rc; ch++) {
+                const uint8_t* e = c + ro + io + 16 * ch;
+                uint64_t po = get64(e);
+                uint64_t nw = get32(e + 8);
+                uint64_t sb = round_up(4ull * K, 16);
+                if (po % 16 || po + sb + 2 * nw > rl) { rc = BSO_EFORMAT; break; }
+                uint32_t n_c = (uint32_t)((n - ch * W) < W ? (n - ch * W) : W);
+                uint32_t* st = (uint32_t*)malloc(sizeof(uint32_t) * K);
+                uint16_t* words = (uint16_t*)malloc(sizeof(uint16_t) * (nw ? nw : 1));
+                if (!st || !words) { free(st); free(words); rc = BSO_ENOMEM; break; }
+                for (uint32_t l = 0; l < K; l++) st[l] = get32(c + ro + po + 4ull * l);
+                for (uint64_t j = 0; j < nw; j++) words[j] = (uint16_t)get16(c + ro + po + sb + 2 * j);
+                rc = chunk_decode(md, st, words, nw, n_c, K, tmp);
+                if (!rc) for (uint32_t j = 0; j < n_c; j++) put16(out + oo + 2 * (ch * W + j), tmp[j]);
+                free(st); free(words);
+            }
+            free(tmp); free(md);
+        } else {
+            rc = BSO_EFORMAT;
+        }
+        if (rec_status) rec_status[i] = rc;
+        if (rc && !first_err) first_err = rc;
+    }
+    return first_err;
+}

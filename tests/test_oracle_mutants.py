@@ -1,0 +1,71 @@
+"""Planted mistakes in the oracle must be caught by its pins (no GPU).
+
+Each case copies oracle/bs_oracle.c, changes one expression the way a
+plausible bug would (a dropped term, a wrong comparison, a reversed order),
+compiles the copy with gcc into a temporary directory and runs the quick pin
+tests against it in a child process.  The pins must fail for every mutant;
+the unmodified oracle must pass the same selection.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "bs_oracle.c")
+PINS = ["tests/test_oracle_coder.py", "tests/test_oracle_model.py", "tests/test_oracle_container.py"]
+SELECT = ["-m", "not slow", "-k", "not cfg1 and not cfg2 and not gaussian and not scale_invariance"]
+
+MUTANTS = {
+    "encode_drops_cum": ("*x = (*x / q) * (1u << t->M) + (*x % q) + cum;", "*x = (*x / q) * (1u << t->M) + (*x % q);"),
+    "decode_drops_cum": ("*x = t->q[s] * (*x >> t->M) + slot - cum;", "*x = t->q[s] * (*x >> t->M) + slot;"),
+    "flush_off_by_one": ("if ((uint64_t)*x >= x_max) {", "if ((uint64_t)*x > x_max) {"),
+    "refill_off_by_one": ("if (*x < BSO_L) {\n        if (*pos >= nw)", "if (*x <= BSO_L) {\n        if (*pos >= nw)"),
+    "chunk_lanes_ascending": ("for (int64_t l = (int64_t)K - 1; l >= 0; l--) {\n                    uint64_t j",
+                              "for (int64_t l = 0; l < (int64_t)K; l++) {\n                    uint64_t j"),
+    "sched_lanes_ascending": ("for (int64_t l = (int64_t)K - 1; l >= 0 && !rc; l--) {",
+                              "for (int64_t l = 0; l < (int64_t)K && !rc; l++) {"),
+    "words_not_reversed": ("put16(b + start + states_bytes + 2 * i, wl.w[wl.n - 1 - i]);",
+                           "put16(b + start + states_bytes + 2 * i, wl.w[i]);"),
+    "phase_order_swapped": ("for (int phase = 1; phase >= 0; phase--) {", "for (int phase = 0; phase <= 1; phase++) {"),
+    "sign_in_wrong_place": ("return (uint16_t)((sign << 15) | (expo << 7) | f);", "return (uint16_t)((sign << 7) | (expo << 8) | f);"),
+    "normalise_tie_high_index": ("(rem[ib] == rem[ibest] && ib < ibest)", "(rem[ib] == rem[ibest] && ib > ibest)"),
+    "normalise_no_floor_one": ("q[i] = (uint32_t)(v < 1 ? 1 : v);", "q[i] = (uint32_t)v;"),
+    "table_always_eligible": ("eligible[k] = (256 * E > n * n + (unsigned __int128)726784 * n);", "eligible[k] = 1;"),
+    "signs_not_merged": ("unsigned __int128 m = (unsigned __int128)cf[e * 128 + f] + cf[(256 + e) * 128 + f];",
+                         "unsigned __int128 m = cf[e * 128 + f];"),
+    "shape_rounding": ("*W = (uint32_t)round_up(n ? n : 1, 8 * (uint64_t)k);", "*W = (uint32_t)round_up(n ? n : 1, 8);"),
+}
+
+
+def _run_pins(lib_path):
+    env = dict(os.environ)
+    env["BSO_ORACLE_LIB"] = lib_path
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PINS, *SELECT],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return r.returncode, r.stdout[-2000:]
+
+
+def _build(src_text, tmp_path, name):
+    c = tmp_path / f"{name}.c"
+    so = tmp_path / f"{name}.so"
+    c.write_text(src_text)
+    subprocess.check_call(["gcc", "-O1", "-std=gnu11", "-fPIC", "-shared", "-o", str(so), str(c)])
+    return str(so)
+
+
+def test_unmodified_oracle_passes_selection(tmp_path):
+    so = _build(open(SRC).read(), tmp_path, "clean")
+    rc, out = _run_pins(so)
+    assert rc == 0, out
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) >= 1, f"mutation anchor not found: {name}"
+    so = _build(text.replace(old, new, 1), tmp_path, name)
+    rc, out = _run_pins(so)
+    assert rc != 0, f"planted mistake {name} was not caught:\n{out}"
