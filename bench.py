@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Benchmark: decoded BF16 GB/s of the HIP decode path on one MI355X, its
+fraction of the HBM roofline, and compressed bits/weight against the
+empirical conditional entropy.
+
+A step is one decode of the whole workload (bs_decode_async over every
+record: the rANS decode kernel plus the verbatim residual copy), with the
+container already resident in HBM and the output buffer preallocated.
+The default workload is the 4096x4096 BF16 matrix with log-normal row scales,
+0.1% outliers and 1% exact zeros, in 256 KiB chunks.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1|2|3|4|5] [--cold]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth, GB/s
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5"])
+    ap.add_argument("--cold", action="store_true", help="write a 1 GiB buffer between timed decodes (not in the timing)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle baseline")
+    ap.add_argument("--cfg5-layers", type=int, default=84, help="config 5: layers to build (84 = full checkpoint)")
+    return ap.parse_args()
+
+
+def cpu_baseline(job, seconds: float):
+    """The CPU oracle (plain scalar C, one thread, not tuned) decoding the same
+    container on the host: whole records while the budget lasts, else a sample
+    of chunks.  Returns decoded BF16 GB/s."""
+    from oracle import oracle as O
+    containers = job.containers() if hasattr(job, "containers") else [job.enc.container]
+    decoded = 0
+    t0 = time.perf_counter()
+    sample = ""
+    done = False
+    for c in containers:
+        info_n = int.from_bytes(c[12:16], "little")
+        # a whole container if it fits the budget (about 7-8 MB/s), else chunks one by one
+        est = len(c) / 5e6
+        if est < seconds - (time.perf_counter() - t0):
+            out, st = O.decode(c)
+            decoded += len(out)
+            sample = "whole containers"
+        else:
+            from lossless_entropy_coding_amd import codec
+            for i in range(info_n):
+                ri = codec.record_info(c, i)
+                if ri.kind != 1:
+                    continue
+                for ch in range(ri.n_chunks):
+                    w = O.decode_chunk(c, i, ch)
+                    decoded += 2 * w.size
+                    if time.perf_counter() - t0 > seconds:
+                        done = True
+                        break
+                if done:
+                    break
+            sample = f"leading chunks of the workload, {decoded / 2:.0f} weights"
+        if done or time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    log(f"cpu baseline: {decoded / 1e6:.1f} MB in {dt:.1f}s")
+    return {"value": round(decoded / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only: this build decodes on a single MI355X and has no multi-GPU "
+              f"path (asked for --gpus {a.gpus}). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from lossless_entropy_coding_amd import _lib as L
+    from lossless_entropy_coding_amd import codec, synth, workloads
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    L.lib()   # fails loudly if the HIP library is missing
+    dev = "cuda"
+    t0 = time.time()
+    if a.config == "5":
+        from lossless_entropy_coding_amd import checkpoint
+        job = checkpoint.build_job(layers=a.cfg5_layers, log=log)
+    else:
+        gen_dev = "cuda" if a.config == "4" else "cpu"
+        enc = workloads.encode_config(a.config, device=gen_dev, keep_reference=False, keep_device_reference=True)
+        job = workloads.DecodeJob(enc)
+    log(f"workload {job.name}: {job.n_weights} BF16 weights, container {job.container_bytes / 1e6:.1f} MB, "
+        f"built in {time.time() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if a.cold else None
+
+    def step():
+        job.decode(stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    # correctness of the measured configuration: status + device compare against the original bits
+    ok, detail = job.verify()
+    if not ok:
+        log("VERIFY FAILED", detail)
+        sys.exit(1)
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    if flush is None:
+        t_start = time.perf_counter()
+        for e0, e1 in evs:
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+    else:
+        wall = 0.0
+        for e0, e1 in evs:
+            flush.fill_(1)
+            torch.cuda.synchronize()
+            t_s = time.perf_counter()
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t_s
+    ev_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    avg_ms = float(np.mean(ev_ms))
+    med_ms = float(np.median(ev_ms))
+    ok, detail = job.verify()
+    if not ok:
+        log("VERIFY FAILED after timing", detail)
+        sys.exit(1)
+
+    out_bytes = 2 * job.n_weights + job.raw_bytes
+    value = job.n_weights * 2 * a.steps / wall / 1e9          # decoded BF16 GB/s, whole job
+    # algorithmic bytes per decode: the container bytes that are read (BF16
+    # records: tables, index, states, words; verbatim spans) + the bytes written
+    alg_bytes = job.read_bytes + out_bytes
+    achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode_kernel<%d>" % job.lanes_per_thread,
+                "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(avg_ms, 4),
+                "median_launch_ms": round(med_ms, 4)}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(job, a.cpu_seconds)
+
+    line = {
+        "metric": "decoded BF16 GB/s on 1 MI355X (% HBM roofline) + compressed bits/weight",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(wall / a.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": job.name, "bf16_weights": job.n_weights, "raw_bytes": job.raw_bytes,
+                   "chunk_weights": job.chunk_weights, "lanes": job.lanes, "m_s": 12, "m_f": 10,
+                   "bits_per_weight": round(job.bits_per_weight, 5), "entropy_bits": round(job.entropy_bits, 5),
+                   "bits_over_entropy_pct": round(100 * (job.bits_per_weight / job.entropy_bits - 1), 3),
+                   "cold_cache": bool(a.cold), "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,256 @@
+/*
+ * bs.h -- C ABI of the MI355X (gfx950) lossless BF16 weight codec.
+ *
+ * What the library computes [Qwen3.8-27B-BF16-NVLC-Lossless model card, codec
+ * paragraph after the metrics table]: every BF16 word is split into its exact
+ * fields [sign:1 | exponent:8 | fraction:7]; the joint 9-bit (sign, exponent)
+ * symbol s is coded with a per-tensor rANS model; the decoded s selects the
+ * distribution of the exact 7-bit fraction f; decoding recombines the fields
+ * bitwise (w = s << 7 | f); spans that are not BF16 pass through verbatim.
+ * Every tensor carries a hash checked after decompression [Gemma 2 9B
+ * Instruct -- Lossless Compressed card, "What lossless means"; NVLC card,
+ * SHA256SUMS verification block] (sha256 here).
+ *
+ * Container ("BF16RANS", version 1, little-endian) -- this library's own layout:
+ *   header 64 B: magic[8] "BF16RANS", u32 version, u32 n_records,
+ *                u64 dir_offset, u64 total_len, u64 out_len, u32 flags, 20 B zero
+ *   directory, 96 B per record: u32 kind (1 = BF16 rANS, 2 = RAW verbatim),
+ *                u32 0, u64 n (weights for BF16, bytes for RAW), u64 out_offset,
+ *                u64 rec_offset, u64 rec_len, u8 sha256[32], 24 B zero
+ *   BF16 record body: u32 W (weights per chunk), u32 K (lanes), u32 n_chunks,
+ *                u8 M_s, u8 M_f, u8 n_tables, u8 0, u32 n_sym, u32 0;
+ *                s-table n_sym x (u16 s, u16 q) ascending s (sum q = 2^M_s);
+ *                route: n_sym bytes (fraction table of each s: 0 = flat,
+ *                1..n_tables), padded to 4 B; n_tables x 128 x u16 q_f
+ *                (each sums to 2^M_f); pad to 16 B; chunk index n_chunks x
+ *                (u64 payload offset from the body start, u32 words, u32 0);
+ *                payloads: K x u32 final encoder states (pad 16 B), then the
+ *                16-bit words in decode order (pad 16 B).
+ *   Coder: 32-bit state in [2^16, 2^32), 16-bit renormalisation words.  In a
+ *   chunk, weight j belongs to lane (j/8) mod K, macro-step (j/8)/K; each lane
+ *   decodes, per weight, s with the s-table then f with the table route[s];
+ *   lanes take turns in ascending order within each (macro-step, position,
+ *   field) sub-step, consuming stream words in that order.  Fraction tables
+ *   with id 0 are flat (q = 2^(M_f - 7) for every f).
+ *
+ * Conventions:
+ *   - Every function returns a bs_status (0 = BS_OK); none throws or aborts.
+ *     bs_last_error() gives a thread-local message for the last failure.
+ *   - "d_" pointers are device (HBM) pointers, "h_" pointers host pointers.
+ *     All tensors and output buffers are caller-owned.  The library owns only
+ *     the opaque objects it returns (bs_tables, bs_blob, bs_plan) and frees
+ *     them in the matching *_free / *_destroy call.
+ *   - Device work is enqueued on the caller's stream (hipStream_t passed as
+ *     void*; NULL = the null stream) and is stream-ordered.
+ */
+#ifndef BS_H
+#define BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BS_OK = 0,
+    BS_E_INVAL = -1,       /* bad argument */
+    BS_E_FORMAT = -2,      /* container malformed or truncated */
+    BS_E_VERSION = -3,     /* container version not supported */
+    BS_E_NOSPACE = -4,     /* output capacity too small */
+    BS_E_NOMEM = -5,       /* host or device allocation failed */
+    BS_E_HIP = -6,         /* HIP runtime error */
+    BS_E_CORRUPT = -7,     /* decoded data failed its per-chunk checks */
+    BS_E_MISMATCH = -8,    /* decoded bytes differ from the reference or digest */
+    BS_E_EXISTS = -9       /* refusing to overwrite existing output */
+} bs_status;
+
+enum { BS_KIND_BF16 = 1, BS_KIND_RAW = 2 };
+
+/* Encoder parameters.  chunk_weights W must be a multiple of 8*lanes; lanes K
+ * is 1..64, 128 or 256 (a power of two); 9 <= m_s <= 12; 7 <= m_f <= 10;
+ * max_tables <= 6; threads = host encoder threads (0 = hardware count). */
+typedef struct {
+    uint32_t chunk_weights;
+    uint32_t lanes;
+    uint32_t m_s;
+    uint32_t m_f;
+    uint32_t max_tables;
+    uint32_t threads;
+} bs_params;
+
+/* Fill *p with the defaults: W = 65536, K = 128, m_s = 12, m_f = 10,
+ * max_tables = 6, threads = 0. */
+void bs_params_default(bs_params* p);
+
+/* ---------------------------------------------------------------- model */
+
+typedef struct bs_tables bs_tables; /* opaque, library-owned */
+
+/* Build the per-tensor model of n BF16 words that are resident on the device
+ * [NVLC card, codec paragraph: the sign/exponent model is per tensor, the
+ * fraction distribution is selected by the decoded symbol].
+ * Two HIP histogram passes with LDS-privatised counters (sign/exponent, then
+ * fraction counts of the 64 most frequent exponents), then host quantisation
+ * of the counts to 2^m_s and 2^m_f and the choice of coded fraction contexts.
+ * d_bf16: n little-endian 16-bit words in device memory (any alignment of 2).
+ * Synchronises `stream`.  *out receives a new bs_tables (free with
+ * bs_tables_free).  Errors: BS_E_INVAL (bad params / NULL), BS_E_HIP,
+ * BS_E_NOMEM. */
+bs_status bs_build_tables(const void* d_bf16, uint64_t n, const bs_params* p, void* stream, bs_tables** out);
+
+/* Same model from host memory (CPU histogram); identical result. */
+bs_status bs_build_tables_host(const uint16_t* h_bf16, uint64_t n, const bs_params* p, bs_tables** out);
+
+void bs_tables_free(bs_tables* t);
+
+/* Read back a model (for inspection and tests).  Arrays are caller-owned:
+ * counts_s[512] (u64, may be NULL), q_s[512], route[512] (table id of each s),
+ * q_f[6*128] (row t-1 = table t); *n_tables, *m_s, *m_f, *n_weights. */
+bs_status bs_tables_get(const bs_tables* t, uint64_t* counts_s, uint32_t* q_s, uint32_t* route,
+                        uint32_t* q_f, uint32_t* n_tables, uint32_t* m_s, uint32_t* m_f, uint64_t* n_weights);
+
+/* ---------------------------------------------------------------- encode */
+
+/* One tensor to encode.  kind BS_KIND_BF16: h_data holds n 16-bit words and
+ * tables is its model (NULL = built on the host here).  kind BS_KIND_RAW:
+ * h_data holds n bytes copied verbatim (the residual for non-BF16 spans
+ * [NVLC card, codec paragraph]).  sha256: 32 bytes or NULL (computed here). */
+typedef struct {
+    uint32_t kind;
+    uint32_t reserved;
+    const void* h_data;
+    uint64_t n;
+    const bs_tables* tables;
+    const uint8_t* sha256;
+} bs_tensor;
+
+typedef struct bs_blob bs_blob; /* opaque, library-owned byte buffer */
+
+/* Encode tensors[0..n_tensors) into one container, in order, on host threads.
+ * Output offsets are assigned in order, each rounded up to 256 B.  A BF16
+ * tensor with more than 256 distinct (sign, exponent) symbols is stored as a
+ * RAW record of its bytes.  The result is deterministic (independent of the
+ * thread count).  *out receives a new bs_blob (free with bs_blob_free).
+ * Errors: BS_E_INVAL (bad params, a model built for another n), BS_E_NOMEM. */
+bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_params* p, bs_blob** out);
+
+const void* bs_blob_data(const bs_blob* b);
+uint64_t bs_blob_size(const bs_blob* b);
+void bs_blob_free(bs_blob* b);
+
+/* ---------------------------------------------------------------- inspect */
+
+typedef struct {
+    uint32_t version;
+    uint32_t n_records;
+    uint64_t total_len;
+    uint64_t out_len;       /* bytes of the fully decoded output */
+    uint64_t n_chunks;      /* chunks over all BF16 records (status array length) */
+    uint64_t bf16_weights;  /* BF16 weights over all BF16 records */
+    uint64_t bf16_bytes;    /* container bytes charged to BF16 records (bodies + their directory share + header share) */
+    uint64_t raw_bytes;     /* verbatim bytes */
+} bs_container_info;
+
+typedef struct {
+    uint32_t kind;
+    uint32_t chunk_weights, lanes, n_chunks;
+    uint32_t m_s, m_f, n_tables, n_sym;
+    uint64_t n, out_offset, rec_offset, rec_len;
+    uint64_t chunk_base;    /* index of the record's first chunk in the status array */
+    uint8_t sha256[32];
+} bs_record_info;
+
+/* Validate a host copy of a container and describe it.  Errors: BS_E_FORMAT,
+ * BS_E_VERSION. */
+bs_status bs_container_info_get(const void* h_container, uint64_t len, bs_container_info* info);
+bs_status bs_record_info_get(const void* h_container, uint64_t len, uint32_t index, bs_record_info* info);
+
+/* ---------------------------------------------------------------- decode */
+
+typedef struct bs_plan bs_plan; /* opaque, library-owned device work list + lookup tables */
+
+/* Prepare decoding of a container resident in device memory.  h_container is
+ * a host copy of the same bytes (only its header, directory, tables and chunk
+ * index are read); d_container the device copy (len bytes, 16-B aligned).
+ * Validates everything the kernels rely on (record bounds, table sums, chunk
+ * payload bounds), allocates the plan's device memory, uploads the work list
+ * and builds each record's decode lookup tables with a HIP kernel on
+ * `stream`.  The plan references d_container, which must stay valid and
+ * unchanged while the plan is used.  Errors: BS_E_FORMAT, BS_E_VERSION,
+ * BS_E_NOMEM, BS_E_HIP. */
+bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_container, void* stream,
+                         bs_plan** out);
+void bs_plan_destroy(bs_plan* plan);
+
+/* Decode records [first, first + count) into d_out, enqueued on `stream`
+ * (no host synchronisation).  Record i is written at
+ * d_out + out_offset(i) - out_offset(first); the bytes between records are not
+ * written.  d_out must be 16-B aligned with at least the returned
+ * bs_plan_out_bytes(plan, first, count) bytes of capacity; nothing outside
+ * [d_out, d_out + that size) is written.  d_status: one u32 per chunk of the
+ * whole container (bs_container_info.n_chunks); the entries of the decoded
+ * records are set to 0 (ok) or a bit set: 1 = a lane did not end at the
+ * initial state, 2 = the words consumed differ from the chunk's count.  The
+ * output is valid after the stream reaches this point.  Errors (returned
+ * before anything is enqueued): BS_E_INVAL (range, alignment), BS_E_NOSPACE
+ * (out_capacity too small), BS_E_HIP (launch failed). */
+bs_status bs_decode_async(const bs_plan* plan, uint32_t first, uint32_t count, void* d_out, uint64_t out_capacity,
+                          uint32_t* d_status, void* stream);
+
+/* Bytes needed to decode records [first, first + count). */
+uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count);
+
+/* Chunks (one per wavefront) that each decode workgroup of this plan takes. */
+uint32_t bs_plan_waves_per_block(const bs_plan* plan);
+
+/* ---------------------------------------------------------------- verify */
+
+enum {
+    BS_VERIFY_STATUS = 1,   /* read back d_status and report corrupt chunks */
+    BS_VERIFY_COMPARE = 2,  /* device byte compare of d_out against d_ref */
+    BS_VERIFY_SHA256 = 4    /* copy each record back and compare its sha256 with the directory */
+};
+
+typedef struct {
+    uint64_t chunks_checked;
+    uint64_t chunks_bad;
+    uint64_t first_bad_chunk;     /* UINT64_MAX if none */
+    uint64_t bytes_compared;
+    uint64_t bytes_mismatched;
+    uint64_t first_mismatch;      /* byte offset relative to d_out, UINT64_MAX if none */
+    uint32_t records_hashed;
+    uint32_t records_hash_bad;
+    uint32_t first_hash_bad;      /* record index, UINT32_MAX if none */
+    uint32_t reserved;
+} bs_report;
+
+/* Synchronise `stream`, then check records [first, first + count) of a
+ * decode made with the same plan and range.  d_ref (BS_VERIFY_COMPARE) holds
+ * the expected bytes laid out like d_out.  Returns BS_OK when every requested
+ * check passes, BS_E_CORRUPT when a chunk status is bad, BS_E_MISMATCH when
+ * bytes or a digest differ; the report is filled in every case.  Errors:
+ * BS_E_INVAL, BS_E_HIP, BS_E_NOMEM. */
+bs_status bs_verify(const bs_plan* plan, uint32_t first, uint32_t count, const void* d_out, const void* d_ref,
+                    const uint32_t* d_status, uint32_t flags, void* stream, bs_report* report);
+
+/* ---------------------------------------------------------------- misc */
+
+/* sha256 of n host bytes (FIPS 180-4), into out[32]. */
+void bs_sha256(const void* h_data, uint64_t n, uint8_t out[32]);
+
+/* Write a container to `path`, refusing to replace an existing file
+ * (BS_E_EXISTS), as the pages' reconstruction tool refuses an existing
+ * output path [NVLC card, reconstruction instructions]. */
+bs_status bs_write_file_new(const char* path, const void* h_data, uint64_t n);
+
+const char* bs_strerror(bs_status s);
+const char* bs_last_error(void);
+const char* bs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BS_H */

@@ -1,0 +1,73 @@
+"""Build the HIP library libbs.so for gfx950 (in-tree), and the oracle.
+
+Usage: python -m lossless_entropy_coding_amd.build [--asm DIR]
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libbs.so")
+ARCH = "gfx950"
+
+SOURCES = ["bs_kernels.hip", "bs_model.cpp", "bs_codec.cpp", "bs_plan.cpp", "bs_sha256.cpp"]
+# packed FP32 instructions are disabled on purpose for every HIP compile
+HIP_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", CSRC, "-I", INCLUDE]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build_lib(asm_dir: str | None = None, verbose: bool = False) -> str:
+    cc = hipcc()
+    with tempfile.TemporaryDirectory() as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            if asm_dir and src.endswith(".hip"):
+                os.makedirs(asm_dir, exist_ok=True)
+                cmd += ["-save-temps=obj"]
+                cmd[cmd.index("-o") + 1] = os.path.join(asm_dir, src + ".o")
+                obj = os.path.join(asm_dir, src + ".o")
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                sys.stderr.write(r.stdout + r.stderr)
+                raise RuntimeError(f"compiling {src} failed")
+            objs.append(obj)
+        tmp_lib = LIB + ".tmp"
+        r = subprocess.run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib, "-lpthread"],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("linking libbs.so failed")
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--asm", default=None, help="keep intermediate files (ISA) in this directory")
+    ap.add_argument("-v", action="store_true")
+    a = ap.parse_args(argv)
+    print(build_lib(a.asm, a.v))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+"""Python face of the codec: thin wrappers over the C ABI (include/bs.h).
+
+PyTorch provides device memory and streams only; every step of building
+tables, encoding, decoding and verifying runs in the library (host C++ for
+the encoder, HIP kernels on gfx950 for histograms, lookup tables, decoding,
+residual copies and compares).
+
+The codec [Qwen3.8-27B-BF16-NVLC-Lossless model card, codec paragraph]: each
+BF16 word is split into [sign:1 | exponent:8 | fraction:7]; the joint
+(sign, exponent) symbol is rANS-coded with a per-tensor model and selects the
+distribution of the fraction; the decoder recombines the fields bitwise and
+copies non-BF16 spans verbatim.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def params(chunk_weights: int = 65536, lanes: int = 128, m_s: int = 12, m_f: int = 10, max_tables: int = 6,
+           threads: int = 0) -> L.Params:
+    p = L.Params()
+    L.lib().bs_params_default(C.byref(p))
+    p.chunk_weights, p.lanes, p.m_s, p.m_f, p.max_tables, p.threads = (chunk_weights, lanes, m_s, m_f,
+                                                                       max_tables, threads)
+    return p
+
+
+class Tables:
+    """A per-tensor model (opaque bs_tables), freed with the object."""
+
+    def __init__(self, handle: int):
+        self.handle = C.c_void_p(handle)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and self.handle.value:
+            L.lib().bs_tables_free(self.handle)
+            self.handle = C.c_void_p(0)
+
+    def get(self) -> dict:
+        cs = np.zeros(512, np.uint64)
+        qs = np.zeros(512, np.uint32)
+        route = np.zeros(512, np.uint32)
+        qf = np.zeros((6, 128), np.uint32)
+        nt, ms, mf = C.c_uint32(), C.c_uint32(), C.c_uint32()
+        n = C.c_uint64()
+        L.check(L.lib().bs_tables_get(self.handle, cs.ctypes.data, qs.ctypes.data, route.ctypes.data,
+                                      qf.ctypes.data, C.byref(nt), C.byref(ms), C.byref(mf), C.byref(n)),
+                "bs_tables_get")
+        return {"counts_s": cs, "q_s": qs, "route": route, "n_tables": nt.value, "q_f": qf[: nt.value].copy(),
+                "m_s": ms.value, "m_f": mf.value, "n": n.value}
+
+
+def build_tables(words: torch.Tensor, p: L.Params | None = None, stream=None) -> Tables:
+    """Model of a device-resident BF16 (or int16-viewed) tensor, built by the HIP histogram kernels."""
+    p = p or params()
+    t = words.contiguous()
+    assert t.is_cuda and t.element_size() == 2
+    out = C.c_void_p()
+    L.check(L.lib().bs_build_tables(C.c_void_p(t.data_ptr()), t.numel(), C.byref(p), C.c_void_p(_stream_handle(stream)),
+                                    C.byref(out)), "bs_build_tables")
+    return Tables(out.value)
+
+
+def build_tables_host(words: np.ndarray, p: L.Params | None = None) -> Tables:
+    p = p or params()
+    w = np.ascontiguousarray(words, np.uint16)
+    out = C.c_void_p()
+    L.check(L.lib().bs_build_tables_host(w.ctypes.data, w.size, C.byref(p), C.byref(out)), "bs_build_tables_host")
+    return Tables(out.value)
+
+
+@dataclass
+class HostTensor:
+    """A tensor to encode: kind 1 = BF16 words (uint16 ndarray), 2 = raw bytes (uint8 ndarray)."""
+    kind: int
+    data: np.ndarray
+    tables: Tables | None = None
+    sha256: bytes | None = None
+
+
+def bf16(words, tables: Tables | None = None) -> HostTensor:
+    return HostTensor(L.KIND_BF16, np.ascontiguousarray(words, np.uint16).reshape(-1), tables)
+
+
+def raw(b) -> HostTensor:
+    a = b if isinstance(b, np.ndarray) else np.frombuffer(bytes(b), np.uint8)
+    return HostTensor(L.KIND_RAW, np.ascontiguousarray(a).view(np.uint8).reshape(-1))
+
+
+def encode(tensors, p: L.Params | None = None) -> bytes:
+    """Encode host tensors into one container (host C++ encoder, multithreaded)."""
+    p = p or params()
+    arr = (L.Tensor * max(len(tensors), 1))()
+    keep = []
+    for i, t in enumerate(tensors):
+        d = np.ascontiguousarray(t.data)
+        keep.append(d)
+        arr[i].kind = t.kind
+        arr[i].h_data = d.ctypes.data if d.size else None
+        arr[i].n = d.size
+        arr[i].tables = t.tables.handle if t.tables is not None else None
+        if t.sha256 is not None:
+            sb = C.create_string_buffer(t.sha256, 32)
+            keep.append(sb)
+            arr[i].sha256 = C.addressof(sb)
+    blob = C.c_void_p()
+    L.check(L.lib().bs_encode_host(arr, len(tensors), C.byref(p), C.byref(blob)), "bs_encode_host")
+    try:
+        n = L.lib().bs_blob_size(blob)
+        return C.string_at(L.lib().bs_blob_data(blob), n)
+    finally:
+        L.lib().bs_blob_free(blob)
+
+
+def container_info(container: bytes) -> L.ContainerInfo:
+    info = L.ContainerInfo()
+    L.check(L.lib().bs_container_info_get(container, len(container), C.byref(info)), "bs_container_info_get")
+    return info
+
+
+def record_info(container: bytes, i: int) -> L.RecordInfo:
+    info = L.RecordInfo()
+    L.check(L.lib().bs_record_info_get(container, len(container), i, C.byref(info)), "bs_record_info_get")
+    return info
+
+
+class Plan:
+    """A container resident in HBM plus its decode plan (opaque bs_plan)."""
+
+    def __init__(self, container: bytes, device: str = "cuda", stream=None):
+        self.host = container
+        self.info = container_info(container)
+        self.n_records = self.info.n_records
+        # 16-byte aligned device copy (torch allocations are 256-B aligned)
+        self.dev = torch.frombuffer(bytearray(container), dtype=torch.uint8).to(device)
+        out = C.c_void_p()
+        L.check(L.lib().bs_plan_create(container, len(container), C.c_void_p(self.dev.data_ptr()),
+                                       C.c_void_p(_stream_handle(stream)), C.byref(out)), "bs_plan_create")
+        self.handle = out
+        self.status = torch.zeros(max(self.info.n_chunks, 1), dtype=torch.int32, device=device)
+
+    def __del__(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            L.lib().bs_plan_destroy(self.handle)
+            self.handle = C.c_void_p(0)
+
+    def out_bytes(self, first: int = 0, count: int | None = None) -> int:
+        count = self.n_records - first if count is None else count
+        return int(L.lib().bs_plan_out_bytes(self.handle, first, count))
+
+    @property
+    def waves_per_block(self) -> int:
+        return int(L.lib().bs_plan_waves_per_block(self.handle))
+
+    def new_output(self, first: int = 0, count: int | None = None) -> torch.Tensor:
+        """A zero-filled output buffer for records [first, first+count) (gaps stay zero)."""
+        n = self.out_bytes(first, count)
+        return torch.zeros(max(n, 16), dtype=torch.uint8, device=self.dev.device)
+
+    def decode_into(self, out: torch.Tensor, first: int = 0, count: int | None = None, stream=None) -> None:
+        """Enqueue the decode of records [first, first+count) into `out` (no sync)."""
+        count = self.n_records - first if count is None else count
+        rc = L.lib().bs_decode_async(self.handle, first, count, C.c_void_p(out.data_ptr()),
+                                     out.numel() * out.element_size(), C.c_void_p(self.status.data_ptr()),
+                                     C.c_void_p(_stream_handle(stream)))
+        L.check(rc, "bs_decode_async")
+
+    def decode(self, first: int = 0, count: int | None = None, stream=None) -> torch.Tensor:
+        out = self.new_output(first, count)
+        self.decode_into(out, first, count, stream)
+        return out
+
+    def verify(self, out: torch.Tensor, ref: torch.Tensor | None = None, flags: int = L.VERIFY_STATUS,
+               first: int = 0, count: int | None = None, stream=None):
+        """Returns (status code, report dict); synchronises the stream."""
+        count = self.n_records - first if count is None else count
+        rep = L.Report()
+        rc = L.lib().bs_verify(self.handle, first, count, C.c_void_p(out.data_ptr()),
+                               C.c_void_p(ref.data_ptr()) if ref is not None else None,
+                               C.c_void_p(self.status.data_ptr()), flags, C.c_void_p(_stream_handle(stream)),
+                               C.byref(rep))
+        return rc, {k: getattr(rep, k) for k, _ in L.Report._fields_}
+
+
+def sha256(data) -> bytes:
+    a = np.ascontiguousarray(np.frombuffer(data, np.uint8) if isinstance(data, (bytes, bytearray)) else data)
+    out = (C.c_uint8 * 32)()
+    L.lib().bs_sha256(a.ctypes.data if a.size else None, a.nbytes, out)
+    return bytes(out)
+
+
+def write_new(path: str, data: bytes) -> None:
+    L.check(L.lib().bs_write_file_new(path.encode(), data, len(data)), "bs_write_file_new")
+
+
+def record_output(out: torch.Tensor, plan: Plan, i: int, first: int = 0) -> torch.Tensor:
+    """View of record i's decoded bytes inside an output buffer decoded from `first`."""
+    ri = record_info(plan.host, i)
+    base = record_info(plan.host, first).out_offset
+    nb = 2 * ri.n if ri.kind == L.KIND_BF16 else ri.n
+    return out[ri.out_offset - base: ri.out_offset - base + nb]

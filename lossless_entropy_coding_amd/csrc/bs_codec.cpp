@@ -1,0 +1,525 @@
+// bs_codec.cpp -- host encoder, container validation and the C ABI for
+// encode / inspect / decode / verify.
+//
+// The coder [Qwen3.8-27B-BF16-NVLC-Lossless card, codec paragraph]: each BF16
+// word is split into the joint (sign, exponent) symbol s = w >> 7 and the
+// fraction f = w & 127; s is coded with the tensor's rANS model and f with the
+// distribution that s selects; decoding recombines them bitwise.  The state
+// width, renormalisation unit, interleave and byte layout are this library's
+// container (bs.h).
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+#include <sys/stat.h>
+
+#include <algorithm>
+#include <atomic>
+#include <new>
+#include <thread>
+#include <vector>
+
+#include "bs_device.h"
+#include "bs_internal.h"
+#include "bs_model.h"
+
+struct bs_tables : bs::Model {};
+
+namespace bs {
+namespace {
+
+constexpr uint32_t kL = 65536u;
+
+// ------------------------------------------------------------------ encoder
+
+// rANS encoder entry of one symbol: flush threshold, frequency, start
+struct EncSym {
+    uint64_t x_max;  // flush the low word first when x >= x_max
+    uint32_t q;
+    uint32_t cum;
+};
+
+struct EncModel {
+    uint32_t m_s, m_f;
+    EncSym s[512];
+    EncSym f[kMaxTables + 1][128];
+    uint8_t route[512];
+};
+
+void make_enc(const Model& md, EncModel& em) {
+    em.m_s = md.m_s;
+    em.m_f = md.m_f;
+    uint32_t cum = 0;
+    for (uint32_t s = 0; s < 512; s++) {
+        em.s[s] = {(uint64_t)md.q_s[s] << (32 - md.m_s), md.q_s[s], cum};
+        cum += md.q_s[s];
+        em.route[s] = (uint8_t)md.route[s];
+    }
+    for (uint32_t t = 0; t <= md.n_tables; t++) {
+        cum = 0;
+        for (uint32_t f = 0; f < 128; f++) {
+            const uint32_t q = t == 0 ? (1u << (md.m_f - 7)) : md.q_f[t - 1][f];
+            em.f[t][f] = {(uint64_t)q << (32 - md.m_f), q, cum};
+            cum += q;
+        }
+    }
+}
+
+inline void put(uint32_t& x, const EncSym& e, uint32_t M, uint16_t*& sink) {
+    if (x >= e.x_max) {
+        *sink++ = (uint16_t)x;
+        x >>= 16;
+    }
+    x = ((x / e.q) << M) + x % e.q + e.cum;
+}
+
+// Encode one chunk (n_c weights, K lanes).  Sub-steps run from last to first,
+// lanes from K-1 down to 0 inside each, so that the decoder reads forwards;
+// the emitted words come out reversed and are turned around by the caller.
+// `scratch` must hold 2 * n_c words.  Returns the word count.
+uint64_t encode_chunk(const EncModel& em, const uint16_t* w, uint32_t n_c, uint32_t K, uint32_t* x,
+                      uint16_t* scratch) {
+    for (uint32_t l = 0; l < K; l++) x[l] = kL;
+    uint16_t* sink = scratch;
+    const uint32_t groups = (n_c + 7) / 8;
+    const uint32_t T = (groups + K - 1) / K;
+    for (uint32_t t = T; t-- > 0;) {
+        for (int p = 7; p >= 0; p--) {
+            // fraction sub-step, then sign/exponent sub-step (reverse of decode order)
+            for (uint32_t l = K; l-- > 0;) {
+                const uint64_t j = 8ull * ((uint64_t)t * K + l) + (uint64_t)p;
+                if (j >= n_c) continue;
+                const uint32_t v = w[j];
+                put(x[l], em.f[em.route[v >> 7]][v & 127], em.m_f, sink);
+            }
+            for (uint32_t l = K; l-- > 0;) {
+                const uint64_t j = 8ull * ((uint64_t)t * K + l) + (uint64_t)p;
+                if (j >= n_c) continue;
+                put(x[l], em.s[w[j] >> 7], em.m_s, sink);
+            }
+        }
+    }
+    return (uint64_t)(sink - scratch);
+}
+
+void record_shape(uint64_t n, uint32_t W, uint32_t K, uint32_t& w_out, uint32_t& k_out) {
+    if (n >= W) { w_out = W; k_out = K; return; }
+    const uint64_t per_lane = W / K;
+    uint32_t k = 1;
+    while (k < K && (uint64_t)k * per_lane < n) k <<= 1;
+    k_out = k;
+    w_out = (uint32_t)align_up(n ? n : 1, 8ull * k);
+}
+
+struct ChunkOut {
+    std::vector<uint32_t> states;
+    std::vector<uint16_t> words;   // decode order
+};
+
+struct EncRecord {
+    uint32_t kind = 0;
+    uint64_t n = 0;
+    const uint8_t* data = nullptr;
+    uint8_t sha[32];
+    const Model* md = nullptr;
+    Model owned;
+    EncModel em;
+    uint32_t W = 0, K = 0, n_chunks = 0;
+    std::vector<ChunkOut> chunks;
+    std::vector<uint8_t> head;   // fixed part + tables + chunk index (index filled at assembly)
+    uint64_t index_off = 0;
+};
+
+uint32_t pick_threads(uint32_t req) {
+    uint32_t hw = std::thread::hardware_concurrency();
+    if (!hw) hw = 4;
+    return req ? req : hw;
+}
+
+template <class F>
+void parallel_for(uint64_t n, uint32_t threads, F&& fn) {
+    std::atomic<uint64_t> next{0};
+    auto body = [&]() {
+        for (;;) {
+            uint64_t i = next.fetch_add(1);
+            if (i >= n) return;
+            fn(i);
+        }
+    };
+    const uint32_t nt = (uint32_t)std::min<uint64_t>(threads, std::max<uint64_t>(n, 1));
+    std::vector<std::thread> pool;
+    for (uint32_t k = 1; k < nt; k++) pool.emplace_back(body);
+    body();
+    for (auto& th : pool) th.join();
+}
+
+void build_head(EncRecord& r) {
+    const Model& md = *r.md;
+    const uint64_t stab = 24;
+    const uint64_t route_off = stab + 4ull * md.n_sym;
+    const uint64_t ftab = align_up(route_off + md.n_sym, 4);
+    const uint64_t tab_end = ftab + 256ull * md.n_tables;
+    r.index_off = align_up(tab_end, 16);
+    r.head.assign(r.index_off + 16ull * r.n_chunks, 0);
+    uint8_t* b = r.head.data();
+    wr32(b + 0, r.W);
+    wr32(b + 4, r.K);
+    wr32(b + 8, r.n_chunks);
+    b[12] = (uint8_t)md.m_s;
+    b[13] = (uint8_t)md.m_f;
+    b[14] = (uint8_t)md.n_tables;
+    wr32(b + 16, md.n_sym);
+    uint32_t k = 0;
+    for (uint32_t s = 0; s < 512; s++) {
+        if (!md.counts_s[s]) continue;
+        wr16(b + stab + 4 * k, s);
+        wr16(b + stab + 4 * k + 2, md.q_s[s]);
+        b[route_off + k] = (uint8_t)md.route[s];
+        k++;
+    }
+    for (uint32_t t = 0; t < md.n_tables; t++)
+        for (uint32_t f = 0; f < 128; f++) wr16(b + ftab + 256 * t + 2 * f, md.q_f[t][f]);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ validation
+
+bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
+    if (!h || len < kHeaderBytes || memcmp(h, kMagic, 8) != 0) {
+        set_error("not a BF16RANS container");
+        return BS_E_FORMAT;
+    }
+    if (rd32(h + 8) != kVersion) {
+        set_error("container version %u is not supported (this library reads version %u)", rd32(h + 8), kVersion);
+        return BS_E_VERSION;
+    }
+    c.n_records = rd32(h + 12);
+    const uint64_t dir = rd64(h + 16);
+    c.total_len = rd64(h + 24);
+    c.out_len = rd64(h + 32);
+    if (c.total_len != len) { set_error("length %llu differs from the header's %llu", (unsigned long long)len, (unsigned long long)c.total_len); return BS_E_FORMAT; }
+    if (dir < kHeaderBytes || dir > len || (len - dir) / kDirEntryBytes < c.n_records) {
+        set_error("directory out of bounds");
+        return BS_E_FORMAT;
+    }
+    c.recs.assign(c.n_records, Record());
+    c.n_chunks = 0;
+    uint64_t out_end = 0;
+    for (uint32_t i = 0; i < c.n_records; i++) {
+        const uint8_t* d = h + dir + kDirEntryBytes * i;
+        Record& r = c.recs[i];
+        r.kind = rd32(d);
+        r.n = rd64(d + 8);
+        r.out_offset = rd64(d + 16);
+        r.rec_offset = rd64(d + 24);
+        r.rec_len = rd64(d + 32);
+        memcpy(r.sha, d + 40, 32);
+        if (r.rec_offset > len || r.rec_len > len - r.rec_offset) { set_error("record %u out of bounds", i); return BS_E_FORMAT; }
+        if (r.kind != BS_KIND_BF16 && r.kind != BS_KIND_RAW) { set_error("record %u has unknown kind %u", i, r.kind); return BS_E_FORMAT; }
+        if (r.n > (1ull << 56) || r.out_offset > (1ull << 60)) { set_error("record %u size out of range", i); return BS_E_FORMAT; }
+        out_end = std::max(out_end, r.out_offset + r.out_bytes());
+        if (r.kind == BS_KIND_RAW) {
+            if (r.rec_len < r.n) { set_error("raw record %u shorter than its size", i); return BS_E_FORMAT; }
+            continue;
+        }
+        if (r.out_offset % 16) { set_error("BF16 record %u output offset not 16-aligned", i); return BS_E_FORMAT; }
+        if (r.rec_offset % 16) { set_error("BF16 record %u not 16-aligned", i); return BS_E_FORMAT; }
+        const uint8_t* b = h + r.rec_offset;
+        if (r.rec_len < 24) { set_error("record %u truncated", i); return BS_E_FORMAT; }
+        r.W = rd32(b);
+        r.K = rd32(b + 4);
+        r.n_chunks = rd32(b + 8);
+        r.m_s = b[12];
+        r.m_f = b[13];
+        r.n_tables = b[14];
+        r.n_sym = rd32(b + 16);
+        const uint32_t K = r.K;
+        if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256) || r.W == 0 || r.W % (8 * K)) {
+            set_error("record %u: bad chunk shape W=%u K=%u", i, r.W, K);
+            return BS_E_FORMAT;
+        }
+        if (r.m_s < 9 || r.m_s > 12 || r.m_f < 7 || r.m_f > 10 || r.n_tables > kMaxTables) {
+            set_error("record %u: bad table parameters", i);
+            return BS_E_FORMAT;
+        }
+        if ((uint64_t)r.n_chunks != (r.n + r.W - 1) / r.W) { set_error("record %u: chunk count mismatch", i); return BS_E_FORMAT; }
+        if (r.n_sym > kMaxSyms || (r.n_sym == 0) != (r.n == 0)) { set_error("record %u: bad symbol count", i); return BS_E_FORMAT; }
+        r.stab_off = 24;
+        r.route_off = 24 + 4 * r.n_sym;
+        r.ftab_off = (uint32_t)align_up(r.route_off + r.n_sym, 4);
+        r.index_off = align_up(r.ftab_off + 256ull * r.n_tables, 16);
+        if (r.index_off + 16ull * r.n_chunks > r.rec_len) { set_error("record %u: chunk index out of bounds", i); return BS_E_FORMAT; }
+        uint64_t sum = 0;
+        int last = -1;
+        for (uint32_t k = 0; k < r.n_sym; k++) {
+            const uint32_t s = rd16(b + r.stab_off + 4 * k), q = rd16(b + r.stab_off + 4 * k + 2);
+            if ((int)s <= last || s >= 512 || q == 0 || b[r.route_off + k] > r.n_tables) {
+                set_error("record %u: bad sign/exponent table", i);
+                return BS_E_FORMAT;
+            }
+            last = (int)s;
+            sum += q;
+        }
+        if (r.n_sym && sum != (1ull << r.m_s)) { set_error("record %u: sign/exponent frequencies do not sum to 2^%u", i, r.m_s); return BS_E_FORMAT; }
+        for (uint32_t t = 0; t < r.n_tables; t++) {
+            uint64_t fs = 0;
+            for (uint32_t f = 0; f < 128; f++) fs += rd16(b + r.ftab_off + 256 * t + 2 * f);
+            if (fs != (1ull << r.m_f)) { set_error("record %u: fraction table %u does not sum to 2^%u", i, t + 1, r.m_f); return BS_E_FORMAT; }
+        }
+        const uint64_t states_bytes = align_up(4ull * K, 16);
+        for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
+            const uint8_t* e = b + r.index_off + 16ull * ch;
+            const uint64_t po = rd64(e);
+            const uint64_t nw = rd32(e + 8);
+            const uint64_t n_c = std::min<uint64_t>(r.W, r.n - (uint64_t)ch * r.W);
+            if (po % 16 || po > r.rec_len || nw > 2 * n_c ||
+                states_bytes + align_up(2 * nw, 16) > r.rec_len - po) {
+                set_error("record %u chunk %u: payload out of bounds", i, ch);
+                return BS_E_FORMAT;
+            }
+        }
+        r.chunk_base = c.n_chunks;
+        c.n_chunks += r.n_chunks;
+    }
+    if (out_end > c.out_len) { set_error("records extend past the declared output length"); return BS_E_FORMAT; }
+    return BS_OK;
+}
+
+}  // namespace bs
+
+using namespace bs;
+
+struct bs_blob {
+    std::vector<uint8_t> bytes;
+};
+
+extern "C" {
+
+bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_params* p, bs_blob** out) {
+    if (!out || (!tensors && n_tensors)) { set_error("NULL argument"); return BS_E_INVAL; }
+    if (!params_ok(p)) return BS_E_INVAL;
+    std::vector<EncRecord> recs(n_tensors);
+    try {
+        // models and record shapes
+        for (uint32_t i = 0; i < n_tensors; i++) {
+            const bs_tensor& t = tensors[i];
+            EncRecord& r = recs[i];
+            r.kind = t.kind;
+            r.n = t.n;
+            r.data = (const uint8_t*)t.h_data;
+            if ((t.kind != BS_KIND_BF16 && t.kind != BS_KIND_RAW) || (!t.h_data && t.n)) {
+                set_error("tensor %u: bad kind or NULL data", i);
+                return BS_E_INVAL;
+            }
+            if (t.kind == BS_KIND_RAW) continue;
+            if (t.tables) {
+                if (t.tables->n != t.n || t.tables->m_s != p->m_s || t.tables->m_f != p->m_f) {
+                    set_error("tensor %u: model was built for other data or parameters", i);
+                    return BS_E_INVAL;
+                }
+                r.md = t.tables;
+            } else {
+                bs_tables* tb = nullptr;
+                bs_status rc = bs_build_tables_host((const uint16_t*)t.h_data, t.n, p, &tb);
+                if (rc) return rc;
+                r.owned = *tb;
+                bs_tables_free(tb);
+                r.md = &r.owned;
+            }
+            if (r.md->n_sym > kMaxSyms) {   // too many distinct symbols: keep the bytes verbatim
+                r.kind = BS_KIND_RAW;
+                r.n = 2 * t.n;
+                continue;
+            }
+            record_shape(t.n, p->chunk_weights, p->lanes, r.W, r.K);
+            r.n_chunks = (uint32_t)(t.n ? (t.n + r.W - 1) / r.W : 0);
+            make_enc(*r.md, r.em);
+            build_head(r);
+            r.chunks.resize(r.n_chunks);
+        }
+        // digests and chunks, in parallel
+        struct Job { uint32_t rec; int32_t chunk; };  // chunk = -1: digest
+        std::vector<Job> jobs;
+        for (uint32_t i = 0; i < n_tensors; i++) {
+            if (tensors[i].sha256) memcpy(recs[i].sha, tensors[i].sha256, 32);
+            else jobs.push_back({i, -1});
+            for (uint32_t ch = 0; ch < recs[i].n_chunks; ch++) jobs.push_back({i, (int32_t)ch});
+        }
+        const uint32_t threads = pick_threads(p->threads);
+        parallel_for(jobs.size(), threads, [&](uint64_t k) {
+            thread_local std::vector<uint16_t> buf;
+            const Job& jb = jobs[k];
+            EncRecord& r = recs[jb.rec];
+            if (jb.chunk < 0) {
+                sha256(r.data, r.kind == BS_KIND_BF16 ? 2 * r.n : r.n, r.sha);
+                return;
+            }
+            const uint64_t c0 = (uint64_t)jb.chunk * r.W;
+            const uint32_t n_c = (uint32_t)std::min<uint64_t>(r.W, r.n - c0);
+            if (buf.size() < 2ull * n_c) buf.resize(2ull * n_c);
+            ChunkOut& co = r.chunks[jb.chunk];
+            co.states.resize(r.K);
+            const uint64_t nw = encode_chunk(r.em, (const uint16_t*)r.data + c0, n_c, r.K, co.states.data(), buf.data());
+            co.words.resize(nw);
+            for (uint64_t i = 0; i < nw; i++) co.words[i] = buf[nw - 1 - i];
+        });
+        // layout
+        uint64_t pos = align_up(kHeaderBytes + kDirEntryBytes * n_tensors, 16);
+        std::vector<uint64_t> rec_off(n_tensors), rec_len(n_tensors), out_off(n_tensors);
+        uint64_t out_pos = 0, out_end = 0;
+        for (uint32_t i = 0; i < n_tensors; i++) {
+            EncRecord& r = recs[i];
+            rec_off[i] = pos;
+            uint64_t len = 0;
+            if (r.kind == BS_KIND_RAW) {
+                len = r.n;
+            } else {
+                len = r.head.size();
+                const uint64_t sb = align_up(4ull * r.K, 16);
+                for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
+                    wr64(r.head.data() + r.index_off + 16ull * ch, len);
+                    wr32(r.head.data() + r.index_off + 16ull * ch + 8, (uint32_t)r.chunks[ch].words.size());
+                    len += sb + align_up(2 * r.chunks[ch].words.size(), 16);
+                }
+            }
+            rec_len[i] = len;
+            pos = align_up(pos + len, 16);
+            out_off[i] = out_pos;
+            const uint64_t ob = r.kind == BS_KIND_BF16 ? 2 * r.n : r.n;
+            out_end = out_pos + ob;
+            out_pos = align_up(out_pos + ob, kOutAlign);
+        }
+        bs_blob* blob = new bs_blob();
+        blob->bytes.assign(pos, 0);
+        uint8_t* c = blob->bytes.data();
+        memcpy(c, kMagic, 8);
+        wr32(c + 8, kVersion);
+        wr32(c + 12, n_tensors);
+        wr64(c + 16, kHeaderBytes);
+        wr64(c + 24, pos);
+        wr64(c + 32, n_tensors ? out_end : 0);
+        for (uint32_t i = 0; i < n_tensors; i++) {
+            EncRecord& r = recs[i];
+            uint8_t* d = c + kHeaderBytes + kDirEntryBytes * i;
+            wr32(d, r.kind);
+            wr64(d + 8, r.n);
+            wr64(d + 16, out_off[i]);
+            wr64(d + 24, rec_off[i]);
+            wr64(d + 32, rec_len[i]);
+            memcpy(d + 40, r.sha, 32);
+            uint8_t* b = c + rec_off[i];
+            if (r.kind == BS_KIND_RAW) {
+                if (r.n) memcpy(b, r.data, r.n);
+                continue;
+            }
+            memcpy(b, r.head.data(), r.head.size());
+            const uint64_t sb = align_up(4ull * r.K, 16);
+            for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
+                const ChunkOut& co = r.chunks[ch];
+                uint8_t* pp = b + rd64(r.head.data() + r.index_off + 16ull * ch);
+                for (uint32_t l = 0; l < r.K; l++) wr32(pp + 4 * l, co.states[l]);
+                for (uint64_t k = 0; k < co.words.size(); k++) wr16(pp + sb + 2 * k, co.words[k]);
+            }
+        }
+        // the decoded extent ends with the last record (the last record may not be the largest offset)
+        uint64_t ext = 0;
+        for (uint32_t i = 0; i < n_tensors; i++)
+            ext = std::max(ext, out_off[i] + (recs[i].kind == BS_KIND_BF16 ? 2 * recs[i].n : recs[i].n));
+        wr64(c + 32, ext);
+        *out = blob;
+    } catch (const std::bad_alloc&) {
+        set_error("out of host memory");
+        return BS_E_NOMEM;
+    }
+    return BS_OK;
+}
+
+const void* bs_blob_data(const bs_blob* b) { return b ? b->bytes.data() : nullptr; }
+uint64_t bs_blob_size(const bs_blob* b) { return b ? b->bytes.size() : 0; }
+void bs_blob_free(bs_blob* b) { delete b; }
+
+bs_status bs_container_info_get(const void* h, uint64_t len, bs_container_info* info) {
+    if (!info) { set_error("NULL info"); return BS_E_INVAL; }
+    Container c;
+    bs_status rc = parse_container((const uint8_t*)h, len, c);
+    if (rc) return rc;
+    memset(info, 0, sizeof(*info));
+    info->version = kVersion;
+    info->n_records = c.n_records;
+    info->total_len = c.total_len;
+    info->out_len = c.out_len;
+    info->n_chunks = c.n_chunks;
+    // bytes charged to BF16 records: everything except the verbatim records
+    // and their directory entries (header and padding go to the BF16 side)
+    uint64_t raw = 0, n_raw = 0;
+    for (const Record& r : c.recs) {
+        if (r.kind == BS_KIND_BF16) info->bf16_weights += r.n;
+        else { raw += r.rec_len; n_raw++; }
+    }
+    info->raw_bytes = raw;
+    info->bf16_bytes = info->bf16_weights ? len - raw - kDirEntryBytes * n_raw : 0;
+    return BS_OK;
+}
+
+bs_status bs_record_info_get(const void* h, uint64_t len, uint32_t index, bs_record_info* info) {
+    if (!info) { set_error("NULL info"); return BS_E_INVAL; }
+    Container c;
+    bs_status rc = parse_container((const uint8_t*)h, len, c);
+    if (rc) return rc;
+    if (index >= c.n_records) { set_error("record %u out of range", index); return BS_E_INVAL; }
+    const Record& r = c.recs[index];
+    memset(info, 0, sizeof(*info));
+    info->kind = r.kind;
+    info->chunk_weights = r.W;
+    info->lanes = r.K;
+    info->n_chunks = r.n_chunks;
+    info->m_s = r.m_s;
+    info->m_f = r.m_f;
+    info->n_tables = r.n_tables;
+    info->n_sym = r.n_sym;
+    info->n = r.n;
+    info->out_offset = r.out_offset;
+    info->rec_offset = r.rec_offset;
+    info->rec_len = r.rec_len;
+    info->chunk_base = r.chunk_base;
+    memcpy(info->sha256, r.sha, 32);
+    return BS_OK;
+}
+
+void bs_sha256(const void* h, uint64_t n, uint8_t out[32]) { sha256(h, n, out); }
+
+bs_status bs_write_file_new(const char* path, const void* h, uint64_t n) {
+    if (!path || (!h && n)) { set_error("NULL argument"); return BS_E_INVAL; }
+    FILE* f = fopen(path, "wbx");   // 'x': fail if the file exists
+    if (!f) {
+        struct stat st;
+        if (stat(path, &st) == 0) { set_error("%s already exists", path); return BS_E_EXISTS; }
+        set_error("cannot create %s", path);
+        return BS_E_INVAL;
+    }
+    const size_t w = n ? fwrite(h, 1, n, f) : 0;
+    const int cl = fclose(f);
+    if (w != n || cl != 0) { set_error("short write to %s", path); return BS_E_INVAL; }
+    return BS_OK;
+}
+
+const char* bs_strerror(bs_status s) {
+    switch (s) {
+        case BS_OK: return "ok";
+        case BS_E_INVAL: return "invalid argument";
+        case BS_E_FORMAT: return "malformed container";
+        case BS_E_VERSION: return "unsupported container version";
+        case BS_E_NOSPACE: return "output buffer too small";
+        case BS_E_NOMEM: return "out of memory";
+        case BS_E_HIP: return "HIP runtime error";
+        case BS_E_CORRUPT: return "corrupt data";
+        case BS_E_MISMATCH: return "decoded bytes differ from the reference";
+        case BS_E_EXISTS: return "output already exists";
+    }
+    return "unknown status";
+}
+
+const char* bs_last_error(void) { return last_error(); }
+const char* bs_version(void) { return "bs 1.0 (container version 1, gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// bs_internal.h -- host-side internals of the codec library (not public).
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "bs.h"
+
+namespace bs {
+
+// container constants (the layout is documented in bs.h)
+constexpr char kMagic[8] = {'B', 'F', '1', '6', 'R', 'A', 'N', 'S'};
+constexpr uint32_t kVersion = 1;
+constexpr uint64_t kHeaderBytes = 64;
+constexpr uint64_t kDirEntryBytes = 96;
+constexpr uint64_t kOutAlign = 256;
+constexpr uint32_t kCandidates = 64;        // exponents whose fraction counts are gathered
+constexpr uint32_t kMaxTables = 6;
+constexpr uint32_t kMaxSyms = 256;
+
+void set_error(const char* fmt, ...);
+void sha256(const void* data, uint64_t n, uint8_t out[32]);
+
+inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+// little-endian field access
+inline uint32_t rd16(const uint8_t* p) { return (uint32_t)p[0] | (uint32_t)p[1] << 8; }
+inline uint32_t rd32(const uint8_t* p) { return rd16(p) | rd16(p + 2) << 16; }
+inline uint64_t rd64(const uint8_t* p) { return (uint64_t)rd32(p) | (uint64_t)rd32(p + 4) << 32; }
+inline void wr16(uint8_t* p, uint32_t v) { p[0] = (uint8_t)v; p[1] = (uint8_t)(v >> 8); }
+inline void wr32(uint8_t* p, uint32_t v) { wr16(p, v & 0xFFFF); wr16(p + 2, v >> 16); }
+inline void wr64(uint8_t* p, uint64_t v) { wr32(p, (uint32_t)v); wr32(p + 4, (uint32_t)(v >> 32)); }
+
+// Parsed view of one record (host side).
+struct Record {
+    uint32_t kind = 0;
+    uint64_t n = 0, out_offset = 0, rec_offset = 0, rec_len = 0;
+    uint8_t sha[32] = {0};
+    // BF16 records
+    uint32_t W = 0, K = 0, n_chunks = 0, m_s = 0, m_f = 0, n_tables = 0, n_sym = 0;
+    uint32_t stab_off = 0, route_off = 0, ftab_off = 0;
+    uint64_t index_off = 0;
+    uint64_t chunk_base = 0;
+    uint64_t out_bytes() const { return kind == BS_KIND_BF16 ? 2 * n : n; }
+};
+
+struct Container {
+    uint32_t n_records = 0;
+    uint64_t total_len = 0, out_len = 0, n_chunks = 0;
+    std::vector<Record> recs;
+};
+
+// Validate h (len bytes) completely (header, directory, tables, chunk index
+// and payload bounds) and fill c.  Returns BS_OK or an error with a message.
+bs_status parse_container(const uint8_t* h, uint64_t len, Container& c);
+
+}  // namespace bs

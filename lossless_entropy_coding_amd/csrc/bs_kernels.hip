@@ -1,0 +1,540 @@
+// bs_kernels.hip -- HIP kernels (gfx950) of the lossless BF16 weight codec.
+//
+// What is decoded [Qwen3.8-27B-BF16-NVLC-Lossless model card, codec
+// paragraph]: each BF16 word w = s << 7 | f, where the joint (sign, exponent)
+// symbol s is rANS-coded with a per-tensor model and the fraction f with the
+// distribution selected by s; non-BF16 spans are copied verbatim.
+//
+// Kernels:
+//   hist_s_kernel / hist_f_kernel  -- model building: field histograms with
+//                                     LDS-privatised counters
+//   lut_kernel                     -- per-record decode lookup tables
+//   decode_kernel                  -- one wavefront per chunk: lane states in
+//                                     VGPRs, lookup tables in LDS, a per-wave
+//                                     LDS ring of stream words filled with
+//                                     coalesced 16-B loads, refills addressed by
+//                                     a wavefront prefix count over the lanes
+//                                     that need a word, 128-bit output stores
+//   raw_copy_kernel                -- verbatim residual spans
+//   compare_kernel                 -- byte compare for verification
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bs_device.h"
+
+using namespace bsd;
+
+namespace {
+
+// ------------------------------------------------------------------ histograms
+
+constexpr int kHistThreads = 1024;
+
+// cs[s] for s = w >> 7 (9-bit sign/exponent symbol).  One 512-bin counter set
+// per wave in LDS (32 KiB) keeps hot-bin contention inside a wave.
+__global__ __launch_bounds__(kHistThreads) void hist_s_kernel(const uint16_t* __restrict__ w, uint64_t n,
+                                                               unsigned long long* __restrict__ cs) {
+    __shared__ uint32_t h[kHistThreads / 64][512];
+    uint32_t* hf = &h[0][0];
+    for (uint32_t i = threadIdx.x; i < (kHistThreads / 64) * 512; i += blockDim.x) hf[i] = 0;
+    __syncthreads();
+    uint32_t* hw = h[threadIdx.x >> 6];
+    // aligned body in 16-B pieces, head and tail word by word
+    const uint64_t addr = (uint64_t)(uintptr_t)w;
+    uint64_t head = ((16 - (addr & 15)) & 15) / 2;
+    if (head > n) head = n;
+    const uint64_t body = (n - head) / 8;
+    const uint4* p = (const uint4*)(w + head);
+    const uint64_t gtid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t gsz = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = gtid; i < body; i += gsz) {
+        uint4 v = p[i];
+        uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            atomicAdd(&hw[(d[k] & 0xFFFFu) >> 7], 1u);
+            atomicAdd(&hw[d[k] >> 23], 1u);
+        }
+    }
+    const uint64_t rest0 = head + body * 8;
+    for (uint64_t i = gtid; i < head + (n - rest0); i += gsz) {
+        uint64_t j = i < head ? i : rest0 + (i - head);
+        atomicAdd(&hw[w[j] >> 7], 1u);
+    }
+    __syncthreads();
+    for (uint32_t b = threadIdx.x; b < 512; b += blockDim.x) {
+        uint64_t s = 0;
+        for (int k = 0; k < kHistThreads / 64; k++) s += h[k][b];
+        if (s) atomicAdd(&cs[b], (unsigned long long)s);
+    }
+}
+
+// cf[c][f] for the candidate exponents: cand[e] = candidate index (0..63) of
+// exponent e (both signs), or -1.  One 64x128 counter set per workgroup.
+__global__ __launch_bounds__(kHistThreads) void hist_f_kernel(const uint16_t* __restrict__ w, uint64_t n,
+                                                               const int16_t* __restrict__ cand,
+                                                               unsigned long long* __restrict__ cf) {
+    __shared__ uint32_t h[64 * 128];
+    __shared__ int32_t cmap[256];
+    for (uint32_t i = threadIdx.x; i < 64 * 128; i += blockDim.x) h[i] = 0;
+    for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) cmap[i] = cand[i];
+    __syncthreads();
+    const uint64_t addr = (uint64_t)(uintptr_t)w;
+    uint64_t head = ((16 - (addr & 15)) & 15) / 2;
+    if (head > n) head = n;
+    const uint64_t body = (n - head) / 8;
+    const uint4* p = (const uint4*)(w + head);
+    const uint64_t gtid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t gsz = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = gtid; i < body; i += gsz) {
+        uint4 v = p[i];
+        uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            uint32_t x = (d[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+            int32_t c = cmap[(x >> 7) & 0xFF];
+            if (c >= 0) atomicAdd(&h[c * 128 + (x & 0x7F)], 1u);
+        }
+    }
+    const uint64_t rest0 = head + body * 8;
+    for (uint64_t i = gtid; i < head + (n - rest0); i += gsz) {
+        uint64_t j = i < head ? i : rest0 + (i - head);
+        uint32_t x = w[j];
+        int32_t c = cmap[(x >> 7) & 0xFF];
+        if (c >= 0) atomicAdd(&h[c * 128 + (x & 0x7F)], 1u);
+    }
+    __syncthreads();
+    for (uint32_t b = threadIdx.x; b < 64 * 128; b += blockDim.x) {
+        if (h[b]) atomicAdd(&cf[b], (unsigned long long)h[b]);
+    }
+}
+
+// ------------------------------------------------------------------ lookup tables
+
+__device__ __forceinline__ uint32_t ld16(const uint8_t* p) { return (uint32_t)p[0] | ((uint32_t)p[1] << 8); }
+
+// last index i in [0, A) with cum[i] <= v (cum non-decreasing, cum[0] = 0)
+__device__ __forceinline__ uint32_t last_le(const uint32_t* cum, uint32_t A, uint32_t v) {
+    uint32_t lo = 0, hi = A;  // answer in [lo, hi)
+    while (hi - lo > 1) {
+        uint32_t mid = (lo + hi) >> 1;
+        if (cum[mid] <= v) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// One workgroup per BF16 record: expand the container's compact tables into
+// the record's lookup-table image (layout in bs_device.h).
+__global__ __launch_bounds__(256) void lut_kernel(const uint8_t* __restrict__ c, const RecDev* __restrict__ recs,
+                                                  uint8_t* __restrict__ luts) {
+    __shared__ uint32_t qs[512], cums[512], route[512];
+    __shared__ uint32_t qf[kMaxTables + 1][128], cumf[kMaxTables + 1][128];
+    const RecDev r = recs[blockIdx.x];
+    const uint8_t* body = c + r.body;
+    for (uint32_t i = threadIdx.x; i < 512; i += blockDim.x) { qs[i] = 0; route[i] = 0; }
+    __syncthreads();
+    for (uint32_t k = threadIdx.x; k < r.n_sym; k += blockDim.x) {
+        uint32_t s = ld16(body + r.stab_off + 4 * k);
+        qs[s] = ld16(body + r.stab_off + 4 * k + 2);
+        route[s] = body[r.route_off + k];
+    }
+    const uint32_t nt = r.n_tables + 1;
+    for (uint32_t i = threadIdx.x; i < nt * 128; i += blockDim.x) {
+        uint32_t t = i / 128, f = i % 128;
+        qf[t][f] = t == 0 ? (1u << (r.m_f - 7)) : ld16(body + r.ftab_off + 256 * (t - 1) + 2 * f);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t a = 0;
+        for (int s = 0; s < 512; s++) { cums[s] = a; a += qs[s]; }
+    }
+    if (threadIdx.x >= 64 && threadIdx.x < 64 + nt) {
+        uint32_t t = threadIdx.x - 64, a = 0;
+        for (int f = 0; f < 128; f++) { cumf[t][f] = a; a += qf[t][f]; }
+    }
+    __syncthreads();
+    uint2* out = (uint2*)(luts + r.lut_off);
+    const uint32_t ns = 1u << r.m_s;
+    for (uint32_t slot = threadIdx.x; slot < ns; slot += blockDim.x) {
+        uint32_t s = last_le(cums, 512, slot);
+        uint32_t page = (kFlutOff + route[s] * kFPage) >> 11;
+        out[slot] = make_uint2(qs[s] | (page << 24), s | ((slot - cums[s]) << 20));
+    }
+    uint2* fo = (uint2*)(luts + r.lut_off + 8ull * ns);
+    const uint32_t nf = 1u << r.m_f;
+    for (uint32_t i = threadIdx.x; i < nt * nf; i += blockDim.x) {
+        uint32_t t = i / nf, slot = i % nf;
+        uint32_t f = last_le(cumf[t], 128, slot);
+        fo[t * (kFPage / 8) + slot] = make_uint2(qf[t][f] | (f << 25), slot - cumf[t][f]);
+    }
+}
+
+// ------------------------------------------------------------------ decode
+
+// Ring loads go through a buffer resource (gfx9 descriptor: raw 32-bit
+// elements, no stride) whose base is the current stream position and whose
+// size is what is left of the chunk's word area: the hardware range check
+// returns zeros past the chunk's end, so the read-ahead never touches memory
+// outside it.  The per-lane offset is a loop-invariant VGPR, so an in-flight
+// load never pins a register that the loop overwrites.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const uint8_t* words, uint32_t bytes, uint32_t from) {
+    // every input is wave-uniform; readfirstlane keeps the descriptor in SGPRs
+    const uint64_t a = (uint64_t)(uintptr_t)(words + from);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t left = __builtin_amdgcn_readfirstlane(bytes > from ? bytes - from : 0u);
+    const uint8_t* base = (const uint8_t*)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)left, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 load_piece(__amdgpu_buffer_rsrc_t rs, uint32_t lane_off) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane_off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Per-wave ring of stream words in LDS.  Words are refilled 1024 at a time
+// (two 16-B pieces per lane, loaded one refill ahead into pa/pb); the ring
+// holds 2048 words plus a 64-word copy of its head after its end, so that a
+// refill of up to 64 consecutive words never wraps.
+struct Ring {
+    uint16_t* base;       // LDS ring of this wave (kRingWords + kRingMirror words)
+    uint4 pa, pb;         // the next 1024 words, in flight
+    uint32_t fill;        // stream words written into the ring so far
+    const uint8_t* words; // the chunk's word area (uniform)
+    uint32_t bytes;       // its size, a multiple of 16
+    uint32_t off_a, off_b;  // per-lane byte offsets of the two prefetched pieces
+};
+
+__device__ __forceinline__ void ring_init(Ring& g, uint32_t lane) {
+    uint4* r4 = (uint4*)g.base;
+    g.off_a = 16 * (128 + lane);
+    g.off_b = 16 * (192 + lane);
+    const __amdgpu_buffer_rsrc_t rs = stream_rsrc(g.words, g.bytes, 0);
+    const uint4 b0 = load_piece(rs, 16 * lane);
+    const uint4 b1 = load_piece(rs, 16 * (64 + lane));
+    g.pa = load_piece(rs, g.off_a);
+    g.pb = load_piece(rs, g.off_b);
+    r4[lane] = b0;
+    r4[64 + lane] = b1;
+    if (lane < kRingMirror / 8) r4[kRingWords / 8 + lane] = b0;
+    g.fill = 2 * kBlockWords;
+}
+
+// keep at least 1024 words ahead of `pos` in the ring (uniform branch)
+__device__ __forceinline__ void ring_top_up(Ring& g, uint32_t pos, uint32_t lane) {
+    if (g.fill - pos < 2 * kBlockWords) {
+        uint4* r4 = (uint4*)g.base;
+        const uint32_t ro = (g.fill & (kRingWords - 1)) >> 3;
+        r4[ro + lane] = g.pa;
+        r4[ro + 64 + lane] = g.pb;
+        if (ro == 0 && lane < kRingMirror / 8) r4[kRingWords / 8 + lane] = g.pa;
+        const __amdgpu_buffer_rsrc_t rs = stream_rsrc(g.words, g.bytes, 2 * g.fill);
+        g.pa = load_piece(rs, g.off_a);
+        g.pb = load_piece(rs, g.off_b);
+        g.fill += 2 * kBlockWords;
+    }
+}
+
+// renormalise one group of 64 lanes: lanes whose state fell below 2^16 take
+// the next stream words, in lane order
+__device__ __forceinline__ void refill(uint32_t& x, bool active, const Ring& g, uint32_t& pos) {
+    const bool need = active && x < kStateLow;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(need);
+    const uint32_t pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const uint16_t* rp = g.base + (pos & (kRingWords - 1));
+    if (need) x = (x << 16) | (uint32_t)rp[pre];
+    pos += (uint32_t)__builtin_popcountll(m);
+}
+
+struct Model {
+    const uint8_t* lds;
+    uint32_t m_s, m_f;
+    uint32_t smask8;      // (2^m_s - 1) << 3
+    uint32_t fmask8;      // (2^m_f - 1) << 3
+};
+
+// decode the s symbol of one weight for one lane; returns the s-entry
+__device__ __forceinline__ uint2 step_s(uint32_t& x, const Model& md) {
+    const uint2 e = *(const uint2*)(md.lds + ((x << 3) & md.smask8));
+    x = __umul24(x >> md.m_s, e.x) + (e.y >> 20);
+    return e;
+}
+
+// decode the fraction with the table the s-entry routes to; returns w (low 16 bits)
+__device__ __forceinline__ uint32_t step_f(uint32_t& x, const uint2 se, const Model& md) {
+    // the s-entry's top byte is the fraction table's LDS address >> 11, and
+    // its low 24 bits hold q_s <= 4096, so se.x >> 13 is that address exactly
+    const uint32_t addr = ((x << 3) & md.fmask8) | (se.x >> 13);
+    const uint2 e = *(const uint2*)(md.lds + addr);
+    x = __umul24(x >> md.m_f, e.x) + e.y;
+    return __builtin_amdgcn_alignbit(se.y, e.x, 25);
+}
+
+template <int R>
+__device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, uint32_t wave, uint8_t* lds) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint8_t* body = a.container + r.body;
+    const uint8_t* ent = body + r.index_off + 16ull * ch;
+    const uint64_t poff = *(const uint64_t*)ent;
+    const uint32_t nw = *(const uint32_t*)(ent + 8);
+    const uint8_t* payload = body + poff;
+    const uint32_t K = r.K;
+    const uint64_t n_left = r.n - (uint64_t)ch * r.W;
+    const uint32_t n_c = (uint32_t)(n_left < r.W ? n_left : r.W);
+
+    // lane states first, then the ring: both are complete before the loop so
+    // that no load issued here is still pending when the loop first runs
+    uint32_t x[R];
+    const uint32_t* st = (const uint32_t*)payload;
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        const uint32_t l = 64 * q + lane;
+        x[q] = l < K ? st[l] : kStateLow;
+    }
+    Ring g;
+    g.base = (uint16_t*)(lds + kLutLds + wave * kRingBytes);
+    g.words = payload + ((4 * K + 15) & ~15u);
+    g.bytes = (2 * nw + 15) & ~15u;
+    ring_init(g, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+
+    const Model md{lds, r.m_s, r.m_f, ((1u << r.m_s) - 1) << 3, ((1u << r.m_f) - 1) << 3};
+
+    uint32_t pos = 0;
+    uint8_t* out = a.out + (r.out_off - a.out_base) + 2ull * ch * r.W;
+
+    const uint32_t groups = (n_c + 7) / 8;
+    const uint32_t T = (groups + K - 1) / K;
+    const uint32_t T_full = (K % 64 == 0) ? n_c / (8 * K) : 0;
+
+    // full macro-steps: every lane decodes 8 weights, one 128-bit store per lane group
+    for (uint32_t t = 0; t < T_full; t++) {
+        uint32_t o[R][4];
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            ring_top_up(g, pos, lane);
+            uint2 se[R];
+#pragma unroll
+            for (int q = 0; q < R; q++) se[q] = step_s(x[q], md);
+#pragma unroll
+            for (int q = 0; q < R; q++) refill(x[q], true, g, pos);
+            uint32_t wv[R];
+#pragma unroll
+            for (int q = 0; q < R; q++) wv[q] = step_f(x[q], se[q], md);
+#pragma unroll
+            for (int q = 0; q < R; q++) refill(x[q], true, g, pos);
+#pragma unroll
+            for (int q = 0; q < R; q++) {
+                if (p & 1) o[q][p >> 1] = __builtin_amdgcn_perm(wv[q], o[q][p >> 1], 0x05040100u);
+                else o[q][p >> 1] = wv[q];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < R; q++) {
+            uint4* op = (uint4*)out + (uint64_t)t * K + 64 * q + lane;
+            *op = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
+        }
+    }
+
+    // remaining macro-steps (partial groups, or fewer than 64 lanes): lanes
+    // take part while they still have weights
+    for (uint32_t t = T_full; t < T; t++) {
+        int32_t cnt[R];
+        uint32_t o[R][4];
+#pragma unroll
+        for (int q = 0; q < R; q++) {
+            const uint32_t l = 64 * q + lane;
+            const int64_t left = (int64_t)n_c - 8 * ((int64_t)t * K + l);
+            cnt[q] = l < K ? (int32_t)(left < 0 ? 0 : (left > 8 ? 8 : left)) : 0;
+#pragma unroll
+            for (int k = 0; k < 4; k++) o[q][k] = 0;
+        }
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            ring_top_up(g, pos, lane);
+            uint2 se[R];
+#pragma unroll
+            for (int q = 0; q < R; q++) {
+                uint32_t xs = x[q];
+                se[q] = step_s(xs, md);
+                if (p < cnt[q]) x[q] = xs;
+            }
+#pragma unroll
+            for (int q = 0; q < R; q++) refill(x[q], p < cnt[q], g, pos);
+            uint32_t wv[R];
+#pragma unroll
+            for (int q = 0; q < R; q++) {
+                uint32_t xs = x[q];
+                wv[q] = step_f(xs, se[q], md);
+                if (p < cnt[q]) x[q] = xs;
+            }
+#pragma unroll
+            for (int q = 0; q < R; q++) refill(x[q], p < cnt[q], g, pos);
+#pragma unroll
+            for (int q = 0; q < R; q++) {
+                if (p & 1) o[q][p >> 1] = __builtin_amdgcn_perm(wv[q], o[q][p >> 1], 0x05040100u);
+                else o[q][p >> 1] = wv[q];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < R; q++) {
+            const uint64_t g16 = (uint64_t)t * K + 64 * q + lane;
+            if (cnt[q] == 8) {
+                ((uint4*)out)[g16] = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
+            } else if (cnt[q] > 0) {
+                uint16_t* o16 = (uint16_t*)out + 8 * g16;
+#pragma unroll
+                for (int k = 0; k < 8; k++)
+                    if (k < cnt[q]) o16[k] = (uint16_t)(o[q][k >> 1] >> (16 * (k & 1)));
+            }
+        }
+    }
+
+    // a chunk is whole when every lane is back at the encoder's initial state
+    // and exactly the chunk's words were consumed
+    bool bad = false;
+#pragma unroll
+    for (int q = 0; q < R; q++) bad |= x[q] != kStateLow;
+    const uint64_t badm = __builtin_amdgcn_ballot_w64(bad);
+    if (lane == 0) a.status[r.chunk_base + ch] = (badm ? 1u : 0u) | (pos != nw ? 2u : 0u);
+}
+
+// Workgroups of up to 16 waves share one copy of the record's lookup tables;
+// the 4-lanes-per-thread variant keeps 8 waves so that it has 256 VGPRs.
+template <int R>
+__global__ __launch_bounds__(R == 4 ? 512 : 1024) void decode_kernel(const DecodeArgs a) {
+    // static allocation: the LDS base is a compile-time constant, so table and
+    // ring addresses fold into the instructions' offsets
+    __shared__ __align__(16) uint8_t lds[kLutLds + (R == 4 ? kMaxWavesR4 : kMaxWaves) * kRingBytes];
+    const TaskDev tk = a.tasks[a.task_begin + blockIdx.x];
+    const RecDev r = a.recs[tk.rec];
+    // stage the record's lookup tables into LDS
+    {
+        const uint4* src = (const uint4*)(a.luts + r.lut_off);
+        const uint32_t ns16 = (8u << r.m_s) / 16;
+        uint4* d = (uint4*)(lds + kSlutOff);
+        for (uint32_t i = threadIdx.x; i < ns16; i += blockDim.x) d[i] = src[i];
+        const uint32_t nf16 = (r.n_tables + 1) * (kFPage / 16);
+        const uint4* fs = src + ns16;
+        uint4* fd = (uint4*)(lds + kFlutOff);
+        for (uint32_t i = threadIdx.x; i < nf16; i += blockDim.x) fd[i] = fs[i];
+    }
+    __syncthreads();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave >= tk.nc) return;
+    decode_chunk<R>(a, r, tk.c0 + wave, wave, lds);
+}
+
+// ------------------------------------------------------------------ residual and compare
+
+__global__ __launch_bounds__(256) void raw_copy_kernel(const uint8_t* __restrict__ c, const RawDev* __restrict__ raw,
+                                                       uint8_t* __restrict__ out, uint64_t out_base) {
+    const RawDev rd = raw[blockIdx.y];
+    const uint8_t* s = c + rd.src;
+    uint8_t* d = out + (rd.dst - out_base);
+    const uint64_t gtid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t gsz = (uint64_t)gridDim.x * blockDim.x;
+    if ((((uintptr_t)s | (uintptr_t)d) & 15) == 0) {
+        const uint64_t n16 = rd.n / 16;
+        for (uint64_t i = gtid; i < n16; i += gsz) ((uint4*)d)[i] = ((const uint4*)s)[i];
+        for (uint64_t i = n16 * 16 + gtid; i < rd.n; i += gsz) d[i] = s[i];
+    } else {
+        for (uint64_t i = gtid; i < rd.n; i += gsz) d[i] = s[i];
+    }
+}
+
+__global__ __launch_bounds__(256) void compare_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
+                                                      uint64_t n, unsigned long long* __restrict__ res) {
+    const uint64_t gtid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t gsz = (uint64_t)gridDim.x * blockDim.x;
+    unsigned long long bad = 0, first = ~0ull;
+    if ((((uintptr_t)a | (uintptr_t)b) & 15) == 0) {
+        const uint64_t n16 = n / 16;
+        for (uint64_t i = gtid; i < n16; i += gsz) {
+            uint4 u = ((const uint4*)a)[i], v = ((const uint4*)b)[i];
+            uint32_t du[4] = {u.x ^ v.x, u.y ^ v.y, u.z ^ v.z, u.w ^ v.w};
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                for (int j = 0; j < 4; j++) {
+                    if ((du[k] >> (8 * j)) & 0xFF) {
+                        bad++;
+                        unsigned long long idx = 16 * i + 4 * k + j;
+                        if (idx < first) first = idx;
+                    }
+                }
+            }
+        }
+        for (uint64_t i = n16 * 16 + gtid; i < n; i += gsz)
+            if (a[i] != b[i]) { bad++; if (i < first) first = i; }
+    } else {
+        for (uint64_t i = gtid; i < n; i += gsz)
+            if (a[i] != b[i]) { bad++; if (i < first) first = i; }
+    }
+    if (bad) {
+        atomicAdd(&res[0], bad);
+        atomicMin(&res[1], first);
+    }
+}
+
+inline int grid_for(uint64_t work, uint64_t per_block, int cap) {
+    uint64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > (uint64_t)cap) g = cap;
+    return (int)g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsk_device_cus(int* cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    return (int)hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+}
+
+int bsk_hist_s(const uint16_t* d_w, uint64_t n, unsigned long long* d_cs, void* stream) {
+    int g = grid_for(n, (uint64_t)kHistThreads * 32, 1024);
+    hipLaunchKernelGGL(hist_s_kernel, dim3(g), dim3(kHistThreads), 0, (hipStream_t)stream, d_w, n, d_cs);
+    return (int)hipGetLastError();
+}
+
+int bsk_hist_f(const uint16_t* d_w, uint64_t n, const int16_t* d_cand, unsigned long long* d_cf, void* stream) {
+    int g = grid_for(n, (uint64_t)kHistThreads * 32, 1024);
+    hipLaunchKernelGGL(hist_f_kernel, dim3(g), dim3(kHistThreads), 0, (hipStream_t)stream, d_w, n, d_cand, d_cf);
+    return (int)hipGetLastError();
+}
+
+int bsk_build_luts(const uint8_t* d_container, const RecDev* d_recs, uint32_t n_recs, uint8_t* d_luts, void* stream) {
+    if (n_recs == 0) return 0;
+    hipLaunchKernelGGL(lut_kernel, dim3(n_recs), dim3(256), 0, (hipStream_t)stream, d_container, d_recs, d_luts);
+    return (int)hipGetLastError();
+}
+
+int bsk_decode(const DecodeArgs* args, uint32_t n_tasks, uint32_t lanes_per_thread, void* stream) {
+    if (n_tasks == 0) return 0;
+    const dim3 grid(n_tasks), block(64 * args->waves);
+    hipStream_t st = (hipStream_t)stream;
+    if (lanes_per_thread == 1) hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, st, *args);
+    else if (lanes_per_thread == 2) hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, st, *args);
+    else hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, st, *args);
+    return (int)hipGetLastError();
+}
+
+int bsk_raw_copy(const uint8_t* d_container, const RawDev* d_raw, uint32_t n_raw, uint8_t* d_out, uint64_t out_base,
+                 void* stream) {
+    if (n_raw == 0) return 0;
+    hipLaunchKernelGGL(raw_copy_kernel, dim3(64, n_raw), dim3(256), 0, (hipStream_t)stream, d_container, d_raw, d_out,
+                       out_base);
+    return (int)hipGetLastError();
+}
+
+int bsk_compare(const uint8_t* a, const uint8_t* b, uint64_t n, unsigned long long* d_result, void* stream) {
+    int g = grid_for(n, 256ull * 64, 4096);
+    hipLaunchKernelGGL(compare_kernel, dim3(g), dim3(256), 0, (hipStream_t)stream, a, b, n, d_result);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -1,0 +1,328 @@
+// bs_plan.cpp -- decode plans, the decode entry point and verification.
+//
+// A plan holds, in device memory, the validated work list of a container
+// (one entry per workgroup: a record and up to `waves` of its chunks, one
+// chunk per wave) and each record's decode lookup tables, built once by a HIP
+// kernel.  Decoding a record range is then one kernel launch for the BF16
+// records plus one for the verbatim residual spans [Qwen3.8-27B-BF16-NVLC-
+// Lossless card, codec paragraph: the residual keeps non-BF16 spans].
+// Verification re-reads the per-chunk status, compares bytes on the device and
+// checks each record's sha256 [Gemma 2 9B Instruct -- Lossless Compressed
+// card, "What lossless means": every tensor is hash-checked at decompression].
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "bs_device.h"
+#include "bs_internal.h"
+#include "bs_model.h"
+
+using namespace bs;
+
+struct bs_plan {
+    int device = 0;
+    const uint8_t* d_container = nullptr;
+    uint64_t len = 0;
+    Container c;
+    // one work list per lanes-per-thread class (1, 2, 4): each class is its
+    // own kernel instantiation with its own workgroup size
+    static constexpr int kClasses = 3;
+    uint32_t waves[kClasses] = {1, 1, 1};
+    std::vector<uint32_t> dev_index;   // record -> index in d_recs (BF16) or d_raws (RAW)
+    std::vector<uint32_t> rclass;      // record -> class (BF16)
+    std::vector<uint32_t> task_first, task_count;   // within the record's class list
+    std::vector<bsd::TaskDev> tasks[kClasses];
+    std::vector<bsd::RawDev> raws;
+    bsd::RecDev* d_recs = nullptr;
+    bsd::TaskDev* d_tasks[kClasses] = {nullptr, nullptr, nullptr};
+    bsd::RawDev* d_raws = nullptr;
+    uint8_t* d_luts = nullptr;
+    unsigned long long* d_cmp = nullptr;   // compare results (2 words)
+};
+
+namespace {
+
+void plan_free(bs_plan* p) {
+    if (!p) return;
+    if (p->d_recs) (void)hipFree(p->d_recs);
+    for (auto* t : p->d_tasks)
+        if (t) (void)hipFree(t);
+    if (p->d_raws) (void)hipFree(p->d_raws);
+    if (p->d_luts) (void)hipFree(p->d_luts);
+    if (p->d_cmp) (void)hipFree(p->d_cmp);
+    delete p;
+}
+
+bs_status hip_err(hipError_t e, const char* what) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return BS_E_HIP;
+}
+
+// records [first, first+count) -> contiguous task range of each class and the raw range
+void ranges(const bs_plan* p, uint32_t first, uint32_t count, uint32_t* t0, uint32_t* t1, uint32_t& r0,
+            uint32_t& r1) {
+    r0 = r1 = 0;
+    bool have_t[bs_plan::kClasses] = {false, false, false}, have_r = false;
+    for (int k = 0; k < bs_plan::kClasses; k++) t0[k] = t1[k] = 0;
+    for (uint32_t i = first; i < first + count; i++) {
+        const Record& r = p->c.recs[i];
+        if (r.kind == BS_KIND_BF16) {
+            if (!p->task_count[i]) continue;
+            const uint32_t k = p->rclass[i];
+            if (!have_t[k]) { t0[k] = p->task_first[i]; have_t[k] = true; }
+            t1[k] = p->task_first[i] + p->task_count[i];
+        } else {
+            if (!have_r) { r0 = p->dev_index[i]; have_r = true; }
+            r1 = p->dev_index[i] + 1;
+        }
+    }
+}
+
+uint64_t out_extent(const bs_plan* p, uint32_t first, uint32_t count) {
+    if (!count) return 0;
+    const uint64_t base = p->c.recs[first].out_offset;
+    uint64_t e = 0;
+    for (uint32_t i = first; i < first + count; i++) {
+        const Record& r = p->c.recs[i];
+        if (r.out_offset < base) return UINT64_MAX;   // records must ascend in output offset
+        e = std::max(e, r.out_offset + r.out_bytes() - base);
+    }
+    return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_container, void* stream,
+                         bs_plan** out) {
+    if (!out || !h_container || !d_container) { set_error("NULL argument"); return BS_E_INVAL; }
+    if ((uintptr_t)d_container & 15) { set_error("device container must be 16-byte aligned"); return BS_E_INVAL; }
+    bs_plan* p = new (std::nothrow) bs_plan();
+    if (!p) return BS_E_NOMEM;
+    bs_status rc = parse_container((const uint8_t*)h_container, len, p->c);
+    if (rc) { delete p; return rc; }
+    p->d_container = (const uint8_t*)d_container;
+    p->len = len;
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) { plan_free(p); return hip_err(e, "hipGetDevice"); }
+    int cus = 0;
+    if (bsk_device_cus(&cus) != 0 || cus <= 0) cus = 256;
+    const uint32_t n = p->c.n_records;
+    // chunks per class decide the workgroup size: enough workgroups to cover
+    // the CUs, at most 16 waves (8 for four lanes per thread)
+    uint64_t class_chunks[bs_plan::kClasses] = {0, 0, 0};
+    p->rclass.assign(n, 0);
+    for (uint32_t i = 0; i < n; i++) {
+        const Record& r = p->c.recs[i];
+        if (r.kind != BS_KIND_BF16) continue;
+        const uint32_t R = r.K <= 64 ? 1 : r.K / 64;
+        p->rclass[i] = R == 1 ? 0 : R == 2 ? 1 : 2;
+        class_chunks[p->rclass[i]] += r.n_chunks;
+    }
+    for (int k = 0; k < bs_plan::kClasses; k++) {
+        const uint64_t cap = k == 2 ? bsd::kMaxWavesR4 : bsd::kMaxWaves;
+        p->waves[k] = (uint32_t)std::min<uint64_t>(cap, std::max<uint64_t>(1, (class_chunks[k] + cus - 1) / cus));
+    }
+
+    std::vector<bsd::RecDev> recs;
+    uint64_t lut_bytes = 0;
+    p->dev_index.assign(n, 0);
+    p->task_first.assign(n, 0);
+    p->task_count.assign(n, 0);
+    for (uint32_t i = 0; i < n; i++) {
+        const Record& r = p->c.recs[i];
+        if (r.kind == BS_KIND_RAW) {
+            p->dev_index[i] = (uint32_t)p->raws.size();
+            p->raws.push_back({r.rec_offset, r.out_offset, r.n});
+            continue;
+        }
+        p->dev_index[i] = (uint32_t)recs.size();
+        bsd::RecDev d{};
+        d.body = r.rec_offset;
+        d.index_off = r.index_off;
+        d.out_off = r.out_offset;
+        d.n = r.n;
+        d.lut_off = lut_bytes;
+        d.W = r.W;
+        d.K = r.K;
+        d.n_chunks = r.n_chunks;
+        d.chunk_base = (uint32_t)r.chunk_base;
+        d.m_s = r.m_s;
+        d.m_f = r.m_f;
+        d.n_tables = r.n_tables;
+        d.lanes_per_thread = r.K <= 64 ? 1 : r.K / 64;
+        d.n_sym = r.n_sym;
+        d.stab_off = r.stab_off;
+        d.route_off = r.route_off;
+        d.ftab_off = r.ftab_off;
+        lut_bytes += (8ull << r.m_s) + (r.n_tables + 1ull) * bsd::kFPage;
+        const uint32_t k = p->rclass[i];
+        std::vector<bsd::TaskDev>& tl = p->tasks[k];
+        p->task_first[i] = (uint32_t)tl.size();
+        for (uint32_t c0 = 0; c0 < r.n_chunks; c0 += p->waves[k])
+            tl.push_back({(uint32_t)recs.size(), c0, std::min(p->waves[k], r.n_chunks - c0), 0});
+        p->task_count[i] = (uint32_t)tl.size() - p->task_first[i];
+        recs.push_back(d);
+    }
+    if (p->c.n_chunks > 0xFFFFFFFFull) { plan_free(p); set_error("too many chunks"); return BS_E_FORMAT; }
+    hipStream_t s = (hipStream_t)stream;
+    auto up = [&](void** dst, const void* src, size_t bytes) -> hipError_t {
+        hipError_t ee = hipMalloc(dst, std::max<size_t>(bytes, 16));
+        if (ee != hipSuccess || !bytes) return ee;
+        return hipMemcpyAsync(*dst, src, bytes, hipMemcpyHostToDevice, s);
+    };
+    e = up((void**)&p->d_recs, recs.data(), recs.size() * sizeof(bsd::RecDev));
+    for (int k = 0; k < bs_plan::kClasses && e == hipSuccess; k++)
+        e = up((void**)&p->d_tasks[k], p->tasks[k].data(), p->tasks[k].size() * sizeof(bsd::TaskDev));
+    if (e == hipSuccess) e = up((void**)&p->d_raws, p->raws.data(), p->raws.size() * sizeof(bsd::RawDev));
+    if (e == hipSuccess) e = hipMalloc(&p->d_luts, std::max<uint64_t>(lut_bytes, 16));
+    if (e == hipSuccess) e = hipMalloc(&p->d_cmp, 2 * sizeof(unsigned long long));
+    if (e == hipSuccess) e = (hipError_t)bsk_build_luts(p->d_container, p->d_recs, (uint32_t)recs.size(), p->d_luts, stream);
+    // the host vectors passed to the copies above must outlive them
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        rc = hip_err(e, "plan upload");
+        plan_free(p);
+        return rc;
+    }
+    *out = p;
+    return BS_OK;
+}
+
+void bs_plan_destroy(bs_plan* plan) { plan_free(plan); }
+
+uint32_t bs_plan_waves_per_block(const bs_plan* plan) {
+    if (!plan) return 0;
+    uint32_t w = 0;
+    for (int k = 0; k < bs_plan::kClasses; k++)
+        if (!plan->tasks[k].empty()) w = std::max(w, plan->waves[k]);
+    return w;
+}
+
+uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count) {
+    if (!plan || first > plan->c.n_records || count > plan->c.n_records - first) return 0;
+    return out_extent(plan, first, count);
+}
+
+bs_status bs_decode_async(const bs_plan* p, uint32_t first, uint32_t count, void* d_out, uint64_t out_capacity,
+                          uint32_t* d_status, void* stream) {
+    if (!p || (!d_out && count) || (!d_status && p->c.n_chunks)) { set_error("NULL argument"); return BS_E_INVAL; }
+    if (first > p->c.n_records || count > p->c.n_records - first) { set_error("record range out of bounds"); return BS_E_INVAL; }
+    if ((uintptr_t)d_out & 15) { set_error("output must be 16-byte aligned"); return BS_E_INVAL; }
+    if (!count) return BS_OK;
+    const uint64_t need = out_extent(p, first, count);
+    if (need == UINT64_MAX) { set_error("records of the range do not ascend in output offset"); return BS_E_INVAL; }
+    if (need > out_capacity) {
+        set_error("output needs %llu bytes, capacity is %llu", (unsigned long long)need, (unsigned long long)out_capacity);
+        return BS_E_NOSPACE;
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != p->device) { set_error("plan belongs to device %d", p->device); return BS_E_INVAL; }
+    uint32_t t0[bs_plan::kClasses], t1[bs_plan::kClasses], r0, r1;
+    ranges(p, first, count, t0, t1, r0, r1);
+    const uint64_t out_base = p->c.recs[first].out_offset;
+    for (int k = 0; k < bs_plan::kClasses; k++) {
+        if (t1[k] <= t0[k]) continue;
+        bsd::DecodeArgs a{};
+        a.container = p->d_container;
+        a.recs = p->d_recs;
+        a.tasks = p->d_tasks[k];
+        a.luts = p->d_luts;
+        a.out = (uint8_t*)d_out;
+        a.status = d_status;
+        a.out_base = out_base;
+        a.task_begin = t0[k];
+        a.waves = p->waves[k];
+        int e = bsk_decode(&a, t1[k] - t0[k], k == 0 ? 1 : k == 1 ? 2 : 4, stream);
+        if (e) return hip_err((hipError_t)e, "decode launch");
+    }
+    if (r1 > r0) {
+        int e = bsk_raw_copy(p->d_container, p->d_raws + r0, r1 - r0, (uint8_t*)d_out, out_base, stream);
+        if (e) return hip_err((hipError_t)e, "residual copy launch");
+    }
+    return BS_OK;
+}
+
+bs_status bs_verify(const bs_plan* p, uint32_t first, uint32_t count, const void* d_out, const void* d_ref,
+                    const uint32_t* d_status, uint32_t flags, void* stream, bs_report* rep) {
+    if (!p || !rep) { set_error("NULL argument"); return BS_E_INVAL; }
+    if (first > p->c.n_records || count > p->c.n_records - first) { set_error("record range out of bounds"); return BS_E_INVAL; }
+    memset(rep, 0, sizeof(*rep));
+    rep->first_bad_chunk = UINT64_MAX;
+    rep->first_mismatch = UINT64_MAX;
+    rep->first_hash_bad = UINT32_MAX;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_err(e, "stream");
+    const uint64_t base = count ? p->c.recs[first].out_offset : 0;
+    bool corrupt = false, mismatch = false;
+    if ((flags & BS_VERIFY_STATUS) && count) {
+        if (!d_status && p->c.n_chunks) { set_error("NULL status"); return BS_E_INVAL; }
+        for (uint32_t i = first; i < first + count; i++) {
+            const Record& r = p->c.recs[i];
+            if (r.kind != BS_KIND_BF16 || !r.n_chunks) continue;
+            std::vector<uint32_t> st(r.n_chunks);
+            e = hipMemcpy(st.data(), d_status + r.chunk_base, 4ull * r.n_chunks, hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return hip_err(e, "status read-back");
+            for (uint32_t k = 0; k < r.n_chunks; k++) {
+                rep->chunks_checked++;
+                if (st[k]) {
+                    rep->chunks_bad++;
+                    rep->first_bad_chunk = std::min<uint64_t>(rep->first_bad_chunk, r.chunk_base + k);
+                    corrupt = true;
+                }
+            }
+        }
+    }
+    if ((flags & BS_VERIFY_COMPARE) && count) {
+        if (!d_out || !d_ref) { set_error("compare needs d_out and d_ref"); return BS_E_INVAL; }
+        for (uint32_t i = first; i < first + count; i++) {
+            const Record& r = p->c.recs[i];
+            const uint64_t off = r.out_offset - base, nb = r.out_bytes();
+            if (!nb) continue;
+            unsigned long long res[2] = {0, ~0ull};
+            e = hipMemcpyAsync(p->d_cmp, res, sizeof(res), hipMemcpyHostToDevice, s);
+            if (e == hipSuccess)
+                e = (hipError_t)bsk_compare((const uint8_t*)d_out + off, (const uint8_t*)d_ref + off, nb, p->d_cmp, stream);
+            if (e == hipSuccess) e = hipMemcpyAsync(res, p->d_cmp, sizeof(res), hipMemcpyDeviceToHost, s);
+            if (e == hipSuccess) e = hipStreamSynchronize(s);
+            if (e != hipSuccess) return hip_err(e, "compare");
+            rep->bytes_compared += nb;
+            if (res[0]) {
+                mismatch = true;
+                rep->bytes_mismatched += res[0];
+                rep->first_mismatch = std::min<uint64_t>(rep->first_mismatch, off + res[1]);
+            }
+        }
+    }
+    if ((flags & BS_VERIFY_SHA256) && count) {
+        if (!d_out) { set_error("sha256 check needs d_out"); return BS_E_INVAL; }
+        std::vector<uint8_t> host;
+        for (uint32_t i = first; i < first + count; i++) {
+            const Record& r = p->c.recs[i];
+            const uint64_t nb = r.out_bytes();
+            try { host.resize(nb); } catch (const std::bad_alloc&) { set_error("out of host memory"); return BS_E_NOMEM; }
+            if (nb) {
+                e = hipMemcpy(host.data(), (const uint8_t*)d_out + (r.out_offset - base), nb, hipMemcpyDeviceToHost);
+                if (e != hipSuccess) return hip_err(e, "read-back");
+            }
+            uint8_t dg[32];
+            sha256(host.data(), nb, dg);
+            rep->records_hashed++;
+            if (memcmp(dg, r.sha, 32) != 0) {
+                rep->records_hash_bad++;
+                rep->first_hash_bad = std::min(rep->first_hash_bad, i);
+                mismatch = true;
+            }
+        }
+    }
+    if (corrupt) return BS_E_CORRUPT;
+    if (mismatch) return BS_E_MISMATCH;
+    return BS_OK;
+}
+
+}  // extern "C"

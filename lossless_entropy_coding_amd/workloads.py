@@ -1,0 +1,127 @@
+"""Encode the synthetic workloads into containers (used by the benchmark, the
+smoke check and the tests).
+
+Models are built by the HIP histogram kernels when the data is on a GPU, else
+on the host; the container is written by the library's host encoder.  The
+empirical conditional entropy H(S) + H(F|S) that the bits/weight target is
+stated against equals the entropy of the 16-bit word histogram (the word and
+the pair (S, F) determine each other); it is computed here with torch for
+reporting only.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from . import codec, synth
+
+
+def word_entropy_bits(words: torch.Tensor) -> float:
+    """Plug-in entropy (bits/word) of a 16-bit word tensor (any device)."""
+    w = words.reshape(-1).to(torch.int32) & 0xFFFF
+    if w.numel() == 0:
+        return 0.0
+    h = torch.bincount(w, minlength=65536).to(torch.float64)
+    p = h[h > 0] / w.numel()
+    return float(-(p * torch.log2(p)).sum())
+
+
+@dataclass
+class Encoded:
+    name: str
+    container: bytes
+    n_weights: int
+    raw_bytes: int
+    entropy_bits: float              # weighted over BF16 tensors
+    bits_per_weight: float           # container bytes charged to BF16 records, per weight
+    params: dict
+    reference: bytes | None = None   # expected output bytes (host), gaps zero
+    reference_device: torch.Tensor | None = None
+    tensors_device: list = field(default_factory=list)
+
+
+def encode_workload(wl: synth.Workload, device: str = "cpu", keep_reference: bool = True,
+                    keep_device_reference: bool = False, threads: int = 0) -> Encoded:
+    p = codec.params(chunk_weights=wl.chunk_weights, lanes=wl.lanes, threads=threads)
+    tensors = []
+    ent_sum, n_bf16 = 0.0, 0
+    for it in wl.items:
+        if it.kind == "bf16":
+            words = synth.as_words(it.tensor)
+            tables = codec.build_tables(words, p) if words.is_cuda else None
+            host = words.cpu().numpy().view(np.uint16)
+            tensors.append(codec.bf16(host, tables))
+            ent_sum += word_entropy_bits(words) * words.numel()
+            n_bf16 += words.numel()
+        else:
+            tensors.append(codec.raw(it.tensor.contiguous().cpu().numpy().view(np.uint8).reshape(-1)))
+    container = codec.encode(tensors, p)
+    info = codec.container_info(container)
+    enc = Encoded(name=wl.name, container=container, n_weights=int(info.bf16_weights), raw_bytes=int(info.raw_bytes),
+                  entropy_bits=ent_sum / n_bf16 if n_bf16 else math.nan,
+                  bits_per_weight=8.0 * info.bf16_bytes / info.bf16_weights if info.bf16_weights else math.nan,
+                  params=dict(chunk_weights=wl.chunk_weights, lanes=wl.lanes, m_s=12, m_f=10, max_tables=6))
+    if keep_reference or keep_device_reference:
+        ref = np.zeros(info.out_len, np.uint8)
+        for i, t in enumerate(tensors):
+            ri = codec.record_info(container, i)
+            b = t.data.view(np.uint8)
+            ref[ri.out_offset: ri.out_offset + b.size] = b
+        if keep_reference:
+            enc.reference = ref.tobytes()
+        if keep_device_reference:
+            enc.reference_device = torch.from_numpy(ref).to("cuda")
+    return enc
+
+
+CONFIG_BUILDERS = {
+    "1": lambda device: synth.cfg1(device),
+    "2": lambda device: synth.cfg2(device, lanes=256),
+    "3": lambda device: synth.cfg3(device),
+    "4": lambda device: synth.cfg4(device),
+}
+
+
+def encode_config(cfg: str, device: str = "cpu", **kw) -> Encoded:
+    wl = CONFIG_BUILDERS[cfg](device)
+    if cfg == "4":
+        kw.setdefault("keep_reference", False)
+        kw.setdefault("keep_device_reference", True)
+    return encode_workload(wl, device=device, **kw)
+
+
+class DecodeJob:
+    """A resident container, its plan and a preallocated output: one decode
+    step = bs_decode_async over all records."""
+
+    def __init__(self, enc: Encoded, device: str = "cuda"):
+        self.enc = enc
+        self.name = enc.name
+        self.n_weights = enc.n_weights
+        self.raw_bytes = enc.raw_bytes
+        self.bits_per_weight = enc.bits_per_weight
+        self.entropy_bits = enc.entropy_bits
+        self.chunk_weights = enc.params["chunk_weights"]
+        self.lanes = enc.params["lanes"]
+        self.lanes_per_thread = 1 if self.lanes <= 64 else self.lanes // 64
+        self.container_bytes = len(enc.container)
+        info = codec.container_info(enc.container)
+        # bytes a decode reads: BF16 record bytes (tables, index, states, words) and verbatim spans
+        self.read_bytes = int(info.bf16_bytes) + int(info.raw_bytes)
+        self.plan = codec.Plan(enc.container, device)
+        self.out = torch.zeros(max(self.plan.out_bytes(), 16), dtype=torch.uint8, device=device)
+        if enc.reference_device is not None:
+            self.ref = enc.reference_device
+        else:
+            self.ref = torch.from_numpy(np.frombuffer(enc.reference, np.uint8).copy()).to(device)
+
+    def decode(self, stream=None):
+        self.plan.decode_into(self.out, stream=stream)
+
+    def verify(self):
+        rc, rep = self.plan.verify(self.out, ref=self.ref, flags=L.VERIFY_STATUS | L.VERIFY_COMPARE)
+        return rc == L.BS_OK, rep

@@ -740,3 +740,51 @@ int bso_decode_container(const uint8_t* c, uint64_t len, uint8_t* out, uint64_t 
     }
     return first_err;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Decode one chunk of one BF16 record (for sampled checks on big inputs).   */
+/* out receives the chunk's n_c words; *n_c_out their count.                 */
+/* ------------------------------------------------------------------------ */
+int bso_decode_chunk(const uint8_t* c, uint64_t len, uint32_t record, uint64_t chunk,
+                     uint16_t* out, uint64_t out_cap, uint64_t* n_c_out) {
+    if (len < BSO_HDR_BYTES || memcmp(c, BSO_MAGIC, 8) != 0) return BSO_EFORMAT;
+    if (get32(c + 8) != BSO_VERSION) return BSO_EVERSION;
+    uint32_t n_rec = get32(c + 12);
+    uint64_t dir = get64(c + 16);
+    if (record >= n_rec || dir + (uint64_t)BSO_DIR_BYTES * n_rec > len) return BSO_EINVAL;
+    const uint8_t* d = c + dir + (uint64_t)BSO_DIR_BYTES * record;
+    if (get32(d) != BSO_KIND_BF16) return BSO_EINVAL;
+    uint64_t n = get64(d + 8), ro = get64(d + 24), rl = get64(d + 32);
+    if (ro > len || rl > len - ro) return BSO_EFORMAT;
+    bso_model* md = (bso_model*)calloc(1, sizeof(bso_model));
+    if (!md) return BSO_ENOMEM;
+    uint32_t W, K; uint64_t nch, io;
+    int rc = parse_model(c + ro, rl, n, md, &W, &K, &nch, &io);
+    if (!rc && chunk >= nch) rc = BSO_EINVAL;
+    uint64_t n_c = 0;
+    if (!rc) {
+        n_c = (n - chunk * W) < W ? (n - chunk * W) : W;
+        if (n_c > out_cap) rc = BSO_ENOSPACE;
+    }
+    if (!rc) {
+        const uint8_t* e = c + ro + io + 16 * chunk;
+        uint64_t po = get64(e), nw = get32(e + 8), sb = round_up(4ull * K, 16);
+        if (po % 16 || po + sb + 2 * nw > rl) rc = BSO_EFORMAT;
+        uint32_t* st = NULL;
+        uint16_t* words = NULL;
+        if (!rc) {
+            st = (uint32_t*)malloc(sizeof(uint32_t) * K);
+            words = (uint16_t*)malloc(sizeof(uint16_t) * (nw ? nw : 1));
+            if (!st || !words) rc = BSO_ENOMEM;
+        }
+        if (!rc) {
+            for (uint32_t l = 0; l < K; l++) st[l] = get32(c + ro + po + 4ull * l);
+            for (uint64_t j = 0; j < nw; j++) words[j] = (uint16_t)get16(c + ro + po + sb + 2 * j);
+            rc = chunk_decode(md, st, words, nw, (uint32_t)n_c, K, out);
+        }
+        free(st); free(words);
+    }
+    free(md);
+    *n_c_out = n_c;
+    return rc;
+}

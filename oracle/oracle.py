@@ -76,6 +76,8 @@ def lib():
         l.bso_decode_container.argtypes = [C.c_void_p, C.c_uint64, C.c_void_p, C.c_uint64, C.c_void_p]
         l.bso_decode_container.restype = C.c_int
         l.bso_free.argtypes = [C.c_void_p]; l.bso_free.restype = None
+        l.bso_decode_chunk.argtypes = [C.c_void_p, C.c_uint64, C.c_uint32, C.c_uint64, C.c_void_p, C.c_uint64, u64p]
+        l.bso_decode_chunk.restype = C.c_int
         _lib = l
     return _lib
 
@@ -286,3 +288,14 @@ def decode_status(container: bytes, out_cap: int | None = None):
     st = np.zeros(max(n_rec, 1), np.int32)
     rc = lib().bso_decode_container(_ptr(buf), buf.size, _ptr(out), cap, _ptr(st))
     return rc, out[:cap].tobytes(), [int(v) for v in st[:n_rec]]
+
+
+def decode_chunk(container, record: int, chunk: int, max_weights: int = 1 << 20) -> np.ndarray:
+    """The words of one chunk of one BF16 record, decoded by the oracle."""
+    buf = np.frombuffer(container, np.uint8)
+    out = np.zeros(max_weights, np.uint16)
+    n_c = np.zeros(1, np.uint64)
+    rc = lib().bso_decode_chunk(_ptr(buf), buf.size, record, chunk, _ptr(out), max_weights, _u64p(n_c))
+    if rc:
+        raise OracleError(rc, "decode_chunk")
+    return out[: int(n_c[0])].copy()

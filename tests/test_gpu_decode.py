@@ -1,0 +1,198 @@
+"""GPU parity: the HIP decode path against the original bits and the oracle.
+
+Bit-exact equality is the bar: decoding must reproduce every BF16 word
+[Qwen3.8-27B-BF16-NVLC-Lossless card, metrics table: per-codec and integrated
+inverse verification; Gemma 2 9B Instruct -- Lossless Compressed card, "What
+lossless means"].  Every call goes through the C ABI (bs_plan_create,
+bs_decode_async, bs_verify, bs_build_tables) via the ctypes binding.
+"""
+import hashlib
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from lossless_entropy_coding_amd import _lib as L
+from lossless_entropy_coding_amd import codec, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _words(x) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+
+
+def _decode_check(container: bytes, expect: bytes, flags=L.VERIFY_STATUS | L.VERIFY_SHA256):
+    plan = codec.Plan(container)
+    out = plan.decode()
+    rc, rep = plan.verify(out, flags=flags)
+    got = out[: len(expect)].cpu().numpy().tobytes()
+    return plan, out, rc, rep, got
+
+
+def _expected_bytes(container: bytes) -> bytes:
+    out, st = O.decode(container)
+    assert all(s == 0 for s in st)
+    return out
+
+
+CASES = [
+    # (name, n, scale, W, K)
+    ("one_group", 8, 0.02, 64, 1),
+    ("ragged_k1", 1001, 0.02, 64, 1),
+    ("k8_ragged", 40000 + 13, 0.02, 4096, 8),
+    ("k32_cfg1_shape", 3 * 32768 + 777, 0.02, 32768, 32),
+    ("k64_full", 4 * 65536, 0.02, 65536, 64),
+    ("k64_ragged", 3 * 65536 + 4099, 0.05, 65536, 64),
+    ("k128_full", 6 * 65536, 0.02, 65536, 128),
+    ("k128_ragged", 2 * 65536 + 1025, 0.003, 65536, 128),
+    ("k256_full", 4 * 131072, 0.02, 131072, 256),
+    ("k256_ragged", 131072 + 2049 + 7, 0.1, 131072, 256),
+    ("small_k_tiny_chunks", 5000, 0.02, 512, 4),
+]
+
+
+@pytest.mark.parametrize("name,n,scale,W,K", CASES, ids=[c[0] for c in CASES])
+def test_decode_matches_oracle_and_original(name, n, scale, W, K):
+    say("case", name, n, W, K)
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal(n) * scale
+    x[rng.random(n) < 0.01] = 0.0
+    w = _words(x)
+    c = codec.encode([codec.bf16(w)], codec.params(chunk_weights=W, lanes=K))
+    assert c == O.encode([O.bf16(w)], W=W, K=K)
+    expect = _expected_bytes(c)
+    assert expect == w.tobytes()
+    plan, out, rc, rep, got = _decode_check(c, expect)
+    assert got == expect
+    assert rc == L.BS_OK, rep
+    assert rep["chunks_bad"] == 0 and rep["records_hash_bad"] == 0
+
+
+def test_special_values_and_residual():
+    say("special values + residual")
+    rng = np.random.default_rng(1)
+    specials = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81, 0x0001, 0x807F, 0x0080, 0x7F7F,
+                         0xFF7F], np.uint16)
+    body = _words(rng.standard_normal(70000) * 0.02)
+    mix = np.concatenate([body, np.tile(specials, 500)])
+    rng.shuffle(mix)
+    allw = synth.as_words(synth.special_words()).numpy().astype(np.uint16)   # stored verbatim (> 256 symbols)
+    raw = np.arange(3584, dtype=np.float32).tobytes()
+    tensors = [codec.bf16(mix), codec.raw(raw), codec.bf16(allw), codec.raw(b"xyz"), codec.bf16(np.zeros(0, np.uint16)),
+               codec.bf16(np.full(77, 0x3F80, np.uint16))]
+    c = codec.encode(tensors, codec.params(chunk_weights=8192, lanes=64))
+    expect = _expected_bytes(c)
+    plan = codec.Plan(c)
+    out = plan.decode()
+    rc, rep = plan.verify(out, flags=L.VERIFY_STATUS | L.VERIFY_SHA256)
+    assert rc == L.BS_OK, rep
+    host = out.cpu().numpy().tobytes()
+    for i in range(plan.n_records):
+        ri = codec.record_info(c, i)
+        nb = 2 * ri.n if ri.kind == L.KIND_BF16 else ri.n
+        assert host[ri.out_offset: ri.out_offset + nb] == expect[ri.out_offset: ri.out_offset + nb], i
+
+
+def test_record_range_and_determinism():
+    say("record ranges")
+    rng = np.random.default_rng(2)
+    ws = [_words(rng.standard_normal(n) * s) for n, s in [(65536 * 3, 0.02), (5000, 0.01), (131072 + 99, 0.04)]]
+    tensors = [codec.bf16(ws[0]), codec.raw(b"q" * 1000), codec.bf16(ws[1]), codec.bf16(ws[2])]
+    c = codec.encode(tensors, codec.params(chunk_weights=65536, lanes=128))
+    plan = codec.Plan(c)
+    full = plan.decode()
+    again = plan.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(full, again)
+    for first, count in [(0, 1), (1, 2), (2, 2), (3, 1), (0, 4)]:
+        out = plan.decode(first, count)
+        torch.cuda.synchronize()
+        for i in range(first, first + count):
+            a = codec.record_output(out, plan, i, first)
+            b = codec.record_output(full, plan, i, 0)
+            assert torch.equal(a, b), (first, count, i)
+    rc, rep = plan.verify(plan.decode(1, 3), flags=L.VERIFY_STATUS | L.VERIFY_SHA256, first=1, count=3)
+    assert rc == L.BS_OK, rep
+
+
+def test_output_capacity_and_alignment_errors():
+    say("capacity errors")
+    w = _words(np.random.default_rng(3).standard_normal(10000) * 0.02)
+    c = codec.encode([codec.bf16(w)], codec.params(chunk_weights=4096, lanes=8))
+    plan = codec.Plan(c)
+    small = torch.empty(100, dtype=torch.uint8, device="cuda")
+    with pytest.raises(L.BSError) as e:
+        plan.decode_into(small)
+    assert e.value.rc == L.BS_E_NOSPACE
+    big = torch.empty(plan.out_bytes() + 64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(L.BSError) as e:
+        plan.decode_into(big[8:])
+    assert e.value.rc == L.BS_E_INVAL
+
+
+def test_guard_bytes_untouched():
+    say("guard bytes")
+    w = _words(np.random.default_rng(4).standard_normal(65536 * 2 + 333) * 0.02)
+    c = codec.encode([codec.bf16(w)], codec.params(chunk_weights=65536, lanes=128))
+    plan = codec.Plan(c)
+    n = plan.out_bytes()
+    buf = torch.full((n + 4096 + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    out = buf[4096: 4096 + n]
+    plan.decode_into(out)
+    torch.cuda.synchronize()
+    assert bool((buf[:4096] == 0xA5).all()) and bool((buf[4096 + n:] == 0xA5).all())
+    assert out.cpu().numpy().tobytes() == w.tobytes()
+
+
+def test_corrupt_payload_is_reported_not_crashing():
+    say("corrupt payload")
+    rng = np.random.default_rng(5)
+    w = _words(rng.standard_normal(65536 * 4) * 0.02)
+    c = bytearray(codec.encode([codec.bf16(w)], codec.params(chunk_weights=65536, lanes=64)))
+    ri = codec.record_info(bytes(c), 0)
+    # flip bytes inside the payload area of the first and third chunk (past the index)
+    for frac in (0.2, 0.7):
+        pos = ri.rec_offset + int(ri.rec_len * frac)
+        c[pos] ^= 0x5A
+    plan = codec.Plan(bytes(c))
+    out = plan.decode()
+    ref = torch.from_numpy(w.view(np.uint8).copy()).cuda()
+    rc, rep = plan.verify(out, ref=ref, flags=L.VERIFY_STATUS | L.VERIFY_COMPARE | L.VERIFY_SHA256)
+    assert rc in (L.BS_E_CORRUPT, L.BS_E_MISMATCH)
+    assert rep["chunks_bad"] >= 1 and rep["bytes_mismatched"] > 0 and rep["records_hash_bad"] == 1
+
+
+def test_device_tables_match_host_tables():
+    say("device histogram tables")
+    rng = np.random.default_rng(6)
+    for x in [rng.standard_normal(1 << 20) * 0.02, rng.standard_normal(300001) * 0.3,
+              np.where(rng.random(123457) < 0.1, 0.0, rng.standard_normal(123457))]:
+        w = _words(x)
+        dev = torch.from_numpy(w.view(np.int16)).cuda()
+        for off in (0, 1, 3):   # unaligned starts exercise the head/tail path
+            td = codec.build_tables(dev[off:]).get()
+            th = codec.build_tables_host(w[off:]).get()
+            for k in ("counts_s", "q_s", "route", "q_f"):
+                assert np.array_equal(td[k], th[k]), (k, off)
+            assert td["n_tables"] == th["n_tables"]
+            cs, cf = O.histogram(w[off:])
+            assert np.array_equal(td["counts_s"], cs)
+
+
+def test_device_tables_encode_same_container():
+    say("encode with device tables")
+    wl = synth.cfg1()
+    w = synth.as_words(wl.items[0].tensor).numpy().astype(np.uint16)
+    p = codec.params(chunk_weights=wl.chunk_weights, lanes=wl.lanes)
+    t = codec.build_tables(torch.from_numpy(w.view(np.int16)).cuda(), p)
+    c1 = codec.encode([codec.bf16(w, t)], p)
+    c2 = O.encode([O.bf16(w)], W=wl.chunk_weights, K=wl.lanes)
+    assert c1 == c2
