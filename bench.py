@@ -39,6 +39,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle baseline")
     ap.add_argument("--cfg5-layers", type=int, default=84, help="config 5: layers to build (84 = full checkpoint)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB a few times (to scale HBM byte counters)")
+    ap.add_argument("--lanes", type=int, default=None, help="override the lanes per chunk of the workload")
+    ap.add_argument("--chunk-weights", type=int, default=None, help="override the weights per chunk")
     return ap.parse_args()
 
 
@@ -94,6 +98,16 @@ def main():
     from lossless_entropy_coding_amd import codec, synth, workloads
 
     assert torch.cuda.is_available(), "no GPU visible"
+    if a.calibrate_copy:
+        n = a.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                          "copies": 5}))
+        return
     L.lib()   # fails loudly if the HIP library is missing
     dev = "cuda"
     t0 = time.time()
@@ -102,7 +116,8 @@ def main():
         job = checkpoint.build_job(layers=a.cfg5_layers, log=log)
     else:
         gen_dev = "cuda" if a.config == "4" else "cpu"
-        enc = workloads.encode_config(a.config, device=gen_dev, keep_reference=False, keep_device_reference=True)
+        enc = workloads.encode_config(a.config, device=gen_dev, keep_reference=False, keep_device_reference=True,
+                                      lanes=a.lanes, chunk_weights=a.chunk_weights)
         job = workloads.DecodeJob(enc)
     log(f"workload {job.name}: {job.n_weights} BF16 weights, container {job.container_bytes / 1e6:.1f} MB, "
         f"built in {time.time() - t0:.1f}s")

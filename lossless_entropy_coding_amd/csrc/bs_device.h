@@ -24,7 +24,6 @@ constexpr uint32_t kRingMirror = 64;        // copy of the ring's first 64 words
 constexpr uint32_t kRingBytes = (kRingWords + kRingMirror) * 2;      // 4224
 constexpr uint32_t kBlockWords = 512;       // ring fill unit: 16 B per lane
 constexpr uint32_t kMaxWaves = 16;
-constexpr uint32_t kMaxWavesR4 = 8;      // 4 lanes per thread: 8 waves per workgroup
 
 // Device lookup-table image of one record (built once per plan):
 //   s part: 2^M_s x {A, B}

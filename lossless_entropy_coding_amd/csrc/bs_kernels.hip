@@ -236,15 +236,25 @@ __device__ __forceinline__ void ring_top_up(Ring& g, uint32_t pos, uint32_t lane
     }
 }
 
-// renormalise one group of 64 lanes: lanes whose state fell below 2^16 take
-// the next stream words, in lane order
-__device__ __forceinline__ void refill(uint32_t& x, bool active, const Ring& g, uint32_t& pos) {
-    const bool need = active && x < kStateLow;
-    const uint64_t m = __builtin_amdgcn_ballot_w64(need);
-    const uint32_t pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    const uint16_t* rp = g.base + (pos & (kRingWords - 1));
-    if (need) x = (x << 16) | (uint32_t)rp[pre];
-    pos += (uint32_t)__builtin_popcountll(m);
+// Renormalise the R groups of 64 lanes of one sub-step: lanes whose state
+// fell below 2^16 take the next stream words, group 0 first and ascending lane
+// order inside a group (a prefix count over the ballot).  Every lane reads
+// its candidate word (always a valid ring index) and keeps it only if it
+// needed one, so the R ring reads are in flight together.
+template <int R>
+__device__ __forceinline__ void refill_all(uint32_t (&x)[R], const bool (&active)[R], const Ring& g, uint32_t& pos) {
+    bool need[R];
+    uint32_t w[R];
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        need[q] = active[q] && x[q] < kStateLow;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(need[q]);
+        const uint32_t pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        w[q] = g.base[(pos & (kRingWords - 1)) + pre];
+        pos += (uint32_t)__builtin_popcountll(m);
+    }
+#pragma unroll
+    for (int q = 0; q < R; q++) x[q] = need[q] ? (x[q] << 16) | w[q] : x[q];
 }
 
 struct Model {
@@ -308,6 +318,10 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
     const uint32_t T = (groups + K - 1) / K;
     const uint32_t T_full = (K % 64 == 0) ? n_c / (8 * K) : 0;
 
+    bool all_on[R];
+#pragma unroll
+    for (int q = 0; q < R; q++) all_on[q] = true;
+
     // full macro-steps: every lane decodes 8 weights, one 128-bit store per lane group
     for (uint32_t t = 0; t < T_full; t++) {
         uint32_t o[R][4];
@@ -317,17 +331,19 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
             uint2 se[R];
 #pragma unroll
             for (int q = 0; q < R; q++) se[q] = step_s(x[q], md);
-#pragma unroll
-            for (int q = 0; q < R; q++) refill(x[q], true, g, pos);
+            refill_all<R>(x, all_on, g, pos);
             uint32_t wv[R];
 #pragma unroll
             for (int q = 0; q < R; q++) wv[q] = step_f(x[q], se[q], md);
-#pragma unroll
-            for (int q = 0; q < R; q++) refill(x[q], true, g, pos);
+            refill_all<R>(x, all_on, g, pos);
 #pragma unroll
             for (int q = 0; q < R; q++) {
                 if (p & 1) o[q][p >> 1] = __builtin_amdgcn_perm(wv[q], o[q][p >> 1], 0x05040100u);
                 else o[q][p >> 1] = wv[q];
+                // pack now: keeps the table entries of earlier positions dead
+                // (otherwise the compiler sinks the packing to the store and
+                // keeps 8 positions of entries live)
+                asm volatile("" : "+v"(o[q][p >> 1]));
             }
         }
 #pragma unroll
@@ -338,7 +354,8 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
     }
 
     // remaining macro-steps (partial groups, or fewer than 64 lanes): lanes
-    // take part while they still have weights
+    // take part while they still have weights.  One position per iteration;
+    // each lane's eight output words move through a 128-bit shift register.
     for (uint32_t t = T_full; t < T; t++) {
         int32_t cnt[R];
         uint32_t o[R][4];
@@ -350,32 +367,31 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
 #pragma unroll
             for (int k = 0; k < 4; k++) o[q][k] = 0;
         }
-#pragma unroll
+#pragma unroll 1
         for (int p = 0; p < 8; p++) {
             ring_top_up(g, pos, lane);
+            bool act[R];
             uint2 se[R];
 #pragma unroll
             for (int q = 0; q < R; q++) {
+                act[q] = p < cnt[q];
                 uint32_t xs = x[q];
                 se[q] = step_s(xs, md);
-                if (p < cnt[q]) x[q] = xs;
+                if (act[q]) x[q] = xs;
             }
-#pragma unroll
-            for (int q = 0; q < R; q++) refill(x[q], p < cnt[q], g, pos);
-            uint32_t wv[R];
+            refill_all<R>(x, act, g, pos);
 #pragma unroll
             for (int q = 0; q < R; q++) {
                 uint32_t xs = x[q];
-                wv[q] = step_f(xs, se[q], md);
-                if (p < cnt[q]) x[q] = xs;
+                const uint32_t w = step_f(xs, se[q], md);
+                if (act[q]) x[q] = xs;
+                // shift the 128-bit register right by 16 and insert w on top
+                o[q][0] = __builtin_amdgcn_alignbit(o[q][1], o[q][0], 16);
+                o[q][1] = __builtin_amdgcn_alignbit(o[q][2], o[q][1], 16);
+                o[q][2] = __builtin_amdgcn_alignbit(o[q][3], o[q][2], 16);
+                o[q][3] = __builtin_amdgcn_alignbit(w, o[q][3], 16);
             }
-#pragma unroll
-            for (int q = 0; q < R; q++) refill(x[q], p < cnt[q], g, pos);
-#pragma unroll
-            for (int q = 0; q < R; q++) {
-                if (p & 1) o[q][p >> 1] = __builtin_amdgcn_perm(wv[q], o[q][p >> 1], 0x05040100u);
-                else o[q][p >> 1] = wv[q];
-            }
+            refill_all<R>(x, act, g, pos);
         }
 #pragma unroll
         for (int q = 0; q < R; q++) {
@@ -400,13 +416,12 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
     if (lane == 0) a.status[r.chunk_base + ch] = (badm ? 1u : 0u) | (pos != nw ? 2u : 0u);
 }
 
-// Workgroups of up to 16 waves share one copy of the record's lookup tables;
-// the 4-lanes-per-thread variant keeps 8 waves so that it has 256 VGPRs.
+// Workgroups of up to 16 waves share one copy of the record's lookup tables.
 template <int R>
-__global__ __launch_bounds__(R == 4 ? 512 : 1024) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(1024) void decode_kernel(const DecodeArgs a) {
     // static allocation: the LDS base is a compile-time constant, so table and
     // ring addresses fold into the instructions' offsets
-    __shared__ __align__(16) uint8_t lds[kLutLds + (R == 4 ? kMaxWavesR4 : kMaxWaves) * kRingBytes];
+    __shared__ __align__(16) uint8_t lds[kLutLds + kMaxWaves * kRingBytes];
     const TaskDev tk = a.tasks[a.task_begin + blockIdx.x];
     const RecDev r = a.recs[tk.rec];
     // stage the record's lookup tables into LDS

@@ -113,7 +113,7 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
     if (bsk_device_cus(&cus) != 0 || cus <= 0) cus = 256;
     const uint32_t n = p->c.n_records;
     // chunks per class decide the workgroup size: enough workgroups to cover
-    // the CUs, at most 16 waves (8 for four lanes per thread)
+    // the CUs, at most 16 waves
     uint64_t class_chunks[bs_plan::kClasses] = {0, 0, 0};
     p->rclass.assign(n, 0);
     for (uint32_t i = 0; i < n; i++) {
@@ -124,8 +124,7 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
         class_chunks[p->rclass[i]] += r.n_chunks;
     }
     for (int k = 0; k < bs_plan::kClasses; k++) {
-        const uint64_t cap = k == 2 ? bsd::kMaxWavesR4 : bsd::kMaxWaves;
-        p->waves[k] = (uint32_t)std::min<uint64_t>(cap, std::max<uint64_t>(1, (class_chunks[k] + cus - 1) / cus));
+        p->waves[k] = (uint32_t)std::min<uint64_t>(bsd::kMaxWaves, std::max<uint64_t>(1, (class_chunks[k] + cus - 1) / cus));
     }
 
     std::vector<bsd::RecDev> recs;

@@ -86,8 +86,13 @@ CONFIG_BUILDERS = {
 }
 
 
-def encode_config(cfg: str, device: str = "cpu", **kw) -> Encoded:
+def encode_config(cfg: str, device: str = "cpu", lanes: int | None = None, chunk_weights: int | None = None,
+                  **kw) -> Encoded:
     wl = CONFIG_BUILDERS[cfg](device)
+    if lanes:
+        wl.lanes = lanes
+    if chunk_weights:
+        wl.chunk_weights = chunk_weights
     if cfg == "4":
         kw.setdefault("keep_reference", False)
         kw.setdefault("keep_device_reference", True)
