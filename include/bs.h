@@ -69,7 +69,7 @@ typedef enum {
 enum { BS_KIND_BF16 = 1, BS_KIND_RAW = 2 };
 
 /* Encoder parameters.  chunk_weights W must be a multiple of 8*lanes; lanes K
- * is 1..64, 128 or 256 (a power of two); 9 <= m_s <= 12; 7 <= m_f <= 10;
+ * is a power of two: 1..64, 128, 256 or 512; 9 <= m_s <= 12; 7 <= m_f <= 10;
  * max_tables <= 6; threads = host encoder threads (0 = hardware count). */
 typedef struct {
     uint32_t chunk_weights;

@@ -234,7 +234,7 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         r.n_tables = b[14];
         r.n_sym = rd32(b + 16);
         const uint32_t K = r.K;
-        if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256) || r.W == 0 || r.W % (8 * K)) {
+        if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256 || K == 512) || r.W == 0 || r.W % (8 * K)) {
             set_error("record %u: bad chunk shape W=%u K=%u", i, r.W, K);
             return BS_E_FORMAT;
         }

@@ -19,11 +19,15 @@ constexpr uint32_t kFlutOff = 32768;
 constexpr uint32_t kFPage = 8192;
 constexpr uint32_t kFPageShift = 13;
 constexpr uint32_t kLutLds = kFlutOff + (kMaxTables + 1) * kFPage;   // 90112
-constexpr uint32_t kRingWords = 2048;       // power of two
 constexpr uint32_t kRingMirror = 64;        // copy of the ring's first 64 words after its end
-constexpr uint32_t kRingBytes = (kRingWords + kRingMirror) * 2;      // 4224
-constexpr uint32_t kBlockWords = 512;       // ring fill unit: 16 B per lane
 constexpr uint32_t kMaxWaves = 16;
+
+// ring size (16-bit words, a power of two), ring bytes and the workgroup cap
+// for R lanes per thread: 2048 words and 16 waves up to R = 4; 4096 words and
+// 8 waves for R = 8 (it consumes up to 1024 words per weight position)
+constexpr uint32_t ring_words(uint32_t R) { return R >= 8 ? 4096u : 2048u; }
+constexpr uint32_t ring_bytes(uint32_t R) { return (ring_words(R) + kRingMirror) * 2u; }
+constexpr uint32_t max_waves(uint32_t R) { return R >= 8 ? 8u : 16u; }
 
 // Device lookup-table image of one record (built once per plan):
 //   s part: 2^M_s x {A, B}
@@ -42,18 +46,18 @@ struct RecDev {
     uint32_t chunk_base;    // first chunk's index in the status array
     uint32_t m_s, m_f;
     uint32_t n_tables;
-    uint32_t lanes_per_thread;  // R = 1, 2 or 4
+    uint32_t lanes_per_thread;  // R = 1, 2, 4 or 8
     uint32_t n_sym;
     uint32_t stab_off;      // byte offset (from body) of the s-table
     uint32_t route_off;     // byte offset (from body) of the route bytes
     uint32_t ftab_off;      // byte offset (from body) of the fraction tables
 };
 
-struct TaskDev {
-    uint32_t rec;           // index into the RecDev array
-    uint32_t c0;            // first chunk of the record handled by this workgroup
-    uint32_t nc;            // chunks (one per wave)
-    uint32_t pad;
+// One lanes-per-thread class of a plan: its BF16 records in container order
+// and the running chunk count before each (n + 1 entries).
+struct ClassDev {
+    const uint32_t* recs;   // RecDev index of each record of the class
+    const uint32_t* start;  // first class-wide chunk of each record; start[n] = total
 };
 
 struct RawDev {
@@ -65,12 +69,13 @@ struct RawDev {
 struct DecodeArgs {
     const uint8_t* container;
     const RecDev* recs;
-    const TaskDev* tasks;
+    ClassDev cls;
     const uint8_t* luts;
     uint8_t* out;
     uint32_t* status;
     uint64_t out_base;      // output offset that maps to out[0]
-    uint32_t task_begin;
+    uint32_t i0, i1;        // class entries of the decoded records
+    uint32_t run;           // chunks per workgroup (a run inside one record)
     uint32_t waves;         // waves per workgroup (rings allocated)
 };
 
@@ -82,7 +87,7 @@ int bsk_hist_s(const uint16_t* d_w, uint64_t n, unsigned long long* d_cs, void* 
 int bsk_hist_f(const uint16_t* d_w, uint64_t n, const int16_t* d_cand, unsigned long long* d_cf, void* stream);
 int bsk_build_luts(const uint8_t* d_container, const bsd::RecDev* d_recs, uint32_t n_recs, uint8_t* d_luts,
                    void* stream);
-int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_tasks, uint32_t lanes_per_thread, void* stream);
+int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t lanes_per_thread, void* stream);
 int bsk_raw_copy(const uint8_t* d_container, const bsd::RawDev* d_raw, uint32_t n_raw, uint8_t* d_out,
                  uint64_t out_base, void* stream);
 int bsk_compare(const uint8_t* a, const uint8_t* b, uint64_t n, unsigned long long* d_result /*2*/, void* stream);

@@ -193,46 +193,51 @@ __device__ __forceinline__ uint4 load_piece(__amdgpu_buffer_rsrc_t rs, uint32_t 
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Per-wave ring of stream words in LDS.  Words are refilled 1024 at a time
-// (two 16-B pieces per lane, loaded one refill ahead into pa/pb); the ring
-// holds 2048 words plus a 64-word copy of its head after its end, so that a
-// refill of up to 64 consecutive words never wraps.
+// Per-wave ring of stream words in LDS: RW words (2048, or 4096 for eight
+// lanes per thread) plus a 64-word copy of its head after its end, so that a
+// refill of up to 64 consecutive words never wraps.  Words are refilled RW/2
+// at a time (RW/1024 16-B pieces per lane), loaded one refill ahead.
+template <uint32_t RW>
 struct Ring {
-    uint16_t* base;       // LDS ring of this wave (kRingWords + kRingMirror words)
-    uint4 pa, pb;         // the next 1024 words, in flight
+    static constexpr uint32_t kPieces = RW / 1024;   // 16-B pieces per lane per refill
+    uint16_t* base;       // LDS ring of this wave
+    uint4 pf[kPieces];    // the next RW/2 words, in flight
     uint32_t fill;        // stream words written into the ring so far
     const uint8_t* words; // the chunk's word area (uniform)
     uint32_t bytes;       // its size, a multiple of 16
-    uint32_t off_a, off_b;  // per-lane byte offsets of the two prefetched pieces
+    uint32_t lane;
 };
 
-__device__ __forceinline__ void ring_init(Ring& g, uint32_t lane) {
+template <uint32_t RW>
+__device__ __forceinline__ void ring_init(Ring<RW>& g, uint32_t lane) {
     uint4* r4 = (uint4*)g.base;
-    g.off_a = 16 * (128 + lane);
-    g.off_b = 16 * (192 + lane);
+    g.lane = lane;
     const __amdgpu_buffer_rsrc_t rs = stream_rsrc(g.words, g.bytes, 0);
-    const uint4 b0 = load_piece(rs, 16 * lane);
-    const uint4 b1 = load_piece(rs, 16 * (64 + lane));
-    g.pa = load_piece(rs, g.off_a);
-    g.pb = load_piece(rs, g.off_b);
-    r4[lane] = b0;
-    r4[64 + lane] = b1;
-    if (lane < kRingMirror / 8) r4[kRingWords / 8 + lane] = b0;
-    g.fill = 2 * kBlockWords;
+    uint4 first[Ring<RW>::kPieces];
+#pragma unroll
+    for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) first[k] = load_piece(rs, 16 * (64 * k + lane));
+#pragma unroll
+    for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) g.pf[k] = load_piece(rs, 16 * (64 * (Ring<RW>::kPieces + k) + lane));
+#pragma unroll
+    for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) r4[64 * k + lane] = first[k];
+    if (lane < kRingMirror / 8) r4[RW / 8 + lane] = first[0];
+    g.fill = RW / 2;
 }
 
-// keep at least 1024 words ahead of `pos` in the ring (uniform branch)
-__device__ __forceinline__ void ring_top_up(Ring& g, uint32_t pos, uint32_t lane) {
-    if (g.fill - pos < 2 * kBlockWords) {
+// keep at least RW/2 words ahead of `pos` in the ring (uniform branch)
+template <uint32_t RW>
+__device__ __forceinline__ void ring_top_up(Ring<RW>& g, uint32_t pos) {
+    if (g.fill - pos < RW / 2) {
         uint4* r4 = (uint4*)g.base;
-        const uint32_t ro = (g.fill & (kRingWords - 1)) >> 3;
-        r4[ro + lane] = g.pa;
-        r4[ro + 64 + lane] = g.pb;
-        if (ro == 0 && lane < kRingMirror / 8) r4[kRingWords / 8 + lane] = g.pa;
+        const uint32_t ro = (g.fill & (RW - 1)) >> 3;
+#pragma unroll
+        for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) r4[ro + 64 * k + g.lane] = g.pf[k];
+        if (ro == 0 && g.lane < kRingMirror / 8) r4[RW / 8 + g.lane] = g.pf[0];
         const __amdgpu_buffer_rsrc_t rs = stream_rsrc(g.words, g.bytes, 2 * g.fill);
-        g.pa = load_piece(rs, g.off_a);
-        g.pb = load_piece(rs, g.off_b);
-        g.fill += 2 * kBlockWords;
+#pragma unroll
+        for (uint32_t k = 0; k < Ring<RW>::kPieces; k++)
+            g.pf[k] = load_piece(rs, 16 * (64 * (Ring<RW>::kPieces + k) + g.lane));
+        g.fill += RW / 2;
     }
 }
 
@@ -241,8 +246,8 @@ __device__ __forceinline__ void ring_top_up(Ring& g, uint32_t pos, uint32_t lane
 // order inside a group (a prefix count over the ballot).  Every lane reads
 // its candidate word (always a valid ring index) and keeps it only if it
 // needed one, so the R ring reads are in flight together.
-template <int R>
-__device__ __forceinline__ void refill_all(uint32_t (&x)[R], const bool (&active)[R], const Ring& g, uint32_t& pos) {
+template <int R, uint32_t RW>
+__device__ __forceinline__ void refill_all(uint32_t (&x)[R], const bool (&active)[R], const Ring<RW>& g, uint32_t& pos) {
     bool need[R];
     uint32_t w[R];
 #pragma unroll
@@ -250,7 +255,7 @@ __device__ __forceinline__ void refill_all(uint32_t (&x)[R], const bool (&active
         need[q] = active[q] && x[q] < kStateLow;
         const uint64_t m = __builtin_amdgcn_ballot_w64(need[q]);
         const uint32_t pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        w[q] = g.base[(pos & (kRingWords - 1)) + pre];
+        w[q] = g.base[(pos & (RW - 1)) + pre];
         pos += (uint32_t)__builtin_popcountll(m);
     }
 #pragma unroll
@@ -302,8 +307,9 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
         const uint32_t l = 64 * q + lane;
         x[q] = l < K ? st[l] : kStateLow;
     }
-    Ring g;
-    g.base = (uint16_t*)(lds + kLutLds + wave * kRingBytes);
+    constexpr uint32_t RW = ring_words(R);
+    Ring<RW> g;
+    g.base = (uint16_t*)(lds + kLutLds + wave * ring_bytes(R));
     g.words = payload + ((4 * K + 15) & ~15u);
     g.bytes = (2 * nw + 15) & ~15u;
     ring_init(g, lane);
@@ -327,15 +333,15 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
         uint32_t o[R][4];
 #pragma unroll
         for (int p = 0; p < 8; p++) {
-            ring_top_up(g, pos, lane);
+            ring_top_up(g, pos);
             uint2 se[R];
 #pragma unroll
             for (int q = 0; q < R; q++) se[q] = step_s(x[q], md);
-            refill_all<R>(x, all_on, g, pos);
+            refill_all<R, RW>(x, all_on, g, pos);
             uint32_t wv[R];
 #pragma unroll
             for (int q = 0; q < R; q++) wv[q] = step_f(x[q], se[q], md);
-            refill_all<R>(x, all_on, g, pos);
+            refill_all<R, RW>(x, all_on, g, pos);
 #pragma unroll
             for (int q = 0; q < R; q++) {
                 if (p & 1) o[q][p >> 1] = __builtin_amdgcn_perm(wv[q], o[q][p >> 1], 0x05040100u);
@@ -369,7 +375,7 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
         }
 #pragma unroll 1
         for (int p = 0; p < 8; p++) {
-            ring_top_up(g, pos, lane);
+            ring_top_up(g, pos);
             bool act[R];
             uint2 se[R];
 #pragma unroll
@@ -379,7 +385,7 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
                 se[q] = step_s(xs, md);
                 if (act[q]) x[q] = xs;
             }
-            refill_all<R>(x, act, g, pos);
+            refill_all<R, RW>(x, act, g, pos);
 #pragma unroll
             for (int q = 0; q < R; q++) {
                 uint32_t xs = x[q];
@@ -391,7 +397,7 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
                 o[q][2] = __builtin_amdgcn_alignbit(o[q][3], o[q][2], 16);
                 o[q][3] = __builtin_amdgcn_alignbit(w, o[q][3], 16);
             }
-            refill_all<R>(x, act, g, pos);
+            refill_all<R, RW>(x, act, g, pos);
         }
 #pragma unroll
         for (int q = 0; q < R; q++) {
@@ -416,29 +422,66 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
     if (lane == 0) a.status[r.chunk_base + ch] = (badm ? 1u : 0u) | (pos != nw ? 2u : 0u);
 }
 
-// Workgroups of up to 16 waves share one copy of the record's lookup tables.
+// Stage one record's lookup tables into LDS (all threads of the workgroup).
+__device__ __forceinline__ void stage_luts(const DecodeArgs& a, const RecDev& r, uint8_t* lds) {
+    const uint4* src = (const uint4*)(a.luts + r.lut_off);
+    const uint32_t ns16 = (8u << r.m_s) / 16;
+    uint4* d = (uint4*)(lds + kSlutOff);
+    for (uint32_t i = threadIdx.x; i < ns16; i += blockDim.x) d[i] = src[i];
+    const uint32_t nf16 = (r.n_tables + 1) * (kFPage / 16);
+    const uint4* fs = src + ns16;
+    uint4* fd = (uint4*)(lds + kFlutOff);
+    for (uint32_t i = threadIdx.x; i < nf16; i += blockDim.x) fd[i] = fs[i];
+}
+
+// Workgroup b of a launch decodes one run of chunks inside one record: each
+// record r of the class entries [i0, i1) is cut into ceil(chunks_r / run)
+// runs of `run` chunks (the last one shorter), and the runs are numbered in
+// record order.  Wave 0 finds b's record with a prefix sum over the records'
+// run counts; the record's lookup tables are staged into LDS once and up to
+// 16 waves (8 for eight lanes per thread) then take the run's chunks in turn.
 template <int R>
-__global__ __launch_bounds__(1024) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(R == 8 ? 512 : 1024) void decode_kernel(const DecodeArgs a) {
     // static allocation: the LDS base is a compile-time constant, so table and
     // ring addresses fold into the instructions' offsets
-    __shared__ __align__(16) uint8_t lds[kLutLds + kMaxWaves * kRingBytes];
-    const TaskDev tk = a.tasks[a.task_begin + blockIdx.x];
-    const RecDev r = a.recs[tk.rec];
-    // stage the record's lookup tables into LDS
-    {
-        const uint4* src = (const uint4*)(a.luts + r.lut_off);
-        const uint32_t ns16 = (8u << r.m_s) / 16;
-        uint4* d = (uint4*)(lds + kSlutOff);
-        for (uint32_t i = threadIdx.x; i < ns16; i += blockDim.x) d[i] = src[i];
-        const uint32_t nf16 = (r.n_tables + 1) * (kFPage / 16);
-        const uint4* fs = src + ns16;
-        uint4* fd = (uint4*)(lds + kFlutOff);
-        for (uint32_t i = threadIdx.x; i < nf16; i += blockDim.x) fd[i] = fs[i];
+    __shared__ __align__(16) uint8_t lds[kLutLds + max_waves(R) * ring_bytes(R)];
+    __shared__ uint32_t pick[2];
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t b = blockIdx.x;
+    if (wave == 0) {
+        const uint32_t lane = threadIdx.x & 63;
+        uint32_t carry = 0, e = UINT32_MAX, j = 0;
+        for (uint32_t base = a.i0; base < a.i1; base += 64) {
+            const uint32_t i = base + lane;
+            uint32_t k = 0;
+            if (i < a.i1) k = (a.cls.start[i + 1] - a.cls.start[i] + a.run - 1) / a.run;
+            uint32_t incl = k;
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t v = __shfl_up(incl, d, 64);
+                if (lane >= (uint32_t)d) incl += v;
+            }
+            const uint32_t excl = carry + incl - k;
+            const unsigned long long hit = __ballot(k != 0 && excl <= b && b < excl + k);
+            if (hit) {
+                const int src = __ffsll(hit) - 1;
+                e = __shfl(i, src, 64);
+                j = b - __shfl(excl, src, 64);
+                break;
+            }
+            carry += __shfl(incl, 63, 64);
+        }
+        if (lane == 0) { pick[0] = e; pick[1] = j; }
     }
     __syncthreads();
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (wave >= tk.nc) return;
-    decode_chunk<R>(a, r, tk.c0 + wave, wave, lds);
+    // the picked run is the same for every wave: keep it in scalar registers
+    const uint32_t e = __builtin_amdgcn_readfirstlane(pick[0]);
+    if (e == UINT32_MAX) return;   // no run for this workgroup (launch larger than the runs)
+    const RecDev r = a.recs[a.cls.recs[e]];
+    const uint32_t c0 = __builtin_amdgcn_readfirstlane(pick[1]) * a.run;
+    const uint32_t c1 = min(r.n_chunks, c0 + a.run);
+    stage_luts(a, r, lds);
+    __syncthreads();
+    for (uint32_t ch = c0 + wave; ch < c1; ch += a.waves) decode_chunk<R>(a, r, ch, wave, lds);
 }
 
 // ------------------------------------------------------------------ residual and compare
@@ -528,13 +571,15 @@ int bsk_build_luts(const uint8_t* d_container, const RecDev* d_recs, uint32_t n_
     return (int)hipGetLastError();
 }
 
-int bsk_decode(const DecodeArgs* args, uint32_t n_tasks, uint32_t lanes_per_thread, void* stream) {
-    if (n_tasks == 0) return 0;
-    const dim3 grid(n_tasks), block(64 * args->waves);
+int bsk_decode(const DecodeArgs* args, uint32_t n_groups, uint32_t lanes_per_thread, void* stream) {
+    if (n_groups == 0) return 0;
+    const dim3 grid(n_groups), block(64 * args->waves);
     hipStream_t st = (hipStream_t)stream;
+    if (args->waves == 0 || args->waves > max_waves(lanes_per_thread)) return (int)hipErrorInvalidValue;
     if (lanes_per_thread == 1) hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, st, *args);
     else if (lanes_per_thread == 2) hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, st, *args);
-    else hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, st, *args);
+    else if (lanes_per_thread == 4) hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, st, *args);
+    else hipLaunchKernelGGL(decode_kernel<8>, grid, block, 0, st, *args);
     return (int)hipGetLastError();
 }
 

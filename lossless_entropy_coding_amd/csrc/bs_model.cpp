@@ -41,8 +41,8 @@ const char* last_error() { return g_err.c_str(); }
 bool params_ok(const bs_params* p) {
     if (!p) { set_error("params is NULL"); return false; }
     const uint32_t K = p->lanes;
-    if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256)) {
-        set_error("lanes must be a power of two in 1..64, or 128 or 256 (got %u)", K);
+    if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256 || K == 512)) {
+        set_error("lanes must be a power of two in 1..64, or 128, 256 or 512 (got %u)", K);
         return false;
     }
     if (p->chunk_weights == 0 || p->chunk_weights % (8 * K)) {

@@ -1,11 +1,13 @@
 // bs_plan.cpp -- decode plans, the decode entry point and verification.
 //
-// A plan holds, in device memory, the validated work list of a container
-// (one entry per workgroup: a record and up to `waves` of its chunks, one
-// chunk per wave) and each record's decode lookup tables, built once by a HIP
-// kernel.  Decoding a record range is then one kernel launch for the BF16
-// records plus one for the verbatim residual spans [Qwen3.8-27B-BF16-NVLC-
-// Lossless card, codec paragraph: the residual keeps non-BF16 spans].
+// A plan holds, in device memory, the validated record descriptors of a
+// container, grouped by lanes-per-thread class with each class's running chunk
+// count, and each record's decode lookup tables, built once by a HIP kernel.
+// Decoding a record range is then one kernel launch per class present (each
+// workgroup takes a run of chunks inside one record) plus
+// one for the verbatim residual spans [Qwen3.8-27B-BF16-NVLC-Lossless card,
+// codec paragraph: the residual keeps non-BF16 spans].  A decode call uploads
+// nothing.
 // Verification re-reads the per-chunk status, compares bytes on the device and
 // checks each record's sha256 [Gemma 2 9B Instruct -- Lossless Compressed
 // card, "What lossless means": every tensor is hash-checked at decompression].
@@ -27,17 +29,18 @@ struct bs_plan {
     const uint8_t* d_container = nullptr;
     uint64_t len = 0;
     Container c;
-    // one work list per lanes-per-thread class (1, 2, 4): each class is its
-    // own kernel instantiation with its own workgroup size
-    static constexpr int kClasses = 3;
-    uint32_t waves[kClasses] = {1, 1, 1};
+    // one record list per lanes-per-thread class: each class is its own
+    // kernel instantiation with its own workgroup size
+    static constexpr int kClasses = 4;   // R = 1, 2, 4, 8
+    int cus = 256;
     std::vector<uint32_t> dev_index;   // record -> index in d_recs (BF16) or d_raws (RAW)
     std::vector<uint32_t> rclass;      // record -> class (BF16)
-    std::vector<uint32_t> task_first, task_count;   // within the record's class list
-    std::vector<bsd::TaskDev> tasks[kClasses];
+    std::vector<uint32_t> cls_pos;     // record -> entry in its class list (BF16)
+    std::vector<uint32_t> cls_recs[kClasses], cls_start[kClasses];
     std::vector<bsd::RawDev> raws;
     bsd::RecDev* d_recs = nullptr;
-    bsd::TaskDev* d_tasks[kClasses] = {nullptr, nullptr, nullptr};
+    uint32_t* d_cls_recs[kClasses] = {nullptr, nullptr, nullptr, nullptr};
+    uint32_t* d_cls_start[kClasses] = {nullptr, nullptr, nullptr, nullptr};
     bsd::RawDev* d_raws = nullptr;
     uint8_t* d_luts = nullptr;
     unsigned long long* d_cmp = nullptr;   // compare results (2 words)
@@ -48,8 +51,10 @@ namespace {
 void plan_free(bs_plan* p) {
     if (!p) return;
     if (p->d_recs) (void)hipFree(p->d_recs);
-    for (auto* t : p->d_tasks)
-        if (t) (void)hipFree(t);
+    for (int k = 0; k < bs_plan::kClasses; k++) {
+        if (p->d_cls_recs[k]) (void)hipFree(p->d_cls_recs[k]);
+        if (p->d_cls_start[k]) (void)hipFree(p->d_cls_start[k]);
+    }
     if (p->d_raws) (void)hipFree(p->d_raws);
     if (p->d_luts) (void)hipFree(p->d_luts);
     if (p->d_cmp) (void)hipFree(p->d_cmp);
@@ -61,24 +66,55 @@ bs_status hip_err(hipError_t e, const char* what) {
     return BS_E_HIP;
 }
 
-// records [first, first+count) -> contiguous task range of each class and the raw range
-void ranges(const bs_plan* p, uint32_t first, uint32_t count, uint32_t* t0, uint32_t* t1, uint32_t& r0,
+// records [first, first+count) -> the run of class entries [e0, e1) of each
+// class (class lists keep container order) and the residual range [r0, r1)
+void ranges(const bs_plan* p, uint32_t first, uint32_t count, uint32_t* e0, uint32_t* e1, uint32_t& r0,
             uint32_t& r1) {
     r0 = r1 = 0;
-    bool have_t[bs_plan::kClasses] = {false, false, false}, have_r = false;
-    for (int k = 0; k < bs_plan::kClasses; k++) t0[k] = t1[k] = 0;
+    bool have_e[bs_plan::kClasses] = {false, false, false, false}, have_r = false;
+    for (int k = 0; k < bs_plan::kClasses; k++) e0[k] = e1[k] = 0;
     for (uint32_t i = first; i < first + count; i++) {
         const Record& r = p->c.recs[i];
         if (r.kind == BS_KIND_BF16) {
-            if (!p->task_count[i]) continue;
             const uint32_t k = p->rclass[i];
-            if (!have_t[k]) { t0[k] = p->task_first[i]; have_t[k] = true; }
-            t1[k] = p->task_first[i] + p->task_count[i];
+            if (!have_e[k]) { e0[k] = p->cls_pos[i]; have_e[k] = true; }
+            e1[k] = p->cls_pos[i] + 1;
         } else {
             if (!have_r) { r0 = p->dev_index[i]; have_r = true; }
             r1 = p->dev_index[i] + 1;
         }
     }
+}
+
+// Launch shape for the class entries [e0, e1) of class k: every record is cut
+// into runs of `run` chunks, one workgroup per run (a workgroup's tables and
+// rings fill most of a CU's LDS, so one workgroup runs per CU).  `run` is the
+// smallest length whose run count fits the CUs; when the records alone
+// outnumber the CUs, runs are sized to the average share of a CU.
+void launch_shape(const bs_plan* p, int k, uint32_t e0, uint32_t e1, uint32_t& waves, uint32_t& run,
+                  uint32_t& groups) {
+    const std::vector<uint32_t>& st = p->cls_start[k];
+    const uint32_t total = st[e1] - st[e0];
+    uint32_t biggest = 0;
+    for (uint32_t e = e0; e < e1; e++) biggest = std::max(biggest, st[e + 1] - st[e]);
+    auto count = [&](uint32_t len) {
+        uint64_t g = 0;
+        for (uint32_t e = e0; e < e1; e++) g += (st[e + 1] - st[e] + len - 1) / len;
+        return g;
+    };
+    const uint32_t cus = (uint32_t)p->cus;
+    uint32_t lo = std::max<uint32_t>(1, (total + cus - 1) / cus), hi = std::max(lo, biggest);
+    if (count(hi) > cus) {
+        run = lo;
+    } else {
+        while (lo < hi) {
+            const uint32_t mid = lo + (hi - lo) / 2;
+            if (count(mid) <= cus) hi = mid; else lo = mid + 1;
+        }
+        run = lo;
+    }
+    groups = (uint32_t)count(run);
+    waves = std::min<uint32_t>(bsd::max_waves(1u << k), run);
 }
 
 uint64_t out_extent(const bs_plan* p, uint32_t first, uint32_t count) {
@@ -111,27 +147,15 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
     if (e != hipSuccess) { plan_free(p); return hip_err(e, "hipGetDevice"); }
     int cus = 0;
     if (bsk_device_cus(&cus) != 0 || cus <= 0) cus = 256;
+    p->cus = cus;
     const uint32_t n = p->c.n_records;
-    // chunks per class decide the workgroup size: enough workgroups to cover
-    // the CUs, at most 16 waves
-    uint64_t class_chunks[bs_plan::kClasses] = {0, 0, 0};
-    p->rclass.assign(n, 0);
-    for (uint32_t i = 0; i < n; i++) {
-        const Record& r = p->c.recs[i];
-        if (r.kind != BS_KIND_BF16) continue;
-        const uint32_t R = r.K <= 64 ? 1 : r.K / 64;
-        p->rclass[i] = R == 1 ? 0 : R == 2 ? 1 : 2;
-        class_chunks[p->rclass[i]] += r.n_chunks;
-    }
-    for (int k = 0; k < bs_plan::kClasses; k++) {
-        p->waves[k] = (uint32_t)std::min<uint64_t>(bsd::kMaxWaves, std::max<uint64_t>(1, (class_chunks[k] + cus - 1) / cus));
-    }
-
+    if (p->c.n_chunks > 0xFFFFFFFFull) { plan_free(p); set_error("too many chunks"); return BS_E_FORMAT; }
     std::vector<bsd::RecDev> recs;
     uint64_t lut_bytes = 0;
     p->dev_index.assign(n, 0);
-    p->task_first.assign(n, 0);
-    p->task_count.assign(n, 0);
+    p->rclass.assign(n, 0);
+    p->cls_pos.assign(n, 0);
+    for (int k = 0; k < bs_plan::kClasses; k++) p->cls_start[k].push_back(0);
     for (uint32_t i = 0; i < n; i++) {
         const Record& r = p->c.recs[i];
         if (r.kind == BS_KIND_RAW) {
@@ -159,15 +183,14 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
         d.route_off = r.route_off;
         d.ftab_off = r.ftab_off;
         lut_bytes += (8ull << r.m_s) + (r.n_tables + 1ull) * bsd::kFPage;
-        const uint32_t k = p->rclass[i];
-        std::vector<bsd::TaskDev>& tl = p->tasks[k];
-        p->task_first[i] = (uint32_t)tl.size();
-        for (uint32_t c0 = 0; c0 < r.n_chunks; c0 += p->waves[k])
-            tl.push_back({(uint32_t)recs.size(), c0, std::min(p->waves[k], r.n_chunks - c0), 0});
-        p->task_count[i] = (uint32_t)tl.size() - p->task_first[i];
+        const uint32_t R = d.lanes_per_thread;
+        const uint32_t k = R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : 3;
+        p->rclass[i] = k;
+        p->cls_pos[i] = (uint32_t)p->cls_recs[k].size();
+        p->cls_recs[k].push_back((uint32_t)recs.size());
+        p->cls_start[k].push_back(p->cls_start[k].back() + r.n_chunks);
         recs.push_back(d);
     }
-    if (p->c.n_chunks > 0xFFFFFFFFull) { plan_free(p); set_error("too many chunks"); return BS_E_FORMAT; }
     hipStream_t s = (hipStream_t)stream;
     auto up = [&](void** dst, const void* src, size_t bytes) -> hipError_t {
         hipError_t ee = hipMalloc(dst, std::max<size_t>(bytes, 16));
@@ -175,8 +198,10 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
         return hipMemcpyAsync(*dst, src, bytes, hipMemcpyHostToDevice, s);
     };
     e = up((void**)&p->d_recs, recs.data(), recs.size() * sizeof(bsd::RecDev));
-    for (int k = 0; k < bs_plan::kClasses && e == hipSuccess; k++)
-        e = up((void**)&p->d_tasks[k], p->tasks[k].data(), p->tasks[k].size() * sizeof(bsd::TaskDev));
+    for (int k = 0; k < bs_plan::kClasses && e == hipSuccess; k++) {
+        e = up((void**)&p->d_cls_recs[k], p->cls_recs[k].data(), p->cls_recs[k].size() * 4);
+        if (e == hipSuccess) e = up((void**)&p->d_cls_start[k], p->cls_start[k].data(), p->cls_start[k].size() * 4);
+    }
     if (e == hipSuccess) e = up((void**)&p->d_raws, p->raws.data(), p->raws.size() * sizeof(bsd::RawDev));
     if (e == hipSuccess) e = hipMalloc(&p->d_luts, std::max<uint64_t>(lut_bytes, 16));
     if (e == hipSuccess) e = hipMalloc(&p->d_cmp, 2 * sizeof(unsigned long long));
@@ -197,8 +222,12 @@ void bs_plan_destroy(bs_plan* plan) { plan_free(plan); }
 uint32_t bs_plan_waves_per_block(const bs_plan* plan) {
     if (!plan) return 0;
     uint32_t w = 0;
-    for (int k = 0; k < bs_plan::kClasses; k++)
-        if (!plan->tasks[k].empty()) w = std::max(w, plan->waves[k]);
+    for (int k = 0; k < bs_plan::kClasses; k++) {
+        if (!plan->cls_start[k].back()) continue;
+        uint32_t waves, run, groups;
+        launch_shape(plan, k, 0, (uint32_t)plan->cls_recs[k].size(), waves, run, groups);
+        w = std::max(w, waves);
+    }
     return w;
 }
 
@@ -221,22 +250,26 @@ bs_status bs_decode_async(const bs_plan* p, uint32_t first, uint32_t count, void
     }
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != p->device) { set_error("plan belongs to device %d", p->device); return BS_E_INVAL; }
-    uint32_t t0[bs_plan::kClasses], t1[bs_plan::kClasses], r0, r1;
-    ranges(p, first, count, t0, t1, r0, r1);
+    uint32_t e0[bs_plan::kClasses], e1[bs_plan::kClasses], r0, r1;
+    ranges(p, first, count, e0, e1, r0, r1);
     const uint64_t out_base = p->c.recs[first].out_offset;
     for (int k = 0; k < bs_plan::kClasses; k++) {
-        if (t1[k] <= t0[k]) continue;
+        if (e1[k] <= e0[k]) continue;
+        if (p->cls_start[k][e1[k]] <= p->cls_start[k][e0[k]]) continue;
         bsd::DecodeArgs a{};
         a.container = p->d_container;
         a.recs = p->d_recs;
-        a.tasks = p->d_tasks[k];
+        a.cls.recs = p->d_cls_recs[k];
+        a.cls.start = p->d_cls_start[k];
         a.luts = p->d_luts;
         a.out = (uint8_t*)d_out;
         a.status = d_status;
         a.out_base = out_base;
-        a.task_begin = t0[k];
-        a.waves = p->waves[k];
-        int e = bsk_decode(&a, t1[k] - t0[k], k == 0 ? 1 : k == 1 ? 2 : 4, stream);
+        a.i0 = e0[k];
+        a.i1 = e1[k];
+        uint32_t groups;
+        launch_shape(p, k, e0[k], e1[k], a.waves, a.run, groups);
+        int e = bsk_decode(&a, groups, 1u << k, stream);
         if (e) return hip_err((hipError_t)e, "decode launch");
     }
     if (r1 > r0) {

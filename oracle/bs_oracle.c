@@ -567,7 +567,7 @@ int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* 
                          uint32_t Wmax, uint32_t Kmax, uint32_t M_s, uint32_t M_f, uint32_t cmax,
                          uint8_t** out, uint64_t* out_len) {
     if (M_s < 9 || M_s > 12 || M_f < 7 || M_f > 10 || cmax > BSO_MAX_TABLES) return BSO_EINVAL;
-    if (!(Kmax <= 64 || Kmax == 128 || Kmax == 256) || Kmax == 0) return BSO_EINVAL;
+    if (!(Kmax <= 64 || Kmax == 128 || Kmax == 256 || Kmax == 512) || Kmax == 0) return BSO_EINVAL;
     if ((Kmax & (Kmax - 1)) != 0) return BSO_EINVAL;
     bytebuf c = {0, 0, 0};
     uint64_t dir = BSO_HDR_BYTES;
@@ -658,7 +658,7 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md
     if (md->M_s < 9 || md->M_s > 12 || md->M_f < 7 || md->M_f > 10 || md->n_tables > BSO_MAX_TABLES)
         return BSO_EFORMAT;
     if (*K == 0 || *W == 0 || *W % (8 * *K)) return BSO_EFORMAT;
-    if (!(*K <= 64 || *K == 128 || *K == 256)) return BSO_EFORMAT;
+    if (!(*K <= 64 || *K == 128 || *K == 256 || *K == 512)) return BSO_EFORMAT;
     if (*n_chunks != (n + *W - 1) / *W) return BSO_EFORMAT;
     if (n_sym > BSO_MAX_SYMS || (n_sym == 0) != (n == 0)) return BSO_EFORMAT;
     uint64_t off = 24;

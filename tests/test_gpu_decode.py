@@ -56,6 +56,9 @@ CASES = [
     ("k256_full", 4 * 131072, 0.02, 131072, 256),
     ("k256_ragged", 131072 + 2049 + 7, 0.1, 131072, 256),
     ("small_k_tiny_chunks", 5000, 0.02, 512, 4),
+    ("k512_full", 2 * 262144, 0.02, 262144, 512),
+    ("k512_ragged", 262144 + 4096 * 3 + 5, 0.05, 262144, 512),
+    ("k512_one_chunk_short", 70001, 0.02, 262144, 512),
 ]
 
 
@@ -99,6 +102,37 @@ def test_special_values_and_residual():
         ri = codec.record_info(c, i)
         nb = 2 * ri.n if ri.kind == L.KIND_BF16 else ri.n
         assert host[ri.out_offset: ri.out_offset + nb] == expect[ri.out_offset: ri.out_offset + nb], i
+
+
+def test_many_records_mixed_lane_classes():
+    """Hundreds of records of ragged sizes in one container: small records get
+    fewer lanes (other lanes-per-thread classes) and the persistent workgroups'
+    chunk runs cross record boundaries, re-staging the lookup tables."""
+    say("many records, mixed classes")
+    rng = np.random.default_rng(11)
+    sizes = list(rng.integers(1, 3000, 700)) + list(rng.integers(3000, 140000, 60)) + [0, 8, 131072, 262144 + 17]
+    rng.shuffle(sizes)
+    tensors = []
+    for i, n in enumerate(sizes):
+        x = rng.standard_normal(int(n)) * float(rng.choice([0.003, 0.02, 0.08]))
+        tensors.append(codec.bf16(_words(x)))
+        if i % 37 == 0:
+            tensors.append(codec.raw(rng.integers(0, 256, int(rng.integers(1, 5000)), dtype=np.uint8)))
+    c = codec.encode(tensors, codec.params(chunk_weights=131072, lanes=256))
+    info = codec.container_info(c)
+    ris = [codec.record_info(c, i) for i in range(info.n_records)]
+    ks = {ri.lanes for ri in ris if ri.kind == L.KIND_BF16 and ri.n}
+    assert len({max(k // 64, 1) for k in ks}) >= 3, ks
+    expect = _expected_bytes(c)
+    plan, out, rc, rep, got = _decode_check(c, expect)
+    assert rc == L.BS_OK, rep
+    assert got == expect
+    # a middle sub-range decodes to the same bytes as in the full decode
+    first, count = 50, 400
+    sub = plan.decode(first, count)
+    torch.cuda.synchronize()
+    for i in range(first, first + count):
+        assert torch.equal(codec.record_output(sub, plan, i, first), codec.record_output(out, plan, i, 0)), i
 
 
 def test_record_range_and_determinism():

@@ -45,7 +45,8 @@ def _same(tensors_o, tensors_l, **kw):
 
 
 @pytest.mark.parametrize("seed,n,W,K", [(0, 100000, 4096, 8), (1, 33333, 2048, 16), (2, 8, 64, 1), (3, 0, 64, 2),
-                                        (4, 70000, 65536, 128), (5, 5000, 65536, 256), (6, 262144, 131072, 256)])
+                                        (4, 70000, 65536, 128), (5, 5000, 65536, 256), (6, 262144, 131072, 256),
+                                        (7, 300000, 262144, 512)])
 def test_encoder_bytes_match_oracle(seed, n, W, K):
     rng = np.random.default_rng(seed)
     w = _words(rng.standard_normal(n) * rng.choice([0.004, 0.02, 0.1]))
@@ -145,7 +146,7 @@ def test_validation_errors():
 
 def test_bad_params_rejected():
     w = np.zeros(100, np.uint16)
-    for kw in [dict(lanes=3), dict(lanes=96), dict(chunk_weights=100, lanes=8), dict(m_s=13), dict(m_f=6),
+    for kw in [dict(lanes=3), dict(lanes=96), dict(lanes=1024, chunk_weights=1 << 20), dict(chunk_weights=100, lanes=8), dict(m_s=13), dict(m_f=6),
                dict(max_tables=7)]:
         with pytest.raises(L.BSError) as e:
             codec.encode([codec.bf16(w)], codec.params(**kw))

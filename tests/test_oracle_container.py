@@ -88,7 +88,7 @@ def test_every_bf16_bit_pattern_roundtrips():
     assert int.from_bytes(c[64:68], "little") == O.KIND_BF16
 
 
-@pytest.mark.parametrize("K", [1, 2, 3, 8, 32, 64, 128])
+@pytest.mark.parametrize("K", [1, 2, 3, 8, 32, 64, 128, 256, 512])
 def test_edge_sizes_roundtrip(K):
     if K == 3:
         with pytest.raises(O.OracleError):
