@@ -62,3 +62,35 @@ def test_config4_full_size():
         got = out[2 * a: 2 * (a + o.size)].cpu().numpy().view(np.uint16)
         assert np.array_equal(got, o), ch
     assert enc.bits_per_weight <= 1.01 * enc.entropy_bits, (enc.bits_per_weight, enc.entropy_bits)
+
+
+def test_config5_layers_into_one_buffer():
+    """Config 5 in the benchmark's launch configuration, cut to its first
+    decoder layer plus the trailing vectors (the full run repeats the same
+    layer shapes 84 times): every layer container resident in HBM, decoded
+    in order into one reused buffer, each layer compared on the device with
+    its original words, and a sample of chunks against the oracle."""
+    from lossless_entropy_coding_amd import checkpoint
+    say("config 5, one layer + tail")
+    job = checkpoint.build_job(layers=1, log=say)
+    assert len(job.plans) == 2
+    job.decode()
+    torch.cuda.synchronize()
+    ok, bad = job.verify()
+    assert ok, bad
+    c = job.first_container
+    plan = job.plans[0]
+    plan.decode_into(job.out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    info = codec.container_info(c)
+    for i in sorted(rng.choice(info.n_records, 4, replace=False).tolist()):
+        ri = codec.record_info(c, i)
+        if ri.kind != L.KIND_BF16 or ri.n_chunks == 0:
+            continue
+        for ch in sorted({0, ri.n_chunks - 1, int(rng.integers(ri.n_chunks))}):
+            o = O.decode_chunk(c, i, ch)
+            a = ri.out_offset + 2 * ch * ri.chunk_weights
+            got = job.out[a: a + 2 * o.size].cpu().numpy().view(np.uint16)
+            assert np.array_equal(got, o), (i, ch)
+    assert job.bits_per_weight <= 1.01 * job.entropy_bits, (job.bits_per_weight, job.entropy_bits)
