@@ -386,6 +386,10 @@ int bso_sched_decode(uint32_t K, uint32_t nsteps, const int32_t* active, const u
 /* l = g mod K, macro-step t = g / K.  A lane's symbols are, for t then p    */
 /* ascending, the s symbol of the weight followed by its f symbol.  The      */
 /* sub-step is (t, p, phase); lane l takes part iff 8(tK + l) + p < n_c.     */
+/* The K lanes are split into S streams of P = K/S consecutive lanes; each   */
+/* stream has its own word sequence, in which a sub-step's refills come in   */
+/* ascending lane order.  The coder below handles the lanes [l0, l1) of one  */
+/* stream.                                                                   */
 /* ------------------------------------------------------------------------ */
 typedef struct {
     uint32_t M_s, M_f;
@@ -396,15 +400,15 @@ typedef struct {
 } bso_model;
 
 static int chunk_encode(const bso_model* md, const uint16_t* w, uint32_t n_c, uint32_t K,
-                        uint32_t* states, wordlist* wl) {
+                        uint32_t l0, uint32_t l1, uint32_t* states, wordlist* wl) {
     bso_table ts = { md->M_s, 512, md->qs };
     uint32_t groups = (n_c + 7) / 8;
     uint32_t T = (groups + K - 1) / K;
-    for (uint32_t l = 0; l < K; l++) states[l] = BSO_L;
+    for (uint32_t l = l0; l < l1; l++) states[l] = BSO_L;
     for (int64_t t = (int64_t)T - 1; t >= 0; t--) {
         for (int p = 7; p >= 0; p--) {
             for (int phase = 1; phase >= 0; phase--) {
-                for (int64_t l = (int64_t)K - 1; l >= 0; l--) {
+                for (int64_t l = (int64_t)l1 - 1; l >= (int64_t)l0; l--) {
                     uint64_t j = 8 * ((uint64_t)t * K + (uint64_t)l) + (uint64_t)p;
                     if (j >= n_c) continue;
                     uint32_t s = bso_symbol_s(w[j]);
@@ -424,20 +428,20 @@ static int chunk_encode(const bso_model* md, const uint16_t* w, uint32_t n_c, ui
 }
 
 static int chunk_decode(const bso_model* md, const uint32_t* states_in, const uint16_t* words,
-                        uint64_t nw, uint32_t n_c, uint32_t K, uint16_t* out) {
+                        uint64_t nw, uint32_t n_c, uint32_t K, uint32_t l0, uint32_t l1, uint16_t* out) {
     bso_table ts = { md->M_s, 512, md->qs };
     uint32_t groups = (n_c + 7) / 8;
     uint32_t T = (groups + K - 1) / K;
     uint32_t* x = (uint32_t*)malloc(sizeof(uint32_t) * K);
     uint32_t* s_now = (uint32_t*)malloc(sizeof(uint32_t) * K);
     if (!x || !s_now) { free(x); free(s_now); return BSO_ENOMEM; }
-    for (uint32_t l = 0; l < K; l++) x[l] = states_in[l];
+    for (uint32_t l = l0; l < l1; l++) x[l] = states_in[l];
     uint64_t pos = 0;
     int rc = BSO_OK;
     for (uint32_t t = 0; t < T && !rc; t++) {
         for (uint32_t p = 0; p < 8 && !rc; p++) {
             for (int phase = 0; phase < 2 && !rc; phase++) {
-                for (uint32_t l = 0; l < K && !rc; l++) {
+                for (uint32_t l = l0; l < l1 && !rc; l++) {
                     uint64_t j = 8 * ((uint64_t)t * K + l) + p;
                     if (j >= n_c) continue;
                     uint32_t sym;
@@ -453,8 +457,8 @@ static int chunk_decode(const bso_model* md, const uint32_t* states_in, const ui
             }
         }
     }
-    /* the encoder started every lane at L, so a whole chunk must end there */
-    for (uint32_t l = 0; l < K && !rc; l++) if (x[l] != BSO_L) rc = BSO_ECORRUPT;
+    /* the encoder started every lane at L, so a whole stream must end there */
+    for (uint32_t l = l0; l < l1 && !rc; l++) if (x[l] != BSO_L) rc = BSO_ECORRUPT;
     if (!rc && pos != nw) rc = BSO_ECORRUPT;
     free(x); free(s_now);
     return rc;
@@ -479,11 +483,15 @@ static int bb_reserve(bytebuf* b, uint64_t need) {
 /* ------------------------------------------------------------------------ */
 /* Encode one BF16 record body.                                              */
 /* ------------------------------------------------------------------------ */
-static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32_t Kmax,
+static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32_t Kmax, uint32_t Pmax,
                             uint32_t M_s, uint32_t M_f, uint32_t cmax, bytebuf* body) {
     uint32_t W, K;
     int rc = bso_record_shape(n, Wmax, Kmax, &W, &K);
     if (rc) return rc;
+    /* streams per chunk: the record's lanes in groups of at most Pmax */
+    uint32_t P = K < Pmax ? K : Pmax;
+    uint32_t S = K / P, log2S = 0;
+    while ((1u << log2S) < S) log2S++;
     bso_model* md = (bso_model*)calloc(1, sizeof(bso_model));
     uint64_t* cs = (uint64_t*)calloc(512, sizeof(uint64_t));
     uint64_t* cf = (uint64_t*)calloc(512 * 128, sizeof(uint64_t));
@@ -512,7 +520,7 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
     body->n = payload_off;
     uint8_t* b = body->p;
     put32(b + 0, W); put32(b + 4, K); put32(b + 8, (uint32_t)n_chunks);
-    b[12] = (uint8_t)M_s; b[13] = (uint8_t)M_f; b[14] = (uint8_t)md->n_tables; b[15] = 0;
+    b[12] = (uint8_t)M_s; b[13] = (uint8_t)M_f; b[14] = (uint8_t)md->n_tables; b[15] = (uint8_t)log2S;
     put32(b + 16, n_sym); put32(b + 20, 0);
     uint64_t k = 0;
     for (uint32_t s = 0; s < 512; s++) {
@@ -526,28 +534,43 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
     for (uint32_t t = 1; t <= md->n_tables; t++)
         for (uint32_t f = 0; f < 128; f++) put16(b + ft + 256ull * (t - 1) + 2 * f, md->qf[t][f]);
 
-    /* chunks */
+    /* chunks: states of all K lanes, then (S > 1) the S stream word counts,
+       then each stream's words; every part padded to 16 bytes */
     uint32_t* states = (uint32_t*)malloc(sizeof(uint32_t) * K);
-    if (!states) { rc = BSO_ENOMEM; goto done; }
+    wordlist* wls = (wordlist*)calloc(S, sizeof(wordlist));
+    if (!states || !wls) { free(states); free(wls); rc = BSO_ENOMEM; goto done; }
     for (uint64_t c = 0; c < n_chunks && !rc; c++) {
         uint32_t n_c = (uint32_t)((n - c * W) < W ? (n - c * W) : W);
-        wordlist wl = {0, 0, 0};
-        rc = chunk_encode(md, w + c * W, n_c, K, states, &wl);
-        if (rc) { free(wl.w); break; }
+        for (uint32_t st = 0; st < S; st++) wls[st].n = 0;
+        for (uint32_t st = 0; st < S && !rc; st++)
+            rc = chunk_encode(md, w + c * W, n_c, K, st * P, (st + 1) * P, states, &wls[st]);
+        if (rc) break;
         uint64_t start = body->n;
         uint64_t states_bytes = round_up(4ull * K, 16);
-        uint64_t end = start + states_bytes + round_up(2 * wl.n, 16);
+        uint64_t counts_bytes = S > 1 ? round_up(4ull * S, 16) : 0;
+        uint64_t end = start + states_bytes + counts_bytes, total_words = 0;
+        for (uint32_t st = 0; st < S; st++) { end += round_up(2 * wls[st].n, 16); total_words += wls[st].n; }
         rc = bb_reserve(body, end);
-        if (rc) { free(wl.w); break; }
+        if (rc) break;
         b = body->p;
+        memset(b + start, 0, end - start);
         put64(b + index_off + 16 * c, start);
-        put32(b + index_off + 16 * c + 8, (uint32_t)wl.n);
+        put32(b + index_off + 16 * c + 8, (uint32_t)total_words);
         put32(b + index_off + 16 * c + 12, 0);
         for (uint32_t l = 0; l < K; l++) put32(b + start + 4ull * l, states[l]);
-        for (uint64_t i = 0; i < wl.n; i++) put16(b + start + states_bytes + 2 * i, wl.w[wl.n - 1 - i]);
+        uint64_t at = start + states_bytes;
+        if (S > 1)
+            for (uint32_t st = 0; st < S; st++) put32(b + at + 4ull * st, (uint32_t)wls[st].n);
+        at += counts_bytes;
+        for (uint32_t st = 0; st < S; st++) {
+            /* the encoder pushes words in reverse order of their use */
+            for (uint64_t i = 0; i < wls[st].n; i++) put16(b + at + 2 * i, wls[st].w[wls[st].n - 1 - i]);
+            at += round_up(2 * wls[st].n, 16);
+        }
         body->n = end;
-        free(wl.w);
     }
+    for (uint32_t st = 0; st < S; st++) free(wls[st].w);
+    free(wls);
     free(states);
 done:
     free(md); free(cs); free(cf);
@@ -564,11 +587,12 @@ done:
 /* ------------------------------------------------------------------------ */
 int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* const* data,
                          const uint64_t* n, const uint8_t* sha,
-                         uint32_t Wmax, uint32_t Kmax, uint32_t M_s, uint32_t M_f, uint32_t cmax,
+                         uint32_t Wmax, uint32_t Kmax, uint32_t Pmax, uint32_t M_s, uint32_t M_f, uint32_t cmax,
                          uint8_t** out, uint64_t* out_len) {
     if (M_s < 9 || M_s > 12 || M_f < 7 || M_f > 10 || cmax > BSO_MAX_TABLES) return BSO_EINVAL;
     if (!(Kmax <= 64 || Kmax == 128 || Kmax == 256 || Kmax == 512) || Kmax == 0) return BSO_EINVAL;
     if ((Kmax & (Kmax - 1)) != 0) return BSO_EINVAL;
+    if (Pmax == 0 || (Pmax & (Pmax - 1)) != 0 || Pmax > Kmax) return BSO_EINVAL;
     bytebuf c = {0, 0, 0};
     uint64_t dir = BSO_HDR_BYTES;
     uint64_t pos = round_up(dir + (uint64_t)BSO_DIR_BYTES * n_tensors, 16);
@@ -594,7 +618,7 @@ int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* 
             if (occ > BSO_MAX_SYMS) { kind = BSO_KIND_RAW; count = bytes; }
         }
         if (kind == BSO_KIND_BF16) {
-            rc = encode_bf16_body((const uint16_t*)data[i], n[i], Wmax, Kmax, M_s, M_f, cmax, &body);
+            rc = encode_bf16_body((const uint16_t*)data[i], n[i], Wmax, Kmax, Pmax, M_s, M_f, cmax, &body);
         } else if (kind == BSO_KIND_RAW) {
             rc = bb_reserve(&body, bytes ? bytes : 1);
             if (!rc) { if (bytes) memcpy(body.p, data[i], bytes); body.n = bytes; }
@@ -649,16 +673,19 @@ void bso_free(void* p) { free(p); }
 /* Returns the first error, or 0.                                            */
 /* ------------------------------------------------------------------------ */
 static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md,
-                       uint32_t* W, uint32_t* K, uint64_t* n_chunks, uint64_t* index_off) {
+                       uint32_t* W, uint32_t* K, uint32_t* S, uint64_t* n_chunks, uint64_t* index_off) {
     if (len < 24) return BSO_EFORMAT;
     *W = get32(b); *K = get32(b + 4);
     *n_chunks = get32(b + 8);
     md->M_s = b[12]; md->M_f = b[13]; md->n_tables = b[14];
+    if (b[15] > 9) return BSO_EFORMAT;
+    *S = 1u << b[15];
     uint32_t n_sym = get32(b + 16);
     if (md->M_s < 9 || md->M_s > 12 || md->M_f < 7 || md->M_f > 10 || md->n_tables > BSO_MAX_TABLES)
         return BSO_EFORMAT;
     if (*K == 0 || *W == 0 || *W % (8 * *K)) return BSO_EFORMAT;
     if (!(*K <= 64 || *K == 128 || *K == 256 || *K == 512)) return BSO_EFORMAT;
+    if (*K % *S) return BSO_EFORMAT;
     if (*n_chunks != (n + *W - 1) / *W) return BSO_EFORMAT;
     if (n_sym > BSO_MAX_SYMS || (n_sym == 0) != (n == 0)) return BSO_EFORMAT;
     uint64_t off = 24;
@@ -689,6 +716,35 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md
     return BSO_OK;
 }
 
+/* Decode chunk ch of a parsed BF16 record body b (rl bytes) into out[0..n_c). */
+static int decode_one_chunk(const bso_model* md, const uint8_t* b, uint64_t rl, uint64_t io, uint32_t K,
+                            uint32_t S, uint64_t ch, uint32_t n_c, uint16_t* out) {
+    const uint8_t* e = b + io + 16 * ch;
+    uint64_t po = get64(e), nw = get32(e + 8);
+    uint64_t sb = round_up(4ull * K, 16), cb = S > 1 ? round_up(4ull * S, 16) : 0;
+    if (po % 16 || po > rl || sb + cb > rl - po) return BSO_EFORMAT;
+    uint32_t P = K / S;
+    uint32_t* st = (uint32_t*)malloc(sizeof(uint32_t) * K);
+    if (!st) return BSO_ENOMEM;
+    for (uint32_t l = 0; l < K; l++) st[l] = get32(b + po + 4ull * l);
+    uint64_t at = po + sb + cb, total = 0;
+    int rc = BSO_OK;
+    for (uint32_t s = 0; s < S && !rc; s++) {
+        uint64_t nws = S > 1 ? get32(b + po + sb + 4ull * s) : nw;
+        total += nws;
+        if (2 * nws > rl - at) { rc = BSO_EFORMAT; break; }
+        uint16_t* words = (uint16_t*)malloc(sizeof(uint16_t) * (nws ? nws : 1));
+        if (!words) { rc = BSO_ENOMEM; break; }
+        for (uint64_t j = 0; j < nws; j++) words[j] = (uint16_t)get16(b + at + 2 * j);
+        rc = chunk_decode(md, st, words, nws, n_c, K, s * P, (s + 1) * P, out);
+        free(words);
+        at += round_up(2 * nws, 16);
+    }
+    if (!rc && total != nw) rc = BSO_EFORMAT;
+    free(st);
+    return rc;
+}
+
 int bso_decode_container(const uint8_t* c, uint64_t len, uint8_t* out, uint64_t out_cap, int32_t* rec_status) {
     if (len < BSO_HDR_BYTES || memcmp(c, BSO_MAGIC, 8) != 0) return BSO_EFORMAT;
     if (get32(c + 8) != BSO_VERSION) return BSO_EVERSION;
@@ -709,27 +765,16 @@ int bso_decode_container(const uint8_t* c, uint64_t len, uint8_t* out, uint64_t 
             else if (n) memcpy(out + oo, c + ro, n);
         } else if (kind == BSO_KIND_BF16) {
             bso_model* md = (bso_model*)calloc(1, sizeof(bso_model));
-            uint32_t W, K; uint64_t nch, io;
+            uint32_t W, K, S; uint64_t nch, io;
             if (!md) rc = BSO_ENOMEM;
-            if (!rc) rc = parse_model(c + ro, rl, n, md, &W, &K, &nch, &io);
+            if (!rc) rc = parse_model(c + ro, rl, n, md, &W, &K, &S, &nch, &io);
             if (!rc && (oo + 2 * n > out_cap || oo % 16)) rc = BSO_EFORMAT;
             uint16_t* tmp = NULL;
             if (!rc && n) { tmp = (uint16_t*)malloc(sizeof(uint16_t) * W); if (!tmp) rc = BSO_ENOMEM; }
             for (uint64_t ch = 0; ch < nch && !rc; ch++) {
-                const uint8_t* e = c + ro + io + 16 * ch;
-                uint64_t po = get64(e);
-                uint64_t nw = get32(e + 8);
-                uint64_t sb = round_up(4ull * K, 16);
-                if (po % 16 || po + sb + 2 * nw > rl) { rc = BSO_EFORMAT; break; }
                 uint32_t n_c = (uint32_t)((n - ch * W) < W ? (n - ch * W) : W);
-                uint32_t* st = (uint32_t*)malloc(sizeof(uint32_t) * K);
-                uint16_t* words = (uint16_t*)malloc(sizeof(uint16_t) * (nw ? nw : 1));
-                if (!st || !words) { free(st); free(words); rc = BSO_ENOMEM; break; }
-                for (uint32_t l = 0; l < K; l++) st[l] = get32(c + ro + po + 4ull * l);
-                for (uint64_t j = 0; j < nw; j++) words[j] = (uint16_t)get16(c + ro + po + sb + 2 * j);
-                rc = chunk_decode(md, st, words, nw, n_c, K, tmp);
+                rc = decode_one_chunk(md, c + ro, rl, io, K, S, ch, n_c, tmp);
                 if (!rc) for (uint32_t j = 0; j < n_c; j++) put16(out + oo + 2 * (ch * W + j), tmp[j]);
-                free(st); free(words);
             }
             free(tmp); free(md);
         } else {
@@ -758,32 +803,15 @@ int bso_decode_chunk(const uint8_t* c, uint64_t len, uint32_t record, uint64_t c
     if (ro > len || rl > len - ro) return BSO_EFORMAT;
     bso_model* md = (bso_model*)calloc(1, sizeof(bso_model));
     if (!md) return BSO_ENOMEM;
-    uint32_t W, K; uint64_t nch, io;
-    int rc = parse_model(c + ro, rl, n, md, &W, &K, &nch, &io);
+    uint32_t W, K, S; uint64_t nch, io;
+    int rc = parse_model(c + ro, rl, n, md, &W, &K, &S, &nch, &io);
     if (!rc && chunk >= nch) rc = BSO_EINVAL;
     uint64_t n_c = 0;
     if (!rc) {
         n_c = (n - chunk * W) < W ? (n - chunk * W) : W;
         if (n_c > out_cap) rc = BSO_ENOSPACE;
     }
-    if (!rc) {
-        const uint8_t* e = c + ro + io + 16 * chunk;
-        uint64_t po = get64(e), nw = get32(e + 8), sb = round_up(4ull * K, 16);
-        if (po % 16 || po + sb + 2 * nw > rl) rc = BSO_EFORMAT;
-        uint32_t* st = NULL;
-        uint16_t* words = NULL;
-        if (!rc) {
-            st = (uint32_t*)malloc(sizeof(uint32_t) * K);
-            words = (uint16_t*)malloc(sizeof(uint16_t) * (nw ? nw : 1));
-            if (!st || !words) rc = BSO_ENOMEM;
-        }
-        if (!rc) {
-            for (uint32_t l = 0; l < K; l++) st[l] = get32(c + ro + po + 4ull * l);
-            for (uint64_t j = 0; j < nw; j++) words[j] = (uint16_t)get16(c + ro + po + sb + 2 * j);
-            rc = chunk_decode(md, st, words, nw, (uint32_t)n_c, K, out);
-        }
-        free(st); free(words);
-    }
+    if (!rc) rc = decode_one_chunk(md, c + ro, rl, io, K, S, chunk, (uint32_t)n_c, out);
     free(md);
     *n_c_out = n_c;
     return rc;

@@ -70,7 +70,7 @@ def lib():
                                        C.c_uint64, C.c_void_p, C.c_void_p]
         l.bso_sched_decode.restype = C.c_int
         l.bso_encode_container.argtypes = [C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
-                                           C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32,
+                                           C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32,
                                            C.POINTER(C.POINTER(C.c_uint8)), u64p]
         l.bso_encode_container.restype = C.c_int
         l.bso_decode_container.argtypes = [C.c_void_p, C.c_uint64, C.c_void_p, C.c_uint64, C.c_void_p]
@@ -235,8 +235,12 @@ def sha256(t: Tensor) -> bytes:
     return hashlib.sha256(t.data.tobytes()).digest()
 
 
-def encode(tensors, W: int = 65536, K: int = 64, M_s: int = 12, M_f: int = 10, cmax: int = 6) -> bytes:
+def encode(tensors, W: int = 65536, K: int = 64, M_s: int = 12, M_f: int = 10, cmax: int = 6,
+           P: int | None = None) -> bytes:
+    """Container of the tensors: chunks of W weights with K lanes, split into
+    streams of P lanes (default: one stream of all K lanes)."""
     n = len(tensors)
+    P = K if P is None else P
     kinds = np.array([t.kind for t in tensors] or [0], np.uint32)
     counts = np.array([t.data.size for t in tensors] or [0], np.uint64)
     keep = [np.ascontiguousarray(t.data) for t in tensors]
@@ -244,7 +248,7 @@ def encode(tensors, W: int = 65536, K: int = 64, M_s: int = 12, M_f: int = 10, c
     sha = np.frombuffer(b"".join(sha256(t) for t in tensors) or b"\0" * 32, np.uint8).copy()
     out = C.POINTER(C.c_uint8)()
     out_len = C.c_uint64(0)
-    rc = lib().bso_encode_container(n, _ptr(kinds), ptrs, _ptr(counts), _ptr(sha), W, K, M_s, M_f, cmax,
+    rc = lib().bso_encode_container(n, _ptr(kinds), ptrs, _ptr(counts), _ptr(sha), W, K, P, M_s, M_f, cmax,
                                     C.byref(out), C.byref(out_len))
     if rc:
         raise OracleError(rc, "encode")

@@ -14,7 +14,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "bs_oracle.c")
-PINS = ["tests/test_oracle_coder.py", "tests/test_oracle_model.py", "tests/test_oracle_container.py"]
+PINS = ["tests/test_oracle_coder.py", "tests/test_oracle_model.py", "tests/test_oracle_container.py",
+        "tests/test_oracle_streams.py"]
 SELECT = ["-m", "not slow", "-k", "not cfg1 and not cfg2 and not gaussian and not scale_invariance"]
 
 MUTANTS = {
@@ -22,12 +23,15 @@ MUTANTS = {
     "decode_drops_cum": ("*x = t->q[s] * (*x >> t->M) + slot - cum;", "*x = t->q[s] * (*x >> t->M) + slot;"),
     "flush_off_by_one": ("if ((uint64_t)*x >= x_max) {", "if ((uint64_t)*x > x_max) {"),
     "refill_off_by_one": ("if (*x < BSO_L) {\n        if (*pos >= nw)", "if (*x <= BSO_L) {\n        if (*pos >= nw)"),
-    "chunk_lanes_ascending": ("for (int64_t l = (int64_t)K - 1; l >= 0; l--) {\n                    uint64_t j",
-                              "for (int64_t l = 0; l < (int64_t)K; l++) {\n                    uint64_t j"),
+    "chunk_lanes_ascending": ("for (int64_t l = (int64_t)l1 - 1; l >= (int64_t)l0; l--) {\n                    uint64_t j",
+                              "for (int64_t l = (int64_t)l0; l < (int64_t)l1; l++) {\n                    uint64_t j"),
     "sched_lanes_ascending": ("for (int64_t l = (int64_t)K - 1; l >= 0 && !rc; l--) {",
                               "for (int64_t l = 0; l < (int64_t)K && !rc; l++) {"),
-    "words_not_reversed": ("put16(b + start + states_bytes + 2 * i, wl.w[wl.n - 1 - i]);",
-                           "put16(b + start + states_bytes + 2 * i, wl.w[i]);"),
+    "words_not_reversed": ("put16(b + at + 2 * i, wls[st].w[wls[st].n - 1 - i]);",
+                           "put16(b + at + 2 * i, wls[st].w[i]);"),
+    "streams_swapped": ("states, &wls[st]);", "states, &wls[S - 1 - st]);"),
+    "stream_lanes_overlap": ("rc = chunk_decode(md, st, words, nws, n_c, K, s * P, (s + 1) * P, out);",
+                             "rc = chunk_decode(md, st, words, nws, n_c, K, s * P, (s + 1) * P + (s + 1 < S), out);"),
     "phase_order_swapped": ("for (int phase = 1; phase >= 0; phase--) {", "for (int phase = 0; phase <= 1; phase++) {"),
     "sign_in_wrong_place": ("return (uint16_t)((sign << 15) | (expo << 7) | f);", "return (uint16_t)((sign << 7) | (expo << 8) | f);"),
     "normalise_tie_high_index": ("(rem[ib] == rem[ibest] && ib < ibest)", "(rem[ib] == rem[ibest] && ib > ibest)"),

@@ -1,0 +1,186 @@
+"""Pins for chunks whose lanes are split into several word streams.
+
+A chunk's K lanes form S = K/P streams of P consecutive lanes; each stream
+keeps its own 16-bit word sequence, so the streams of one chunk can be
+decoded independently.  This is part of the container's own layout (the
+pages give no chunk layout).  The pins:
+  - a hand-built two-stream container, derived field by field from the
+    one-lane hand example;
+  - every stream's states and words equal the explicit-schedule coder (a
+    separate code path pinned by the worked examples) run on the schedule
+    that the lane interleave defines, with the tables read from the record;
+  - round trips over ragged sizes and stream widths.
+"""
+import hashlib
+import json
+import os
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "container_16x_one_two_streams.json")
+
+
+def _hand_two_streams():
+    g = json.load(open(GOLD))
+    words = np.array([int(h, 16) for h in g["weights_hex"]], np.uint16)
+    body = bytearray()
+    body += struct.pack("<IIIBBBBII", 16, 2, 1, 12, 10, 0, 1, 1, 0)  # W, K, chunks, M_s, M_f, tables, log2 S, n_sym, 0
+    body += struct.pack("<HH", 127, 4096)                             # s-table
+    body += bytes([0])                                                # route
+    body += bytes(32 - len(body))                                     # pad to 32 (index offset)
+    body += struct.pack("<QII", 48, 6, 0)                             # chunk index: payload at 48, 6 words
+    body += struct.pack("<II", 1 << 24, 1 << 24) + bytes(8)           # two states + pad
+    body += struct.pack("<II", 3, 3) + bytes(8)                       # stream word counts + pad
+    body += bytes(6) + bytes(10)                                      # stream 0: three zero words + pad
+    body += bytes(6) + bytes(10)                                      # stream 1
+    assert len(body) == 112
+    hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 272, 32, 0) + bytes(20)
+    d = struct.pack("<IIQQQQ", 1, 0, 16, 0, 160, 112) + hashlib.sha256(words.tobytes()).digest() + bytes(24)
+    return words, g["params"], hdr + d + bytes(body)
+
+
+def test_hand_built_two_stream_container_matches_encoder():
+    words, p, expect = _hand_two_streams()
+    got = O.encode([O.bf16(words)], W=p["W"], K=p["K"], P=p["P"], M_s=p["M_s"], M_f=p["M_f"], cmax=p["cmax"])
+    assert got == expect
+
+
+def test_hand_built_two_stream_container_decodes():
+    words, p, c = _hand_two_streams()
+    out, st = O.decode(c)
+    assert st == [0]
+    assert np.frombuffer(out, np.uint16).tolist() == words.tolist()
+    assert O.decode_chunk(c, 0, 0).tolist() == words.tolist()
+
+
+def _words(n, scale, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(n) * scale).astype(np.float32)
+    x[rng.random(n) < 0.02] = 0.0
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+
+
+def _u(b, off, fmt):
+    return struct.unpack_from("<" + fmt, b, off)[0]
+
+
+def _record_model(c, i):
+    """Read record i's shape and tables straight from the bytes."""
+    d = 64 + 96 * i
+    n, ro = _u(c, d + 8, "Q"), _u(c, d + 24, "Q")
+    b = c[ro:]
+    W, K, nch = _u(b, 0, "I"), _u(b, 4, "I"), _u(b, 8, "I")
+    M_s, M_f, nt, log2S = b[12], b[13], b[14], b[15]
+    n_sym = _u(b, 16, "I")
+    qs = np.zeros(512, np.uint32)
+    route = np.zeros(512, np.uint32)
+    for k in range(n_sym):
+        s, q = _u(b, 24 + 4 * k, "H"), _u(b, 26 + 4 * k, "H")
+        qs[s] = q
+        route[s] = b[24 + 4 * n_sym + k]
+    ft = (24 + 5 * n_sym + 3) // 4 * 4
+    qf = [np.full(128, 1 << (M_f - 7), np.uint32)]
+    for t in range(nt):
+        qf.append(np.frombuffer(b[ft + 256 * t: ft + 256 * (t + 1)], np.uint16).astype(np.uint32))
+    index = (ft + 256 * nt + 15) // 16 * 16
+    return dict(n=n, b=b, W=W, K=K, nch=nch, S=1 << log2S, qs=qs, route=route, qf=qf, M_s=M_s, M_f=M_f,
+                index=index)
+
+
+def _stream_schedule(w, n_c, K, lanes):
+    """Symbols and table ids of one stream, by sub-step: (t, p, phase) with
+    phase 0 the (sign, exponent) symbol and 1 the fraction; idle = -1."""
+    groups = (n_c + 7) // 8
+    T = (groups + K - 1) // K
+    P = len(lanes)
+    syms = np.full((T * 16, P), -1, np.int32)
+    kind = np.zeros((T * 16, P), np.int32)     # 0 = s, 1 = f
+    for t in range(T):
+        for p in range(8):
+            for i, l in enumerate(lanes):
+                j = 8 * (t * K + l) + p
+                if j >= n_c:
+                    continue
+                syms[(t * 8 + p) * 2, i] = int(w[j]) >> 7
+                syms[(t * 8 + p) * 2 + 1, i] = int(w[j]) & 0x7F
+                kind[(t * 8 + p) * 2 + 1, i] = 1
+    return syms, kind
+
+
+@pytest.mark.parametrize("n,W,K,P", [(5000, 1024, 8, 8), (5000, 1024, 8, 2), (3005, 512, 16, 4),
+                                     (4096 + 77, 4096, 64, 16), (777, 64, 1, 1), (20000, 8192, 32, 8)])
+def test_stream_payload_equals_schedule_coder(n, W, K, P):
+    w = _words(n, 0.03, n + K + P)
+    c = O.encode([O.bf16(w)], W=W, K=K, P=P)
+    m = _record_model(c, 0)
+    b, K, S = m["b"], m["K"], m["S"]
+    assert S == K // min(P, K)
+    Ps = K // S
+    tables = [O.Table(m["M_s"], m["qs"])] + [O.Table(m["M_f"], q) for q in m["qf"]]
+    for ch in range(m["nch"]):
+        n_c = min(m["W"], n - ch * m["W"])
+        po, nw = _u(b, m["index"] + 16 * ch, "Q"), _u(b, m["index"] + 16 * ch + 8, "I")
+        states = np.frombuffer(b[po: po + 4 * K], np.uint32)
+        sb = (4 * K + 15) // 16 * 16
+        cb = (4 * S + 15) // 16 * 16 if S > 1 else 0
+        at = po + sb + cb
+        total = 0
+        for s in range(S):
+            nws = _u(b, po + sb + 4 * s, "I") if S > 1 else nw
+            stream = np.frombuffer(b[at: at + 2 * nws], np.uint16)
+            lanes = list(range(s * Ps, (s + 1) * Ps))
+            syms, kind = _stream_schedule(w[ch * m["W"]:], n_c, K, lanes)
+            tab_of = np.where(kind == 1, 1 + m["route"][np.clip(syms_prev(syms), 0, 511)], 0)
+            st_ref, w_ref = O.sched_encode(Ps, syms, tab_of.astype(np.uint32), tables)
+            assert np.array_equal(states[s * Ps: (s + 1) * Ps], st_ref), (ch, s)
+            assert np.array_equal(stream, w_ref), (ch, s)
+            at += (2 * nws + 15) // 16 * 16
+            total += nws
+        assert total == nw
+
+
+def syms_prev(syms):
+    """For every fraction cell, the (sign, exponent) symbol one sub-step
+    earlier in the same lane (the symbol that routes it); other cells -1."""
+    prev = np.full_like(syms, -1)
+    prev[1::2] = syms[0::2]
+    return prev
+
+
+@pytest.mark.parametrize("P", [1, 2, 8, 64, 128])
+def test_stream_roundtrip_ragged(P):
+    K = 128 if P <= 128 else P
+    W = 8 * K * 4
+    rng = np.random.default_rng(P)
+    for n in sorted({0, 1, 9, 8 * K - 1, 8 * K + 3, W - 1, W, W + 5, 3 * W + 11}):
+        w = _words(n, float(rng.choice([0.003, 0.02, 0.1])), n + P)
+        c = O.encode([O.bf16(w)], W=W, K=K, P=P)
+        out, st = O.decode(c)
+        assert st == [0]
+        assert out[: 2 * n] == w.tobytes()
+
+
+def test_bad_stream_widths_rejected():
+    w = _words(100, 0.02, 0)
+    for K, P in [(8, 3), (8, 16), (8, 0)]:
+        with pytest.raises(O.OracleError):
+            O.encode([O.bf16(w)], W=64 * 8, K=K, P=P)
+
+
+def test_stream_word_count_corruption_detected():
+    w = _words(4096, 0.02, 3)
+    c = bytearray(O.encode([O.bf16(w)], W=4096, K=8, P=2))
+    m = _record_model(bytes(c), 0)
+    ro = _u(c, 64 + 24, "Q")
+    po = _u(m["b"], m["index"], "Q")
+    cnt_off = ro + po + (4 * 8 + 15) // 16 * 16
+    a, b2 = _u(c, cnt_off, "I"), _u(c, cnt_off + 4, "I")
+    # move one word from stream 0 to stream 1: totals agree, streams do not
+    struct.pack_into("<II", c, cnt_off, a - 1, b2 + 1)
+    rc, out, st = O.decode_status(bytes(c))
+    assert rc != 0 and st[0] != 0
