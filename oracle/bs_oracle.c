@@ -326,17 +326,18 @@ static int dec_symbol(uint32_t* x, const bso_table* t, const uint16_t* words, ui
 /* nsteps sub-steps x K lanes; syms[step*K+l] = -1 where a lane is idle;     */
 /* tab_of[step*K+l] picks the table.  Encoding walks the sub-steps from last */
 /* to first and, inside one, the lanes from K-1 down to 0; the emitted words */
-/* are then reversed, so decoding walks everything forwards.                 */
+/* are then reversed, so decoding walks everything forwards.  Every lane     */
+/* starts at init[l] (NULL: at L).                                           */
 /* ------------------------------------------------------------------------ */
 int bso_sched_encode(uint32_t K, uint32_t nsteps, const int32_t* syms, const uint32_t* tab_of,
                      const uint32_t* tabM, const uint32_t* tabA, const uint32_t* tabq, uint32_t ntab,
-                     uint32_t* states, uint16_t* words, uint64_t cap, uint64_t* nw) {
+                     const uint32_t* init, uint32_t* states, uint16_t* words, uint64_t cap, uint64_t* nw) {
     bso_table* tabs = (bso_table*)malloc(sizeof(bso_table) * (ntab ? ntab : 1));
     if (!tabs) return BSO_ENOMEM;
     uint64_t off = 0;
     for (uint32_t i = 0; i < ntab; i++) { tabs[i].M = tabM[i]; tabs[i].A = tabA[i]; tabs[i].q = tabq + off; off += tabA[i]; }
     wordlist wl = {0, 0, 0};
-    for (uint32_t l = 0; l < K; l++) states[l] = BSO_L;
+    for (uint32_t l = 0; l < K; l++) states[l] = init ? init[l] : BSO_L;
     int rc = BSO_OK;
     for (int64_t st = (int64_t)nsteps - 1; st >= 0 && !rc; st--) {
         for (int64_t l = (int64_t)K - 1; l >= 0 && !rc; l--) {
@@ -390,7 +391,20 @@ int bso_sched_decode(uint32_t K, uint32_t nsteps, const int32_t* active, const u
 /* stream has its own word sequence, in which a sub-step's refills come in   */
 /* ascending lane order.  The coder below handles the lanes [l0, l1) of one  */
 /* stream.                                                                   */
+/* The last weight of every lane (in decode order) is not coded: the lane's  */
+/* encoder starts from x = L + that weight's 16-bit word instead of L, so    */
+/* the decoder finds the word in its final state.  A lane without weights    */
+/* starts, and must end, at L.                                               */
 /* ------------------------------------------------------------------------ */
+
+/* Chunk index of the last weight of lane l, or -1 when the lane is empty.   */
+static int64_t lane_last_weight(uint32_t n_c, uint32_t K, uint32_t l) {
+    uint64_t groups = ((uint64_t)n_c + 7) / 8;
+    if (l >= groups) return -1;
+    uint64_t g = l + (uint64_t)K * ((groups - 1 - l) / K);
+    uint64_t j = 8 * g + 7;
+    return (int64_t)(j < n_c ? j : (uint64_t)n_c - 1);
+}
 typedef struct {
     uint32_t M_s, M_f;
     uint32_t qs[512];
@@ -404,13 +418,16 @@ static int chunk_encode(const bso_model* md, const uint16_t* w, uint32_t n_c, ui
     bso_table ts = { md->M_s, 512, md->qs };
     uint32_t groups = (n_c + 7) / 8;
     uint32_t T = (groups + K - 1) / K;
-    for (uint32_t l = l0; l < l1; l++) states[l] = BSO_L;
+    for (uint32_t l = l0; l < l1; l++) {
+        int64_t last = lane_last_weight(n_c, K, l);
+        states[l] = BSO_L + (last >= 0 ? w[last] : 0u);
+    }
     for (int64_t t = (int64_t)T - 1; t >= 0; t--) {
         for (int p = 7; p >= 0; p--) {
             for (int phase = 1; phase >= 0; phase--) {
                 for (int64_t l = (int64_t)l1 - 1; l >= (int64_t)l0; l--) {
                     uint64_t j = 8 * ((uint64_t)t * K + (uint64_t)l) + (uint64_t)p;
-                    if (j >= n_c) continue;
+                    if (j >= n_c || (int64_t)j == lane_last_weight(n_c, K, (uint32_t)l)) continue;
                     uint32_t s = bso_symbol_s(w[j]);
                     int rc;
                     if (phase == 0) {
@@ -443,7 +460,7 @@ static int chunk_decode(const bso_model* md, const uint32_t* states_in, const ui
             for (int phase = 0; phase < 2 && !rc; phase++) {
                 for (uint32_t l = l0; l < l1 && !rc; l++) {
                     uint64_t j = 8 * ((uint64_t)t * K + l) + p;
-                    if (j >= n_c) continue;
+                    if (j >= n_c || (int64_t)j == lane_last_weight(n_c, K, l)) continue;
                     uint32_t sym;
                     if (phase == 0) {
                         rc = dec_symbol(&x[l], &ts, words, nw, &pos, &sym);
@@ -457,8 +474,14 @@ static int chunk_decode(const bso_model* md, const uint32_t* states_in, const ui
             }
         }
     }
-    /* the encoder started every lane at L, so a whole stream must end there */
-    for (uint32_t l = l0; l < l1 && !rc; l++) if (x[l] != BSO_L) rc = BSO_ECORRUPT;
+    /* every lane ends at the state its encoder started from: L plus its last
+       weight, or L for an empty lane */
+    for (uint32_t l = l0; l < l1 && !rc; l++) {
+        int64_t last = lane_last_weight(n_c, K, l);
+        if (last < 0) { if (x[l] != BSO_L) rc = BSO_ECORRUPT; }
+        else if (x[l] < BSO_L || x[l] - BSO_L > 0xFFFFu) rc = BSO_ECORRUPT;
+        else out[last] = (uint16_t)(x[l] - BSO_L);
+    }
     if (!rc && pos != nw) rc = BSO_ECORRUPT;
     free(x); free(s_now);
     return rc;

@@ -62,7 +62,7 @@ def lib():
         l.bso_record_shape.argtypes = [C.c_uint64, C.c_uint32, C.c_uint32, u32p, u32p]
         l.bso_record_shape.restype = C.c_int
         l.bso_sched_encode.argtypes = [C.c_uint32, C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p,
-                                       C.c_void_p, C.c_void_p, C.c_uint32, C.c_void_p, C.c_void_p,
+                                       C.c_void_p, C.c_void_p, C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p,
                                        C.c_uint64, u64p]
         l.bso_sched_encode.restype = C.c_int
         l.bso_sched_decode.argtypes = [C.c_uint32, C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -168,10 +168,11 @@ def _tables(tables):
     return M, A, np.ascontiguousarray(q, np.uint32)
 
 
-def sched_encode(K: int, syms, tab_of, tables):
+def sched_encode(K: int, syms, tab_of, tables, init=None):
     """Interleaved rANS over an explicit schedule.
 
     syms, tab_of: int arrays of shape (nsteps, K); syms = -1 where a lane is idle.
+    init: the lanes' initial states (default: all L).
     Returns (states[K] uint32, words uint16).
     """
     syms = np.ascontiguousarray(syms, np.int32).reshape(-1, K)
@@ -182,8 +183,9 @@ def sched_encode(K: int, syms, tab_of, tables):
     words = np.zeros(cap, np.uint16)
     states = np.zeros(K, np.uint32)
     nw = np.zeros(1, np.uint64)
+    ini = None if init is None else np.ascontiguousarray(init, np.uint32)
     rc = lib().bso_sched_encode(K, nsteps, _ptr(syms), _ptr(tab_of), _ptr(M), _ptr(A), _ptr(q), len(tables),
-                                _ptr(states), _ptr(words), cap, _u64p(nw))
+                                None if ini is None else _ptr(ini), _ptr(states), _ptr(words), cap, _u64p(nw))
     if rc:
         raise OracleError(rc, "sched_encode")
     return states, words[: int(nw[0])].copy()

@@ -33,7 +33,7 @@ def _hand_container():
     body += bytes([0])                                                 # route
     body += bytes(32 - len(body))                                      # pad to 32 (index offset)
     body += struct.pack("<QII", 48, 3, 0)                              # chunk index
-    body += struct.pack("<I", 1 << 24) + bytes(12)                     # state + pad
+    body += struct.pack("<I", g["final_state"]) + bytes(12)            # state + pad
     body += struct.pack("<HHH", 0, 0, 0) + bytes(10)                   # words + pad
     assert len(body) == 80
     hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 240, 16, 0) + bytes(20)

@@ -30,6 +30,10 @@ MUTANTS = {
     "words_not_reversed": ("put16(b + at + 2 * i, wls[st].w[wls[st].n - 1 - i]);",
                            "put16(b + at + 2 * i, wls[st].w[i]);"),
     "streams_swapped": ("states, &wls[st]);", "states, &wls[S - 1 - st]);"),
+    "last_weight_not_in_state": ("states[l] = BSO_L + (last >= 0 ? w[last] : 0u);", "states[l] = BSO_L;"),
+    "last_weight_read_off_by_one": ("else out[last] = (uint16_t)(x[l] - BSO_L);",
+                                    "else out[last] = (uint16_t)(x[l] - BSO_L + 1);"),
+    "last_weight_wrong_position": ("uint64_t j = 8 * g + 7;\n    return", "uint64_t j = 8 * g + 6;\n    return"),
     "stream_lanes_overlap": ("rc = chunk_decode(md, st, words, nws, n_c, K, s * P, (s + 1) * P, out);",
                              "rc = chunk_decode(md, st, words, nws, n_c, K, s * P, (s + 1) * P + (s + 1 < S), out);"),
     "phase_order_swapped": ("for (int phase = 1; phase >= 0; phase--) {", "for (int phase = 0; phase <= 1; phase++) {"),

@@ -8,7 +8,8 @@ pages give no chunk layout).  The pins:
     one-lane hand example;
   - every stream's states and words equal the explicit-schedule coder (a
     separate code path pinned by the worked examples) run on the schedule
-    that the lane interleave defines, with the tables read from the record;
+    that the lane interleave defines, with the tables read from the record
+    and each lane started from 2^16 plus its last weight;
   - round trips over ragged sizes and stream widths.
 """
 import hashlib
@@ -34,7 +35,7 @@ def _hand_two_streams():
     body += bytes([0])                                                # route
     body += bytes(32 - len(body))                                     # pad to 32 (index offset)
     body += struct.pack("<QII", 48, 6, 0)                             # chunk index: payload at 48, 6 words
-    body += struct.pack("<II", 1 << 24, 1 << 24) + bytes(8)           # two states + pad
+    body += struct.pack("<II", g["final_state"], g["final_state"]) + bytes(8)   # two states + pad
     body += struct.pack("<II", 3, 3) + bytes(8)                       # stream word counts + pad
     body += bytes(6) + bytes(10)                                      # stream 0: three zero words + pad
     body += bytes(6) + bytes(10)                                      # stream 1
@@ -93,23 +94,32 @@ def _record_model(c, i):
 
 
 def _stream_schedule(w, n_c, K, lanes):
-    """Symbols and table ids of one stream, by sub-step: (t, p, phase) with
-    phase 0 the (sign, exponent) symbol and 1 the fraction; idle = -1."""
+    """Symbols and table kinds of one stream, by sub-step: (t, p, phase) with
+    phase 0 the (sign, exponent) symbol and 1 the fraction; idle = -1.  Each
+    lane's last weight is left out of the schedule: it is the lane's start
+    state, 2^16 + its word (an empty lane starts at 2^16)."""
     groups = (n_c + 7) // 8
     T = (groups + K - 1) // K
     P = len(lanes)
     syms = np.full((T * 16, P), -1, np.int32)
     kind = np.zeros((T * 16, P), np.int32)     # 0 = s, 1 = f
+    init = np.full(P, 1 << 16, np.uint32)
+    last = {}
+    for i, l in enumerate(lanes):
+        js = [8 * (t * K + l) + p for t in range(T) for p in range(8) if 8 * (t * K + l) + p < n_c]
+        if js:
+            last[i] = max(js)
+            init[i] += int(w[last[i]])
     for t in range(T):
         for p in range(8):
             for i, l in enumerate(lanes):
                 j = 8 * (t * K + l) + p
-                if j >= n_c:
+                if j >= n_c or last.get(i) == j:
                     continue
                 syms[(t * 8 + p) * 2, i] = int(w[j]) >> 7
                 syms[(t * 8 + p) * 2 + 1, i] = int(w[j]) & 0x7F
                 kind[(t * 8 + p) * 2 + 1, i] = 1
-    return syms, kind
+    return syms, kind, init
 
 
 @pytest.mark.parametrize("n,W,K,P", [(5000, 1024, 8, 8), (5000, 1024, 8, 2), (3005, 512, 16, 4),
@@ -134,9 +144,9 @@ def test_stream_payload_equals_schedule_coder(n, W, K, P):
             nws = _u(b, po + sb + 4 * s, "I") if S > 1 else nw
             stream = np.frombuffer(b[at: at + 2 * nws], np.uint16)
             lanes = list(range(s * Ps, (s + 1) * Ps))
-            syms, kind = _stream_schedule(w[ch * m["W"]:], n_c, K, lanes)
+            syms, kind, init = _stream_schedule(w[ch * m["W"]:], n_c, K, lanes)
             tab_of = np.where(kind == 1, 1 + m["route"][np.clip(syms_prev(syms), 0, 511)], 0)
-            st_ref, w_ref = O.sched_encode(Ps, syms, tab_of.astype(np.uint32), tables)
+            st_ref, w_ref = O.sched_encode(Ps, syms, tab_of.astype(np.uint32), tables, init=init)
             assert np.array_equal(states[s * Ps: (s + 1) * Ps], st_ref), (ch, s)
             assert np.array_equal(stream, w_ref), (ch, s)
             at += (2 * nws + 15) // 16 * 16
