@@ -43,6 +43,7 @@ def parse():
                     help="only run a plain device copy of this many MiB a few times (to scale HBM byte counters)")
     ap.add_argument("--lanes", type=int, default=None, help="override the lanes per chunk of the workload")
     ap.add_argument("--chunk-weights", type=int, default=None, help="override the weights per chunk")
+    ap.add_argument("--stream-lanes", type=int, default=None, help="override the lanes per word stream")
     return ap.parse_args()
 
 
@@ -62,7 +63,7 @@ def measured_traffic(job):
         return None
     if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
         return None
-    w = rec.get("workloads", {}).get(f"{job.name}|W={job.chunk_weights}|K={job.lanes}")
+    w = rec.get("workloads", {}).get(f"{job.name}|W={job.chunk_weights}|K={job.lanes}|P={job.stream_lanes}")
     return None if w is None else int(w["traffic_bytes"])
 
 
@@ -137,7 +138,7 @@ def main():
     else:
         gen_dev = "cuda" if a.config == "4" else "cpu"
         enc = workloads.encode_config(a.config, device=gen_dev, keep_reference=False, keep_device_reference=True,
-                                      lanes=a.lanes, chunk_weights=a.chunk_weights)
+                                      lanes=a.lanes, chunk_weights=a.chunk_weights, stream_lanes=a.stream_lanes)
         job = workloads.DecodeJob(enc)
     log(f"workload {job.name}: {job.n_weights} BF16 weights, container {job.container_bytes / 1e6:.1f} MB, "
         f"built in {time.time() - t0:.1f}s")
@@ -218,7 +219,8 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {"workload": job.name, "bf16_weights": job.n_weights, "raw_bytes": job.raw_bytes,
-                   "chunk_weights": job.chunk_weights, "lanes": job.lanes, "m_s": 12, "m_f": 10,
+                   "chunk_weights": job.chunk_weights, "lanes": job.lanes, "stream_lanes": job.stream_lanes,
+                   "m_s": 12, "m_f": 10,
                    "bits_per_weight": round(job.bits_per_weight, 5), "entropy_bits": round(job.entropy_bits, 5),
                    "bits_over_entropy_pct": round(100 * (job.bits_per_weight / job.entropy_bits - 1), 3),
                    "cold_cache": bool(a.cold), "parallelism": "single GPU"},

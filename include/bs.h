@@ -18,20 +18,24 @@
  *                u32 0, u64 n (weights for BF16, bytes for RAW), u64 out_offset,
  *                u64 rec_offset, u64 rec_len, u8 sha256[32], 24 B zero
  *   BF16 record body: u32 W (weights per chunk), u32 K (lanes), u32 n_chunks,
- *                u8 M_s, u8 M_f, u8 n_tables, u8 0, u32 n_sym, u32 0;
+ *                u8 M_s, u8 M_f, u8 n_tables, u8 log2 S (word streams per
+ *                chunk), u32 n_sym, u32 0;
  *                s-table n_sym x (u16 s, u16 q) ascending s (sum q = 2^M_s);
  *                route: n_sym bytes (fraction table of each s: 0 = flat,
  *                1..n_tables), padded to 4 B; n_tables x 128 x u16 q_f
  *                (each sums to 2^M_f); pad to 16 B; chunk index n_chunks x
- *                (u64 payload offset from the body start, u32 words, u32 0);
- *                payloads: K x u32 final encoder states (pad 16 B), then the
- *                16-bit words in decode order (pad 16 B).
+ *                (u64 payload offset from the body start, u32 words of all
+ *                streams, u32 0); payloads: K x u32 final encoder states (pad
+ *                16 B); when S > 1, S x u32 word counts (pad 16 B); then
+ *                each stream's 16-bit words in decode order (pad 16 B).
  *   Coder: 32-bit state in [2^16, 2^32), 16-bit renormalisation words.  In a
  *   chunk, weight j belongs to lane (j/8) mod K, macro-step (j/8)/K; each lane
  *   decodes, per weight, s with the s-table then f with the table route[s];
- *   lanes take turns in ascending order within each (macro-step, position,
- *   field) sub-step, consuming stream words in that order.  Fraction tables
- *   with id 0 are flat (q = 2^(M_f - 7) for every f).
+ *   the K lanes form S streams of P = K/S consecutive lanes, each with its
+ *   own word sequence; within a stream, lanes take turns in ascending order
+ *   in each (macro-step, position, field) sub-step, consuming its words in
+ *   that order.  Fraction tables with id 0 are flat (q = 2^(M_f - 7) for
+ *   every f).
  *
  * Conventions:
  *   - Every function returns a bs_status (0 = BS_OK); none throws or aborts.
@@ -69,8 +73,11 @@ typedef enum {
 enum { BS_KIND_BF16 = 1, BS_KIND_RAW = 2 };
 
 /* Encoder parameters.  chunk_weights W must be a multiple of 8*lanes; lanes K
- * is a power of two: 1..64, 128, 256 or 512; 9 <= m_s <= 12; 7 <= m_f <= 10;
- * max_tables <= 6; threads = host encoder threads (0 = hardware count). */
+ * is a power of two: 1..64, 128, 256 or 512; stream_lanes P (0 = K) is a
+ * power of two <= K: each chunk's lanes are split into word streams of P
+ * lanes (fewer when a small record gets fewer lanes), which the decoder runs
+ * on separate wavefronts; 9 <= m_s <= 12; 7 <= m_f <= 10; max_tables <= 6;
+ * threads = host encoder threads (0 = hardware count). */
 typedef struct {
     uint32_t chunk_weights;
     uint32_t lanes;
@@ -78,10 +85,11 @@ typedef struct {
     uint32_t m_f;
     uint32_t max_tables;
     uint32_t threads;
+    uint32_t stream_lanes;
 } bs_params;
 
 /* Fill *p with the defaults: W = 65536, K = 128, m_s = 12, m_f = 10,
- * max_tables = 6, threads = 0. */
+ * max_tables = 6, threads = 0, stream_lanes = 0 (one stream per chunk). */
 void bs_params_default(bs_params* p);
 
 /* ---------------------------------------------------------------- model */
@@ -147,10 +155,11 @@ typedef struct {
     uint32_t n_records;
     uint64_t total_len;
     uint64_t out_len;       /* bytes of the fully decoded output */
-    uint64_t n_chunks;      /* chunks over all BF16 records (status array length) */
+    uint64_t n_chunks;      /* chunks over all BF16 records */
     uint64_t bf16_weights;  /* BF16 weights over all BF16 records */
     uint64_t bf16_bytes;    /* container bytes charged to BF16 records (bodies + their directory share + header share) */
     uint64_t raw_bytes;     /* verbatim bytes */
+    uint64_t n_streams;     /* word streams over all BF16 chunks (status array length) */
 } bs_container_info;
 
 typedef struct {
@@ -158,8 +167,11 @@ typedef struct {
     uint32_t chunk_weights, lanes, n_chunks;
     uint32_t m_s, m_f, n_tables, n_sym;
     uint64_t n, out_offset, rec_offset, rec_len;
-    uint64_t chunk_base;    /* index of the record's first chunk in the status array */
+    uint64_t chunk_base;    /* index of the record's first chunk over all BF16 records */
     uint8_t sha256[32];
+    uint64_t stream_base;   /* status index of the record's first stream */
+    uint32_t streams;       /* word streams per chunk */
+    uint32_t reserved;
 } bs_record_info;
 
 /* Validate a host copy of a container and describe it.  Errors: BS_E_FORMAT,
@@ -189,10 +201,11 @@ void bs_plan_destroy(bs_plan* plan);
  * d_out + out_offset(i) - out_offset(first); the bytes between records are not
  * written.  d_out must be 16-B aligned with at least the returned
  * bs_plan_out_bytes(plan, first, count) bytes of capacity; nothing outside
- * [d_out, d_out + that size) is written.  d_status: one u32 per chunk of the
- * whole container (bs_container_info.n_chunks); the entries of the decoded
+ * [d_out, d_out + that size) is written.  d_status: one u32 per word stream
+ * of the whole container (bs_container_info.n_streams; stream s of chunk c of
+ * a record at stream_base + c * streams + s); the entries of the decoded
  * records are set to 0 (ok) or a bit set: 1 = a lane did not end at the
- * initial state, 2 = the words consumed differ from the chunk's count.  The
+ * initial state, 2 = the words consumed differ from the stream's count.  The
  * output is valid after the stream reaches this point.  Errors (returned
  * before anything is enqueued): BS_E_INVAL (range, alignment), BS_E_NOSPACE
  * (out_capacity too small), BS_E_HIP (launch failed). */
@@ -202,7 +215,8 @@ bs_status bs_decode_async(const bs_plan* plan, uint32_t first, uint32_t count, v
 /* Bytes needed to decode records [first, first + count). */
 uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count);
 
-/* Chunks (one per wavefront) that each decode workgroup of this plan takes. */
+/* Wavefronts per decode workgroup when the whole container is decoded (one
+ * word stream of a chunk per wavefront at a time). */
 uint32_t bs_plan_waves_per_block(const bs_plan* plan);
 
 /* ---------------------------------------------------------------- verify */
@@ -215,8 +229,8 @@ enum {
 
 typedef struct {
     uint64_t chunks_checked;
-    uint64_t chunks_bad;
-    uint64_t first_bad_chunk;     /* UINT64_MAX if none */
+    uint64_t chunks_bad;          /* chunks with at least one bad stream status */
+    uint64_t first_bad_chunk;     /* chunk index over all BF16 records, UINT64_MAX if none */
     uint64_t bytes_compared;
     uint64_t bytes_mismatched;
     uint64_t first_mismatch;      /* byte offset relative to d_out, UINT64_MAX if none */

@@ -33,7 +33,8 @@ VERIFY_SHA256 = 4
 
 class Params(C.Structure):
     _fields_ = [("chunk_weights", C.c_uint32), ("lanes", C.c_uint32), ("m_s", C.c_uint32),
-                ("m_f", C.c_uint32), ("max_tables", C.c_uint32), ("threads", C.c_uint32)]
+                ("m_f", C.c_uint32), ("max_tables", C.c_uint32), ("threads", C.c_uint32),
+                ("stream_lanes", C.c_uint32)]
 
 
 class Tensor(C.Structure):
@@ -44,14 +45,15 @@ class Tensor(C.Structure):
 class ContainerInfo(C.Structure):
     _fields_ = [("version", C.c_uint32), ("n_records", C.c_uint32), ("total_len", C.c_uint64),
                 ("out_len", C.c_uint64), ("n_chunks", C.c_uint64), ("bf16_weights", C.c_uint64),
-                ("bf16_bytes", C.c_uint64), ("raw_bytes", C.c_uint64)]
+                ("bf16_bytes", C.c_uint64), ("raw_bytes", C.c_uint64), ("n_streams", C.c_uint64)]
 
 
 class RecordInfo(C.Structure):
     _fields_ = [("kind", C.c_uint32), ("chunk_weights", C.c_uint32), ("lanes", C.c_uint32),
                 ("n_chunks", C.c_uint32), ("m_s", C.c_uint32), ("m_f", C.c_uint32), ("n_tables", C.c_uint32),
                 ("n_sym", C.c_uint32), ("n", C.c_uint64), ("out_offset", C.c_uint64), ("rec_offset", C.c_uint64),
-                ("rec_len", C.c_uint64), ("chunk_base", C.c_uint64), ("sha256", C.c_uint8 * 32)]
+                ("rec_len", C.c_uint64), ("chunk_base", C.c_uint64), ("sha256", C.c_uint8 * 32),
+                ("stream_base", C.c_uint64), ("streams", C.c_uint32), ("reserved", C.c_uint32)]
 
 
 class Report(C.Structure):

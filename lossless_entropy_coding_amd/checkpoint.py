@@ -28,7 +28,7 @@ class CheckpointJob:
                  device: str = "cuda", keep_host_first: bool = True):
         layout = synth.cfg5_layout(layers=layers)
         self.name = "cfg5_checkpoint_%dlayers_%dtensors" % (layers, len(layout))
-        self.chunk_weights, self.lanes = chunk_weights, lanes
+        self.chunk_weights, self.lanes, self.stream_lanes = chunk_weights, lanes, lanes
         self.lanes_per_thread = 1 if lanes <= 64 else lanes // 64
         self.plans, self.refs = [], []
         self.n_weights = self.raw_bytes = self.read_bytes = self.container_bytes = 0

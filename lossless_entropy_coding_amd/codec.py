@@ -29,11 +29,13 @@ def _stream_handle(stream) -> int:
 
 
 def params(chunk_weights: int = 65536, lanes: int = 128, m_s: int = 12, m_f: int = 10, max_tables: int = 6,
-           threads: int = 0) -> L.Params:
+           threads: int = 0, stream_lanes: int = 0) -> L.Params:
+    """Encoder parameters; stream_lanes 0 keeps each chunk one word stream."""
     p = L.Params()
     L.lib().bs_params_default(C.byref(p))
     p.chunk_weights, p.lanes, p.m_s, p.m_f, p.max_tables, p.threads = (chunk_weights, lanes, m_s, m_f,
                                                                        max_tables, threads)
+    p.stream_lanes = stream_lanes
     return p
 
 
@@ -149,7 +151,8 @@ class Plan:
         L.check(L.lib().bs_plan_create(container, len(container), C.c_void_p(self.dev.data_ptr()),
                                        C.c_void_p(_stream_handle(stream)), C.byref(out)), "bs_plan_create")
         self.handle = out
-        self.status = torch.zeros(max(self.info.n_chunks, 1), dtype=torch.int32, device=device)
+        # one status word per chunk stream
+        self.status = torch.zeros(max(self.info.n_streams, 1), dtype=torch.int32, device=device)
 
     def __del__(self):
         if getattr(self, "handle", None) is not None and self.handle.value:

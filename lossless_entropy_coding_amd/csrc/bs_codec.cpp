@@ -72,28 +72,44 @@ inline void put(uint32_t& x, const EncSym& e, uint32_t M, uint16_t*& sink) {
     x = ((x / e.q) << M) + x % e.q + e.cum;
 }
 
-// Encode one chunk (n_c weights, K lanes).  Sub-steps run from last to first,
-// lanes from K-1 down to 0 inside each, so that the decoder reads forwards;
-// the emitted words come out reversed and are turned around by the caller.
-// `scratch` must hold 2 * n_c words.  Returns the word count.
-uint64_t encode_chunk(const EncModel& em, const uint16_t* w, uint32_t n_c, uint32_t K, uint32_t* x,
-                      uint16_t* scratch) {
-    for (uint32_t l = 0; l < K; l++) x[l] = kL;
+// Chunk index of the last weight of lane l in decode order (its last group,
+// last position), or UINT64_MAX for a lane without weights.
+inline uint64_t lane_last(uint32_t n_c, uint32_t K, uint32_t l) {
+    const uint64_t groups = ((uint64_t)n_c + 7) / 8;
+    if (l >= groups) return UINT64_MAX;
+    const uint64_t g = l + (uint64_t)K * ((groups - 1 - l) / K);
+    return std::min<uint64_t>(8 * g + 7, (uint64_t)n_c - 1);
+}
+
+// Encode the lanes [l0, l1) of one chunk (n_c weights, K lanes): one word
+// stream.  Each lane's last weight is not coded: the lane starts from
+// 2^16 + that word, which the decoder finds in its final state.  Sub-steps
+// run from last to first, lanes from l1-1 down to l0 inside each, so that the
+// decoder reads forwards; the emitted words come out reversed and are turned
+// around by the caller.  `scratch` must hold 2 * n_c words.  Returns the word
+// count.
+uint64_t encode_stream(const EncModel& em, const uint16_t* w, uint32_t n_c, uint32_t K, uint32_t l0, uint32_t l1,
+                       uint32_t* x, uint16_t* scratch) {
+    uint64_t last[512];
+    for (uint32_t l = l0; l < l1; l++) {
+        last[l - l0] = lane_last(n_c, K, l);
+        x[l] = kL + (last[l - l0] != UINT64_MAX ? w[last[l - l0]] : 0u);
+    }
     uint16_t* sink = scratch;
     const uint32_t groups = (n_c + 7) / 8;
     const uint32_t T = (groups + K - 1) / K;
     for (uint32_t t = T; t-- > 0;) {
         for (int p = 7; p >= 0; p--) {
             // fraction sub-step, then sign/exponent sub-step (reverse of decode order)
-            for (uint32_t l = K; l-- > 0;) {
+            for (uint32_t l = l1; l-- > l0;) {
                 const uint64_t j = 8ull * ((uint64_t)t * K + l) + (uint64_t)p;
-                if (j >= n_c) continue;
+                if (j >= n_c || j == last[l - l0]) continue;
                 const uint32_t v = w[j];
                 put(x[l], em.f[em.route[v >> 7]][v & 127], em.m_f, sink);
             }
-            for (uint32_t l = K; l-- > 0;) {
+            for (uint32_t l = l1; l-- > l0;) {
                 const uint64_t j = 8ull * ((uint64_t)t * K + l) + (uint64_t)p;
-                if (j >= n_c) continue;
+                if (j >= n_c || j == last[l - l0]) continue;
                 put(x[l], em.s[w[j] >> 7], em.m_s, sink);
             }
         }
@@ -112,8 +128,20 @@ void record_shape(uint64_t n, uint32_t W, uint32_t K, uint32_t& w_out, uint32_t&
 
 struct ChunkOut {
     std::vector<uint32_t> states;
-    std::vector<uint16_t> words;   // decode order
+    std::vector<std::vector<uint16_t>> words;   // per stream, decode order
+    uint64_t total() const {
+        uint64_t t = 0;
+        for (const auto& v : words) t += v.size();
+        return t;
+    }
 };
+
+// chunk payload bytes: states, stream word counts (S > 1), streams
+uint64_t payload_bytes(const ChunkOut& co, uint32_t K, uint32_t S) {
+    uint64_t b = align_up(4ull * K, 16) + (S > 1 ? align_up(4ull * S, 16) : 0);
+    for (const auto& v : co.words) b += align_up(2 * v.size(), 16);
+    return b;
+}
 
 struct EncRecord {
     uint32_t kind = 0;
@@ -123,7 +151,7 @@ struct EncRecord {
     const Model* md = nullptr;
     Model owned;
     EncModel em;
-    uint32_t W = 0, K = 0, n_chunks = 0;
+    uint32_t W = 0, K = 0, S = 1, n_chunks = 0;
     std::vector<ChunkOut> chunks;
     std::vector<uint8_t> head;   // fixed part + tables + chunk index (index filled at assembly)
     uint64_t index_off = 0;
@@ -167,6 +195,9 @@ void build_head(EncRecord& r) {
     b[12] = (uint8_t)md.m_s;
     b[13] = (uint8_t)md.m_f;
     b[14] = (uint8_t)md.n_tables;
+    uint32_t log2s = 0;
+    while ((1u << log2s) < r.S) log2s++;
+    b[15] = (uint8_t)log2s;
     wr32(b + 16, md.n_sym);
     uint32_t k = 0;
     for (uint32_t s = 0; s < 512; s++) {
@@ -204,6 +235,7 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
     }
     c.recs.assign(c.n_records, Record());
     c.n_chunks = 0;
+    c.n_streams = 0;
     uint64_t out_end = 0;
     for (uint32_t i = 0; i < c.n_records; i++) {
         const uint8_t* d = h + dir + kDirEntryBytes * i;
@@ -234,6 +266,8 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         r.n_tables = b[14];
         r.n_sym = rd32(b + 16);
         const uint32_t K = r.K;
+        if (b[15] > 9 || (1u << b[15]) > K) { set_error("record %u: bad stream count", i); return BS_E_FORMAT; }
+        r.S = 1u << b[15];
         if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256 || K == 512) || r.W == 0 || r.W % (8 * K)) {
             set_error("record %u: bad chunk shape W=%u K=%u", i, r.W, K);
             return BS_E_FORMAT;
@@ -267,19 +301,33 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
             if (fs != (1ull << r.m_f)) { set_error("record %u: fraction table %u does not sum to 2^%u", i, t + 1, r.m_f); return BS_E_FORMAT; }
         }
         const uint64_t states_bytes = align_up(4ull * K, 16);
+        const uint64_t counts_bytes = r.S > 1 ? align_up(4ull * r.S, 16) : 0;
         for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
             const uint8_t* e = b + r.index_off + 16ull * ch;
             const uint64_t po = rd64(e);
             const uint64_t nw = rd32(e + 8);
             const uint64_t n_c = std::min<uint64_t>(r.W, r.n - (uint64_t)ch * r.W);
-            if (po % 16 || po > r.rec_len || nw > 2 * n_c ||
-                states_bytes + align_up(2 * nw, 16) > r.rec_len - po) {
+            bool ok = po % 16 == 0 && po <= r.rec_len && nw <= 2 * n_c &&
+                      states_bytes + counts_bytes <= r.rec_len - po;
+            if (ok) {
+                // every stream's words within the record; the counts add up to the index's
+                uint64_t need = states_bytes + counts_bytes, total = 0;
+                for (uint32_t st = 0; st < r.S; st++) {
+                    const uint64_t ns = r.S > 1 ? rd32(b + po + states_bytes + 4ull * st) : nw;
+                    total += ns;
+                    need += align_up(2 * ns, 16);
+                }
+                ok = total == nw && need <= r.rec_len - po;
+            }
+            if (!ok) {
                 set_error("record %u chunk %u: payload out of bounds", i, ch);
                 return BS_E_FORMAT;
             }
         }
         r.chunk_base = c.n_chunks;
         c.n_chunks += r.n_chunks;
+        r.stream_base = c.n_streams;
+        c.n_streams += (uint64_t)r.n_chunks * r.S;
     }
     if (out_end > c.out_len) { set_error("records extend past the declared output length"); return BS_E_FORMAT; }
     return BS_OK;
@@ -332,6 +380,8 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
                 continue;
             }
             record_shape(t.n, p->chunk_weights, p->lanes, r.W, r.K);
+            const uint32_t P = p->stream_lanes ? std::min(p->stream_lanes, r.K) : r.K;
+            r.S = r.K / P;
             r.n_chunks = (uint32_t)(t.n ? (t.n + r.W - 1) / r.W : 0);
             make_enc(*r.md, r.em);
             build_head(r);
@@ -359,9 +409,15 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
             if (buf.size() < 2ull * n_c) buf.resize(2ull * n_c);
             ChunkOut& co = r.chunks[jb.chunk];
             co.states.resize(r.K);
-            const uint64_t nw = encode_chunk(r.em, (const uint16_t*)r.data + c0, n_c, r.K, co.states.data(), buf.data());
-            co.words.resize(nw);
-            for (uint64_t i = 0; i < nw; i++) co.words[i] = buf[nw - 1 - i];
+            co.words.resize(r.S);
+            const uint32_t P = r.K / r.S;
+            for (uint32_t st = 0; st < r.S; st++) {
+                const uint64_t nw = encode_stream(r.em, (const uint16_t*)r.data + c0, n_c, r.K, st * P, (st + 1) * P,
+                                                  co.states.data(), buf.data());
+                std::vector<uint16_t>& v = co.words[st];
+                v.resize(nw);
+                for (uint64_t i = 0; i < nw; i++) v[i] = buf[nw - 1 - i];
+            }
         });
         // layout
         uint64_t pos = align_up(kHeaderBytes + kDirEntryBytes * n_tensors, 16);
@@ -375,11 +431,10 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
                 len = r.n;
             } else {
                 len = r.head.size();
-                const uint64_t sb = align_up(4ull * r.K, 16);
                 for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
                     wr64(r.head.data() + r.index_off + 16ull * ch, len);
-                    wr32(r.head.data() + r.index_off + 16ull * ch + 8, (uint32_t)r.chunks[ch].words.size());
-                    len += sb + align_up(2 * r.chunks[ch].words.size(), 16);
+                    wr32(r.head.data() + r.index_off + 16ull * ch + 8, (uint32_t)r.chunks[ch].total());
+                    len += payload_bytes(r.chunks[ch], r.K, r.S);
                 }
             }
             rec_len[i] = len;
@@ -414,11 +469,17 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
             }
             memcpy(b, r.head.data(), r.head.size());
             const uint64_t sb = align_up(4ull * r.K, 16);
+            const uint64_t cb = r.S > 1 ? align_up(4ull * r.S, 16) : 0;
             for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
                 const ChunkOut& co = r.chunks[ch];
                 uint8_t* pp = b + rd64(r.head.data() + r.index_off + 16ull * ch);
                 for (uint32_t l = 0; l < r.K; l++) wr32(pp + 4 * l, co.states[l]);
-                for (uint64_t k = 0; k < co.words.size(); k++) wr16(pp + sb + 2 * k, co.words[k]);
+                uint8_t* at = pp + sb + cb;
+                for (uint32_t st = 0; st < r.S; st++) {
+                    if (r.S > 1) wr32(pp + sb + 4 * st, (uint32_t)co.words[st].size());
+                    for (uint64_t k = 0; k < co.words[st].size(); k++) wr16(at + 2 * k, co.words[st][k]);
+                    at += align_up(2 * co.words[st].size(), 16);
+                }
             }
         }
         // the decoded extent ends with the last record (the last record may not be the largest offset)
@@ -449,6 +510,7 @@ bs_status bs_container_info_get(const void* h, uint64_t len, bs_container_info* 
     info->total_len = c.total_len;
     info->out_len = c.out_len;
     info->n_chunks = c.n_chunks;
+    info->n_streams = c.n_streams;
     // bytes charged to BF16 records: everything except the verbatim records
     // and their directory entries (header and padding go to the BF16 side)
     uint64_t raw = 0, n_raw = 0;
@@ -483,6 +545,8 @@ bs_status bs_record_info_get(const void* h, uint64_t len, uint32_t index, bs_rec
     info->rec_len = r.rec_len;
     info->chunk_base = r.chunk_base;
     memcpy(info->sha256, r.sha, 32);
+    info->stream_base = r.stream_base;
+    info->streams = r.S;
     return BS_OK;
 }
 

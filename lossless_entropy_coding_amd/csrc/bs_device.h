@@ -43,10 +43,12 @@ struct RecDev {
     uint64_t lut_off;       // byte offset of the record's lookup-table image
     uint32_t W, K;          // weights per chunk, lanes
     uint32_t n_chunks;
-    uint32_t chunk_base;    // first chunk's index in the status array
+    uint32_t status_base;   // status index of the first chunk's first stream
     uint32_t m_s, m_f;
     uint32_t n_tables;
-    uint32_t lanes_per_thread;  // R = 1, 2, 4 or 8
+    uint32_t lanes_per_thread;  // R = 1, 2, 4 or 8 (lanes per stream / 64, at least 1)
+    uint32_t streams_log2;  // word streams per chunk = 2^streams_log2
+    uint32_t P;             // lanes per stream (K >> streams_log2)
     uint32_t n_sym;
     uint32_t stab_off;      // byte offset (from body) of the s-table
     uint32_t route_off;     // byte offset (from body) of the route bytes
@@ -54,10 +56,11 @@ struct RecDev {
 };
 
 // One lanes-per-thread class of a plan: its BF16 records in container order
-// and the running chunk count before each (n + 1 entries).
+// and the running count of decode units (chunk streams) before each (n + 1
+// entries).  Unit u of a record is stream u mod S of chunk u / S.
 struct ClassDev {
     const uint32_t* recs;   // RecDev index of each record of the class
-    const uint32_t* start;  // first class-wide chunk of each record; start[n] = total
+    const uint32_t* start;  // first class-wide unit of each record; start[n] = total
 };
 
 struct RawDev {
@@ -75,7 +78,7 @@ struct DecodeArgs {
     uint32_t* status;
     uint64_t out_base;      // output offset that maps to out[0]
     uint32_t i0, i1;        // class entries of the decoded records
-    uint32_t run;           // chunks per workgroup (a run inside one record)
+    uint32_t run;           // units per workgroup (a run inside one record)
     uint32_t waves;         // waves per workgroup (rings allocated)
 };
 

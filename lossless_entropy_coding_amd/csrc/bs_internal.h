@@ -39,15 +39,17 @@ struct Record {
     uint8_t sha[32] = {0};
     // BF16 records
     uint32_t W = 0, K = 0, n_chunks = 0, m_s = 0, m_f = 0, n_tables = 0, n_sym = 0;
+    uint32_t S = 1;                 // word streams per chunk (K / S lanes each)
     uint32_t stab_off = 0, route_off = 0, ftab_off = 0;
     uint64_t index_off = 0;
     uint64_t chunk_base = 0;
+    uint64_t stream_base = 0;       // status index of the first stream
     uint64_t out_bytes() const { return kind == BS_KIND_BF16 ? 2 * n : n; }
 };
 
 struct Container {
     uint32_t n_records = 0;
-    uint64_t total_len = 0, out_len = 0, n_chunks = 0;
+    uint64_t total_len = 0, out_len = 0, n_chunks = 0, n_streams = 0;
     std::vector<Record> recs;
 };
 

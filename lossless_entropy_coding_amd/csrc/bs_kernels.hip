@@ -286,31 +286,45 @@ __device__ __forceinline__ uint32_t step_f(uint32_t& x, const uint2 se, const Mo
     return __builtin_amdgcn_alignbit(se.y, e.x, 25);
 }
 
+// Decode unit u of a record: word stream st = u mod S of chunk ch = u / S,
+// whose P lanes are lanes [st * P, st * P + P) of the chunk.
 template <int R>
-__device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, uint32_t wave, uint8_t* lds) {
+__device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit, uint32_t wave, uint8_t* lds) {
     const uint32_t lane = threadIdx.x & 63;
+    const uint32_t ch = unit >> r.streams_log2;
+    const uint32_t st = unit & ((1u << r.streams_log2) - 1);
     const uint8_t* body = a.container + r.body;
     const uint8_t* ent = body + r.index_off + 16ull * ch;
     const uint64_t poff = *(const uint64_t*)ent;
-    const uint32_t nw = *(const uint32_t*)(ent + 8);
     const uint8_t* payload = body + poff;
-    const uint32_t K = r.K;
+    const uint32_t K = r.K, P = r.P, LB = st * P;
     const uint64_t n_left = r.n - (uint64_t)ch * r.W;
     const uint32_t n_c = (uint32_t)(n_left < r.W ? n_left : r.W);
+    // this stream's word count and the start of its words
+    const uint8_t* words = payload + ((4 * K + 15) & ~15u);
+    uint32_t nw;
+    if (r.streams_log2 == 0) {
+        nw = *(const uint32_t*)(ent + 8);
+    } else {
+        const uint32_t* counts = (const uint32_t*)words;
+        words += ((4u << r.streams_log2) + 15) & ~15u;
+        for (uint32_t k = 0; k < st; k++) words += (2 * counts[k] + 15) & ~15u;
+        nw = counts[st];
+    }
 
     // lane states first, then the ring: both are complete before the loop so
     // that no load issued here is still pending when the loop first runs
     uint32_t x[R];
-    const uint32_t* st = (const uint32_t*)payload;
+    const uint32_t* sp = (const uint32_t*)payload + LB;
 #pragma unroll
     for (int q = 0; q < R; q++) {
         const uint32_t l = 64 * q + lane;
-        x[q] = l < K ? st[l] : kStateLow;
+        x[q] = l < P ? sp[l] : kStateLow;
     }
     constexpr uint32_t RW = ring_words(R);
     Ring<RW> g;
     g.base = (uint16_t*)(lds + kLutLds + wave * ring_bytes(R));
-    g.words = payload + ((4 * K + 15) & ~15u);
+    g.words = words;
     g.bytes = (2 * nw + 15) & ~15u;
     ring_init(g, lane);
     __builtin_amdgcn_s_waitcnt(0);
@@ -322,14 +336,18 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
 
     const uint32_t groups = (n_c + 7) / 8;
     const uint32_t T = (groups + K - 1) / K;
-    const uint32_t T_full = (K % 64 == 0) ? n_c / (8 * K) : 0;
+    // macro-steps in which every lane decodes 8 weights, none of them a lane's
+    // last (that one is in the lane's start state, not in the stream): all
+    // full macro-steps but the last
+    const uint32_t T_full = (P % 64 == 0) ? n_c / (8 * K) : 0;
+    const uint32_t T_main = T_full ? T_full - 1 : 0;
 
     bool all_on[R];
 #pragma unroll
     for (int q = 0; q < R; q++) all_on[q] = true;
 
     // full macro-steps: every lane decodes 8 weights, one 128-bit store per lane group
-    for (uint32_t t = 0; t < T_full; t++) {
+    for (uint32_t t = 0; t < T_main; t++) {
         uint32_t o[R][4];
 #pragma unroll
         for (int p = 0; p < 8; p++) {
@@ -354,22 +372,29 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
         }
 #pragma unroll
         for (int q = 0; q < R; q++) {
-            uint4* op = (uint4*)out + (uint64_t)t * K + 64 * q + lane;
+            uint4* op = (uint4*)out + (uint64_t)t * K + LB + 64 * q + lane;
             *op = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
         }
     }
 
-    // remaining macro-steps (partial groups, or fewer than 64 lanes): lanes
-    // take part while they still have weights.  One position per iteration;
+    // remaining macro-steps (a lane's last weights, partial groups, or fewer
+    // than 64 lanes): lanes take part while they still have weights, and a
+    // lane's last weight is read off its state.  One position per iteration;
     // each lane's eight output words move through a 128-bit shift register.
-    for (uint32_t t = T_full; t < T; t++) {
-        int32_t cnt[R];
+    bool has[R];     // the lane has any weight in this chunk
+#pragma unroll
+    for (int q = 0; q < R; q++) has[q] = 64 * q + lane < P && 8ull * (LB + 64 * q + lane) < n_c;
+    for (uint32_t t = T_main; t < T; t++) {
+        int32_t cnt[R], last[R];
         uint32_t o[R][4];
 #pragma unroll
         for (int q = 0; q < R; q++) {
             const uint32_t l = 64 * q + lane;
-            const int64_t left = (int64_t)n_c - 8 * ((int64_t)t * K + l);
-            cnt[q] = l < K ? (int32_t)(left < 0 ? 0 : (left > 8 ? 8 : left)) : 0;
+            const int64_t left = (int64_t)n_c - 8 * ((int64_t)t * K + LB + l);
+            cnt[q] = l < P ? (int32_t)(left < 0 ? 0 : (left > 8 ? 8 : left)) : 0;
+            // the lane's last weight is in this macro-step when the next one
+            // has none of its weights
+            last[q] = (cnt[q] > 0 && left - 8 * (int64_t)K <= 0) ? cnt[q] - 1 : -1;
 #pragma unroll
             for (int k = 0; k < 4; k++) o[q][k] = 0;
         }
@@ -380,7 +405,7 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
             uint2 se[R];
 #pragma unroll
             for (int q = 0; q < R; q++) {
-                act[q] = p < cnt[q];
+                act[q] = p < cnt[q] && p != last[q];
                 uint32_t xs = x[q];
                 se[q] = step_s(xs, md);
                 if (act[q]) x[q] = xs;
@@ -389,8 +414,9 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
 #pragma unroll
             for (int q = 0; q < R; q++) {
                 uint32_t xs = x[q];
-                const uint32_t w = step_f(xs, se[q], md);
+                uint32_t w = step_f(xs, se[q], md);
                 if (act[q]) x[q] = xs;
+                if (p == last[q]) w = x[q] - kStateLow;
                 // shift the 128-bit register right by 16 and insert w on top
                 o[q][0] = __builtin_amdgcn_alignbit(o[q][1], o[q][0], 16);
                 o[q][1] = __builtin_amdgcn_alignbit(o[q][2], o[q][1], 16);
@@ -401,7 +427,7 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
         }
 #pragma unroll
         for (int q = 0; q < R; q++) {
-            const uint64_t g16 = (uint64_t)t * K + 64 * q + lane;
+            const uint64_t g16 = (uint64_t)t * K + LB + 64 * q + lane;
             if (cnt[q] == 8) {
                 ((uint4*)out)[g16] = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
             } else if (cnt[q] > 0) {
@@ -413,13 +439,14 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t ch, 
         }
     }
 
-    // a chunk is whole when every lane is back at the encoder's initial state
-    // and exactly the chunk's words were consumed
+    // a stream is whole when every lane ends at the state its encoder
+    // started from (2^16 plus its last weight; 2^16 for a lane without
+    // weights) and exactly the stream's words were consumed
     bool bad = false;
 #pragma unroll
-    for (int q = 0; q < R; q++) bad |= x[q] != kStateLow;
+    for (int q = 0; q < R; q++) bad |= has[q] ? (x[q] - kStateLow) > 0xFFFFu : x[q] != kStateLow;
     const uint64_t badm = __builtin_amdgcn_ballot_w64(bad);
-    if (lane == 0) a.status[r.chunk_base + ch] = (badm ? 1u : 0u) | (pos != nw ? 2u : 0u);
+    if (lane == 0) a.status[r.status_base + unit] = (badm ? 1u : 0u) | (pos != nw ? 2u : 0u);
 }
 
 // Stage one record's lookup tables into LDS (all threads of the workgroup).
@@ -434,12 +461,13 @@ __device__ __forceinline__ void stage_luts(const DecodeArgs& a, const RecDev& r,
     for (uint32_t i = threadIdx.x; i < nf16; i += blockDim.x) fd[i] = fs[i];
 }
 
-// Workgroup b of a launch decodes one run of chunks inside one record: each
-// record r of the class entries [i0, i1) is cut into ceil(chunks_r / run)
-// runs of `run` chunks (the last one shorter), and the runs are numbered in
-// record order.  Wave 0 finds b's record with a prefix sum over the records'
-// run counts; the record's lookup tables are staged into LDS once and up to
-// 16 waves (8 for eight lanes per thread) then take the run's chunks in turn.
+// Workgroup b of a launch decodes one run of units (chunk streams) inside one
+// record: each record r of the class entries [i0, i1) is cut into
+// ceil(units_r / run) runs of `run` units (the last one shorter), and the runs
+// are numbered in record order.  Wave 0 finds b's record with a prefix sum
+// over the records' run counts; the record's lookup tables are staged into
+// LDS once and up to 16 waves (8 for eight lanes per thread) then take the
+// run's units in turn.
 template <int R>
 __global__ __launch_bounds__(R == 8 ? 512 : 1024) void decode_kernel(const DecodeArgs a) {
     // static allocation: the LDS base is a compile-time constant, so table and
@@ -477,11 +505,11 @@ __global__ __launch_bounds__(R == 8 ? 512 : 1024) void decode_kernel(const Decod
     const uint32_t e = __builtin_amdgcn_readfirstlane(pick[0]);
     if (e == UINT32_MAX) return;   // no run for this workgroup (launch larger than the runs)
     const RecDev r = a.recs[a.cls.recs[e]];
-    const uint32_t c0 = __builtin_amdgcn_readfirstlane(pick[1]) * a.run;
-    const uint32_t c1 = min(r.n_chunks, c0 + a.run);
+    const uint32_t u0 = __builtin_amdgcn_readfirstlane(pick[1]) * a.run;
+    const uint32_t u1 = min(r.n_chunks << r.streams_log2, u0 + a.run);
     stage_luts(a, r, lds);
     __syncthreads();
-    for (uint32_t ch = c0 + wave; ch < c1; ch += a.waves) decode_chunk<R>(a, r, ch, wave, lds);
+    for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<R>(a, r, u, wave, lds);
 }
 
 // ------------------------------------------------------------------ residual and compare

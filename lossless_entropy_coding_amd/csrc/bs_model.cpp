@@ -45,6 +45,10 @@ bool params_ok(const bs_params* p) {
         set_error("lanes must be a power of two in 1..64, or 128, 256 or 512 (got %u)", K);
         return false;
     }
+    if (p->stream_lanes && ((p->stream_lanes & (p->stream_lanes - 1)) || p->stream_lanes > K)) {
+        set_error("stream_lanes must be 0 or a power of two <= lanes (got %u)", p->stream_lanes);
+        return false;
+    }
     if (p->chunk_weights == 0 || p->chunk_weights % (8 * K)) {
         set_error("chunk_weights must be a positive multiple of 8*lanes (got %u)", p->chunk_weights);
         return false;
@@ -168,6 +172,7 @@ void bs_params_default(bs_params* p) {
     p->m_f = 10;
     p->max_tables = 6;
     p->threads = 0;
+    p->stream_lanes = 0;
 }
 
 bs_status bs_build_tables_host(const uint16_t* h, uint64_t n, const bs_params* p, bs_tables** out) {

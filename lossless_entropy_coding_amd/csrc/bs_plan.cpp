@@ -149,7 +149,7 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
     if (bsk_device_cus(&cus) != 0 || cus <= 0) cus = 256;
     p->cus = cus;
     const uint32_t n = p->c.n_records;
-    if (p->c.n_chunks > 0xFFFFFFFFull) { plan_free(p); set_error("too many chunks"); return BS_E_FORMAT; }
+    if (p->c.n_streams > 0xFFFFFFFFull) { plan_free(p); set_error("too many chunk streams"); return BS_E_FORMAT; }
     std::vector<bsd::RecDev> recs;
     uint64_t lut_bytes = 0;
     p->dev_index.assign(n, 0);
@@ -173,11 +173,14 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
         d.W = r.W;
         d.K = r.K;
         d.n_chunks = r.n_chunks;
-        d.chunk_base = (uint32_t)r.chunk_base;
+        d.status_base = (uint32_t)r.stream_base;
         d.m_s = r.m_s;
         d.m_f = r.m_f;
         d.n_tables = r.n_tables;
-        d.lanes_per_thread = r.K <= 64 ? 1 : r.K / 64;
+        d.streams_log2 = 0;
+        while ((1u << d.streams_log2) < r.S) d.streams_log2++;
+        d.P = r.K / r.S;
+        d.lanes_per_thread = d.P <= 64 ? 1 : d.P / 64;
         d.n_sym = r.n_sym;
         d.stab_off = r.stab_off;
         d.route_off = r.route_off;
@@ -188,7 +191,7 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
         p->rclass[i] = k;
         p->cls_pos[i] = (uint32_t)p->cls_recs[k].size();
         p->cls_recs[k].push_back((uint32_t)recs.size());
-        p->cls_start[k].push_back(p->cls_start[k].back() + r.n_chunks);
+        p->cls_start[k].push_back(p->cls_start[k].back() + r.n_chunks * r.S);
         recs.push_back(d);
     }
     hipStream_t s = (hipStream_t)stream;
@@ -238,7 +241,7 @@ uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count) 
 
 bs_status bs_decode_async(const bs_plan* p, uint32_t first, uint32_t count, void* d_out, uint64_t out_capacity,
                           uint32_t* d_status, void* stream) {
-    if (!p || (!d_out && count) || (!d_status && p->c.n_chunks)) { set_error("NULL argument"); return BS_E_INVAL; }
+    if (!p || (!d_out && count) || (!d_status && p->c.n_streams)) { set_error("NULL argument"); return BS_E_INVAL; }
     if (first > p->c.n_records || count > p->c.n_records - first) { set_error("record range out of bounds"); return BS_E_INVAL; }
     if ((uintptr_t)d_out & 15) { set_error("output must be 16-byte aligned"); return BS_E_INVAL; }
     if (!count) return BS_OK;
@@ -293,16 +296,18 @@ bs_status bs_verify(const bs_plan* p, uint32_t first, uint32_t count, const void
     const uint64_t base = count ? p->c.recs[first].out_offset : 0;
     bool corrupt = false, mismatch = false;
     if ((flags & BS_VERIFY_STATUS) && count) {
-        if (!d_status && p->c.n_chunks) { set_error("NULL status"); return BS_E_INVAL; }
+        if (!d_status && p->c.n_streams) { set_error("NULL status"); return BS_E_INVAL; }
         for (uint32_t i = first; i < first + count; i++) {
             const Record& r = p->c.recs[i];
             if (r.kind != BS_KIND_BF16 || !r.n_chunks) continue;
-            std::vector<uint32_t> st(r.n_chunks);
-            e = hipMemcpy(st.data(), d_status + r.chunk_base, 4ull * r.n_chunks, hipMemcpyDeviceToHost);
+            std::vector<uint32_t> st((size_t)r.n_chunks * r.S);
+            e = hipMemcpy(st.data(), d_status + r.stream_base, 4ull * st.size(), hipMemcpyDeviceToHost);
             if (e != hipSuccess) return hip_err(e, "status read-back");
             for (uint32_t k = 0; k < r.n_chunks; k++) {
                 rep->chunks_checked++;
-                if (st[k]) {
+                bool bad = false;
+                for (uint32_t s2 = 0; s2 < r.S; s2++) bad |= st[(size_t)k * r.S + s2] != 0;
+                if (bad) {
                     rep->chunks_bad++;
                     rep->first_bad_chunk = std::min<uint64_t>(rep->first_bad_chunk, r.chunk_base + k);
                     corrupt = true;

@@ -33,6 +33,7 @@ class Workload:
     items: list = field(default_factory=list)
     chunk_weights: int = 65536
     lanes: int = 64
+    stream_lanes: int = 0     # lanes per word stream (0: one stream per chunk)
 
     @property
     def n_bf16(self) -> int:

@@ -46,7 +46,7 @@ class Encoded:
 
 def encode_workload(wl: synth.Workload, device: str = "cpu", keep_reference: bool = True,
                     keep_device_reference: bool = False, threads: int = 0) -> Encoded:
-    p = codec.params(chunk_weights=wl.chunk_weights, lanes=wl.lanes, threads=threads)
+    p = codec.params(chunk_weights=wl.chunk_weights, lanes=wl.lanes, threads=threads, stream_lanes=wl.stream_lanes)
     tensors = []
     ent_sum, n_bf16 = 0.0, 0
     for it in wl.items:
@@ -64,7 +64,8 @@ def encode_workload(wl: synth.Workload, device: str = "cpu", keep_reference: boo
     enc = Encoded(name=wl.name, container=container, n_weights=int(info.bf16_weights), raw_bytes=int(info.raw_bytes),
                   entropy_bits=ent_sum / n_bf16 if n_bf16 else math.nan,
                   bits_per_weight=8.0 * info.bf16_bytes / info.bf16_weights if info.bf16_weights else math.nan,
-                  params=dict(chunk_weights=wl.chunk_weights, lanes=wl.lanes, m_s=12, m_f=10, max_tables=6))
+                  params=dict(chunk_weights=wl.chunk_weights, lanes=wl.lanes, stream_lanes=wl.stream_lanes or wl.lanes,
+                              m_s=12, m_f=10, max_tables=6))
     if keep_reference or keep_device_reference:
         ref = np.zeros(info.out_len, np.uint8)
         for i, t in enumerate(tensors):
@@ -78,21 +79,33 @@ def encode_workload(wl: synth.Workload, device: str = "cpu", keep_reference: boo
     return enc
 
 
+def _with_streams(wl: synth.Workload, stream_lanes: int) -> synth.Workload:
+    wl.stream_lanes = stream_lanes
+    return wl
+
+
+# The 4096x4096 matrix is only 128 chunks of 256 KiB: 512 lanes per chunk
+# (256 weights per lane) still keep the lane-state overhead inside the 1% size
+# budget, and streams of 64 lanes let eight wavefronts decode each chunk, so
+# that 1024 wavefronts cover the GPU.
 CONFIG_BUILDERS = {
     "1": lambda device: synth.cfg1(device),
-    "2": lambda device: synth.cfg2(device, lanes=256),
+    "2": lambda device: _with_streams(synth.cfg2(device, lanes=512), 64),
     "3": lambda device: synth.cfg3(device),
     "4": lambda device: synth.cfg4(device),
 }
 
 
 def encode_config(cfg: str, device: str = "cpu", lanes: int | None = None, chunk_weights: int | None = None,
-                  **kw) -> Encoded:
+                  stream_lanes: int | None = None, **kw) -> Encoded:
     wl = CONFIG_BUILDERS[cfg](device)
     if lanes:
         wl.lanes = lanes
+        wl.stream_lanes = min(wl.stream_lanes, lanes) if wl.stream_lanes else 0
     if chunk_weights:
         wl.chunk_weights = chunk_weights
+    if stream_lanes is not None:
+        wl.stream_lanes = stream_lanes
     if cfg == "4":
         kw.setdefault("keep_reference", False)
         kw.setdefault("keep_device_reference", True)
@@ -112,7 +125,8 @@ class DecodeJob:
         self.entropy_bits = enc.entropy_bits
         self.chunk_weights = enc.params["chunk_weights"]
         self.lanes = enc.params["lanes"]
-        self.lanes_per_thread = 1 if self.lanes <= 64 else self.lanes // 64
+        self.stream_lanes = enc.params["stream_lanes"]
+        self.lanes_per_thread = max(1, self.stream_lanes // 64)
         self.container_bytes = len(enc.container)
         info = codec.container_info(enc.container)
         # bytes a decode reads: BF16 record bytes (tables, index, states, words) and verbatim spans

@@ -44,33 +44,42 @@ def _expected_bytes(container: bytes) -> bytes:
 
 
 CASES = [
-    # (name, n, scale, W, K)
-    ("one_group", 8, 0.02, 64, 1),
-    ("ragged_k1", 1001, 0.02, 64, 1),
-    ("k8_ragged", 40000 + 13, 0.02, 4096, 8),
-    ("k32_cfg1_shape", 3 * 32768 + 777, 0.02, 32768, 32),
-    ("k64_full", 4 * 65536, 0.02, 65536, 64),
-    ("k64_ragged", 3 * 65536 + 4099, 0.05, 65536, 64),
-    ("k128_full", 6 * 65536, 0.02, 65536, 128),
-    ("k128_ragged", 2 * 65536 + 1025, 0.003, 65536, 128),
-    ("k256_full", 4 * 131072, 0.02, 131072, 256),
-    ("k256_ragged", 131072 + 2049 + 7, 0.1, 131072, 256),
-    ("small_k_tiny_chunks", 5000, 0.02, 512, 4),
-    ("k512_full", 2 * 262144, 0.02, 262144, 512),
-    ("k512_ragged", 262144 + 4096 * 3 + 5, 0.05, 262144, 512),
-    ("k512_one_chunk_short", 70001, 0.02, 262144, 512),
+    # (name, n, scale, W, K, P = lanes per word stream)
+    ("one_group", 8, 0.02, 64, 1, 1),
+    ("ragged_k1", 1001, 0.02, 64, 1, 1),
+    ("k8_ragged", 40000 + 13, 0.02, 4096, 8, 8),
+    ("k32_cfg1_shape", 3 * 32768 + 777, 0.02, 32768, 32, 32),
+    ("k64_full", 4 * 65536, 0.02, 65536, 64, 64),
+    ("k64_ragged", 3 * 65536 + 4099, 0.05, 65536, 64, 64),
+    ("k128_full", 6 * 65536, 0.02, 65536, 128, 128),
+    ("k128_ragged", 2 * 65536 + 1025, 0.003, 65536, 128, 128),
+    ("k256_full", 4 * 131072, 0.02, 131072, 256, 256),
+    ("k256_ragged", 131072 + 2049 + 7, 0.1, 131072, 256, 256),
+    ("small_k_tiny_chunks", 5000, 0.02, 512, 4, 4),
+    ("k512_full", 2 * 262144, 0.02, 262144, 512, 512),
+    ("k512_ragged", 262144 + 4096 * 3 + 5, 0.05, 262144, 512, 512),
+    ("k512_one_chunk_short", 70001, 0.02, 262144, 512, 512),
+    # chunks split into word streams, one wavefront per stream
+    ("k256_p64_full", 4 * 131072, 0.02, 131072, 256, 64),
+    ("k256_p64_ragged", 2 * 131072 + 8 * 100 + 3, 0.05, 131072, 256, 64),
+    ("k512_p64_ragged", 262144 + 9999, 0.02, 262144, 512, 64),
+    ("k256_p128", 3 * 131072 + 77, 0.02, 131072, 256, 128),
+    ("k512_p256", 2 * 262144 + 11, 0.03, 262144, 512, 256),
+    ("k128_p32", 3 * 65536 + 5, 0.02, 65536, 128, 32),
+    ("k64_p8_small", 20000 + 3, 0.02, 8192, 64, 8),
+    ("k8_p1", 4096 + 9, 0.02, 4096, 8, 1),
 ]
 
 
-@pytest.mark.parametrize("name,n,scale,W,K", CASES, ids=[c[0] for c in CASES])
-def test_decode_matches_oracle_and_original(name, n, scale, W, K):
-    say("case", name, n, W, K)
+@pytest.mark.parametrize("name,n,scale,W,K,P", CASES, ids=[c[0] for c in CASES])
+def test_decode_matches_oracle_and_original(name, n, scale, W, K, P):
+    say("case", name, n, W, K, P)
     rng = np.random.default_rng(n)
     x = rng.standard_normal(n) * scale
     x[rng.random(n) < 0.01] = 0.0
     w = _words(x)
-    c = codec.encode([codec.bf16(w)], codec.params(chunk_weights=W, lanes=K))
-    assert c == O.encode([O.bf16(w)], W=W, K=K)
+    c = codec.encode([codec.bf16(w)], codec.params(chunk_weights=W, lanes=K, stream_lanes=P))
+    assert c == O.encode([O.bf16(w)], W=W, K=K, P=P)
     expect = _expected_bytes(c)
     assert expect == w.tobytes()
     plan, out, rc, rep, got = _decode_check(c, expect)
@@ -104,11 +113,12 @@ def test_special_values_and_residual():
         assert host[ri.out_offset: ri.out_offset + nb] == expect[ri.out_offset: ri.out_offset + nb], i
 
 
-def test_many_records_mixed_lane_classes():
+@pytest.mark.parametrize("stream_lanes", [0, 64])
+def test_many_records_mixed_lane_classes(stream_lanes):
     """Hundreds of records of ragged sizes in one container: small records get
-    fewer lanes (other lanes-per-thread classes) and the persistent workgroups'
-    chunk runs cross record boundaries, re-staging the lookup tables."""
-    say("many records, mixed classes")
+    fewer lanes (other lanes-per-thread classes, or fewer word streams), more
+    records than CUs, and records cut into several workgroup runs."""
+    say("many records, mixed classes, stream lanes", stream_lanes)
     rng = np.random.default_rng(11)
     sizes = list(rng.integers(1, 3000, 700)) + list(rng.integers(3000, 140000, 60)) + [0, 8, 131072, 262144 + 17]
     rng.shuffle(sizes)
@@ -118,11 +128,14 @@ def test_many_records_mixed_lane_classes():
         tensors.append(codec.bf16(_words(x)))
         if i % 37 == 0:
             tensors.append(codec.raw(rng.integers(0, 256, int(rng.integers(1, 5000)), dtype=np.uint8)))
-    c = codec.encode(tensors, codec.params(chunk_weights=131072, lanes=256))
+    c = codec.encode(tensors, codec.params(chunk_weights=131072, lanes=256, stream_lanes=stream_lanes))
     info = codec.container_info(c)
     ris = [codec.record_info(c, i) for i in range(info.n_records)]
-    ks = {ri.lanes for ri in ris if ri.kind == L.KIND_BF16 and ri.n}
-    assert len({max(k // 64, 1) for k in ks}) >= 3, ks
+    bf = [ri for ri in ris if ri.kind == L.KIND_BF16 and ri.n]
+    if stream_lanes:
+        assert {ri.streams for ri in bf} >= {1, 2, 4}
+    else:
+        assert len({max(ri.lanes // 64, 1) for ri in bf}) >= 3
     expect = _expected_bytes(c)
     plan, out, rc, rep, got = _decode_check(c, expect)
     assert rc == L.BS_OK, rep

@@ -37,7 +37,7 @@ def _words(x: np.ndarray) -> np.ndarray:
 
 def _same(tensors_o, tensors_l, **kw):
     p = codec.params(chunk_weights=kw.get("W", 65536), lanes=kw.get("K", 64), m_s=kw.get("M_s", 12),
-                     m_f=kw.get("M_f", 10), max_tables=kw.get("cmax", 6))
+                     m_f=kw.get("M_f", 10), max_tables=kw.get("cmax", 6), stream_lanes=kw.get("P") or 0)
     a = O.encode(tensors_o, **kw)
     b = codec.encode(tensors_l, p)
     assert a == b
@@ -51,6 +51,19 @@ def test_encoder_bytes_match_oracle(seed, n, W, K):
     rng = np.random.default_rng(seed)
     w = _words(rng.standard_normal(n) * rng.choice([0.004, 0.02, 0.1]))
     _same([O.bf16(w)], [codec.bf16(w)], W=W, K=K)
+
+
+@pytest.mark.parametrize("seed,n,W,K,P", [(10, 100000, 4096, 8, 2), (11, 40000, 8192, 64, 16), (12, 300000, 131072, 256, 64),
+                                          (13, 5000, 131072, 256, 64), (14, 70001, 65536, 128, 1), (15, 0, 64, 8, 4),
+                                          (16, 262144 * 2 + 5, 262144, 512, 128)])
+def test_encoder_bytes_match_oracle_streams(seed, n, W, K, P):
+    rng = np.random.default_rng(seed)
+    w = _words(rng.standard_normal(n) * rng.choice([0.004, 0.02, 0.1]))
+    c = _same([O.bf16(w)], [codec.bf16(w)], W=W, K=K, P=P)
+    info = codec.container_info(c)
+    ri = codec.record_info(c, 0)
+    assert ri.streams == (ri.lanes // min(P, ri.lanes) if n else 1)
+    assert info.n_streams == ri.n_chunks * ri.streams
 
 
 def test_encoder_bytes_match_oracle_cfg1():
@@ -146,7 +159,8 @@ def test_validation_errors():
 
 def test_bad_params_rejected():
     w = np.zeros(100, np.uint16)
-    for kw in [dict(lanes=3), dict(lanes=96), dict(lanes=1024, chunk_weights=1 << 20), dict(chunk_weights=100, lanes=8), dict(m_s=13), dict(m_f=6),
+    for kw in [dict(lanes=3), dict(lanes=96), dict(lanes=1024, chunk_weights=1 << 20), dict(lanes=64, stream_lanes=128),
+               dict(lanes=64, stream_lanes=48), dict(chunk_weights=100, lanes=8), dict(m_s=13), dict(m_f=6),
                dict(max_tables=7)]:
         with pytest.raises(L.BSError) as e:
             codec.encode([codec.bf16(w)], codec.params(**kw))
