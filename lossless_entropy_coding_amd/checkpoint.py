@@ -65,6 +65,16 @@ class CheckpointJob:
         for plan in self.plans:
             plan.decode_into(self.out, stream=stream)
 
+    def fast_decoder(self, stream):
+        """One callable that enqueues every layer's decode into the shared
+        buffer, with the C arguments of each marshalled once."""
+        calls = [plan.bound_decode(self.out, stream=stream) for plan in self.plans]
+
+        def run():
+            for c in calls:
+                c()
+        return run
+
     def verify(self):
         """Every layer decoded into the shared buffer, checked on the device
         against its original words, with every chunk's status word."""

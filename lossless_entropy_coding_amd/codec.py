@@ -180,6 +180,23 @@ class Plan:
                                      C.c_void_p(_stream_handle(stream)))
         L.check(rc, "bs_decode_async")
 
+    def bound_decode(self, out: torch.Tensor, first: int = 0, count: int | None = None, stream=None):
+        """decode_into with its ctypes arguments converted once: returns a
+        callable that enqueues the same decode each time it is called."""
+        count = self.n_records - first if count is None else count
+        f = L.lib().bs_decode_async
+        args = (self.handle, C.c_uint32(first), C.c_uint32(count), C.c_void_p(out.data_ptr()),
+                C.c_uint64(out.numel() * out.element_size()), C.c_void_p(self.status.data_ptr()),
+                C.c_void_p(_stream_handle(stream)))
+        keep = (out, self.status)
+
+        def run():
+            rc = f(*args)
+            if rc:
+                L.check(rc, "bs_decode_async")
+            return keep
+        return run
+
     def decode(self, first: int = 0, count: int | None = None, stream=None) -> torch.Tensor:
         out = self.new_output(first, count)
         self.decode_into(out, first, count, stream)

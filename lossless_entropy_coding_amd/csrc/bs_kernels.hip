@@ -248,18 +248,20 @@ __device__ __forceinline__ void ring_top_up(Ring<RW>& g, uint32_t pos) {
 // needed one, so the R ring reads are in flight together.
 template <int R, uint32_t RW>
 __device__ __forceinline__ void refill_all(uint32_t (&x)[R], const bool (&active)[R], const Ring<RW>& g, uint32_t& pos) {
-    bool need[R];
-    uint32_t w[R];
+    uint32_t sel[R], w[R];
 #pragma unroll
     for (int q = 0; q < R; q++) {
-        need[q] = active[q] && x[q] < kStateLow;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(need[q]);
+        const bool need = active[q] && x[q] < kStateLow;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(need);
         const uint32_t pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        // byte selector of the merge, chosen while the word is in flight:
+        // (x << 16) | w for a refill, x unchanged otherwise
+        sel[q] = need ? 0x05040100u : 0x07060504u;
         w[q] = g.base[(pos & (RW - 1)) + pre];
         pos += (uint32_t)__builtin_popcountll(m);
     }
 #pragma unroll
-    for (int q = 0; q < R; q++) x[q] = need[q] ? (x[q] << 16) | w[q] : x[q];
+    for (int q = 0; q < R; q++) x[q] = __builtin_amdgcn_perm(x[q], w[q], sel[q]);
 }
 
 struct Model {

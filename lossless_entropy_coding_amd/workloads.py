@@ -141,6 +141,11 @@ class DecodeJob:
     def decode(self, stream=None):
         self.plan.decode_into(self.out, stream=stream)
 
+    def fast_decoder(self, stream):
+        """A zero-argument callable that enqueues one full decode on `stream`
+        with its C arguments marshalled once (for tight timing loops)."""
+        return self.plan.bound_decode(self.out, stream=stream)
+
     def verify(self):
         rc, rep = self.plan.verify(self.out, ref=self.ref, flags=L.VERIFY_STATUS | L.VERIFY_COMPARE)
         return rc == L.BS_OK, rep
