@@ -55,7 +55,7 @@ struct RecDev {
     uint32_t ftab_off;      // byte offset (from body) of the fraction tables
 };
 
-// One lanes-per-thread class of a plan: its BF16 records in container order
+// One launch class of a plan (lanes per thread 1, 2 or 4; or 8): its BF16 records in container order
 // and the running count of decode units (chunk streams) before each (n + 1
 // entries).  Unit u of a record is stream u mod S of chunk u / S.
 struct ClassDev {
@@ -90,7 +90,9 @@ int bsk_hist_s(const uint16_t* d_w, uint64_t n, unsigned long long* d_cs, void* 
 int bsk_hist_f(const uint16_t* d_w, uint64_t n, const int16_t* d_cand, unsigned long long* d_cf, void* stream);
 int bsk_build_luts(const uint8_t* d_container, const bsd::RecDev* d_recs, uint32_t n_recs, uint8_t* d_luts,
                    void* stream);
-int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t lanes_per_thread, void* stream);
+// variant 1, 2, 4 or 8: every record of the launch has that many lanes per
+// thread; variant 0: a mix of 1, 2 and 4
+int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream);
 int bsk_raw_copy(const uint8_t* d_container, const bsd::RawDev* d_raw, uint32_t n_raw, uint8_t* d_out,
                  uint64_t out_base, void* stream);
 int bsk_compare(const uint8_t* a, const uint8_t* b, uint64_t n, unsigned long long* d_result /*2*/, void* stream);

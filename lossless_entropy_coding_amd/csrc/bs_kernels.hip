@@ -468,13 +468,17 @@ __device__ __forceinline__ void stage_luts(const DecodeArgs& a, const RecDev& r,
 // ceil(units_r / run) runs of `run` units (the last one shorter), and the runs
 // are numbered in record order.  Wave 0 finds b's record with a prefix sum
 // over the records' run counts; the record's lookup tables are staged into
-// LDS once and up to 16 waves (8 for eight lanes per thread) then take the
-// run's units in turn.
-template <int R>
-__global__ __launch_bounds__(R == 8 ? 512 : 1024) void decode_kernel(const DecodeArgs a) {
+// LDS once and the waves then take the run's units in turn.
+// One launch covers every record with 1, 2 or 4 lanes per thread (16 waves,
+// 2048-word rings), so that small tensors decode alongside large ones: G is
+// that lane width when all the launch's records share it, or 0 for a mix (the
+// width is then picked per workgroup).  Records with eight lanes per thread
+// (G = 8: 8 waves, 4096-word rings) have a launch of their own.
+template <int G>
+__global__ __launch_bounds__(G == 8 ? 512 : 1024) void decode_kernel(const DecodeArgs a) {
     // static allocation: the LDS base is a compile-time constant, so table and
     // ring addresses fold into the instructions' offsets
-    __shared__ __align__(16) uint8_t lds[kLutLds + max_waves(R) * ring_bytes(R)];
+    __shared__ __align__(16) uint8_t lds[kLutLds + max_waves(G ? G : 1) * ring_bytes(G ? G : 1)];
     __shared__ uint32_t pick[2];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t b = blockIdx.x;
@@ -511,7 +515,15 @@ __global__ __launch_bounds__(R == 8 ? 512 : 1024) void decode_kernel(const Decod
     const uint32_t u1 = min(r.n_chunks << r.streams_log2, u0 + a.run);
     stage_luts(a, r, lds);
     __syncthreads();
-    for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<R>(a, r, u, wave, lds);
+    if (G != 0) {
+        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<(G ? G : 1)>(a, r, u, wave, lds);
+    } else if (r.lanes_per_thread == 1) {
+        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<1>(a, r, u, wave, lds);
+    } else if (r.lanes_per_thread == 2) {
+        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<2>(a, r, u, wave, lds);
+    } else {
+        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<4>(a, r, u, wave, lds);
+    }
 }
 
 // ------------------------------------------------------------------ residual and compare
@@ -601,15 +613,19 @@ int bsk_build_luts(const uint8_t* d_container, const RecDev* d_recs, uint32_t n_
     return (int)hipGetLastError();
 }
 
-int bsk_decode(const DecodeArgs* args, uint32_t n_groups, uint32_t lanes_per_thread, void* stream) {
+int bsk_decode(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream) {
     if (n_groups == 0) return 0;
     const dim3 grid(n_groups), block(64 * args->waves);
     hipStream_t st = (hipStream_t)stream;
-    if (args->waves == 0 || args->waves > max_waves(lanes_per_thread)) return (int)hipErrorInvalidValue;
-    if (lanes_per_thread == 1) hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, st, *args);
-    else if (lanes_per_thread == 2) hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, st, *args);
-    else if (lanes_per_thread == 4) hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, st, *args);
-    else hipLaunchKernelGGL(decode_kernel<8>, grid, block, 0, st, *args);
+    if (args->waves == 0 || args->waves > max_waves(variant ? variant : 1)) return (int)hipErrorInvalidValue;
+    switch (variant) {
+        case 0: hipLaunchKernelGGL(decode_kernel<0>, grid, block, 0, st, *args); break;
+        case 1: hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, st, *args); break;
+        case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, st, *args); break;
+        case 4: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, st, *args); break;
+        case 8: hipLaunchKernelGGL(decode_kernel<8>, grid, block, 0, st, *args); break;
+        default: return (int)hipErrorInvalidValue;
+    }
     return (int)hipGetLastError();
 }
 

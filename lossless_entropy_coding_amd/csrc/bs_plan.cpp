@@ -29,18 +29,21 @@ struct bs_plan {
     const uint8_t* d_container = nullptr;
     uint64_t len = 0;
     Container c;
-    // one record list per lanes-per-thread class: each class is its own
-    // kernel instantiation with its own workgroup size
-    static constexpr int kClasses = 4;   // R = 1, 2, 4, 8
+    // one record list per launch class: records with 1, 2 or 4 lanes per
+    // thread share one kernel (16-wave workgroups), eight lanes per thread
+    // have their own (8-wave workgroups)
+    static constexpr int kClasses = 2;
+    static constexpr uint32_t kMaxR[kClasses] = {4, 8};
     int cus = 256;
     std::vector<uint32_t> dev_index;   // record -> index in d_recs (BF16) or d_raws (RAW)
     std::vector<uint32_t> rclass;      // record -> class (BF16)
     std::vector<uint32_t> cls_pos;     // record -> entry in its class list (BF16)
     std::vector<uint32_t> cls_recs[kClasses], cls_start[kClasses];
+    std::vector<uint32_t> cls_R[kClasses];   // lanes per thread of each class entry
     std::vector<bsd::RawDev> raws;
     bsd::RecDev* d_recs = nullptr;
-    uint32_t* d_cls_recs[kClasses] = {nullptr, nullptr, nullptr, nullptr};
-    uint32_t* d_cls_start[kClasses] = {nullptr, nullptr, nullptr, nullptr};
+    uint32_t* d_cls_recs[kClasses] = {nullptr, nullptr};
+    uint32_t* d_cls_start[kClasses] = {nullptr, nullptr};
     bsd::RawDev* d_raws = nullptr;
     uint8_t* d_luts = nullptr;
     unsigned long long* d_cmp = nullptr;   // compare results (2 words)
@@ -71,7 +74,7 @@ bs_status hip_err(hipError_t e, const char* what) {
 void ranges(const bs_plan* p, uint32_t first, uint32_t count, uint32_t* e0, uint32_t* e1, uint32_t& r0,
             uint32_t& r1) {
     r0 = r1 = 0;
-    bool have_e[bs_plan::kClasses] = {false, false, false, false}, have_r = false;
+    bool have_e[bs_plan::kClasses] = {false, false}, have_r = false;
     for (int k = 0; k < bs_plan::kClasses; k++) e0[k] = e1[k] = 0;
     for (uint32_t i = first; i < first + count; i++) {
         const Record& r = p->c.recs[i];
@@ -87,7 +90,7 @@ void ranges(const bs_plan* p, uint32_t first, uint32_t count, uint32_t* e0, uint
 }
 
 // Launch shape for the class entries [e0, e1) of class k: every record is cut
-// into runs of `run` chunks, one workgroup per run (a workgroup's tables and
+// into runs of `run` units (chunk streams), one workgroup per run (a workgroup's tables and
 // rings fill most of a CU's LDS, so one workgroup runs per CU).  `run` is the
 // smallest length whose run count fits the CUs; when the records alone
 // outnumber the CUs, runs are sized to the average share of a CU.
@@ -114,7 +117,7 @@ void launch_shape(const bs_plan* p, int k, uint32_t e0, uint32_t e1, uint32_t& w
         run = lo;
     }
     groups = (uint32_t)count(run);
-    waves = std::min<uint32_t>(bsd::max_waves(1u << k), run);
+    waves = std::min<uint32_t>(bsd::max_waves(bs_plan::kMaxR[k]), run);
 }
 
 uint64_t out_extent(const bs_plan* p, uint32_t first, uint32_t count) {
@@ -187,10 +190,11 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
         d.ftab_off = r.ftab_off;
         lut_bytes += (8ull << r.m_s) + (r.n_tables + 1ull) * bsd::kFPage;
         const uint32_t R = d.lanes_per_thread;
-        const uint32_t k = R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : 3;
+        const uint32_t k = R == 8 ? 1 : 0;
         p->rclass[i] = k;
         p->cls_pos[i] = (uint32_t)p->cls_recs[k].size();
         p->cls_recs[k].push_back((uint32_t)recs.size());
+        p->cls_R[k].push_back(R);
         p->cls_start[k].push_back(p->cls_start[k].back() + r.n_chunks * r.S);
         recs.push_back(d);
     }
@@ -272,7 +276,15 @@ bs_status bs_decode_async(const bs_plan* p, uint32_t first, uint32_t count, void
         a.i1 = e1[k];
         uint32_t groups;
         launch_shape(p, k, e0[k], e1[k], a.waves, a.run, groups);
-        int e = bsk_decode(&a, groups, 1u << k, stream);
+        // the specialised kernel when every record of the launch has the same
+        // lanes per thread, else the mixed one
+        uint32_t rmin = 8, rmax = 0;
+        for (uint32_t i = e0[k]; i < e1[k]; i++) {
+            const uint32_t R = p->cls_R[k][i];
+            rmin = std::min(rmin, R);
+            rmax = std::max(rmax, R);
+        }
+        int e = bsk_decode(&a, groups, rmin == rmax ? rmax : 0, stream);
         if (e) return hip_err((hipError_t)e, "decode launch");
     }
     if (r1 > r0) {
