@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--lanes", type=int, default=None, help="override the lanes per chunk of the workload")
     ap.add_argument("--chunk-weights", type=int, default=None, help="override the weights per chunk")
     ap.add_argument("--stream-lanes", type=int, default=None, help="override the lanes per word stream")
+    ap.add_argument("--m-s", type=int, default=None, help="override the (sign, exponent) table precision")
+    ap.add_argument("--m-f", type=int, default=None, help="override the fraction table precision")
     return ap.parse_args()
 
 
@@ -134,11 +136,12 @@ def main():
     t0 = time.time()
     if a.config == "5":
         from lossless_entropy_coding_amd import checkpoint
-        job = checkpoint.build_job(layers=a.cfg5_layers, log=log)
+        job = checkpoint.build_job(layers=a.cfg5_layers, log=log, **{k: v for k, v in (("m_s", a.m_s), ("m_f", a.m_f)) if v})
     else:
         gen_dev = "cuda" if a.config == "4" else "cpu"
         enc = workloads.encode_config(a.config, device=gen_dev, keep_reference=False, keep_device_reference=True,
-                                      lanes=a.lanes, chunk_weights=a.chunk_weights, stream_lanes=a.stream_lanes)
+                                      lanes=a.lanes, chunk_weights=a.chunk_weights, stream_lanes=a.stream_lanes,
+                                      m_s=a.m_s, m_f=a.m_f)
         job = workloads.DecodeJob(enc)
     log(f"workload {job.name}: {job.n_weights} BF16 weights, container {job.container_bytes / 1e6:.1f} MB, "
         f"built in {time.time() - t0:.1f}s")
@@ -222,7 +225,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": job.name, "bf16_weights": job.n_weights, "raw_bytes": job.raw_bytes,
                    "chunk_weights": job.chunk_weights, "lanes": job.lanes, "stream_lanes": job.stream_lanes,
-                   "m_s": 12, "m_f": 10,
+                   "m_s": job.m_s, "m_f": job.m_f,
                    "bits_per_weight": round(job.bits_per_weight, 5), "entropy_bits": round(job.entropy_bits, 5),
                    "bits_over_entropy_pct": round(100 * (job.bits_per_weight / job.entropy_bits - 1), 3),
                    "cold_cache": bool(a.cold), "parallelism": "single GPU"},

@@ -76,7 +76,8 @@ enum { BS_KIND_BF16 = 1, BS_KIND_RAW = 2 };
  * is a power of two: 1..64, 128, 256 or 512; stream_lanes P (0 = K) is a
  * power of two <= K: each chunk's lanes are split into word streams of P
  * lanes (fewer when a small record gets fewer lanes), which the decoder runs
- * on separate wavefronts; 9 <= m_s <= 12; 7 <= m_f <= 10; max_tables <= 6;
+ * on separate wavefronts; 9 <= m_s <= 12; 8 <= m_f <= 10 (the decoder multiplies
+ * x >> m in 24 bits, so m >= 8); max_tables <= 6;
  * threads = host encoder threads (0 = hardware count). */
 typedef struct {
     uint32_t chunk_weights;

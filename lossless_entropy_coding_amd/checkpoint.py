@@ -25,10 +25,11 @@ class CheckpointJob:
     """One Plan per layer container; decode() decodes every layer in order."""
 
     def __init__(self, layers: int = 84, chunk_weights: int = 65536, lanes: int = 128, log=print,
-                 device: str = "cuda", keep_host_first: bool = True):
+                 device: str = "cuda", keep_host_first: bool = True, m_s: int = 12, m_f: int = 10):
         layout = synth.cfg5_layout(layers=layers)
         self.name = "cfg5_checkpoint_%dlayers_%dtensors" % (layers, len(layout))
         self.chunk_weights, self.lanes, self.stream_lanes = chunk_weights, lanes, lanes
+        self.m_s, self.m_f = m_s, m_f
         self.lanes_per_thread = 1 if lanes <= 64 else lanes // 64
         self.plans, self.refs = [], []
         self.n_weights = self.raw_bytes = self.read_bytes = self.container_bytes = 0
@@ -38,6 +39,7 @@ class CheckpointJob:
         out_max = 16
         for layer in range(layers + 1):
             wl = synth.cfg5_layer(layer, device=device, chunk_weights=chunk_weights, lanes=lanes, layout=layout)
+            wl.m_s, wl.m_f = m_s, m_f
             enc = workloads.encode_workload(wl, device=device, keep_reference=False, keep_device_reference=True)
             plan = codec.Plan(enc.container, device)
             if layer == 0 and keep_host_first:

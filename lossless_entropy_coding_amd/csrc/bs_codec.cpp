@@ -272,7 +272,7 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
             set_error("record %u: bad chunk shape W=%u K=%u", i, r.W, K);
             return BS_E_FORMAT;
         }
-        if (r.m_s < 9 || r.m_s > 12 || r.m_f < 7 || r.m_f > 10 || r.n_tables > kMaxTables) {
+        if (r.m_s < 9 || r.m_s > 12 || r.m_f < 8 || r.m_f > 10 || r.n_tables > kMaxTables) {
             set_error("record %u: bad table parameters", i);
             return BS_E_FORMAT;
         }

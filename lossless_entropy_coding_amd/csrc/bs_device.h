@@ -9,31 +9,40 @@ constexpr uint32_t kStateLow = 65536u;      // lower end of the rANS state inter
 constexpr uint32_t kMaxTables = 6;          // coded fraction tables per record
 constexpr uint32_t kMaxSyms = 256;          // occupied (sign, exponent) symbols per BF16 record
 
-// LDS layout of one decode workgroup (bytes).
-//   [0, 32 KiB)            s lookup table: 2^M_s entries of 8 B (M_s <= 12)
-//   [32 KiB, 88 KiB)       fraction lookup tables: page t (8 KiB) = table t,
-//                          t = 0 flat, 1..6 coded; 2^M_f entries of 8 B (M_f <= 10)
-//   [88 KiB, ...)          one stream ring per wave
-constexpr uint32_t kSlutOff = 0;
-constexpr uint32_t kFlutOff = 32768;
-constexpr uint32_t kFPage = 8192;
-constexpr uint32_t kFPageShift = 13;
-constexpr uint32_t kLutLds = kFlutOff + (kMaxTables + 1) * kFPage;   // 90112
+// Two LDS layouts of a decode workgroup (bytes):
+//   full    (M_s <= 12, M_f <= 10): s lookup table, 2^M_s entries of 8 B, at 0
+//           (32 KiB); fraction lookup tables in pages of 8 KiB from 32 KiB
+//           (page t = table t, t = 0 flat, 1..6 coded; 2^M_f entries of 8 B);
+//           then one stream ring per wave, 2048 words (4096 for eight lanes
+//           per thread).  One 16-wave workgroup fills a CU's LDS.
+//   compact (M_s <= 11, M_f <= 9): the s table in 16 KiB, pages of 4 KiB from
+//           16 KiB, rings of 1024 words: 79,872 B, so that two 16-wave
+//           workgroups share a CU.
 constexpr uint32_t kRingMirror = 64;        // copy of the ring's first 64 words after its end
 constexpr uint32_t kMaxWaves = 16;
+constexpr uint32_t slut_bytes(bool compact) { return compact ? 16384u : 32768u; }
+constexpr uint32_t fpage_bytes(bool compact) { return compact ? 4096u : 8192u; }
+constexpr uint32_t lut_lds(bool compact) { return slut_bytes(compact) + (kMaxTables + 1) * fpage_bytes(compact); }
 
 // ring size (16-bit words, a power of two), ring bytes and the workgroup cap
-// for R lanes per thread: 2048 words and 16 waves up to R = 4; 4096 words and
-// 8 waves for R = 8 (it consumes up to 1024 words per weight position)
-constexpr uint32_t ring_words(uint32_t R) { return R >= 8 ? 4096u : 2048u; }
-constexpr uint32_t ring_bytes(uint32_t R) { return (ring_words(R) + kRingMirror) * 2u; }
+// for R lanes per thread.  A position consumes at most 2 * 64 * R words and
+// the ring is topped up to at least half full before each position, so it
+// needs at least 256 * R words.
+constexpr uint32_t ring_words(uint32_t R, bool compact) { return compact ? 1024u : (R >= 8 ? 4096u : 2048u); }
+constexpr uint32_t ring_bytes(uint32_t R, bool compact) { return (ring_words(R, compact) + kRingMirror) * 2u; }
 constexpr uint32_t max_waves(uint32_t R) { return R >= 8 ? 8u : 16u; }
+static_assert(ring_words(4, true) >= 256 * 4 && ring_words(4, false) >= 256 * 4 && ring_words(8, false) >= 256 * 8,
+              "ring too small for one position");
+static_assert(lut_lds(true) + 16 * ring_bytes(4, true) + 8 <= 81920, "compact layout must fit twice in 160 KiB");
+static_assert(lut_lds(false) + 16 * ring_bytes(4, false) + 8 <= 163840, "full layout must fit in 160 KiB");
+static_assert(lut_lds(false) + 8 * ring_bytes(8, false) + 8 <= 163840, "full layout must fit in 160 KiB");
 
 // Device lookup-table image of one record (built once per plan):
 //   s part: 2^M_s x {A, B}
 //     A = q_s | (page << 24), page = LDS address of the routed fraction table >> 11
+//     (in the record's LDS layout)
 //     B = s | (slot - cum_s) << 20
-//   f part: (n_tables + 1) pages of 8 KiB, each 2^M_f x {F0, F1}
+//   f part: (n_tables + 1) pages of fpage_bytes(compact), each 2^M_f x {F0, F1}
 //     F0 = q_f | f << 25, F1 = slot - cum_f
 struct RecDev {
     uint64_t body;          // byte offset of the record body in the container
@@ -49,6 +58,7 @@ struct RecDev {
     uint32_t lanes_per_thread;  // R = 1, 2, 4 or 8 (lanes per stream / 64, at least 1)
     uint32_t streams_log2;  // word streams per chunk = 2^streams_log2
     uint32_t P;             // lanes per stream (K >> streams_log2)
+    uint32_t compact;       // 1: compact LDS layout (M_s <= 11, M_f <= 9, R <= 4)
     uint32_t n_sym;
     uint32_t stab_off;      // byte offset (from body) of the s-table
     uint32_t route_off;     // byte offset (from body) of the route bytes
@@ -91,8 +101,9 @@ int bsk_hist_f(const uint16_t* d_w, uint64_t n, const int16_t* d_cand, unsigned 
 int bsk_build_luts(const uint8_t* d_container, const bsd::RecDev* d_recs, uint32_t n_recs, uint8_t* d_luts,
                    void* stream);
 // variant 1, 2, 4 or 8: every record of the launch has that many lanes per
-// thread; variant 0: a mix of 1, 2 and 4
-int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream);
+// thread; variant 0: a mix of 1 and 2; variant 3: a mix of 1, 2 and 4.
+// compact: the records use the compact LDS layout (not with variant 8).
+int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, bool compact, void* stream);
 int bsk_raw_copy(const uint8_t* d_container, const bsd::RawDev* d_raw, uint32_t n_raw, uint8_t* d_out,
                  uint64_t out_base, void* stream);
 int bsk_compare(const uint8_t* a, const uint8_t* b, uint64_t n, unsigned long long* d_result /*2*/, void* stream);

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void lut_kernel(const uint8_t* __restrict__ c,
     const uint32_t ns = 1u << r.m_s;
     for (uint32_t slot = threadIdx.x; slot < ns; slot += blockDim.x) {
         uint32_t s = last_le(cums, 512, slot);
-        uint32_t page = (kFlutOff + route[s] * kFPage) >> 11;
+        uint32_t page = (slut_bytes(r.compact) + route[s] * fpage_bytes(r.compact)) >> 11;
         out[slot] = make_uint2(qs[s] | (page << 24), s | ((slot - cums[s]) << 20));
     }
     uint2* fo = (uint2*)(luts + r.lut_off + 8ull * ns);
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void lut_kernel(const uint8_t* __restrict__ c,
     for (uint32_t i = threadIdx.x; i < nt * nf; i += blockDim.x) {
         uint32_t t = i / nf, slot = i % nf;
         uint32_t f = last_le(cumf[t], 128, slot);
-        fo[t * (kFPage / 8) + slot] = make_uint2(qf[t][f] | (f << 25), slot - cumf[t][f]);
+        fo[t * (fpage_bytes(r.compact) / 8) + slot] = make_uint2(qf[t][f] | (f << 25), slot - cumf[t][f]);
     }
 }
 
@@ -290,7 +290,7 @@ __device__ __forceinline__ uint32_t step_f(uint32_t& x, const uint2 se, const Mo
 
 // Decode unit u of a record: word stream st = u mod S of chunk ch = u / S,
 // whose P lanes are lanes [st * P, st * P + P) of the chunk.
-template <int R>
+template <int R, bool C>
 __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit, uint32_t wave, uint8_t* lds) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t ch = unit >> r.streams_log2;
@@ -323,9 +323,9 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
         const uint32_t l = 64 * q + lane;
         x[q] = l < P ? sp[l] : kStateLow;
     }
-    constexpr uint32_t RW = ring_words(R);
+    constexpr uint32_t RW = ring_words(R, C);
     Ring<RW> g;
-    g.base = (uint16_t*)(lds + kLutLds + wave * ring_bytes(R));
+    g.base = (uint16_t*)(lds + lut_lds(C) + wave * ring_bytes(R, C));
     g.words = words;
     g.bytes = (2 * nw + 15) & ~15u;
     ring_init(g, lane);
@@ -452,14 +452,15 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
 }
 
 // Stage one record's lookup tables into LDS (all threads of the workgroup).
+template <bool C>
 __device__ __forceinline__ void stage_luts(const DecodeArgs& a, const RecDev& r, uint8_t* lds) {
     const uint4* src = (const uint4*)(a.luts + r.lut_off);
     const uint32_t ns16 = (8u << r.m_s) / 16;
-    uint4* d = (uint4*)(lds + kSlutOff);
+    uint4* d = (uint4*)lds;
     for (uint32_t i = threadIdx.x; i < ns16; i += blockDim.x) d[i] = src[i];
-    const uint32_t nf16 = (r.n_tables + 1) * (kFPage / 16);
+    const uint32_t nf16 = (r.n_tables + 1) * (fpage_bytes(C) / 16);
     const uint4* fs = src + ns16;
-    uint4* fd = (uint4*)(lds + kFlutOff);
+    uint4* fd = (uint4*)(lds + slut_bytes(C));
     for (uint32_t i = threadIdx.x; i < nf16; i += blockDim.x) fd[i] = fs[i];
 }
 
@@ -469,16 +470,18 @@ __device__ __forceinline__ void stage_luts(const DecodeArgs& a, const RecDev& r,
 // are numbered in record order.  Wave 0 finds b's record with a prefix sum
 // over the records' run counts; the record's lookup tables are staged into
 // LDS once and the waves then take the run's units in turn.
-// One launch covers every record with 1, 2 or 4 lanes per thread (16 waves,
-// 2048-word rings), so that small tensors decode alongside large ones: G is
-// that lane width when all the launch's records share it, or 0 for a mix (the
-// width is then picked per workgroup).  Records with eight lanes per thread
-// (G = 8: 8 waves, 4096-word rings) have a launch of their own.
-template <int G>
+// One launch covers every record with 1, 2 or 4 lanes per thread (16-wave
+// workgroups), so that small tensors decode alongside large ones: G is that
+// lane width when all the launch's records share it, 0 for a mix of 1 and 2,
+// or 3 for a mix that includes 4 (the width is then picked per workgroup; the
+// narrower mix keeps the register count low enough for two workgroups per CU
+// in the compact layout).  Records with eight lanes per thread (G = 8:
+// 8 waves, 4096-word rings) have a launch of their own.
+template <int G, bool C>
 __global__ __launch_bounds__(G == 8 ? 512 : 1024) void decode_kernel(const DecodeArgs a) {
     // static allocation: the LDS base is a compile-time constant, so table and
     // ring addresses fold into the instructions' offsets
-    __shared__ __align__(16) uint8_t lds[kLutLds + max_waves(G ? G : 1) * ring_bytes(G ? G : 1)];
+    __shared__ __align__(16) uint8_t lds[lut_lds(C) + max_waves(G == 8 ? 8 : 1) * ring_bytes(G == 8 ? 8 : 1, C)];
     __shared__ uint32_t pick[2];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t b = blockIdx.x;
@@ -513,16 +516,17 @@ __global__ __launch_bounds__(G == 8 ? 512 : 1024) void decode_kernel(const Decod
     const RecDev r = a.recs[a.cls.recs[e]];
     const uint32_t u0 = __builtin_amdgcn_readfirstlane(pick[1]) * a.run;
     const uint32_t u1 = min(r.n_chunks << r.streams_log2, u0 + a.run);
-    stage_luts(a, r, lds);
+    stage_luts<C>(a, r, lds);
     __syncthreads();
-    if (G != 0) {
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<(G ? G : 1)>(a, r, u, wave, lds);
+    if (G == 1 || G == 2 || G == 4 || G == 8) {
+        constexpr int R = (G == 1 || G == 2 || G == 4 || G == 8) ? G : 1;
+        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<R, C>(a, r, u, wave, lds);
     } else if (r.lanes_per_thread == 1) {
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<1>(a, r, u, wave, lds);
-    } else if (r.lanes_per_thread == 2) {
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<2>(a, r, u, wave, lds);
+        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<1, C>(a, r, u, wave, lds);
+    } else if (G == 0 || r.lanes_per_thread == 2) {
+        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<2, C>(a, r, u, wave, lds);
     } else {
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<4>(a, r, u, wave, lds);
+        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<4, C>(a, r, u, wave, lds);
     }
 }
 
@@ -613,18 +617,30 @@ int bsk_build_luts(const uint8_t* d_container, const RecDev* d_recs, uint32_t n_
     return (int)hipGetLastError();
 }
 
-int bsk_decode(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream) {
+int bsk_decode(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, bool compact, void* stream) {
     if (n_groups == 0) return 0;
     const dim3 grid(n_groups), block(64 * args->waves);
     hipStream_t st = (hipStream_t)stream;
-    if (args->waves == 0 || args->waves > max_waves(variant ? variant : 1)) return (int)hipErrorInvalidValue;
-    switch (variant) {
-        case 0: hipLaunchKernelGGL(decode_kernel<0>, grid, block, 0, st, *args); break;
-        case 1: hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, st, *args); break;
-        case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, st, *args); break;
-        case 4: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, st, *args); break;
-        case 8: hipLaunchKernelGGL(decode_kernel<8>, grid, block, 0, st, *args); break;
-        default: return (int)hipErrorInvalidValue;
+    if (args->waves == 0 || args->waves > max_waves(variant == 8 ? 8 : 1)) return (int)hipErrorInvalidValue;
+    if (compact) {
+        switch (variant) {
+            case 0: hipLaunchKernelGGL((decode_kernel<0, true>), grid, block, 0, st, *args); break;
+            case 3: hipLaunchKernelGGL((decode_kernel<3, true>), grid, block, 0, st, *args); break;
+            case 1: hipLaunchKernelGGL((decode_kernel<1, true>), grid, block, 0, st, *args); break;
+            case 2: hipLaunchKernelGGL((decode_kernel<2, true>), grid, block, 0, st, *args); break;
+            case 4: hipLaunchKernelGGL((decode_kernel<4, true>), grid, block, 0, st, *args); break;
+            default: return (int)hipErrorInvalidValue;
+        }
+    } else {
+        switch (variant) {
+            case 0: hipLaunchKernelGGL((decode_kernel<0, false>), grid, block, 0, st, *args); break;
+            case 3: hipLaunchKernelGGL((decode_kernel<3, false>), grid, block, 0, st, *args); break;
+            case 1: hipLaunchKernelGGL((decode_kernel<1, false>), grid, block, 0, st, *args); break;
+            case 2: hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, st, *args); break;
+            case 4: hipLaunchKernelGGL((decode_kernel<4, false>), grid, block, 0, st, *args); break;
+            case 8: hipLaunchKernelGGL((decode_kernel<8, false>), grid, block, 0, st, *args); break;
+            default: return (int)hipErrorInvalidValue;
+        }
     }
     return (int)hipGetLastError();
 }

@@ -53,8 +53,8 @@ bool params_ok(const bs_params* p) {
         set_error("chunk_weights must be a positive multiple of 8*lanes (got %u)", p->chunk_weights);
         return false;
     }
-    if (p->m_s < 9 || p->m_s > 12 || p->m_f < 7 || p->m_f > 10 || p->max_tables > kMaxTables) {
-        set_error("need 9 <= m_s <= 12, 7 <= m_f <= 10, max_tables <= %u", kMaxTables);
+    if (p->m_s < 9 || p->m_s > 12 || p->m_f < 8 || p->m_f > 10 || p->max_tables > kMaxTables) {
+        set_error("need 9 <= m_s <= 12, 8 <= m_f <= 10, max_tables <= %u", kMaxTables);
         return false;
     }
     return true;

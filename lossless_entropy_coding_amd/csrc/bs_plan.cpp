@@ -30,10 +30,11 @@ struct bs_plan {
     uint64_t len = 0;
     Container c;
     // one record list per launch class: records with 1, 2 or 4 lanes per
-    // thread share one kernel (16-wave workgroups), eight lanes per thread
-    // have their own (8-wave workgroups)
-    static constexpr int kClasses = 2;
-    static constexpr uint32_t kMaxR[kClasses] = {4, 8};
+    // thread share one kernel (16-wave workgroups), in the full or the compact
+    // LDS layout; eight lanes per thread have their own (8-wave workgroups)
+    static constexpr int kClasses = 3;
+    static constexpr uint32_t kMaxR[kClasses] = {4, 4, 8};
+    static constexpr bool kCompact[kClasses] = {false, true, false};
     int cus = 256;
     std::vector<uint32_t> dev_index;   // record -> index in d_recs (BF16) or d_raws (RAW)
     std::vector<uint32_t> rclass;      // record -> class (BF16)
@@ -42,8 +43,8 @@ struct bs_plan {
     std::vector<uint32_t> cls_R[kClasses];   // lanes per thread of each class entry
     std::vector<bsd::RawDev> raws;
     bsd::RecDev* d_recs = nullptr;
-    uint32_t* d_cls_recs[kClasses] = {nullptr, nullptr};
-    uint32_t* d_cls_start[kClasses] = {nullptr, nullptr};
+    uint32_t* d_cls_recs[kClasses] = {nullptr, nullptr, nullptr};
+    uint32_t* d_cls_start[kClasses] = {nullptr, nullptr, nullptr};
     bsd::RawDev* d_raws = nullptr;
     uint8_t* d_luts = nullptr;
     unsigned long long* d_cmp = nullptr;   // compare results (2 words)
@@ -74,7 +75,7 @@ bs_status hip_err(hipError_t e, const char* what) {
 void ranges(const bs_plan* p, uint32_t first, uint32_t count, uint32_t* e0, uint32_t* e1, uint32_t& r0,
             uint32_t& r1) {
     r0 = r1 = 0;
-    bool have_e[bs_plan::kClasses] = {false, false}, have_r = false;
+    bool have_e[bs_plan::kClasses] = {false, false, false}, have_r = false;
     for (int k = 0; k < bs_plan::kClasses; k++) e0[k] = e1[k] = 0;
     for (uint32_t i = first; i < first + count; i++) {
         const Record& r = p->c.recs[i];
@@ -91,9 +92,9 @@ void ranges(const bs_plan* p, uint32_t first, uint32_t count, uint32_t* e0, uint
 
 // Launch shape for the class entries [e0, e1) of class k: every record is cut
 // into runs of `run` units (chunk streams), one workgroup per run (a workgroup's tables and
-// rings fill most of a CU's LDS, so one workgroup runs per CU).  `run` is the
-// smallest length whose run count fits the CUs; when the records alone
-// outnumber the CUs, runs are sized to the average share of a CU.
+// rings fill a CU's LDS, or half of it in the compact layout).  `run` is the
+// smallest length whose run count fits the workgroups that run at once; when
+// the records alone outnumber those, runs are sized to the average share.
 void launch_shape(const bs_plan* p, int k, uint32_t e0, uint32_t e1, uint32_t& waves, uint32_t& run,
                   uint32_t& groups) {
     const std::vector<uint32_t>& st = p->cls_start[k];
@@ -105,7 +106,11 @@ void launch_shape(const bs_plan* p, int k, uint32_t e0, uint32_t e1, uint32_t& w
         for (uint32_t e = e0; e < e1; e++) g += (st[e + 1] - st[e] + len - 1) / len;
         return g;
     };
-    const uint32_t cus = (uint32_t)p->cus;
+    // workgroups that run at once: one per CU, or two in the compact layout
+    // when their registers allow it (up to 2 lanes per thread)
+    uint32_t rmax = 0;
+    for (uint32_t e = e0; e < e1; e++) rmax = std::max(rmax, p->cls_R[k][e]);
+    const uint32_t cus = (uint32_t)p->cus * (bs_plan::kCompact[k] && rmax <= 2 ? 2 : 1);
     uint32_t lo = std::max<uint32_t>(1, (total + cus - 1) / cus), hi = std::max(lo, biggest);
     if (count(hi) > cus) {
         run = lo;
@@ -188,9 +193,10 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
         d.stab_off = r.stab_off;
         d.route_off = r.route_off;
         d.ftab_off = r.ftab_off;
-        lut_bytes += (8ull << r.m_s) + (r.n_tables + 1ull) * bsd::kFPage;
         const uint32_t R = d.lanes_per_thread;
-        const uint32_t k = R == 8 ? 1 : 0;
+        d.compact = R <= 4 && r.m_s <= 11 && r.m_f <= 9;
+        lut_bytes += (8ull << r.m_s) + (r.n_tables + 1ull) * bsd::fpage_bytes(d.compact);
+        const uint32_t k = R == 8 ? 2 : d.compact ? 1 : 0;
         p->rclass[i] = k;
         p->cls_pos[i] = (uint32_t)p->cls_recs[k].size();
         p->cls_recs[k].push_back((uint32_t)recs.size());
@@ -284,7 +290,8 @@ bs_status bs_decode_async(const bs_plan* p, uint32_t first, uint32_t count, void
             rmin = std::min(rmin, R);
             rmax = std::max(rmax, R);
         }
-        int e = bsk_decode(&a, groups, rmin == rmax ? rmax : 0, stream);
+        const uint32_t variant = rmin == rmax ? rmax : rmax <= 2 ? 0 : 3;
+        int e = bsk_decode(&a, groups, variant, bs_plan::kCompact[k], stream);
         if (e) return hip_err((hipError_t)e, "decode launch");
     }
     if (r1 > r0) {

@@ -34,6 +34,8 @@ class Workload:
     chunk_weights: int = 65536
     lanes: int = 64
     stream_lanes: int = 0     # lanes per word stream (0: one stream per chunk)
+    m_s: int = 12             # precision of the (sign, exponent) table
+    m_f: int = 10             # precision of the fraction tables
 
     @property
     def n_bf16(self) -> int:

@@ -46,7 +46,8 @@ class Encoded:
 
 def encode_workload(wl: synth.Workload, device: str = "cpu", keep_reference: bool = True,
                     keep_device_reference: bool = False, threads: int = 0) -> Encoded:
-    p = codec.params(chunk_weights=wl.chunk_weights, lanes=wl.lanes, threads=threads, stream_lanes=wl.stream_lanes)
+    p = codec.params(chunk_weights=wl.chunk_weights, lanes=wl.lanes, threads=threads, stream_lanes=wl.stream_lanes,
+                     m_s=wl.m_s, m_f=wl.m_f)
     tensors = []
     ent_sum, n_bf16 = 0.0, 0
     for it in wl.items:
@@ -65,7 +66,7 @@ def encode_workload(wl: synth.Workload, device: str = "cpu", keep_reference: boo
                   entropy_bits=ent_sum / n_bf16 if n_bf16 else math.nan,
                   bits_per_weight=8.0 * info.bf16_bytes / info.bf16_weights if info.bf16_weights else math.nan,
                   params=dict(chunk_weights=wl.chunk_weights, lanes=wl.lanes, stream_lanes=wl.stream_lanes or wl.lanes,
-                              m_s=12, m_f=10, max_tables=6))
+                              m_s=wl.m_s, m_f=wl.m_f, max_tables=6))
     if keep_reference or keep_device_reference:
         ref = np.zeros(info.out_len, np.uint8)
         for i, t in enumerate(tensors):
@@ -97,7 +98,7 @@ CONFIG_BUILDERS = {
 
 
 def encode_config(cfg: str, device: str = "cpu", lanes: int | None = None, chunk_weights: int | None = None,
-                  stream_lanes: int | None = None, **kw) -> Encoded:
+                  stream_lanes: int | None = None, m_s: int | None = None, m_f: int | None = None, **kw) -> Encoded:
     wl = CONFIG_BUILDERS[cfg](device)
     if lanes:
         wl.lanes = lanes
@@ -106,6 +107,10 @@ def encode_config(cfg: str, device: str = "cpu", lanes: int | None = None, chunk
         wl.chunk_weights = chunk_weights
     if stream_lanes is not None:
         wl.stream_lanes = stream_lanes
+    if m_s:
+        wl.m_s = m_s
+    if m_f:
+        wl.m_f = m_f
     if cfg == "4":
         kw.setdefault("keep_reference", False)
         kw.setdefault("keep_device_reference", True)
@@ -127,6 +132,7 @@ class DecodeJob:
         self.lanes = enc.params["lanes"]
         self.stream_lanes = enc.params["stream_lanes"]
         self.lanes_per_thread = max(1, self.stream_lanes // 64)
+        self.m_s, self.m_f = enc.params["m_s"], enc.params["m_f"]
         self.container_bytes = len(enc.container)
         info = codec.container_info(enc.container)
         # bytes a decode reads: BF16 record bytes (tables, index, states, words) and verbatim spans

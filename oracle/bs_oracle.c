@@ -612,7 +612,7 @@ int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* 
                          const uint64_t* n, const uint8_t* sha,
                          uint32_t Wmax, uint32_t Kmax, uint32_t Pmax, uint32_t M_s, uint32_t M_f, uint32_t cmax,
                          uint8_t** out, uint64_t* out_len) {
-    if (M_s < 9 || M_s > 12 || M_f < 7 || M_f > 10 || cmax > BSO_MAX_TABLES) return BSO_EINVAL;
+    if (M_s < 9 || M_s > 12 || M_f < 8 || M_f > 10 || cmax > BSO_MAX_TABLES) return BSO_EINVAL;
     if (!(Kmax <= 64 || Kmax == 128 || Kmax == 256 || Kmax == 512) || Kmax == 0) return BSO_EINVAL;
     if ((Kmax & (Kmax - 1)) != 0) return BSO_EINVAL;
     if (Pmax == 0 || (Pmax & (Pmax - 1)) != 0 || Pmax > Kmax) return BSO_EINVAL;
@@ -704,7 +704,7 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md
     if (b[15] > 9) return BSO_EFORMAT;
     *S = 1u << b[15];
     uint32_t n_sym = get32(b + 16);
-    if (md->M_s < 9 || md->M_s > 12 || md->M_f < 7 || md->M_f > 10 || md->n_tables > BSO_MAX_TABLES)
+    if (md->M_s < 9 || md->M_s > 12 || md->M_f < 8 || md->M_f > 10 || md->n_tables > BSO_MAX_TABLES)
         return BSO_EFORMAT;
     if (*K == 0 || *W == 0 || *W % (8 * *K)) return BSO_EFORMAT;
     if (!(*K <= 64 || *K == 128 || *K == 256 || *K == 512)) return BSO_EFORMAT;

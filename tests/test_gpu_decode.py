@@ -88,6 +88,33 @@ def test_decode_matches_oracle_and_original(name, n, scale, W, K, P):
     assert rep["chunks_bad"] == 0 and rep["records_hash_bad"] == 0
 
 
+COMPACT_CASES = [
+    # (name, n, scale, W, K, P, M_s, M_f): tables small enough for the compact LDS layout
+    ("compact_k128", 3 * 65536 + 999, 0.02, 65536, 128, 128, 11, 9),
+    ("compact_k128_p64", 2 * 65536 + 17, 0.05, 65536, 128, 64, 11, 9),
+    ("compact_k256_r4", 2 * 131072 + 3, 0.02, 131072, 256, 256, 11, 9),
+    ("compact_k32_small_tables", 50000 + 1, 0.02, 32768, 32, 32, 9, 8),
+    ("full_k128_ms11_mf10", 2 * 65536 + 5, 0.02, 65536, 128, 128, 11, 10),
+    ("k512_ms10_mf8", 262144 + 1001, 0.02, 262144, 512, 512, 10, 8),
+]
+
+
+@pytest.mark.parametrize("name,n,scale,W,K,P,ms,mf", COMPACT_CASES, ids=[c[0] for c in COMPACT_CASES])
+def test_decode_table_precisions(name, n, scale, W, K, P, ms, mf):
+    say("case", name, n, W, K, P, ms, mf)
+    rng = np.random.default_rng(n + ms)
+    x = rng.standard_normal(n) * scale
+    x[rng.random(n) < 0.01] = 0.0
+    w = _words(x)
+    c = codec.encode([codec.bf16(w)], codec.params(chunk_weights=W, lanes=K, stream_lanes=P, m_s=ms, m_f=mf))
+    assert c == O.encode([O.bf16(w)], W=W, K=K, P=P, M_s=ms, M_f=mf)
+    expect = _expected_bytes(c)
+    assert expect == w.tobytes()
+    plan, out, rc, rep, got = _decode_check(c, expect)
+    assert got == expect
+    assert rc == L.BS_OK, rep
+
+
 def test_special_values_and_residual():
     say("special values + residual")
     rng = np.random.default_rng(1)
@@ -113,8 +140,8 @@ def test_special_values_and_residual():
         assert host[ri.out_offset: ri.out_offset + nb] == expect[ri.out_offset: ri.out_offset + nb], i
 
 
-@pytest.mark.parametrize("stream_lanes", [0, 64])
-def test_many_records_mixed_lane_classes(stream_lanes):
+@pytest.mark.parametrize("stream_lanes,ms,mf", [(0, 12, 10), (64, 12, 10), (0, 11, 9), (64, 11, 9)])
+def test_many_records_mixed_lane_classes(stream_lanes, ms, mf):
     """Hundreds of records of ragged sizes in one container: small records get
     fewer lanes (other lanes-per-thread classes, or fewer word streams), more
     records than CUs, and records cut into several workgroup runs."""
@@ -128,7 +155,7 @@ def test_many_records_mixed_lane_classes(stream_lanes):
         tensors.append(codec.bf16(_words(x)))
         if i % 37 == 0:
             tensors.append(codec.raw(rng.integers(0, 256, int(rng.integers(1, 5000)), dtype=np.uint8)))
-    c = codec.encode(tensors, codec.params(chunk_weights=131072, lanes=256, stream_lanes=stream_lanes))
+    c = codec.encode(tensors, codec.params(chunk_weights=131072, lanes=256, stream_lanes=stream_lanes, m_s=ms, m_f=mf))
     info = codec.container_info(c)
     ris = [codec.record_info(c, i) for i in range(info.n_records)]
     bf = [ri for ri in ris if ri.kind == L.KIND_BF16 and ri.n]

@@ -160,7 +160,7 @@ def test_validation_errors():
 def test_bad_params_rejected():
     w = np.zeros(100, np.uint16)
     for kw in [dict(lanes=3), dict(lanes=96), dict(lanes=1024, chunk_weights=1 << 20), dict(lanes=64, stream_lanes=128),
-               dict(lanes=64, stream_lanes=48), dict(chunk_weights=100, lanes=8), dict(m_s=13), dict(m_f=6),
+               dict(lanes=64, stream_lanes=48), dict(chunk_weights=100, lanes=8), dict(m_s=13), dict(m_f=6), dict(m_f=7),
                dict(max_tables=7)]:
         with pytest.raises(L.BSError) as e:
             codec.encode([codec.bf16(w)], codec.params(**kw))

@@ -186,3 +186,15 @@ def test_bits_within_one_percent_cfg3():
     raw = sum(t.nbytes for t in tensors if t.kind == O.KIND_RAW)
     bpw = 8.0 * (len(c) - raw) / n
     assert bpw <= 1.01 * hsum / n
+
+
+def test_table_precision_range():
+    """M_s in 9..12 and M_f in 8..10 are the container's precisions; others
+    are refused (a fraction precision of 8 or more keeps x >> M_f below
+    2^24 for a 24-bit multiply)."""
+    w = np.full(64, 0x3F80, np.uint16)
+    for ms, mf in [(8, 10), (13, 10), (12, 7), (12, 11)]:
+        with pytest.raises(O.OracleError):
+            O.encode([O.bf16(w)], W=64, K=1, M_s=ms, M_f=mf)
+    for ms, mf in [(9, 8), (12, 10), (11, 9)]:
+        _rt([O.bf16(w)], W=64, K=1, M_s=ms, M_f=mf)
