@@ -203,7 +203,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                "kernel": "decode_kernel<%d>" % job.lanes_per_thread,
+                "kernel": job.kernel_name if hasattr(job, "kernel_name") else "decode_kernel",
                 "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(avg_ms, 4)}
 
     cpu = None

@@ -30,6 +30,8 @@ class CheckpointJob:
         self.name = "cfg5_checkpoint_%dlayers_%dtensors" % (layers, len(layout))
         self.chunk_weights, self.lanes, self.stream_lanes = chunk_weights, lanes, lanes
         self.m_s, self.m_f = m_s, m_f
+        # one mixed launch per layer: matrices (two lanes per thread) and vectors (one)
+        self.kernel_name = "decode_kernel<0, %s>" % ("true" if m_s <= 11 and m_f <= 9 else "false")
         self.lanes_per_thread = 1 if lanes <= 64 else lanes // 64
         self.plans, self.refs = [], []
         self.n_weights = self.raw_bytes = self.read_bytes = self.container_bytes = 0

@@ -133,6 +133,9 @@ class DecodeJob:
         self.stream_lanes = enc.params["stream_lanes"]
         self.lanes_per_thread = max(1, self.stream_lanes // 64)
         self.m_s, self.m_f = enc.params["m_s"], enc.params["m_f"]
+        # the decode kernel instance the workload's large records run on
+        compact = self.lanes_per_thread <= 4 and self.m_s <= 11 and self.m_f <= 9
+        self.kernel_name = "decode_kernel<%d, %s>" % (self.lanes_per_thread, "true" if compact else "false")
         self.container_bytes = len(enc.container)
         info = codec.container_info(enc.container)
         # bytes a decode reads: BF16 record bytes (tables, index, states, words) and verbatim spans
