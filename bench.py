@@ -69,6 +69,29 @@ def measured_traffic(job):
     return None if w is None else int(w["traffic_bytes"])
 
 
+def model_build_rate(job):
+    """bs_build_tables (the HIP histogram pass + host quantisation) on the
+    workload's first BF16 tensor, already in HBM: wall time per call."""
+    import torch
+    from lossless_entropy_coding_amd import codec
+    if not hasattr(job, "ref") or not hasattr(job, "plan"):
+        return None
+    ri = codec.record_info(job.plan.host, 0) if job.plan.host is not None else None
+    if ri is None or ri.kind != 1 or ri.n == 0:
+        return None
+    words = job.ref[ri.out_offset: ri.out_offset + 2 * ri.n].view(torch.int16)
+    p = codec.params(chunk_weights=job.chunk_weights, lanes=job.lanes, m_s=job.m_s, m_f=job.m_f)
+    codec.build_tables(words, p)          # warm-up
+    best = float("inf")
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        codec.build_tables(words, p)
+        best = min(best, time.perf_counter() - t0)
+    return {"weights": int(ri.n), "ms": round(best * 1e3, 3), "read_GB_s": round(2 * ri.n / best / 1e9, 1),
+            "what": "bs_build_tables wall time: one HIP histogram pass, the counts read back, host quantisation"}
+
+
 def cpu_baseline(job, seconds: float):
     """The CPU oracle (plain scalar C, one thread, not tuned) decoding the same
     container on the host: whole records while the budget lasts, else a sample
@@ -206,6 +229,8 @@ def main():
                 "kernel": job.kernel_name if hasattr(job, "kernel_name") else "decode_kernel",
                 "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(avg_ms, 4)}
 
+    model = model_build_rate(job)
+
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(job, a.cpu_seconds)
@@ -230,6 +255,7 @@ def main():
                    "bits_over_entropy_pct": round(100 * (job.bits_per_weight / job.entropy_bits - 1), 3),
                    "cold_cache": bool(a.cold), "parallelism": "single GPU"},
         "roofline": roofline,
+        "model_build": model,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

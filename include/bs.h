@@ -100,9 +100,10 @@ typedef struct bs_tables bs_tables; /* opaque, library-owned */
 /* Build the per-tensor model of n BF16 words that are resident on the device
  * [NVLC card, codec paragraph: the sign/exponent model is per tensor, the
  * fraction distribution is selected by the decoded symbol].
- * Two HIP histogram passes with LDS-privatised counters (sign/exponent, then
- * fraction counts of the 64 most frequent exponents), then host quantisation
- * of the counts to 2^m_s and 2^m_f and the choice of coded fraction contexts.
+ * One HIP histogram pass with LDS-privatised counters (fraction counts per
+ * exponent over both signs, and negative words per exponent), then host
+ * quantisation of the counts to 2^m_s and 2^m_f and the choice of coded
+ * fraction contexts.
  * d_bf16: n little-endian 16-bit words in device memory (any alignment of 2).
  * Synchronises `stream`.  *out receives a new bs_tables (free with
  * bs_tables_free).  Errors: BS_E_INVAL (bad params / NULL), BS_E_HIP,

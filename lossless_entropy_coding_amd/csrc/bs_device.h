@@ -96,8 +96,9 @@ struct DecodeArgs {
 
 // Launchers (bs_kernels.hip).  All return a hipError_t as int.
 extern "C" {
-int bsk_hist_s(const uint16_t* d_w, uint64_t n, unsigned long long* d_cs, void* stream);
-int bsk_hist_f(const uint16_t* d_w, uint64_t n, const int16_t* d_cand, unsigned long long* d_cf, void* stream);
+// d_cf: 256 x 128 counters (exponent, fraction; both signs), d_cneg: 256
+// counters (negative words per exponent); both zeroed by the caller
+int bsk_hist(const uint16_t* d_w, uint64_t n, unsigned long long* d_cf, unsigned long long* d_cneg, void* stream);
 int bsk_build_luts(const uint8_t* d_container, const bsd::RecDev* d_recs, uint32_t n_recs, uint8_t* d_luts,
                    void* stream);
 // variant 1, 2, 4 or 8: every record of the launch has that many lanes per

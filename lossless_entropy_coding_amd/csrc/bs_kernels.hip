@@ -6,8 +6,8 @@
 // distribution selected by s; non-BF16 spans are copied verbatim.
 //
 // Kernels:
-//   hist_s_kernel / hist_f_kernel  -- model building: field histograms with
-//                                     LDS-privatised counters
+//   hist_kernel                    -- model building: one pass of field
+//                                     histograms with LDS-privatised counters
 //   lut_kernel                     -- per-record decode lookup tables
 //   decode_kernel                  -- one wavefront per chunk: lane states in
 //                                     VGPRs, lookup tables in LDS, a per-wave
@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "bs_device.h"
 
 using namespace bsd;
@@ -30,15 +32,22 @@ namespace {
 
 constexpr int kHistThreads = 1024;
 
-// cs[s] for s = w >> 7 (9-bit sign/exponent symbol).  One 512-bin counter set
-// per wave in LDS (32 KiB) keeps hot-bin contention inside a wave.
-__global__ __launch_bounds__(kHistThreads) void hist_s_kernel(const uint16_t* __restrict__ w, uint64_t n,
-                                                               unsigned long long* __restrict__ cs) {
-    __shared__ uint32_t h[kHistThreads / 64][512];
-    uint32_t* hf = &h[0][0];
-    for (uint32_t i = threadIdx.x; i < (kHistThreads / 64) * 512; i += blockDim.x) hf[i] = 0;
+// One pass over the words of a tensor.  cf[e * 128 + f] counts exponent e and
+// fraction f over both signs (the sign-merged fraction counts that the choice
+// of coded contexts needs), and cneg[e] counts the negative words of exponent
+// e, from which the sign split of the (sign, exponent) histogram follows:
+// cs[256 + e] = cneg[e], cs[e] = sum_f cf[e][f] - cneg[e].  The counters are
+// privatised in LDS per workgroup (128 KiB + 8 KiB); the negative counts are
+// spread over 8 sub-bins by f mod 8, because a tensor's exponents concentrate
+// on a few values and same-address LDS atomics serialise.
+__global__ __launch_bounds__(kHistThreads) void hist_kernel(const uint16_t* __restrict__ w, uint64_t n,
+                                                             unsigned long long* __restrict__ cf,
+                                                             unsigned long long* __restrict__ cneg) {
+    __shared__ uint32_t hb[256 * 128];
+    __shared__ uint32_t hn[256 * 8];
+    for (uint32_t i = threadIdx.x; i < 256 * 128; i += blockDim.x) hb[i] = 0;
+    for (uint32_t i = threadIdx.x; i < 256 * 8; i += blockDim.x) hn[i] = 0;
     __syncthreads();
-    uint32_t* hw = h[threadIdx.x >> 6];
     // aligned body in 16-B pieces, head and tail word by word
     const uint64_t addr = (uint64_t)(uintptr_t)w;
     uint64_t head = ((16 - (addr & 15)) & 15) / 2;
@@ -48,64 +57,29 @@ __global__ __launch_bounds__(kHistThreads) void hist_s_kernel(const uint16_t* __
     const uint64_t gtid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const uint64_t gsz = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t i = gtid; i < body; i += gsz) {
-        uint4 v = p[i];
-        uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            atomicAdd(&hw[(d[k] & 0xFFFFu) >> 7], 1u);
-            atomicAdd(&hw[d[k] >> 23], 1u);
-        }
-    }
-    const uint64_t rest0 = head + body * 8;
-    for (uint64_t i = gtid; i < head + (n - rest0); i += gsz) {
-        uint64_t j = i < head ? i : rest0 + (i - head);
-        atomicAdd(&hw[w[j] >> 7], 1u);
-    }
-    __syncthreads();
-    for (uint32_t b = threadIdx.x; b < 512; b += blockDim.x) {
-        uint64_t s = 0;
-        for (int k = 0; k < kHistThreads / 64; k++) s += h[k][b];
-        if (s) atomicAdd(&cs[b], (unsigned long long)s);
-    }
-}
-
-// cf[c][f] for the candidate exponents: cand[e] = candidate index (0..63) of
-// exponent e (both signs), or -1.  One 64x128 counter set per workgroup.
-__global__ __launch_bounds__(kHistThreads) void hist_f_kernel(const uint16_t* __restrict__ w, uint64_t n,
-                                                               const int16_t* __restrict__ cand,
-                                                               unsigned long long* __restrict__ cf) {
-    __shared__ uint32_t h[64 * 128];
-    __shared__ int32_t cmap[256];
-    for (uint32_t i = threadIdx.x; i < 64 * 128; i += blockDim.x) h[i] = 0;
-    for (uint32_t i = threadIdx.x; i < 256; i += blockDim.x) cmap[i] = cand[i];
-    __syncthreads();
-    const uint64_t addr = (uint64_t)(uintptr_t)w;
-    uint64_t head = ((16 - (addr & 15)) & 15) / 2;
-    if (head > n) head = n;
-    const uint64_t body = (n - head) / 8;
-    const uint4* p = (const uint4*)(w + head);
-    const uint64_t gtid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const uint64_t gsz = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t i = gtid; i < body; i += gsz) {
-        uint4 v = p[i];
-        uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        const uint4 v = p[i];
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-            uint32_t x = (d[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-            int32_t c = cmap[(x >> 7) & 0xFF];
-            if (c >= 0) atomicAdd(&h[c * 128 + (x & 0x7F)], 1u);
+            const uint32_t x = (d[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+            atomicAdd(&hb[x & 0x7FFFu], 1u);
+            if (x & 0x8000u) atomicAdd(&hn[((x >> 4) & 0x7F8u) | (x & 7u)], 1u);
         }
     }
     const uint64_t rest0 = head + body * 8;
     for (uint64_t i = gtid; i < head + (n - rest0); i += gsz) {
-        uint64_t j = i < head ? i : rest0 + (i - head);
-        uint32_t x = w[j];
-        int32_t c = cmap[(x >> 7) & 0xFF];
-        if (c >= 0) atomicAdd(&h[c * 128 + (x & 0x7F)], 1u);
+        const uint64_t j = i < head ? i : rest0 + (i - head);
+        const uint32_t x = w[j];
+        atomicAdd(&hb[x & 0x7FFFu], 1u);
+        if (x & 0x8000u) atomicAdd(&hn[((x >> 4) & 0x7F8u) | (x & 7u)], 1u);
     }
     __syncthreads();
-    for (uint32_t b = threadIdx.x; b < 64 * 128; b += blockDim.x) {
-        if (h[b]) atomicAdd(&cf[b], (unsigned long long)h[b]);
+    for (uint32_t b = threadIdx.x; b < 256 * 128; b += blockDim.x)
+        if (hb[b]) atomicAdd(&cf[b], (unsigned long long)hb[b]);
+    for (uint32_t e = threadIdx.x; e < 256; e += blockDim.x) {
+        uint32_t t = 0;
+        for (int k = 0; k < 8; k++) t += hn[e * 8 + k];
+        if (t) atomicAdd(&cneg[e], (unsigned long long)t);
     }
 }
 
@@ -599,15 +573,14 @@ int bsk_device_cus(int* cus) {
     return (int)hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
 }
 
-int bsk_hist_s(const uint16_t* d_w, uint64_t n, unsigned long long* d_cs, void* stream) {
-    int g = grid_for(n, (uint64_t)kHistThreads * 32, 1024);
-    hipLaunchKernelGGL(hist_s_kernel, dim3(g), dim3(kHistThreads), 0, (hipStream_t)stream, d_w, n, d_cs);
-    return (int)hipGetLastError();
-}
-
-int bsk_hist_f(const uint16_t* d_w, uint64_t n, const int16_t* d_cand, unsigned long long* d_cf, void* stream) {
-    int g = grid_for(n, (uint64_t)kHistThreads * 32, 1024);
-    hipLaunchKernelGGL(hist_f_kernel, dim3(g), dim3(kHistThreads), 0, (hipStream_t)stream, d_w, n, d_cand, d_cf);
+int bsk_hist(const uint16_t* d_w, uint64_t n, unsigned long long* d_cf, unsigned long long* d_cneg, void* stream) {
+    // about a million words per workgroup: each workgroup zeroes and flushes
+    // 136 KiB of counters, so small tensors get few workgroups
+    int cus = 0;
+    if (bsk_device_cus(&cus) != 0 || cus <= 0) cus = 256;
+    const uint64_t want = (n + (1u << 20) - 1) >> 20;
+    const int g = (int)std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)cus));
+    hipLaunchKernelGGL(hist_kernel, dim3(g), dim3(kHistThreads), 0, (hipStream_t)stream, d_w, n, d_cf, d_cneg);
     return (int)hipGetLastError();
 }
 

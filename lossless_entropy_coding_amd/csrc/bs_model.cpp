@@ -209,48 +209,44 @@ bs_status bs_build_tables(const void* d_bf16, uint64_t n, const bs_params* p, vo
     if (!t) return BS_E_NOMEM;
     t->n = n;
     hipStream_t s = (hipStream_t)stream;
-    unsigned long long* d_cs = nullptr;
-    unsigned long long* d_cf = nullptr;
-    int16_t* d_cand = nullptr;
+    unsigned long long* d_cnt = nullptr;   // 256 x 128 sign-merged (exponent, fraction) counts, then 256 negative counts
     bs_status rc = BS_OK;
     std::vector<uint32_t> cand;
     std::vector<std::array<uint64_t, 128>> merged;
+    constexpr size_t kCounters = 256 * 128 + 256;
     auto hip_fail = [&](hipError_t e, const char* what) {
         set_error("%s: %s", what, hipGetErrorString(e));
         rc = BS_E_HIP;
     };
-    hipError_t e = hipMalloc(&d_cs, 512 * sizeof(unsigned long long));
-    if (e == hipSuccess) e = hipMalloc(&d_cf, 64 * 128 * sizeof(unsigned long long));
-    if (e == hipSuccess) e = hipMalloc(&d_cand, 256 * sizeof(int16_t));
+    hipError_t e = hipMalloc(&d_cnt, kCounters * sizeof(unsigned long long));
     if (e != hipSuccess) { hip_fail(e, "hipMalloc"); goto done; }
     if (n) {
-        e = hipMemsetAsync(d_cs, 0, 512 * sizeof(unsigned long long), s);
-        if (e == hipSuccess) e = (hipError_t)bsk_hist_s((const uint16_t*)d_bf16, n, d_cs, stream);
-        if (e == hipSuccess) e = hipMemcpyAsync(t->counts_s.data(), d_cs, 512 * 8, hipMemcpyDeviceToHost, s);
+        std::vector<unsigned long long> cnt(kCounters);
+        e = hipMemsetAsync(d_cnt, 0, kCounters * sizeof(unsigned long long), s);
+        if (e == hipSuccess) e = (hipError_t)bsk_hist((const uint16_t*)d_bf16, n, d_cnt, d_cnt + 256 * 128, stream);
+        if (e == hipSuccess) e = hipMemcpyAsync(cnt.data(), d_cnt, kCounters * 8, hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
-        if (e != hipSuccess) { hip_fail(e, "sign/exponent histogram"); goto done; }
+        if (e != hipSuccess) { hip_fail(e, "histogram"); goto done; }
+        // the (sign, exponent) counts: negatives counted directly, positives
+        // as the exponent's total minus its negatives
         uint64_t ec[256];
-        for (uint32_t x = 0; x < 256; x++) ec[x] = t->counts_s[x] + t->counts_s[256 + x];
+        for (uint32_t x = 0; x < 256; x++) {
+            uint64_t tot = 0;
+            for (uint32_t f = 0; f < 128; f++) tot += cnt[x * 128 + f];
+            const uint64_t neg = cnt[256 * 128 + x];
+            if (neg > tot) { set_error("histogram counts are inconsistent"); rc = BS_E_HIP; goto done; }
+            t->counts_s[256 + x] = neg;
+            t->counts_s[x] = tot - neg;
+            ec[x] = tot;
+        }
         cand = candidates(ec);
-        int16_t map[256];
-        for (int x = 0; x < 256; x++) map[x] = -1;
-        for (uint32_t c = 0; c < cand.size(); c++) map[cand[c]] = (int16_t)c;
-        std::vector<unsigned long long> cf(64 * 128);
-        e = hipMemcpyAsync(d_cand, map, sizeof(map), hipMemcpyHostToDevice, s);
-        if (e == hipSuccess) e = hipMemsetAsync(d_cf, 0, 64 * 128 * sizeof(unsigned long long), s);
-        if (e == hipSuccess) e = (hipError_t)bsk_hist_f((const uint16_t*)d_bf16, n, d_cand, d_cf, stream);
-        if (e == hipSuccess) e = hipMemcpyAsync(cf.data(), d_cf, cf.size() * 8, hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipStreamSynchronize(s);
-        if (e != hipSuccess) { hip_fail(e, "fraction histogram"); goto done; }
         merged.resize(cand.size());
         for (uint32_t c = 0; c < cand.size(); c++)
-            for (uint32_t f = 0; f < 128; f++) merged[c][f] = cf[c * 128 + f];
+            for (uint32_t f = 0; f < 128; f++) merged[c][f] = cnt[cand[c] * 128 + f];
     }
     if (!finish_model(*t, p, cand, merged)) rc = BS_E_INVAL;
 done:
-    if (d_cs) (void)hipFree(d_cs);
-    if (d_cf) (void)hipFree(d_cf);
-    if (d_cand) (void)hipFree(d_cand);
+    if (d_cnt) (void)hipFree(d_cnt);
     if (rc != BS_OK) { delete t; return rc; }
     *out = t;
     return BS_OK;
