@@ -60,7 +60,7 @@ def measured_traffic(job):
         with open(os.path.join(root, "profiles", "hbm_traffic.json")) as f:
             rec = json.load(f)
         src = b"".join(open(os.path.join(root, "lossless_entropy_coding_amd", "csrc", n), "rb").read()
-                       for n in ("bs_kernels.hip", "bs_device.h"))
+                       for n in ("bs_decode.hip", "bs_device.h"))
     except OSError:
         return None
     if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):

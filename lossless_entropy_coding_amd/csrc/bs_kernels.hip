@@ -5,16 +5,10 @@
 // symbol s is rANS-coded with a per-tensor model and the fraction f with the
 // distribution selected by s; non-BF16 spans are copied verbatim.
 //
-// Kernels:
+// Kernels here (the decode kernel is in bs_decode.hip):
 //   hist_kernel                    -- model building: one pass of field
 //                                     histograms with LDS-privatised counters
 //   lut_kernel                     -- per-record decode lookup tables
-//   decode_kernel                  -- one wavefront per chunk: lane states in
-//                                     VGPRs, lookup tables in LDS, a per-wave
-//                                     LDS ring of stream words filled with
-//                                     coalesced 16-B loads, refills addressed by
-//                                     a wavefront prefix count over the lanes
-//                                     that need a word, 128-bit output stores
 //   raw_copy_kernel                -- verbatim residual spans
 //   compare_kernel                 -- byte compare for verification
 #include <hip/hip_runtime.h>
@@ -143,367 +137,6 @@ __global__ __launch_bounds__(256) void lut_kernel(const uint8_t* __restrict__ c,
     }
 }
 
-// ------------------------------------------------------------------ decode
-
-// Ring loads go through a buffer resource (gfx9 descriptor: raw 32-bit
-// elements, no stride) whose base is the current stream position and whose
-// size is what is left of the chunk's word area: the hardware range check
-// returns zeros past the chunk's end, so the read-ahead never touches memory
-// outside it.  The per-lane offset is a loop-invariant VGPR, so an in-flight
-// load never pins a register that the loop overwrites.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const uint8_t* words, uint32_t bytes, uint32_t from) {
-    // every input is wave-uniform; readfirstlane keeps the descriptor in SGPRs
-    const uint64_t a = (uint64_t)(uintptr_t)(words + from);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const uint32_t left = __builtin_amdgcn_readfirstlane(bytes > from ? bytes - from : 0u);
-    const uint8_t* base = (const uint8_t*)(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)left, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 load_piece(__amdgpu_buffer_rsrc_t rs, uint32_t lane_off) {
-    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane_off, 0, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// Per-wave ring of stream words in LDS: RW words (2048, or 4096 for eight
-// lanes per thread) plus a 64-word copy of its head after its end, so that a
-// refill of up to 64 consecutive words never wraps.  Words are refilled RW/2
-// at a time (RW/1024 16-B pieces per lane), loaded one refill ahead.
-template <uint32_t RW>
-struct Ring {
-    static constexpr uint32_t kPieces = RW / 1024;   // 16-B pieces per lane per refill
-    uint16_t* base;       // LDS ring of this wave
-    uint4 pf[kPieces];    // the next RW/2 words, in flight
-    uint32_t fill;        // stream words written into the ring so far
-    const uint8_t* words; // the chunk's word area (uniform)
-    uint32_t bytes;       // its size, a multiple of 16
-    uint32_t lane;
-};
-
-template <uint32_t RW>
-__device__ __forceinline__ void ring_init(Ring<RW>& g, uint32_t lane) {
-    uint4* r4 = (uint4*)g.base;
-    g.lane = lane;
-    const __amdgpu_buffer_rsrc_t rs = stream_rsrc(g.words, g.bytes, 0);
-    uint4 first[Ring<RW>::kPieces];
-#pragma unroll
-    for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) first[k] = load_piece(rs, 16 * (64 * k + lane));
-#pragma unroll
-    for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) g.pf[k] = load_piece(rs, 16 * (64 * (Ring<RW>::kPieces + k) + lane));
-#pragma unroll
-    for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) r4[64 * k + lane] = first[k];
-    if (lane < kRingMirror / 8) r4[RW / 8 + lane] = first[0];
-    g.fill = RW / 2;
-}
-
-// keep at least RW/2 words ahead of `pos` in the ring (uniform branch)
-template <uint32_t RW>
-__device__ __forceinline__ void ring_top_up(Ring<RW>& g, uint32_t pos) {
-    if (g.fill - pos < RW / 2) {
-        uint4* r4 = (uint4*)g.base;
-        const uint32_t ro = (g.fill & (RW - 1)) >> 3;
-#pragma unroll
-        for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) r4[ro + 64 * k + g.lane] = g.pf[k];
-        if (ro == 0 && g.lane < kRingMirror / 8) r4[RW / 8 + g.lane] = g.pf[0];
-        const __amdgpu_buffer_rsrc_t rs = stream_rsrc(g.words, g.bytes, 2 * g.fill);
-#pragma unroll
-        for (uint32_t k = 0; k < Ring<RW>::kPieces; k++)
-            g.pf[k] = load_piece(rs, 16 * (64 * (Ring<RW>::kPieces + k) + g.lane));
-        g.fill += RW / 2;
-    }
-}
-
-// Renormalise the R groups of 64 lanes of one sub-step: lanes whose state
-// fell below 2^16 take the next stream words, group 0 first and ascending lane
-// order inside a group (a prefix count over the ballot).  Every lane reads
-// its candidate word (always a valid ring index) and keeps it only if it
-// needed one, so the R ring reads are in flight together.
-template <int R, uint32_t RW>
-__device__ __forceinline__ void refill_all(uint32_t (&x)[R], const bool (&active)[R], const Ring<RW>& g, uint32_t& pos) {
-    uint32_t sel[R], w[R];
-#pragma unroll
-    for (int q = 0; q < R; q++) {
-        const bool need = active[q] && x[q] < kStateLow;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(need);
-        const uint32_t pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        // byte selector of the merge, chosen while the word is in flight:
-        // (x << 16) | w for a refill, x unchanged otherwise
-        sel[q] = need ? 0x05040100u : 0x07060504u;
-        w[q] = g.base[(pos & (RW - 1)) + pre];
-        pos += (uint32_t)__builtin_popcountll(m);
-    }
-#pragma unroll
-    for (int q = 0; q < R; q++) x[q] = __builtin_amdgcn_perm(x[q], w[q], sel[q]);
-}
-
-struct Model {
-    const uint8_t* lds;
-    uint32_t m_s, m_f;
-    uint32_t smask8;      // (2^m_s - 1) << 3
-    uint32_t fmask8;      // (2^m_f - 1) << 3
-};
-
-// decode the s symbol of one weight for one lane; returns the s-entry
-__device__ __forceinline__ uint2 step_s(uint32_t& x, const Model& md) {
-    const uint2 e = *(const uint2*)(md.lds + ((x << 3) & md.smask8));
-    x = __umul24(x >> md.m_s, e.x) + (e.y >> 20);
-    return e;
-}
-
-// decode the fraction with the table the s-entry routes to; returns w (low 16 bits)
-__device__ __forceinline__ uint32_t step_f(uint32_t& x, const uint2 se, const Model& md) {
-    // the s-entry's top byte is the fraction table's LDS address >> 11, and
-    // its low 24 bits hold q_s <= 4096, so se.x >> 13 is that address exactly
-    const uint32_t addr = ((x << 3) & md.fmask8) | (se.x >> 13);
-    const uint2 e = *(const uint2*)(md.lds + addr);
-    x = __umul24(x >> md.m_f, e.x) + e.y;
-    return __builtin_amdgcn_alignbit(se.y, e.x, 25);
-}
-
-// Decode unit u of a record: word stream st = u mod S of chunk ch = u / S,
-// whose P lanes are lanes [st * P, st * P + P) of the chunk.
-template <int R, bool C>
-__device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit, uint32_t wave, uint8_t* lds) {
-    const uint32_t lane = threadIdx.x & 63;
-    const uint32_t ch = unit >> r.streams_log2;
-    const uint32_t st = unit & ((1u << r.streams_log2) - 1);
-    const uint8_t* body = a.container + r.body;
-    const uint8_t* ent = body + r.index_off + 16ull * ch;
-    const uint64_t poff = *(const uint64_t*)ent;
-    const uint8_t* payload = body + poff;
-    const uint32_t K = r.K, P = r.P, LB = st * P;
-    const uint64_t n_left = r.n - (uint64_t)ch * r.W;
-    const uint32_t n_c = (uint32_t)(n_left < r.W ? n_left : r.W);
-    // this stream's word count and the start of its words
-    const uint8_t* words = payload + ((4 * K + 15) & ~15u);
-    uint32_t nw;
-    if (r.streams_log2 == 0) {
-        nw = *(const uint32_t*)(ent + 8);
-    } else {
-        const uint32_t* counts = (const uint32_t*)words;
-        words += ((4u << r.streams_log2) + 15) & ~15u;
-        for (uint32_t k = 0; k < st; k++) words += (2 * counts[k] + 15) & ~15u;
-        nw = counts[st];
-    }
-
-    // lane states first, then the ring: both are complete before the loop so
-    // that no load issued here is still pending when the loop first runs
-    uint32_t x[R];
-    const uint32_t* sp = (const uint32_t*)payload + LB;
-#pragma unroll
-    for (int q = 0; q < R; q++) {
-        const uint32_t l = 64 * q + lane;
-        x[q] = l < P ? sp[l] : kStateLow;
-    }
-    constexpr uint32_t RW = ring_words(R, C);
-    Ring<RW> g;
-    g.base = (uint16_t*)(lds + lut_lds(C) + wave * ring_bytes(R, C));
-    g.words = words;
-    g.bytes = (2 * nw + 15) & ~15u;
-    ring_init(g, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-
-    const Model md{lds, r.m_s, r.m_f, ((1u << r.m_s) - 1) << 3, ((1u << r.m_f) - 1) << 3};
-
-    uint32_t pos = 0;
-    uint8_t* out = a.out + (r.out_off - a.out_base) + 2ull * ch * r.W;
-
-    const uint32_t groups = (n_c + 7) / 8;
-    const uint32_t T = (groups + K - 1) / K;
-    // macro-steps in which every lane decodes 8 weights, none of them a lane's
-    // last (that one is in the lane's start state, not in the stream): all
-    // full macro-steps but the last
-    const uint32_t T_full = (P % 64 == 0) ? n_c / (8 * K) : 0;
-    const uint32_t T_main = T_full ? T_full - 1 : 0;
-
-    bool all_on[R];
-#pragma unroll
-    for (int q = 0; q < R; q++) all_on[q] = true;
-
-    // full macro-steps: every lane decodes 8 weights, one 128-bit store per lane group
-    for (uint32_t t = 0; t < T_main; t++) {
-        uint32_t o[R][4];
-#pragma unroll
-        for (int p = 0; p < 8; p++) {
-            ring_top_up(g, pos);
-            uint2 se[R];
-#pragma unroll
-            for (int q = 0; q < R; q++) se[q] = step_s(x[q], md);
-            refill_all<R, RW>(x, all_on, g, pos);
-            uint32_t wv[R];
-#pragma unroll
-            for (int q = 0; q < R; q++) wv[q] = step_f(x[q], se[q], md);
-            refill_all<R, RW>(x, all_on, g, pos);
-#pragma unroll
-            for (int q = 0; q < R; q++) {
-                if (p & 1) o[q][p >> 1] = __builtin_amdgcn_perm(wv[q], o[q][p >> 1], 0x05040100u);
-                else o[q][p >> 1] = wv[q];
-                // pack now: keeps the table entries of earlier positions dead
-                // (otherwise the compiler sinks the packing to the store and
-                // keeps 8 positions of entries live)
-                asm volatile("" : "+v"(o[q][p >> 1]));
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < R; q++) {
-            uint4* op = (uint4*)out + (uint64_t)t * K + LB + 64 * q + lane;
-            *op = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
-        }
-    }
-
-    // remaining macro-steps (a lane's last weights, partial groups, or fewer
-    // than 64 lanes): lanes take part while they still have weights, and a
-    // lane's last weight is read off its state.  One position per iteration;
-    // each lane's eight output words move through a 128-bit shift register.
-    bool has[R];     // the lane has any weight in this chunk
-#pragma unroll
-    for (int q = 0; q < R; q++) has[q] = 64 * q + lane < P && 8ull * (LB + 64 * q + lane) < n_c;
-    for (uint32_t t = T_main; t < T; t++) {
-        int32_t cnt[R], last[R];
-        uint32_t o[R][4];
-#pragma unroll
-        for (int q = 0; q < R; q++) {
-            const uint32_t l = 64 * q + lane;
-            const int64_t left = (int64_t)n_c - 8 * ((int64_t)t * K + LB + l);
-            cnt[q] = l < P ? (int32_t)(left < 0 ? 0 : (left > 8 ? 8 : left)) : 0;
-            // the lane's last weight is in this macro-step when the next one
-            // has none of its weights
-            last[q] = (cnt[q] > 0 && left - 8 * (int64_t)K <= 0) ? cnt[q] - 1 : -1;
-#pragma unroll
-            for (int k = 0; k < 4; k++) o[q][k] = 0;
-        }
-#pragma unroll 1
-        for (int p = 0; p < 8; p++) {
-            ring_top_up(g, pos);
-            bool act[R];
-            uint2 se[R];
-#pragma unroll
-            for (int q = 0; q < R; q++) {
-                act[q] = p < cnt[q] && p != last[q];
-                uint32_t xs = x[q];
-                se[q] = step_s(xs, md);
-                if (act[q]) x[q] = xs;
-            }
-            refill_all<R, RW>(x, act, g, pos);
-#pragma unroll
-            for (int q = 0; q < R; q++) {
-                uint32_t xs = x[q];
-                uint32_t w = step_f(xs, se[q], md);
-                if (act[q]) x[q] = xs;
-                if (p == last[q]) w = x[q] - kStateLow;
-                // shift the 128-bit register right by 16 and insert w on top
-                o[q][0] = __builtin_amdgcn_alignbit(o[q][1], o[q][0], 16);
-                o[q][1] = __builtin_amdgcn_alignbit(o[q][2], o[q][1], 16);
-                o[q][2] = __builtin_amdgcn_alignbit(o[q][3], o[q][2], 16);
-                o[q][3] = __builtin_amdgcn_alignbit(w, o[q][3], 16);
-            }
-            refill_all<R, RW>(x, act, g, pos);
-        }
-#pragma unroll
-        for (int q = 0; q < R; q++) {
-            const uint64_t g16 = (uint64_t)t * K + LB + 64 * q + lane;
-            if (cnt[q] == 8) {
-                ((uint4*)out)[g16] = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
-            } else if (cnt[q] > 0) {
-                uint16_t* o16 = (uint16_t*)out + 8 * g16;
-#pragma unroll
-                for (int k = 0; k < 8; k++)
-                    if (k < cnt[q]) o16[k] = (uint16_t)(o[q][k >> 1] >> (16 * (k & 1)));
-            }
-        }
-    }
-
-    // a stream is whole when every lane ends at the state its encoder
-    // started from (2^16 plus its last weight; 2^16 for a lane without
-    // weights) and exactly the stream's words were consumed
-    bool bad = false;
-#pragma unroll
-    for (int q = 0; q < R; q++) bad |= has[q] ? (x[q] - kStateLow) > 0xFFFFu : x[q] != kStateLow;
-    const uint64_t badm = __builtin_amdgcn_ballot_w64(bad);
-    if (lane == 0) a.status[r.status_base + unit] = (badm ? 1u : 0u) | (pos != nw ? 2u : 0u);
-}
-
-// Stage one record's lookup tables into LDS (all threads of the workgroup).
-template <bool C>
-__device__ __forceinline__ void stage_luts(const DecodeArgs& a, const RecDev& r, uint8_t* lds) {
-    const uint4* src = (const uint4*)(a.luts + r.lut_off);
-    const uint32_t ns16 = (8u << r.m_s) / 16;
-    uint4* d = (uint4*)lds;
-    for (uint32_t i = threadIdx.x; i < ns16; i += blockDim.x) d[i] = src[i];
-    const uint32_t nf16 = (r.n_tables + 1) * (fpage_bytes(C) / 16);
-    const uint4* fs = src + ns16;
-    uint4* fd = (uint4*)(lds + slut_bytes(C));
-    for (uint32_t i = threadIdx.x; i < nf16; i += blockDim.x) fd[i] = fs[i];
-}
-
-// Workgroup b of a launch decodes one run of units (chunk streams) inside one
-// record: each record r of the class entries [i0, i1) is cut into
-// ceil(units_r / run) runs of `run` units (the last one shorter), and the runs
-// are numbered in record order.  Wave 0 finds b's record with a prefix sum
-// over the records' run counts; the record's lookup tables are staged into
-// LDS once and the waves then take the run's units in turn.
-// One launch covers every record with 1, 2 or 4 lanes per thread (16-wave
-// workgroups), so that small tensors decode alongside large ones: G is that
-// lane width when all the launch's records share it, 0 for a mix of 1 and 2,
-// or 3 for a mix that includes 4 (the width is then picked per workgroup; the
-// narrower mix keeps the register count low enough for two workgroups per CU
-// in the compact layout).  Records with eight lanes per thread (G = 8:
-// 8 waves, 4096-word rings) have a launch of their own.
-template <int G, bool C>
-__global__ __launch_bounds__(G == 8 ? 512 : 1024) void decode_kernel(const DecodeArgs a) {
-    // static allocation: the LDS base is a compile-time constant, so table and
-    // ring addresses fold into the instructions' offsets
-    __shared__ __align__(16) uint8_t lds[lut_lds(C) + max_waves(G == 8 ? 8 : 1) * ring_bytes(G == 8 ? 8 : 1, C)];
-    __shared__ uint32_t pick[2];
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t b = blockIdx.x;
-    if (wave == 0) {
-        const uint32_t lane = threadIdx.x & 63;
-        uint32_t carry = 0, e = UINT32_MAX, j = 0;
-        for (uint32_t base = a.i0; base < a.i1; base += 64) {
-            const uint32_t i = base + lane;
-            uint32_t k = 0;
-            if (i < a.i1) k = (a.cls.start[i + 1] - a.cls.start[i] + a.run - 1) / a.run;
-            uint32_t incl = k;
-            for (int d = 1; d < 64; d <<= 1) {
-                const uint32_t v = __shfl_up(incl, d, 64);
-                if (lane >= (uint32_t)d) incl += v;
-            }
-            const uint32_t excl = carry + incl - k;
-            const unsigned long long hit = __ballot(k != 0 && excl <= b && b < excl + k);
-            if (hit) {
-                const int src = __ffsll(hit) - 1;
-                e = __shfl(i, src, 64);
-                j = b - __shfl(excl, src, 64);
-                break;
-            }
-            carry += __shfl(incl, 63, 64);
-        }
-        if (lane == 0) { pick[0] = e; pick[1] = j; }
-    }
-    __syncthreads();
-    // the picked run is the same for every wave: keep it in scalar registers
-    const uint32_t e = __builtin_amdgcn_readfirstlane(pick[0]);
-    if (e == UINT32_MAX) return;   // no run for this workgroup (launch larger than the runs)
-    const RecDev r = a.recs[a.cls.recs[e]];
-    const uint32_t u0 = __builtin_amdgcn_readfirstlane(pick[1]) * a.run;
-    const uint32_t u1 = min(r.n_chunks << r.streams_log2, u0 + a.run);
-    stage_luts<C>(a, r, lds);
-    __syncthreads();
-    if (G == 1 || G == 2 || G == 4 || G == 8) {
-        constexpr int R = (G == 1 || G == 2 || G == 4 || G == 8) ? G : 1;
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<R, C>(a, r, u, wave, lds);
-    } else if (r.lanes_per_thread == 1) {
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<1, C>(a, r, u, wave, lds);
-    } else if (G == 0 || r.lanes_per_thread == 2) {
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<2, C>(a, r, u, wave, lds);
-    } else {
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<4, C>(a, r, u, wave, lds);
-    }
-}
-
 // ------------------------------------------------------------------ residual and compare
 
 __global__ __launch_bounds__(256) void raw_copy_kernel(const uint8_t* __restrict__ c, const RawDev* __restrict__ raw,
@@ -587,34 +220,6 @@ int bsk_hist(const uint16_t* d_w, uint64_t n, unsigned long long* d_cf, unsigned
 int bsk_build_luts(const uint8_t* d_container, const RecDev* d_recs, uint32_t n_recs, uint8_t* d_luts, void* stream) {
     if (n_recs == 0) return 0;
     hipLaunchKernelGGL(lut_kernel, dim3(n_recs), dim3(256), 0, (hipStream_t)stream, d_container, d_recs, d_luts);
-    return (int)hipGetLastError();
-}
-
-int bsk_decode(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, bool compact, void* stream) {
-    if (n_groups == 0) return 0;
-    const dim3 grid(n_groups), block(64 * args->waves);
-    hipStream_t st = (hipStream_t)stream;
-    if (args->waves == 0 || args->waves > max_waves(variant == 8 ? 8 : 1)) return (int)hipErrorInvalidValue;
-    if (compact) {
-        switch (variant) {
-            case 0: hipLaunchKernelGGL((decode_kernel<0, true>), grid, block, 0, st, *args); break;
-            case 3: hipLaunchKernelGGL((decode_kernel<3, true>), grid, block, 0, st, *args); break;
-            case 1: hipLaunchKernelGGL((decode_kernel<1, true>), grid, block, 0, st, *args); break;
-            case 2: hipLaunchKernelGGL((decode_kernel<2, true>), grid, block, 0, st, *args); break;
-            case 4: hipLaunchKernelGGL((decode_kernel<4, true>), grid, block, 0, st, *args); break;
-            default: return (int)hipErrorInvalidValue;
-        }
-    } else {
-        switch (variant) {
-            case 0: hipLaunchKernelGGL((decode_kernel<0, false>), grid, block, 0, st, *args); break;
-            case 3: hipLaunchKernelGGL((decode_kernel<3, false>), grid, block, 0, st, *args); break;
-            case 1: hipLaunchKernelGGL((decode_kernel<1, false>), grid, block, 0, st, *args); break;
-            case 2: hipLaunchKernelGGL((decode_kernel<2, false>), grid, block, 0, st, *args); break;
-            case 4: hipLaunchKernelGGL((decode_kernel<4, false>), grid, block, 0, st, *args); break;
-            case 8: hipLaunchKernelGGL((decode_kernel<8, false>), grid, block, 0, st, *args); break;
-            default: return (int)hipErrorInvalidValue;
-        }
-    }
     return (int)hipGetLastError();
 }
 
