@@ -159,7 +159,9 @@ def main():
     t0 = time.time()
     if a.config == "5":
         from lossless_entropy_coding_amd import checkpoint
-        job = checkpoint.build_job(layers=a.cfg5_layers, log=log, **{k: v for k, v in (("m_s", a.m_s), ("m_f", a.m_f)) if v})
+        over = {k: v for k, v in (("m_s", a.m_s), ("m_f", a.m_f), ("lanes", a.lanes), ("chunk_weights", a.chunk_weights),
+                                  ("stream_lanes", a.stream_lanes)) if v}
+        job = checkpoint.build_job(layers=a.cfg5_layers, log=log, **over)
     else:
         gen_dev = "cuda" if a.config == "4" else "cpu"
         enc = workloads.encode_config(a.config, device=gen_dev, keep_reference=False, keep_device_reference=True,

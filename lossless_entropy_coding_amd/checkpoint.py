@@ -24,15 +24,17 @@ from . import codec, synth, workloads
 class CheckpointJob:
     """One Plan per layer container; decode() decodes every layer in order."""
 
-    def __init__(self, layers: int = 84, chunk_weights: int = 65536, lanes: int = 128, log=print,
-                 device: str = "cuda", keep_host_first: bool = True, m_s: int = 12, m_f: int = 10):
+    def __init__(self, layers: int = 84, chunk_weights: int = 65536, lanes: int = 256, log=print,
+                 device: str = "cuda", keep_host_first: bool = True, m_s: int = 12, m_f: int = 10,
+                 stream_lanes: int = 0):
         layout = synth.cfg5_layout(layers=layers)
         self.name = "cfg5_checkpoint_%dlayers_%dtensors" % (layers, len(layout))
-        self.chunk_weights, self.lanes, self.stream_lanes = chunk_weights, lanes, lanes
+        self.chunk_weights, self.lanes, self.stream_lanes = chunk_weights, lanes, stream_lanes or lanes
         self.m_s, self.m_f = m_s, m_f
-        # one mixed launch per layer: matrices (two lanes per thread) and vectors (one)
-        self.kernel_name = "decode_kernel<0, %s>" % ("true" if m_s <= 11 and m_f <= 9 else "false")
-        self.lanes_per_thread = 1 if lanes <= 64 else lanes // 64
+        self.lanes_per_thread = max(1, self.stream_lanes // 64)
+        # one mixed launch per layer: matrices (several lanes per thread) and vectors (one)
+        self.kernel_name = "decode_kernel<%d, %s>" % (0 if self.lanes_per_thread <= 2 else 3,
+                                                      "true" if m_s <= 11 and m_f <= 9 else "false")
         self.plans, self.refs = [], []
         self.n_weights = self.raw_bytes = self.read_bytes = self.container_bytes = 0
         bits = ent = 0.0
@@ -41,7 +43,7 @@ class CheckpointJob:
         out_max = 16
         for layer in range(layers + 1):
             wl = synth.cfg5_layer(layer, device=device, chunk_weights=chunk_weights, lanes=lanes, layout=layout)
-            wl.m_s, wl.m_f = m_s, m_f
+            wl.m_s, wl.m_f, wl.stream_lanes = m_s, m_f, stream_lanes
             enc = workloads.encode_workload(wl, device=device, keep_reference=False, keep_device_reference=True)
             plan = codec.Plan(enc.container, device)
             if layer == 0 and keep_host_first:

@@ -85,6 +85,11 @@ def _with_streams(wl: synth.Workload, stream_lanes: int) -> synth.Workload:
     return wl
 
 
+# The Gemma-2-9B layer and the 27.7B checkpoint's layers fill the GPU only
+# about once: 256 lanes per 128 KiB chunk (256 weights per lane) give more
+# wavefronts than 128 lanes, for about 0.25% more size; the 917M-weight
+# embedding keeps 128 lanes, because it is bound by VALU issue and more lanes
+# only add state overhead.
 # The 4096x4096 matrix is only 128 chunks of 256 KiB: 512 lanes per chunk
 # (256 weights per lane) still keep the lane-state overhead inside the 1% size
 # budget, and streams of 64 lanes let eight wavefronts decode each chunk, so
@@ -92,7 +97,7 @@ def _with_streams(wl: synth.Workload, stream_lanes: int) -> synth.Workload:
 CONFIG_BUILDERS = {
     "1": lambda device: synth.cfg1(device),
     "2": lambda device: _with_streams(synth.cfg2(device, lanes=512), 64),
-    "3": lambda device: synth.cfg3(device),
+    "3": lambda device: synth.cfg3(device, lanes=256),
     "4": lambda device: synth.cfg4(device),
 }
 
