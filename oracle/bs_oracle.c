@@ -504,6 +504,39 @@ static int bb_reserve(bytebuf* b, uint64_t need) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* Final lane states of a chunk, packed.  A state x in [2^16, 2^32) is       */
+/* written as its length code e = floor(log2 x) - 16 (0..15, one nibble per */
+/* lane, lane l in the low nibble of byte l/2 when l is even) and its 16 + e */
+/* bits below the leading one.  Those bits are concatenated in lane order,   */
+/* least significant first, from bit 0 of the mantissa block.                */
+/* ------------------------------------------------------------------------ */
+static uint32_t state_code(uint32_t x) {
+    uint32_t e = 0;
+    while (e < 15 && (x >> (17 + e)) != 0) e++;
+    return e;
+}
+
+/* bytes of the nibble block and of the mantissa block for K lanes whose codes sum to esum */
+static uint64_t code_block_bytes(uint32_t K) { return round_up(((uint64_t)K + 1) / 2, 16); }
+static uint64_t mant_block_bytes(uint32_t K, uint64_t esum) { return round_up((16ull * K + esum + 7) / 8, 16); }
+
+static void put_bits(uint8_t* b, uint64_t off, uint32_t v, uint32_t len) {
+    for (uint32_t i = 0; i < len; i++) {
+        uint64_t bit = off + i;
+        if ((v >> i) & 1u) b[bit / 8] |= (uint8_t)(1u << (bit % 8));
+    }
+}
+
+static uint32_t get_bits(const uint8_t* b, uint64_t off, uint32_t len) {
+    uint32_t v = 0;
+    for (uint32_t i = 0; i < len; i++) {
+        uint64_t bit = off + i;
+        v |= (uint32_t)((b[bit / 8] >> (bit % 8)) & 1u) << i;
+    }
+    return v;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Encode one BF16 record body.                                              */
 /* ------------------------------------------------------------------------ */
 static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32_t Kmax, uint32_t Pmax,
@@ -557,8 +590,9 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
     for (uint32_t t = 1; t <= md->n_tables; t++)
         for (uint32_t f = 0; f < 128; f++) put16(b + ft + 256ull * (t - 1) + 2 * f, md->qf[t][f]);
 
-    /* chunks: states of all K lanes, then (S > 1) the S stream word counts,
-       then each stream's words; every part padded to 16 bytes */
+    /* chunks: the K lanes' length codes, then (S > 1) the S stream word
+       counts, then the states' mantissa bits, then each stream's words;
+       every part padded to 16 bytes */
     uint32_t* states = (uint32_t*)malloc(sizeof(uint32_t) * K);
     wordlist* wls = (wordlist*)calloc(S, sizeof(wordlist));
     if (!states || !wls) { free(states); free(wls); rc = BSO_ENOMEM; goto done; }
@@ -568,10 +602,13 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
         for (uint32_t st = 0; st < S && !rc; st++)
             rc = chunk_encode(md, w + c * W, n_c, K, st * P, (st + 1) * P, states, &wls[st]);
         if (rc) break;
+        uint64_t esum = 0;
+        for (uint32_t l = 0; l < K; l++) esum += state_code(states[l]);
         uint64_t start = body->n;
-        uint64_t states_bytes = round_up(4ull * K, 16);
+        uint64_t code_bytes = code_block_bytes(K);
         uint64_t counts_bytes = S > 1 ? round_up(4ull * S, 16) : 0;
-        uint64_t end = start + states_bytes + counts_bytes, total_words = 0;
+        uint64_t mant_bytes = mant_block_bytes(K, esum);
+        uint64_t end = start + code_bytes + counts_bytes + mant_bytes, total_words = 0;
         for (uint32_t st = 0; st < S; st++) { end += round_up(2 * wls[st].n, 16); total_words += wls[st].n; }
         rc = bb_reserve(body, end);
         if (rc) break;
@@ -580,11 +617,17 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
         put64(b + index_off + 16 * c, start);
         put32(b + index_off + 16 * c + 8, (uint32_t)total_words);
         put32(b + index_off + 16 * c + 12, 0);
-        for (uint32_t l = 0; l < K; l++) put32(b + start + 4ull * l, states[l]);
-        uint64_t at = start + states_bytes;
+        uint64_t moff = 0;
+        uint8_t* mant = b + start + code_bytes + counts_bytes;
+        for (uint32_t l = 0; l < K; l++) {
+            uint32_t e = state_code(states[l]);
+            b[start + l / 2] |= (uint8_t)(e << (4 * (l % 2)));
+            put_bits(mant, moff, states[l] - (1u << (16 + e)), 16 + e);
+            moff += 16 + e;
+        }
         if (S > 1)
-            for (uint32_t st = 0; st < S; st++) put32(b + at + 4ull * st, (uint32_t)wls[st].n);
-        at += counts_bytes;
+            for (uint32_t st = 0; st < S; st++) put32(b + start + code_bytes + 4ull * st, (uint32_t)wls[st].n);
+        uint64_t at = start + code_bytes + counts_bytes + mant_bytes;
         for (uint32_t st = 0; st < S; st++) {
             /* the encoder pushes words in reverse order of their use */
             for (uint64_t i = 0; i < wls[st].n; i++) put16(b + at + 2 * i, wls[st].w[wls[st].n - 1 - i]);
@@ -613,9 +656,9 @@ int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* 
                          uint32_t Wmax, uint32_t Kmax, uint32_t Pmax, uint32_t M_s, uint32_t M_f, uint32_t cmax,
                          uint8_t** out, uint64_t* out_len) {
     if (M_s < 9 || M_s > 12 || M_f < 8 || M_f > 10 || cmax > BSO_MAX_TABLES) return BSO_EINVAL;
-    if (!(Kmax <= 64 || Kmax == 128 || Kmax == 256 || Kmax == 512) || Kmax == 0) return BSO_EINVAL;
+    if (!(Kmax <= 64 || Kmax == 128 || Kmax == 256 || Kmax == 512 || Kmax == 1024) || Kmax == 0) return BSO_EINVAL;
     if ((Kmax & (Kmax - 1)) != 0) return BSO_EINVAL;
-    if (Pmax == 0 || (Pmax & (Pmax - 1)) != 0 || Pmax > Kmax) return BSO_EINVAL;
+    if (Pmax == 0 || (Pmax & (Pmax - 1)) != 0 || Pmax > Kmax || Pmax > 512) return BSO_EINVAL;
     bytebuf c = {0, 0, 0};
     uint64_t dir = BSO_HDR_BYTES;
     uint64_t pos = round_up(dir + (uint64_t)BSO_DIR_BYTES * n_tensors, 16);
@@ -707,8 +750,8 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md
     if (md->M_s < 9 || md->M_s > 12 || md->M_f < 8 || md->M_f > 10 || md->n_tables > BSO_MAX_TABLES)
         return BSO_EFORMAT;
     if (*K == 0 || *W == 0 || *W % (8 * *K)) return BSO_EFORMAT;
-    if (!(*K <= 64 || *K == 128 || *K == 256 || *K == 512)) return BSO_EFORMAT;
-    if (*K % *S) return BSO_EFORMAT;
+    if (!(*K <= 64 || *K == 128 || *K == 256 || *K == 512 || *K == 1024)) return BSO_EFORMAT;
+    if (*K % *S || *K / *S > 512) return BSO_EFORMAT;
     if (*n_chunks != (n + *W - 1) / *W) return BSO_EFORMAT;
     if (n_sym > BSO_MAX_SYMS || (n_sym == 0) != (n == 0)) return BSO_EFORMAT;
     uint64_t off = 24;
@@ -744,16 +787,26 @@ static int decode_one_chunk(const bso_model* md, const uint8_t* b, uint64_t rl, 
                             uint32_t S, uint64_t ch, uint32_t n_c, uint16_t* out) {
     const uint8_t* e = b + io + 16 * ch;
     uint64_t po = get64(e), nw = get32(e + 8);
-    uint64_t sb = round_up(4ull * K, 16), cb = S > 1 ? round_up(4ull * S, 16) : 0;
-    if (po % 16 || po > rl || sb + cb > rl - po) return BSO_EFORMAT;
+    uint64_t code_bytes = code_block_bytes(K), counts_bytes = S > 1 ? round_up(4ull * S, 16) : 0;
+    if (po % 16 || po > rl || code_bytes + counts_bytes > rl - po) return BSO_EFORMAT;
+    uint64_t esum = 0;
+    for (uint32_t l = 0; l < K; l++) esum += (b[po + l / 2] >> (4 * (l % 2))) & 15u;
+    uint64_t mant_bytes = mant_block_bytes(K, esum);
+    if (mant_bytes > rl - po - code_bytes - counts_bytes) return BSO_EFORMAT;
     uint32_t P = K / S;
     uint32_t* st = (uint32_t*)malloc(sizeof(uint32_t) * K);
     if (!st) return BSO_ENOMEM;
-    for (uint32_t l = 0; l < K; l++) st[l] = get32(b + po + 4ull * l);
-    uint64_t at = po + sb + cb, total = 0;
+    const uint8_t* mant = b + po + code_bytes + counts_bytes;
+    uint64_t moff = 0;
+    for (uint32_t l = 0; l < K; l++) {
+        uint32_t el = (b[po + l / 2] >> (4 * (l % 2))) & 15u;
+        st[l] = (1u << (16 + el)) | get_bits(mant, moff, 16 + el);
+        moff += 16 + el;
+    }
+    uint64_t at = po + code_bytes + counts_bytes + mant_bytes, total = 0;
     int rc = BSO_OK;
     for (uint32_t s = 0; s < S && !rc; s++) {
-        uint64_t nws = S > 1 ? get32(b + po + sb + 4ull * s) : nw;
+        uint64_t nws = S > 1 ? get32(b + po + code_bytes + 4ull * s) : nw;
         total += nws;
         if (2 * nws > rl - at) { rc = BSO_EFORMAT; break; }
         uint16_t* words = (uint16_t*)malloc(sizeof(uint16_t) * (nws ? nws : 1));

@@ -33,11 +33,16 @@ def _hand_container():
     body += bytes([0])                                                 # route
     body += bytes(32 - len(body))                                      # pad to 32 (index offset)
     body += struct.pack("<QII", 48, 3, 0)                              # chunk index
-    body += struct.pack("<I", g["final_state"]) + bytes(12)            # state + pad
+    x = g["final_state"]
+    e = x.bit_length() - 17                                            # length code: 2^(16+e) <= x < 2^(17+e)
+    assert e == 1
+    body += bytes([e]) + bytes(15)                                     # length codes + pad
+    mant = x - (1 << (16 + e))                                         # 16 + e bits below the leading one
+    body += mant.to_bytes(3, "little") + bytes(13)                     # mantissa bits + pad
     body += struct.pack("<HHH", 0, 0, 0) + bytes(10)                   # words + pad
-    assert len(body) == 80
-    hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 240, 16, 0) + bytes(20)
-    d = struct.pack("<IIQQQQ", 1, 0, 8, 0, 160, 80) + hashlib.sha256(data).digest() + bytes(24)
+    assert len(body) == 96
+    hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 256, 16, 0) + bytes(20)
+    d = struct.pack("<IIQQQQ", 1, 0, 8, 0, 160, 96) + hashlib.sha256(data).digest() + bytes(24)
     c = hdr + d
     assert len(c) == 160
     return words, g["params"], c + bytes(body)
@@ -88,7 +93,7 @@ def test_every_bf16_bit_pattern_roundtrips():
     assert int.from_bytes(c[64:68], "little") == O.KIND_BF16
 
 
-@pytest.mark.parametrize("K", [1, 2, 3, 8, 32, 64, 128, 256, 512])
+@pytest.mark.parametrize("K", [1, 2, 3, 8, 32, 64, 128, 256, 512, 1024])
 def test_edge_sizes_roundtrip(K):
     if K == 3:
         with pytest.raises(O.OracleError):
@@ -99,7 +104,7 @@ def test_edge_sizes_roundtrip(K):
     for n in sorted({0, 1, 7, 8, 9, 8 * K - 1, 8 * K, 8 * K + 1, W - 1, W, W + 1, 3 * W + 5}):
         x = (rng.standard_normal(n) * 0.05).astype(np.float32)
         w = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
-        _rt([O.bf16(w)], W=W, K=K)
+        _rt([O.bf16(w)], W=W, K=K, P=min(K, 512))
 
 
 def test_raw_and_mixed_records():

@@ -30,6 +30,11 @@ MUTANTS = {
     "words_not_reversed": ("put16(b + at + 2 * i, wls[st].w[wls[st].n - 1 - i]);",
                            "put16(b + at + 2 * i, wls[st].w[i]);"),
     "streams_swapped": ("states, &wls[st]);", "states, &wls[S - 1 - st]);"),
+    "state_code_off_by_one": ("while (e < 15 && (x >> (17 + e)) != 0) e++;", "while (e < 15 && (x >> (16 + e)) != 0) e++;"),
+    "state_nibbles_swapped": ("b[start + l / 2] |= (uint8_t)(e << (4 * (l % 2)));",
+                              "b[start + l / 2] |= (uint8_t)(e << (4 * (1 - l % 2)));"),
+    "state_bits_msb_first": ("if ((v >> i) & 1u) b[bit / 8] |= (uint8_t)(1u << (bit % 8));",
+                             "if ((v >> i) & 1u) b[bit / 8] |= (uint8_t)(0x80u >> (bit % 8));"),
     "last_weight_not_in_state": ("states[l] = BSO_L + (last >= 0 ? w[last] : 0u);", "states[l] = BSO_L;"),
     "last_weight_read_off_by_one": ("else out[last] = (uint16_t)(x[l] - BSO_L);",
                                     "else out[last] = (uint16_t)(x[l] - BSO_L + 1);"),

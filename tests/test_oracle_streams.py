@@ -35,13 +35,18 @@ def _hand_two_streams():
     body += bytes([0])                                                # route
     body += bytes(32 - len(body))                                     # pad to 32 (index offset)
     body += struct.pack("<QII", 48, 6, 0)                             # chunk index: payload at 48, 6 words
-    body += struct.pack("<II", g["final_state"], g["final_state"]) + bytes(8)   # two states + pad
+    x = g["final_state"]
+    e = x.bit_length() - 17                                           # length code of both lanes
+    body += bytes([e | e << 4]) + bytes(15)                           # two length codes + pad
     body += struct.pack("<II", 3, 3) + bytes(8)                       # stream word counts + pad
+    mant = x - (1 << (16 + e))
+    bits = mant | mant << (16 + e)                                    # lane 0's bits, then lane 1's
+    body += bits.to_bytes(5, "little") + bytes(11)                    # mantissas + pad
     body += bytes(6) + bytes(10)                                      # stream 0: three zero words + pad
     body += bytes(6) + bytes(10)                                      # stream 1
-    assert len(body) == 112
-    hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 272, 32, 0) + bytes(20)
-    d = struct.pack("<IIQQQQ", 1, 0, 16, 0, 160, 112) + hashlib.sha256(words.tobytes()).digest() + bytes(24)
+    assert len(body) == 128
+    hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 288, 32, 0) + bytes(20)
+    d = struct.pack("<IIQQQQ", 1, 0, 16, 0, 160, 128) + hashlib.sha256(words.tobytes()).digest() + bytes(24)
     return words, g["params"], hdr + d + bytes(body)
 
 
@@ -135,10 +140,8 @@ def test_stream_payload_equals_schedule_coder(n, W, K, P):
     for ch in range(m["nch"]):
         n_c = min(m["W"], n - ch * m["W"])
         po, nw = _u(b, m["index"] + 16 * ch, "Q"), _u(b, m["index"] + 16 * ch + 8, "I")
-        states = np.frombuffer(b[po: po + 4 * K], np.uint32)
-        sb = (4 * K + 15) // 16 * 16
-        cb = (4 * S + 15) // 16 * 16 if S > 1 else 0
-        at = po + sb + cb
+        states, sb, cb, mb = _packed_states(b, po, K, S)
+        at = po + sb + cb + mb
         total = 0
         for s in range(S):
             nws = _u(b, po + sb + 4 * s, "I") if S > 1 else nw
@@ -154,6 +157,23 @@ def test_stream_payload_equals_schedule_coder(n, W, K, P):
         assert total == nw
 
 
+def _packed_states(b, po, K, S):
+    """The chunk's K final states from their length codes (a nibble per lane)
+    and mantissa bits (16 + e bits per lane, least significant first), and the
+    byte sizes of the code, count and mantissa blocks."""
+    codes = [(b[po + l // 2] >> (4 * (l % 2))) & 15 for l in range(K)]
+    cb_codes = ((K + 1) // 2 + 15) // 16 * 16
+    cb_counts = (4 * S + 15) // 16 * 16 if S > 1 else 0
+    mbits = 16 * K + sum(codes)
+    mb = ((mbits + 7) // 8 + 15) // 16 * 16
+    stream = int.from_bytes(b[po + cb_codes + cb_counts: po + cb_codes + cb_counts + mb], "little")
+    states, off = [], 0
+    for e in codes:
+        states.append((1 << (16 + e)) | ((stream >> off) & ((1 << (16 + e)) - 1)))
+        off += 16 + e
+    return np.array(states, np.uint32), cb_codes, cb_counts, mb
+
+
 def syms_prev(syms):
     """For every fraction cell, the (sign, exponent) symbol one sub-step
     earlier in the same lane (the symbol that routes it); other cells -1."""
@@ -162,9 +182,9 @@ def syms_prev(syms):
     return prev
 
 
-@pytest.mark.parametrize("P", [1, 2, 8, 64, 128])
+@pytest.mark.parametrize("P", [1, 2, 8, 64, 128, 512])
 def test_stream_roundtrip_ragged(P):
-    K = 128 if P <= 128 else P
+    K = 128 if P <= 128 else 2 * P
     W = 8 * K * 4
     rng = np.random.default_rng(P)
     for n in sorted({0, 1, 9, 8 * K - 1, 8 * K + 3, W - 1, W, W + 5, 3 * W + 11}):
@@ -177,7 +197,7 @@ def test_stream_roundtrip_ragged(P):
 
 def test_bad_stream_widths_rejected():
     w = _words(100, 0.02, 0)
-    for K, P in [(8, 3), (8, 16), (8, 0)]:
+    for K, P in [(8, 3), (8, 16), (8, 0), (1024, 1024), (2048, 64)]:
         with pytest.raises(O.OracleError):
             O.encode([O.bf16(w)], W=64 * 8, K=K, P=P)
 
@@ -188,7 +208,7 @@ def test_stream_word_count_corruption_detected():
     m = _record_model(bytes(c), 0)
     ro = _u(c, 64 + 24, "Q")
     po = _u(m["b"], m["index"], "Q")
-    cnt_off = ro + po + (4 * 8 + 15) // 16 * 16
+    cnt_off = ro + po + ((8 + 1) // 2 + 15) // 16 * 16     # after the 8 lanes' length codes
     a, b2 = _u(c, cnt_off, "I"), _u(c, cnt_off + 4, "I")
     # move one word from stream 0 to stream 1: totals agree, streams do not
     struct.pack_into("<II", c, cnt_off, a - 1, b2 + 1)
