@@ -80,7 +80,8 @@ def model_build_rate(job):
     if ri is None or ri.kind != 1 or ri.n == 0:
         return None
     words = job.ref[ri.out_offset: ri.out_offset + 2 * ri.n].view(torch.int16)
-    p = codec.params(chunk_weights=job.chunk_weights, lanes=job.lanes, m_s=job.m_s, m_f=job.m_f)
+    p = codec.params(chunk_weights=job.chunk_weights, lanes=job.lanes, m_s=job.m_s, m_f=job.m_f,
+                     stream_lanes=job.stream_lanes)
     codec.build_tables(words, p)          # warm-up
     best = float("inf")
     for _ in range(3):

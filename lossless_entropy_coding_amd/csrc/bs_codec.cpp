@@ -136,9 +136,22 @@ struct ChunkOut {
     }
 };
 
-// chunk payload bytes: states, stream word counts (S > 1), streams
+// A final state x in [2^16, 2^32) is stored as its length code
+// e = floor(log2 x) - 16 (a nibble per lane) and its 16 + e bits below the
+// leading one (concatenated in lane order, least significant bit first).
+inline uint32_t state_code(uint32_t x) { return 31u - (uint32_t)__builtin_clz(x) - 16u; }
+inline uint64_t code_bytes(uint32_t K) { return align_up((K + 1ull) / 2, 16); }
+inline uint64_t mant_bytes(uint32_t K, uint64_t esum) { return align_up((16ull * K + esum + 7) / 8, 16); }
+
+uint64_t state_code_sum(const ChunkOut& co) {
+    uint64_t t = 0;
+    for (uint32_t x : co.states) t += state_code(x);
+    return t;
+}
+
+// chunk payload bytes: length codes, stream word counts (S > 1), state bits, streams
 uint64_t payload_bytes(const ChunkOut& co, uint32_t K, uint32_t S) {
-    uint64_t b = align_up(4ull * K, 16) + (S > 1 ? align_up(4ull * S, 16) : 0);
+    uint64_t b = code_bytes(K) + (S > 1 ? align_up(4ull * S, 16) : 0) + mant_bytes(K, state_code_sum(co));
     for (const auto& v : co.words) b += align_up(2 * v.size(), 16);
     return b;
 }
@@ -268,7 +281,8 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         const uint32_t K = r.K;
         if (b[15] > 9 || (1u << b[15]) > K) { set_error("record %u: bad stream count", i); return BS_E_FORMAT; }
         r.S = 1u << b[15];
-        if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256 || K == 512) || r.W == 0 || r.W % (8 * K)) {
+        if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256 || K == 512 || K == 1024) || r.W == 0 ||
+            r.W % (8 * K) || K / r.S > 512) {
             set_error("record %u: bad chunk shape W=%u K=%u", i, r.W, K);
             return BS_E_FORMAT;
         }
@@ -300,7 +314,7 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
             for (uint32_t f = 0; f < 128; f++) fs += rd16(b + r.ftab_off + 256 * t + 2 * f);
             if (fs != (1ull << r.m_f)) { set_error("record %u: fraction table %u does not sum to 2^%u", i, t + 1, r.m_f); return BS_E_FORMAT; }
         }
-        const uint64_t states_bytes = align_up(4ull * K, 16);
+        const uint64_t cbytes = code_bytes(K);
         const uint64_t counts_bytes = r.S > 1 ? align_up(4ull * r.S, 16) : 0;
         for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
             const uint8_t* e = b + r.index_off + 16ull * ch;
@@ -308,12 +322,15 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
             const uint64_t nw = rd32(e + 8);
             const uint64_t n_c = std::min<uint64_t>(r.W, r.n - (uint64_t)ch * r.W);
             bool ok = po % 16 == 0 && po <= r.rec_len && nw <= 2 * n_c &&
-                      states_bytes + counts_bytes <= r.rec_len - po;
+                      cbytes + counts_bytes <= r.rec_len - po;
             if (ok) {
-                // every stream's words within the record; the counts add up to the index's
-                uint64_t need = states_bytes + counts_bytes, total = 0;
+                // the state bits and every stream's words within the record;
+                // the counts add up to the index's
+                uint64_t esum = 0;
+                for (uint32_t l = 0; l < K; l++) esum += (b[po + l / 2] >> (4 * (l % 2))) & 15u;
+                uint64_t need = cbytes + counts_bytes + mant_bytes(K, esum), total = 0;
                 for (uint32_t st = 0; st < r.S; st++) {
-                    const uint64_t ns = r.S > 1 ? rd32(b + po + states_bytes + 4ull * st) : nw;
+                    const uint64_t ns = r.S > 1 ? rd32(b + po + cbytes + 4ull * st) : nw;
                     total += ns;
                     need += align_up(2 * ns, 16);
                 }
@@ -468,13 +485,22 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
                 continue;
             }
             memcpy(b, r.head.data(), r.head.size());
-            const uint64_t sb = align_up(4ull * r.K, 16);
+            const uint64_t sb = code_bytes(r.K);
             const uint64_t cb = r.S > 1 ? align_up(4ull * r.S, 16) : 0;
             for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
                 const ChunkOut& co = r.chunks[ch];
                 uint8_t* pp = b + rd64(r.head.data() + r.index_off + 16ull * ch);
-                for (uint32_t l = 0; l < r.K; l++) wr32(pp + 4 * l, co.states[l]);
-                uint8_t* at = pp + sb + cb;
+                // length codes, then the state bits (the buffer is zero-filled)
+                uint8_t* mp = pp + sb + cb;
+                uint64_t moff = 0;
+                for (uint32_t l = 0; l < r.K; l++) {
+                    const uint32_t x = co.states[l], e = state_code(x), len = 16 + e;
+                    pp[l / 2] |= (uint8_t)(e << (4 * (l % 2)));
+                    const uint64_t v = (uint64_t)(x - (1u << len)) << (moff % 8);
+                    for (uint32_t k = 0; k * 8 < (moff % 8) + len; k++) mp[moff / 8 + k] |= (uint8_t)(v >> (8 * k));
+                    moff += len;
+                }
+                uint8_t* at = mp + mant_bytes(r.K, state_code_sum(co));
                 for (uint32_t st = 0; st < r.S; st++) {
                     if (r.S > 1) wr32(pp + sb + 4 * st, (uint32_t)co.words[st].size());
                     for (uint64_t k = 0; k < co.words[st].size(); k++) wr16(at + 2 * k, co.words[st][k]);

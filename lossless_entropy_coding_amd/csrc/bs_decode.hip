@@ -137,6 +137,30 @@ __device__ __forceinline__ uint32_t step_f(uint32_t& x, const uint2 se, const Mo
     return __builtin_amdgcn_alignbit(se.y, e.x, 25);
 }
 
+// sum of the eight 4-bit fields of v
+__device__ __forceinline__ uint32_t nibble_sum(uint32_t v) {
+    const uint32_t t = (v & 0x0F0F0F0Fu) + ((v >> 4) & 0x0F0F0F0Fu);
+    return (t * 0x01010101u) >> 24;
+}
+
+// sum of v over the wave
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
+
+// inclusive prefix sum of v over the wave's lanes
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
+    const uint32_t lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t u = __shfl_up(v, d, 64);
+        if (lane >= (uint32_t)d) v += u;
+    }
+    return v;
+}
+
 // Decode unit u of a record: word stream st = u mod S of chunk ch = u / S,
 // whose P lanes are lanes [st * P, st * P + P) of the chunk.
 template <int R, bool C>
@@ -152,25 +176,56 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
     const uint64_t n_left = r.n - (uint64_t)ch * r.W;
     const uint32_t n_c = (uint32_t)(n_left < r.W ? n_left : r.W);
     // this stream's word count and the start of its words
-    const uint8_t* words = payload + ((4 * K + 15) & ~15u);
+    // payload: the K lanes' length codes (a nibble each), the streams' word
+    // counts (several streams), the states' bits, then each stream's words
+    const uint32_t code_bytes = ((K + 1) / 2 + 15) & ~15u;
+    const uint32_t count_bytes = r.streams_log2 ? ((4u << r.streams_log2) + 15) & ~15u : 0u;
+    const uint32_t* codes32 = (const uint32_t*)payload;
+    // sum of all the codes and of those of the lanes below this stream
+    uint32_t esum_all = 0, esum_below = 0;
+    for (uint32_t d = lane; d < (K + 7) / 8; d += 64) {
+        const uint32_t v = codes32[d];
+        const int32_t below = (int32_t)LB - (int32_t)(8 * d);   // lanes of this dword that are below LB
+        const uint32_t vb = below >= 8 ? v : below <= 0 ? 0u : v & ((1u << (4 * below)) - 1u);
+        esum_all += nibble_sum(v);
+        esum_below += nibble_sum(vb);
+    }
+    esum_all = wave_sum(esum_all);
+    esum_below = wave_sum(esum_below);
+    const uint32_t* mant32 = (const uint32_t*)(payload + code_bytes + count_bytes);
+    const uint8_t* words = payload + code_bytes + count_bytes + (((16 * K + esum_all + 7) / 8 + 15) & ~15u);
     uint32_t nw;
     if (r.streams_log2 == 0) {
         nw = *(const uint32_t*)(ent + 8);
     } else {
-        const uint32_t* counts = (const uint32_t*)words;
-        words += ((4u << r.streams_log2) + 15) & ~15u;
+        const uint32_t* counts = (const uint32_t*)(payload + code_bytes);
         for (uint32_t k = 0; k < st; k++) words += (2 * counts[k] + 15) & ~15u;
         nw = counts[st];
     }
 
     // lane states first, then the ring: both are complete before the loop so
-    // that no load issued here is still pending when the loop first runs
+    // that no load issued here is still pending when the loop first runs.
+    // Lane LB + l's bits start at 16 (LB + l) plus the codes of the lanes
+    // before it; a state is 1 << (16 + e) plus its 16 + e low bits.
     uint32_t x[R];
-    const uint32_t* sp = (const uint32_t*)payload + LB;
+    uint32_t before = esum_below;
 #pragma unroll
     for (int q = 0; q < R; q++) {
         const uint32_t l = 64 * q + lane;
-        x[q] = l < P ? sp[l] : kStateLow;
+        const uint32_t gl = LB + l;
+        const uint32_t e = l < P ? (payload[gl >> 1] >> (4 * (gl & 1))) & 15u : 0u;
+        const uint32_t incl = wave_scan(e);
+        const uint32_t off = 16 * gl + before + (incl - e);   // < 16 K + 15 K bits
+        const uint32_t len = 16 + e;
+        const uint32_t d0 = off >> 5, sh = off & 31;
+        uint32_t lo = 0, hi = 0;
+        if (l < P) {
+            lo = mant32[d0];
+            if (sh + len > 32) hi = mant32[d0 + 1];
+        }
+        const uint32_t bits = __builtin_amdgcn_alignbit(hi, lo, sh) & ((1u << len) - 1u);
+        x[q] = l < P ? (1u << len) | bits : kStateLow;
+        before += __builtin_amdgcn_readlane(incl, 63);
     }
     constexpr uint32_t RW = ring_words(R, C);
     Ring<RW> g;

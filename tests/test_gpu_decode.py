@@ -68,6 +68,9 @@ CASES = [
     ("k128_p32", 3 * 65536 + 5, 0.02, 65536, 128, 32),
     ("k64_p8_small", 20000 + 3, 0.02, 8192, 64, 8),
     ("k8_p1", 4096 + 9, 0.02, 4096, 8, 1),
+    ("k1024_p64", 2 * 131072 + 8 * 1000 + 5, 0.02, 131072, 1024, 64),
+    ("k1024_p512", 262144 + 3, 0.03, 262144, 1024, 512),
+    ("k1024_p128_short", 9000, 0.02, 131072, 1024, 128),
 ]
 
 
