@@ -391,19 +391,39 @@ int bso_sched_decode(uint32_t K, uint32_t nsteps, const int32_t* active, const u
 /* stream has its own word sequence, in which a sub-step's refills come in   */
 /* ascending lane order.  The coder below handles the lanes [l0, l1) of one  */
 /* stream.                                                                   */
-/* The last weight of every lane (in decode order) is not coded: the lane's  */
-/* encoder starts from x = L + that weight's 16-bit word instead of L, so    */
-/* the decoder finds the word in its final state.  A lane without weights    */
-/* starts, and must end, at L.                                               */
+/* Start states.  A lane's last group holds c = min(8, weights left) weights */
+/* and its last m = min(4, c) weights carry only their s symbol in the      */
+/* stream: their 7-bit fractions are the low 7m bits of the lane's start    */
+/* state, the first of them (in decode order) lowest, under a leading one   */
+/* at bit max(16, 7m).  The fractions are close to uniform, so holding them */
+/* raw costs about what coding them would, while the state itself carries   */
+/* some 7m bits that would otherwise cost stream words.  The decoder finds  */
+/* them in its final state.  A lane without weights starts, and must end,   */
+/* at L.                                                                     */
 /* ------------------------------------------------------------------------ */
 
-/* Chunk index of the last weight of lane l, or -1 when the lane is empty.   */
-static int64_t lane_last_weight(uint32_t n_c, uint32_t K, uint32_t l) {
+/* m for lane l, and through j0 the chunk index of the first of its m        */
+/* weights (they are j0 .. j0 + m - 1); 0 for an empty lane.                 */
+static uint32_t lane_raw_fractions(uint32_t n_c, uint32_t K, uint32_t l, uint64_t* j0) {
     uint64_t groups = ((uint64_t)n_c + 7) / 8;
-    if (l >= groups) return -1;
-    uint64_t g = l + (uint64_t)K * ((groups - 1 - l) / K);
-    uint64_t j = 8 * g + 7;
-    return (int64_t)(j < n_c ? j : (uint64_t)n_c - 1);
+    *j0 = 0;
+    if (l >= groups) return 0;
+    uint64_t g = l + (uint64_t)K * ((groups - 1 - l) / K);   /* the lane's last group */
+    uint64_t end = 8 * g + 8 < n_c ? 8 * g + 8 : (uint64_t)n_c;
+    uint64_t c = end - 8 * g;
+    uint32_t m = c < 4 ? (uint32_t)c : 4u;
+    *j0 = end - m;
+    return m;
+}
+
+/* bit of the leading one of a start state that holds m fractions */
+static uint32_t start_lead(uint32_t m) { return 7 * m > 16 ? 7 * m : 16; }
+
+/* is chunk weight j of lane l one whose fraction is in the start state? */
+static int raw_fraction(uint32_t n_c, uint32_t K, uint32_t l, uint64_t j) {
+    uint64_t j0;
+    uint32_t m = lane_raw_fractions(n_c, K, l, &j0);
+    return m > 0 && j >= j0 && j < j0 + m;
 }
 typedef struct {
     uint32_t M_s, M_f;
@@ -419,15 +439,18 @@ static int chunk_encode(const bso_model* md, const uint16_t* w, uint32_t n_c, ui
     uint32_t groups = (n_c + 7) / 8;
     uint32_t T = (groups + K - 1) / K;
     for (uint32_t l = l0; l < l1; l++) {
-        int64_t last = lane_last_weight(n_c, K, l);
-        states[l] = BSO_L + (last >= 0 ? w[last] : 0u);
+        uint64_t j0;
+        uint32_t m = lane_raw_fractions(n_c, K, l, &j0);
+        uint32_t x = m ? 1u << start_lead(m) : BSO_L;
+        for (uint32_t i = 0; i < m; i++) x |= bso_symbol_f(w[j0 + i]) << (7 * i);
+        states[l] = x;
     }
     for (int64_t t = (int64_t)T - 1; t >= 0; t--) {
         for (int p = 7; p >= 0; p--) {
             for (int phase = 1; phase >= 0; phase--) {
                 for (int64_t l = (int64_t)l1 - 1; l >= (int64_t)l0; l--) {
                     uint64_t j = 8 * ((uint64_t)t * K + (uint64_t)l) + (uint64_t)p;
-                    if (j >= n_c || (int64_t)j == lane_last_weight(n_c, K, (uint32_t)l)) continue;
+                    if (j >= n_c || (phase == 1 && raw_fraction(n_c, K, (uint32_t)l, j))) continue;
                     uint32_t s = bso_symbol_s(w[j]);
                     int rc;
                     if (phase == 0) {
@@ -460,11 +483,14 @@ static int chunk_decode(const bso_model* md, const uint32_t* states_in, const ui
             for (int phase = 0; phase < 2 && !rc; phase++) {
                 for (uint32_t l = l0; l < l1 && !rc; l++) {
                     uint64_t j = 8 * ((uint64_t)t * K + l) + p;
-                    if (j >= n_c || (int64_t)j == lane_last_weight(n_c, K, l)) continue;
+                    if (j >= n_c) continue;
+                    int raw = raw_fraction(n_c, K, l, j);
+                    if (phase == 1 && raw) continue;
                     uint32_t sym;
                     if (phase == 0) {
                         rc = dec_symbol(&x[l], &ts, words, nw, &pos, &sym);
                         s_now[l] = sym;
+                        if (!rc && raw) out[j] = bso_combine(sym, 0);   /* fraction added at the end */
                     } else {
                         bso_table tf = { md->M_f, 128, md->qf[md->route[s_now[l]]] };
                         rc = dec_symbol(&x[l], &tf, words, nw, &pos, &sym);
@@ -474,13 +500,15 @@ static int chunk_decode(const bso_model* md, const uint32_t* states_in, const ui
             }
         }
     }
-    /* every lane ends at the state its encoder started from: L plus its last
-       weight, or L for an empty lane */
+    /* every lane ends at the state its encoder started from: the leading one
+       over its m fractions (nothing else set), or L for an empty lane */
     for (uint32_t l = l0; l < l1 && !rc; l++) {
-        int64_t last = lane_last_weight(n_c, K, l);
-        if (last < 0) { if (x[l] != BSO_L) rc = BSO_ECORRUPT; }
-        else if (x[l] < BSO_L || x[l] - BSO_L > 0xFFFFu) rc = BSO_ECORRUPT;
-        else out[last] = (uint16_t)(x[l] - BSO_L);
+        uint64_t j0;
+        uint32_t m = lane_raw_fractions(n_c, K, l, &j0);
+        if (m == 0) { if (x[l] != BSO_L) rc = BSO_ECORRUPT; continue; }
+        uint32_t lead = start_lead(m);
+        if ((x[l] >> lead) != 1u || (x[l] - (1u << lead)) >= (1u << (7 * m))) { rc = BSO_ECORRUPT; continue; }
+        for (uint32_t i = 0; i < m; i++) out[j0 + i] = (uint16_t)(out[j0 + i] | ((x[l] >> (7 * i)) & 0x7Fu));
     }
     if (!rc && pos != nw) rc = BSO_ECORRUPT;
     free(x); free(s_now);
@@ -591,8 +619,9 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
         for (uint32_t f = 0; f < 128; f++) put16(b + ft + 256ull * (t - 1) + 2 * f, md->qf[t][f]);
 
     /* chunks: the K lanes' length codes, then (S > 1) the S stream word
-       counts, then the states' mantissa bits, then each stream's words;
-       every part padded to 16 bytes */
+       counts, then the states' mantissa bits, each padded to 16 bytes, then
+       each stream's words padded to 4 bytes; the chunk's payload as a whole
+       is padded to 16 bytes */
     uint32_t* states = (uint32_t*)malloc(sizeof(uint32_t) * K);
     wordlist* wls = (wordlist*)calloc(S, sizeof(wordlist));
     if (!states || !wls) { free(states); free(wls); rc = BSO_ENOMEM; goto done; }
@@ -609,7 +638,8 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
         uint64_t counts_bytes = S > 1 ? round_up(4ull * S, 16) : 0;
         uint64_t mant_bytes = mant_block_bytes(K, esum);
         uint64_t end = start + code_bytes + counts_bytes + mant_bytes, total_words = 0;
-        for (uint32_t st = 0; st < S; st++) { end += round_up(2 * wls[st].n, 16); total_words += wls[st].n; }
+        for (uint32_t st = 0; st < S; st++) { end += round_up(2 * wls[st].n, 4); total_words += wls[st].n; }
+        end = start + round_up(end - start, 16);
         rc = bb_reserve(body, end);
         if (rc) break;
         b = body->p;
@@ -631,7 +661,7 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
         for (uint32_t st = 0; st < S; st++) {
             /* the encoder pushes words in reverse order of their use */
             for (uint64_t i = 0; i < wls[st].n; i++) put16(b + at + 2 * i, wls[st].w[wls[st].n - 1 - i]);
-            at += round_up(2 * wls[st].n, 16);
+            at += round_up(2 * wls[st].n, 4);
         }
         body->n = end;
     }
@@ -656,7 +686,7 @@ int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* 
                          uint32_t Wmax, uint32_t Kmax, uint32_t Pmax, uint32_t M_s, uint32_t M_f, uint32_t cmax,
                          uint8_t** out, uint64_t* out_len) {
     if (M_s < 9 || M_s > 12 || M_f < 8 || M_f > 10 || cmax > BSO_MAX_TABLES) return BSO_EINVAL;
-    if (!(Kmax <= 64 || Kmax == 128 || Kmax == 256 || Kmax == 512 || Kmax == 1024) || Kmax == 0) return BSO_EINVAL;
+    if (!(Kmax <= 64 || Kmax == 128 || Kmax == 256 || Kmax == 512 || Kmax == 1024 || Kmax == 2048) || Kmax == 0) return BSO_EINVAL;
     if ((Kmax & (Kmax - 1)) != 0) return BSO_EINVAL;
     if (Pmax == 0 || (Pmax & (Pmax - 1)) != 0 || Pmax > Kmax || Pmax > 512) return BSO_EINVAL;
     bytebuf c = {0, 0, 0};
@@ -750,7 +780,7 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md
     if (md->M_s < 9 || md->M_s > 12 || md->M_f < 8 || md->M_f > 10 || md->n_tables > BSO_MAX_TABLES)
         return BSO_EFORMAT;
     if (*K == 0 || *W == 0 || *W % (8 * *K)) return BSO_EFORMAT;
-    if (!(*K <= 64 || *K == 128 || *K == 256 || *K == 512 || *K == 1024)) return BSO_EFORMAT;
+    if (!(*K <= 64 || *K == 128 || *K == 256 || *K == 512 || *K == 1024 || *K == 2048)) return BSO_EFORMAT;
     if (*K % *S || *K / *S > 512) return BSO_EFORMAT;
     if (*n_chunks != (n + *W - 1) / *W) return BSO_EFORMAT;
     if (n_sym > BSO_MAX_SYMS || (n_sym == 0) != (n == 0)) return BSO_EFORMAT;
@@ -814,7 +844,7 @@ static int decode_one_chunk(const bso_model* md, const uint8_t* b, uint64_t rl, 
         for (uint64_t j = 0; j < nws; j++) words[j] = (uint16_t)get16(b + at + 2 * j);
         rc = chunk_decode(md, st, words, nws, n_c, K, s * P, (s + 1) * P, out);
         free(words);
-        at += round_up(2 * nws, 16);
+        at += round_up(2 * nws, 4);
     }
     if (!rc && total != nw) rc = BSO_EFORMAT;
     free(st);

@@ -32,14 +32,15 @@ def _hand_container():
     body += struct.pack("<HH", 127, 4096)                              # s-table
     body += bytes([0])                                                 # route
     body += bytes(32 - len(body))                                      # pad to 32 (index offset)
-    body += struct.pack("<QII", 48, 3, 0)                              # chunk index
+    nw = g["n_words"]
+    body += struct.pack("<QII", 48, nw, 0)                             # chunk index
     x = g["final_state"]
     e = x.bit_length() - 17                                            # length code: 2^(16+e) <= x < 2^(17+e)
-    assert e == 1
+    assert e == 8
     body += bytes([e]) + bytes(15)                                     # length codes + pad
     mant = x - (1 << (16 + e))                                         # 16 + e bits below the leading one
     body += mant.to_bytes(3, "little") + bytes(13)                     # mantissa bits + pad
-    body += struct.pack("<HHH", 0, 0, 0) + bytes(10)                   # words + pad
+    body += bytes(2 * nw) + bytes(16 - 2 * nw)                         # words (all zero) + pad
     assert len(body) == 96
     hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 256, 16, 0) + bytes(20)
     d = struct.pack("<IIQQQQ", 1, 0, 8, 0, 160, 96) + hashlib.sha256(data).digest() + bytes(24)
@@ -93,7 +94,7 @@ def test_every_bf16_bit_pattern_roundtrips():
     assert int.from_bytes(c[64:68], "little") == O.KIND_BF16
 
 
-@pytest.mark.parametrize("K", [1, 2, 3, 8, 32, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("K", [1, 2, 3, 8, 32, 64, 128, 256, 512, 1024, 2048])
 def test_edge_sizes_roundtrip(K):
     if K == 3:
         with pytest.raises(O.OracleError):

@@ -35,10 +35,14 @@ MUTANTS = {
                               "b[start + l / 2] |= (uint8_t)(e << (4 * (1 - l % 2)));"),
     "state_bits_msb_first": ("if ((v >> i) & 1u) b[bit / 8] |= (uint8_t)(1u << (bit % 8));",
                              "if ((v >> i) & 1u) b[bit / 8] |= (uint8_t)(0x80u >> (bit % 8));"),
-    "last_weight_not_in_state": ("states[l] = BSO_L + (last >= 0 ? w[last] : 0u);", "states[l] = BSO_L;"),
-    "last_weight_read_off_by_one": ("else out[last] = (uint16_t)(x[l] - BSO_L);",
-                                    "else out[last] = (uint16_t)(x[l] - BSO_L + 1);"),
-    "last_weight_wrong_position": ("uint64_t j = 8 * g + 7;\n    return", "uint64_t j = 8 * g + 6;\n    return"),
+    "raw_fractions_not_in_state": ("for (uint32_t i = 0; i < m; i++) x |= bso_symbol_f(w[j0 + i]) << (7 * i);",
+                                   "for (uint32_t i = 0; i < m; i++) x |= 0u;"),
+    "raw_fractions_reversed": ("x |= bso_symbol_f(w[j0 + i]) << (7 * i);", "x |= bso_symbol_f(w[j0 + i]) << (7 * (m - 1 - i));"),
+    "raw_fraction_read_shifted": ("((x[l] >> (7 * i)) & 0x7Fu)", "((x[l] >> (7 * i + 1)) & 0x7Fu)"),
+    "raw_count_three": ("uint32_t m = c < 4 ? (uint32_t)c : 4u;", "uint32_t m = c < 3 ? (uint32_t)c : 3u;"),
+    "raw_lead_always_16": ("return 7 * m > 16 ? 7 * m : 16;", "return 16;"),
+    "raw_in_first_group": ("uint64_t g = l + (uint64_t)K * ((groups - 1 - l) / K);   /* the lane's last group */",
+                           "uint64_t g = l;"),
     "stream_lanes_overlap": ("rc = chunk_decode(md, st, words, nws, n_c, K, s * P, (s + 1) * P, out);",
                              "rc = chunk_decode(md, st, words, nws, n_c, K, s * P, (s + 1) * P + (s + 1 < S), out);"),
     "phase_order_swapped": ("for (int phase = 1; phase >= 0; phase--) {", "for (int phase = 0; phase <= 1; phase++) {"),

@@ -9,7 +9,7 @@ pages give no chunk layout).  The pins:
   - every stream's states and words equal the explicit-schedule coder (a
     separate code path pinned by the worked examples) run on the schedule
     that the lane interleave defines, with the tables read from the record
-    and each lane started from 2^16 plus its last weight;
+    and each lane started from a state holding its last fractions;
   - round trips over ragged sizes and stream widths.
 """
 import hashlib
@@ -34,19 +34,23 @@ def _hand_two_streams():
     body += struct.pack("<HH", 127, 4096)                             # s-table
     body += bytes([0])                                                # route
     body += bytes(32 - len(body))                                     # pad to 32 (index offset)
-    body += struct.pack("<QII", 48, 6, 0)                             # chunk index: payload at 48, 6 words
+    nw = g["n_words"]                                                 # per stream
+    body += struct.pack("<QII", 48, 2 * nw, 0)                        # chunk index: payload at 48, all words
     x = g["final_state"]
     e = x.bit_length() - 17                                           # length code of both lanes
+    assert e == 8
     body += bytes([e | e << 4]) + bytes(15)                           # two length codes + pad
-    body += struct.pack("<II", 3, 3) + bytes(8)                       # stream word counts + pad
+    body += struct.pack("<II", nw, nw) + bytes(8)                     # stream word counts + pad
     mant = x - (1 << (16 + e))
     bits = mant | mant << (16 + e)                                    # lane 0's bits, then lane 1's
-    body += bits.to_bytes(5, "little") + bytes(11)                    # mantissas + pad
-    body += bytes(6) + bytes(10)                                      # stream 0: three zero words + pad
-    body += bytes(6) + bytes(10)                                      # stream 1
-    assert len(body) == 128
-    hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 288, 32, 0) + bytes(20)
-    d = struct.pack("<IIQQQQ", 1, 0, 16, 0, 160, 128) + hashlib.sha256(words.tobytes()).digest() + bytes(24)
+    body += bits.to_bytes(6, "little") + bytes(10)                    # mantissas + pad
+    assert 2 * nw == 4
+    body += bytes(2 * nw)                                             # stream 0: zero words (4 B)
+    body += bytes(2 * nw)                                             # stream 1
+    body += bytes(8)                                                  # the payload padded to 16 B
+    assert len(body) == 112
+    hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 272, 32, 0) + bytes(20)
+    d = struct.pack("<IIQQQQ", 1, 0, 16, 0, 160, 112) + hashlib.sha256(words.tobytes()).digest() + bytes(24)
     return words, g["params"], hdr + d + bytes(body)
 
 
@@ -100,29 +104,38 @@ def _record_model(c, i):
 
 def _stream_schedule(w, n_c, K, lanes):
     """Symbols and table kinds of one stream, by sub-step: (t, p, phase) with
-    phase 0 the (sign, exponent) symbol and 1 the fraction; idle = -1.  Each
-    lane's last weight is left out of the schedule: it is the lane's start
-    state, 2^16 + its word (an empty lane starts at 2^16)."""
+    phase 0 the (sign, exponent) symbol and 1 the fraction; idle = -1.  The
+    lane's last group of c weights (its last macro-step) hands the fractions
+    of its last min(4, c) weights to the start state: they are left out of
+    the schedule and packed 7 bits each, first one lowest, under a leading
+    one at bit max(16, 7m) (an empty lane starts at 2^16)."""
     groups = (n_c + 7) // 8
     T = (groups + K - 1) // K
     P = len(lanes)
     syms = np.full((T * 16, P), -1, np.int32)
     kind = np.zeros((T * 16, P), np.int32)     # 0 = s, 1 = f
     init = np.full(P, 1 << 16, np.uint32)
-    last = {}
+    raw = set()
     for i, l in enumerate(lanes):
-        js = [8 * (t * K + l) + p for t in range(T) for p in range(8) if 8 * (t * K + l) + p < n_c]
-        if js:
-            last[i] = max(js)
-            init[i] += int(w[last[i]])
+        tl = [t for t in range(T) if 8 * (t * K + l) < n_c]
+        if not tl:
+            continue
+        js = [8 * (tl[-1] * K + l) + p for p in range(8) if 8 * (tl[-1] * K + l) + p < n_c]
+        mine = js[-min(4, len(js)):]
+        x = 1 << max(16, 7 * len(mine))
+        for k, j in enumerate(mine):
+            x |= (int(w[j]) & 0x7F) << (7 * k)
+            raw.add((i, j))
+        init[i] = x
     for t in range(T):
         for p in range(8):
             for i, l in enumerate(lanes):
                 j = 8 * (t * K + l) + p
-                if j >= n_c or last.get(i) == j:
+                if j >= n_c:
                     continue
                 syms[(t * 8 + p) * 2, i] = int(w[j]) >> 7
-                syms[(t * 8 + p) * 2 + 1, i] = int(w[j]) & 0x7F
+                if (i, j) not in raw:
+                    syms[(t * 8 + p) * 2 + 1, i] = int(w[j]) & 0x7F
                 kind[(t * 8 + p) * 2 + 1, i] = 1
     return syms, kind, init
 
@@ -152,7 +165,7 @@ def test_stream_payload_equals_schedule_coder(n, W, K, P):
             st_ref, w_ref = O.sched_encode(Ps, syms, tab_of.astype(np.uint32), tables, init=init)
             assert np.array_equal(states[s * Ps: (s + 1) * Ps], st_ref), (ch, s)
             assert np.array_equal(stream, w_ref), (ch, s)
-            at += (2 * nws + 15) // 16 * 16
+            at += (2 * nws + 3) // 4 * 4
             total += nws
         assert total == nw
 
@@ -182,9 +195,9 @@ def syms_prev(syms):
     return prev
 
 
-@pytest.mark.parametrize("P", [1, 2, 8, 64, 128, 512])
-def test_stream_roundtrip_ragged(P):
-    K = 128 if P <= 128 else 2 * P
+@pytest.mark.parametrize("P,K", [(1, 128), (2, 128), (8, 128), (64, 128), (128, 128), (512, 1024), (64, 2048),
+                                 (512, 2048)])
+def test_stream_roundtrip_ragged(P, K):
     W = 8 * K * 4
     rng = np.random.default_rng(P)
     for n in sorted({0, 1, 9, 8 * K - 1, 8 * K + 3, W - 1, W, W + 5, 3 * W + 11}):
@@ -197,7 +210,7 @@ def test_stream_roundtrip_ragged(P):
 
 def test_bad_stream_widths_rejected():
     w = _words(100, 0.02, 0)
-    for K, P in [(8, 3), (8, 16), (8, 0), (1024, 1024), (2048, 64)]:
+    for K, P in [(8, 3), (8, 16), (8, 0), (1024, 1024), (4096, 64)]:
         with pytest.raises(O.OracleError):
             O.encode([O.bf16(w)], W=64 * 8, K=K, P=P)
 
