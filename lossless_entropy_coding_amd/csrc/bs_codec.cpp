@@ -72,28 +72,41 @@ inline void put(uint32_t& x, const EncSym& e, uint32_t M, uint16_t*& sink) {
     x = ((x / e.q) << M) + x % e.q + e.cum;
 }
 
-// Chunk index of the last weight of lane l in decode order (its last group,
-// last position), or UINT64_MAX for a lane without weights.
-inline uint64_t lane_last(uint32_t n_c, uint32_t K, uint32_t l) {
+// Start states.  Lane l's last group holds c = min(8, weights left) weights;
+// its last m = min(4, c) weights keep only their s symbol in the stream, and
+// their 7-bit fractions are the low 7m bits of the lane's start state (the
+// first of them lowest) under a leading one at bit max(16, 7m).  The decoder
+// finds them in its final state.  A lane without weights starts at 2^16.
+struct RawTail {
+    uint64_t j0;   // chunk index of the first of the m weights
+    uint32_t m;    // 0 for a lane without weights
+};
+
+inline RawTail raw_tail(uint32_t n_c, uint32_t K, uint32_t l) {
     const uint64_t groups = ((uint64_t)n_c + 7) / 8;
-    if (l >= groups) return UINT64_MAX;
-    const uint64_t g = l + (uint64_t)K * ((groups - 1 - l) / K);
-    return std::min<uint64_t>(8 * g + 7, (uint64_t)n_c - 1);
+    if (l >= groups) return {0, 0};
+    const uint64_t g = l + (uint64_t)K * ((groups - 1 - l) / K);   // the lane's last group
+    const uint64_t end = std::min<uint64_t>(8 * g + 8, n_c);
+    const uint32_t m = (uint32_t)std::min<uint64_t>(end - 8 * g, 4);
+    return {end - m, m};
 }
 
 // Encode the lanes [l0, l1) of one chunk (n_c weights, K lanes): one word
-// stream.  Each lane's last weight is not coded: the lane starts from
-// 2^16 + that word, which the decoder finds in its final state.  Sub-steps
-// run from last to first, lanes from l1-1 down to l0 inside each, so that the
-// decoder reads forwards; the emitted words come out reversed and are turned
-// around by the caller.  `scratch` must hold 2 * n_c words.  Returns the word
-// count.
+// stream.  Sub-steps run from last to first, lanes from l1-1 down to l0
+// inside each, so that the decoder reads forwards; the emitted words come out
+// reversed and are turned around by the caller.  `scratch` must hold 2 * n_c
+// words.  Returns the word count.
 uint64_t encode_stream(const EncModel& em, const uint16_t* w, uint32_t n_c, uint32_t K, uint32_t l0, uint32_t l1,
                        uint32_t* x, uint16_t* scratch) {
-    uint64_t last[512];
+    uint64_t j0[512];
+    uint32_t m[512];
     for (uint32_t l = l0; l < l1; l++) {
-        last[l - l0] = lane_last(n_c, K, l);
-        x[l] = kL + (last[l - l0] != UINT64_MAX ? w[last[l - l0]] : 0u);
+        const RawTail rt = raw_tail(n_c, K, l);
+        j0[l - l0] = rt.j0;
+        m[l - l0] = rt.m;
+        uint32_t v = rt.m ? 1u << std::max(16u, 7 * rt.m) : kL;
+        for (uint32_t i = 0; i < rt.m; i++) v |= (w[rt.j0 + i] & 127u) << (7 * i);
+        x[l] = v;
     }
     uint16_t* sink = scratch;
     const uint32_t groups = (n_c + 7) / 8;
@@ -103,13 +116,13 @@ uint64_t encode_stream(const EncModel& em, const uint16_t* w, uint32_t n_c, uint
             // fraction sub-step, then sign/exponent sub-step (reverse of decode order)
             for (uint32_t l = l1; l-- > l0;) {
                 const uint64_t j = 8ull * ((uint64_t)t * K + l) + (uint64_t)p;
-                if (j >= n_c || j == last[l - l0]) continue;
+                if (j >= n_c || (j >= j0[l - l0] && j < j0[l - l0] + m[l - l0])) continue;
                 const uint32_t v = w[j];
                 put(x[l], em.f[em.route[v >> 7]][v & 127], em.m_f, sink);
             }
             for (uint32_t l = l1; l-- > l0;) {
                 const uint64_t j = 8ull * ((uint64_t)t * K + l) + (uint64_t)p;
-                if (j >= n_c || j == last[l - l0]) continue;
+                if (j >= n_c) continue;
                 put(x[l], em.s[w[j] >> 7], em.m_s, sink);
             }
         }
@@ -149,11 +162,13 @@ uint64_t state_code_sum(const ChunkOut& co) {
     return t;
 }
 
-// chunk payload bytes: length codes, stream word counts (S > 1), state bits, streams
+// chunk payload bytes: length codes, stream word counts (S > 1) and state
+// bits, each padded to 16 bytes, then the streams, each padded to 4 bytes;
+// the whole padded to 16 bytes
 uint64_t payload_bytes(const ChunkOut& co, uint32_t K, uint32_t S) {
     uint64_t b = code_bytes(K) + (S > 1 ? align_up(4ull * S, 16) : 0) + mant_bytes(K, state_code_sum(co));
-    for (const auto& v : co.words) b += align_up(2 * v.size(), 16);
-    return b;
+    for (const auto& v : co.words) b += align_up(2 * v.size(), 4);
+    return align_up(b, 16);
 }
 
 struct EncRecord {
@@ -281,7 +296,7 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         const uint32_t K = r.K;
         if (b[15] > 9 || (1u << b[15]) > K) { set_error("record %u: bad stream count", i); return BS_E_FORMAT; }
         r.S = 1u << b[15];
-        if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256 || K == 512 || K == 1024) || r.W == 0 ||
+        if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256 || K == 512 || K == 1024 || K == 2048) || r.W == 0 ||
             r.W % (8 * K) || K / r.S > 512) {
             set_error("record %u: bad chunk shape W=%u K=%u", i, r.W, K);
             return BS_E_FORMAT;
@@ -332,7 +347,7 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
                 for (uint32_t st = 0; st < r.S; st++) {
                     const uint64_t ns = r.S > 1 ? rd32(b + po + cbytes + 4ull * st) : nw;
                     total += ns;
-                    need += align_up(2 * ns, 16);
+                    need += align_up(2 * ns, 4);
                 }
                 ok = total == nw && need <= r.rec_len - po;
             }
@@ -504,7 +519,7 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
                 for (uint32_t st = 0; st < r.S; st++) {
                     if (r.S > 1) wr32(pp + sb + 4 * st, (uint32_t)co.words[st].size());
                     for (uint64_t k = 0; k < co.words[st].size(); k++) wr16(at + 2 * k, co.words[st][k]);
-                    at += align_up(2 * co.words[st].size(), 16);
+                    at += align_up(2 * co.words[st].size(), 4);
                 }
             }
         }

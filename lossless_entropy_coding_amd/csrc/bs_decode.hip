@@ -193,15 +193,29 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
     esum_all = wave_sum(esum_all);
     esum_below = wave_sum(esum_below);
     const uint32_t* mant32 = (const uint32_t*)(payload + code_bytes + count_bytes);
-    const uint8_t* words = payload + code_bytes + count_bytes + (((16 * K + esum_all + 7) / 8 + 15) & ~15u);
+    // the streams' words follow the state bits, each stream padded to 4 bytes
+    uint32_t woff = code_bytes + count_bytes + (((16 * K + esum_all + 7) / 8 + 15) & ~15u);
     uint32_t nw;
     if (r.streams_log2 == 0) {
         nw = *(const uint32_t*)(ent + 8);
     } else {
         const uint32_t* counts = (const uint32_t*)(payload + code_bytes);
-        for (uint32_t k = 0; k < st; k++) words += (2 * counts[k] + 15) & ~15u;
+        uint32_t below = 0;
+        for (uint32_t k = lane; k < st; k += 64) below += (2 * counts[k] + 3) & ~3u;
+        woff += wave_sum(below);
         nw = counts[st];
     }
+    // Ring loads start at the 16-byte boundary at or below the stream (the
+    // payload starts on one) and may run to the boundary at or above its end,
+    // which the payload's own padding covers; the first `skip` words loaded
+    // belong to the stream before.
+    // (woff and nw are wave-uniform; readfirstlane keeps the stream position
+    // and everything derived from it in scalar registers)
+    woff = __builtin_amdgcn_readfirstlane(woff);
+    nw = __builtin_amdgcn_readfirstlane(nw);
+    const uint32_t w16 = woff & ~15u;
+    const uint32_t skip = (woff - w16) / 2;
+    const uint32_t wend16 = (woff + 2 * nw + 15) & ~15u;
 
     // lane states first, then the ring: both are complete before the loop so
     // that no load issued here is still pending when the loop first runs.
@@ -230,21 +244,21 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
     constexpr uint32_t RW = ring_words(R, C);
     Ring<RW> g;
     g.base = (uint16_t*)(lds + lut_lds(C) + wave * ring_bytes(R, C));
-    g.words = words;
-    g.bytes = (2 * nw + 15) & ~15u;
+    g.words = payload + w16;
+    g.bytes = wend16 - w16;
     ring_init(g, lane);
     __builtin_amdgcn_s_waitcnt(0);
 
     const Model md{lds, r.m_s, r.m_f, ((1u << r.m_s) - 1) << 3, ((1u << r.m_f) - 1) << 3};
 
-    uint32_t pos = 0;
+    uint32_t pos = skip;
     uint8_t* out = a.out + (r.out_off - a.out_base) + 2ull * ch * r.W;
 
     const uint32_t groups = (n_c + 7) / 8;
     const uint32_t T = (groups + K - 1) / K;
-    // macro-steps in which every lane decodes 8 weights, none of them a lane's
-    // last (that one is in the lane's start state, not in the stream): all
-    // full macro-steps but the last
+    // macro-steps in which every lane decodes 8 weights and none of them is in
+    // the lane's last group (whose last weights keep their fractions in the
+    // lane's start state, not in the stream): all full macro-steps but the last
     const uint32_t T_full = (P % 64 == 0) ? n_c / (8 * K) : 0;
     const uint32_t T_main = T_full ? T_full - 1 : 0;
 
@@ -283,56 +297,76 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
         }
     }
 
-    // remaining macro-steps (a lane's last weights, partial groups, or fewer
-    // than 64 lanes): lanes take part while they still have weights, and a
-    // lane's last weight is read off its state.  One position per iteration;
-    // each lane's eight output words move through a 128-bit shift register.
+    // remaining macro-steps (a lane's last group, partial groups, or fewer
+    // than 64 lanes): lanes take part while they still have weights.  In its
+    // last group of c weights a lane decodes only the s symbol of the last
+    // m = min(4, c); their fractions are the low 7m bits of the state the lane
+    // ends in, under a leading one at bit max(16, 7m).  One position per
+    // iteration; each lane's eight output words move through a 128-bit shift
+    // register.
     bool has[R];     // the lane has any weight in this chunk
+    uint32_t mraw[R];
 #pragma unroll
-    for (int q = 0; q < R; q++) has[q] = 64 * q + lane < P && 8ull * (LB + 64 * q + lane) < n_c;
+    for (int q = 0; q < R; q++) {
+        has[q] = 64 * q + lane < P && 8ull * (LB + 64 * q + lane) < n_c;
+        mraw[q] = 0;
+    }
     for (uint32_t t = T_main; t < T; t++) {
-        int32_t cnt[R], last[R];
+        int32_t cnt[R], raw0[R];
+        bool fin[R];
         uint32_t o[R][4];
 #pragma unroll
         for (int q = 0; q < R; q++) {
             const uint32_t l = 64 * q + lane;
             const int64_t left = (int64_t)n_c - 8 * ((int64_t)t * K + LB + l);
             cnt[q] = l < P ? (int32_t)(left < 0 ? 0 : (left > 8 ? 8 : left)) : 0;
-            // the lane's last weight is in this macro-step when the next one
+            // the lane's last group is in this macro-step when the next one
             // has none of its weights
-            last[q] = (cnt[q] > 0 && left - 8 * (int64_t)K <= 0) ? cnt[q] - 1 : -1;
+            fin[q] = cnt[q] > 0 && left - 8 * (int64_t)K <= 0;
+            if (fin[q]) mraw[q] = cnt[q] < 4 ? (uint32_t)cnt[q] : 4u;
+            raw0[q] = fin[q] ? cnt[q] - (int32_t)mraw[q] : 8;
 #pragma unroll
             for (int k = 0; k < 4; k++) o[q][k] = 0;
         }
 #pragma unroll 1
         for (int p = 0; p < 8; p++) {
             ring_top_up(g, pos);
-            bool act[R];
+            bool act_s[R], act_f[R];
             uint2 se[R];
 #pragma unroll
             for (int q = 0; q < R; q++) {
-                act[q] = p < cnt[q] && p != last[q];
+                act_s[q] = p < cnt[q];
+                act_f[q] = p < cnt[q] && p < raw0[q];
                 uint32_t xs = x[q];
                 se[q] = step_s(xs, md);
-                if (act[q]) x[q] = xs;
+                if (act_s[q]) x[q] = xs;
             }
-            refill_all<R, RW>(x, act, g, pos);
+            refill_all<R, RW>(x, act_s, g, pos);
 #pragma unroll
             for (int q = 0; q < R; q++) {
                 uint32_t xs = x[q];
                 uint32_t w = step_f(xs, se[q], md);
-                if (act[q]) x[q] = xs;
-                if (p == last[q]) w = x[q] - kStateLow;
+                if (act_f[q]) x[q] = xs;
+                if (p >= raw0[q]) w = se[q].y << 7;   // s alone; the fraction comes from the final state
                 // shift the 128-bit register right by 16 and insert w on top
                 o[q][0] = __builtin_amdgcn_alignbit(o[q][1], o[q][0], 16);
                 o[q][1] = __builtin_amdgcn_alignbit(o[q][2], o[q][1], 16);
                 o[q][2] = __builtin_amdgcn_alignbit(o[q][3], o[q][2], 16);
                 o[q][3] = __builtin_amdgcn_alignbit(w, o[q][3], 16);
             }
-            refill_all<R, RW>(x, act, g, pos);
+            refill_all<R, RW>(x, act_f, g, pos);
         }
 #pragma unroll
         for (int q = 0; q < R; q++) {
+            // after its last group a lane is back at its start state: put the
+            // fractions it holds into the words of the group's last weights
+            if (fin[q]) {
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    const int32_t i = k - raw0[q];
+                    if (i >= 0 && k < cnt[q]) o[q][k >> 1] |= ((x[q] >> (7 * i)) & 127u) << (16 * (k & 1));
+                }
+            }
             const uint64_t g16 = (uint64_t)t * K + LB + 64 * q + lane;
             if (cnt[q] == 8) {
                 ((uint4*)out)[g16] = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
@@ -346,13 +380,17 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
     }
 
     // a stream is whole when every lane ends at the state its encoder
-    // started from (2^16 plus its last weight; 2^16 for a lane without
-    // weights) and exactly the stream's words were consumed
+    // started from (the leading one over its m fractions and nothing else;
+    // 2^16 for a lane without weights) and exactly the stream's words were
+    // consumed
     bool bad = false;
 #pragma unroll
-    for (int q = 0; q < R; q++) bad |= has[q] ? (x[q] - kStateLow) > 0xFFFFu : x[q] != kStateLow;
+    for (int q = 0; q < R; q++) {
+        const uint32_t lead = mraw[q] > 2 ? 7 * mraw[q] : 16u;
+        bad |= has[q] ? ((x[q] >> lead) != 1u || ((x[q] - (1u << lead)) >> (7 * mraw[q])) != 0u) : x[q] != kStateLow;
+    }
     const uint64_t badm = __builtin_amdgcn_ballot_w64(bad);
-    if (lane == 0) a.status[r.status_base + unit] = (badm ? 1u : 0u) | (pos != nw ? 2u : 0u);
+    if (lane == 0) a.status[r.status_base + unit] = (badm ? 1u : 0u) | (pos - skip != nw ? 2u : 0u);
 }
 
 // Stage one record's lookup tables into LDS (all threads of the workgroup).

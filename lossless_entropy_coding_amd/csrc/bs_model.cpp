@@ -41,8 +41,8 @@ const char* last_error() { return g_err.c_str(); }
 bool params_ok(const bs_params* p) {
     if (!p) { set_error("params is NULL"); return false; }
     const uint32_t K = p->lanes;
-    if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256 || K == 512 || K == 1024)) {
-        set_error("lanes must be a power of two in 1..64, or 128, 256, 512 or 1024 (got %u)", K);
+    if (K == 0 || (K & (K - 1)) || !(K <= 64 || K == 128 || K == 256 || K == 512 || K == 1024 || K == 2048)) {
+        set_error("lanes must be a power of two in 1..64, or 128, 256, 512, 1024 or 2048 (got %u)", K);
         return false;
     }
     if (p->stream_lanes && ((p->stream_lanes & (p->stream_lanes - 1)) || p->stream_lanes > K)) {
@@ -50,7 +50,7 @@ bool params_ok(const bs_params* p) {
         return false;
     }
     if ((p->stream_lanes ? p->stream_lanes : K) > 512) {
-        set_error("a word stream holds at most 512 lanes: set stream_lanes for 1024 lanes");
+        set_error("a word stream holds at most 512 lanes: set stream_lanes for 1024 or 2048 lanes");
         return false;
     }
     if (p->chunk_weights == 0 || p->chunk_weights % (8 * K)) {

@@ -90,13 +90,13 @@ def _with_streams(wl: synth.Workload, stream_lanes: int) -> synth.Workload:
 # wavefronts than 128 lanes, for about 0.25% more size; the 917M-weight
 # embedding keeps 128 lanes, because it is bound by VALU issue and more lanes
 # only add state overhead.
-# The 4096x4096 matrix is only 128 chunks of 256 KiB: 1024 lanes per chunk
-# (128 weights per lane) still keep the lane-state overhead inside the 1% size
-# budget, and streams of 64 lanes let sixteen wavefronts decode each chunk, so
-# that 2048 wavefronts share the GPU.
+# The 4096x4096 matrix is only 128 chunks of 256 KiB: 2048 lanes per chunk
+# (64 weights per lane) still keep the lane-state overhead inside the 1% size
+# budget, and streams of 64 lanes let 32 wavefronts decode each chunk, so
+# that 4096 wavefronts share the GPU.
 CONFIG_BUILDERS = {
     "1": lambda device: synth.cfg1(device),
-    "2": lambda device: _with_streams(synth.cfg2(device, lanes=1024), 64),
+    "2": lambda device: _with_streams(synth.cfg2(device, lanes=2048), 64),
     "3": lambda device: synth.cfg3(device, lanes=256),
     "4": lambda device: synth.cfg4(device),
 }

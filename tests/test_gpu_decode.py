@@ -71,6 +71,9 @@ CASES = [
     ("k1024_p64", 2 * 131072 + 8 * 1000 + 5, 0.02, 131072, 1024, 64),
     ("k1024_p512", 262144 + 3, 0.03, 262144, 1024, 512),
     ("k1024_p128_short", 9000, 0.02, 131072, 1024, 128),
+    ("k2048_p64", 3 * 131072 + 8 * 2000 + 3, 0.02, 131072, 2048, 64),
+    ("k2048_p256_ragged", 131072 + 12345, 0.03, 131072, 2048, 256),
+    ("k2048_p64_short", 20001, 0.02, 131072, 2048, 64),
 ]
 
 

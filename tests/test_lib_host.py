@@ -56,7 +56,8 @@ def test_encoder_bytes_match_oracle(seed, n, W, K):
 @pytest.mark.parametrize("seed,n,W,K,P", [(10, 100000, 4096, 8, 2), (11, 40000, 8192, 64, 16), (12, 300000, 131072, 256, 64),
                                           (13, 5000, 131072, 256, 64), (14, 70001, 65536, 128, 1), (15, 0, 64, 8, 4),
                                           (16, 262144 * 2 + 5, 262144, 512, 128), (17, 131072 * 2 + 77, 131072, 1024, 64),
-                                          (18, 3000, 131072, 1024, 512)])
+                                          (18, 3000, 131072, 1024, 512), (19, 131072 * 2 + 8 * 2047 + 3, 131072, 2048, 64),
+                                          (20, 5000, 131072, 2048, 512)])
 def test_encoder_bytes_match_oracle_streams(seed, n, W, K, P):
     rng = np.random.default_rng(seed)
     w = _words(rng.standard_normal(n) * rng.choice([0.004, 0.02, 0.1]))
