@@ -42,8 +42,8 @@ __device__ __forceinline__ uint4 load_piece(__amdgpu_buffer_rsrc_t rs, uint32_t 
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Per-wave ring of stream words in LDS: RW words (2048, or 4096 for eight
-// lanes per thread) plus a 64-word copy of its head after its end, so that a
+// Per-wave ring of stream words in LDS: RW words (1024 to 4096, by lanes per
+// thread and layout) plus a 64-word copy of its head after its end, so that a
 // refill of up to 64 consecutive words never wraps.  Words are refilled RW/2
 // at a time (RW/1024 16-B pieces per lane), loaded one refill ahead.
 template <uint32_t RW>
@@ -57,20 +57,25 @@ struct Ring {
     uint32_t lane;
 };
 
+// Start the ring: issue the loads of the first RW/2 words (into `first`) and
+// of the RW/2 after them (the prefetch); ring_commit writes `first` into LDS.
 template <uint32_t RW>
-__device__ __forceinline__ void ring_init(Ring<RW>& g, uint32_t lane) {
-    uint4* r4 = (uint4*)g.base;
+__device__ __forceinline__ void ring_issue(Ring<RW>& g, uint32_t lane, uint4 (&first)[Ring<RW>::kPieces]) {
     g.lane = lane;
     const __amdgpu_buffer_rsrc_t rs = stream_rsrc(g.words, g.bytes, 0);
-    uint4 first[Ring<RW>::kPieces];
 #pragma unroll
     for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) first[k] = load_piece(rs, 16 * (64 * k + lane));
 #pragma unroll
     for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) g.pf[k] = load_piece(rs, 16 * (64 * (Ring<RW>::kPieces + k) + lane));
-#pragma unroll
-    for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) r4[64 * k + lane] = first[k];
-    if (lane < kRingMirror / 8) r4[RW / 8 + lane] = first[0];
     g.fill = RW / 2;
+}
+
+template <uint32_t RW>
+__device__ __forceinline__ void ring_commit(Ring<RW>& g, const uint4 (&first)[Ring<RW>::kPieces]) {
+    uint4* r4 = (uint4*)g.base;
+#pragma unroll
+    for (uint32_t k = 0; k < Ring<RW>::kPieces; k++) r4[64 * k + g.lane] = first[k];
+    if (g.lane < kRingMirror / 8) r4[RW / 8 + g.lane] = first[0];
 }
 
 // keep at least RW/2 words ahead of `pos` in the ring (uniform branch)
@@ -137,6 +142,21 @@ __device__ __forceinline__ uint32_t step_f(uint32_t& x, const uint2 se, const Mo
     return __builtin_amdgcn_alignbit(se.y, e.x, 25);
 }
 
+// Waves that share a SIMD issue oldest first, so when a workgroup's waves all
+// start together its youngest waves finish well after the oldest.  Giving the
+// four waves of a SIMD the four issue priorities in turn, one macro-step each,
+// lets them progress evenly.  That only pays when every wave has a single
+// unit (the kernel then ends with the slowest wave); with several units per
+// wave the default order is faster overall.
+__device__ __forceinline__ void rotate_priority(uint32_t k) {
+    switch (k & 3) {
+        case 0: __builtin_amdgcn_s_setprio(0); break;
+        case 1: __builtin_amdgcn_s_setprio(1); break;
+        case 2: __builtin_amdgcn_s_setprio(2); break;
+        default: __builtin_amdgcn_s_setprio(3); break;
+    }
+}
+
 // sum of the eight 4-bit fields of v
 __device__ __forceinline__ uint32_t nibble_sum(uint32_t v) {
     const uint32_t t = (v & 0x0F0F0F0Fu) + ((v >> 4) & 0x0F0F0F0Fu);
@@ -161,10 +181,25 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
     return v;
 }
 
-// Decode unit u of a record: word stream st = u mod S of chunk ch = u / S,
-// whose P lanes are lanes [st * P, st * P + P) of the chunk.
+// One decode unit of a record: word stream st = u mod S of chunk ch = u / S,
+// whose P lanes are lanes [st * P, st * P + P) of the chunk.  unit_open
+// reads the chunk's index entry, the lanes' start states and the head of the
+// stream into the wave's ring; unit_decode then decodes the unit (it needs
+// the lookup tables in LDS).
 template <int R, bool C>
-__device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit, uint32_t wave, uint8_t* lds) {
+struct Unit {
+    uint32_t x[R];                 // lane states
+    Ring<ring_words(R, C)> g;
+    uint32_t pos;                  // ring read position (stream words, from the 16-byte boundary)
+    uint32_t skip;                 // words of the stream before, loaded ahead of this one
+    uint32_t nw;                   // this stream's words
+    uint32_t ch, st, n_c;          // chunk, stream, weights in the chunk
+    uint32_t unit;
+};
+
+template <int R, bool C>
+__device__ __forceinline__ void unit_open(const DecodeArgs& a, const RecDev& r, uint32_t unit, uint32_t wave, uint8_t* lds,
+                          Unit<R, C>& u) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t ch = unit >> r.streams_log2;
     const uint32_t st = unit & ((1u << r.streams_log2) - 1);
@@ -217,11 +252,19 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
     const uint32_t skip = (woff - w16) / 2;
     const uint32_t wend16 = (woff + 2 * nw + 15) & ~15u;
 
-    // lane states first, then the ring: both are complete before the loop so
-    // that no load issued here is still pending when the loop first runs.
+    // the ring's first loads, then the lane states, so that both sets of
+    // loads are in flight together; everything is complete before the
+    // decode loop runs, so that no load issued here is still pending there.
+    constexpr uint32_t RW = ring_words(R, C);
+    Ring<RW>& g = u.g;
+    g.base = (uint16_t*)(lds + lut_lds(C) + wave * ring_bytes(R, C));
+    g.words = payload + w16;
+    g.bytes = wend16 - w16;
+    uint4 first[Ring<RW>::kPieces];
+    ring_issue(g, lane, first);
     // Lane LB + l's bits start at 16 (LB + l) plus the codes of the lanes
     // before it; a state is 1 << (16 + e) plus its 16 + e low bits.
-    uint32_t x[R];
+    uint32_t (&x)[R] = u.x;
     uint32_t before = esum_below;
 #pragma unroll
     for (int q = 0; q < R; q++) {
@@ -241,17 +284,29 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
         x[q] = l < P ? (1u << len) | bits : kStateLow;
         before += __builtin_amdgcn_readlane(incl, 63);
     }
-    constexpr uint32_t RW = ring_words(R, C);
-    Ring<RW> g;
-    g.base = (uint16_t*)(lds + lut_lds(C) + wave * ring_bytes(R, C));
-    g.words = payload + w16;
-    g.bytes = wend16 - w16;
-    ring_init(g, lane);
+    ring_commit(g, first);
     __builtin_amdgcn_s_waitcnt(0);
+    u.pos = skip;
+    u.skip = skip;
+    u.nw = nw;
+    u.ch = ch;
+    u.st = st;
+    u.n_c = n_c;
+    u.unit = unit;
+}
 
+template <int R, bool C>
+__device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r, uint8_t* lds, Unit<R, C>& u,
+                                            bool fair) {
+    const uint32_t lane = threadIdx.x & 63;
+    constexpr uint32_t RW = ring_words(R, C);
+    Ring<RW>& g = u.g;
+    uint32_t (&x)[R] = u.x;
+    const uint32_t K = r.K, P = r.P, LB = u.st * P;
+    const uint32_t n_c = u.n_c, ch = u.ch, unit = u.unit, nw = u.nw, skip = u.skip;
     const Model md{lds, r.m_s, r.m_f, ((1u << r.m_s) - 1) << 3, ((1u << r.m_f) - 1) << 3};
 
-    uint32_t pos = skip;
+    uint32_t pos = u.pos;
     uint8_t* out = a.out + (r.out_off - a.out_base) + 2ull * ch * r.W;
 
     const uint32_t groups = (n_c + 7) / 8;
@@ -267,7 +322,9 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
     for (int q = 0; q < R; q++) all_on[q] = true;
 
     // full macro-steps: every lane decodes 8 weights, one 128-bit store per lane group
+    const uint32_t prio0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);   // wave / 4: rank on its SIMD
     for (uint32_t t = 0; t < T_main; t++) {
+        if (fair) rotate_priority(prio0 + t);
         uint32_t o[R][4];
 #pragma unroll
         for (int p = 0; p < 8; p++) {
@@ -312,6 +369,7 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
         mraw[q] = 0;
     }
     for (uint32_t t = T_main; t < T; t++) {
+        if (fair) rotate_priority(prio0 + t);
         int32_t cnt[R], raw0[R];
         bool fin[R];
         uint32_t o[R][4];
@@ -393,25 +451,90 @@ __device__ void decode_chunk(const DecodeArgs& a, const RecDev& r, uint32_t unit
     if (lane == 0) a.status[r.status_base + unit] = (badm ? 1u : 0u) | (pos - skip != nw ? 2u : 0u);
 }
 
-// Stage one record's lookup tables into LDS (all threads of the workgroup).
-template <bool C>
-__device__ __forceinline__ void stage_luts(const DecodeArgs& a, const RecDev& r, uint8_t* lds) {
-    const uint4* src = (const uint4*)(a.luts + r.lut_off);
+// Stage one record's lookup tables into LDS (all threads of the workgroup):
+// the image's s part goes to the start of the LDS tables and its fraction
+// pages after the s region.  Each thread moves up to kStageBatch 16-byte
+// pieces per round trip, so that a 16-wave workgroup copies the largest image
+// in one; the first batch's loads are issued before a wave opens its first
+// unit, so that the two overlap.
+constexpr int kStageBatch = 8;
+
+// LDS piece of image piece i
+__device__ __forceinline__ uint32_t stage_slot(uint32_t i, uint32_t ns16, uint32_t gap16) {
+    return i < ns16 ? i : i + gap16;
+}
+
+// The units [u0, u1) of one record, taken by the workgroup's waves in turn.
+// Every wave takes part in the staging and the barrier after it.
+template <int R, bool C>
+__device__ __forceinline__ void run_units(const DecodeArgs& a, const RecDev& r, uint32_t u0, uint32_t u1,
+                                          uint32_t wave, uint8_t* lds) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));   // plain vector: stays in registers
+    const v4u* src = (const v4u*)(a.luts + r.lut_off);
     const uint32_t ns16 = (8u << r.m_s) / 16;
-    uint4* d = (uint4*)lds;
-    for (uint32_t i = threadIdx.x; i < ns16; i += blockDim.x) d[i] = src[i];
-    const uint32_t nf16 = (r.n_tables + 1) * (fpage_bytes(C) / 16);
-    const uint4* fs = src + ns16;
-    uint4* fd = (uint4*)(lds + slut_bytes(C));
-    for (uint32_t i = threadIdx.x; i < nf16; i += blockDim.x) fd[i] = fs[i];
+    const uint32_t n16 = ns16 + (r.n_tables + 1) * (fpage_bytes(C) / 16);
+    const uint32_t gap16 = slut_bytes(C) / 16 - ns16;
+    const uint32_t step = kStageBatch * blockDim.x;
+    v4u* d = (v4u*)lds;
+    v4u sv[kStageBatch];
+#pragma unroll
+    for (int k = 0; k < kStageBatch; k++) {
+        const uint32_t i = threadIdx.x + k * blockDim.x;
+        if (i < n16) sv[k] = src[i];
+    }
+    Unit<R, C> un;
+    uint32_t u = u0 + wave;
+    if (u < u1) unit_open<R, C>(a, r, u, wave, lds, un);
+#pragma unroll
+    for (int k = 0; k < kStageBatch; k++) {
+        const uint32_t i = threadIdx.x + k * blockDim.x;
+        if (i < n16) d[stage_slot(i, ns16, gap16)] = sv[k];
+    }
+    for (uint32_t base = threadIdx.x + step; base < n16; base += step) {
+        v4u t[kStageBatch];
+#pragma unroll
+        for (int k = 0; k < kStageBatch; k++) {
+            const uint32_t i = base + k * blockDim.x;
+            if (i < n16) t[k] = src[i];
+        }
+#pragma unroll
+        for (int k = 0; k < kStageBatch; k++) {
+            const uint32_t i = base + k * blockDim.x;
+            if (i < n16) d[stage_slot(i, ns16, gap16)] = t[k];
+        }
+    }
+    __syncthreads();
+    for (; u < u1; u += a.waves) {
+        if (u != u0 + wave) unit_open<R, C>(a, r, u, wave, lds, un);
+        unit_decode<R, C>(a, r, lds, un, u1 - u0 <= a.waves);
+    }
+}
+
+// The run of units starting at u0 of record r, with the lane width that the
+// kernel instance G fixes or, for a mixed instance, the record's own.
+template <int G, bool C>
+__device__ __forceinline__ void run_record(const DecodeArgs& a, const RecDev& r, uint32_t u0, uint32_t wave,
+                                           uint8_t* lds) {
+    const uint32_t u1 = min(r.n_chunks << r.streams_log2, u0 + a.run);
+    if (G == 1 || G == 2 || G == 4 || G == 8) {
+        constexpr int R = (G == 1 || G == 2 || G == 4 || G == 8) ? G : 1;
+        run_units<R, C>(a, r, u0, u1, wave, lds);
+    } else if (r.lanes_per_thread == 1) {
+        run_units<1, C>(a, r, u0, u1, wave, lds);
+    } else if (G == 0 || r.lanes_per_thread == 2) {
+        run_units<2, C>(a, r, u0, u1, wave, lds);
+    } else {
+        run_units<4, C>(a, r, u0, u1, wave, lds);
+    }
 }
 
 // Workgroup b of a launch decodes one run of units (chunk streams) inside one
 // record: each record r of the class entries [i0, i1) is cut into
 // ceil(units_r / run) runs of `run` units (the last one shorter), and the runs
-// are numbered in record order.  Wave 0 finds b's record with a prefix sum
-// over the records' run counts; the record's lookup tables are staged into
-// LDS once and the waves then take the run's units in turn.
+// are numbered in record order.  With one record the run is b; otherwise
+// wave 0 finds b's record with a prefix sum over the records' run counts.
+// The record's lookup tables are staged into LDS once and the waves then take
+// the run's units in turn.
 // One launch covers every record with 1, 2 or 4 lanes per thread (16-wave
 // workgroups), so that small tensors decode alongside large ones: G is that
 // lane width when all the launch's records share it, 0 for a mix of 1 and 2,
@@ -423,10 +546,20 @@ template <int G, bool C>
 __global__ __launch_bounds__(G == 8 ? 512 : 1024) void decode_kernel(const DecodeArgs a) {
     // static allocation: the LDS base is a compile-time constant, so table and
     // ring addresses fold into the instructions' offsets
-    __shared__ __align__(16) uint8_t lds[lut_lds(C) + max_waves(G == 8 ? 8 : 1) * ring_bytes(G == 8 ? 8 : 1, C)];
+    // rings sized for the widest lane count the instance runs (a narrower
+    // record's waves use smaller rings at smaller offsets)
+    constexpr uint32_t RMAX = G == 8 ? 8 : (G == 1 ? 1 : G == 2 || G == 0 ? 2 : 4);
+    __shared__ __align__(16) uint8_t lds[lut_lds(C) + max_waves(RMAX) * ring_bytes(RMAX, C)];
     __shared__ uint32_t pick[2];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t b = blockIdx.x;
+    if (a.i1 - a.i0 == 1) {
+        // one record, passed by value: no lookup before the tables
+        const uint32_t u0 = b * a.run;
+        if (u0 >= (a.one.n_chunks << a.one.streams_log2)) return;   // uniform over the workgroup
+        run_record<G, C>(a, a.one, u0, wave, lds);
+        return;
+    }
     if (wave == 0) {
         const uint32_t lane = threadIdx.x & 63;
         uint32_t carry = 0, e = UINT32_MAX, j = 0;
@@ -456,20 +589,7 @@ __global__ __launch_bounds__(G == 8 ? 512 : 1024) void decode_kernel(const Decod
     const uint32_t e = __builtin_amdgcn_readfirstlane(pick[0]);
     if (e == UINT32_MAX) return;   // no run for this workgroup (launch larger than the runs)
     const RecDev r = a.recs[a.cls.recs[e]];
-    const uint32_t u0 = __builtin_amdgcn_readfirstlane(pick[1]) * a.run;
-    const uint32_t u1 = min(r.n_chunks << r.streams_log2, u0 + a.run);
-    stage_luts<C>(a, r, lds);
-    __syncthreads();
-    if (G == 1 || G == 2 || G == 4 || G == 8) {
-        constexpr int R = (G == 1 || G == 2 || G == 4 || G == 8) ? G : 1;
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<R, C>(a, r, u, wave, lds);
-    } else if (r.lanes_per_thread == 1) {
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<1, C>(a, r, u, wave, lds);
-    } else if (G == 0 || r.lanes_per_thread == 2) {
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<2, C>(a, r, u, wave, lds);
-    } else {
-        for (uint32_t u = u0 + wave; u < u1; u += a.waves) decode_chunk<4, C>(a, r, u, wave, lds);
-    }
+    run_record<G, C>(a, r, __builtin_amdgcn_readfirstlane(pick[1]) * a.run, wave, lds);
 }
 
 }  // namespace

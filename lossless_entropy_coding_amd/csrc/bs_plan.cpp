@@ -42,6 +42,7 @@ struct bs_plan {
     std::vector<uint32_t> cls_recs[kClasses], cls_start[kClasses];
     std::vector<uint32_t> cls_R[kClasses];   // lanes per thread of each class entry
     std::vector<bsd::RawDev> raws;
+    std::vector<bsd::RecDev> h_recs;   // host copy of d_recs (a launch of one record passes it by value)
     bsd::RecDev* d_recs = nullptr;
     uint32_t* d_cls_recs[kClasses] = {nullptr, nullptr, nullptr};
     uint32_t* d_cls_start[kClasses] = {nullptr, nullptr, nullptr};
@@ -210,6 +211,7 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
         if (ee != hipSuccess || !bytes) return ee;
         return hipMemcpyAsync(*dst, src, bytes, hipMemcpyHostToDevice, s);
     };
+    p->h_recs = recs;
     e = up((void**)&p->d_recs, recs.data(), recs.size() * sizeof(bsd::RecDev));
     for (int k = 0; k < bs_plan::kClasses && e == hipSuccess; k++) {
         e = up((void**)&p->d_cls_recs[k], p->cls_recs[k].data(), p->cls_recs[k].size() * 4);
@@ -280,6 +282,7 @@ bs_status bs_decode_async(const bs_plan* p, uint32_t first, uint32_t count, void
         a.out_base = out_base;
         a.i0 = e0[k];
         a.i1 = e1[k];
+        if (e1[k] - e0[k] == 1) a.one = p->h_recs[p->cls_recs[k][e0[k]]];
         uint32_t groups;
         launch_shape(p, k, e0[k], e1[k], a.waves, a.run, groups);
         // the specialised kernel when every record of the launch has the same
