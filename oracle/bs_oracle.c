@@ -544,9 +544,10 @@ static uint32_t state_code(uint32_t x) {
     return e;
 }
 
-/* bytes of the nibble block and of the mantissa block for K lanes whose codes sum to esum */
+/* bytes of the nibble block of K lanes; 16-bit units of the state bits of P
+   lanes whose codes sum to esum */
 static uint64_t code_block_bytes(uint32_t K) { return round_up(((uint64_t)K + 1) / 2, 16); }
-static uint64_t mant_block_bytes(uint32_t K, uint64_t esum) { return round_up((16ull * K + esum + 7) / 8, 16); }
+static uint64_t mant_units(uint32_t P, uint64_t esum) { return (16ull * P + esum + 15) / 16; }
 
 static void put_bits(uint8_t* b, uint64_t off, uint32_t v, uint32_t len) {
     for (uint32_t i = 0; i < len; i++) {
@@ -592,13 +593,14 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
     for (uint32_t f = 0; f < 128; f++) md->qf[0][f] = 1u << (M_f - 7);
     if (rc) goto done;
 
-    /* fixed part and tables */
+    /* fixed part, tables, chunk index and (S > 1) stream table */
     uint64_t off = 24;
     uint64_t tables_end = off + 4ull * n_sym;
     tables_end = round_up(tables_end + n_sym, 4);
     tables_end += 256ull * md->n_tables;
     uint64_t index_off = round_up(tables_end, 16);
-    uint64_t payload_off = index_off + 16 * n_chunks;
+    uint64_t stab_off = index_off + 16 * n_chunks;
+    uint64_t payload_off = round_up(stab_off + 4ull * (S - 1) * n_chunks, 16);
     rc = bb_reserve(body, payload_off);
     if (rc) goto done;
     body->n = payload_off;
@@ -618,53 +620,58 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
     for (uint32_t t = 1; t <= md->n_tables; t++)
         for (uint32_t f = 0; f < 128; f++) put16(b + ft + 256ull * (t - 1) + 2 * f, md->qf[t][f]);
 
-    /* chunks: the K lanes' length codes, then (S > 1) the S stream word
-       counts, then the states' mantissa bits, each padded to 16 bytes, then
-       each stream's words padded to 4 bytes; the chunk's payload as a whole
-       is padded to 16 bytes */
+    /* chunks: the K lanes' length codes, padded to 16 bytes, then the
+       streams back to back, each the state bits of its P lanes (padded to a
+       16-bit unit) followed by its words; the payload is padded to 16 bytes.
+       The index gives the payload's offset and the units of its stream area;
+       the stream table the start unit of streams 1 .. S-1 */
     uint32_t* states = (uint32_t*)malloc(sizeof(uint32_t) * K);
     wordlist* wls = (wordlist*)calloc(S, sizeof(wordlist));
-    if (!states || !wls) { free(states); free(wls); rc = BSO_ENOMEM; goto done; }
+    uint64_t* units = (uint64_t*)calloc(S, sizeof(uint64_t));
+    uint64_t* mu = (uint64_t*)calloc(S, sizeof(uint64_t));
+    if (!states || !wls || !units || !mu) { free(states); free(wls); free(units); free(mu); rc = BSO_ENOMEM; goto done; }
     for (uint64_t c = 0; c < n_chunks && !rc; c++) {
         uint32_t n_c = (uint32_t)((n - c * W) < W ? (n - c * W) : W);
         for (uint32_t st = 0; st < S; st++) wls[st].n = 0;
         for (uint32_t st = 0; st < S && !rc; st++)
             rc = chunk_encode(md, w + c * W, n_c, K, st * P, (st + 1) * P, states, &wls[st]);
         if (rc) break;
-        uint64_t esum = 0;
-        for (uint32_t l = 0; l < K; l++) esum += state_code(states[l]);
+        uint64_t total = 0;
+        for (uint32_t st = 0; st < S; st++) {
+            uint64_t esum = 0;
+            for (uint32_t l = st * P; l < (st + 1) * P; l++) esum += state_code(states[l]);
+            mu[st] = mant_units(P, esum);
+            units[st] = mu[st] + wls[st].n;
+            total += units[st];
+        }
         uint64_t start = body->n;
         uint64_t code_bytes = code_block_bytes(K);
-        uint64_t counts_bytes = S > 1 ? round_up(4ull * S, 16) : 0;
-        uint64_t mant_bytes = mant_block_bytes(K, esum);
-        uint64_t end = start + code_bytes + counts_bytes + mant_bytes, total_words = 0;
-        for (uint32_t st = 0; st < S; st++) { end += round_up(2 * wls[st].n, 4); total_words += wls[st].n; }
-        end = start + round_up(end - start, 16);
+        uint64_t end = start + round_up(code_bytes + 2 * total, 16);
         rc = bb_reserve(body, end);
         if (rc) break;
         b = body->p;
         memset(b + start, 0, end - start);
         put64(b + index_off + 16 * c, start);
-        put32(b + index_off + 16 * c + 8, (uint32_t)total_words);
+        put32(b + index_off + 16 * c + 8, (uint32_t)total);
         put32(b + index_off + 16 * c + 12, 0);
-        uint64_t moff = 0;
-        uint8_t* mant = b + start + code_bytes + counts_bytes;
-        for (uint32_t l = 0; l < K; l++) {
-            uint32_t e = state_code(states[l]);
-            b[start + l / 2] |= (uint8_t)(e << (4 * (l % 2)));
-            put_bits(mant, moff, states[l] - (1u << (16 + e)), 16 + e);
-            moff += 16 + e;
-        }
-        if (S > 1)
-            for (uint32_t st = 0; st < S; st++) put32(b + start + code_bytes + 4ull * st, (uint32_t)wls[st].n);
-        uint64_t at = start + code_bytes + counts_bytes + mant_bytes;
+        for (uint32_t l = 0; l < K; l++) b[start + l / 2] |= (uint8_t)(state_code(states[l]) << (4 * (l % 2)));
+        uint64_t at = 0;   /* units from the start of the stream area */
         for (uint32_t st = 0; st < S; st++) {
+            if (st > 0) put32(b + stab_off + 4 * ((S - 1) * c + st - 1), (uint32_t)at);
+            uint8_t* area = b + start + code_bytes + 2 * at;
+            uint64_t moff = 0;
+            for (uint32_t l = st * P; l < (st + 1) * P; l++) {
+                uint32_t e = state_code(states[l]);
+                put_bits(area, moff, states[l] - (1u << (16 + e)), 16 + e);
+                moff += 16 + e;
+            }
             /* the encoder pushes words in reverse order of their use */
-            for (uint64_t i = 0; i < wls[st].n; i++) put16(b + at + 2 * i, wls[st].w[wls[st].n - 1 - i]);
-            at += round_up(2 * wls[st].n, 4);
+            for (uint64_t i = 0; i < wls[st].n; i++) put16(area + 2 * (mu[st] + i), wls[st].w[wls[st].n - 1 - i]);
+            at += units[st];
         }
         body->n = end;
     }
+    free(units); free(mu);
     for (uint32_t st = 0; st < S; st++) free(wls[st].w);
     free(wls);
     free(states);
@@ -788,7 +795,7 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md
     uint64_t ft = round_up(off + 4ull * n_sym + n_sym, 4);
     uint64_t tab_end = ft + 256ull * md->n_tables;
     *index_off = round_up(tab_end, 16);
-    if (*index_off + 16 * *n_chunks > len) return BSO_EFORMAT;
+    if (*index_off + 16 * *n_chunks + 4ull * (*S - 1) * *n_chunks > len) return BSO_EFORMAT;
     memset(md->qs, 0, sizeof(md->qs));
     memset(md->route, 0, sizeof(md->route));
     uint64_t sum = 0;
@@ -814,39 +821,42 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md
 
 /* Decode chunk ch of a parsed BF16 record body b (rl bytes) into out[0..n_c). */
 static int decode_one_chunk(const bso_model* md, const uint8_t* b, uint64_t rl, uint64_t io, uint32_t K,
-                            uint32_t S, uint64_t ch, uint32_t n_c, uint16_t* out) {
+                            uint32_t S, uint64_t n_chunks, uint64_t ch, uint32_t n_c, uint16_t* out) {
     const uint8_t* e = b + io + 16 * ch;
-    uint64_t po = get64(e), nw = get32(e + 8);
-    uint64_t code_bytes = code_block_bytes(K), counts_bytes = S > 1 ? round_up(4ull * S, 16) : 0;
-    if (po % 16 || po > rl || code_bytes + counts_bytes > rl - po) return BSO_EFORMAT;
-    uint64_t esum = 0;
-    for (uint32_t l = 0; l < K; l++) esum += (b[po + l / 2] >> (4 * (l % 2))) & 15u;
-    uint64_t mant_bytes = mant_block_bytes(K, esum);
-    if (mant_bytes > rl - po - code_bytes - counts_bytes) return BSO_EFORMAT;
+    uint64_t po = get64(e), total = get32(e + 8);
+    uint64_t code_bytes = code_block_bytes(K);
+    if (po % 16 || po > rl || code_bytes > rl - po || 2 * total > rl - po - code_bytes) return BSO_EFORMAT;
+    const uint8_t* stab = b + io + 16 * n_chunks + 4 * (S - 1) * ch;
     uint32_t P = K / S;
     uint32_t* st = (uint32_t*)malloc(sizeof(uint32_t) * K);
     if (!st) return BSO_ENOMEM;
-    const uint8_t* mant = b + po + code_bytes + counts_bytes;
-    uint64_t moff = 0;
-    for (uint32_t l = 0; l < K; l++) {
-        uint32_t el = (b[po + l / 2] >> (4 * (l % 2))) & 15u;
-        st[l] = (1u << (16 + el)) | get_bits(mant, moff, 16 + el);
-        moff += 16 + el;
-    }
-    uint64_t at = po + code_bytes + counts_bytes + mant_bytes, total = 0;
     int rc = BSO_OK;
     for (uint32_t s = 0; s < S && !rc; s++) {
-        uint64_t nws = S > 1 ? get32(b + po + code_bytes + 4ull * s) : nw;
-        total += nws;
-        if (2 * nws > rl - at) { rc = BSO_EFORMAT; break; }
+        uint64_t from = s ? get32(stab + 4 * (s - 1)) : 0;
+        uint64_t to = s + 1 < S ? get32(stab + 4 * s) : total;
+        if (from > to || to > total) { rc = BSO_EFORMAT; break; }
+        const uint8_t* area = b + po + code_bytes + 2 * from;
+        /* the stream's lanes' states: length codes from the chunk's nibble
+           block, bits from the head of the stream's area */
+        uint64_t moff = 0, esum = 0;
+        for (uint32_t l = s * P; l < (s + 1) * P; l++) {
+            uint32_t el = (b[po + l / 2] >> (4 * (l % 2))) & 15u;
+            esum += el;
+        }
+        uint64_t mu = mant_units(P, esum);
+        if (mu > to - from) { rc = BSO_EFORMAT; break; }
+        for (uint32_t l = s * P; l < (s + 1) * P; l++) {
+            uint32_t el = (b[po + l / 2] >> (4 * (l % 2))) & 15u;
+            st[l] = (1u << (16 + el)) | get_bits(area, moff, 16 + el);
+            moff += 16 + el;
+        }
+        uint64_t nws = to - from - mu;
         uint16_t* words = (uint16_t*)malloc(sizeof(uint16_t) * (nws ? nws : 1));
         if (!words) { rc = BSO_ENOMEM; break; }
-        for (uint64_t j = 0; j < nws; j++) words[j] = (uint16_t)get16(b + at + 2 * j);
+        for (uint64_t j = 0; j < nws; j++) words[j] = (uint16_t)get16(area + 2 * (mu + j));
         rc = chunk_decode(md, st, words, nws, n_c, K, s * P, (s + 1) * P, out);
         free(words);
-        at += round_up(2 * nws, 4);
     }
-    if (!rc && total != nw) rc = BSO_EFORMAT;
     free(st);
     return rc;
 }
@@ -879,7 +889,7 @@ int bso_decode_container(const uint8_t* c, uint64_t len, uint8_t* out, uint64_t 
             if (!rc && n) { tmp = (uint16_t*)malloc(sizeof(uint16_t) * W); if (!tmp) rc = BSO_ENOMEM; }
             for (uint64_t ch = 0; ch < nch && !rc; ch++) {
                 uint32_t n_c = (uint32_t)((n - ch * W) < W ? (n - ch * W) : W);
-                rc = decode_one_chunk(md, c + ro, rl, io, K, S, ch, n_c, tmp);
+                rc = decode_one_chunk(md, c + ro, rl, io, K, S, nch, ch, n_c, tmp);
                 if (!rc) for (uint32_t j = 0; j < n_c; j++) put16(out + oo + 2 * (ch * W + j), tmp[j]);
             }
             free(tmp); free(md);
@@ -917,7 +927,7 @@ int bso_decode_chunk(const uint8_t* c, uint64_t len, uint32_t record, uint64_t c
         n_c = (n - chunk * W) < W ? (n - chunk * W) : W;
         if (n_c > out_cap) rc = BSO_ENOSPACE;
     }
-    if (!rc) rc = decode_one_chunk(md, c + ro, rl, io, K, S, chunk, (uint32_t)n_c, out);
+    if (!rc) rc = decode_one_chunk(md, c + ro, rl, io, K, S, nch, chunk, (uint32_t)n_c, out);
     free(md);
     *n_c_out = n_c;
     return rc;

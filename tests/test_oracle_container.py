@@ -32,18 +32,21 @@ def _hand_container():
     body += struct.pack("<HH", 127, 4096)                              # s-table
     body += bytes([0])                                                 # route
     body += bytes(32 - len(body))                                      # pad to 32 (index offset)
-    nw = g["n_words"]
-    body += struct.pack("<QII", 48, nw, 0)                             # chunk index
+    nw, units = g["n_words"], g["stream_units"]
+    body += struct.pack("<QII", 48, units, 0)                          # chunk index: payload at 48
     x = g["final_state"]
     e = x.bit_length() - 17                                            # length code: 2^(16+e) <= x < 2^(17+e)
     assert e == 8
     body += bytes([e]) + bytes(15)                                     # length codes + pad
     mant = x - (1 << (16 + e))                                         # 16 + e bits below the leading one
-    body += mant.to_bytes(3, "little") + bytes(13)                     # mantissa bits + pad
-    body += bytes(2 * nw) + bytes(16 - 2 * nw)                         # words (all zero) + pad
-    assert len(body) == 96
-    hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 256, 16, 0) + bytes(20)
-    d = struct.pack("<IIQQQQ", 1, 0, 8, 0, 160, 96) + hashlib.sha256(data).digest() + bytes(24)
+    mu = (16 + e + 15) // 16                                           # state units
+    assert mu + nw == units
+    body += mant.to_bytes(2 * mu, "little")                            # the stream: state bits, then words
+    body += bytes(2 * nw)                                              # words (all zero)
+    body += bytes(-len(body) % 16)                                     # payload padded to 16 B
+    assert len(body) == 80
+    hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 240, 16, 0) + bytes(20)
+    d = struct.pack("<IIQQQQ", 1, 0, 8, 0, 160, 80) + hashlib.sha256(data).digest() + bytes(24)
     c = hdr + d
     assert len(c) == 160
     return words, g["params"], c + bytes(body)

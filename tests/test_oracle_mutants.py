@@ -27,12 +27,15 @@ MUTANTS = {
                               "for (int64_t l = (int64_t)l0; l < (int64_t)l1; l++) {\n                    uint64_t j"),
     "sched_lanes_ascending": ("for (int64_t l = (int64_t)K - 1; l >= 0 && !rc; l--) {",
                               "for (int64_t l = 0; l < (int64_t)K && !rc; l++) {"),
-    "words_not_reversed": ("put16(b + at + 2 * i, wls[st].w[wls[st].n - 1 - i]);",
-                           "put16(b + at + 2 * i, wls[st].w[i]);"),
+    "words_not_reversed": ("put16(area + 2 * (mu[st] + i), wls[st].w[wls[st].n - 1 - i]);",
+                           "put16(area + 2 * (mu[st] + i), wls[st].w[i]);"),
+    "state_units_floor": ("return (16ull * P + esum + 15) / 16;", "return (16ull * P + esum) / 16;"),
+    "stream_table_off_by_one": ("if (st > 0) put32(b + stab_off + 4 * ((S - 1) * c + st - 1), (uint32_t)at);",
+                                "if (st > 0) put32(b + stab_off + 4 * ((S - 1) * c + st - 1), (uint32_t)at + 1);"),
     "streams_swapped": ("states, &wls[st]);", "states, &wls[S - 1 - st]);"),
     "state_code_off_by_one": ("while (e < 15 && (x >> (17 + e)) != 0) e++;", "while (e < 15 && (x >> (16 + e)) != 0) e++;"),
-    "state_nibbles_swapped": ("b[start + l / 2] |= (uint8_t)(e << (4 * (l % 2)));",
-                              "b[start + l / 2] |= (uint8_t)(e << (4 * (1 - l % 2)));"),
+    "state_nibbles_swapped": ("b[start + l / 2] |= (uint8_t)(state_code(states[l]) << (4 * (l % 2)));",
+                              "b[start + l / 2] |= (uint8_t)(state_code(states[l]) << (4 * (1 - l % 2)));"),
     "state_bits_msb_first": ("if ((v >> i) & 1u) b[bit / 8] |= (uint8_t)(1u << (bit % 8));",
                              "if ((v >> i) & 1u) b[bit / 8] |= (uint8_t)(0x80u >> (bit % 8));"),
     "raw_fractions_not_in_state": ("for (uint32_t i = 0; i < m; i++) x |= bso_symbol_f(w[j0 + i]) << (7 * i);",

@@ -34,23 +34,21 @@ def _hand_two_streams():
     body += struct.pack("<HH", 127, 4096)                             # s-table
     body += bytes([0])                                                # route
     body += bytes(32 - len(body))                                     # pad to 32 (index offset)
-    nw = g["n_words"]                                                 # per stream
-    body += struct.pack("<QII", 48, 2 * nw, 0)                        # chunk index: payload at 48, all words
+    nw, units = g["n_words"], g["stream_units"]                      # per stream
+    body += struct.pack("<QII", 64, 2 * units, 0)                     # chunk index: payload at 64, both streams' units
+    body += struct.pack("<I", units) + bytes(12)                      # stream table: stream 1 starts at unit 4; pad
     x = g["final_state"]
     e = x.bit_length() - 17                                           # length code of both lanes
     assert e == 8
     body += bytes([e | e << 4]) + bytes(15)                           # two length codes + pad
-    body += struct.pack("<II", nw, nw) + bytes(8)                     # stream word counts + pad
     mant = x - (1 << (16 + e))
-    bits = mant | mant << (16 + e)                                    # lane 0's bits, then lane 1's
-    body += bits.to_bytes(6, "little") + bytes(10)                    # mantissas + pad
-    assert 2 * nw == 4
-    body += bytes(2 * nw)                                             # stream 0: zero words (4 B)
-    body += bytes(2 * nw)                                             # stream 1
-    body += bytes(8)                                                  # the payload padded to 16 B
-    assert len(body) == 112
-    hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 272, 32, 0) + bytes(20)
-    d = struct.pack("<IIQQQQ", 1, 0, 16, 0, 160, 112) + hashlib.sha256(words.tobytes()).digest() + bytes(24)
+    mu = (16 + e + 15) // 16
+    assert mu + nw == units
+    for _ in range(2):                                                # stream 0, then stream 1
+        body += mant.to_bytes(2 * mu, "little") + bytes(2 * nw)       # its lane's state bits, then its words
+    assert len(body) == 96
+    hdr = b"BF16RANS" + struct.pack("<IIQQQI", 1, 1, 64, 256, 32, 0) + bytes(20)
+    d = struct.pack("<IIQQQQ", 1, 0, 16, 0, 160, 96) + hashlib.sha256(words.tobytes()).digest() + bytes(24)
     return words, g["params"], hdr + d + bytes(body)
 
 
@@ -152,39 +150,40 @@ def test_stream_payload_equals_schedule_coder(n, W, K, P):
     tables = [O.Table(m["M_s"], m["qs"])] + [O.Table(m["M_f"], q) for q in m["qf"]]
     for ch in range(m["nch"]):
         n_c = min(m["W"], n - ch * m["W"])
-        po, nw = _u(b, m["index"] + 16 * ch, "Q"), _u(b, m["index"] + 16 * ch + 8, "I")
-        states, sb, cb, mb = _packed_states(b, po, K, S)
-        at = po + sb + cb + mb
-        total = 0
+        po, total = _u(b, m["index"] + 16 * ch, "Q"), _u(b, m["index"] + 16 * ch + 8, "I")
+        stab = m["index"] + 16 * m["nch"] + 4 * (S - 1) * ch
+        starts = [0] + [_u(b, stab + 4 * (s - 1), "I") for s in range(1, S)] + [total]
+        cb = ((K + 1) // 2 + 15) // 16 * 16
         for s in range(S):
-            nws = _u(b, po + sb + 4 * s, "I") if S > 1 else nw
-            stream = np.frombuffer(b[at: at + 2 * nws], np.uint16)
+            area = po + cb + 2 * starts[s]
+            units = starts[s + 1] - starts[s]
             lanes = list(range(s * Ps, (s + 1) * Ps))
+            states, mu = _stream_states(b, po, area, lanes)
+            stream = np.frombuffer(b[area + 2 * mu: area + 2 * units], np.uint16)
             syms, kind, init = _stream_schedule(w[ch * m["W"]:], n_c, K, lanes)
             tab_of = np.where(kind == 1, 1 + m["route"][np.clip(syms_prev(syms), 0, 511)], 0)
             st_ref, w_ref = O.sched_encode(Ps, syms, tab_of.astype(np.uint32), tables, init=init)
-            assert np.array_equal(states[s * Ps: (s + 1) * Ps], st_ref), (ch, s)
+            assert np.array_equal(states, st_ref), (ch, s)
             assert np.array_equal(stream, w_ref), (ch, s)
-            at += (2 * nws + 3) // 4 * 4
-            total += nws
-        assert total == nw
+        # the payload holds the codes and the stream area, padded to 16 bytes
+        nxt = _u(b, m["index"] + 16 * (ch + 1), "Q") if ch + 1 < m["nch"] else len(b)
+        assert nxt - po == (cb + 2 * total + 15) // 16 * 16
 
 
-def _packed_states(b, po, K, S):
-    """The chunk's K final states from their length codes (a nibble per lane)
-    and mantissa bits (16 + e bits per lane, least significant first), and the
-    byte sizes of the code, count and mantissa blocks."""
-    codes = [(b[po + l // 2] >> (4 * (l % 2))) & 15 for l in range(K)]
-    cb_codes = ((K + 1) // 2 + 15) // 16 * 16
-    cb_counts = (4 * S + 15) // 16 * 16 if S > 1 else 0
-    mbits = 16 * K + sum(codes)
-    mb = ((mbits + 7) // 8 + 15) // 16 * 16
-    stream = int.from_bytes(b[po + cb_codes + cb_counts: po + cb_codes + cb_counts + mb], "little")
+def _stream_states(b, po, area, lanes):
+    """Final states of a stream's lanes: length codes from the chunk's nibble
+    block (lane l in the low nibble of byte l/2 when l is even), state bits
+    (16 + e per lane, least significant first, in lane order) from the head
+    of the stream's area; and the 16-bit units those bits take."""
+    codes = [(b[po + l // 2] >> (4 * (l % 2))) & 15 for l in lanes]
+    mbits = 16 * len(lanes) + sum(codes)
+    mu = (mbits + 15) // 16
+    bits = int.from_bytes(b[area: area + 2 * mu], "little")
     states, off = [], 0
     for e in codes:
-        states.append((1 << (16 + e)) | ((stream >> off) & ((1 << (16 + e)) - 1)))
+        states.append((1 << (16 + e)) | ((bits >> off) & ((1 << (16 + e)) - 1)))
         off += 16 + e
-    return np.array(states, np.uint32), cb_codes, cb_counts, mb
+    return np.array(states, np.uint32), mu
 
 
 def syms_prev(syms):
@@ -220,10 +219,9 @@ def test_stream_word_count_corruption_detected():
     c = bytearray(O.encode([O.bf16(w)], W=4096, K=8, P=2))
     m = _record_model(bytes(c), 0)
     ro = _u(c, 64 + 24, "Q")
-    po = _u(m["b"], m["index"], "Q")
-    cnt_off = ro + po + ((8 + 1) // 2 + 15) // 16 * 16     # after the 8 lanes' length codes
-    a, b2 = _u(c, cnt_off, "I"), _u(c, cnt_off + 4, "I")
+    stab = ro + m["index"] + 16 * m["nch"]                 # stream table of chunk 0: start of stream 1
+    a = _u(c, stab, "I")
     # move one word from stream 0 to stream 1: totals agree, streams do not
-    struct.pack_into("<II", c, cnt_off, a - 1, b2 + 1)
+    struct.pack_into("<I", c, stab, a - 1)
     rc, out, st = O.decode_status(bytes(c))
     assert rc != 0 and st[0] != 0
