@@ -139,37 +139,30 @@ void record_shape(uint64_t n, uint32_t W, uint32_t K, uint32_t& w_out, uint32_t&
     w_out = (uint32_t)align_up(n ? n : 1, 8ull * k);
 }
 
+// A final state x in [2^16, 2^32) is stored as its length code
+// e = floor(log2 x) - 16 (a nibble per lane, in the chunk's code block) and
+// its 16 + e bits below the leading one (concatenated in lane order, least
+// significant bit first, at the head of its stream, padded to a 16-bit unit).
+inline uint32_t state_code(uint32_t x) { return 31u - (uint32_t)__builtin_clz(x) - 16u; }
+inline uint64_t code_bytes(uint32_t K) { return align_up((K + 1ull) / 2, 16); }
+// 16-bit units of the state bits of P lanes whose codes sum to esum
+inline uint64_t state_units(uint32_t P, uint64_t esum) { return (16ull * P + esum + 15) / 16; }
+
 struct ChunkOut {
     std::vector<uint32_t> states;
     std::vector<std::vector<uint16_t>> words;   // per stream, decode order
+    std::vector<uint64_t> mu;                   // per stream, units of its state bits
+    uint64_t units(uint32_t st) const { return mu[st] + words[st].size(); }
     uint64_t total() const {
         uint64_t t = 0;
-        for (const auto& v : words) t += v.size();
+        for (uint32_t st = 0; st < words.size(); st++) t += units(st);
         return t;
     }
 };
 
-// A final state x in [2^16, 2^32) is stored as its length code
-// e = floor(log2 x) - 16 (a nibble per lane) and its 16 + e bits below the
-// leading one (concatenated in lane order, least significant bit first).
-inline uint32_t state_code(uint32_t x) { return 31u - (uint32_t)__builtin_clz(x) - 16u; }
-inline uint64_t code_bytes(uint32_t K) { return align_up((K + 1ull) / 2, 16); }
-inline uint64_t mant_bytes(uint32_t K, uint64_t esum) { return align_up((16ull * K + esum + 7) / 8, 16); }
-
-uint64_t state_code_sum(const ChunkOut& co) {
-    uint64_t t = 0;
-    for (uint32_t x : co.states) t += state_code(x);
-    return t;
-}
-
-// chunk payload bytes: length codes, stream word counts (S > 1) and state
-// bits, each padded to 16 bytes, then the streams, each padded to 4 bytes;
-// the whole padded to 16 bytes
-uint64_t payload_bytes(const ChunkOut& co, uint32_t K, uint32_t S) {
-    uint64_t b = code_bytes(K) + (S > 1 ? align_up(4ull * S, 16) : 0) + mant_bytes(K, state_code_sum(co));
-    for (const auto& v : co.words) b += align_up(2 * v.size(), 4);
-    return align_up(b, 16);
-}
+// chunk payload bytes: the length codes padded to 16 bytes, then the streams
+// back to back (state bits, then words), the whole padded to 16 bytes
+uint64_t payload_bytes(const ChunkOut& co, uint32_t K) { return align_up(code_bytes(K) + 2 * co.total(), 16); }
 
 struct EncRecord {
     uint32_t kind = 0;
@@ -181,8 +174,9 @@ struct EncRecord {
     EncModel em;
     uint32_t W = 0, K = 0, S = 1, n_chunks = 0;
     std::vector<ChunkOut> chunks;
-    std::vector<uint8_t> head;   // fixed part + tables + chunk index (index filled at assembly)
+    std::vector<uint8_t> head;   // fixed part, tables, chunk index and stream table (the last two filled at assembly)
     uint64_t index_off = 0;
+    uint64_t stab_off = 0;       // stream table: per chunk, the start unit of streams 1 .. S-1
 };
 
 uint32_t pick_threads(uint32_t req) {
@@ -215,7 +209,8 @@ void build_head(EncRecord& r) {
     const uint64_t ftab = align_up(route_off + md.n_sym, 4);
     const uint64_t tab_end = ftab + 256ull * md.n_tables;
     r.index_off = align_up(tab_end, 16);
-    r.head.assign(r.index_off + 16ull * r.n_chunks, 0);
+    r.stab_off = r.index_off + 16ull * r.n_chunks;
+    r.head.assign(align_up(r.stab_off + 4ull * (r.S - 1) * r.n_chunks, 16), 0);
     uint8_t* b = r.head.data();
     wr32(b + 0, r.W);
     wr32(b + 4, r.K);
@@ -311,7 +306,10 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         r.route_off = 24 + 4 * r.n_sym;
         r.ftab_off = (uint32_t)align_up(r.route_off + r.n_sym, 4);
         r.index_off = align_up(r.ftab_off + 256ull * r.n_tables, 16);
-        if (r.index_off + 16ull * r.n_chunks > r.rec_len) { set_error("record %u: chunk index out of bounds", i); return BS_E_FORMAT; }
+        if (r.index_off + 16ull * r.n_chunks + 4ull * (r.S - 1) * r.n_chunks > r.rec_len) {
+            set_error("record %u: chunk index or stream table out of bounds", i);
+            return BS_E_FORMAT;
+        }
         uint64_t sum = 0;
         int last = -1;
         for (uint32_t k = 0; k < r.n_sym; k++) {
@@ -330,26 +328,22 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
             if (fs != (1ull << r.m_f)) { set_error("record %u: fraction table %u does not sum to 2^%u", i, t + 1, r.m_f); return BS_E_FORMAT; }
         }
         const uint64_t cbytes = code_bytes(K);
-        const uint64_t counts_bytes = r.S > 1 ? align_up(4ull * r.S, 16) : 0;
+        const uint32_t P = K / r.S;
+        const uint8_t* stab = b + r.index_off + 16ull * r.n_chunks;
         for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
             const uint8_t* e = b + r.index_off + 16ull * ch;
             const uint64_t po = rd64(e);
-            const uint64_t nw = rd32(e + 8);
-            const uint64_t n_c = std::min<uint64_t>(r.W, r.n - (uint64_t)ch * r.W);
-            bool ok = po % 16 == 0 && po <= r.rec_len && nw <= 2 * n_c &&
-                      cbytes + counts_bytes <= r.rec_len - po;
-            if (ok) {
-                // the state bits and every stream's words within the record;
-                // the counts add up to the index's
+            const uint64_t total = rd32(e + 8);
+            // the payload (codes and stream area, padded to 16 bytes) within
+            // the record; the streams' starts ascend within the area and each
+            // stream holds at least its state bits
+            bool ok = po % 16 == 0 && po <= r.rec_len && align_up(cbytes + 2 * total, 16) <= r.rec_len - po;
+            for (uint32_t st = 0; ok && st < r.S; st++) {
+                const uint64_t from = st ? rd32(stab + 4ull * ((r.S - 1) * ch + st - 1)) : 0;
+                const uint64_t to = st + 1 < r.S ? rd32(stab + 4ull * ((r.S - 1) * ch + st)) : total;
                 uint64_t esum = 0;
-                for (uint32_t l = 0; l < K; l++) esum += (b[po + l / 2] >> (4 * (l % 2))) & 15u;
-                uint64_t need = cbytes + counts_bytes + mant_bytes(K, esum), total = 0;
-                for (uint32_t st = 0; st < r.S; st++) {
-                    const uint64_t ns = r.S > 1 ? rd32(b + po + cbytes + 4ull * st) : nw;
-                    total += ns;
-                    need += align_up(2 * ns, 4);
-                }
-                ok = total == nw && need <= r.rec_len - po;
+                for (uint32_t l = st * P; l < (st + 1) * P; l++) esum += (b[po + l / 2] >> (4 * (l % 2))) & 15u;
+                ok = from <= to && to <= total && state_units(P, esum) <= to - from;
             }
             if (!ok) {
                 set_error("record %u chunk %u: payload out of bounds", i, ch);
@@ -443,12 +437,16 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
             co.states.resize(r.K);
             co.words.resize(r.S);
             const uint32_t P = r.K / r.S;
+            co.mu.resize(r.S);
             for (uint32_t st = 0; st < r.S; st++) {
                 const uint64_t nw = encode_stream(r.em, (const uint16_t*)r.data + c0, n_c, r.K, st * P, (st + 1) * P,
                                                   co.states.data(), buf.data());
                 std::vector<uint16_t>& v = co.words[st];
                 v.resize(nw);
                 for (uint64_t i = 0; i < nw; i++) v[i] = buf[nw - 1 - i];
+                uint64_t esum = 0;
+                for (uint32_t l = st * P; l < (st + 1) * P; l++) esum += state_code(co.states[l]);
+                co.mu[st] = state_units(P, esum);
             }
         });
         // layout
@@ -464,9 +462,15 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
             } else {
                 len = r.head.size();
                 for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
+                    const ChunkOut& co = r.chunks[ch];
                     wr64(r.head.data() + r.index_off + 16ull * ch, len);
-                    wr32(r.head.data() + r.index_off + 16ull * ch + 8, (uint32_t)r.chunks[ch].total());
-                    len += payload_bytes(r.chunks[ch], r.K, r.S);
+                    wr32(r.head.data() + r.index_off + 16ull * ch + 8, (uint32_t)co.total());
+                    uint64_t at = 0;
+                    for (uint32_t st = 0; st < r.S; st++) {
+                        if (st) wr32(r.head.data() + r.stab_off + 4ull * ((r.S - 1) * ch + st - 1), (uint32_t)at);
+                        at += co.units(st);
+                    }
+                    len += payload_bytes(co, r.K);
                 }
             }
             rec_len[i] = len;
@@ -501,25 +505,25 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
             }
             memcpy(b, r.head.data(), r.head.size());
             const uint64_t sb = code_bytes(r.K);
-            const uint64_t cb = r.S > 1 ? align_up(4ull * r.S, 16) : 0;
+            const uint32_t P = r.K / r.S;
             for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
                 const ChunkOut& co = r.chunks[ch];
                 uint8_t* pp = b + rd64(r.head.data() + r.index_off + 16ull * ch);
-                // length codes, then the state bits (the buffer is zero-filled)
-                uint8_t* mp = pp + sb + cb;
-                uint64_t moff = 0;
-                for (uint32_t l = 0; l < r.K; l++) {
-                    const uint32_t x = co.states[l], e = state_code(x), len = 16 + e;
-                    pp[l / 2] |= (uint8_t)(e << (4 * (l % 2)));
-                    const uint64_t v = (uint64_t)(x - (1u << len)) << (moff % 8);
-                    for (uint32_t k = 0; k * 8 < (moff % 8) + len; k++) mp[moff / 8 + k] |= (uint8_t)(v >> (8 * k));
-                    moff += len;
-                }
-                uint8_t* at = mp + mant_bytes(r.K, state_code_sum(co));
+                // length codes, then each stream: its lanes' state bits, then
+                // its words (the buffer is zero-filled)
+                for (uint32_t l = 0; l < r.K; l++) pp[l / 2] |= (uint8_t)(state_code(co.states[l]) << (4 * (l % 2)));
+                uint8_t* area = pp + sb;
                 for (uint32_t st = 0; st < r.S; st++) {
-                    if (r.S > 1) wr32(pp + sb + 4 * st, (uint32_t)co.words[st].size());
-                    for (uint64_t k = 0; k < co.words[st].size(); k++) wr16(at + 2 * k, co.words[st][k]);
-                    at += align_up(2 * co.words[st].size(), 4);
+                    uint64_t moff = 0;
+                    for (uint32_t l = st * P; l < (st + 1) * P; l++) {
+                        const uint32_t x = co.states[l], len = 16 + state_code(x);
+                        const uint64_t v = (uint64_t)(x - (1u << len)) << (moff % 8);
+                        for (uint32_t k = 0; k * 8 < (moff % 8) + len; k++) area[moff / 8 + k] |= (uint8_t)(v >> (8 * k));
+                        moff += len;
+                    }
+                    uint8_t* wp = area + 2 * co.mu[st];
+                    for (uint64_t k = 0; k < co.words[st].size(); k++) wr16(wp + 2 * k, co.words[st][k]);
+                    area += 2 * co.units(st);
                 }
             }
         }

@@ -157,19 +157,6 @@ __device__ __forceinline__ void rotate_priority(uint32_t k) {
     }
 }
 
-// sum of the eight 4-bit fields of v
-__device__ __forceinline__ uint32_t nibble_sum(uint32_t v) {
-    const uint32_t t = (v & 0x0F0F0F0Fu) + ((v >> 4) & 0x0F0F0F0Fu);
-    return (t * 0x01010101u) >> 24;
-}
-
-// sum of v over the wave
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d, 64);
-    return v;
-}
-
 // inclusive prefix sum of v over the wave's lanes
 __device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
     const uint32_t lane = threadIdx.x & 63;
@@ -191,7 +178,7 @@ struct Unit {
     uint32_t x[R];                 // lane states
     Ring<ring_words(R, C)> g;
     uint32_t pos;                  // ring read position (stream words, from the 16-byte boundary)
-    uint32_t skip;                 // words of the stream before, loaded ahead of this one
+    uint32_t skip;                 // ring units before the stream's first word (what precedes it, its state bits)
     uint32_t nw;                   // this stream's words
     uint32_t ch, st, n_c;          // chunk, stream, weights in the chunk
     uint32_t unit;
@@ -199,96 +186,83 @@ struct Unit {
 
 template <int R, bool C>
 __device__ __forceinline__ void unit_open(const DecodeArgs& a, const RecDev& r, uint32_t unit, uint32_t wave, uint8_t* lds,
-                          Unit<R, C>& u) {
+                                          Unit<R, C>& u) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t ch = unit >> r.streams_log2;
     const uint32_t st = unit & ((1u << r.streams_log2) - 1);
+    const uint32_t S = 1u << r.streams_log2;
     const uint8_t* body = a.container + r.body;
+    // first read: the chunk's index entry (payload offset, 16-bit units of
+    // its stream area) and, with several streams, the stream's start and end
+    // units from the record's stream table
     const uint8_t* ent = body + r.index_off + 16ull * ch;
+    const uint32_t* stab = (const uint32_t*)(body + r.index_off + 16ull * r.n_chunks) + (uint64_t)(S - 1) * ch;
     const uint64_t poff = *(const uint64_t*)ent;
-    const uint8_t* payload = body + poff;
+    const uint32_t total = *(const uint32_t*)(ent + 8);
+    uint32_t from = st ? stab[st - 1] : 0u;
+    uint32_t to = st + 1 < S ? stab[st] : total;
+    // (all wave-uniform; readfirstlane keeps the stream position and what
+    // derives from it in scalar registers)
+    const uint8_t* payload = body + (((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(poff >> 32)) << 32) |
+                                     __builtin_amdgcn_readfirstlane((uint32_t)poff));
+    from = __builtin_amdgcn_readfirstlane(from);
+    to = __builtin_amdgcn_readfirstlane(to);
     const uint32_t K = r.K, P = r.P, LB = st * P;
     const uint64_t n_left = r.n - (uint64_t)ch * r.W;
     const uint32_t n_c = (uint32_t)(n_left < r.W ? n_left : r.W);
-    // this stream's word count and the start of its words
-    // payload: the K lanes' length codes (a nibble each), the streams' word
-    // counts (several streams), the states' bits, then each stream's words
+    // payload: the K lanes' length codes (a nibble each, padded to 16 bytes),
+    // then the streams back to back, each its lanes' state bits (padded to a
+    // 16-bit unit) and then its words.  Ring loads start at the 16-byte
+    // boundary at or below the stream and may run to the boundary at or above
+    // its end, which the payload's own padding covers; the first `skip` units
+    // loaded belong to what comes before.
     const uint32_t code_bytes = ((K + 1) / 2 + 15) & ~15u;
-    const uint32_t count_bytes = r.streams_log2 ? ((4u << r.streams_log2) + 15) & ~15u : 0u;
-    const uint32_t* codes32 = (const uint32_t*)payload;
-    // sum of all the codes and of those of the lanes below this stream
-    uint32_t esum_all = 0, esum_below = 0;
-    for (uint32_t d = lane; d < (K + 7) / 8; d += 64) {
-        const uint32_t v = codes32[d];
-        const int32_t below = (int32_t)LB - (int32_t)(8 * d);   // lanes of this dword that are below LB
-        const uint32_t vb = below >= 8 ? v : below <= 0 ? 0u : v & ((1u << (4 * below)) - 1u);
-        esum_all += nibble_sum(v);
-        esum_below += nibble_sum(vb);
-    }
-    esum_all = wave_sum(esum_all);
-    esum_below = wave_sum(esum_below);
-    const uint32_t* mant32 = (const uint32_t*)(payload + code_bytes + count_bytes);
-    // the streams' words follow the state bits, each stream padded to 4 bytes
-    uint32_t woff = code_bytes + count_bytes + (((16 * K + esum_all + 7) / 8 + 15) & ~15u);
-    uint32_t nw;
-    if (r.streams_log2 == 0) {
-        nw = *(const uint32_t*)(ent + 8);
-    } else {
-        const uint32_t* counts = (const uint32_t*)(payload + code_bytes);
-        uint32_t below = 0;
-        for (uint32_t k = lane; k < st; k += 64) below += (2 * counts[k] + 3) & ~3u;
-        woff += wave_sum(below);
-        nw = counts[st];
-    }
-    // Ring loads start at the 16-byte boundary at or below the stream (the
-    // payload starts on one) and may run to the boundary at or above its end,
-    // which the payload's own padding covers; the first `skip` words loaded
-    // belong to the stream before.
-    // (woff and nw are wave-uniform; readfirstlane keeps the stream position
-    // and everything derived from it in scalar registers)
-    woff = __builtin_amdgcn_readfirstlane(woff);
-    nw = __builtin_amdgcn_readfirstlane(nw);
-    const uint32_t w16 = woff & ~15u;
-    const uint32_t skip = (woff - w16) / 2;
-    const uint32_t wend16 = (woff + 2 * nw + 15) & ~15u;
+    const uint32_t aoff = code_bytes + 2 * from;
+    const uint32_t w16 = aoff & ~15u;
+    const uint32_t skip = (aoff - w16) / 2;
+    const uint32_t aend16 = (code_bytes + 2 * to + 15) & ~15u;
 
-    // the ring's first loads, then the lane states, so that both sets of
-    // loads are in flight together; everything is complete before the
-    // decode loop runs, so that no load issued here is still pending there.
+    // second read: the head of the stream into the ring, and the lanes'
+    // length codes
     constexpr uint32_t RW = ring_words(R, C);
     Ring<RW>& g = u.g;
     g.base = (uint16_t*)(lds + lut_lds(C) + wave * ring_bytes(R, C));
     g.words = payload + w16;
-    g.bytes = wend16 - w16;
+    g.bytes = aend16 - w16;
     uint4 first[Ring<RW>::kPieces];
     ring_issue(g, lane, first);
-    // Lane LB + l's bits start at 16 (LB + l) plus the codes of the lanes
-    // before it; a state is 1 << (16 + e) plus its 16 + e low bits.
+    uint32_t e[R];
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        const uint32_t l = 64 * q + lane, gl = LB + l;
+        e[q] = l < P ? (payload[gl >> 1] >> (4 * (gl & 1))) & 15u : 0u;
+    }
+    ring_commit(g, first);
+
+    // The state bits sit at the head of the stream, which is in the ring's
+    // first half (at most 31 bits for each of up to 512 lanes, after at most
+    // 7 skipped units): lane l's 16 + e bits start 16 l plus the codes of the
+    // lanes before it into the stream, and a state is 1 << (16 + e) plus them.
     uint32_t (&x)[R] = u.x;
-    uint32_t before = esum_below;
+    uint32_t before = 0;
 #pragma unroll
     for (int q = 0; q < R; q++) {
         const uint32_t l = 64 * q + lane;
-        const uint32_t gl = LB + l;
-        const uint32_t e = l < P ? (payload[gl >> 1] >> (4 * (gl & 1))) & 15u : 0u;
-        const uint32_t incl = wave_scan(e);
-        const uint32_t off = 16 * gl + before + (incl - e);   // < 16 K + 15 K bits
-        const uint32_t len = 16 + e;
-        const uint32_t d0 = off >> 5, sh = off & 31;
-        uint32_t lo = 0, hi = 0;
-        if (l < P) {
-            lo = mant32[d0];
-            if (sh + len > 32) hi = mant32[d0 + 1];
-        }
-        const uint32_t bits = __builtin_amdgcn_alignbit(hi, lo, sh) & ((1u << len) - 1u);
+        const uint32_t incl = wave_scan(e[q]);
+        const uint32_t bit = 16 * l + before + (incl - e[q]);
+        const uint32_t len = 16 + e[q];
+        const uint32_t wi = skip + (bit >> 4), sh = bit & 15;
+        const uint32_t w0 = g.base[wi], w1 = g.base[wi + 1], w2 = g.base[wi + 2];
+        const uint32_t bits = __builtin_amdgcn_alignbit(w2, w0 | (w1 << 16), sh) & ((1u << len) - 1u);
         x[q] = l < P ? (1u << len) | bits : kStateLow;
         before += __builtin_amdgcn_readlane(incl, 63);
     }
-    ring_commit(g, first);
+    // units of state bits: 16 P plus the codes, rounded up
+    const uint32_t mu = (16 * P + before + 15) / 16;
     __builtin_amdgcn_s_waitcnt(0);
-    u.pos = skip;
-    u.skip = skip;
-    u.nw = nw;
+    u.pos = skip + mu;
+    u.skip = skip + mu;
+    u.nw = to - from - mu;
     u.ch = ch;
     u.st = st;
     u.n_c = n_c;
