@@ -24,18 +24,31 @@
  *                route: n_sym bytes (fraction table of each s: 0 = flat,
  *                1..n_tables), padded to 4 B; n_tables x 128 x u16 q_f
  *                (each sums to 2^M_f); pad to 16 B; chunk index n_chunks x
- *                (u64 payload offset from the body start, u32 words of all
- *                streams, u32 0); payloads: K x u32 final encoder states (pad
- *                16 B); when S > 1, S x u32 word counts (pad 16 B); then
- *                each stream's 16-bit words in decode order (pad 16 B).
+ *                (u64 payload offset from the body start, u32 16-bit units
+ *                of the chunk's stream area, u32 0); when S > 1 the stream
+ *                table n_chunks x (S - 1) x u32: the start unit of streams
+ *                1 .. S-1 in the chunk's stream area; pad to 16 B; payloads,
+ *                each 16-B aligned: the K lanes' length codes (a nibble per
+ *                lane, lane l in the low nibble of byte l/2 when l is even;
+ *                pad 16 B), then the stream area: the S streams back to back,
+ *                each the state bits of its P lanes (below), padded to a
+ *                16-bit unit, followed by its 16-bit words in decode order;
+ *                the payload is padded to 16 B.
+ *   Final lane states: a state x in [2^16, 2^32) is its length code
+ *   e = floor(log2 x) - 16 and its 16 + e bits below the leading one, the
+ *   stream's lanes' bits concatenated in lane order, least significant first.
  *   Coder: 32-bit state in [2^16, 2^32), 16-bit renormalisation words.  In a
  *   chunk, weight j belongs to lane (j/8) mod K, macro-step (j/8)/K; each lane
  *   decodes, per weight, s with the s-table then f with the table route[s];
  *   the K lanes form S streams of P = K/S consecutive lanes, each with its
  *   own word sequence; within a stream, lanes take turns in ascending order
  *   in each (macro-step, position, field) sub-step, consuming its words in
- *   that order.  Fraction tables with id 0 are flat (q = 2^(M_f - 7) for
- *   every f).
+ *   that order.  A lane's last group holds c = min(8, weights left) weights;
+ *   the last m = min(4, c) of them carry only s in the stream: their
+ *   fractions are the low 7m bits of the lane's start state (first of them
+ *   lowest) under a leading one at bit max(16, 7m), so the decoder reads them
+ *   off the state it ends in.  A lane without weights starts and ends at
+ *   2^16.  Fraction tables with id 0 are flat (q = 2^(M_f - 7) for every f).
  *
  * Conventions:
  *   - Every function returns a bs_status (0 = BS_OK); none throws or aborts.
@@ -73,10 +86,10 @@ typedef enum {
 enum { BS_KIND_BF16 = 1, BS_KIND_RAW = 2 };
 
 /* Encoder parameters.  chunk_weights W must be a multiple of 8*lanes; lanes K
- * is a power of two: 1..64, 128, 256 or 512; stream_lanes P (0 = K) is a
- * power of two <= K: each chunk's lanes are split into word streams of P
- * lanes (fewer when a small record gets fewer lanes), which the decoder runs
- * on separate wavefronts; 9 <= m_s <= 12; 8 <= m_f <= 10 (the decoder multiplies
+ * is a power of two: 1..64, 128, 256, 512, 1024 or 2048; stream_lanes P
+ * (0 = K) is a power of two <= K and <= 512: each chunk's lanes are split into
+ * word streams of P lanes (fewer when a small record gets fewer lanes), which
+ * the decoder runs on separate wavefronts; 9 <= m_s <= 12; 8 <= m_f <= 10 (the decoder multiplies
  * x >> m in 24 bits, so m >= 8); max_tables <= 6;
  * threads = host encoder threads (0 = hardware count). */
 typedef struct {

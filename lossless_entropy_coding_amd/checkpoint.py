@@ -24,9 +24,9 @@ from . import codec, synth, workloads
 class CheckpointJob:
     """One Plan per layer container; decode() decodes every layer in order."""
 
-    def __init__(self, layers: int = 84, chunk_weights: int = 65536, lanes: int = 256, log=print,
+    def __init__(self, layers: int = 84, chunk_weights: int = 65536, lanes: int = 512, log=print,
                  device: str = "cuda", keep_host_first: bool = True, m_s: int = 12, m_f: int = 10,
-                 stream_lanes: int = 0):
+                 stream_lanes: int = 256):
         layout = synth.cfg5_layout(layers=layers)
         self.name = "cfg5_checkpoint_%dlayers_%dtensors" % (layers, len(layout))
         self.chunk_weights, self.lanes, self.stream_lanes = chunk_weights, lanes, stream_lanes or lanes
