@@ -159,6 +159,32 @@ def test_validation_errors():
     assert e.value.rc == L.BS_E_FORMAT
 
 
+def test_stream_table_validation():
+    """The record's stream table must give ascending starts inside the chunk's
+    stream area, each stream at least as long as its lanes' state bits."""
+    rng = np.random.default_rng(7)
+    w = _words(rng.standard_normal(4096 * 3) * 0.02)
+    c = codec.encode([codec.bf16(w)], codec.params(chunk_weights=4096, lanes=64, stream_lanes=16))
+    assert c == O.encode([O.bf16(w)], W=4096, K=64, P=16)
+    codec.container_info(c)
+    ri = codec.record_info(c, 0)
+    body = ri.rec_offset
+    n_sym = struct.unpack_from("<I", c, body + 16)[0]
+    nt = c[body + 14]
+    idx = body + ((((24 + 5 * n_sym + 3) // 4) * 4 + 256 * nt + 15) // 16) * 16
+    n_chunks = struct.unpack_from("<I", c, body + 8)[0]
+    stab = idx + 16 * n_chunks            # chunk 0: starts of streams 1, 2, 3
+    s1, s2, s3 = struct.unpack_from("<III", c, stab)
+    total = struct.unpack_from("<I", c, idx + 8)[0]
+    assert 0 < s1 < s2 < s3 < total
+    for vals in [(s2 + 1, s2, s3), (s1, s2, total + 1), (1, s2, s3)]:
+        bad = bytearray(c)
+        struct.pack_into("<III", bad, stab, *vals)
+        with pytest.raises(L.BSError) as e:
+            codec.container_info(bytes(bad))
+        assert e.value.rc == L.BS_E_FORMAT, vals
+
+
 def test_bad_params_rejected():
     w = np.zeros(100, np.uint16)
     for kw in [dict(lanes=3), dict(lanes=96), dict(lanes=1024, chunk_weights=1 << 20), dict(lanes=64, stream_lanes=128),
