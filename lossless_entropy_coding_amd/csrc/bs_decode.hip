@@ -43,7 +43,8 @@ __device__ __forceinline__ uint4 load_piece(__amdgpu_buffer_rsrc_t rs, uint32_t 
 }
 
 // Per-wave ring of stream words in LDS: RW words (1024 to 4096, by lanes per
-// thread and layout) plus a 64-word copy of its head after its end, so that a
+// thread and layout; topped up every RW / (256 R) positions) plus a 64-word
+// copy of its head after its end, so that a
 // refill of up to 64 consecutive words never wraps.  Words are refilled RW/2
 // at a time (RW/1024 16-B pieces per lane), loaded one refill ahead.
 template <uint32_t RW>
@@ -302,7 +303,7 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
         uint32_t o[R][4];
 #pragma unroll
         for (int p = 0; p < 8; p++) {
-            ring_top_up(g, pos);
+            if (p % top_up_every(R, C) == 0) ring_top_up(g, pos);
             uint2 se[R];
 #pragma unroll
             for (int q = 0; q < R; q++) se[q] = step_s(x[q], md);
@@ -362,7 +363,7 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
         }
 #pragma unroll 1
         for (int p = 0; p < 8; p++) {
-            ring_top_up(g, pos);
+            if (p % top_up_every(R, C) == 0) ring_top_up(g, pos);
             bool act_s[R], act_f[R];
             uint2 se[R];
 #pragma unroll
@@ -520,9 +521,7 @@ template <int G, bool C>
 __global__ __launch_bounds__(G == 8 ? 512 : 1024) void decode_kernel(const DecodeArgs a) {
     // static allocation: the LDS base is a compile-time constant, so table and
     // ring addresses fold into the instructions' offsets
-    // rings sized for the widest lane count the instance runs (a narrower
-    // record's waves use smaller rings at smaller offsets)
-    constexpr uint32_t RMAX = G == 8 ? 8 : (G == 1 ? 1 : G == 2 || G == 0 ? 2 : 4);
+    constexpr uint32_t RMAX = G == 8 ? 8 : 1;   // ring size: one for 1, 2 and 4 lanes per thread, one for 8
     __shared__ __align__(16) uint8_t lds[lut_lds(C) + max_waves(RMAX) * ring_bytes(RMAX, C)];
     __shared__ uint32_t pick[2];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

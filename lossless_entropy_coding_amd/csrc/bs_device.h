@@ -13,9 +13,8 @@ constexpr uint32_t kMaxSyms = 256;          // occupied (sign, exponent) symbols
 //   full    (M_s <= 12, M_f <= 10): s lookup table, 2^M_s entries of 8 B, at 0
 //           (32 KiB); fraction lookup tables in pages of 8 KiB from 32 KiB
 //           (page t = table t, t = 0 flat, 1..6 coded; 2^M_f entries of 8 B);
-//           then one stream ring per wave, 1024 words for one lane per
-//           thread, 2048 for two or four, 4096 for eight.  One 16-wave
-//           workgroup fills a CU's LDS.
+//           then one stream ring per wave, 2048 words (4096 for eight lanes
+//           per thread).  One 16-wave workgroup fills a CU's LDS.
 //   compact (M_s <= 11, M_f <= 9): the s table in 16 KiB, pages of 4 KiB from
 //           16 KiB, rings of 1024 words: 79,872 B, so that two 16-wave
 //           workgroups share a CU.
@@ -26,19 +25,18 @@ constexpr uint32_t fpage_bytes(bool compact) { return compact ? 4096u : 8192u; }
 constexpr uint32_t lut_lds(bool compact) { return slut_bytes(compact) + (kMaxTables + 1) * fpage_bytes(compact); }
 
 // ring size (16-bit words, a power of two), ring bytes and the workgroup cap
-// for R lanes per thread.  A position consumes at most 2 * 64 * R words and
-// the ring is topped up to at least half full before each position, so it
-// needs at least 256 * R words.  The smallest ring for one lane per thread
-// keeps the loads issued before a wave starts decoding small (a workload
-// whose waves all start together reads less before any of them decodes).
-constexpr uint32_t ring_words(uint32_t R, bool compact) {
-    return compact ? 1024u : (R >= 8 ? 4096u : R >= 2 ? 2048u : 1024u);
-}
+// for R lanes per thread.  A position consumes at most 2 * 64 * R words, and
+// the ring is topped up to at least half full every top_up_every(R) positions,
+// so it needs at least 256 * R words times that.  Checking less often than
+// every position keeps the top-up (which waits for its prefetch) away from
+// the positions right after an output store: on this hardware a wait for a
+// load also waits for the stores issued after it.
+constexpr uint32_t ring_words(uint32_t R, bool compact) { return compact ? 1024u : (R >= 8 ? 4096u : 2048u); }
+constexpr uint32_t top_up_every(uint32_t R, bool compact) { return ring_words(R, compact) / (256u * R); }
 constexpr uint32_t ring_bytes(uint32_t R, bool compact) { return (ring_words(R, compact) + kRingMirror) * 2u; }
 constexpr uint32_t max_waves(uint32_t R) { return R >= 8 ? 8u : 16u; }
-static_assert(ring_words(4, true) >= 256 * 4 && ring_words(1, false) >= 256 && ring_words(2, false) >= 256 * 2 &&
-              ring_words(4, false) >= 256 * 4 && ring_words(8, false) >= 256 * 8,
-              "ring too small for one position");
+static_assert(top_up_every(4, true) >= 1 && top_up_every(4, false) >= 1 && top_up_every(8, false) >= 1 &&
+              top_up_every(1, false) == 8 && top_up_every(1, true) == 4, "ring too small for one position");
 static_assert(lut_lds(true) + 16 * ring_bytes(4, true) + 8 <= 81920, "compact layout must fit twice in 160 KiB");
 static_assert(lut_lds(false) + 16 * ring_bytes(4, false) + 8 <= 163840, "full layout must fit in 160 KiB");
 static_assert(lut_lds(false) + 8 * ring_bytes(8, false) + 8 <= 163840, "full layout must fit in 160 KiB");
