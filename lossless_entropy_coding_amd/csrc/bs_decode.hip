@@ -290,7 +290,14 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
     // the lane's last group (whose last weights keep their fractions in the
     // lane's start state, not in the stream): all full macro-steps but the last
     const uint32_t T_full = (P % 64 == 0) ? n_c / (8 * K) : 0;
-    const uint32_t T_main = T_full ? T_full - 1 : 0;
+    // A whole chunk of full waves: every lane's last group is the last
+    // macro-step and holds 8 weights, so positions 4..7 of that macro-step
+    // carry only s for every lane, and the main loop runs it too (for one
+    // lane per thread, whose chunks are a few macro-steps long; the wider
+    // instances keep a main loop without the extra case, which measured
+    // faster for them).
+    const bool whole = R == 1 && T_full != 0 && T_full == T;
+    const uint32_t T_main = whole ? T_full : (T_full ? T_full - 1 : 0);
 
     bool all_on[R];
 #pragma unroll
@@ -300,6 +307,7 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
     const uint32_t prio0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);   // wave / 4: rank on its SIMD
     for (uint32_t t = 0; t < T_main; t++) {
         if (fair) rotate_priority(prio0 + t);
+        const bool last = whole && t + 1 == T_main;   // uniform
         uint32_t o[R][4];
 #pragma unroll
         for (int p = 0; p < 8; p++) {
@@ -309,9 +317,14 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
             for (int q = 0; q < R; q++) se[q] = step_s(x[q], md);
             refill_all<R, RW>(x, all_on, g, pos);
             uint32_t wv[R];
+            if (p >= 4 && last) {
 #pragma unroll
-            for (int q = 0; q < R; q++) wv[q] = step_f(x[q], se[q], md);
-            refill_all<R, RW>(x, all_on, g, pos);
+                for (int q = 0; q < R; q++) wv[q] = se[q].y << 7;   // s alone; the fraction is in the final state
+            } else {
+#pragma unroll
+                for (int q = 0; q < R; q++) wv[q] = step_f(x[q], se[q], md);
+                refill_all<R, RW>(x, all_on, g, pos);
+            }
 #pragma unroll
             for (int q = 0; q < R; q++) {
                 if (p & 1) o[q][p >> 1] = __builtin_amdgcn_perm(wv[q], o[q][p >> 1], 0x05040100u);
@@ -324,9 +337,22 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
         }
 #pragma unroll
         for (int q = 0; q < R; q++) {
+            if (last) {
+                // every lane is back at its start state 2^28 plus four fractions
+                o[q][2] |= (x[q] & 127u) | ((x[q] >> 7) & 127u) << 16;
+                o[q][3] |= ((x[q] >> 14) & 127u) | ((x[q] >> 21) & 127u) << 16;
+            }
             uint4* op = (uint4*)out + (uint64_t)t * K + LB + 64 * q + lane;
             *op = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
         }
+    }
+    if (whole) {
+        bool bad = false;
+#pragma unroll
+        for (int q = 0; q < R; q++) bad |= (x[q] >> 28) != 1u;
+        const uint64_t badm = __builtin_amdgcn_ballot_w64(bad);
+        if (lane == 0) a.status[r.status_base + unit] = (badm ? 1u : 0u) | (pos - skip != nw ? 2u : 0u);
+        return;
     }
 
     // remaining macro-steps (a lane's last group, partial groups, or fewer
