@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--stream-lanes", type=int, default=None, help="override the lanes per word stream")
     ap.add_argument("--m-s", type=int, default=None, help="override the (sign, exponent) table precision")
     ap.add_argument("--m-f", type=int, default=None, help="override the fraction table precision")
+    ap.add_argument("--gemv", action="store_true",
+                    help="time the fused decode and matrix-vector product (bs_gemv_async) of the 4096x4096 "
+                         "workload against decode-then-GEMV and a GEMV on the uncompressed matrix")
     return ap.parse_args()
 
 
@@ -143,6 +146,63 @@ def cpu_baseline(job, seconds: float):
             "seconds": round(t1 + tT, 2)}
 
 
+def gemv_bench(a):
+    """Fused decode and GEMV on the 4096x4096 workload (y = W x, x BF16, y fp32)
+    against (1) bs_decode_async then torch.mv on the decoded BF16 matrix and
+    (2) torch.mv on the uncompressed BF16 matrix resident in HBM."""
+    import torch
+    from lossless_entropy_coding_amd import workloads
+    enc = workloads.encode_config(a.config, device="cpu", keep_reference=False, keep_device_reference=True,
+                                  lanes=a.lanes, chunk_weights=a.chunk_weights, stream_lanes=a.stream_lanes,
+                                  m_s=a.m_s, m_f=a.m_f)
+    assert a.config == "2", "the fused product is timed on the 4096x4096 workload"
+    rows = cols = 4096
+    job = workloads.DecodeJob(enc)
+    W = job.ref[: 2 * rows * cols].view(torch.bfloat16).reshape(rows, cols)
+    g = torch.Generator(device="cpu").manual_seed(1)
+    x = torch.randn(cols, generator=g).to(torch.bfloat16).cuda()
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fused = job.plan.bound_gemv(y, x.view(torch.int16), rows, cols, stream=stream)
+    dec = job.fast_decoder(stream)
+    Wd = job.out[: 2 * rows * cols].view(torch.bfloat16).reshape(rows, cols)
+
+    def two_step():
+        dec()
+        torch.mv(Wd, x)
+
+    def plain():
+        torch.mv(W, x)
+
+    def timed(fn):
+        for _ in range(a.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(a.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / a.steps     # us per call
+
+    t_fused, t_two, t_plain = timed(fused), timed(two_step), timed(plain)
+    fused()
+    torch.cuda.synchronize()
+    ref = (W.float() @ x.float())
+    err = float((y - ref).abs().max() / ref.abs().max())
+    comp = int(job.read_bytes)
+    line = {"metric": "fused decode + GEMV (4096x4096 BF16 weights, batch 1)", "unit": "us per product",
+            "fused_us": round(t_fused, 2), "decode_then_gemv_us": round(t_two, 2), "plain_bf16_gemv_us": round(t_plain, 2),
+            "fused_weight_bytes_read": comp, "plain_weight_bytes_read": 2 * rows * cols,
+            "fused_GB_s_of_compressed_weights": round(comp / t_fused / 1e3, 1),
+            "plain_GB_s_of_bf16_weights": round(2 * rows * cols / t_plain / 1e3, 1),
+            "max_rel_diff_vs_fp32_product": err, "steps": a.steps, "data": "synthetic",
+            "config": {"workload": job.name, "lanes": job.lanes, "stream_lanes": job.stream_lanes,
+                       "chunk_weights": job.chunk_weights}}
+    print(json.dumps(line))
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -165,6 +225,9 @@ def main():
                           "copies": 5}))
         return
     L.lib()   # fails loudly if the HIP library is missing
+    if a.gemv:
+        gemv_bench(a)
+        return
     dev = "cuda"
     t0 = time.time()
     if a.config == "5":

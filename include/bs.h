@@ -227,6 +227,22 @@ void bs_plan_destroy(bs_plan* plan);
 bs_status bs_decode_async(const bs_plan* plan, uint32_t first, uint32_t count, void* d_out, uint64_t out_capacity,
                           uint32_t* d_status, void* stream);
 
+/* Fused decode and matrix-vector product [Qwen3.8-27B-BF16-NVLC-Lossless
+ * card, runtime paragraphs: the compressed-only runtime decodes weights where
+ * they are used and keeps no decoded copy]: y[r] = sum over c of W[r, c] x[c]
+ * for BF16 record `record` read as a row-major rows x cols matrix
+ * (rows * cols = its weight count; cols a multiple of 8 and at least 512).
+ * The weights are decoded in registers and never written out.  d_x: cols
+ * BF16 words, 16-B aligned; d_y: rows floats, overwritten (a fill kernel
+ * clears it first, then the products are added in fp32, in an order that
+ * varies from run to run, so the result matches the exact sum within the
+ * usual fp32 summation bound, not bit for bit).  d_status as for
+ * bs_decode_async (only the record's entries are written).  Records in the
+ * compact table layout or with more than 4 lanes per thread are rejected
+ * (BS_E_INVAL).  Enqueued on `stream`; nothing is allocated. */
+bs_status bs_gemv_async(const bs_plan* plan, uint32_t record, uint64_t rows, uint64_t cols, const void* d_x, float* d_y,
+                        uint32_t* d_status, void* stream);
+
 /* Bytes needed to decode records [first, first + count). */
 uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count);
 

@@ -82,6 +82,8 @@ SIGNATURES = {
     "bs_decode_async": (C.c_int, [C.c_void_p, C.c_uint32, C.c_uint32, C.c_void_p, C.c_uint64, C.c_void_p,
                                   C.c_void_p]),
     "bs_plan_out_bytes": (C.c_uint64, [C.c_void_p, C.c_uint32, C.c_uint32]),
+    "bs_gemv_async": (C.c_int, [C.c_void_p, C.c_uint32, C.c_uint64, C.c_uint64, C.c_void_p, C.c_void_p, C.c_void_p,
+                                C.c_void_p]),
     "bs_plan_waves_per_block": (C.c_uint32, [C.c_void_p]),
     "bs_verify": (C.c_int, [C.c_void_p, C.c_uint32, C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_uint32,
                             C.c_void_p, C.POINTER(Report)]),

@@ -202,6 +202,35 @@ class Plan:
         self.decode_into(out, first, count, stream)
         return out
 
+    def gemv_into(self, y: torch.Tensor, x: torch.Tensor, rows: int, cols: int, record: int = 0, stream=None) -> None:
+        """Enqueue y = W x for BF16 record `record` read as a rows x cols matrix,
+        decoding W on the fly (bs_gemv_async): x a bfloat16 (or int16) tensor of
+        cols elements, y a float32 tensor of rows elements (overwritten)."""
+        assert x.dtype in (torch.bfloat16, torch.int16) and x.numel() == cols and x.is_contiguous()
+        assert y.dtype == torch.float32 and y.numel() == rows and y.is_contiguous()
+        rc = L.lib().bs_gemv_async(self.handle, record, rows, cols, C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()),
+                                   C.c_void_p(self.status.data_ptr()), C.c_void_p(_stream_handle(stream)))
+        L.check(rc, "bs_gemv_async")
+
+    def bound_gemv(self, y: torch.Tensor, x: torch.Tensor, rows: int, cols: int, record: int = 0, stream=None):
+        """gemv_into with its ctypes arguments converted once (for timing loops)."""
+        f = L.lib().bs_gemv_async
+        args = (self.handle, C.c_uint32(record), C.c_uint64(rows), C.c_uint64(cols), C.c_void_p(x.data_ptr()),
+                C.c_void_p(y.data_ptr()), C.c_void_p(self.status.data_ptr()), C.c_void_p(_stream_handle(stream)))
+        keep = (x, y, self.status)
+
+        def run():
+            rc = f(*args)
+            if rc:
+                L.check(rc, "bs_gemv_async")
+            return keep
+        return run
+
+    def gemv(self, x: torch.Tensor, rows: int, cols: int, record: int = 0, stream=None) -> torch.Tensor:
+        y = torch.empty(rows, dtype=torch.float32, device=self.dev.device)
+        self.gemv_into(y, x, rows, cols, record, stream)
+        return y
+
     def verify(self, out: torch.Tensor, ref: torch.Tensor | None = None, flags: int = L.VERIFY_STATUS,
                first: int = 0, count: int | None = None, stream=None):
         """Returns (status code, report dict); synchronises the stream."""

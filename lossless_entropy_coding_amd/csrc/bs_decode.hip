@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "bs_device.h"
 
 using namespace bsd;
@@ -270,7 +272,47 @@ __device__ __forceinline__ void unit_open(const DecodeArgs& a, const RecDev& r, 
     u.unit = unit;
 }
 
-template <int R, bool C>
+// The fused product's epilogue for one group of 8 weights per lane (cnt of
+// them present): the lane's weights are record elements e0 + 8 lane .. + 7,
+// which lie in one matrix row; the wave's 512 elements span at most two rows
+// (gcols >= 512).  Each lane multiplies its weights by the matching x, the
+// wave sums the products per row, and lane 0 adds the sums into y.
+__device__ __forceinline__ uint32_t bf16_lo(uint32_t v) { return v << 16; }
+__device__ __forceinline__ uint32_t bf16_hi(uint32_t v) { return v & 0xFFFF0000u; }
+
+__device__ __forceinline__ void gemv_group(const DecodeArgs& a, const uint32_t (&o)[4], uint32_t cnt, uint64_t e0,
+                                           uint32_t lane) {
+    const uint64_t cols = a.gcols;
+    const uint64_t row0 = e0 / cols;                 // uniform
+    const uint32_t c0 = (uint32_t)(e0 - row0 * cols);
+    const uint32_t c = c0 + 8 * lane;
+    const bool wrap = c >= cols;
+    const uint32_t col = wrap ? c - (uint32_t)cols : c;
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u xv = *(const v4u*)(a.gx + col);
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const uint32_t wk = k & 1 ? bf16_hi(o[k >> 1]) : bf16_lo(o[k >> 1]);
+        const uint32_t xk = k & 1 ? bf16_hi(xw[k >> 1]) : bf16_lo(xw[k >> 1]);
+        if ((uint32_t)k < cnt) sum = __builtin_fmaf(__uint_as_float(wk), __uint_as_float(xk), sum);
+    }
+    float s0 = wrap ? 0.f : sum, s1 = wrap ? sum : 0.f;
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+        s0 += __shfl_xor(s0, d, 64);
+        s1 += __shfl_xor(s1, d, 64);
+    }
+    const uint64_t wrapped = __builtin_amdgcn_ballot_w64(wrap && cnt > 0);
+    const uint64_t here = __builtin_amdgcn_ballot_w64(!wrap && cnt > 0);
+    if (lane == 0) {
+        if (here) __hip_atomic_fetch_add(a.gy + row0, s0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (wrapped) __hip_atomic_fetch_add(a.gy + row0 + 1, s1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <int R, bool C, bool V>
 __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r, uint8_t* lds, Unit<R, C>& u,
                                             bool fair) {
     const uint32_t lane = threadIdx.x & 63;
@@ -342,8 +384,12 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
                 o[q][2] |= (x[q] & 127u) | ((x[q] >> 7) & 127u) << 16;
                 o[q][3] |= ((x[q] >> 14) & 127u) | ((x[q] >> 21) & 127u) << 16;
             }
-            uint4* op = (uint4*)out + (uint64_t)t * K + LB + 64 * q + lane;
-            *op = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
+            if (V) {
+                gemv_group(a, o[q], 8u, (uint64_t)ch * r.W + 8ull * ((uint64_t)t * K + LB + 64 * q), lane);
+            } else {
+                uint4* op = (uint4*)out + (uint64_t)t * K + LB + 64 * q + lane;
+                *op = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
+            }
         }
     }
     if (whole) {
@@ -427,7 +473,9 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
                 }
             }
             const uint64_t g16 = (uint64_t)t * K + LB + 64 * q + lane;
-            if (cnt[q] == 8) {
+            if (V) {
+                gemv_group(a, o[q], (uint32_t)cnt[q], (uint64_t)ch * r.W + 8ull * (g16 - lane), lane);
+            } else if (cnt[q] == 8) {
                 ((uint4*)out)[g16] = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
             } else if (cnt[q] > 0) {
                 uint16_t* o16 = (uint16_t*)out + 8 * g16;
@@ -467,7 +515,7 @@ __device__ __forceinline__ uint32_t stage_slot(uint32_t i, uint32_t ns16, uint32
 
 // The units [u0, u1) of one record, taken by the workgroup's waves in turn.
 // Every wave takes part in the staging and the barrier after it.
-template <int R, bool C>
+template <int R, bool C, bool V>
 __device__ __forceinline__ void run_units(const DecodeArgs& a, const RecDev& r, uint32_t u0, uint32_t u1,
                                           uint32_t wave, uint8_t* lds) {
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));   // plain vector: stays in registers
@@ -507,25 +555,25 @@ __device__ __forceinline__ void run_units(const DecodeArgs& a, const RecDev& r, 
     __syncthreads();
     for (; u < u1; u += a.waves) {
         if (u != u0 + wave) unit_open<R, C>(a, r, u, wave, lds, un);
-        unit_decode<R, C>(a, r, lds, un, u1 - u0 <= a.waves);
+        unit_decode<R, C, V>(a, r, lds, un, u1 - u0 <= a.waves);
     }
 }
 
 // The run of units starting at u0 of record r, with the lane width that the
 // kernel instance G fixes or, for a mixed instance, the record's own.
-template <int G, bool C>
+template <int G, bool C, bool V>
 __device__ __forceinline__ void run_record(const DecodeArgs& a, const RecDev& r, uint32_t u0, uint32_t wave,
                                            uint8_t* lds) {
     const uint32_t u1 = min(r.n_chunks << r.streams_log2, u0 + a.run);
     if (G == 1 || G == 2 || G == 4 || G == 8) {
         constexpr int R = (G == 1 || G == 2 || G == 4 || G == 8) ? G : 1;
-        run_units<R, C>(a, r, u0, u1, wave, lds);
+        run_units<R, C, V>(a, r, u0, u1, wave, lds);
     } else if (r.lanes_per_thread == 1) {
-        run_units<1, C>(a, r, u0, u1, wave, lds);
+        run_units<1, C, V>(a, r, u0, u1, wave, lds);
     } else if (G == 0 || r.lanes_per_thread == 2) {
-        run_units<2, C>(a, r, u0, u1, wave, lds);
+        run_units<2, C, V>(a, r, u0, u1, wave, lds);
     } else {
-        run_units<4, C>(a, r, u0, u1, wave, lds);
+        run_units<4, C, V>(a, r, u0, u1, wave, lds);
     }
 }
 
@@ -543,7 +591,7 @@ __device__ __forceinline__ void run_record(const DecodeArgs& a, const RecDev& r,
 // narrower mix keeps the register count low enough for two workgroups per CU
 // in the compact layout).  Records with eight lanes per thread (G = 8:
 // 8 waves, 4096-word rings) have a launch of their own.
-template <int G, bool C>
+template <int G, bool C, bool V = false>
 __global__ __launch_bounds__(G == 8 ? 512 : 1024) void decode_kernel(const DecodeArgs a) {
     // static allocation: the LDS base is a compile-time constant, so table and
     // ring addresses fold into the instructions' offsets
@@ -556,7 +604,7 @@ __global__ __launch_bounds__(G == 8 ? 512 : 1024) void decode_kernel(const Decod
         // one record, passed by value: no lookup before the tables
         const uint32_t u0 = b * a.run;
         if (u0 >= (a.one.n_chunks << a.one.streams_log2)) return;   // uniform over the workgroup
-        run_record<G, C>(a, a.one, u0, wave, lds);
+        run_record<G, C, V>(a, a.one, u0, wave, lds);
         return;
     }
     if (wave == 0) {
@@ -588,7 +636,13 @@ __global__ __launch_bounds__(G == 8 ? 512 : 1024) void decode_kernel(const Decod
     const uint32_t e = __builtin_amdgcn_readfirstlane(pick[0]);
     if (e == UINT32_MAX) return;   // no run for this workgroup (launch larger than the runs)
     const RecDev r = a.recs[a.cls.recs[e]];
-    run_record<G, C>(a, r, __builtin_amdgcn_readfirstlane(pick[1]) * a.run, wave, lds);
+    run_record<G, C, V>(a, r, __builtin_amdgcn_readfirstlane(pick[1]) * a.run, wave, lds);
+}
+
+// y = 0 before a fused product (a plain fill kernel, so that the enqueued
+// work stays capturable)
+__global__ void zero_f32_kernel(float* y, uint64_t n) {
+    for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += 256ull * gridDim.x) y[i] = 0.f;
 }
 
 }  // namespace
@@ -619,6 +673,24 @@ int bsk_decode(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, bool
             case 8: hipLaunchKernelGGL((decode_kernel<8, false>), grid, block, 0, st, *args); break;
             default: return (int)hipErrorInvalidValue;
         }
+    }
+    return (int)hipGetLastError();
+}
+
+int bsk_gemv(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    if (rows) {
+        hipLaunchKernelGGL(zero_f32_kernel, dim3((uint32_t)std::min<uint64_t>((rows + 255) / 256, 65535)), dim3(256), 0,
+                           st, args->gy, rows);
+    }
+    if (n_groups == 0) return (int)hipGetLastError();
+    const dim3 grid(n_groups), block(64 * args->waves);
+    if (args->waves == 0 || args->waves > max_waves(1)) return (int)hipErrorInvalidValue;
+    switch (variant) {
+        case 1: hipLaunchKernelGGL((decode_kernel<1, false, true>), grid, block, 0, st, *args); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<2, false, true>), grid, block, 0, st, *args); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<4, false, true>), grid, block, 0, st, *args); break;
+        default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
 }

@@ -95,6 +95,12 @@ struct DecodeArgs {
     uint32_t run;           // units per workgroup (a run inside one record)
     uint32_t waves;         // waves per workgroup (rings allocated)
     RecDev one;             // the record itself when the launch has one (i1 = i0 + 1)
+    // fused product with a vector (the kernel instances with V set): the
+    // record is a row-major matrix of gcols columns; y[r] += sum over c of
+    // W[r, c] x[c], accumulated in fp32 (y zeroed before the launch)
+    const uint16_t* gx;     // x: gcols BF16 words, 16-B aligned
+    float* gy;              // y: n / gcols floats
+    uint64_t gcols;         // a multiple of 8, at least 512
 };
 
 }  // namespace bsd
@@ -110,6 +116,8 @@ int bsk_build_luts(const uint8_t* d_container, const bsd::RecDev* d_recs, uint32
 // thread; variant 0: a mix of 1 and 2; variant 3: a mix of 1, 2 and 4.
 // compact: the records use the compact LDS layout (not with variant 8).
 int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, bool compact, void* stream);
+// the fused matrix-vector product of one record (full layout, variant 1, 2 or 4), y zeroed first
+int bsk_gemv(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream);
 int bsk_raw_copy(const uint8_t* d_container, const bsd::RawDev* d_raw, uint32_t n_raw, uint8_t* d_out,
                  uint64_t out_base, void* stream);
 int bsk_compare(const uint8_t* a, const uint8_t* b, uint64_t n, unsigned long long* d_result /*2*/, void* stream);

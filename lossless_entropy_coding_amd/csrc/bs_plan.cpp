@@ -304,6 +304,49 @@ bs_status bs_decode_async(const bs_plan* p, uint32_t first, uint32_t count, void
     return BS_OK;
 }
 
+bs_status bs_gemv_async(const bs_plan* p, uint32_t record, uint64_t rows, uint64_t cols, const void* d_x, float* d_y,
+                        uint32_t* d_status, void* stream) {
+    if (!p || !d_x || !d_y || (!d_status && p->c.n_streams)) { set_error("NULL argument"); return BS_E_INVAL; }
+    if (record >= p->c.n_records) { set_error("record %u out of range", record); return BS_E_INVAL; }
+    const Record& rec = p->c.recs[record];
+    if (rec.kind != BS_KIND_BF16) { set_error("record %u is not a BF16 record", record); return BS_E_INVAL; }
+    if (cols < 512 || cols % 8 || rows == 0 || rows * cols != rec.n || rec.n / cols != rows) {
+        set_error("record %u holds %llu weights: not a %llu x %llu matrix with a multiple of 8 (at least 512) columns",
+                  record, (unsigned long long)rec.n, (unsigned long long)rows, (unsigned long long)cols);
+        return BS_E_INVAL;
+    }
+    if (((uintptr_t)d_x & 15) || ((uintptr_t)d_y & 3)) { set_error("x must be 16-byte aligned, y 4-byte aligned"); return BS_E_INVAL; }
+    const int k = (int)p->rclass[record];
+    if (bs_plan::kCompact[k] || bs_plan::kMaxR[k] > 4) {
+        set_error("the fused product runs on records in the full table layout with at most 4 lanes per thread");
+        return BS_E_INVAL;
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != p->device) { set_error("plan belongs to device %d", p->device); return BS_E_INVAL; }
+    const uint32_t e = p->cls_pos[record];
+    bsd::DecodeArgs a{};
+    a.container = p->d_container;
+    a.recs = p->d_recs;
+    a.cls.recs = p->d_cls_recs[k];
+    a.cls.start = p->d_cls_start[k];
+    a.luts = p->d_luts;
+    a.out = nullptr;
+    a.status = d_status;
+    a.out_base = rec.out_offset;
+    a.i0 = e;
+    a.i1 = e + 1;
+    a.one = p->h_recs[p->cls_recs[k][e]];
+    a.gx = (const uint16_t*)d_x;
+    a.gy = d_y;
+    a.gcols = cols;
+    uint32_t groups;
+    launch_shape(p, k, e, e + 1, a.waves, a.run, groups);
+    if (p->cls_start[k][e + 1] == p->cls_start[k][e]) groups = 0;
+    const int err = bsk_gemv(&a, groups, p->cls_R[k][e], rows, stream);
+    if (err) return hip_err((hipError_t)err, "fused product launch");
+    return BS_OK;
+}
+
 bs_status bs_verify(const bs_plan* p, uint32_t first, uint32_t count, const void* d_out, const void* d_ref,
                     const uint32_t* d_status, uint32_t flags, void* stream, bs_report* rep) {
     if (!p || !rep) { set_error("NULL argument"); return BS_E_INVAL; }
