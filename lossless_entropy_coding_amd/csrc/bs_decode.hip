@@ -273,42 +273,75 @@ __device__ __forceinline__ void unit_open(const DecodeArgs& a, const RecDev& r, 
 }
 
 // The fused product's epilogue for one group of 8 weights per lane (cnt of
-// them present): the lane's weights are record elements e0 + 8 lane .. + 7,
-// which lie in one matrix row; the wave's 512 elements span at most two rows
-// (gcols >= 512).  Each lane multiplies its weights by the matching x, the
-// wave sums the products per row, and lane 0 adds the sums into y.
-__device__ __forceinline__ uint32_t bf16_lo(uint32_t v) { return v << 16; }
-__device__ __forceinline__ uint32_t bf16_hi(uint32_t v) { return v & 0xFFFF0000u; }
+// them present).  The wave's groups are 512 consecutive record elements from
+// (row0, c0), 8 per lane in lane order, so with gcols >= 512 they span at most
+// two matrix rows.  Each lane takes the dot product of its weights with the
+// matching x (packed BF16 pairs, v_dot2 with fp32 accumulation), the wave
+// sums the products per row (DPP steps, no LDS), and lane 0 adds the sums
+// into y.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ void gemv_group(const DecodeArgs& a, const uint32_t (&o)[4], uint32_t cnt, uint64_t e0,
-                                           uint32_t lane) {
-    const uint64_t cols = a.gcols;
-    const uint64_t row0 = e0 / cols;                 // uniform
-    const uint32_t c0 = (uint32_t)(e0 - row0 * cols);
+// sum of v over the wave, in lane 63: quad, row and row-broadcast DPP steps
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+#define BS_DPP_ADD(ctrl, rows) \
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, rows, 0xF, false))
+    BS_DPP_ADD(0xB1, 0xF);    // quad_perm [1,0,3,2]
+    BS_DPP_ADD(0x4E, 0xF);    // quad_perm [2,3,0,1]
+    BS_DPP_ADD(0x124, 0xF);   // row_ror:4
+    BS_DPP_ADD(0x128, 0xF);   // row_ror:8: every lane holds its row's sum
+    BS_DPP_ADD(0x142, 0xA);   // row_bcast:15 into rows 1 and 3
+    BS_DPP_ADD(0x143, 0xC);   // row_bcast:31 into rows 2 and 3
+#undef BS_DPP_ADD
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__device__ __forceinline__ void gemv_group(const DecodeArgs& a, const uint32_t (&o)[4], uint32_t cnt, uint64_t row0,
+                                           uint32_t c0, uint32_t lane) {
+    const uint32_t cols = (uint32_t)a.gcols;
     const uint32_t c = c0 + 8 * lane;
     const bool wrap = c >= cols;
-    const uint32_t col = wrap ? c - (uint32_t)cols : c;
+    const uint32_t col = wrap ? c - cols : c;
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
     const v4u xv = *(const v4u*)(a.gx + col);
     const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
     float sum = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-        const uint32_t wk = k & 1 ? bf16_hi(o[k >> 1]) : bf16_lo(o[k >> 1]);
-        const uint32_t xk = k & 1 ? bf16_hi(xw[k >> 1]) : bf16_lo(xw[k >> 1]);
-        if ((uint32_t)k < cnt) sum = __builtin_fmaf(__uint_as_float(wk), __uint_as_float(xk), sum);
+    for (int k = 0; k < 4; k++) {
+        // weights 2k and 2k + 1 of the group, the upper one dropped when absent
+        const uint32_t w = 2 * k + 1 < (int)cnt ? o[k] : 2 * k < (int)cnt ? (o[k] & 0xFFFFu) : 0u;
+        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, xw[k]), sum,
+                                              false);
     }
-    float s0 = wrap ? 0.f : sum, s1 = wrap ? sum : 0.f;
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-        s0 += __shfl_xor(s0, d, 64);
-        s1 += __shfl_xor(s1, d, 64);
-    }
+    const float s0 = wave_sum_dpp(wrap ? 0.f : sum);
+    const float s1 = wave_sum_dpp(wrap ? sum : 0.f);
     const uint64_t wrapped = __builtin_amdgcn_ballot_w64(wrap && cnt > 0);
     const uint64_t here = __builtin_amdgcn_ballot_w64(!wrap && cnt > 0);
     if (lane == 0) {
         if (here) __hip_atomic_fetch_add(a.gy + row0, s0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (wrapped) __hip_atomic_fetch_add(a.gy + row0 + 1, s1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Matrix position (row, column) of a group start, advanced by whole groups
+// without dividing (uniform values, kept in scalar registers).
+struct MatPos {
+    uint64_t row;
+    uint32_t col;
+    __device__ __forceinline__ void advance(uint32_t by, uint32_t cols) {
+        col += by;
+        while (col >= cols) { col -= cols; row++; }
+    }
+};
+
+// the product of one group per lane group q of the macro-step that starts at p
+template <int R>
+__device__ __forceinline__ void gemv_step(const DecodeArgs& a, const uint32_t (&o)[R][4], const int32_t* cnt,
+                                          MatPos p, uint32_t lane) {
+    const uint32_t cols = (uint32_t)a.gcols;
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        gemv_group(a, o[q], cnt ? (uint32_t)cnt[q] : 8u, p.row, p.col, lane);
+        p.advance(512, cols);
     }
 }
 
@@ -325,6 +358,15 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
 
     uint32_t pos = u.pos;
     uint8_t* out = a.out + (r.out_off - a.out_base) + 2ull * ch * r.W;
+    // the fused product: matrix position of the stream's first group
+    MatPos mpos{0, 0};
+    if (V) {
+        const uint64_t e = (uint64_t)ch * r.W + 8ull * LB;
+        const uint64_t row = e / a.gcols;
+        mpos.row = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(row >> 32)) << 32) |
+                   __builtin_amdgcn_readfirstlane((uint32_t)row);
+        mpos.col = __builtin_amdgcn_readfirstlane((uint32_t)(e - row * a.gcols));
+    }
 
     const uint32_t groups = (n_c + 7) / 8;
     const uint32_t T = (groups + K - 1) / K;
@@ -384,12 +426,14 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
                 o[q][2] |= (x[q] & 127u) | ((x[q] >> 7) & 127u) << 16;
                 o[q][3] |= ((x[q] >> 14) & 127u) | ((x[q] >> 21) & 127u) << 16;
             }
-            if (V) {
-                gemv_group(a, o[q], 8u, (uint64_t)ch * r.W + 8ull * ((uint64_t)t * K + LB + 64 * q), lane);
-            } else {
+            if (!V) {
                 uint4* op = (uint4*)out + (uint64_t)t * K + LB + 64 * q + lane;
                 *op = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
             }
+        }
+        if (V) {
+            gemv_step<R>(a, o, nullptr, mpos, lane);
+            mpos.advance(8 * K, (uint32_t)a.gcols);
         }
     }
     if (whole) {
@@ -474,7 +518,7 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
             }
             const uint64_t g16 = (uint64_t)t * K + LB + 64 * q + lane;
             if (V) {
-                gemv_group(a, o[q], (uint32_t)cnt[q], (uint64_t)ch * r.W + 8ull * (g16 - lane), lane);
+                // below, after the R groups
             } else if (cnt[q] == 8) {
                 ((uint4*)out)[g16] = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
             } else if (cnt[q] > 0) {
@@ -483,6 +527,10 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
                 for (int k = 0; k < 8; k++)
                     if (k < cnt[q]) o16[k] = (uint16_t)(o[q][k >> 1] >> (16 * (k & 1)));
             }
+        }
+        if (V) {
+            gemv_step<R>(a, o, cnt, mpos, lane);
+            mpos.advance(8 * K, (uint32_t)a.gcols);
         }
     }
 
