@@ -56,6 +56,10 @@ def lib():
         l.bso_symbol_f.argtypes = [C.c_uint16]; l.bso_symbol_f.restype = C.c_uint32
         l.bso_combine.argtypes = [C.c_uint32, C.c_uint32]; l.bso_combine.restype = C.c_uint16
         l.bso_histogram.argtypes = [C.c_void_p, C.c_uint64, u64p, u64p]; l.bso_histogram.restype = None
+        l.bso_fixed_encode.argtypes = [C.c_void_p, C.c_uint64, C.POINTER(C.c_void_p), u64p]
+        l.bso_fixed_encode.restype = C.c_int
+        l.bso_fixed_decode.argtypes = [C.c_void_p, C.c_uint64, C.c_void_p, C.c_uint64]
+        l.bso_fixed_decode.restype = C.c_int
         l.bso_normalise.argtypes = [u64p, C.c_uint32, C.c_uint32, u32p]; l.bso_normalise.restype = C.c_int
         l.bso_select_tables.argtypes = [u64p, u64p, C.c_uint32, C.c_uint32, u32p, u32p, u32p]
         l.bso_select_tables.restype = C.c_int
@@ -305,3 +309,32 @@ def decode_chunk(container, record: int, chunk: int, max_weights: int = 1 << 20)
     if rc:
         raise OracleError(rc, "decode_chunk")
     return out[: int(n_c[0])].copy()
+
+
+# --------------------------------------------------------------------------- fixed-width lane streams
+def fixed_encode(words) -> bytes:
+    """The fixed-width lane-stream form of one BF16 tensor (see the C source)."""
+    w = np.ascontiguousarray(np.asarray(words, np.uint16))
+    out = C.c_void_p()
+    n = np.zeros(1, np.uint64)
+    rc = lib().bso_fixed_encode(_ptr(w), w.size, C.byref(out), _u64p(n))
+    if rc:
+        raise OracleError(rc, "fixed_encode")
+    try:
+        return C.string_at(out, int(n[0]))
+    finally:
+        lib().bso_free(out)
+
+
+def fixed_decode(blob: bytes, cap: int | None = None) -> np.ndarray:
+    """Decode a fixed-width blob; `cap` is the output capacity in weights
+    (default: the header's count, bounded by what the blob can hold)."""
+    buf = np.frombuffer(blob, np.uint8)
+    n = int.from_bytes(blob[16:24], "little") if len(blob) >= 24 else 0
+    n = min(n, (len(blob) // 2816 + 1) * 2048)
+    cap = n if cap is None else cap
+    out = np.zeros(max(cap, 1), np.uint16)
+    rc = lib().bso_fixed_decode(_ptr(buf), buf.size, _ptr(out), cap)
+    if rc:
+        raise OracleError(rc, "fixed_decode")
+    return out[:n].copy()

@@ -15,7 +15,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "bs_oracle.c")
 PINS = ["tests/test_oracle_coder.py", "tests/test_oracle_model.py", "tests/test_oracle_container.py",
-        "tests/test_oracle_streams.py"]
+        "tests/test_oracle_streams.py", "tests/test_oracle_fixed.py"]
 SELECT = ["-m", "not slow", "-k", "not cfg1 and not cfg2 and not gaussian and not scale_invariance"]
 
 MUTANTS = {
@@ -55,6 +55,15 @@ MUTANTS = {
     "table_always_eligible": ("eligible[k] = (256 * E > n * n + (unsigned __int128)726784 * n);", "eligible[k] = 1;"),
     "signs_not_merged": ("unsigned __int128 m = (unsigned __int128)cf[e * 128 + f] + cf[(256 + e) * 128 + f];",
                          "unsigned __int128 m = cf[e * 128 + f];"),
+    "fixed_table_tie_high": ("if (!used[s] && cs[s] && (best < 0 || cs[s] > cs[best])) best = s;",
+                             "if (!used[s] && cs[s] && (best < 0 || cs[s] >= cs[best])) best = s;"),
+    "fixed_sixteen_codes": ("while (m < 15) {", "while (m < 16) {"),
+    "fixed_nibbles_swapped": ("cw[(i % 8) / 2] |= (uint8_t)(code << (4 * (i % 2)));",
+                              "cw[(i % 8) / 2] |= (uint8_t)(code << (4 * (1 - i % 2)));"),
+    "fixed_lane_major_codes": ("uint8_t* cw = base + 4 * (64 * (i / 8) + l);", "uint8_t* cw = base + 4 * (4 * l + i / 8);"),
+    "fixed_fraction_msb_first": ("put_bits(frac, 7ull * i, f, 7);", "put_bits(frac, 7ull * (31 - i), f, 7);"),
+    "fixed_no_escape_check": ("if (e != (blk + 1 < n_blocks ? get32(b + offs + 4 * (blk + 1)) : n_esc)) return BSO_ECORRUPT;",
+                              "if (0) return BSO_ECORRUPT;"),
     "shape_rounding": ("*W = (uint32_t)round_up(n ? n : 1, 8 * (uint64_t)k);", "*W = (uint32_t)round_up(n ? n : 1, 8);"),
 }
 
