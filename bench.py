@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--gemv", action="store_true",
                     help="time the fused decode and matrix-vector product (bs_gemv_async) of the 4096x4096 "
                          "workload against decode-then-GEMV and a GEMV on the uncompressed matrix")
+    ap.add_argument("--fixed", action="store_true",
+                    help="time the decode of the fixed-width lane-stream form (bs_fixed_decode_async) derived from "
+                         "the workload's container, against the rANS decode of the same container")
     return ap.parse_args()
 
 
@@ -203,6 +206,90 @@ def gemv_bench(a):
     print(json.dumps(line))
 
 
+def fixed_bench(a):
+    """The fixed-width lane-stream form of every BF16 record of the workload,
+    transcoded on the host from the GPU decode of the canonical container, then
+    decoded by bs_fixed_decode_async (one launch per record).  Reports decoded
+    GB/s, the kernel's HBM roofline fraction and bits/weight, next to the rANS
+    decode of the same container."""
+    import torch
+    from lossless_entropy_coding_amd import _lib as L
+    from lossless_entropy_coding_amd import codec, workloads
+    gen_dev = "cuda" if a.config == "4" else "cpu"
+    enc = workloads.encode_config(a.config, device=gen_dev, keep_reference=False, keep_device_reference=True,
+                                  lanes=a.lanes, chunk_weights=a.chunk_weights, stream_lanes=a.stream_lanes,
+                                  m_s=a.m_s, m_f=a.m_f)
+    job = workloads.DecodeJob(enc)
+    stream = torch.cuda.current_stream()
+    job.decode(stream)
+    torch.cuda.synchronize()
+    ok, detail = job.verify()
+    assert ok, detail
+    # derive the fixed form of each BF16 record from the decoded canonical container
+    t0 = time.perf_counter()
+    plans, outs, refs = [], [], []
+    for i in range(job.plan.n_records):
+        ri = codec.record_info(enc.container, i)
+        if ri.kind != L.KIND_BF16:
+            continue
+        dec = codec.record_output(job.out, job.plan, i)
+        words = dec.view(torch.int16).cpu().numpy().view(np.uint16)
+        plans.append(codec.FixedPlan(codec.fixed_encode(words)))
+        outs.append(torch.empty(max(ri.n, 8), dtype=torch.int16, device="cuda"))
+        refs.append(dec.view(torch.int16))
+    t_transcode = time.perf_counter() - t0
+    n = sum(p.n for p in plans)
+    blob_bytes = sum(p.bytes for p in plans)
+    steps = [p.bound_decode(o, status=False, stream=stream) for p, o in zip(plans, outs)]
+
+    def step():
+        for s_ in steps:
+            s_()
+
+    def check():
+        for p, o, r in zip(plans, outs, refs):
+            p.decode_into(o, stream=stream)
+        torch.cuda.synchronize()
+        for p, o, r in zip(plans, outs, refs):
+            if not torch.equal(o[: p.n], r) or int(p.status[: p.info.n_blocks].abs().sum()) != 0:
+                log("FIXED DECODE MISMATCH")
+                sys.exit(1)
+
+    def timed(fn):
+        for _ in range(a.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_s = time.perf_counter()
+        e0.record(stream)
+        for _ in range(a.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t_s) / a.steps, e0.elapsed_time(e1) * 1e-3 / a.steps
+
+    check()
+    wall, dev_s = timed(step)
+    check()
+    rans_wall, rans_dev = timed(job.fast_decoder(stream))
+    alg = blob_bytes + 2 * n
+    achieved = alg / dev_s / 1e9          # algorithmic bytes over the launches' device time
+    line = {"metric": "fixed-width lane-stream decode: decoded BF16 GB/s on 1 MI355X (% HBM roofline) + bits/weight",
+            "value": round(2 * n / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+            "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "dtype": "u32", "data": "synthetic",
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "fixed_decode_kernel",
+                         "alg_bytes_per_step": alg, "launches_per_step": len(plans),
+                         "avg_step_ms": round(dev_s * 1e3, 4)},
+            "bits_per_weight": round(8 * blob_bytes / n, 4),
+            "rans": {"value": round(2 * n / rans_wall / 1e9, 2), "avg_step_ms": round(rans_dev * 1e3, 4),
+                     "bits_per_weight": round(job.bits_per_weight, 4)},
+            "transcode_s_host": round(t_transcode, 2),
+            "config": {"workload": job.name, "bf16_weights": n, "tensors": len(plans),
+                       "escapes": sum(p.info.n_esc for p in plans)}}
+    print(json.dumps(line))
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -227,6 +314,9 @@ def main():
     L.lib()   # fails loudly if the HIP library is missing
     if a.gemv:
         gemv_bench(a)
+        return
+    if a.fixed:
+        fixed_bench(a)
         return
     dev = "cuda"
     t0 = time.time()

@@ -243,6 +243,67 @@ bs_status bs_decode_async(const bs_plan* plan, uint32_t first, uint32_t count, v
 bs_status bs_gemv_async(const bs_plan* plan, uint32_t record, uint64_t rows, uint64_t cols, const void* d_x, float* d_y,
                         uint32_t* d_status, void* stream);
 
+/* -------------------------------------------------- fixed-width lane streams
+ *
+ * A second device form of one BF16 tensor, derived from it once and decoded
+ * without any sequential chain [NVLC card, runtime paragraphs and runtime
+ * accounting table: the measured GPU runtime derives fixed-width,
+ * lane-oriented streams (the Fixed7/Compact11 runtime) from the canonical
+ * model at initialisation, about 71% of the raw BF16 bytes resident; the
+ * layout below is this library's own].  Every weight is an 11-bit code
+ * word: a 4-bit code naming one of the tensor's 15 most frequent
+ * (sign, exponent) symbols, or 15 = escape, and the exact 7-bit fraction.
+ * Layout (all integers little-endian):
+ *   header, 96 B: "BF16FIX1", u32 version (1), u32 0, u64 n (weights),
+ *     u64 n_blocks = ceil(n / 2048), u64 esc_off, u64 n_esc, 16 B zero,
+ *     16 x u16: the symbol of codes 0..14 in order of count (descending,
+ *     ties to the lower symbol; 0 where fewer than 15 occur), entry 15 = 0
+ *   n_blocks blocks of 2816 B from byte 96; lane l (0..63) of block b holds
+ *     weights 2048 b + 32 l .. + 31 (past n: code 0, fraction 0):
+ *     code plane: dword k (0..3) of lane l at +4 (64 k + l), the code of the
+ *       lane's weight 8 k + i in bits 4 i .. 4 i + 3;
+ *     fraction plane: dword k (0..6) of lane l at +1024 + 4 (64 k + l): the
+ *       lane's 32 fractions, weight i at bit 7 i of the 224 bits these seven
+ *       dwords hold (least significant first)
+ *   n_blocks x u32 from 96 + 2816 n_blocks: index of each block's first
+ *     escape in the escape list
+ *   the escape list at esc_off = 96 + 2820 n_blocks: n_esc u16 symbols, one
+ *     per code 15, in weight order; the blob is zero-padded to 16 B. */
+typedef struct {
+    uint64_t n;             /* weights */
+    uint64_t n_blocks;
+    uint64_t n_esc;         /* escaped weights */
+    uint64_t esc_off;       /* byte offset of the escape list */
+    uint64_t bytes;         /* blob length */
+    uint16_t table[16];     /* symbol of codes 0..14; entry 15 = 0 */
+} bs_fixed_info;
+
+/* Fixed-width form of h_words[0..n) (host), built on up to `threads` host
+ * threads (0 = all); deterministic.  *out receives a new bs_blob.  Errors:
+ * BS_E_INVAL (NULL), BS_E_NOMEM. */
+bs_status bs_fixed_encode_host(const uint16_t* h_words, uint64_t n, uint32_t threads, bs_blob** out);
+
+/* Validate the header of a fixed-width blob and describe it.  h_header: a
+ * host copy of at least its first 96 bytes (header_len of them readable);
+ * blob_len: the whole blob's length.  Checks the magic, version, block count,
+ * escape list offset and that the escape list fits in blob_len; symbols
+ * above 511 in the table are a format error.  Errors: BS_E_INVAL,
+ * BS_E_FORMAT, BS_E_VERSION. */
+bs_status bs_fixed_info_get(const void* h_header, uint64_t header_len, uint64_t blob_len, bs_fixed_info* info);
+
+/* Decode a fixed-width blob resident in device memory (d_blob, info->bytes
+ * bytes, 16-B aligned; `info` from bs_fixed_info_get on the same bytes) into
+ * d_out (info->n BF16 words, 16-B aligned, at least 2 n bytes of capacity;
+ * nothing else is written).  d_status: NULL, or info->n_blocks u32, each set
+ * to 0 (ok) or a bit set: 1 = the block's codes hold another number of
+ * escapes than its escape range, 2 = its escape range is out of order or
+ * beyond n_esc, 4 = an escape symbol above 511.  Escaped weights that such a
+ * block cannot resolve get symbol 0.  Enqueued on `stream`; nothing is
+ * allocated.  Errors (before anything is enqueued): BS_E_INVAL (NULL,
+ * alignment), BS_E_NOSPACE, BS_E_HIP. */
+bs_status bs_fixed_decode_async(const bs_fixed_info* info, const void* d_blob, void* d_out, uint64_t out_capacity,
+                                uint32_t* d_status, void* stream);
+
 /* Bytes needed to decode records [first, first + count). */
 uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count);
 

@@ -63,6 +63,11 @@ class Report(C.Structure):
                 ("reserved", C.c_uint32)]
 
 
+class FixedInfo(C.Structure):
+    _fields_ = [("n", C.c_uint64), ("n_blocks", C.c_uint64), ("n_esc", C.c_uint64), ("esc_off", C.c_uint64),
+                ("bytes", C.c_uint64), ("table", C.c_uint16 * 16)]
+
+
 # every symbol declared in include/bs.h, with (restype, argtypes)
 SIGNATURES = {
     "bs_params_default": (None, [C.POINTER(Params)]),
@@ -84,6 +89,10 @@ SIGNATURES = {
     "bs_plan_out_bytes": (C.c_uint64, [C.c_void_p, C.c_uint32, C.c_uint32]),
     "bs_gemv_async": (C.c_int, [C.c_void_p, C.c_uint32, C.c_uint64, C.c_uint64, C.c_void_p, C.c_void_p, C.c_void_p,
                                 C.c_void_p]),
+    "bs_fixed_encode_host": (C.c_int, [C.c_void_p, C.c_uint64, C.c_uint32, C.POINTER(C.c_void_p)]),
+    "bs_fixed_info_get": (C.c_int, [C.c_void_p, C.c_uint64, C.c_uint64, C.POINTER(FixedInfo)]),
+    "bs_fixed_decode_async": (C.c_int, [C.POINTER(FixedInfo), C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p,
+                                        C.c_void_p]),
     "bs_plan_waves_per_block": (C.c_uint32, [C.c_void_p]),
     "bs_verify": (C.c_int, [C.c_void_p, C.c_uint32, C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_uint32,
                             C.c_void_p, C.POINTER(Report)]),

@@ -260,3 +260,69 @@ def record_output(out: torch.Tensor, plan: Plan, i: int, first: int = 0) -> torc
     base = record_info(plan.host, first).out_offset
     nb = 2 * ri.n if ri.kind == L.KIND_BF16 else ri.n
     return out[ri.out_offset - base: ri.out_offset - base + nb]
+
+
+# --------------------------------------------------------------------------- fixed-width lane streams
+def fixed_encode(words, threads: int = 0) -> bytes:
+    """Fixed-width lane-stream form of one BF16 tensor (host uint16 words),
+    built by the library's host transcoder (bs_fixed_encode_host)."""
+    w = np.ascontiguousarray(np.asarray(words).view(np.uint16).reshape(-1))
+    blob = C.c_void_p()
+    L.check(L.lib().bs_fixed_encode_host(w.ctypes.data if w.size else None, w.size, threads, C.byref(blob)),
+            "bs_fixed_encode_host")
+    try:
+        return C.string_at(L.lib().bs_blob_data(blob), L.lib().bs_blob_size(blob))
+    finally:
+        L.lib().bs_blob_free(blob)
+
+
+def fixed_info(blob: bytes, blob_len: int | None = None) -> L.FixedInfo:
+    info = L.FixedInfo()
+    L.check(L.lib().bs_fixed_info_get(blob, len(blob), len(blob) if blob_len is None else blob_len, C.byref(info)),
+            "bs_fixed_info_get")
+    return info
+
+
+class FixedPlan:
+    """A fixed-width blob resident in HBM and its validated header."""
+
+    def __init__(self, blob: bytes, device: str = "cuda"):
+        self.info = fixed_info(blob)
+        self.n = self.info.n
+        self.bytes = self.info.bytes
+        self.dev = torch.frombuffer(bytearray(blob), dtype=torch.uint8).to(device)
+        self.status = torch.zeros(max(self.info.n_blocks, 1), dtype=torch.int32, device=device)
+
+    def new_output(self) -> torch.Tensor:
+        return torch.empty(max(self.n, 8), dtype=torch.int16, device=self.dev.device)
+
+    def decode_into(self, out: torch.Tensor, status: bool = True, stream=None) -> None:
+        """Enqueue the decode of all n weights into `out` (bs_fixed_decode_async)."""
+        rc = L.lib().bs_fixed_decode_async(C.byref(self.info), C.c_void_p(self.dev.data_ptr()),
+                                           C.c_void_p(out.data_ptr()), C.c_uint64(out.numel() * out.element_size()),
+                                           C.c_void_p(self.status.data_ptr()) if status else None,
+                                           C.c_void_p(_stream_handle(stream)))
+        L.check(rc, "bs_fixed_decode_async")
+
+    def bound_decode(self, out: torch.Tensor, status: bool = True, stream=None):
+        """decode_into with its ctypes arguments converted once."""
+        f = L.lib().bs_fixed_decode_async
+        args = (C.byref(self.info), C.c_void_p(self.dev.data_ptr()), C.c_void_p(out.data_ptr()),
+                C.c_uint64(out.numel() * out.element_size()),
+                C.c_void_p(self.status.data_ptr()) if status else None, C.c_void_p(_stream_handle(stream)))
+        keep = (out, self.status, self.dev)
+
+        def run():
+            rc = f(*args)
+            if rc:
+                L.check(rc, "bs_fixed_decode_async")
+            return keep
+        return run
+
+    def decode(self, stream=None) -> torch.Tensor:
+        out = self.new_output()
+        self.decode_into(out, stream=stream)
+        return out[: self.n]
+
+    def block_status(self) -> np.ndarray:
+        return self.status[: self.info.n_blocks].cpu().numpy().view(np.uint32)

@@ -179,29 +179,6 @@ struct EncRecord {
     uint64_t stab_off = 0;       // stream table: per chunk, the start unit of streams 1 .. S-1
 };
 
-uint32_t pick_threads(uint32_t req) {
-    uint32_t hw = std::thread::hardware_concurrency();
-    if (!hw) hw = 4;
-    return req ? req : hw;
-}
-
-template <class F>
-void parallel_for(uint64_t n, uint32_t threads, F&& fn) {
-    std::atomic<uint64_t> next{0};
-    auto body = [&]() {
-        for (;;) {
-            uint64_t i = next.fetch_add(1);
-            if (i >= n) return;
-            fn(i);
-        }
-    };
-    const uint32_t nt = (uint32_t)std::min<uint64_t>(threads, std::max<uint64_t>(n, 1));
-    std::vector<std::thread> pool;
-    for (uint32_t k = 1; k < nt; k++) pool.emplace_back(body);
-    body();
-    for (auto& th : pool) th.join();
-}
-
 void build_head(EncRecord& r) {
     const Model& md = *r.md;
     const uint64_t stab = 24;
@@ -362,10 +339,6 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
 }  // namespace bs
 
 using namespace bs;
-
-struct bs_blob {
-    std::vector<uint8_t> bytes;
-};
 
 extern "C" {
 

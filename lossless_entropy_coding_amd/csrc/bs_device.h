@@ -103,6 +103,22 @@ struct DecodeArgs {
     uint64_t gcols;         // a multiple of 8, at least 512
 };
 
+// fixed-width lane-stream form (layout in bs.h): one wavefront decodes a
+// block of 2048 weights (64 lanes x 32) at a time
+constexpr uint32_t kFixHeader = 96;
+constexpr uint32_t kFixBlockW = 2048;
+constexpr uint32_t kFixBlockBytes = 2816;
+constexpr uint32_t kFixWaves = 4;           // waves per workgroup
+constexpr uint32_t kFixEscLds = 512;        // escapes per block staged in LDS (more are read from HBM)
+
+struct FixedArgs {
+    const uint8_t* blob;    // the whole blob (header at 0)
+    uint16_t* out;          // n BF16 words
+    uint32_t* status;       // n_blocks words or null
+    uint64_t n, n_blocks, n_esc, esc_off;
+    uint32_t tab[8];        // symbols of codes 0..15, two per word (code 2k low); code 15 = 0
+};
+
 }  // namespace bsd
 
 // Launchers (bs_kernels.hip).  All return a hipError_t as int.
@@ -118,6 +134,9 @@ int bsk_build_luts(const uint8_t* d_container, const bsd::RecDev* d_recs, uint32
 int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, bool compact, void* stream);
 // the fused matrix-vector product of one record (full layout, variant 1, 2 or 4), y zeroed first
 int bsk_gemv(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream);
+// decode a fixed-width blob: n_groups workgroups of kFixWaves waves, each wave
+// striding over the blocks
+int bsk_fixed_decode(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
 int bsk_raw_copy(const uint8_t* d_container, const bsd::RawDev* d_raw, uint32_t n_raw, uint8_t* d_out,
                  uint64_t out_base, void* stream);
 int bsk_compare(const uint8_t* a, const uint8_t* b, uint64_t n, unsigned long long* d_result /*2*/, void* stream);

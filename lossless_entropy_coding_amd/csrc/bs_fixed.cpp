@@ -1,0 +1,188 @@
+// bs_fixed.cpp -- the fixed-width lane-stream form: host transcoder, header
+// validation and the decode entry point.
+//
+// The form is derived once from a BF16 tensor (the canonical container's
+// decode) and read by a kernel without any sequential chain [NVLC card,
+// runtime paragraphs: the measured GPU runtime derives fixed-width,
+// lane-oriented streams at initialisation].  Layout: see bs.h.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <algorithm>
+#include <array>
+#include <new>
+#include <vector>
+
+#include "bs_device.h"
+#include "bs_internal.h"
+
+using namespace bs;
+
+namespace {
+
+constexpr char kFixMagic[8] = {'B', 'F', '1', '6', 'F', 'I', 'X', '1'};
+constexpr uint32_t kFixVersion = 1;
+constexpr uint64_t kEscapeCode = 15;
+
+uint64_t fixed_blocks(uint64_t n) { return (n + bsd::kFixBlockW - 1) / bsd::kFixBlockW; }
+uint64_t fixed_esc_off(uint64_t nb) { return bsd::kFixHeader + (uint64_t)(bsd::kFixBlockBytes + 4) * nb; }
+
+// codes 0..14: the up to 15 most frequent symbols, count descending, ties to
+// the lower symbol
+uint32_t fixed_table(const uint64_t* cs, uint16_t* table) {
+    std::array<uint32_t, 512> order;
+    for (uint32_t s = 0; s < 512; s++) order[s] = s;
+    std::stable_sort(order.begin(), order.end(), [&](uint32_t x, uint32_t y) { return cs[x] > cs[y]; });
+    uint32_t m = 0;
+    for (uint32_t k = 0; k < 15 && cs[order[k]]; k++) table[m++] = (uint16_t)order[k];
+    for (uint32_t k = m; k < 16; k++) table[k] = 0;
+    return m;
+}
+
+// one block: code and fraction planes, and its escapes from esc (in weight order)
+void pack_block(const uint16_t* w, uint64_t n, uint64_t blk, const uint8_t* code_of, uint8_t* base, uint8_t* esc) {
+    for (uint32_t l = 0; l < 64; l++) {
+        const uint64_t j0 = blk * bsd::kFixBlockW + 32ull * l;
+        uint32_t cw[4] = {0, 0, 0, 0}, fr[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (uint32_t i = 0; i < 32 && j0 + i < n; i++) {
+            const uint32_t x = w[j0 + i], s = x >> 7, f = x & 0x7Fu, code = code_of[s];
+            cw[i / 8] |= code << (4 * (i % 8));
+            const uint32_t bit = 7 * i;
+            fr[bit / 32] |= f << (bit % 32);
+            if (bit % 32 > 25) fr[bit / 32 + 1] |= f >> (32 - bit % 32);
+            if (code == kEscapeCode) { wr16(esc, s); esc += 2; }
+        }
+        for (uint32_t k = 0; k < 4; k++) wr32(base + 4 * (64 * k + l), cw[k]);
+        for (uint32_t k = 0; k < 7; k++) wr32(base + 1024 + 4 * (64 * k + l), fr[k]);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+bs_status bs_fixed_encode_host(const uint16_t* w, uint64_t n, uint32_t threads, bs_blob** out) {
+    if (!out || (n && !w)) { set_error("NULL argument"); return BS_E_INVAL; }
+    *out = nullptr;
+    try {
+        const uint32_t nt = pick_threads(threads);
+        const uint64_t nb = fixed_blocks(n);
+        // symbol counts
+        const uint64_t slice = 1ull << 20, n_slices = (n + slice - 1) / slice;
+        std::vector<std::array<uint64_t, 512>> part(n_slices);
+        parallel_for(n_slices, nt, [&](uint64_t i) {
+            auto& h = part[i];
+            h.fill(0);
+            for (uint64_t j = i * slice, e = std::min(n, j + slice); j < e; j++) h[w[j] >> 7]++;
+        });
+        uint64_t cs[512] = {0};
+        for (auto& h : part)
+            for (uint32_t s = 0; s < 512; s++) cs[s] += h[s];
+        uint16_t table[16];
+        const uint32_t m = fixed_table(cs, table);
+        uint8_t code_of[512];
+        memset(code_of, (int)kEscapeCode, sizeof code_of);
+        for (uint32_t k = 0; k < m; k++) code_of[table[k]] = (uint8_t)k;
+        // escapes per block, then each block's first
+        std::vector<uint64_t> first(nb + 1, 0);
+        parallel_for(nb, nt, [&](uint64_t b) {
+            uint64_t e = 0;
+            for (uint64_t j = b * bsd::kFixBlockW, end = std::min(n, j + bsd::kFixBlockW); j < end; j++)
+                e += code_of[w[j] >> 7] == kEscapeCode;
+            first[b + 1] = e;
+        });
+        for (uint64_t b = 0; b < nb; b++) first[b + 1] += first[b];
+        const uint64_t n_esc = first[nb];
+        if (n_esc > 0xFFFFFFFFull) { set_error("more than 2^32 - 1 escapes"); return BS_E_INVAL; }
+        const uint64_t esc_off = fixed_esc_off(nb);
+        auto* blob = new bs_blob;
+        blob->bytes.assign(align_up(esc_off + 2 * n_esc, 16), 0);
+        uint8_t* b = blob->bytes.data();
+        memcpy(b, kFixMagic, 8);
+        wr32(b + 8, kFixVersion);
+        wr64(b + 16, n);
+        wr64(b + 24, nb);
+        wr64(b + 32, esc_off);
+        wr64(b + 40, n_esc);
+        for (uint32_t k = 0; k < 16; k++) wr16(b + 64 + 2 * k, table[k]);
+        parallel_for(nb, nt, [&](uint64_t blk) {
+            wr32(b + bsd::kFixHeader + (uint64_t)bsd::kFixBlockBytes * nb + 4 * blk, (uint32_t)first[blk]);
+            pack_block(w, n, blk, code_of, b + bsd::kFixHeader + (uint64_t)bsd::kFixBlockBytes * blk,
+                       b + esc_off + 2 * first[blk]);
+        });
+        *out = blob;
+        return BS_OK;
+    } catch (const std::bad_alloc&) {
+        set_error("out of host memory");
+        return BS_E_NOMEM;
+    }
+}
+
+bs_status bs_fixed_info_get(const void* h_header, uint64_t header_len, uint64_t blob_len, bs_fixed_info* info) {
+    if (!h_header || !info) { set_error("NULL argument"); return BS_E_INVAL; }
+    const uint8_t* h = (const uint8_t*)h_header;
+    if (header_len < bsd::kFixHeader || blob_len < bsd::kFixHeader || memcmp(h, kFixMagic, 8) != 0) {
+        set_error("not a fixed-width blob");
+        return BS_E_FORMAT;
+    }
+    if (rd32(h + 8) != kFixVersion) { set_error("fixed-width blob version %u", rd32(h + 8)); return BS_E_VERSION; }
+    bs_fixed_info fi;
+    memset(&fi, 0, sizeof fi);
+    fi.n = rd64(h + 16);
+    fi.n_blocks = rd64(h + 24);
+    fi.esc_off = rd64(h + 32);
+    fi.n_esc = rd64(h + 40);
+    if (fi.n > (1ull << 50) || fi.n_blocks != fixed_blocks(fi.n) || fi.esc_off != fixed_esc_off(fi.n_blocks) ||
+        fi.n_esc > fi.n || fi.n_esc > 0xFFFFFFFFull) {
+        set_error("fixed-width header fields inconsistent");
+        return BS_E_FORMAT;
+    }
+    fi.bytes = align_up(fi.esc_off + 2 * fi.n_esc, 16);
+    if (fi.bytes > blob_len) { set_error("fixed-width blob truncated (%llu of %llu bytes)",
+                                         (unsigned long long)blob_len, (unsigned long long)fi.bytes);
+        return BS_E_FORMAT; }
+    for (uint32_t k = 0; k < 16; k++) {
+        fi.table[k] = (uint16_t)rd16(h + 64 + 2 * k);
+        if (fi.table[k] > 511 || (k == 15 && fi.table[k] != 0)) { set_error("bad symbol table"); return BS_E_FORMAT; }
+    }
+    *info = fi;
+    return BS_OK;
+}
+
+bs_status bs_fixed_decode_async(const bs_fixed_info* info, const void* d_blob, void* d_out, uint64_t out_capacity,
+                                uint32_t* d_status, void* stream) {
+    if (!info || !d_blob || (!d_out && info->n)) { set_error("NULL argument"); return BS_E_INVAL; }
+    if (((uintptr_t)d_blob | (uintptr_t)d_out) & 15) { set_error("blob and output must be 16-B aligned"); return BS_E_INVAL; }
+    if (info->n_blocks != fixed_blocks(info->n) || info->esc_off != fixed_esc_off(info->n_blocks) ||
+        info->n_esc > 0xFFFFFFFFull || info->bytes < info->esc_off + 2 * info->n_esc) {
+        set_error("bs_fixed_info not from bs_fixed_info_get");
+        return BS_E_INVAL;
+    }
+    if (out_capacity < 2 * info->n) { set_error("output capacity %llu < %llu", (unsigned long long)out_capacity,
+                                                (unsigned long long)(2 * info->n));
+        return BS_E_NOSPACE; }
+    if (info->n == 0) return BS_OK;
+    bsd::FixedArgs a;
+    memset(&a, 0, sizeof a);
+    a.blob = (const uint8_t*)d_blob;
+    a.out = (uint16_t*)d_out;
+    a.status = d_status;
+    a.n = info->n;
+    a.n_blocks = info->n_blocks;
+    a.n_esc = info->n_esc;
+    a.esc_off = info->esc_off;
+    for (uint32_t k = 0; k < 15; k++) {
+        if (info->table[k] > 511) { set_error("bad symbol table"); return BS_E_INVAL; }
+        a.tab[k / 2] |= (uint32_t)info->table[k] << (16 * (k % 2));
+    }
+    int cus = 0;
+    if (bsk_device_cus(&cus) != 0 || cus <= 0) cus = 256;
+    // one wave per block up to 8 workgroups per CU; beyond, waves stride
+    const uint64_t want = (info->n_blocks + bsd::kFixWaves - 1) / bsd::kFixWaves;
+    const uint32_t groups = (uint32_t)std::min<uint64_t>(want, 8ull * (uint64_t)cus);
+    const int e = bsk_fixed_decode(&a, groups, stream);
+    if (e != 0) { set_error("fixed decode launch: %s", hipGetErrorString((hipError_t)e)); return BS_E_HIP; }
+    return BS_OK;
+}
+
+}  // extern "C"

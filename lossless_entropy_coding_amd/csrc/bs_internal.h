@@ -2,7 +2,10 @@
 #pragma once
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "bs.h"
@@ -23,6 +26,32 @@ void set_error(const char* fmt, ...);
 void sha256(const void* data, uint64_t n, uint8_t out[32]);
 
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+// host worker threads: `req`, or the hardware's count when 0
+inline uint32_t pick_threads(uint32_t req) {
+    uint32_t hw = std::thread::hardware_concurrency();
+    if (!hw) hw = 4;
+    return req ? req : hw;
+}
+
+// fn(i) for i in [0, n) on up to `threads` threads (the caller's included),
+// items handed out one at a time
+template <class F>
+void parallel_for(uint64_t n, uint32_t threads, F&& fn) {
+    std::atomic<uint64_t> next{0};
+    auto body = [&]() {
+        for (;;) {
+            uint64_t i = next.fetch_add(1);
+            if (i >= n) return;
+            fn(i);
+        }
+    };
+    const uint32_t nt = (uint32_t)std::min<uint64_t>(threads, std::max<uint64_t>(n, 1));
+    std::vector<std::thread> pool;
+    for (uint32_t k = 1; k < nt; k++) pool.emplace_back(body);
+    body();
+    for (auto& th : pool) th.join();
+}
 
 // little-endian field access
 inline uint32_t rd16(const uint8_t* p) { return (uint32_t)p[0] | (uint32_t)p[1] << 8; }
@@ -58,3 +87,8 @@ struct Container {
 bs_status parse_container(const uint8_t* h, uint64_t len, Container& c);
 
 }  // namespace bs
+
+// the library's opaque byte buffer
+struct bs_blob {
+    std::vector<uint8_t> bytes;
+};

@@ -1,0 +1,159 @@
+"""GPU parity: the fixed-width lane-stream decode against the oracle.
+
+The form is the runtime's second device format [NVLC card, runtime
+paragraphs: fixed-width, lane-oriented streams derived once from the
+canonical model]; decoding it must give back every BF16 word bit for bit.
+Every blob here is built by the library's host transcoder, checked byte for
+byte against the oracle's encoder, and every GPU output is compared with the
+oracle's decode of the same blob.  All calls go through the C ABI
+(bs_fixed_info_get, bs_fixed_decode_async).
+"""
+import struct
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from lossless_entropy_coding_amd import _lib as L
+from lossless_entropy_coding_amd import codec, synth
+
+pytestmark = pytest.mark.gpu
+
+HDR, BLOCK_BYTES = 96, 2816
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _bf16(x) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _case_words(name, n, seed):
+    rng = np.random.default_rng(seed)
+    if name.startswith("gauss"):
+        w = rng.standard_normal(n) * 0.02
+        w[rng.random(n) < 0.001] *= 100.0
+        return _bf16(w)
+    if name.startswith("uniform"):                       # every symbol: almost all escapes
+        return rng.integers(0, 1 << 16, n, dtype=np.uint16)
+    if name.startswith("wide"):                          # a wide exponent spread: many escapes per block
+        return _bf16(rng.standard_normal(n) * np.exp(rng.standard_normal(n) * 4))
+    if name.startswith("patterns"):
+        return np.arange(1 << 16, dtype=np.uint16)
+    if name.startswith("zeros"):
+        return np.zeros(n, np.uint16)
+    raise ValueError(name)
+
+
+CASES = [
+    ("gauss_1", 1), ("gauss_3", 3), ("gauss_63", 63), ("gauss_2047", 2047), ("gauss_2048", 2048),
+    ("gauss_2049", 2049), ("gauss_ragged", 70001), ("gauss_many_blocks", 64 * 2048 * 5 + 1234),
+    ("uniform_ragged", 3 * 2048 + 77), ("wide_ragged", 41 * 2048 + 5), ("patterns", 65536), ("zeros", 10000),
+]
+
+
+def _run(words):
+    blob = codec.fixed_encode(words)
+    assert blob == O.fixed_encode(words)                 # host transcoder = the oracle's encoder
+    expect = O.fixed_decode(blob)
+    assert (expect == words).all()
+    plan = codec.FixedPlan(blob)
+    out = plan.decode()
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    return plan, blob, expect, got
+
+
+@pytest.mark.parametrize("name,n", CASES, ids=[c[0] for c in CASES])
+def test_fixed_decode_matches_oracle(name, n):
+    say("fixed case", name, n)
+    words = _case_words(name, n, n)
+    plan, blob, expect, got = _run(words)
+    assert got.size == expect.size
+    bad = np.flatnonzero(got != expect)
+    assert bad.size == 0, (bad[:8], got[bad[:8]], expect[bad[:8]])
+    assert (plan.block_status() == 0).all()
+
+
+def test_fixed_decode_4096x4096_workload():
+    # the 4096 x 4096 matrix workload at full size (16.8M weights, 8192 blocks)
+    wl = synth.cfg2("cpu")
+    words = synth.as_words(wl.items[0].tensor).numpy().view(np.uint16).reshape(-1)
+    say("fixed 4096x4096", words.size)
+    plan, blob, expect, got = _run(words)
+    assert (got == expect).all()
+    assert (plan.block_status() == 0).all()
+    # a second decode into a dirty buffer, with no status array
+    out = torch.full((words.size,), -1, dtype=torch.int16, device="cuda")
+    plan.decode_into(out, status=False)
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy().view(np.uint16) == expect).all()
+
+
+def test_fixed_writes_nothing_past_n():
+    words = _case_words("gauss", 2048 + 100, 5)
+    blob = codec.fixed_encode(words)
+    plan = codec.FixedPlan(blob)
+    out = torch.full((4096,), 0x5A5A, dtype=torch.int16, device="cuda")
+    plan.decode_into(out)
+    torch.cuda.synchronize()
+    h = out.cpu().numpy().view(np.uint16)
+    assert (h[: words.size] == O.fixed_decode(blob)).all()
+    assert (h[words.size:] == 0x5A5A).all()
+
+
+def _corrupt_device(plan, off, fmt, value):
+    b = bytearray(plan.dev.cpu().numpy().tobytes())
+    struct.pack_into(fmt, b, off, value)
+    plan.dev.copy_(torch.frombuffer(b, dtype=torch.uint8))
+
+
+def test_fixed_status_flags_corrupt_blocks():
+    s = (np.arange(5 * 2048) % 15) + 1
+    s[[10, 3000, 4999, 7000, 9000]] = [300, 301, 302, 303, 304]
+    words = (s << 7).astype(np.uint16)
+    blob = codec.fixed_encode(words)
+    info = codec.fixed_info(blob)
+    offs = HDR + BLOCK_BYTES * info.n_blocks
+    assert struct.unpack_from("<5I", blob, offs) == (0, 1, 2, 3, 4)
+
+    plan = codec.FixedPlan(blob)                             # block 1 starts one escape late
+    _corrupt_device(plan, offs + 4, "<I", 2)
+    plan.decode()
+    torch.cuda.synchronize()
+    assert plan.block_status().tolist() == [1, 1, 0, 0, 0]
+
+    plan = codec.FixedPlan(blob)                             # offsets out of order
+    _corrupt_device(plan, offs + 8, "<I", 0)
+    plan.decode()
+    torch.cuda.synchronize()
+    assert plan.block_status().tolist() == [0, 3, 1, 0, 0]
+
+    plan = codec.FixedPlan(blob)                             # block 4's escape is not a symbol
+    _corrupt_device(plan, info.esc_off + 2 * 4, "<H", 600)
+    out = plan.decode()
+    torch.cuda.synchronize()
+    assert plan.block_status().tolist() == [0, 0, 0, 0, 4]
+    got = out.cpu().numpy().view(np.uint16)
+    assert got[9000] == 0 and (np.delete(got, 9000) == np.delete(words, 9000)).all()
+
+
+def test_fixed_argument_errors():
+    words = _case_words("gauss", 5000, 9)
+    blob = codec.fixed_encode(words)
+    plan = codec.FixedPlan(blob)
+    out = torch.empty(5000 + 16, dtype=torch.int16, device="cuda")
+    with pytest.raises(L.BSError) as e:                      # misaligned output
+        plan.decode_into(out[1:])
+    assert e.value.rc == L.BS_E_INVAL
+    with pytest.raises(L.BSError) as e:                      # too small
+        plan.decode_into(out[:4999])
+    assert e.value.rc == L.BS_E_NOSPACE
+    plan.decode_into(out[:5000])
+    torch.cuda.synchronize()
+    assert (out[:5000].cpu().numpy().view(np.uint16) == words).all()

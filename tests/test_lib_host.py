@@ -203,3 +203,61 @@ def test_write_file_refuses_existing(tmp_path):
         codec.write_new(p, b"xyz")
     assert e.value.rc == L.BS_E_EXISTS
     assert open(p, "rb").read() == b"abc"
+
+
+# --------------------------------------------------------------------------- fixed-width lane streams
+@pytest.mark.parametrize("n,kind", [(0, "gauss"), (1, "gauss"), (35, "gauss"), (2048, "gauss"), (70001, "gauss"),
+                                    (3 * 2048 + 77, "uniform"), (65536, "patterns"), (5 * 2048 + 9, "wide")])
+def test_fixed_encoder_matches_oracle(n, kind):
+    rng = np.random.default_rng(n)
+    if kind == "gauss":
+        w = _words(rng.standard_normal(n) * 0.02)
+    elif kind == "uniform":
+        w = rng.integers(0, 1 << 16, n, dtype=np.uint16)
+    elif kind == "wide":
+        w = _words(rng.standard_normal(n) * np.exp(rng.standard_normal(n) * 4))
+    else:
+        w = np.arange(n, dtype=np.uint16)
+    want = O.fixed_encode(w)
+    for threads in (0, 1, 3):
+        assert codec.fixed_encode(w, threads=threads) == want
+    info = codec.fixed_info(want)
+    assert (info.n, info.n_blocks, info.bytes) == (n, (n + 2047) // 2048, len(want))
+    assert list(info.table) == list(struct.unpack_from("<16H", want, 64))
+
+
+def test_fixed_info_validation():
+    w = _words(np.random.default_rng(4).standard_normal(5000) * 0.02)
+    blob = codec.fixed_encode(w)
+
+    def bad(off, fmt, value):
+        b = bytearray(blob)
+        struct.pack_into(fmt, b, off, value)
+        return bytes(b)
+    for b, rc in [(b"BF16FIX0" + blob[8:], L.BS_E_FORMAT), (bad(8, "<I", 2), L.BS_E_VERSION),
+                  (bad(24, "<Q", 4), L.BS_E_FORMAT), (bad(32, "<Q", 0), L.BS_E_FORMAT),
+                  (bad(40, "<Q", 10 ** 6), L.BS_E_FORMAT), (bad(64, "<H", 512), L.BS_E_FORMAT),
+                  (bad(94, "<H", 3), L.BS_E_FORMAT), (blob[:95], L.BS_E_FORMAT)]:
+        with pytest.raises(L.BSError) as e:
+            codec.fixed_info(b)
+        assert e.value.rc == rc
+    with pytest.raises(L.BSError) as e:                      # the whole blob must be there
+        codec.fixed_info(blob[:96], blob_len=len(blob) - 16)
+    assert e.value.rc == L.BS_E_FORMAT
+    assert codec.fixed_info(blob[:96], blob_len=len(blob)).bytes == len(blob)
+
+
+def test_fixed_decode_argument_checks_before_launch():
+    import ctypes as C
+    w = _words(np.random.default_rng(5).standard_normal(5000) * 0.02)
+    info = codec.fixed_info(codec.fixed_encode(w))
+    f = L.lib().bs_fixed_decode_async
+    assert f(None, C.c_void_p(4096), C.c_void_p(4096), 10000, None, None) == L.BS_E_INVAL
+    assert f(C.byref(info), C.c_void_p(4100), C.c_void_p(4096), 10000, None, None) == L.BS_E_INVAL
+    assert f(C.byref(info), C.c_void_p(4096), C.c_void_p(4104), 10000, None, None) == L.BS_E_INVAL
+    assert f(C.byref(info), C.c_void_p(4096), C.c_void_p(4096), 9999, None, None) == L.BS_E_NOSPACE
+    forged = L.FixedInfo.from_buffer_copy(info)
+    forged.n_blocks += 1
+    assert f(C.byref(forged), C.c_void_p(4096), C.c_void_p(4096), 10000, None, None) == L.BS_E_INVAL
+    empty = codec.fixed_info(codec.fixed_encode(np.zeros(0, np.uint16)))
+    assert f(C.byref(empty), C.c_void_p(4096), None, 0, None, None) == L.BS_OK     # nothing to do
