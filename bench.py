@@ -274,6 +274,27 @@ def fixed_bench(a):
     rans_wall, rans_dev = timed(job.fast_decoder(stream))
     alg = blob_bytes + 2 * n
     achieved = alg / dev_s / 1e9          # algorithmic bytes over the launches' device time
+    gemv = None
+    if a.config == "2":
+        # y = W x on the 4096 x 4096 matrix: fused on the fixed form, fused on the
+        # rANS container, and torch.mv on the uncompressed matrix
+        rows = cols = 4096
+        g = torch.Generator(device="cpu").manual_seed(1)
+        x = torch.randn(cols, generator=g).to(torch.bfloat16).cuda()
+        y = torch.empty(rows, dtype=torch.float32, device="cuda")
+        W = refs[0].view(torch.bfloat16).reshape(rows, cols)
+        fx = plans[0].bound_gemv(y, x.view(torch.int16), rows, cols, stream=stream)
+        rx = job.plan.bound_gemv(y, x.view(torch.int16), rows, cols, stream=stream)
+        _, t_fixed = timed(fx)
+        _, t_rans = timed(rx)
+        _, t_plain = timed(lambda: torch.mv(W, x))
+        fx()
+        torch.cuda.synchronize()
+        ref = W.float() @ x.float()
+        gemv = {"fixed_fused_us": round(t_fixed * 1e6, 2), "rans_fused_us": round(t_rans * 1e6, 2),
+                "plain_bf16_gemv_us": round(t_plain * 1e6, 2),
+                "fixed_fused_GB_s_of_blob": round(plans[0].bytes / t_fixed / 1e9, 1),
+                "max_rel_diff_vs_fp32_product": float((y - ref).abs().max() / ref.abs().max())}
     line = {"metric": "fixed-width lane-stream decode: decoded BF16 GB/s on 1 MI355X (% HBM roofline) + bits/weight",
             "value": round(2 * n / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
             "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "dtype": "u32", "data": "synthetic",
@@ -284,7 +305,7 @@ def fixed_bench(a):
             "bits_per_weight": round(8 * blob_bytes / n, 4),
             "rans": {"value": round(2 * n / rans_wall / 1e9, 2), "avg_step_ms": round(rans_dev * 1e3, 4),
                      "bits_per_weight": round(job.bits_per_weight, 4)},
-            "transcode_s_host": round(t_transcode, 2),
+            "transcode_s_host": round(t_transcode, 2), "gemv": gemv,
             "config": {"workload": job.name, "bf16_weights": n, "tensors": len(plans),
                        "escapes": sum(p.info.n_esc for p in plans)}}
     print(json.dumps(line))

@@ -304,6 +304,21 @@ bs_status bs_fixed_info_get(const void* h_header, uint64_t header_len, uint64_t 
 bs_status bs_fixed_decode_async(const bs_fixed_info* info, const void* d_blob, void* d_out, uint64_t out_capacity,
                                 uint32_t* d_status, void* stream);
 
+/* Fused decode and matrix-vector product on a fixed-width blob [NVLC card,
+ * runtime paragraphs: the compressed-only runtime multiplies with weights
+ * decoded where they are used and keeps no decoded copy]: y[r] = sum over c
+ * of W[r, c] x[c], the blob's n weights read as a row-major rows x cols
+ * matrix (rows * cols = n, cols a multiple of 32 and below 2^26).  The
+ * weights are decoded in registers and never written out.  d_x: cols BF16
+ * words, 16-B aligned; d_y: rows floats, overwritten.  One workgroup owns
+ * whole rows, so the products of a row are summed in fp32 in one fixed order:
+ * the result is the same on every run and matches the exact sum within the
+ * usual fp32 summation bound (not bit for bit).  d_status as for
+ * bs_fixed_decode_async.  One kernel launch on `stream`; nothing is
+ * allocated.  Errors: BS_E_INVAL (shape, NULL, alignment), BS_E_HIP. */
+bs_status bs_fixed_gemv_async(const bs_fixed_info* info, const void* d_blob, uint64_t rows, uint64_t cols,
+                              const void* d_x, float* d_y, uint32_t* d_status, void* stream);
+
 /* Bytes needed to decode records [first, first + count). */
 uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count);
 

@@ -324,5 +324,39 @@ class FixedPlan:
         self.decode_into(out, stream=stream)
         return out[: self.n]
 
+    def gemv_into(self, y: torch.Tensor, x: torch.Tensor, rows: int, cols: int, status: bool = True,
+                  stream=None) -> None:
+        """Enqueue y = W x with W the blob's weights as a rows x cols matrix,
+        decoded in registers (bs_fixed_gemv_async): x bfloat16 (or int16) of
+        cols elements, y float32 of rows elements (overwritten)."""
+        assert x.dtype in (torch.bfloat16, torch.int16) and x.numel() == cols and x.is_contiguous()
+        assert y.dtype == torch.float32 and y.numel() == rows and y.is_contiguous()
+        rc = L.lib().bs_fixed_gemv_async(C.byref(self.info), C.c_void_p(self.dev.data_ptr()), rows, cols,
+                                         C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()),
+                                         C.c_void_p(self.status.data_ptr()) if status else None,
+                                         C.c_void_p(_stream_handle(stream)))
+        L.check(rc, "bs_fixed_gemv_async")
+
+    def bound_gemv(self, y: torch.Tensor, x: torch.Tensor, rows: int, cols: int, status: bool = False,
+                   stream=None):
+        """gemv_into with its ctypes arguments converted once."""
+        f = L.lib().bs_fixed_gemv_async
+        args = (C.byref(self.info), C.c_void_p(self.dev.data_ptr()), C.c_uint64(rows), C.c_uint64(cols),
+                C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()),
+                C.c_void_p(self.status.data_ptr()) if status else None, C.c_void_p(_stream_handle(stream)))
+        keep = (x, y, self.status, self.dev)
+
+        def run():
+            rc = f(*args)
+            if rc:
+                L.check(rc, "bs_fixed_gemv_async")
+            return keep
+        return run
+
+    def gemv(self, x: torch.Tensor, rows: int, cols: int, stream=None) -> torch.Tensor:
+        y = torch.empty(rows, dtype=torch.float32, device=self.dev.device)
+        self.gemv_into(y, x, rows, cols, stream=stream)
+        return y
+
     def block_status(self) -> np.ndarray:
         return self.status[: self.info.n_blocks].cpu().numpy().view(np.uint32)

@@ -15,6 +15,7 @@
 #include <algorithm>
 
 #include "bs_device.h"
+#include "bs_wave.h"
 
 using namespace bsd;
 
@@ -279,22 +280,6 @@ __device__ __forceinline__ void unit_open(const DecodeArgs& a, const RecDev& r, 
 // matching x (packed BF16 pairs, v_dot2 with fp32 accumulation), the wave
 // sums the products per row (DPP steps, no LDS), and lane 0 adds the sums
 // into y.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// sum of v over the wave, in lane 63: quad, row and row-broadcast DPP steps
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-#define BS_DPP_ADD(ctrl, rows) \
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, rows, 0xF, false))
-    BS_DPP_ADD(0xB1, 0xF);    // quad_perm [1,0,3,2]
-    BS_DPP_ADD(0x4E, 0xF);    // quad_perm [2,3,0,1]
-    BS_DPP_ADD(0x124, 0xF);   // row_ror:4
-    BS_DPP_ADD(0x128, 0xF);   // row_ror:8: every lane holds its row's sum
-    BS_DPP_ADD(0x142, 0xA);   // row_bcast:15 into rows 1 and 3
-    BS_DPP_ADD(0x143, 0xC);   // row_bcast:31 into rows 2 and 3
-#undef BS_DPP_ADD
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
 __device__ __forceinline__ void gemv_group(const DecodeArgs& a, const uint32_t (&o)[4], uint32_t cnt, uint64_t row0,
                                            uint32_t c0, uint32_t lane) {
     const uint32_t cols = (uint32_t)a.gcols;

@@ -1,5 +1,5 @@
 // bs_fixed.cpp -- the fixed-width lane-stream form: host transcoder, header
-// validation and the decode entry point.
+// validation, and the decode and fused matrix-vector product entry points.
 //
 // The form is derived once from a BF16 tensor (the canonical container's
 // decode) and read by a kernel without any sequential chain [NVLC card,
@@ -55,6 +55,41 @@ void pack_block(const uint16_t* w, uint64_t n, uint64_t blk, const uint8_t* code
         for (uint32_t k = 0; k < 4; k++) wr32(base + 4 * (64 * k + l), cw[k]);
         for (uint32_t k = 0; k < 7; k++) wr32(base + 1024 + 4 * (64 * k + l), fr[k]);
     }
+}
+
+bool info_consistent(const bs_fixed_info* info) {
+    if (info->n_blocks != fixed_blocks(info->n) || info->esc_off != fixed_esc_off(info->n_blocks) ||
+        info->n_esc > 0xFFFFFFFFull || info->bytes < info->esc_off + 2 * info->n_esc) {
+        set_error("bs_fixed_info not from bs_fixed_info_get");
+        return false;
+    }
+    for (uint32_t k = 0; k < 16; k++)
+        if (info->table[k] > 511 || (k == 15 && info->table[k])) { set_error("bad symbol table"); return false; }
+    return true;
+}
+
+// kernel arguments common to the decode and the product
+bs_status fixed_args(const bs_fixed_info* info, const void* d_blob, bsd::FixedArgs& a) {
+    if (!info || !d_blob) { set_error("NULL argument"); return BS_E_INVAL; }
+    if ((uintptr_t)d_blob & 15) { set_error("blob must be 16-B aligned"); return BS_E_INVAL; }
+    if (!info_consistent(info)) return BS_E_INVAL;
+    memset(&a, 0, sizeof a);
+    a.blob = (const uint8_t*)d_blob;
+    a.n = info->n;
+    a.n_blocks = info->n_blocks;
+    a.n_esc = info->n_esc;
+    a.esc_off = info->esc_off;
+    for (uint32_t k = 0; k < 15; k++) a.tab[k / 2] |= (uint32_t)info->table[k] << (16 * (k % 2));
+    return BS_OK;
+}
+
+// one wave per work item (a block, or a unit of rows) up to 16 workgroups per
+// CU; beyond, waves stride
+uint32_t fixed_groups(uint64_t items) {
+    int cus = 0;
+    if (bsk_device_cus(&cus) != 0 || cus <= 0) cus = 256;
+    const uint64_t want = (items + bsd::kFixWaves - 1) / bsd::kFixWaves;
+    return (uint32_t)std::min<uint64_t>(want, 16ull * (uint64_t)cus);
 }
 
 }  // namespace
@@ -152,36 +187,56 @@ bs_status bs_fixed_info_get(const void* h_header, uint64_t header_len, uint64_t 
 bs_status bs_fixed_decode_async(const bs_fixed_info* info, const void* d_blob, void* d_out, uint64_t out_capacity,
                                 uint32_t* d_status, void* stream) {
     if (!info || !d_blob || (!d_out && info->n)) { set_error("NULL argument"); return BS_E_INVAL; }
-    if (((uintptr_t)d_blob | (uintptr_t)d_out) & 15) { set_error("blob and output must be 16-B aligned"); return BS_E_INVAL; }
-    if (info->n_blocks != fixed_blocks(info->n) || info->esc_off != fixed_esc_off(info->n_blocks) ||
-        info->n_esc > 0xFFFFFFFFull || info->bytes < info->esc_off + 2 * info->n_esc) {
-        set_error("bs_fixed_info not from bs_fixed_info_get");
-        return BS_E_INVAL;
-    }
+    if ((uintptr_t)d_out & 15) { set_error("output must be 16-B aligned"); return BS_E_INVAL; }
+    if (!info_consistent(info)) return BS_E_INVAL;
     if (out_capacity < 2 * info->n) { set_error("output capacity %llu < %llu", (unsigned long long)out_capacity,
                                                 (unsigned long long)(2 * info->n));
         return BS_E_NOSPACE; }
     if (info->n == 0) return BS_OK;
     bsd::FixedArgs a;
-    memset(&a, 0, sizeof a);
-    a.blob = (const uint8_t*)d_blob;
+    const bs_status rc = fixed_args(info, d_blob, a);
+    if (rc != BS_OK) return rc;
     a.out = (uint16_t*)d_out;
     a.status = d_status;
-    a.n = info->n;
-    a.n_blocks = info->n_blocks;
-    a.n_esc = info->n_esc;
-    a.esc_off = info->esc_off;
-    for (uint32_t k = 0; k < 15; k++) {
-        if (info->table[k] > 511) { set_error("bad symbol table"); return BS_E_INVAL; }
-        a.tab[k / 2] |= (uint32_t)info->table[k] << (16 * (k % 2));
+    const int e = bsk_fixed_decode(&a, fixed_groups(info->n_blocks), stream);
+    if (e != 0) { set_error("fixed decode launch: %s", hipGetErrorString((hipError_t)e)); return BS_E_HIP; }
+    return BS_OK;
+}
+
+bs_status bs_fixed_gemv_async(const bs_fixed_info* info, const void* d_blob, uint64_t rows, uint64_t cols,
+                              const void* d_x, float* d_y, uint32_t* d_status, void* stream) {
+    bsd::FixedArgs a;
+    const bs_status rc = fixed_args(info, d_blob, a);
+    if (rc != BS_OK) return rc;
+    if (!d_x || !d_y) { set_error("NULL argument"); return BS_E_INVAL; }
+    if (cols == 0 || cols % 32 || cols >= (1ull << 26) || rows * cols != info->n || rows > info->n) {
+        set_error("a %llu x %llu matrix does not fit %llu weights with columns a multiple of 32 below 2^26",
+                  (unsigned long long)rows, (unsigned long long)cols, (unsigned long long)info->n);
+        return BS_E_INVAL;
     }
+    if ((uintptr_t)d_x & 15) { set_error("x must be 16-B aligned"); return BS_E_INVAL; }
+    a.status = d_status;
+    a.gx = (const uint16_t*)d_x;
+    a.gy = d_y;
+    a.rows = rows;
+    a.cols = (uint32_t)cols;
+    // units of rows that end on a block boundary (lcm(cols, 2048) weights),
+    // grouped so that a workgroup gets about one block per wave and at most
+    // 64 rows
+    uint64_t g = bsd::kFixBlockW, c = cols;
+    while (c) { const uint64_t r = g % c; g = c; c = r; }
+    a.unit_rows = (uint32_t)(bsd::kFixBlockW / g);
+    a.unit_blocks = (uint32_t)(cols / g);
+    a.group_units = std::max<uint32_t>(1, std::min<uint32_t>(bsd::kFixWaves / a.unit_blocks, 64 / a.unit_rows));
+    const uint64_t grows = (uint64_t)a.unit_rows * a.group_units;
+    a.n_groups = (rows + grows - 1) / grows;
+    a.q_step = (uint32_t)(bsd::kFixWaves * bsd::kFixBlockW / cols);
+    a.r_step = (uint32_t)(bsd::kFixWaves * bsd::kFixBlockW % cols);
     int cus = 0;
     if (bsk_device_cus(&cus) != 0 || cus <= 0) cus = 256;
-    // one wave per block up to 8 workgroups per CU; beyond, waves stride
-    const uint64_t want = (info->n_blocks + bsd::kFixWaves - 1) / bsd::kFixWaves;
-    const uint32_t groups = (uint32_t)std::min<uint64_t>(want, 8ull * (uint64_t)cus);
-    const int e = bsk_fixed_decode(&a, groups, stream);
-    if (e != 0) { set_error("fixed decode launch: %s", hipGetErrorString((hipError_t)e)); return BS_E_HIP; }
+    const uint32_t groups = (uint32_t)std::min<uint64_t>(a.n_groups, 16ull * (uint64_t)cus);
+    const int e = bsk_fixed_gemv(&a, groups, stream);
+    if (e != 0) { set_error("fixed product launch: %s", hipGetErrorString((hipError_t)e)); return BS_E_HIP; }
     return BS_OK;
 }
 

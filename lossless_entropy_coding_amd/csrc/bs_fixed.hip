@@ -1,11 +1,14 @@
-// bs_fixed.hip -- decode of the fixed-width lane-stream form (gfx950).
+// bs_fixed.hip -- kernels of the fixed-width lane-stream form (gfx950):
+// decode, and decode fused with a matrix-vector product.
 //
 // The form keeps every weight as an 11-bit code word (a 4-bit symbol code,
 // 15 = escape, and the exact 7-bit fraction) in 2048-weight blocks of 64
 // lanes [NVLC card, runtime paragraphs: the GPU runtime decodes fixed-width,
-// lane-oriented streams derived once from the canonical model; the layout is
-// the library's own and is given in bs.h].  Nothing in a block depends on
-// another block, so the decode is a plain data-parallel pass:
+// lane-oriented streams derived once from the canonical model, and its
+// compressed-only runtime multiplies with weights decoded where they are
+// used; the layout is the library's own and is given in bs.h].  Nothing in a
+// block depends on another block, so both kernels are plain data-parallel
+// passes:
 //   - one wavefront takes a block: each lane loads its 4 code dwords and 7
 //     fraction dwords, every load instruction covering 256 contiguous bytes;
 //   - a 256-entry LDS table maps a code byte (two weights) to both symbols
@@ -13,18 +16,27 @@
 //     two fractions are inserted with a shift and masks;
 //   - the lane's 16 output dwords go to a per-wave LDS block (its four 16-B
 //     pieces rotated by lane pair, so the writes of a wave spread over all
-//     banks), escaped symbols are OR-ed in there, and the block leaves LDS as
-//     16-B stores that cover 1 KiB of contiguous output per instruction;
+//     banks) and escaped symbols are OR-ed in there;
 //   - escapes: the block's range of the escape list (from the per-block
 //     offsets) is staged in LDS while the planes load; a lane's escapes
 //     start at the wave's exclusive prefix of its escape count, and an
-//     escape's rank among the lane's follows from the codes below it.
+//     escape's rank among the lane's follows from the codes below it;
+//   - decode: the block leaves LDS as 16-B non-temporal stores, 1 KiB of
+//     contiguous output per instruction (the output is not read again by
+//     this kernel, so it bypasses the caches' normal allocation);
+//   - product: a workgroup owns whole rows (groups of rows that end on a
+//     block boundary) and deals their blocks to its waves; each lane reads
+//     its own 32 patched weights back and multiplies them with x (packed BF16
+//     pairs, v_dot2 with fp32 accumulation), the waves sum per row (DPP
+//     steps, then LDS), and the workgroup stores its rows' totals.  Nothing
+//     is written but y, and no atomics are used.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <algorithm>
 
 #include "bs_device.h"
+#include "bs_wave.h"
 
 using namespace bsd;
 
@@ -56,97 +68,143 @@ __device__ __forceinline__ uint32_t wave_prefix(uint32_t v, uint32_t& total) {
 // LDS executes a wave's instructions in order, so no wait is needed)
 __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
-__global__ __launch_bounds__(64 * kFixWaves) void fixed_decode_kernel(FixedArgs a) {
+// A block's loaded data: the lane's code and fraction dwords, its share of
+// the block's first escapes (two dwords, up to 254 escapes for the wave) and
+// the block's escape range.
+struct BlockIn {
+    uint32_t c[4], f[7];
+    uint32_t ev0, ev1;
+    uint64_t eb0;           // the block's first escape (0 when its range is bad)
+    uint32_t cnt;           // escapes in its range
+    uint32_t bad;
+};
+
+// Issue the loads of block blk (nothing waits for them here).
+__device__ __forceinline__ BlockIn load_block(const FixedArgs& a, uint64_t blk, uint32_t lane) {
+    BlockIn b;
+    const uint32_t* plane = (const uint32_t*)(a.blob + kFixHeader + (uint64_t)kFixBlockBytes * blk) + lane;
+#pragma unroll
+    for (int k = 0; k < 4; k++) b.c[k] = plane[64 * k];
+#pragma unroll
+    for (int k = 0; k < 7; k++) b.f[k] = plane[256 + 64 * k];
+    const uint32_t* offs = (const uint32_t*)(a.blob + kFixHeader + (uint64_t)kFixBlockBytes * a.n_blocks);
+    const uint64_t e0 = offs[blk];
+    const uint64_t e1 = blk + 1 < a.n_blocks ? (uint64_t)offs[blk + 1] : a.n_esc;
+    b.bad = 0;
+    b.cnt = 0;
+    if (e0 <= e1 && e1 <= a.n_esc) b.cnt = (uint32_t)std::min<uint64_t>(e1 - e0, kFixBlockW + 1);
+    else b.bad = 2u;
+    b.eb0 = b.bad ? 0 : e0;
+    // dwords from the one holding escape eb0 (the escape list is 4-B aligned
+    // and padded, so the dword holding the last escape is inside the blob)
+    const uint32_t* ew = (const uint32_t*)(a.blob + a.esc_off) + (b.eb0 >> 1);
+    const uint32_t ndw = (std::min<uint32_t>(b.cnt, kFixEscLds - 2) + (uint32_t)(b.eb0 & 1) + 1) >> 1;
+    b.ev0 = b.ev1 = 0;
+    if (ndw) {
+        b.ev0 = ew[std::min(lane, ndw - 1)];
+        b.ev1 = ew[std::min(lane + 64, ndw - 1)];
+    }
+    return b;
+}
+
+// Decode a loaded block into the wave's LDS block st (lane l's 32 weights at
+// dwords 16 l .. 16 l + 15, 16-B piece k at slot (k + l / 2) mod 4); returns
+// the block's status bits (this lane's view).  el: the wave's escape staging.
+__device__ __forceinline__ uint32_t finish_block(const FixedArgs& a, const BlockIn& b, uint32_t lane,
+                                                 const uint32_t* lut, uint32_t* st, uint16_t* el) {
+    uint32_t bad = b.bad;
+    const uint32_t cnt = b.cnt;
+    // escape eb0 + r is LDS half-word sh + r for r < lim, else read from HBM
+    const uint16_t* eb = (const uint16_t*)(a.blob + a.esc_off) + b.eb0;
+    const uint32_t* ew = (const uint32_t*)(a.blob + a.esc_off) + (b.eb0 >> 1);
+    const uint32_t sh = (uint32_t)(b.eb0 & 1);
+    const uint32_t lim = std::min<uint32_t>(cnt, kFixEscLds - 2);
+    const uint32_t ndw = (lim + sh + 1) >> 1;
+
+    // escapes in the lane's codes: bit 4 i + k of m <-> weight 8 k + i of the lane
+    const uint32_t m =
+        nibbles_15(b.c[0]) | nibbles_15(b.c[1]) << 1 | nibbles_15(b.c[2]) << 2 | nibbles_15(b.c[3]) << 3;
+    uint32_t total;
+    const uint32_t pre = wave_prefix((uint32_t)__builtin_popcount(m), total);
+    if (total != cnt) bad |= 1u;
+
+    // symbols and fractions, two weights per dword
+    uint32_t o[16];
+#pragma unroll
+    for (int p = 0; p < 16; p++) {
+        const uint32_t sy = lut[(b.c[p >> 2] >> (8 * (p & 3))) & 0xFFu];
+        const int q = (14 * p) >> 5, r = (14 * p) & 31;
+        const uint32_t w = r <= 18 ? b.f[q] >> r : __builtin_amdgcn_alignbit(b.f[q + 1], b.f[q], r);
+        o[p] = sy | (w & 0x7Fu) | ((w << 9) & 0x7F0000u);
+    }
+    uint32_t* el32 = (uint32_t*)el;
+    if (lane < ndw) el32[lane] = b.ev0;
+    if (lane + 64 < ndw) el32[lane + 64] = b.ev1;
+    for (uint32_t u = 2; 64 * u < ndw; u++)          // blocks with more escapes (rare)
+        if (lane + 64 * u < ndw) el32[lane + 64 * u] = ew[lane + 64 * u];
+    const uint32_t rot = lane >> 1;
+#pragma unroll
+    for (uint32_t k = 0; k < 4; k++)
+        *(v4u*)(st + 16 * lane + 4 * ((k + rot) & 3u)) = v4u{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+    wave_lds_fence();
+
+    // escaped symbols: the rank of an escape among the lane's is the count
+    // of the lane's escapes at lower weights
+    for (uint32_t left = m; left;) {
+        const uint32_t bit = __builtin_ctz(left);
+        left &= left - 1;
+        const uint32_t k = bit & 3u, i = bit >> 2;
+        const uint32_t km = 0x11111111u << k;
+        const uint32_t below = (km - 0x11111111u) | (km & ((1u << (4 * i)) - 1u));
+        const uint32_t r = pre + (uint32_t)__builtin_popcount(m & below);
+        uint32_t s = 0;
+        if (r < lim) s = el[sh + r];
+        else if (r < cnt) s = eb[r];
+        if (r >= cnt) bad |= 1u;
+        if (s > 511u) { bad |= 4u; s = 0; }
+        atomicOr(st + 16 * lane + 4 * ((k + rot) & 3u) + (i >> 1), s << (7 + 16 * (i & 1u)));
+    }
+    wave_lds_fence();
+    return bad;
+}
+
+__device__ __forceinline__ void write_status(const FixedArgs& a, uint64_t blk, uint32_t bad, uint32_t lane) {
+    if (!a.status) return;
+    uint32_t any = 0;
+#pragma unroll
+    for (uint32_t bit = 0; bit < 3; bit++)
+        if (__builtin_amdgcn_ballot_w64((bad >> bit) & 1u)) any |= 1u << bit;
+    if (lane == 0) a.status[blk] = any;
+}
+
+// the 256-entry pair table: entry b = both symbols of code byte b in place
+__device__ __forceinline__ void build_lut(const FixedArgs& a, uint32_t t, uint32_t* lut) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < 15; k++) {
+        const uint32_t sym = (a.tab[k >> 1] >> (16 * (k & 1))) & 511u;
+        lo = (t & 15u) == k ? sym : lo;
+        hi = (t >> 4) == k ? sym : hi;
+    }
+    lut[t] = (lo << 7) | (hi << 23);
+}
+
+// decode: one wave per block at a time, out written with 16-B stores
+__global__ __launch_bounds__(64 * kFixWaves, 8) void fixed_decode_kernel(FixedArgs a) {
     __shared__ uint32_t lut[256];
     __shared__ __attribute__((aligned(16))) uint32_t stage[kFixWaves][kFixBlockW / 2];
-    __shared__ uint16_t escl[kFixWaves][kFixEscLds];
+    __shared__ __attribute__((aligned(4))) uint16_t escl[kFixWaves][kFixEscLds];
 
     const uint32_t t = threadIdx.x, lane = t & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (uint32_t k = 0; k < 15; k++) {
-            const uint32_t sym = (a.tab[k >> 1] >> (16 * (k & 1))) & 511u;
-            lo = (t & 15u) == k ? sym : lo;
-            hi = (t >> 4) == k ? sym : hi;
-        }
-        lut[t] = (lo << 7) | (hi << 23);
-    }
+    build_lut(a, t, lut);
     __syncthreads();
 
     uint32_t* st = stage[wave];
     uint16_t* el = escl[wave];
-    const uint32_t* offs = (const uint32_t*)(a.blob + kFixHeader + (uint64_t)kFixBlockBytes * a.n_blocks);
-    const uint16_t* esc = (const uint16_t*)(a.blob + a.esc_off);
-    const uint32_t rot = lane >> 1;
-
     for (uint64_t blk = (uint64_t)blockIdx.x * kFixWaves + wave; blk < a.n_blocks;
          blk += (uint64_t)gridDim.x * kFixWaves) {
-        const uint32_t* plane = (const uint32_t*)(a.blob + kFixHeader + (uint64_t)kFixBlockBytes * blk) + lane;
-        uint32_t c[4], f[7];
-#pragma unroll
-        for (int k = 0; k < 4; k++) c[k] = plane[64 * k];
-#pragma unroll
-        for (int k = 0; k < 7; k++) f[k] = plane[256 + 64 * k];
-
-        // the block's escape range, staged in LDS (its first kFixEscLds)
-        const uint64_t e0 = offs[blk];
-        const uint64_t e1 = blk + 1 < a.n_blocks ? (uint64_t)offs[blk + 1] : a.n_esc;
-        uint32_t bad = 0;
-        uint32_t cnt = 0;
-        if (e0 <= e1 && e1 <= a.n_esc) cnt = (uint32_t)std::min<uint64_t>(e1 - e0, kFixBlockW + 1);
-        else bad |= 2u;
-        const uint16_t* eb = esc + (bad ? 0 : e0);
-        const uint32_t lim = std::min<uint32_t>(cnt, kFixEscLds);
-        uint32_t ev[kFixEscLds / 64];
-#pragma unroll
-        for (uint32_t u = 0; u < kFixEscLds / 64; u++) {
-            ev[u] = 0;
-            if (64 * u < lim && lane + 64 * u < lim) ev[u] = eb[lane + 64 * u];
-        }
-
-        // escapes in the lane's codes: bit 4 i + k of m <-> weight 8 k + i of the lane
-        const uint32_t m = nibbles_15(c[0]) | nibbles_15(c[1]) << 1 | nibbles_15(c[2]) << 2 | nibbles_15(c[3]) << 3;
-        uint32_t total;
-        const uint32_t pre = wave_prefix((uint32_t)__builtin_popcount(m), total);
-        if (total != cnt) bad |= 1u;
-
-        // symbols and fractions, two weights per dword
-        uint32_t o[16];
-#pragma unroll
-        for (int p = 0; p < 16; p++) {
-            const uint32_t sy = lut[(c[p >> 2] >> (8 * (p & 3))) & 0xFFu];
-            const int q = (14 * p) >> 5, r = (14 * p) & 31;
-            const uint32_t w = r <= 18 ? f[q] >> r : __builtin_amdgcn_alignbit(f[q + 1], f[q], r);
-            o[p] = sy | (w & 0x7Fu) | ((w << 9) & 0x7F0000u);
-        }
-#pragma unroll
-        for (int u = 0; u < kFixEscLds / 64; u++)
-            if (64 * u < lim && lane + 64 * u < lim) el[lane + 64 * u] = (uint16_t)ev[u];
-#pragma unroll
-        for (uint32_t k = 0; k < 4; k++)
-            *(v4u*)(st + 16 * lane + 4 * ((k + rot) & 3u)) = v4u{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
-        wave_lds_fence();
-
-        // escaped symbols: the rank of an escape among the lane's is the count
-        // of the lane's escapes at lower weights
-        for (uint32_t left = m; left;) {
-            const uint32_t b = __builtin_ctz(left);
-            left &= left - 1;
-            const uint32_t k = b & 3u, i = b >> 2;
-            const uint32_t km = 0x11111111u << k;
-            const uint32_t below = (km - 0x11111111u) | (km & ((1u << (4 * i)) - 1u));
-            const uint32_t r = pre + (uint32_t)__builtin_popcount(m & below);
-            uint32_t s = 0;
-            if (r < lim) s = el[r];
-            else if (r < cnt) s = eb[r];
-            if (r >= cnt) bad |= 1u;
-            if (s > 511u) { bad |= 4u; s = 0; }
-            atomicOr(st + 16 * lane + 4 * ((k + rot) & 3u) + (i >> 1), s << (7 + 16 * (i & 1u)));
-        }
-        wave_lds_fence();
-
+        const uint32_t bad = finish_block(a, load_block(a, blk, lane), lane, lut, st, el);
         // out: 16-B pieces in order, 1 KiB per store instruction; the last,
         // partial block word by word
         uint16_t* ob = a.out + blk * kFixBlockW;
@@ -155,7 +213,8 @@ __global__ __launch_bounds__(64 * kFixWaves) void fixed_decode_kernel(FixedArgs 
 #pragma unroll
             for (uint32_t u = 0; u < 4; u++) {
                 const uint32_t cc = 64 * u + lane, L = cc >> 2, pc = cc & 3u;
-                *(v4u*)(ob + 8 * cc) = *(const v4u*)(st + 16 * L + 4 * ((pc + (L >> 1)) & 3u));
+                const v4u v = *(const v4u*)(st + 16 * L + 4 * ((pc + (L >> 1)) & 3u));
+                __builtin_nontemporal_store(v, (v4u*)(ob + 8 * cc));
             }
         } else {
             const uint16_t* st16 = (const uint16_t*)st;
@@ -164,14 +223,84 @@ __global__ __launch_bounds__(64 * kFixWaves) void fixed_decode_kernel(FixedArgs 
                 ob[e] = st16[32 * L + 8 * (((wi >> 3) + (L >> 1)) & 3u) + (wi & 7u)];
             }
         }
-        if (a.status) {
-            uint32_t any = 0;
+        write_status(a, blk, bad, lane);
+    }
+}
+
+// The fused product: workgroup g takes row groups g, g + groups, ...: a
+// group is group_units units of whole rows (so it starts and ends on a block
+// boundary), its blocks dealt to the four waves in turn.  For each block,
+// each lane multiplies its 32 weights with x, the wave sums the lanes of each
+// row present (DPP steps) and lane 0 adds the sums to its wave's row totals
+// in LDS; at the end of the group the workgroup adds the four waves' totals
+// in wave order and stores them to y.  Every y[r] is summed in one fixed
+// order, so the result is the same on every run.
+__global__ __launch_bounds__(64 * kFixWaves) void fixed_gemv_kernel(FixedArgs a) {
+    __shared__ uint32_t lut[256];
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kFixWaves][kFixBlockW / 2];
+    __shared__ __attribute__((aligned(4))) uint16_t escl[kFixWaves][kFixEscLds];
+    __shared__ float rowsum[kFixWaves][64];
+
+    const uint32_t t = threadIdx.x, lane = t & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    build_lut(a, t, lut);
+
+    uint32_t* st = stage[wave];
+    uint16_t* el = escl[wave];
+    float* rs = rowsum[wave];
+    const uint32_t rot = lane >> 1;
+    const uint32_t grows = a.unit_rows * a.group_units;
+    const uint64_t gblocks = (uint64_t)a.unit_blocks * a.group_units;
+    // the lane's row in the group and column in the wave's first block (the
+    // group starts on a block), then advanced by kFixWaves blocks at a time
+    const uint32_t jr0 = wave * kFixBlockW + 32 * lane;
+    const uint32_t rr0 = jr0 / a.cols, cc0 = jr0 - rr0 * a.cols;
+    for (uint64_t g = blockIdx.x; g < a.n_groups; g += gridDim.x) {
+        const uint64_t ra = g * grows;
+        const uint32_t nrows = (uint32_t)std::min<uint64_t>(grows, a.rows - ra);
+        const uint64_t b0 = g * gblocks;
+        const uint32_t nblk = (uint32_t)((nrows * (uint64_t)a.cols + kFixBlockW - 1) / kFixBlockW);
+        __syncthreads();              // the previous group's totals have been read (and the table built)
+        rs[lane] = 0.f;
+        __syncthreads();
+        uint32_t rr = rr0, col = cc0;
+        for (uint32_t k = wave; k < nblk; k += kFixWaves) {
+            const uint64_t blk = b0 + k;
+            const bool live = rr < nrows;   // cols % 32 == 0 keeps a lane's 32 weights in one row
+            v4u xv[4] = {};
+            if (live) {
+                const v4u* xp = (const v4u*)(a.gx + col);
 #pragma unroll
-            for (uint32_t bit = 0; bit < 3; bit++)
-                if (__builtin_amdgcn_ballot_w64((bad >> bit) & 1u)) any |= 1u << bit;
-            if (lane == 0) a.status[blk] = any;
+                for (int q = 0; q < 4; q++) xv[q] = xp[q];
+            }
+            const uint32_t bad = finish_block(a, load_block(a, blk, lane), lane, lut, st, el);
+            float sum = 0.f;
+#pragma unroll
+            for (uint32_t q = 0; q < 4; q++) {
+                const v4u wv = *(const v4u*)(st + 16 * lane + 4 * ((q + rot) & 3u));
+                const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+                const uint32_t xd[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+#pragma unroll
+                for (int h = 0; h < 4; h++)
+                    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[h]),
+                                                          __builtin_bit_cast(bf16x2, xd[h]), sum, false);
+            }
+            if (!live) sum = 0.f;
+            // the block's rows, from lane 0's to the last live lane's
+            const uint32_t r_first = __builtin_amdgcn_readfirstlane(rr);
+            const uint32_t r_last = std::min<uint32_t>(__builtin_amdgcn_readlane(rr, 63), nrows - 1);
+            for (uint32_t q = r_first; q <= r_last; q++) {
+                const float s = wave_sum_dpp(rr == q ? sum : 0.f);
+                if (lane == 0) rs[q] += s;
+            }
+            write_status(a, blk, bad, lane);
+            wave_lds_fence();
+            col += a.r_step;
+            rr += a.q_step;
+            if (col >= a.cols) { col -= a.cols; rr++; }
         }
-        wave_lds_fence();
+        __syncthreads();
+        if (t < nrows) a.gy[ra + t] = ((rowsum[0][t] + rowsum[1][t]) + rowsum[2][t]) + rowsum[3][t];
     }
 }
 
@@ -180,5 +309,11 @@ __global__ __launch_bounds__(64 * kFixWaves) void fixed_decode_kernel(FixedArgs 
 extern "C" int bsk_fixed_decode(const FixedArgs* args, uint32_t n_groups, void* stream) {
     if (n_groups == 0 || args->n_blocks == 0) return 0;
     hipLaunchKernelGGL(fixed_decode_kernel, dim3(n_groups), dim3(64 * kFixWaves), 0, (hipStream_t)stream, *args);
+    return (int)hipGetLastError();
+}
+
+extern "C" int bsk_fixed_gemv(const FixedArgs* args, uint32_t n_groups, void* stream) {
+    if (n_groups == 0 || args->n_groups == 0) return 0;
+    hipLaunchKernelGGL(fixed_gemv_kernel, dim3(n_groups), dim3(64 * kFixWaves), 0, (hipStream_t)stream, *args);
     return (int)hipGetLastError();
 }

@@ -157,3 +157,69 @@ def test_fixed_argument_errors():
     plan.decode_into(out[:5000])
     torch.cuda.synchronize()
     assert (out[:5000].cpu().numpy().view(np.uint16) == words).all()
+
+
+# --------------------------------------------------------------------------- fused product
+def _as_f64(words: np.ndarray) -> np.ndarray:
+    return (words.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+GEMV_CASES = [
+    # (name, rows, cols): 4096 x 4096 (two blocks per row), ragged rows, blocks over two rows,
+    # many rows per block, a single row, the smallest width, and row units of 8, 64 and 2 rows
+    ("4096x4096", 4096, 4096), ("777x1024", 777, 1024), ("300x3584", 300, 3584), ("640x96", 640, 96),
+    ("1x8192", 1, 8192), ("3x32", 3, 32), ("129x2080", 129, 2080), ("33x18944", 33, 18944),
+    ("65x32", 65, 32), ("7x5120", 7, 5120),
+]
+
+
+@pytest.mark.parametrize("name,rows,cols", GEMV_CASES, ids=[c[0] for c in GEMV_CASES])
+def test_fixed_gemv_matches_fp64_product_of_oracle_decode(name, rows, cols):
+    """y = W x within the fp32 summation bound: along any path a product meets
+    at most 32 roundings in its lane (16 dot2 steps), 6 in the wave sum, one
+    per block of its row added to a wave's total (cols / 2048 + 2) and 3 where
+    the four waves' totals are added, so the error of row r is at most
+    (43 + cols / 2048) 2^-24 sum_c |W[r, c] x[c]|; the test allows twice that.
+    A row is summed by one workgroup in a fixed order, so two runs agree bit
+    for bit."""
+    say("fixed gemv", name)
+    rng = np.random.default_rng(rows * 31 + cols)
+    w = rng.standard_normal(rows * cols) * 0.02
+    w[rng.random(w.size) < 0.002] *= 80.0
+    w[rng.random(w.size) < 0.01] = 0.0
+    words = _bf16(w)
+    blob = codec.fixed_encode(words)
+    W64 = _as_f64(O.fixed_decode(blob)).reshape(rows, cols)
+    xw = _bf16(rng.standard_normal(cols))
+    x64 = _as_f64(xw)
+    y_ref = W64 @ x64
+    bound = 2 * (43 + cols / 2048) * 2.0 ** -24 * (np.abs(W64) @ np.abs(x64))
+    plan = codec.FixedPlan(blob)
+    x = torch.from_numpy(xw.view(np.int16).copy()).cuda()
+    ys = []
+    for rep in range(2):                     # y and the status words are rewritten each time
+        y = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+        plan.gemv_into(y, x, rows, cols)
+        torch.cuda.synchronize()
+        assert (plan.block_status() == 0).all()
+        ys.append(y.cpu().numpy())
+        err = np.abs(ys[-1].astype(np.float64) - y_ref)
+        assert np.all(err <= bound), (rep, float((err - bound).max()))
+    assert ys[0].tobytes() == ys[1].tobytes()
+
+
+def test_fixed_gemv_argument_errors():
+    words = _case_words("gauss", 64 * 1024, 11)
+    plan = codec.FixedPlan(codec.fixed_encode(words))
+    x = torch.zeros(2048, dtype=torch.int16, device="cuda")
+    for rows, cols in [(64, 1000), (100, 1024), (2048, 32 + 16), (0, 1024)]:
+        with pytest.raises(L.BSError) as e:
+            plan.gemv_into(torch.empty(max(rows, 1), dtype=torch.float32, device="cuda")[:rows],
+                           torch.zeros(cols, dtype=torch.int16, device="cuda"), rows, cols)
+        assert e.value.rc == L.BS_E_INVAL
+    with pytest.raises(L.BSError) as e:                      # misaligned x
+        plan.gemv_into(torch.empty(64, dtype=torch.float32, device="cuda"), x[1:1025], 64, 1024)
+    assert e.value.rc == L.BS_E_INVAL
+    y = plan.gemv(x[:1024], 64, 1024)
+    torch.cuda.synchronize()
+    assert float(y.abs().max()) == 0.0
