@@ -55,24 +55,32 @@ def parse():
     return ap.parse_args()
 
 
-def measured_traffic(job):
-    """HBM bytes per launch of the decode kernel on this workload, from the
-    committed rocprofv3 FETCH_SIZE / WRITE_SIZE passes (scaled by a plain-copy
-    calibration), or None when there is no pass for this workload or the
-    kernel source has changed since the counters were taken."""
+TRAFFIC_SOURCES = {"decode_kernel": ("bs_decode.hip", "bs_device.h"), "fixed": ("bs_fixed.hip", "bs_device.h")}
+
+
+def kernel_source_sha256(kind: str) -> str:
     import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    return hashlib.sha256(b"".join(open(os.path.join(root, "lossless_entropy_coding_amd", "csrc", n), "rb").read()
+                                   for n in TRAFFIC_SOURCES[kind])).hexdigest()
+
+
+def measured_traffic(key: str, kind: str = "decode_kernel"):
+    """HBM bytes per launch of a kernel on a workload, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE passes (scaled by a plain-copy
+    calibration), or None when there is no pass for this workload or the
+    kernel's source has changed since the counters were taken."""
     root = os.path.dirname(os.path.abspath(__file__))
     try:
         with open(os.path.join(root, "profiles", "hbm_traffic.json")) as f:
             rec = json.load(f)
-        src = b"".join(open(os.path.join(root, "lossless_entropy_coding_amd", "csrc", n), "rb").read()
-                       for n in ("bs_decode.hip", "bs_device.h"))
+        sha = kernel_source_sha256(kind)
     except OSError:
         return None
-    if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
+    w = rec.get("workloads", {}).get(key)
+    if w is None or w.get("kernel_source_sha256") != sha:
         return None
-    w = rec.get("workloads", {}).get(f"{job.name}|W={job.chunk_weights}|K={job.lanes}|P={job.stream_lanes}")
-    return None if w is None else int(w["traffic_bytes"])
+    return int(w["traffic_bytes"])
 
 
 def model_build_rate(job):
@@ -300,6 +308,8 @@ def fixed_bench(a):
             "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "dtype": "u32", "data": "synthetic",
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "fixed_decode_kernel",
+                         "traffic": measured_traffic(f"fixed|{job.name}", "fixed") if len(plans) == 1 else None,
+                         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                          "alg_bytes_per_step": alg, "launches_per_step": len(plans),
                          "avg_step_ms": round(dev_s * 1e3, 4)},
             "bits_per_weight": round(8 * blob_bytes / n, 4),
@@ -408,7 +418,7 @@ def main():
     # records: tables, index, states, words; verbatim spans) + the bytes written
     alg_bytes = job.read_bytes + out_bytes
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(job)
+    traffic = measured_traffic(f"{job.name}|W={job.chunk_weights}|K={job.lanes}|P={job.stream_lanes}")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",

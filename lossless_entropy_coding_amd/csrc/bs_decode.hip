@@ -21,6 +21,8 @@ using namespace bsd;
 
 namespace {
 
+typedef unsigned int v4o __attribute__((ext_vector_type(4)));   // 16 output bytes
+
 // ------------------------------------------------------------------ decode
 
 // Ring loads go through a buffer resource (gfx9 descriptor: raw 32-bit
@@ -412,8 +414,9 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
                 o[q][3] |= ((x[q] >> 14) & 127u) | ((x[q] >> 21) & 127u) << 16;
             }
             if (!V) {
-                uint4* op = (uint4*)out + (uint64_t)t * K + LB + 64 * q + lane;
-                *op = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
+                // non-temporal: the output is not read again by this kernel
+                v4o* op = (v4o*)out + (uint64_t)t * K + LB + 64 * q + lane;
+                __builtin_nontemporal_store(v4o{o[q][0], o[q][1], o[q][2], o[q][3]}, op);
             }
         }
         if (V) {
@@ -505,7 +508,7 @@ __device__ __forceinline__ void unit_decode(const DecodeArgs& a, const RecDev& r
             if (V) {
                 // below, after the R groups
             } else if (cnt[q] == 8) {
-                ((uint4*)out)[g16] = make_uint4(o[q][0], o[q][1], o[q][2], o[q][3]);
+                __builtin_nontemporal_store(v4o{o[q][0], o[q][1], o[q][2], o[q][3]}, (v4o*)out + g16);
             } else if (cnt[q] > 0) {
                 uint16_t* o16 = (uint16_t*)out + 8 * g16;
 #pragma unroll
