@@ -52,6 +52,11 @@ def parse():
     ap.add_argument("--fixed", action="store_true",
                     help="time the decode of the fixed-width lane-stream form (bs_fixed_decode_async) derived from "
                          "the workload's container, against the rANS decode of the same container")
+    ap.add_argument("--stream", action="store_true",
+                    help="stream the checkpoint's layers from pinned host memory under a device budget "
+                         "(bs_streamer_*), against copying the uncompressed layers")
+    ap.add_argument("--stream-layers", type=int, default=12, help="--stream: layers of the checkpoint to build")
+    ap.add_argument("--stream-slots", type=int, default=3, help="--stream: decoded layers the budget holds")
     return ap.parse_args()
 
 
@@ -321,6 +326,98 @@ def fixed_bench(a):
     print(json.dumps(line))
 
 
+def stream_bench(a):
+    """Layer streaming: the first --stream-layers layers of the synthetic
+    checkpoint (configuration 5's layer layout) are encoded, their containers
+    handed to a streamer (pinned host memory, a budget of --stream-slots
+    decoded layers plus two staging buffers), and one pass over the layers is
+    timed: acquire layer i, prefetch layer i + 1, release layer i.  The copy
+    of the next layer overlaps the decode of the current one.  The same pass
+    with the uncompressed layers (pinned host -> device copies of the BF16
+    bytes) is timed for comparison; both rates include the PCIe transfer."""
+    import torch
+    from lossless_entropy_coding_amd import codec, synth, workloads
+    layout = synth.cfg5_layout(layers=84)
+    containers, refs = [], []
+    t0 = time.time()
+    for layer in range(a.stream_layers):
+        wl = synth.cfg5_layer(layer, device="cuda", chunk_weights=65536, lanes=512, layout=layout)
+        wl.stream_lanes = 256
+        enc = workloads.encode_workload(wl, device="cuda", keep_reference=False, keep_device_reference=True)
+        containers.append(enc.container)
+        refs.append(enc.reference_device)
+        del wl
+    log(f"stream: {len(containers)} layers encoded in {time.time() - t0:.0f}s, "
+        f"{sum(map(len, containers)) / 1e9:.2f} GB compressed")
+    stream = torch.cuda.current_stream()
+    slot = max(r.numel() for r in refs)
+    slot = (slot + 255) // 256 * 256
+    staging = (max(map(len, containers)) + 255) // 256 * 256
+    budget = 2 * staging + a.stream_slots * slot
+    s = codec.Streamer(containers, budget)
+    torch.cuda.synchronize()
+
+    def one_pass():
+        n = len(containers)
+        s.prefetch(0, stream=stream)
+        for i in range(n):
+            s.acquire_ptr(i, stream=stream)
+            if i + 1 < n:
+                s.prefetch(i + 1, stream=stream)
+            s.release(i, stream=stream)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_s = time.perf_counter()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t_s, e0.elapsed_time(e1) * 1e-3
+
+    # warm-up pass, then check every layer against its original bytes
+    one_pass()
+    for i, ref in enumerate(refs):
+        v = s.acquire(i, stream=stream)
+        ok = torch.equal(v[: ref.numel()], ref)
+        s.release(i, stream=stream)
+        if not ok:
+            log(f"STREAMED LAYER {i} MISMATCH")
+            sys.exit(1)
+    before = s.stats()
+    walls = [timed(one_pass)[0] for _ in range(max(1, a.steps))]
+    after = s.stats()
+    wall = min(walls)
+    decoded = sum(r.numel() for r in refs)
+    compressed = sum(map(len, containers))
+    # the uncompressed layers streamed the same way: pinned host -> one device buffer per slot
+    host = [r.cpu().pin_memory() for r in refs]
+    dev = [torch.empty(slot, dtype=torch.uint8, device="cuda") for _ in range(a.stream_slots)]
+
+    def raw_pass():
+        for i, h in enumerate(host):
+            dev[i % len(dev)][: h.numel()].copy_(h, non_blocking=True)
+
+    raw_pass()
+    raw_wall = min(timed(raw_pass)[0] for _ in range(max(1, a.steps)))
+    line = {"metric": "layer streaming from pinned host memory: decoded BF16 GB/s delivered (PCIe-inclusive)",
+            "value": round(decoded / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+            "ms_per_pass": round(wall * 1e3, 2), "higher_is_better": True, "data": "synthetic",
+            "uncompressed_copy_GB_s": round(decoded / raw_wall / 1e9, 2),
+            "uncompressed_ms_per_pass": round(raw_wall * 1e3, 2),
+            "speedup_vs_uncompressed": round(raw_wall / wall, 3),
+            "compressed_h2d_GB_s": round(compressed / wall / 1e9, 2),
+            "bits_per_weight": round(8 * compressed / (decoded / 2), 4),
+            "streamer": {"slots": after["n_slots"], "slot_bytes": after["slot_bytes"],
+                         "staging_bytes": after["staging_bytes"], "plan_bytes": after["plan_bytes"],
+                         "vram_budget": budget, "misses_per_pass": (after["misses"] - before["misses"]) // len(walls),
+                         "hits_per_pass": (after["hits"] - before["hits"]) // len(walls)},
+            "config": {"workload": f"cfg5_checkpoint_first_{len(containers)}_layers", "bf16_bytes": decoded,
+                       "container_bytes": compressed}}
+    print(json.dumps(line))
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -348,6 +445,9 @@ def main():
         return
     if a.fixed:
         fixed_bench(a)
+        return
+    if a.stream:
+        stream_bench(a)
         return
     dev = "cuda"
     t0 = time.time()

@@ -211,6 +211,15 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
                          bs_plan** out);
 void bs_plan_destroy(bs_plan* plan);
 
+/* Point a plan at another device copy of the same container bytes (d_container,
+ * 16-B aligned), for containers that move between device buffers (the layer
+ * streamer below).  Work enqueued before the call keeps the old address.
+ * Errors: BS_E_INVAL. */
+bs_status bs_plan_rebind(bs_plan* plan, const void* d_container);
+
+/* Length in bytes of the plan's container. */
+uint64_t bs_plan_container_bytes(const bs_plan* plan);
+
 /* Decode records [first, first + count) into d_out, enqueued on `stream`
  * (no host synchronisation).  Record i is written at
  * d_out + out_offset(i) - out_offset(first); the bytes between records are not
@@ -325,6 +334,64 @@ uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count);
 /* Wavefronts per decode workgroup when the whole container is decoded (one
  * word stream of a chunk per wavefront at a time). */
 uint32_t bs_plan_waves_per_block(const bs_plan* plan);
+
+/* ------------------------------------------------------- layer streaming
+ *
+ * Layers streamed on demand under a budget of device memory [Gemma 2 9B
+ * Instruct -- Lossless Compressed card, "Low-VRAM streaming": layers are
+ * streamed on demand, with an LRU bound on the device memory they use].  A
+ * streamer keeps a model's containers (one per layer) in pinned host memory.
+ * A layer that is not resident is copied to a device staging buffer on the
+ * streamer's own copy stream (so the copy overlaps the caller's work) and
+ * decoded on the caller's stream into one of a fixed set of device slots,
+ * replacing the least recently used layer that is not acquired.  Every
+ * device buffer (slots, two staging buffers, one plan per layer) is
+ * allocated when the streamer is created; acquiring, prefetching and
+ * releasing allocate nothing.  Not thread-safe: one host thread drives a
+ * streamer. */
+typedef struct bs_streamer bs_streamer; /* opaque, library-owned */
+
+typedef struct {
+    uint32_t n_layers;
+    uint32_t n_slots;           /* decoded layers that fit the budget */
+    uint64_t slot_bytes;        /* the largest decoded layer, rounded to 256 B */
+    uint64_t staging_bytes;     /* each of the two staging buffers */
+    uint64_t plan_bytes;        /* device memory of the layers' plans (tables, descriptors) */
+    uint64_t hits, misses, evictions;
+    uint64_t h2d_bytes;         /* container bytes copied host -> device */
+} bs_streamer_stats;
+
+/* Create a streamer for n_layers containers (h_containers[i], lens[i] bytes;
+ * host memory, copied into the streamer's pinned memory).  vram_budget bounds
+ * the decoded slots plus the two staging buffers; at least two slots must
+ * fit.  Each layer's plan is built here (its container passes through a
+ * staging buffer once, on `stream`, which is synchronised).  Errors:
+ * BS_E_INVAL (NULL, no layers, budget below two slots), BS_E_FORMAT,
+ * BS_E_VERSION (a container), BS_E_NOMEM, BS_E_HIP. */
+bs_status bs_streamer_create(const void* const* h_containers, const uint64_t* lens, uint32_t n_layers,
+                             uint64_t vram_budget, void* stream, bs_streamer** out);
+void bs_streamer_destroy(bs_streamer* s);
+
+/* Make layer `layer` resident and acquired; *d_layer receives its decoded
+ * bytes (laid out as bs_decode_async of all its records), valid for work
+ * enqueued on `stream` after this call until bs_streamer_release.  A miss
+ * enqueues the copy on the copy stream and the decode on `stream`; a hit on a
+ * layer decoded on another stream makes `stream` wait for that decode.
+ * Errors: BS_E_INVAL (layer out of range), BS_E_NOSPACE (every slot is
+ * acquired), BS_E_HIP. */
+bs_status bs_streamer_acquire(bs_streamer* s, uint32_t layer, void* stream, void** d_layer);
+
+/* Release an acquired layer: work enqueued on `stream` before this call is
+ * the last that reads it, and its slot may be reused after that work.
+ * Errors: BS_E_INVAL (not acquired). */
+bs_status bs_streamer_release(bs_streamer* s, uint32_t layer, void* stream);
+
+/* Start making `layer` resident without acquiring it (copy on the copy
+ * stream, decode on `stream`): a later acquire finds it.  Errors as for
+ * acquire. */
+bs_status bs_streamer_prefetch(bs_streamer* s, uint32_t layer, void* stream);
+
+bs_status bs_streamer_get_stats(const bs_streamer* s, bs_streamer_stats* stats);
 
 /* ---------------------------------------------------------------- verify */
 

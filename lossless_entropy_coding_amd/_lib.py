@@ -68,6 +68,12 @@ class FixedInfo(C.Structure):
                 ("bytes", C.c_uint64), ("table", C.c_uint16 * 16)]
 
 
+class StreamerStats(C.Structure):
+    _fields_ = [("n_layers", C.c_uint32), ("n_slots", C.c_uint32), ("slot_bytes", C.c_uint64),
+                ("staging_bytes", C.c_uint64), ("plan_bytes", C.c_uint64), ("hits", C.c_uint64),
+                ("misses", C.c_uint64), ("evictions", C.c_uint64), ("h2d_bytes", C.c_uint64)]
+
+
 # every symbol declared in include/bs.h, with (restype, argtypes)
 SIGNATURES = {
     "bs_params_default": (None, [C.POINTER(Params)]),
@@ -84,6 +90,15 @@ SIGNATURES = {
     "bs_record_info_get": (C.c_int, [C.c_void_p, C.c_uint64, C.c_uint32, C.POINTER(RecordInfo)]),
     "bs_plan_create": (C.c_int, [C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p, C.POINTER(C.c_void_p)]),
     "bs_plan_destroy": (None, [C.c_void_p]),
+    "bs_plan_rebind": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "bs_plan_container_bytes": (C.c_uint64, [C.c_void_p]),
+    "bs_streamer_create": (C.c_int, [C.POINTER(C.c_void_p), C.POINTER(C.c_uint64), C.c_uint32, C.c_uint64, C.c_void_p,
+                                     C.POINTER(C.c_void_p)]),
+    "bs_streamer_destroy": (None, [C.c_void_p]),
+    "bs_streamer_acquire": (C.c_int, [C.c_void_p, C.c_uint32, C.c_void_p, C.POINTER(C.c_void_p)]),
+    "bs_streamer_release": (C.c_int, [C.c_void_p, C.c_uint32, C.c_void_p]),
+    "bs_streamer_prefetch": (C.c_int, [C.c_void_p, C.c_uint32, C.c_void_p]),
+    "bs_streamer_get_stats": (C.c_int, [C.c_void_p, C.POINTER(StreamerStats)]),
     "bs_decode_async": (C.c_int, [C.c_void_p, C.c_uint32, C.c_uint32, C.c_void_p, C.c_uint64, C.c_void_p,
                                   C.c_void_p]),
     "bs_plan_out_bytes": (C.c_uint64, [C.c_void_p, C.c_uint32, C.c_uint32]),

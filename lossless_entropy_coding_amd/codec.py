@@ -360,3 +360,59 @@ class FixedPlan:
 
     def block_status(self) -> np.ndarray:
         return self.status[: self.info.n_blocks].cpu().numpy().view(np.uint32)
+
+
+# --------------------------------------------------------------------------- layer streaming
+class Streamer:
+    """Layers streamed on demand under a device-memory budget (bs_streamer_*):
+    the containers live in the streamer's pinned host memory; acquire()
+    returns a uint8 view of the layer's decoded bytes in a device slot."""
+
+    def __init__(self, containers, vram_budget: int, stream=None):
+        n = len(containers)
+        self._keep = [bytes(c) for c in containers]
+        ptrs = (C.c_void_p * max(n, 1))(*[C.cast(C.c_char_p(c), C.c_void_p) for c in self._keep])
+        lens = (C.c_uint64 * max(n, 1))(*[len(c) for c in self._keep])
+        out = C.c_void_p()
+        L.check(L.lib().bs_streamer_create(ptrs, lens, n, vram_budget, C.c_void_p(_stream_handle(stream)),
+                                           C.byref(out)), "bs_streamer_create")
+        self.handle = out
+        self._keep = None                  # copied into pinned memory
+        self.out_bytes = [int(container_info(c).out_len) for c in containers]
+
+    def __del__(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            L.lib().bs_streamer_destroy(self.handle)
+            self.handle = C.c_void_p(0)
+
+    def acquire_ptr(self, layer: int, stream=None) -> int:
+        p = C.c_void_p()
+        L.check(L.lib().bs_streamer_acquire(self.handle, layer, C.c_void_p(_stream_handle(stream)), C.byref(p)),
+                "bs_streamer_acquire")
+        return int(p.value)
+
+    def acquire(self, layer: int, stream=None) -> torch.Tensor:
+        """The layer's decoded bytes (a view of its slot; valid until release)."""
+        ptr = self.acquire_ptr(layer, stream)
+        return _device_view(ptr, self.out_bytes[layer])
+
+    def release(self, layer: int, stream=None) -> None:
+        L.check(L.lib().bs_streamer_release(self.handle, layer, C.c_void_p(_stream_handle(stream))),
+                "bs_streamer_release")
+
+    def prefetch(self, layer: int, stream=None) -> None:
+        L.check(L.lib().bs_streamer_prefetch(self.handle, layer, C.c_void_p(_stream_handle(stream))),
+                "bs_streamer_prefetch")
+
+    def stats(self) -> dict:
+        st = L.StreamerStats()
+        L.check(L.lib().bs_streamer_get_stats(self.handle, C.byref(st)), "bs_streamer_get_stats")
+        return {k: getattr(st, k) for k, _ in L.StreamerStats._fields_}
+
+
+def _device_view(ptr: int, nbytes: int) -> torch.Tensor:
+    """A uint8 tensor over nbytes of library-owned device memory at ptr (no copy)."""
+    class _Mem:
+        __cuda_array_interface__ = {"shape": (nbytes,), "typestr": "|u1", "data": (ptr, False), "version": 3,
+                                    "strides": None}
+    return torch.as_tensor(_Mem(), device="cuda")

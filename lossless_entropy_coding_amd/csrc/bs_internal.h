@@ -82,6 +82,11 @@ struct Container {
     std::vector<Record> recs;
 };
 
+// Plan facts for other parts of the library (bs_plan.cpp).
+uint64_t plan_device_bytes(const bs_plan* plan);   // device memory the plan allocated
+uint64_t plan_status_words(const bs_plan* plan);   // status words a full decode writes
+uint32_t plan_records(const bs_plan* plan);
+
 // Validate h (len bytes) completely (header, directory, tables, chunk index
 // and payload bounds) and fill c.  Returns BS_OK or an error with a message.
 bs_status parse_container(const uint8_t* h, uint64_t len, Container& c);

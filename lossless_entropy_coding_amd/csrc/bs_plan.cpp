@@ -49,6 +49,7 @@ struct bs_plan {
     bsd::RawDev* d_raws = nullptr;
     uint8_t* d_luts = nullptr;
     unsigned long long* d_cmp = nullptr;   // compare results (2 words)
+    uint64_t device_bytes = 0;             // everything allocated above
 };
 
 namespace {
@@ -208,6 +209,7 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
     hipStream_t s = (hipStream_t)stream;
     auto up = [&](void** dst, const void* src, size_t bytes) -> hipError_t {
         hipError_t ee = hipMalloc(dst, std::max<size_t>(bytes, 16));
+        p->device_bytes += std::max<size_t>(bytes, 16);
         if (ee != hipSuccess || !bytes) return ee;
         return hipMemcpyAsync(*dst, src, bytes, hipMemcpyHostToDevice, s);
     };
@@ -220,6 +222,7 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
     if (e == hipSuccess) e = up((void**)&p->d_raws, p->raws.data(), p->raws.size() * sizeof(bsd::RawDev));
     if (e == hipSuccess) e = hipMalloc(&p->d_luts, std::max<uint64_t>(lut_bytes, 16));
     if (e == hipSuccess) e = hipMalloc(&p->d_cmp, 2 * sizeof(unsigned long long));
+    p->device_bytes += std::max<uint64_t>(lut_bytes, 16) + 2 * sizeof(unsigned long long);
     if (e == hipSuccess) e = (hipError_t)bsk_build_luts(p->d_container, p->d_recs, (uint32_t)recs.size(), p->d_luts, stream);
     // the host vectors passed to the copies above must outlive them
     if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -233,6 +236,25 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
 }
 
 void bs_plan_destroy(bs_plan* plan) { plan_free(plan); }
+
+bs_status bs_plan_rebind(bs_plan* plan, const void* d_container) {
+    if (!plan || !d_container) { set_error("NULL argument"); return BS_E_INVAL; }
+    if ((uintptr_t)d_container & 15) { set_error("device container must be 16-byte aligned"); return BS_E_INVAL; }
+    plan->d_container = (const uint8_t*)d_container;
+    return BS_OK;
+}
+
+uint64_t bs_plan_container_bytes(const bs_plan* plan) { return plan ? plan->len : 0; }
+
+}  // extern "C"
+
+namespace bs {
+uint64_t plan_device_bytes(const bs_plan* plan) { return plan ? plan->device_bytes : 0; }
+uint64_t plan_status_words(const bs_plan* plan) { return plan ? plan->c.n_streams : 0; }
+uint32_t plan_records(const bs_plan* plan) { return plan ? plan->c.n_records : 0; }
+}  // namespace bs
+
+extern "C" {
 
 uint32_t bs_plan_waves_per_block(const bs_plan* plan) {
     if (!plan) return 0;

@@ -261,3 +261,23 @@ def test_fixed_decode_argument_checks_before_launch():
     assert f(C.byref(forged), C.c_void_p(4096), C.c_void_p(4096), 10000, None, None) == L.BS_E_INVAL
     empty = codec.fixed_info(codec.fixed_encode(np.zeros(0, np.uint16)))
     assert f(C.byref(empty), C.c_void_p(4096), None, 0, None, None) == L.BS_OK     # nothing to do
+
+
+def test_streamer_argument_checks_before_any_device_call():
+    import ctypes as C
+    f = L.lib().bs_streamer_create
+    out = C.c_void_p()
+    assert f(None, None, 0, 1 << 30, None, C.byref(out)) == L.BS_E_INVAL
+    c = codec.encode([codec.bf16(_words(np.random.default_rng(1).standard_normal(5000) * 0.02))],
+                     codec.params(chunk_weights=4096, lanes=8))
+    bad = bytearray(c)
+    bad[0] ^= 0xFF
+    ptrs = (C.c_void_p * 1)(C.cast(C.c_char_p(bytes(bad)), C.c_void_p))
+    lens = (C.c_uint64 * 1)(len(bad))
+    assert f(ptrs, lens, 1, 1 << 30, None, C.byref(out)) == L.BS_E_FORMAT
+    ptrs = (C.c_void_p * 1)(C.cast(C.c_char_p(c), C.c_void_p))
+    lens = (C.c_uint64 * 1)(len(c))
+    assert f(ptrs, lens, 1, 1000, None, C.byref(out)) == L.BS_E_INVAL           # budget below two slots
+    assert L.lib().bs_streamer_acquire(None, 0, None, C.byref(out)) == L.BS_E_INVAL
+    assert L.lib().bs_streamer_release(None, 0, None) == L.BS_E_INVAL
+    assert L.lib().bs_plan_rebind(None, C.c_void_p(4096)) == L.BS_E_INVAL
