@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--fixed", action="store_true",
                     help="time the decode of the fixed-width lane-stream form (bs_fixed_decode_async) derived from "
                          "the workload's container, against the rANS decode of the same container")
+    ap.add_argument("--encode", action="store_true",
+                    help="time the GPU encoder (bs_encode_device_*) on the workload against the host encoder")
     ap.add_argument("--stream", action="store_true",
                     help="stream the checkpoint's layers from pinned host memory under a device budget "
                          "(bs_streamer_*), against copying the uncompressed layers")
@@ -326,6 +328,61 @@ def fixed_bench(a):
     print(json.dumps(line))
 
 
+def encode_bench(a):
+    """The workload's tensors encoded on the GPU (models from the HIP
+    histogram, streams coded on the device, container written to device
+    memory), end to end from device-resident words, against the host encoder
+    (host models, all host threads) from host-resident words.  Both produce the
+    same bytes; the check is part of the run."""
+    import hashlib
+    import torch
+    from lossless_entropy_coding_amd import codec, synth, workloads
+    wl = workloads.CONFIG_BUILDERS[a.config]("cuda")
+    p = codec.params(chunk_weights=a.chunk_weights or wl.chunk_weights, lanes=a.lanes or wl.lanes,
+                     stream_lanes=a.stream_lanes if a.stream_lanes is not None else wl.stream_lanes)
+    dev, host, digests = [], [], []
+    n_bf16 = 0
+    for it in wl.items:
+        if it.kind == "bf16":
+            t = synth.as_words(it.tensor).contiguous()
+            dev.append(("bf16", t))
+            h = t.cpu().numpy().view(np.uint16)
+            host.append(codec.bf16(h))
+            n_bf16 += t.numel()
+        else:
+            t = it.tensor.contiguous().view(torch.uint8).reshape(-1)
+            dev.append(("raw", t))
+            h = t.cpu().numpy()
+            host.append(codec.raw(h))
+        digests.append(hashlib.sha256(h.tobytes()).digest())
+    torch.cuda.synchronize()
+    codec.encode_device(dev[:1], p, digests=digests[:1])           # warm-up (module load, first launches)
+    torch.cuda.synchronize()
+    gpu_s = []
+    for _ in range(max(1, a.steps)):
+        t0 = time.perf_counter()
+        dc = codec.encode_device(dev, p, digests=digests)
+        torch.cuda.synchronize()
+        gpu_s.append(time.perf_counter() - t0)
+    t0 = time.perf_counter()
+    hc = codec.encode(host, p)
+    host_s = time.perf_counter() - t0
+    same = dc.cpu().numpy().tobytes() == hc
+    if not same:
+        log("DEVICE CONTAINER DIFFERS FROM THE HOST ENCODER'S")
+        sys.exit(1)
+    gs = min(gpu_s)
+    line = {"metric": "GPU encoder: BF16 GB/s encoded (device words to device container)",
+            "value": round(2 * n_bf16 / gs / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+            "s_per_encode": round(gs, 4), "higher_is_better": True, "data": "synthetic",
+            "host_encoder_GB_s": round(2 * n_bf16 / host_s / 1e9, 3), "host_encoder_s": round(host_s, 3),
+            "host_threads": os.cpu_count(), "speedup_vs_host": round(host_s / gs, 1),
+            "identical_bytes": same, "container_bytes": len(hc),
+            "config": {"workload": wl.name, "bf16_weights": n_bf16, "chunk_weights": p.chunk_weights, "lanes": p.lanes,
+                       "stream_lanes": p.stream_lanes}}
+    print(json.dumps(line))
+
+
 def stream_bench(a):
     """Layer streaming: the first --stream-layers layers of the synthetic
     checkpoint (configuration 5's layer layout) are encoded, their containers
@@ -448,6 +505,9 @@ def main():
         return
     if a.stream:
         stream_bench(a)
+        return
+    if a.encode:
+        encode_bench(a)
         return
     dev = "cuda"
     t0 = time.time()

@@ -159,6 +159,39 @@ typedef struct bs_blob bs_blob; /* opaque, library-owned byte buffer */
  * Errors: BS_E_INVAL (bad params, a model built for another n), BS_E_NOMEM. */
 bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_params* p, bs_blob** out);
 
+/* --------------------------------------------------------------- GPU encoder
+ *
+ * The container bs_encode_host writes, byte for byte, built from tensors in
+ * device memory: each record's word streams are coded on the GPU, one
+ * wavefront per stream, running the decode order backwards (the rANS coding
+ * step of the NVLC card's codec paragraph, in this library's chunk, lane and
+ * stream layout above).  Three calls: begin codes every stream into
+ * library-owned device scratch and lays the container out (it synchronises
+ * `stream` once, to read the streams' sizes back); size gives the container's
+ * length; finish writes the container into caller memory. */
+typedef struct {
+    uint32_t kind;              /* BS_KIND_BF16 or BS_KIND_RAW */
+    uint32_t reserved;
+    const void* d_data;         /* device: n 16-bit words (BF16, 16-B aligned) or n bytes (RAW) */
+    uint64_t n;
+    const bs_tables* tables;    /* NULL: built here with bs_build_tables */
+    const uint8_t* sha256;      /* 32 bytes, or NULL: computed from a host copy (slow) */
+} bs_dtensor;
+
+typedef struct bs_dencoder bs_dencoder; /* opaque, library-owned */
+
+/* Errors: BS_E_INVAL (bad params, kind, NULL or misaligned data, a model
+ * built for other data), BS_E_NOMEM, BS_E_HIP. */
+bs_status bs_encode_device_begin(const bs_dtensor* tensors, uint32_t n_tensors, const bs_params* p, void* stream,
+                                 bs_dencoder** out);
+uint64_t bs_encode_device_size(const bs_dencoder* e);
+/* Write the container (bs_encode_device_size bytes) to d_out (16-B aligned),
+ * enqueued on `stream`; the tensors must stay unchanged until it completes.
+ * Errors: BS_E_INVAL, BS_E_NOSPACE, BS_E_HIP. */
+bs_status bs_encode_device_finish(bs_dencoder* e, void* d_out, uint64_t capacity, void* stream);
+/* Waits for the encoder's work, then frees it. */
+void bs_encode_device_free(bs_dencoder* e);
+
 const void* bs_blob_data(const bs_blob* b);
 uint64_t bs_blob_size(const bs_blob* b);
 void bs_blob_free(bs_blob* b);

@@ -42,6 +42,11 @@ class Tensor(C.Structure):
                 ("tables", C.c_void_p), ("sha256", C.c_void_p)]
 
 
+class DTensor(C.Structure):
+    _fields_ = [("kind", C.c_uint32), ("reserved", C.c_uint32), ("d_data", C.c_void_p), ("n", C.c_uint64),
+                ("tables", C.c_void_p), ("sha256", C.c_void_p)]
+
+
 class ContainerInfo(C.Structure):
     _fields_ = [("version", C.c_uint32), ("n_records", C.c_uint32), ("total_len", C.c_uint64),
                 ("out_len", C.c_uint64), ("n_chunks", C.c_uint64), ("bf16_weights", C.c_uint64),
@@ -83,6 +88,11 @@ SIGNATURES = {
     "bs_tables_get": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(C.c_uint32),
                                 C.POINTER(C.c_uint32), C.POINTER(C.c_uint32), C.POINTER(C.c_uint64)]),
     "bs_encode_host": (C.c_int, [C.POINTER(Tensor), C.c_uint32, C.POINTER(Params), C.POINTER(C.c_void_p)]),
+    "bs_encode_device_begin": (C.c_int, [C.POINTER(DTensor), C.c_uint32, C.POINTER(Params), C.c_void_p,
+                                         C.POINTER(C.c_void_p)]),
+    "bs_encode_device_size": (C.c_uint64, [C.c_void_p]),
+    "bs_encode_device_finish": (C.c_int, [C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p]),
+    "bs_encode_device_free": (None, [C.c_void_p]),
     "bs_blob_data": (C.c_void_p, [C.c_void_p]),
     "bs_blob_size": (C.c_uint64, [C.c_void_p]),
     "bs_blob_free": (None, [C.c_void_p]),

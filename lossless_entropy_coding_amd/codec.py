@@ -126,6 +126,41 @@ def encode(tensors, p: L.Params | None = None) -> bytes:
         L.lib().bs_blob_free(blob)
 
 
+def encode_device(tensors, p: L.Params | None = None, stream=None, tables=None, digests=None) -> torch.Tensor:
+    """Encode device tensors into one container on the GPU (bs_encode_device_*):
+    tensors is a list of ("bf16", int16/bfloat16 cuda tensor) or ("raw", uint8
+    cuda tensor); tables an optional list of Tables (None entries are built on
+    the device); digests an optional list of 32-byte sha256 values (None: the
+    library hashes a host copy).  Returns the container as a uint8 cuda tensor."""
+    p = p or params()
+    n = len(tensors)
+    arr = (L.DTensor * max(n, 1))()
+    keep = []
+    for i, (kind, t) in enumerate(tensors):
+        t = t.contiguous()
+        keep.append(t)
+        arr[i].kind = L.KIND_BF16 if kind == "bf16" else L.KIND_RAW
+        arr[i].d_data = t.data_ptr() if t.numel() else None
+        arr[i].n = t.numel() if kind == "bf16" else t.numel() * t.element_size()
+        if tables is not None and tables[i] is not None:
+            arr[i].tables = tables[i].handle
+        if digests is not None and digests[i] is not None:
+            sb = C.create_string_buffer(bytes(digests[i]), 32)
+            keep.append(sb)
+            arr[i].sha256 = C.addressof(sb)
+    h = _stream_handle(stream)
+    enc = C.c_void_p()
+    L.check(L.lib().bs_encode_device_begin(arr, n, C.byref(p), C.c_void_p(h), C.byref(enc)), "bs_encode_device_begin")
+    try:
+        size = L.lib().bs_encode_device_size(enc)
+        out = torch.empty(max(size, 16), dtype=torch.uint8, device="cuda")
+        L.check(L.lib().bs_encode_device_finish(enc, C.c_void_p(out.data_ptr()), out.numel(), C.c_void_p(h)),
+                "bs_encode_device_finish")
+    finally:
+        L.lib().bs_encode_device_free(enc)
+    return out[:size]
+
+
 def container_info(container: bytes) -> L.ContainerInfo:
     info = L.ContainerInfo()
     L.check(L.lib().bs_container_info_get(container, len(container), C.byref(info)), "bs_container_info_get")

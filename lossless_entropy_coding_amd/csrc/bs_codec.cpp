@@ -605,3 +605,282 @@ const char* bs_last_error(void) { return last_error(); }
 const char* bs_version(void) { return "bs 1.0 (container version 1, gfx950)"; }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ GPU encoder
+//
+// The same container as bs_encode_host, built from tensors in device memory:
+// the models come from the HIP histogram (bs_build_tables) unless given, each
+// record's streams are coded by encode_kernel into scratch, the host reads
+// back the streams' word and state-bit counts and lays the container out
+// exactly as the host encoder does, and assemble_kernel writes the payloads.
+
+struct bs_dencoder {
+    struct Rec {
+        uint32_t kind = 0;
+        uint64_t n = 0;                 // weights (BF16) or bytes (RAW)
+        const uint8_t* d_data = nullptr;
+        uint8_t sha[32];
+        bs::Model model;
+        bs::EncModel em;
+        uint32_t W = 0, K = 0, S = 1, P = 1, n_chunks = 0;
+        std::vector<uint8_t> head;
+        uint64_t index_off = 0, stab_off = 0;
+        uint64_t rec_off = 0, rec_len = 0, out_off = 0;
+        uint64_t o_words = 0, o_states = 0, o_counts = 0, o_tab = 0, o_chunk = 0, o_start = 0, o_mu = 0;
+        std::vector<uint64_t> chunk_off;
+        std::vector<uint32_t> unit_start, unit_mu, counts;
+    };
+    std::vector<Rec> recs;
+    std::vector<uint8_t> top;           // header and directory
+    uint8_t* d_scratch = nullptr;
+    uint64_t total_len = 0;
+    hipEvent_t done = nullptr;
+};
+
+namespace {
+
+bs_status denc_hip(hipError_t e, const char* what) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return e == hipErrorOutOfMemory ? BS_E_NOMEM : BS_E_HIP;
+}
+
+void fill_enc_tab(const bs::EncModel& em, bsd::EncTabDev& t) {
+    memset(&t, 0, sizeof t);
+    for (uint32_t s = 0; s < 512; s++) {
+        t.s_qc[s] = em.s[s].q | em.s[s].cum << 16;
+        t.route[s] = em.route[s];
+    }
+    for (uint32_t k = 0; k <= bs::kMaxTables; k++)
+        for (uint32_t f = 0; f < 128; f++) t.f_qc[k * 128 + f] = em.f[k][f].q | em.f[k][f].cum << 16;
+}
+
+bsd::EncArgs enc_args(const bs_dencoder* e, const bs_dencoder::Rec& r) {
+    bsd::EncArgs a;
+    memset(&a, 0, sizeof a);
+    a.w = (const uint16_t*)r.d_data;
+    a.n = r.n;
+    a.W = r.W; a.K = r.K; a.S = r.S; a.P = r.P;
+    a.n_chunks = r.n_chunks; a.m_s = r.em.m_s; a.m_f = r.em.m_f;
+    a.tab = (const bsd::EncTabDev*)(e->d_scratch + r.o_tab);
+    a.words = (uint16_t*)(e->d_scratch + r.o_words);
+    a.states = (uint32_t*)(e->d_scratch + r.o_states);
+    a.counts = (uint32_t*)(e->d_scratch + r.o_counts);
+    a.chunk_off = (const uint64_t*)(e->d_scratch + r.o_chunk);
+    a.unit_start = (const uint32_t*)(e->d_scratch + r.o_start);
+    a.unit_mu = (const uint32_t*)(e->d_scratch + r.o_mu);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+bs_status bs_encode_device_begin(const bs_dtensor* tensors, uint32_t n_tensors, const bs_params* p, void* stream,
+                                 bs_dencoder** out) {
+    if (!out || (!tensors && n_tensors)) { set_error("NULL argument"); return BS_E_INVAL; }
+    *out = nullptr;
+    if (!params_ok(p)) return BS_E_INVAL;
+    hipStream_t hs = (hipStream_t)stream;
+    bs_dencoder* e = new (std::nothrow) bs_dencoder();
+    if (!e) return BS_E_NOMEM;
+    auto fail = [&](bs_status rc) { bs_encode_device_free(e); return rc; };
+    try {
+        e->recs.resize(n_tensors);
+        uint64_t scratch = 0;
+        auto take = [&](uint64_t bytes) { const uint64_t o = scratch; scratch = align_up(scratch + bytes, 256); return o; };
+        for (uint32_t i = 0; i < n_tensors; i++) {
+            const bs_dtensor& t = tensors[i];
+            bs_dencoder::Rec& r = e->recs[i];
+            r.kind = t.kind;
+            r.n = t.n;
+            r.d_data = (const uint8_t*)t.d_data;
+            if ((t.kind != BS_KIND_BF16 && t.kind != BS_KIND_RAW) || (!t.d_data && t.n)) {
+                set_error("tensor %u: bad kind or NULL data", i);
+                return fail(BS_E_INVAL);
+            }
+            if (t.kind == BS_KIND_BF16 && ((uintptr_t)t.d_data & 15)) {
+                set_error("tensor %u: BF16 data must be 16-B aligned", i);
+                return fail(BS_E_INVAL);
+            }
+            const uint64_t nbytes = t.kind == BS_KIND_BF16 ? 2 * t.n : t.n;
+            if (t.sha256) {
+                memcpy(r.sha, t.sha256, 32);
+            } else {                     // digest of a host copy (slow path)
+                std::vector<uint8_t> h(nbytes);
+                hipError_t he = nbytes ? hipMemcpy(h.data(), t.d_data, nbytes, hipMemcpyDeviceToHost) : hipSuccess;
+                if (he != hipSuccess) return fail(denc_hip(he, "digest copy"));
+                sha256(h.data(), nbytes, r.sha);
+            }
+            if (t.kind == BS_KIND_RAW) continue;
+            if (t.tables) {
+                if (t.tables->n != t.n || t.tables->m_s != p->m_s || t.tables->m_f != p->m_f) {
+                    set_error("tensor %u: model was built for other data or parameters", i);
+                    return fail(BS_E_INVAL);
+                }
+                r.model = *t.tables;
+            } else {
+                bs_tables* tb = nullptr;
+                const bs_status rc = bs_build_tables(t.d_data, t.n, p, stream, &tb);
+                if (rc) return fail(rc);
+                r.model = *tb;
+                bs_tables_free(tb);
+            }
+            if (r.model.n_sym > kMaxSyms) {      // stored verbatim, as the host encoder does
+                r.kind = BS_KIND_RAW;
+                r.n = 2 * t.n;
+                continue;
+            }
+            record_shape(t.n, p->chunk_weights, p->lanes, r.W, r.K);
+            r.P = p->stream_lanes ? std::min(p->stream_lanes, r.K) : r.K;
+            r.S = r.K / r.P;
+            r.n_chunks = (uint32_t)(t.n ? (t.n + r.W - 1) / r.W : 0);
+            make_enc(r.model, r.em);
+            EncRecord er;                         // the record head, as the host encoder builds it
+            er.md = &r.model;
+            er.W = r.W; er.K = r.K; er.S = r.S; er.n_chunks = r.n_chunks;
+            build_head(er);
+            r.head = std::move(er.head);
+            r.index_off = er.index_off;
+            r.stab_off = er.stab_off;
+            const uint64_t units = (uint64_t)r.n_chunks * r.S;
+            r.o_words = take(4ull * r.W * r.n_chunks);
+            r.o_states = take(4ull * r.K * r.n_chunks);
+            r.o_counts = take(8 * units);
+            r.o_tab = take(sizeof(bsd::EncTabDev));
+            r.o_chunk = take(8ull * r.n_chunks);
+            r.o_start = take(4 * units);
+            r.o_mu = take(4 * units);
+        }
+        hipError_t he = hipMalloc(&e->d_scratch, std::max<uint64_t>(scratch, 256));
+        if (he != hipSuccess) return fail(denc_hip(he, "encoder scratch"));
+        he = hipEventCreateWithFlags(&e->done, hipEventDisableTiming);
+        if (he != hipSuccess) return fail(denc_hip(he, "encoder event"));
+        // code every stream
+        std::vector<bsd::EncTabDev> tabs(n_tensors);
+        for (uint32_t i = 0; i < n_tensors; i++) {
+            bs_dencoder::Rec& r = e->recs[i];
+            if (r.kind != BS_KIND_BF16 || r.n_chunks == 0) continue;
+            fill_enc_tab(r.em, tabs[i]);
+            he = hipMemcpyAsync(e->d_scratch + r.o_tab, &tabs[i], sizeof(bsd::EncTabDev), hipMemcpyHostToDevice, hs);
+            if (he != hipSuccess) return fail(denc_hip(he, "encoder tables"));
+            const bsd::EncArgs a = enc_args(e, r);
+            const int ke = bsk_encode(&a, std::max<uint32_t>(1, r.P / 64), stream);
+            if (ke) return fail(denc_hip((hipError_t)ke, "encode launch"));
+            r.counts.resize(2ull * r.n_chunks * r.S);
+            he = hipMemcpyAsync(r.counts.data(), e->d_scratch + r.o_counts, 4 * r.counts.size(), hipMemcpyDeviceToHost, hs);
+            if (he != hipSuccess) return fail(denc_hip(he, "encoder counts"));
+        }
+        he = hipStreamSynchronize(hs);
+        if (he != hipSuccess) return fail(denc_hip(he, "encode"));
+        // layout, as bs_encode_host lays the container out
+        uint64_t pos = align_up(kHeaderBytes + kDirEntryBytes * n_tensors, 16), out_pos = 0, ext = 0;
+        for (uint32_t i = 0; i < n_tensors; i++) {
+            bs_dencoder::Rec& r = e->recs[i];
+            r.rec_off = pos;
+            uint64_t len = 0;
+            if (r.kind == BS_KIND_RAW) {
+                len = r.n;
+            } else {
+                len = r.head.size();
+                r.chunk_off.resize(r.n_chunks);
+                r.unit_start.resize((uint64_t)r.n_chunks * r.S);
+                r.unit_mu.resize((uint64_t)r.n_chunks * r.S);
+                for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
+                    uint64_t at = 0;
+                    for (uint32_t st = 0; st < r.S; st++) {
+                        const uint64_t u = (uint64_t)ch * r.S + st;
+                        const uint64_t mu = state_units(r.P, r.counts[2 * u + 1]);
+                        if (st) wr32(r.head.data() + r.stab_off + 4ull * ((r.S - 1) * ch + st - 1), (uint32_t)at);
+                        r.unit_start[u] = (uint32_t)at;
+                        r.unit_mu[u] = (uint32_t)mu;
+                        at += mu + r.counts[2 * u];
+                    }
+                    wr64(r.head.data() + r.index_off + 16ull * ch, len);
+                    wr32(r.head.data() + r.index_off + 16ull * ch + 8, (uint32_t)at);
+                    r.chunk_off[ch] = len;
+                    len += align_up(code_bytes(r.K) + 2 * at, 16);
+                }
+            }
+            r.rec_len = len;
+            pos = align_up(pos + len, 16);
+            r.out_off = out_pos;
+            const uint64_t ob = r.kind == BS_KIND_BF16 ? 2 * r.n : r.n;
+            ext = std::max(ext, out_pos + ob);
+            out_pos = align_up(out_pos + ob, kOutAlign);
+        }
+        e->total_len = pos;
+        e->top.assign(align_up(kHeaderBytes + kDirEntryBytes * n_tensors, 16), 0);
+        uint8_t* c = e->top.data();
+        memcpy(c, kMagic, 8);
+        wr32(c + 8, kVersion);
+        wr32(c + 12, n_tensors);
+        wr64(c + 16, kHeaderBytes);
+        wr64(c + 24, pos);
+        wr64(c + 32, n_tensors ? ext : 0);
+        for (uint32_t i = 0; i < n_tensors; i++) {
+            const bs_dencoder::Rec& r = e->recs[i];
+            uint8_t* d = c + kHeaderBytes + kDirEntryBytes * i;
+            wr32(d, r.kind);
+            wr64(d + 8, r.n);
+            wr64(d + 16, r.out_off);
+            wr64(d + 24, r.rec_off);
+            wr64(d + 32, r.rec_len);
+            memcpy(d + 40, r.sha, 32);
+        }
+    } catch (const std::bad_alloc&) {
+        set_error("out of host memory");
+        return fail(BS_E_NOMEM);
+    }
+    *out = e;
+    return BS_OK;
+}
+
+uint64_t bs_encode_device_size(const bs_dencoder* e) { return e ? e->total_len : 0; }
+
+bs_status bs_encode_device_finish(bs_dencoder* e, void* d_out, uint64_t capacity, void* stream) {
+    if (!e || !d_out) { set_error("NULL argument"); return BS_E_INVAL; }
+    if ((uintptr_t)d_out & 15) { set_error("output must be 16-B aligned"); return BS_E_INVAL; }
+    if (capacity < e->total_len) { set_error("capacity %llu < %llu", (unsigned long long)capacity, (unsigned long long)e->total_len); return BS_E_NOSPACE; }
+    hipStream_t hs = (hipStream_t)stream;
+    uint8_t* o = (uint8_t*)d_out;
+    int ke = bsk_zero(o, e->total_len, stream);
+    if (ke) return denc_hip((hipError_t)ke, "encoder zero fill");
+    hipError_t he = hipMemcpyAsync(o, e->top.data(), e->top.size(), hipMemcpyHostToDevice, hs);
+    for (bs_dencoder::Rec& r : e->recs) {
+        if (he != hipSuccess) break;
+        if (r.kind == BS_KIND_RAW) {
+            if (r.n) he = hipMemcpyAsync(o + r.rec_off, r.d_data, r.n, hipMemcpyDeviceToDevice, hs);
+            continue;
+        }
+        he = hipMemcpyAsync(o + r.rec_off, r.head.data(), r.head.size(), hipMemcpyHostToDevice, hs);
+        if (he == hipSuccess && r.n_chunks)
+            he = hipMemcpyAsync(e->d_scratch + r.o_chunk, r.chunk_off.data(), 8ull * r.n_chunks, hipMemcpyHostToDevice, hs);
+        if (he == hipSuccess && r.n_chunks)
+            he = hipMemcpyAsync(e->d_scratch + r.o_start, r.unit_start.data(), 4 * r.unit_start.size(), hipMemcpyHostToDevice, hs);
+        if (he == hipSuccess && r.n_chunks)
+            he = hipMemcpyAsync(e->d_scratch + r.o_mu, r.unit_mu.data(), 4 * r.unit_mu.size(), hipMemcpyHostToDevice, hs);
+        if (he != hipSuccess) break;
+        bsd::EncArgs a = enc_args(e, r);
+        a.out = o + r.rec_off;
+        ke = bsk_assemble(&a, stream);
+        if (ke) return denc_hip((hipError_t)ke, "assemble launch");
+    }
+    if (he == hipSuccess) he = hipEventRecord(e->done, hs);
+    if (he != hipSuccess) return denc_hip(he, "encoder finish");
+    return BS_OK;
+}
+
+void bs_encode_device_free(bs_dencoder* e) {
+    if (!e) return;
+    if (e->done) {
+        (void)hipEventSynchronize(e->done);      // the host buffers of finish's copies
+        (void)hipEventDestroy(e->done);
+    }
+    if (e->d_scratch) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(e->d_scratch);
+    }
+    delete e;
+}
+
+}  // extern "C"

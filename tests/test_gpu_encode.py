@@ -1,0 +1,106 @@
+"""GPU encoder: the container built on the device equals the host encoder's,
+byte for byte.
+
+The host encoder's bytes equal the oracle's (tests/test_lib_host.py), so this
+pins the GPU encoder to the oracle as well.  Each case also decodes the
+device-built container with the GPU decoder.  All calls go through the C ABI
+(bs_encode_device_begin / _size / _finish / _free).
+"""
+import hashlib
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from lossless_entropy_coding_amd import _lib as L
+from lossless_entropy_coding_amd import codec
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _bf16(x) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+CASES = [
+    # (name, sizes of the BF16 tensors, chunk weights, lanes, lanes per stream)
+    ("k64_p32_two_streams", [5000, 70001], 4096, 64, 32),
+    ("k128_full_and_ragged", [6 * 65536, 65536 + 1025], 65536, 128, 128),
+    ("k256_p128", [131072 + 2049 + 7], 131072, 256, 128),
+    ("k512_p512_eight_lanes_per_thread", [2 * 262144 + 5], 262144, 512, 512),
+    ("k2048_p64_matrix_shape", [4 * 131072], 131072, 2048, 64),
+    ("k1_tiny", [1, 8, 9], 64, 1, 1),
+    ("k16_p4", [3 * 8192 + 5], 8192, 16, 4),
+]
+
+
+@pytest.mark.parametrize("name,sizes,W,K,P", CASES, ids=[c[0] for c in CASES])
+def test_device_container_equals_host_container(name, sizes, W, K, P):
+    say("encode case", name)
+    rng = np.random.default_rng(len(name))
+    words = []
+    for i, n in enumerate(sizes):
+        x = rng.standard_normal(n) * (0.02 if i % 2 == 0 else 1.0)
+        x[rng.random(n) < 0.001] *= 60.0
+        words.append(_bf16(x))
+    raw = rng.integers(0, 256, 777, dtype=np.uint8)
+    p = codec.params(chunk_weights=W, lanes=K, stream_lanes=P)
+    host = codec.encode([codec.bf16(w) for w in words] + [codec.raw(raw)], p)
+    dev_tensors = [("bf16", torch.from_numpy(w.view(np.int16).copy()).cuda()) for w in words]
+    dev_tensors.append(("raw", torch.from_numpy(raw.copy()).cuda()))
+    # digests given for some tensors, computed by the library for the others
+    digests = [hashlib.sha256(w.tobytes()).digest() if i % 2 == 0 else None for i, w in enumerate(words)] + [None]
+    dc = codec.encode_device(dev_tensors, p, digests=digests)
+    torch.cuda.synchronize()
+    got = dc.cpu().numpy().tobytes()
+    assert len(got) == len(host)
+    if got != host:
+        diff = np.flatnonzero(np.frombuffer(got, np.uint8) != np.frombuffer(host, np.uint8))
+        pytest.fail(f"{diff.size} bytes differ, first at {diff[:8]}")
+    # the device-built container decodes back to the words
+    plan = codec.Plan(got)
+    out = plan.decode()
+    rc, rep = plan.verify(out, flags=L.VERIFY_STATUS | L.VERIFY_SHA256)
+    assert rc == L.BS_OK, rep
+
+
+def test_device_models_and_verbatim_fallback():
+    rng = np.random.default_rng(5)
+    w1 = _bf16(rng.standard_normal(100000) * 0.02)
+    w2 = rng.integers(0, 1 << 16, 50000, dtype=np.uint16)        # > 256 symbols: stored verbatim
+    p = codec.params(chunk_weights=16384, lanes=64)
+    t1 = torch.from_numpy(w1.view(np.int16).copy()).cuda()
+    t2 = torch.from_numpy(w2.view(np.int16).copy()).cuda()
+    tables = [codec.build_tables(t1, p), None]                     # one model given, one built here
+    dc = codec.encode_device([("bf16", t1), ("bf16", t2), ("bf16", t1[:0])], p, tables=tables + [None])
+    host = codec.encode([codec.bf16(w1), codec.bf16(w2), codec.bf16(w1[:0])], p)
+    assert dc.cpu().numpy().tobytes() == host
+    assert codec.record_info(host, 1).kind == L.KIND_RAW
+
+
+def test_device_encoder_errors():
+    import ctypes as C
+    p = codec.params(chunk_weights=4096, lanes=64)
+    t = torch.zeros(4097, dtype=torch.int16, device="cuda")
+    with pytest.raises(L.BSError) as e:                             # BF16 data not 16-B aligned
+        codec.encode_device([("bf16", t[1:])], p)
+    assert e.value.rc == L.BS_E_INVAL
+    arr = (L.DTensor * 1)()
+    arr[0].kind = L.KIND_BF16
+    arr[0].d_data = t.data_ptr()
+    arr[0].n = 4096
+    enc = C.c_void_p()
+    L.check(L.lib().bs_encode_device_begin(arr, 1, C.byref(p), None, C.byref(enc)), "begin")
+    size = L.lib().bs_encode_device_size(enc)
+    out = torch.empty(size, dtype=torch.uint8, device="cuda")
+    assert L.lib().bs_encode_device_finish(enc, C.c_void_p(out.data_ptr()), size - 1, None) == L.BS_E_NOSPACE
+    assert L.lib().bs_encode_device_finish(enc, C.c_void_p(out.data_ptr()), size, None) == L.BS_OK
+    L.lib().bs_encode_device_free(enc)
+    assert out.cpu().numpy().tobytes() == codec.encode([codec.bf16(np.zeros(4096, np.uint16))], p)
