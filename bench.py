@@ -310,6 +310,26 @@ def fixed_bench(a):
                 "plain_bf16_gemv_us": round(t_plain * 1e6, 2),
                 "fixed_fused_GB_s_of_blob": round(plans[0].bytes / t_fixed / 1e9, 1),
                 "max_rel_diff_vs_fp32_product": float((y - ref).abs().max() / ref.abs().max())}
+        # Y = X W^T for batches of 16 and 64 on the matrix cores, against the BLAS product
+        # on the uncompressed matrix and decode-then-BLAS
+        Wd = outs[0][: rows * cols].view(torch.bfloat16).reshape(rows, cols)
+        gemm = {}
+        for batch in (16, 64):
+            X = torch.randn(batch, cols, generator=g).to(torch.bfloat16).cuda()
+            Y = torch.empty(batch, rows, dtype=torch.float32, device="cuda")
+            fg = plans[0].bound_gemm(Y, X.view(torch.int16), rows, cols, stream=stream)
+            _, t_fg = timed(fg)
+            _, t_pg = timed(lambda: torch.matmul(X, W.t()))
+            dec0 = steps[0]
+            _, t_dg = timed(lambda: (dec0(), torch.matmul(X, Wd.t())))
+            fg()
+            torch.cuda.synchronize()
+            R = (X.float() @ W.float().t())
+            gemm[f"batch_{batch}"] = {"fixed_fused_us": round(t_fg * 1e6, 2), "plain_bf16_gemm_us": round(t_pg * 1e6, 2),
+                                      "decode_then_gemm_us": round(t_dg * 1e6, 2),
+                                      "fixed_fused_TFLOP_s": round(2 * batch * rows * cols / t_fg / 1e12, 2),
+                                      "max_rel_diff_vs_fp32_product": float((Y - R).abs().max() / R.abs().max())}
+        gemv["gemm"] = gemm
     line = {"metric": "fixed-width lane-stream decode: decoded BF16 GB/s on 1 MI355X (% HBM roofline) + bits/weight",
             "value": round(2 * n / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
             "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "dtype": "u32", "data": "synthetic",

@@ -361,6 +361,22 @@ bs_status bs_fixed_decode_async(const bs_fixed_info* info, const void* d_blob, v
 bs_status bs_fixed_gemv_async(const bs_fixed_info* info, const void* d_blob, uint64_t rows, uint64_t cols,
                               const void* d_x, float* d_y, uint32_t* d_status, void* stream);
 
+/* Fused decode and product with a batch of vectors on the matrix cores
+ * [NVLC card, runtime paragraphs: the compressed-only runtime multiplies with
+ * weights decoded where they are used]: Y[b, r] = sum over c of W[r, c] X[b, c]
+ * for b < batch (1..64), with W the blob's n weights as a row-major rows x cols
+ * matrix, cols a multiple of 2048 (so every row starts on a block) and below
+ * 2^26.  Each workgroup decodes 16 rows a panel of 2048 columns at a time
+ * into LDS and multiplies them with v_mfma_f32_16x16x32_bf16; the weights are
+ * never written out.  d_x: batch x cols BF16 words, row-major, 16-B aligned;
+ * d_y: batch x rows floats, row-major, overwritten.  Every entry is summed in
+ * fp32 in one fixed order (the same result on every run; within the fp32
+ * summation bound of the exact sum).  d_status as for bs_fixed_decode_async.
+ * One kernel launch on `stream`; nothing is allocated.  Errors: BS_E_INVAL
+ * (shape, batch, NULL, alignment), BS_E_HIP. */
+bs_status bs_fixed_gemm_async(const bs_fixed_info* info, const void* d_blob, uint64_t rows, uint64_t cols,
+                              uint32_t batch, const void* d_x, float* d_y, uint32_t* d_status, void* stream);
+
 /* Bytes needed to decode records [first, first + count). */
 uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count);
 

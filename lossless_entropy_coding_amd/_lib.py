@@ -120,6 +120,8 @@ SIGNATURES = {
                                         C.c_void_p]),
     "bs_fixed_gemv_async": (C.c_int, [C.POINTER(FixedInfo), C.c_void_p, C.c_uint64, C.c_uint64, C.c_void_p,
                                       C.c_void_p, C.c_void_p, C.c_void_p]),
+    "bs_fixed_gemm_async": (C.c_int, [C.POINTER(FixedInfo), C.c_void_p, C.c_uint64, C.c_uint64, C.c_uint32,
+                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "bs_plan_waves_per_block": (C.c_uint32, [C.c_void_p]),
     "bs_verify": (C.c_int, [C.c_void_p, C.c_uint32, C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_uint32,
                             C.c_void_p, C.POINTER(Report)]),

@@ -393,6 +393,38 @@ class FixedPlan:
         self.gemv_into(y, x, rows, cols, stream=stream)
         return y
 
+    def gemm_into(self, y: torch.Tensor, x: torch.Tensor, rows: int, cols: int, status: bool = True,
+                  stream=None) -> None:
+        """Enqueue Y = X W^T on the matrix cores (bs_fixed_gemm_async): x a
+        (batch, cols) bfloat16 (or int16) tensor, y a (batch, rows) float32
+        tensor (overwritten), batch 1..64."""
+        assert x.dtype in (torch.bfloat16, torch.int16) and x.dim() == 2 and x.shape[1] == cols and x.is_contiguous()
+        assert y.dtype == torch.float32 and tuple(y.shape) == (x.shape[0], rows) and y.is_contiguous()
+        rc = L.lib().bs_fixed_gemm_async(C.byref(self.info), C.c_void_p(self.dev.data_ptr()), rows, cols, x.shape[0],
+                                         C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()),
+                                         C.c_void_p(self.status.data_ptr()) if status else None,
+                                         C.c_void_p(_stream_handle(stream)))
+        L.check(rc, "bs_fixed_gemm_async")
+
+    def bound_gemm(self, y: torch.Tensor, x: torch.Tensor, rows: int, cols: int, stream=None):
+        f = L.lib().bs_fixed_gemm_async
+        args = (C.byref(self.info), C.c_void_p(self.dev.data_ptr()), C.c_uint64(rows), C.c_uint64(cols),
+                C.c_uint32(x.shape[0]), C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()), None,
+                C.c_void_p(_stream_handle(stream)))
+        keep = (x, y, self.dev)
+
+        def run():
+            rc = f(*args)
+            if rc:
+                L.check(rc, "bs_fixed_gemm_async")
+            return keep
+        return run
+
+    def gemm(self, x: torch.Tensor, rows: int, cols: int, stream=None) -> torch.Tensor:
+        y = torch.empty(x.shape[0], rows, dtype=torch.float32, device=self.dev.device)
+        self.gemm_into(y, x, rows, cols, stream=stream)
+        return y
+
     def block_status(self) -> np.ndarray:
         return self.status[: self.info.n_blocks].cpu().numpy().view(np.uint32)
 

@@ -131,7 +131,15 @@ struct FixedArgs {
     uint32_t unit_blocks;
     uint32_t group_units;
     uint32_t q_step, r_step;  // kFixWaves * 2048 = q_step * cols + r_step
+    // fused product with a batch of vectors (MFMA): X batch x cols in gx
+    // (row-major BF16), Y batch x rows in gy (row-major fp32), cols a
+    // multiple of 2048 so that every row starts on a block
+    uint32_t batch;
+    uint32_t reserved;
 };
+
+constexpr uint32_t kGemmWaves = 8;          // waves per workgroup of the batched product
+constexpr uint32_t kGemmRowBytes = 4112;    // LDS per decoded row block: 4096 B + 16 B, so the 16 rows start on different banks
 
 // GPU encoder.  Per BF16 record, the encode tables (in device memory): for
 // each s, q | cum << 16 (q <= 2^12, cum < 2^12); for each fraction table t
@@ -179,6 +187,9 @@ int bsk_gemv(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, u
 // decode a fixed-width blob: n_groups workgroups of kFixWaves waves, each wave
 // striding over the blocks
 int bsk_fixed_decode(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
+// the fused product of a fixed-width blob with a batch of vectors: one
+// workgroup of kGemmWaves waves per 16 rows (n_groups workgroups, striding)
+int bsk_fixed_gemm(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
 // the fused product of a fixed-width blob with a vector: n_groups workgroups
 // of kFixWaves waves, each workgroup striding over the row groups
 int bsk_fixed_gemv(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);

@@ -240,4 +240,31 @@ bs_status bs_fixed_gemv_async(const bs_fixed_info* info, const void* d_blob, uin
     return BS_OK;
 }
 
+bs_status bs_fixed_gemm_async(const bs_fixed_info* info, const void* d_blob, uint64_t rows, uint64_t cols,
+                              uint32_t batch, const void* d_x, float* d_y, uint32_t* d_status, void* stream) {
+    bsd::FixedArgs a;
+    const bs_status rc = fixed_args(info, d_blob, a);
+    if (rc != BS_OK) return rc;
+    if (!d_x || !d_y) { set_error("NULL argument"); return BS_E_INVAL; }
+    if (cols == 0 || cols % bsd::kFixBlockW || cols >= (1ull << 26) || rows * cols != info->n || rows > info->n) {
+        set_error("a %llu x %llu matrix does not fit %llu weights with columns a multiple of 2048 below 2^26",
+                  (unsigned long long)rows, (unsigned long long)cols, (unsigned long long)info->n);
+        return BS_E_INVAL;
+    }
+    if (batch == 0 || batch > 64) { set_error("batch %u outside 1..64", batch); return BS_E_INVAL; }
+    if ((uintptr_t)d_x & 15) { set_error("X must be 16-B aligned"); return BS_E_INVAL; }
+    a.status = d_status;
+    a.gx = (const uint16_t*)d_x;
+    a.gy = d_y;
+    a.rows = rows;
+    a.cols = (uint32_t)cols;
+    a.batch = batch;
+    int cus = 0;
+    if (bsk_device_cus(&cus) != 0 || cus <= 0) cus = 256;
+    const uint32_t groups = (uint32_t)std::min<uint64_t>((rows + 15) / 16, 8ull * (uint64_t)cus);
+    const int e = bsk_fixed_gemm(&a, groups, stream);
+    if (e != 0) { set_error("fixed batched product launch: %s", hipGetErrorString((hipError_t)e)); return BS_E_HIP; }
+    return BS_OK;
+}
+
 }  // extern "C"

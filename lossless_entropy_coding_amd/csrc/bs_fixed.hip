@@ -304,7 +304,111 @@ __global__ __launch_bounds__(64 * kFixWaves) void fixed_gemv_kernel(FixedArgs a)
     }
 }
 
+// The fused product with a batch of vectors, Y[n][r] = sum over c of W[r][c] X[n][c],
+// on the matrix cores.  Workgroup g owns rows 16 g .. 16 g + 15 (all their
+// columns, so it stores its part of Y and no atomics are needed).  Rows start
+// on a block (cols % 2048 == 0), so a panel of 2048 columns of the 16 rows is
+// 16 whole blocks: the eight waves decode two each into LDS, then multiply the
+// panel with X with v_mfma_f32_16x16x32_bf16 (A: 16 rows x 32 columns of the
+// panel, a 16-B piece per lane read back through the decode's piece
+// rotation; B: 32 columns x 16 batch rows of X, 16 B per lane from X in HBM or
+// L2); the next panel's blocks are loaded while one is multiplied.  The waves split the batch into NT tiles of 16 and each tile's columns
+// among 8 / NT waves; the K slices are added in wave order at the end, so
+// every Y entry is summed in one fixed order.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int NT>
+__global__ __launch_bounds__(64 * kGemmWaves) void fixed_gemm_kernel(FixedArgs a) {
+    __shared__ uint32_t lut[256];
+    __shared__ __attribute__((aligned(16))) uint8_t wbuf[16][kGemmRowBytes];
+    __shared__ __attribute__((aligned(4))) uint16_t escl[kGemmWaves][kFixEscLds];
+    __shared__ f32x4 red[kGemmWaves][64];
+
+    const uint32_t t = threadIdx.x, lane = t & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    if (t < 256) build_lut(a, t, lut);
+    uint16_t* el = escl[wave];
+    constexpr uint32_t kWpt = kGemmWaves / NT;     // waves per batch tile
+    constexpr uint32_t kSlice = kFixBlockW / kWpt; // panel columns per wave
+    const uint32_t nt = wave / kWpt, ks = wave % kWpt;
+    const uint32_t bpr = a.cols / kFixBlockW;
+    const uint64_t groups = (a.rows + 15) / 16;
+    for (uint64_t g = blockIdx.x; g < groups; g += gridDim.x) {
+        const uint64_t r0 = 16 * g;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const uint32_t m0 = 2 * wave, m1 = 2 * wave + 1;
+        const bool h0 = r0 + m0 < a.rows, h1 = r0 + m1 < a.rows;
+        // this wave's two blocks of the first panel; each later panel's are
+        // loaded while the current one is multiplied
+        BlockIn in0, in1;
+        if (h0) in0 = load_block(a, (r0 + m0) * bpr, lane);
+        if (h1) in1 = load_block(a, (r0 + m1) * bpr, lane);
+        for (uint32_t p = 0; p < bpr; p++) {
+            __syncthreads();          // the previous panel is consumed (and the table built)
+            const uint64_t b0 = (r0 + m0) * bpr + p, b1 = (r0 + m1) * bpr + p;
+#pragma unroll
+            for (uint32_t h = 0; h < 2; h++) {
+                uint32_t* st = (uint32_t*)wbuf[h ? m1 : m0];
+                if (h ? h1 : h0) {
+                    const uint32_t bad = finish_block(a, h ? in1 : in0, lane, lut, st, el);
+                    write_status(a, h ? b1 : b0, bad, lane);
+                } else {
+#pragma unroll
+                    for (uint32_t k = 0; k < 4; k++) *(v4u*)(st + 16 * lane + 4 * k) = v4u{0u, 0u, 0u, 0u};
+                }
+            }
+            __syncthreads();
+            if (p + 1 < bpr) {
+                if (h0) in0 = load_block(a, b0 + 1, lane);
+                if (h1) in1 = load_block(a, b1 + 1, lane);
+            }
+            const uint32_t n = nt * 16 + (lane & 15);
+            const bool n_ok = n < a.batch;
+            const uint16_t* xr = a.gx + (uint64_t)(n_ok ? n : 0) * a.cols + (uint64_t)p * kFixBlockW;
+            const uint8_t* wr = wbuf[lane & 15];
+#pragma unroll 8
+            for (uint32_t s = 0; s < kSlice / 32; s++) {
+                const uint32_t e0 = ks * kSlice + 32 * s + 8 * (lane >> 4);
+                const uint32_t L = e0 >> 5, kp = (e0 >> 3) & 3u;
+                const bf16x8 av = *(const bf16x8*)(wr + 64 * L + 16 * ((kp + (L >> 1)) & 3u));
+                bf16x8 bv = {};
+                if (n_ok) bv = *(const bf16x8*)(xr + e0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+            }
+        }
+        red[wave][lane] = acc;
+        __syncthreads();
+        if (ks == 0) {
+            f32x4 sum = red[wave][lane];
+#pragma unroll
+            for (uint32_t w2 = 1; w2 < kWpt; w2++) sum += red[wave + w2][lane];
+            const uint32_t n = nt * 16 + (lane & 15);
+#pragma unroll
+            for (uint32_t i = 0; i < 4; i++) {
+                const uint64_t r = r0 + 4 * (lane >> 4) + i;      // D row 4 (lane / 16) + i, column lane % 16
+                if (n < a.batch && r < a.rows) a.gy[(uint64_t)n * a.rows + r] = sum[i];
+            }
+        }
+    }
+}
+
 }  // namespace
+
+extern "C" int bsk_fixed_gemm(const FixedArgs* args, uint32_t n_groups, void* stream) {
+    if (n_groups == 0 || args->rows == 0) return 0;
+    const dim3 grid(n_groups), block(64 * kGemmWaves);
+    hipStream_t st = (hipStream_t)stream;
+    const uint32_t nt = (args->batch + 15) / 16;
+    switch (nt) {
+        case 1: hipLaunchKernelGGL(fixed_gemm_kernel<1>, grid, block, 0, st, *args); break;
+        case 2: hipLaunchKernelGGL(fixed_gemm_kernel<2>, grid, block, 0, st, *args); break;
+        case 3:
+        case 4: hipLaunchKernelGGL(fixed_gemm_kernel<4>, grid, block, 0, st, *args); break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
 
 extern "C" int bsk_fixed_decode(const FixedArgs* args, uint32_t n_groups, void* stream) {
     if (n_groups == 0 || args->n_blocks == 0) return 0;

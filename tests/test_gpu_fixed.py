@@ -223,3 +223,64 @@ def test_fixed_gemv_argument_errors():
     y = plan.gemv(x[:1024], 64, 1024)
     torch.cuda.synchronize()
     assert float(y.abs().max()) == 0.0
+
+
+# --------------------------------------------------------------------------- batched product (MFMA)
+GEMM_CASES = [
+    # (name, rows, cols, batch): one tile of 16 batch rows, two, four (and a ragged 3 -> 4), rows not a
+    # multiple of 16, several column panels
+    ("4096x4096_b16", 4096, 4096, 16), ("512x4096_b32", 512, 4096, 32), ("300x2048_b64", 300, 2048, 64),
+    ("77x6144_b1", 77, 6144, 1), ("1000x14336_b8", 1000, 14336, 8), ("64x2048_b40", 64, 2048, 40),
+]
+
+
+@pytest.mark.parametrize("name,rows,cols,batch", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
+def test_fixed_gemm_matches_fp64_product_of_oracle_decode(name, rows, cols, batch):
+    """Y = X W^T within the fp32 summation bound.  The matrix cores add the
+    exact BF16 products of a 32-column step into an fp32 accumulator (at most
+    one rounding per addition: 32 per step, cols / 32 steps per wave) and the
+    waves' K slices are added in order (at most 7 more), so an entry's error
+    is at most (cols + 8) 2^-24 sum_c |W[r, c] X[b, c]|; the test allows twice
+    that.  Each entry is summed in one fixed order: two runs agree bit for bit."""
+    say("fixed gemm", name)
+    rng = np.random.default_rng(rows + cols + batch)
+    w = rng.standard_normal(rows * cols) * 0.02
+    w[rng.random(w.size) < 0.002] *= 80.0
+    words = _bf16(w)
+    blob = codec.fixed_encode(words)
+    W64 = _as_f64(O.fixed_decode(blob)).reshape(rows, cols)
+    xw = _bf16(rng.standard_normal(batch * cols)).reshape(batch, cols)
+    X64 = _as_f64(xw)
+    Y_ref = X64 @ W64.T
+    bound = 2 * (cols + 8) * 2.0 ** -24 * (np.abs(X64) @ np.abs(W64).T)
+    plan = codec.FixedPlan(blob)
+    x = torch.from_numpy(xw.view(np.int16).copy()).cuda()
+    ys = []
+    for rep in range(2):
+        y = torch.full((batch, rows), float("nan"), dtype=torch.float32, device="cuda")
+        plan.gemm_into(y, x, rows, cols)
+        torch.cuda.synchronize()
+        assert (plan.block_status() == 0).all()
+        ys.append(y.cpu().numpy())
+        err = np.abs(ys[-1].astype(np.float64) - Y_ref)
+        assert np.all(err <= bound), (rep, float((err - bound).max()))
+    assert ys[0].tobytes() == ys[1].tobytes()
+
+
+def test_fixed_gemm_argument_errors():
+    words = _case_words("gauss", 64 * 2048, 12)
+    plan = codec.FixedPlan(codec.fixed_encode(words))
+    x = torch.zeros(4, 2048, dtype=torch.int16, device="cuda")
+    y = torch.empty(4, 64, dtype=torch.float32, device="cuda")
+    f = L.lib().bs_fixed_gemm_async
+    import ctypes as C
+    args = lambda rows, cols, batch, xp: (C.byref(plan.info), C.c_void_p(plan.dev.data_ptr()), rows, cols, batch,
+                                          C.c_void_p(xp), C.c_void_p(y.data_ptr()), None, None)
+    assert f(*args(128, 1024, 4, x.data_ptr())) == L.BS_E_INVAL          # cols not a multiple of 2048
+    assert f(*args(32, 2048, 4, x.data_ptr())) == L.BS_E_INVAL           # rows * cols != n
+    assert f(*args(64, 2048, 0, x.data_ptr())) == L.BS_E_INVAL           # batch 0
+    assert f(*args(64, 2048, 65, x.data_ptr())) == L.BS_E_INVAL          # batch above 64
+    assert f(*args(64, 2048, 4, x.data_ptr() + 2)) == L.BS_E_INVAL       # misaligned X
+    assert f(*args(64, 2048, 4, x.data_ptr())) == L.BS_OK
+    torch.cuda.synchronize()
+    assert float(y.abs().max()) == 0.0
