@@ -62,7 +62,7 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_SOURCES = {"decode_kernel": ("bs_decode.hip", "bs_device.h"), "fixed": ("bs_fixed.hip", "bs_device.h")}
+TRAFFIC_SOURCES = {"decode_kernel": ("bs_decode.hip", "bs_device.h"), "fixed": ("bs_fixed.hip", "bs_fixed_device.h")}
 
 
 def kernel_source_sha256(kind: str) -> str:

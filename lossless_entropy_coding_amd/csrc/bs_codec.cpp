@@ -19,6 +19,7 @@
 #include <vector>
 
 #include "bs_device.h"
+#include "bs_encode_device.h"
 #include "bs_internal.h"
 #include "bs_model.h"
 

@@ -103,72 +103,6 @@ struct DecodeArgs {
     uint64_t gcols;         // a multiple of 8, at least 512
 };
 
-// fixed-width lane-stream form (layout in bs.h): one wavefront decodes a
-// block of 2048 weights (64 lanes x 32) at a time
-constexpr uint32_t kFixHeader = 96;
-constexpr uint32_t kFixBlockW = 2048;
-constexpr uint32_t kFixBlockBytes = 2816;
-constexpr uint32_t kFixWaves = 4;           // waves per workgroup
-constexpr uint32_t kFixEscLds = 256;        // escape staging per wave in LDS (up to 254 escapes; more are read from HBM)
-
-struct FixedArgs {
-    const uint8_t* blob;    // the whole blob (header at 0)
-    uint16_t* out;          // n BF16 words (decode)
-    uint32_t* status;       // n_blocks words or null
-    uint64_t n, n_blocks, n_esc, esc_off;
-    uint32_t tab[8];        // symbols of codes 0..15, two per word (code 2k low); code 15 = 0
-    // fused product with a vector: the weights are a row-major rows x cols
-    // matrix (cols a multiple of 32), y[r] = sum over c of W[r, c] x[c] in
-    // fp32.  A unit of unit_rows = 2048 / gcd(cols, 2048) rows spans exactly
-    // unit_blocks = cols / gcd(cols, 2048) whole blocks; a workgroup owns a
-    // group of group_units units (at most 64 rows) and stores its rows.
-    const uint16_t* gx;     // x: cols BF16 words, 16-B aligned
-    float* gy;              // y: rows floats
-    uint64_t rows;
-    uint64_t n_groups;      // ceil(rows / (unit_rows * group_units))
-    uint32_t cols;          // below 2^26
-    uint32_t unit_rows;
-    uint32_t unit_blocks;
-    uint32_t group_units;
-    uint32_t q_step, r_step;  // kFixWaves * 2048 = q_step * cols + r_step
-    // fused product with a batch of vectors (MFMA): X batch x cols in gx
-    // (row-major BF16), Y batch x rows in gy (row-major fp32), cols a
-    // multiple of 2048 so that every row starts on a block
-    uint32_t batch;
-    uint32_t reserved;
-};
-
-constexpr uint32_t kGemmWaves = 8;          // waves per workgroup of the batched product
-constexpr uint32_t kGemmRowBytes = 4112;    // LDS per decoded row block: 4096 B + 16 B, so the 16 rows start on different banks
-
-// GPU encoder.  Per BF16 record, the encode tables (in device memory): for
-// each s, q | cum << 16 (q <= 2^12, cum < 2^12); for each fraction table t
-// (0 = flat) and f, the same; the fraction table of each s.
-struct EncTabDev {
-    uint32_t s_qc[512];
-    uint32_t f_qc[(kMaxTables + 1) * 128];
-    uint8_t route[512];
-};
-
-// One BF16 record to encode: its chunks' streams (chunk c, stream st = unit
-// c * S + st) are coded by one wavefront each into scratch.
-struct EncArgs {
-    const uint16_t* w;          // n weights, 16-B aligned
-    uint64_t n;
-    uint32_t W, K, S, P;        // P = K / S lanes per stream
-    uint32_t n_chunks, m_s, m_f;
-    uint32_t reserved;
-    const EncTabDev* tab;
-    uint16_t* words;            // unit u's words (in emission order) at words + u * 2 * (W / S)
-    uint32_t* states;           // chunk c lane l at states + c * K + l
-    uint32_t* counts;           // unit u: counts[2u] words, counts[2u + 1] sum of its lanes' length codes
-    // assembly
-    uint8_t* out;               // the record's first byte in the container
-    const uint64_t* chunk_off;  // payload offset of each chunk from the record start
-    const uint32_t* unit_start; // 16-bit unit where each stream starts in its chunk's stream area
-    const uint32_t* unit_mu;    // 16-bit units of each stream's state bits
-};
-
 }  // namespace bsd
 
 // Launchers (bs_kernels.hip).  All return a hipError_t as int.
@@ -184,21 +118,6 @@ int bsk_build_luts(const uint8_t* d_container, const bsd::RecDev* d_recs, uint32
 int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, bool compact, void* stream);
 // the fused matrix-vector product of one record (full layout, variant 1, 2 or 4), y zeroed first
 int bsk_gemv(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream);
-// decode a fixed-width blob: n_groups workgroups of kFixWaves waves, each wave
-// striding over the blocks
-int bsk_fixed_decode(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
-// the fused product of a fixed-width blob with a batch of vectors: one
-// workgroup of kGemmWaves waves per 16 rows (n_groups workgroups, striding)
-int bsk_fixed_gemm(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
-// the fused product of a fixed-width blob with a vector: n_groups workgroups
-// of kFixWaves waves, each workgroup striding over the row groups
-int bsk_fixed_gemv(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
-// GPU encoder: code every stream of a record into scratch (lanes per thread R
-// = 1, 2, 4 or 8), then write the record's chunk payloads into the container
-int bsk_encode(const bsd::EncArgs* args, uint32_t R, void* stream);
-int bsk_assemble(const bsd::EncArgs* args, void* stream);
-// fill n bytes at d with zero (a kernel, so that the work stays capturable)
-int bsk_zero(void* d, uint64_t n, void* stream);
 int bsk_raw_copy(const uint8_t* d_container, const bsd::RawDev* d_raw, uint32_t n_raw, uint8_t* d_out,
                  uint64_t out_base, void* stream);
 int bsk_compare(const uint8_t* a, const uint8_t* b, uint64_t n, unsigned long long* d_result /*2*/, void* stream);

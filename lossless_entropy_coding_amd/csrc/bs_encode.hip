@@ -26,6 +26,7 @@
 #include <algorithm>
 
 #include "bs_device.h"
+#include "bs_encode_device.h"
 
 using namespace bsd;
 

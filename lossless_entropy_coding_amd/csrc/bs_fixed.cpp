@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "bs_device.h"
+#include "bs_fixed_device.h"
 #include "bs_internal.h"
 
 using namespace bs;

@@ -36,6 +36,7 @@
 #include <algorithm>
 
 #include "bs_device.h"
+#include "bs_fixed_device.h"
 #include "bs_wave.h"
 
 using namespace bsd;

@@ -1,0 +1,60 @@
+// bs_fixed_device.h -- structures shared by the host side of the library and
+// the kernels of the fixed-width lane-stream form (gfx950).  Not part of the
+// public C ABI.
+#pragma once
+#include <stdint.h>
+
+namespace bsd {
+
+// fixed-width lane-stream form (layout in bs.h): one wavefront decodes a
+// block of 2048 weights (64 lanes x 32) at a time
+constexpr uint32_t kFixHeader = 96;
+constexpr uint32_t kFixBlockW = 2048;
+constexpr uint32_t kFixBlockBytes = 2816;
+constexpr uint32_t kFixWaves = 4;           // waves per workgroup
+constexpr uint32_t kFixEscLds = 256;        // escape staging per wave in LDS (up to 254 escapes; more are read from HBM)
+
+struct FixedArgs {
+    const uint8_t* blob;    // the whole blob (header at 0)
+    uint16_t* out;          // n BF16 words (decode)
+    uint32_t* status;       // n_blocks words or null
+    uint64_t n, n_blocks, n_esc, esc_off;
+    uint32_t tab[8];        // symbols of codes 0..15, two per word (code 2k low); code 15 = 0
+    // fused product with a vector: the weights are a row-major rows x cols
+    // matrix (cols a multiple of 32), y[r] = sum over c of W[r, c] x[c] in
+    // fp32.  A unit of unit_rows = 2048 / gcd(cols, 2048) rows spans exactly
+    // unit_blocks = cols / gcd(cols, 2048) whole blocks; a workgroup owns a
+    // group of group_units units (at most 64 rows) and stores its rows.
+    const uint16_t* gx;     // x: cols BF16 words, 16-B aligned
+    float* gy;              // y: rows floats
+    uint64_t rows;
+    uint64_t n_groups;      // ceil(rows / (unit_rows * group_units))
+    uint32_t cols;          // below 2^26
+    uint32_t unit_rows;
+    uint32_t unit_blocks;
+    uint32_t group_units;
+    uint32_t q_step, r_step;  // kFixWaves * 2048 = q_step * cols + r_step
+    // fused product with a batch of vectors (MFMA): X batch x cols in gx
+    // (row-major BF16), Y batch x rows in gy (row-major fp32), cols a
+    // multiple of 2048 so that every row starts on a block
+    uint32_t batch;
+    uint32_t reserved;
+};
+
+constexpr uint32_t kGemmWaves = 8;          // waves per workgroup of the batched product
+constexpr uint32_t kGemmRowBytes = 4112;    // LDS per decoded row block: 4096 B + 16 B, so the 16 rows start on different banks
+
+}  // namespace bsd
+
+// Launchers (bs_fixed.hip).  All return a hipError_t as int.
+extern "C" {
+// decode a fixed-width blob: n_groups workgroups of kFixWaves waves, each wave
+// striding over the blocks
+int bsk_fixed_decode(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
+// the fused product of a fixed-width blob with a batch of vectors: one
+// workgroup of kGemmWaves waves per 16 rows (n_groups workgroups, striding)
+int bsk_fixed_gemm(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
+// the fused product of a fixed-width blob with a vector: n_groups workgroups
+// of kFixWaves waves, each workgroup striding over the row groups
+int bsk_fixed_gemv(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
+}
