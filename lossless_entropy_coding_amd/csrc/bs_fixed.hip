@@ -309,13 +309,14 @@ __global__ __launch_bounds__(64 * kFixWaves) void fixed_gemv_kernel(FixedArgs a)
 // on the matrix cores.  Workgroup g owns rows 16 g .. 16 g + 15 (all their
 // columns, so it stores its part of Y and no atomics are needed).  Rows start
 // on a block (cols % 2048 == 0), so a panel of 2048 columns of the 16 rows is
-// 16 whole blocks: the eight waves decode two each into LDS, then multiply the
-// panel with X with v_mfma_f32_16x16x32_bf16 (A: 16 rows x 32 columns of the
-// panel, a 16-B piece per lane read back through the decode's piece
-// rotation; B: 32 columns x 16 batch rows of X, 16 B per lane from X in HBM or
-// L2); the next panel's blocks are loaded while one is multiplied.  The waves split the batch into NT tiles of 16 and each tile's columns
-// among 8 / NT waves; the K slices are added in wave order at the end, so
-// every Y entry is summed in one fixed order.
+// 16 whole blocks: the kGemmWaves waves decode 16 / kGemmWaves each into LDS,
+// then multiply the panel with X with v_mfma_f32_16x16x32_bf16 (A: 16 rows x
+// 32 columns of the panel, a 16-B piece per lane read back through the
+// decode's piece rotation; B: 32 columns x 16 batch rows of X, 16 B per lane
+// from X in HBM or L2); the next panel's blocks are loaded while one is
+// multiplied.  The waves split the batch into NT tiles of 16 and each tile's
+// columns among kGemmWaves / NT waves; the K slices are added in wave order
+// at the end, so every Y entry is summed in one fixed order.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -338,22 +339,27 @@ __global__ __launch_bounds__(64 * kGemmWaves) void fixed_gemm_kernel(FixedArgs a
     for (uint64_t g = blockIdx.x; g < groups; g += gridDim.x) {
         const uint64_t r0 = 16 * g;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const uint32_t m0 = 2 * wave, m1 = 2 * wave + 1;
-        const bool h0 = r0 + m0 < a.rows, h1 = r0 + m1 < a.rows;
-        // this wave's two blocks of the first panel; each later panel's are
+        constexpr uint32_t kRpw = 16 / kGemmWaves;      // rows (blocks of a panel) per wave
+        uint32_t mr[kRpw];
+        bool has[kRpw];
+        BlockIn in[kRpw];
+        // this wave's blocks of the first panel; each later panel's are
         // loaded while the current one is multiplied
-        BlockIn in0, in1;
-        if (h0) in0 = load_block(a, (r0 + m0) * bpr, lane);
-        if (h1) in1 = load_block(a, (r0 + m1) * bpr, lane);
+#pragma unroll
+        for (uint32_t h = 0; h < kRpw; h++) {
+            mr[h] = kRpw * wave + h;
+            has[h] = r0 + mr[h] < a.rows;
+            if (has[h]) in[h] = load_block(a, (r0 + mr[h]) * bpr, lane);
+        }
         for (uint32_t p = 0; p < bpr; p++) {
             __syncthreads();          // the previous panel is consumed (and the table built)
-            const uint64_t b0 = (r0 + m0) * bpr + p, b1 = (r0 + m1) * bpr + p;
 #pragma unroll
-            for (uint32_t h = 0; h < 2; h++) {
-                uint32_t* st = (uint32_t*)wbuf[h ? m1 : m0];
-                if (h ? h1 : h0) {
-                    const uint32_t bad = finish_block(a, h ? in1 : in0, lane, lut, st, el);
-                    write_status(a, h ? b1 : b0, bad, lane);
+            for (uint32_t h = 0; h < kRpw; h++) {
+                uint32_t* st = (uint32_t*)wbuf[mr[h]];
+                if (has[h]) {
+                    const uint64_t blk = (r0 + mr[h]) * bpr + p;
+                    const uint32_t bad = finish_block(a, in[h], lane, lut, st, el);
+                    write_status(a, blk, bad, lane);
                 } else {
 #pragma unroll
                     for (uint32_t k = 0; k < 4; k++) *(v4u*)(st + 16 * lane + 4 * k) = v4u{0u, 0u, 0u, 0u};
@@ -361,8 +367,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void fixed_gemm_kernel(FixedArgs a
             }
             __syncthreads();
             if (p + 1 < bpr) {
-                if (h0) in0 = load_block(a, b0 + 1, lane);
-                if (h1) in1 = load_block(a, b1 + 1, lane);
+#pragma unroll
+                for (uint32_t h = 0; h < kRpw; h++)
+                    if (has[h]) in[h] = load_block(a, (r0 + mr[h]) * bpr + p + 1, lane);
             }
             const uint32_t n = nt * 16 + (lane & 15);
             const bool n_ok = n < a.batch;

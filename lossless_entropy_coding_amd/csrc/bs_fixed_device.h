@@ -41,7 +41,10 @@ struct FixedArgs {
     uint32_t reserved;
 };
 
-constexpr uint32_t kGemmWaves = 8;          // waves per workgroup of the batched product
+#ifndef BS_GEMM_WAVES
+#define BS_GEMM_WAVES 16
+#endif
+constexpr uint32_t kGemmWaves = BS_GEMM_WAVES;   // waves per workgroup of the batched product (8 or 16; one block of a panel each at 16)
 constexpr uint32_t kGemmRowBytes = 4112;    // LDS per decoded row block: 4096 B + 16 B, so the 16 rows start on different banks
 
 }  // namespace bsd

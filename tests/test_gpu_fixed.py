@@ -239,8 +239,8 @@ def test_fixed_gemm_matches_fp64_product_of_oracle_decode(name, rows, cols, batc
     """Y = X W^T within the fp32 summation bound.  The matrix cores add the
     exact BF16 products of a 32-column step into an fp32 accumulator (at most
     one rounding per addition: 32 per step, cols / 32 steps per wave) and the
-    waves' K slices are added in order (at most 7 more), so an entry's error
-    is at most (cols + 8) 2^-24 sum_c |W[r, c] X[b, c]|; the test allows twice
+    waves' K slices are added in order (at most 15 more), so an entry's error
+    is at most (cols + 16) 2^-24 sum_c |W[r, c] X[b, c]|; the test allows twice
     that.  Each entry is summed in one fixed order: two runs agree bit for bit."""
     say("fixed gemm", name)
     rng = np.random.default_rng(rows + cols + batch)
@@ -252,7 +252,7 @@ def test_fixed_gemm_matches_fp64_product_of_oracle_decode(name, rows, cols, batc
     xw = _bf16(rng.standard_normal(batch * cols)).reshape(batch, cols)
     X64 = _as_f64(xw)
     Y_ref = X64 @ W64.T
-    bound = 2 * (cols + 8) * 2.0 ** -24 * (np.abs(X64) @ np.abs(W64).T)
+    bound = 2 * (cols + 16) * 2.0 ** -24 * (np.abs(X64) @ np.abs(W64).T)
     plan = codec.FixedPlan(blob)
     x = torch.from_numpy(xw.view(np.int16).copy()).cuda()
     ys = []
