@@ -325,6 +325,20 @@ typedef struct {
  * BS_E_INVAL (NULL), BS_E_NOMEM. */
 bs_status bs_fixed_encode_host(const uint16_t* h_words, uint64_t n, uint32_t threads, bs_blob** out);
 
+/* Largest fixed-width blob of n weights (every weight an escape). */
+uint64_t bs_fixed_max_bytes(uint64_t n);
+
+/* The same blob as bs_fixed_encode_host, built on the GPU from n BF16 words in
+ * device memory (d_words, 16-B aligned) into d_out (16-B aligned, capacity
+ * bytes): a symbol-count kernel, the table on the host, an escape-count
+ * kernel per block, the block offsets on the host, then a pack kernel (one
+ * wavefront per block).  *out_len receives the blob's length (also when the
+ * capacity is too small; bs_fixed_max_bytes(n) always suffices).  Meant for
+ * initialisation: it allocates device scratch and synchronises `stream`.
+ * Errors: BS_E_INVAL, BS_E_NOSPACE, BS_E_NOMEM, BS_E_HIP. */
+bs_status bs_fixed_encode_device(const void* d_words, uint64_t n, void* d_out, uint64_t capacity, uint64_t* out_len,
+                                 void* stream);
+
 /* Validate the header of a fixed-width blob and describe it.  h_header: a
  * host copy of at least its first 96 bytes (header_len of them readable);
  * blob_len: the whole blob's length.  Checks the magic, version, block count,

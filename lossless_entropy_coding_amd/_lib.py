@@ -115,6 +115,9 @@ SIGNATURES = {
     "bs_gemv_async": (C.c_int, [C.c_void_p, C.c_uint32, C.c_uint64, C.c_uint64, C.c_void_p, C.c_void_p, C.c_void_p,
                                 C.c_void_p]),
     "bs_fixed_encode_host": (C.c_int, [C.c_void_p, C.c_uint64, C.c_uint32, C.POINTER(C.c_void_p)]),
+    "bs_fixed_max_bytes": (C.c_uint64, [C.c_uint64]),
+    "bs_fixed_encode_device": (C.c_int, [C.c_void_p, C.c_uint64, C.c_void_p, C.c_uint64, C.POINTER(C.c_uint64),
+                                         C.c_void_p]),
     "bs_fixed_info_get": (C.c_int, [C.c_void_p, C.c_uint64, C.c_uint64, C.POINTER(FixedInfo)]),
     "bs_fixed_decode_async": (C.c_int, [C.POINTER(FixedInfo), C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p,
                                         C.c_void_p]),

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbs.so")
 ARCH = "gfx950"
 
-SOURCES = ["bs_kernels.hip", "bs_decode.hip", "bs_fixed.hip", "bs_encode.hip", "bs_fixed.cpp", "bs_model.cpp", "bs_codec.cpp", "bs_plan.cpp", "bs_stream.cpp",
+SOURCES = ["bs_kernels.hip", "bs_decode.hip", "bs_fixed.hip", "bs_fixed_encode.hip", "bs_encode.hip", "bs_fixed.cpp", "bs_model.cpp", "bs_codec.cpp", "bs_plan.cpp", "bs_stream.cpp",
            "bs_sha256.cpp"]
 # packed FP32 instructions are disabled on purpose for every HIP compile
 HIP_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall",

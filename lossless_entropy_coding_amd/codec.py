@@ -311,6 +311,20 @@ def fixed_encode(words, threads: int = 0) -> bytes:
         L.lib().bs_blob_free(blob)
 
 
+def fixed_encode_device(words: torch.Tensor, stream=None) -> torch.Tensor:
+    """The fixed-width form of device-resident BF16 words (int16 or bfloat16
+    cuda tensor), built on the GPU (bs_fixed_encode_device); returns the blob
+    as a uint8 cuda tensor."""
+    w = words.contiguous().reshape(-1)
+    n = w.numel()
+    out = torch.empty(max(L.lib().bs_fixed_max_bytes(n), 16), dtype=torch.uint8, device=w.device)
+    ln = C.c_uint64()
+    L.check(L.lib().bs_fixed_encode_device(C.c_void_p(w.data_ptr()) if n else None, n, C.c_void_p(out.data_ptr()),
+                                           out.numel(), C.byref(ln), C.c_void_p(_stream_handle(stream))),
+            "bs_fixed_encode_device")
+    return out[: ln.value]
+
+
 def fixed_info(blob: bytes, blob_len: int | None = None) -> L.FixedInfo:
     info = L.FixedInfo()
     L.check(L.lib().bs_fixed_info_get(blob, len(blob), len(blob) if blob_len is None else blob_len, C.byref(info)),
@@ -321,12 +335,16 @@ def fixed_info(blob: bytes, blob_len: int | None = None) -> L.FixedInfo:
 class FixedPlan:
     """A fixed-width blob resident in HBM and its validated header."""
 
-    def __init__(self, blob: bytes, device: str = "cuda"):
-        self.info = fixed_info(blob)
+    def __init__(self, blob, device: str = "cuda"):
+        if isinstance(blob, torch.Tensor):          # a blob already in device memory
+            self.dev = blob
+            self.info = fixed_info(blob[:96].cpu().numpy().tobytes(), blob.numel())
+        else:
+            self.info = fixed_info(blob)
+            self.dev = torch.frombuffer(bytearray(blob), dtype=torch.uint8).to(device)
         self.n = self.info.n
         self.bytes = self.info.bytes
-        self.dev = torch.frombuffer(bytearray(blob), dtype=torch.uint8).to(device)
-        self.status = torch.zeros(max(self.info.n_blocks, 1), dtype=torch.int32, device=device)
+        self.status = torch.zeros(max(self.info.n_blocks, 1), dtype=torch.int32, device=self.dev.device)
 
     def new_output(self) -> torch.Tensor:
         return torch.empty(max(self.n, 8), dtype=torch.int16, device=self.dev.device)

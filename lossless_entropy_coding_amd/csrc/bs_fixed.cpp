@@ -15,6 +15,7 @@
 
 #include "bs_device.h"
 #include "bs_fixed_device.h"
+#include "bs_encode_device.h"
 #include "bs_internal.h"
 
 using namespace bs;
@@ -151,6 +152,84 @@ bs_status bs_fixed_encode_host(const uint16_t* w, uint64_t n, uint32_t threads, 
     } catch (const std::bad_alloc&) {
         set_error("out of host memory");
         return BS_E_NOMEM;
+    }
+}
+
+uint64_t bs_fixed_max_bytes(uint64_t n) {
+    const uint64_t nb = fixed_blocks(n);
+    return align_up(fixed_esc_off(nb) + 2 * n, 16);
+}
+
+bs_status bs_fixed_encode_device(const void* d_words, uint64_t n, void* d_out, uint64_t capacity, uint64_t* out_len,
+                                 void* stream) {
+    if (!out_len || (!d_words && n) || !d_out) { set_error("NULL argument"); return BS_E_INVAL; }
+    if (((uintptr_t)d_words | (uintptr_t)d_out) & 15) { set_error("words and output must be 16-B aligned"); return BS_E_INVAL; }
+    hipStream_t hs = (hipStream_t)stream;
+    const uint64_t nb = fixed_blocks(n);
+    const uint64_t esc_off = fixed_esc_off(nb);
+    // scratch: 512 symbol counts, the code of each symbol, escapes and first escape of each block
+    const uint64_t o_codes = 512 * 8, o_esc = align_up(o_codes + 512, 256), o_first = align_up(o_esc + 4 * nb, 256);
+    uint8_t* d_s = nullptr;
+    hipError_t e = hipMalloc(&d_s, o_first + 4 * nb + 16);
+    if (e != hipSuccess) { set_error("transcoder scratch: %s", hipGetErrorString(e)); return BS_E_NOMEM; }
+    auto done = [&](bs_status rc) { (void)hipStreamSynchronize(hs); (void)hipFree(d_s); return rc; };
+    auto hip = [&](hipError_t he, const char* what) { set_error("%s: %s", what, hipGetErrorString(he)); return done(BS_E_HIP); };
+    try {
+        std::vector<uint64_t> cs(512, 0);
+        int ke = bsk_zero(d_s, 512 * 8, stream);
+        if (!ke) ke = bsk_fixed_sym_count((const uint16_t*)d_words, n, (unsigned long long*)d_s, stream);
+        if (ke) return hip((hipError_t)ke, "symbol counts");
+        e = hipMemcpyAsync(cs.data(), d_s, 512 * 8, hipMemcpyDeviceToHost, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        if (e != hipSuccess) return hip(e, "symbol counts");
+        uint16_t table[16];
+        const uint32_t m = fixed_table(cs.data(), table);
+        uint8_t code_of[512];
+        memset(code_of, (int)kEscapeCode, sizeof code_of);
+        for (uint32_t k = 0; k < m; k++) code_of[table[k]] = (uint8_t)k;
+        std::vector<uint32_t> esc(nb), first(nb + 1, 0);
+        e = hipMemcpyAsync(d_s + o_codes, code_of, 512, hipMemcpyHostToDevice, hs);
+        if (e != hipSuccess) return hip(e, "symbol codes");
+        ke = bsk_fixed_block_esc((const uint16_t*)d_words, n, d_s + o_codes, nb, (uint32_t*)(d_s + o_esc), stream);
+        if (ke) return hip((hipError_t)ke, "escape counts");
+        if (nb) e = hipMemcpyAsync(esc.data(), d_s + o_esc, 4 * nb, hipMemcpyDeviceToHost, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        if (e != hipSuccess) return hip(e, "escape counts");
+        uint64_t n_esc = 0;
+        for (uint64_t b = 0; b < nb; b++) { first[b] = (uint32_t)n_esc; n_esc += esc[b]; }
+        if (n_esc > 0xFFFFFFFFull) { set_error("more than 2^32 - 1 escapes"); return done(BS_E_INVAL); }
+        const uint64_t len = align_up(esc_off + 2 * n_esc, 16);
+        *out_len = len;
+        if (capacity < len) {
+            set_error("capacity %llu < %llu", (unsigned long long)capacity, (unsigned long long)len);
+            return done(BS_E_NOSPACE);
+        }
+        std::vector<uint8_t> head(bsd::kFixHeader, 0), tail(len - esc_off - 2 * n_esc, 0);
+        memcpy(head.data(), kFixMagic, 8);
+        wr32(head.data() + 8, kFixVersion);
+        wr64(head.data() + 16, n);
+        wr64(head.data() + 24, nb);
+        wr64(head.data() + 32, esc_off);
+        wr64(head.data() + 40, n_esc);
+        for (uint32_t k = 0; k < 16; k++) wr16(head.data() + 64 + 2 * k, table[k]);
+        uint8_t* o = (uint8_t*)d_out;
+        e = hipMemcpyAsync(o, head.data(), head.size(), hipMemcpyHostToDevice, hs);
+        if (e == hipSuccess && nb)
+            e = hipMemcpyAsync(o + bsd::kFixHeader + (uint64_t)bsd::kFixBlockBytes * nb, first.data(), 4 * nb,
+                               hipMemcpyHostToDevice, hs);
+        if (e == hipSuccess && nb) e = hipMemcpyAsync(d_s + o_first, first.data(), 4 * nb, hipMemcpyHostToDevice, hs);
+        if (e == hipSuccess && !tail.empty())
+            e = hipMemcpyAsync(o + esc_off + 2 * n_esc, tail.data(), tail.size(), hipMemcpyHostToDevice, hs);
+        if (e != hipSuccess) return hip(e, "transcoder header");
+        ke = bsk_fixed_pack((const uint16_t*)d_words, n, d_s + o_codes, nb, (const uint32_t*)(d_s + o_first), o, esc_off,
+                            stream);
+        if (ke) return hip((hipError_t)ke, "pack");
+        e = hipStreamSynchronize(hs);                 // the host buffers above must outlive the copies
+        if (e != hipSuccess) return hip(e, "transcode");
+        return done(BS_OK);
+    } catch (const std::bad_alloc&) {
+        set_error("out of host memory");
+        return done(BS_E_NOMEM);
     }
 }
 

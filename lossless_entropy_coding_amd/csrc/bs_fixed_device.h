@@ -61,3 +61,15 @@ int bsk_fixed_gemm(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
 // of kFixWaves waves, each workgroup striding over the row groups
 int bsk_fixed_gemv(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
 }
+
+// Launchers (bs_fixed_encode.hip): the fixed-width form built on the GPU.
+extern "C" {
+// 512 (sign, exponent) symbol counts added into counts (zeroed by the caller)
+int bsk_fixed_sym_count(const uint16_t* w, uint64_t n, unsigned long long* counts, void* stream);
+// escapes of each block, given the code of every symbol (15 = escape)
+int bsk_fixed_block_esc(const uint16_t* w, uint64_t n, const uint8_t* code_of, uint64_t n_blocks, uint32_t* esc,
+                        void* stream);
+// the code and fraction planes of every block, and the escapes from each block's first
+int bsk_fixed_pack(const uint16_t* w, uint64_t n, const uint8_t* code_of, uint64_t n_blocks, const uint32_t* first,
+                   uint8_t* blob, uint64_t esc_off, void* stream);
+}

@@ -284,3 +284,45 @@ def test_fixed_gemm_argument_errors():
     assert f(*args(64, 2048, 4, x.data_ptr())) == L.BS_OK
     torch.cuda.synchronize()
     assert float(y.abs().max()) == 0.0
+
+
+# --------------------------------------------------------------------------- built on the GPU
+@pytest.mark.parametrize("name,n", CASES, ids=[c[0] for c in CASES])
+def test_fixed_encode_device_equals_host_transcoder(name, n):
+    """The blob built on the GPU from device words is the host transcoder's
+    (and therefore the oracle's) byte for byte."""
+    say("fixed device encode", name)
+    words = _case_words(name, n, n)
+    host = codec.fixed_encode(words)
+    d = codec.fixed_encode_device(torch.from_numpy(words.view(np.int16).copy()).cuda())
+    torch.cuda.synchronize()
+    assert d.cpu().numpy().tobytes() == host
+    plan = codec.FixedPlan(d)                      # a plan over the device blob itself
+    out = plan.decode()
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy().view(np.uint16) == words).all()
+
+
+def test_fixed_encode_device_from_decoded_container():
+    # derived from the canonical container: rANS decode on the GPU, then the fixed form on the GPU
+    wl = synth.cfg2("cpu")
+    words = synth.as_words(wl.items[0].tensor).numpy().view(np.uint16).reshape(-1)
+    c = codec.encode([codec.bf16(words)], codec.params(chunk_weights=131072, lanes=2048, stream_lanes=64))
+    dec = codec.Plan(c).decode()
+    blob = codec.fixed_encode_device(dec[: 2 * words.size].view(torch.int16))
+    torch.cuda.synchronize()
+    assert blob.cpu().numpy().tobytes() == O.fixed_encode(words)
+
+
+def test_fixed_encode_device_capacity():
+    import ctypes as C
+    words = torch.from_numpy(_case_words("uniform", 5000, 3).view(np.int16).copy()).cuda()
+    need = len(codec.fixed_encode(words.cpu().numpy().view(np.uint16)))
+    out = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ln = C.c_uint64()
+    rc = L.lib().bs_fixed_encode_device(C.c_void_p(words.data_ptr()), 5000, C.c_void_p(out.data_ptr()), need - 16,
+                                        C.byref(ln), None)
+    assert rc == L.BS_E_NOSPACE and ln.value == need
+    rc = L.lib().bs_fixed_encode_device(C.c_void_p(words.data_ptr()), 5000, C.c_void_p(out.data_ptr()), need,
+                                        C.byref(ln), None)
+    assert rc == L.BS_OK and ln.value == need

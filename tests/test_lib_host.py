@@ -281,3 +281,14 @@ def test_streamer_argument_checks_before_any_device_call():
     assert L.lib().bs_streamer_acquire(None, 0, None, C.byref(out)) == L.BS_E_INVAL
     assert L.lib().bs_streamer_release(None, 0, None) == L.BS_E_INVAL
     assert L.lib().bs_plan_rebind(None, C.c_void_p(4096)) == L.BS_E_INVAL
+
+
+def test_fixed_device_transcoder_argument_checks():
+    import ctypes as C
+    assert L.lib().bs_fixed_max_bytes(0) == 96
+    assert L.lib().bs_fixed_max_bytes(2048) == -(-(96 + 2820 + 4096) // 16) * 16
+    f = L.lib().bs_fixed_encode_device
+    ln = C.c_uint64()
+    assert f(C.c_void_p(4096), 10, C.c_void_p(8192), 1 << 20, None, None) == L.BS_E_INVAL          # no out_len
+    assert f(C.c_void_p(4098), 10, C.c_void_p(8192), 1 << 20, C.byref(ln), None) == L.BS_E_INVAL  # misaligned
+    assert f(None, 10, C.c_void_p(8192), 1 << 20, C.byref(ln), None) == L.BS_E_INVAL              # no words
