@@ -10,7 +10,9 @@
 //   - a copy into a staging buffer waits for the decode that last read it;
 //   - a decode waits for its copy and for the last release of the slot's
 //     previous layer;
-//   - a hit from another stream waits for the slot's decode.
+//   - a hit from another stream waits for the slot's decode, and so does a
+//     decode into a slot whose last decode ran on another stream (a layer
+//     prefetched there and never acquired has no release to wait for).
 // Every buffer is allocated at creation; nothing on the acquire path
 // allocates or synchronises the host.
 #include <hip/hip_runtime.h>
@@ -48,6 +50,7 @@ struct bs_streamer {
     std::vector<uint32_t> pins;
     std::vector<uint64_t> stamp;                // last use, for LRU
     std::vector<hipStream_t> decoded_on;
+    std::vector<uint8_t> decoded_ever;          // ev_ready recorded at all
     std::vector<int64_t> layer_slot;            // slot of a layer, -1 if not resident
     uint64_t clock = 0;
     bs_streamer_stats st{};
@@ -101,6 +104,8 @@ bs_status load(bs_streamer* s, uint32_t layer, uint32_t k, hipStream_t stream) {
     if (e == hipSuccess) e = hipEventRecord(s->ev_copied[j], s->copy_stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(stream, s->ev_copied[j], 0);
     if (e == hipSuccess && s->free_ever[k]) e = hipStreamWaitEvent(stream, s->ev_free[k], 0);
+    if (e == hipSuccess && s->decoded_ever[k] && s->decoded_on[k] != stream)
+        e = hipStreamWaitEvent(stream, s->ev_ready[k], 0);
     if (e != hipSuccess) return hip_fail(e, "streamer copy");
     if (s->slot_layer[k] >= 0) {
         s->layer_slot[s->slot_layer[k]] = -1;
@@ -119,6 +124,7 @@ bs_status load(bs_streamer* s, uint32_t layer, uint32_t k, hipStream_t stream) {
     s->slot_layer[k] = layer;
     s->layer_slot[layer] = k;
     s->decoded_on[k] = stream;
+    s->decoded_ever[k] = 1;
     s->free_recorded[k] = 0;
     s->st.h2d_bytes += s->len[layer];
     return BS_OK;
@@ -230,6 +236,7 @@ bs_status bs_streamer_create(const void* const* h_containers, const uint64_t* le
     s->pins.assign(s->n_slots, 0);
     s->stamp.assign(s->n_slots, 0);
     s->decoded_on.assign(s->n_slots, nullptr);
+    s->decoded_ever.assign(s->n_slots, 0);
     s->layer_slot.assign(n_layers, -1);
     s->st.n_layers = n_layers;
     s->st.n_slots = s->n_slots;

@@ -147,6 +147,27 @@ def test_two_streams():
         s.release(layer, stream=sa)
 
 
+def test_prefetched_slots_evicted_from_another_stream():
+    # both slots hold layers decoded on sa and never acquired; each later
+    # acquire on sb reuses one of them and must wait for sa's decode there
+    containers, expect = _layers(4, seed=50)
+    s = codec.Streamer(containers, _two_slot_budget(containers))
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    s.prefetch(0, stream=sa)
+    s.prefetch(1, stream=sa)
+    copies = {}
+    for layer in (2, 3):
+        v = s.acquire(layer, stream=sb)
+        with torch.cuda.stream(sb):
+            copies[layer] = v.clone()
+        s.release(layer, stream=sb)
+    torch.cuda.synchronize()
+    for layer, c in copies.items():
+        _check(c, expect[layer])
+    st = s.stats()
+    assert (st["misses"], st["evictions"]) == (4, 2)
+
+
 def test_budget_and_argument_errors():
     containers, _ = _layers(2, seed=40)
     budget = _two_slot_budget(containers)
