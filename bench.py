@@ -224,8 +224,9 @@ def gemv_bench(a):
 def fixed_bench(a):
     """The fixed-width lane-stream form of every BF16 record of the workload,
     derived on the GPU (bs_fixed_encode_device) from the GPU decode of the
-    canonical container, then decoded by bs_fixed_decode_async (one launch per
-    record).  Reports decoded GB/s, the kernel's HBM roofline fraction and
+    canonical container, then decoded by bs_fixed_decode_async (one tensor) or
+    bs_fixed_decode_many_async (up to 16 tensors per launch; the same tensors
+    in one launch each are timed beside it).  Reports decoded GB/s, the kernel's HBM roofline fraction and
     bits/weight, next to the rANS decode of the same container, and the
     transcoding time on the GPU and with the host transcoder (whose bytes must
     be the same)."""
@@ -265,15 +266,33 @@ def fixed_bench(a):
     refs = [d for _, d in decs]
     n = sum(p.n for p in plans)
     blob_bytes = sum(p.bytes for p in plans)
-    steps = [p.bound_decode(o, status=False, stream=stream) for p, o in zip(plans, outs)]
+    # one launch for a single tensor; several tensors in launches of up to
+    # FIXED_MANY_MAX blobs each (bs_fixed_decode_many_async)
+    groups = [list(range(i, min(i + L.FIXED_MANY_MAX, len(plans)))) for i in range(0, len(plans), L.FIXED_MANY_MAX)]
+    many = len(plans) > 1
+    if many:
+        steps = [codec.bound_fixed_decode_many([plans[i] for i in g], [outs[i] for i in g], stream=stream)
+                 for g in groups]
+    else:
+        steps = [plans[0].bound_decode(outs[0], status=False, stream=stream)]
+    per_tensor = [p.bound_decode(o, status=False, stream=stream) for p, o in zip(plans, outs)]
 
     def step():
         for s_ in steps:
             s_()
 
+    def step_per_tensor():
+        for s_ in per_tensor:
+            s_()
+
     def check():
-        for p, o, r in zip(plans, outs, refs):
-            p.decode_into(o, stream=stream)
+        for o in outs:
+            o.fill_(-1)
+        if many:
+            for g in groups:
+                codec.fixed_decode_many([plans[i] for i in g], [outs[i] for i in g], stream=stream)
+        else:
+            plans[0].decode_into(outs[0], stream=stream)
         torch.cuda.synchronize()
         for p, o, r in zip(plans, outs, refs):
             if not torch.equal(o[: p.n], r) or int(p.status[: p.info.n_blocks].abs().sum()) != 0:
@@ -296,6 +315,11 @@ def fixed_bench(a):
     check()
     wall, dev_s = timed(step)
     check()
+    per_tensor_launches = None
+    if many:
+        pt_wall, pt_dev = timed(step_per_tensor)
+        per_tensor_launches = {"launches": len(plans), "value": round(2 * n / pt_wall / 1e9, 2),
+                               "avg_step_ms": round(pt_dev * 1e3, 4)}
     rans_wall, rans_dev = timed(job.fast_decoder(stream))
     alg = blob_bytes + 2 * n
     achieved = alg / dev_s / 1e9          # algorithmic bytes over the launches' device time
@@ -344,12 +368,13 @@ def fixed_bench(a):
             "value": round(2 * n / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
             "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "dtype": "u32", "data": "synthetic",
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "fixed_decode_kernel",
-                         "traffic": measured_traffic(f"fixed|{job.name}", "fixed") if len(plans) == 1 else None,
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "kernel": "fixed_decode_many_kernel" if many else "fixed_decode_kernel",
+                         "traffic": measured_traffic(f"fixed|{job.name}", "fixed"),
                          "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                         "alg_bytes_per_step": alg, "launches_per_step": len(plans),
+                         "alg_bytes_per_step": alg, "launches_per_step": len(steps),
                          "avg_step_ms": round(dev_s * 1e3, 4)},
-            "bits_per_weight": round(8 * blob_bytes / n, 4),
+            "bits_per_weight": round(8 * blob_bytes / n, 4), "per_tensor_launches": per_tensor_launches,
             "rans": {"value": round(2 * n / rans_wall / 1e9, 2), "avg_step_ms": round(rans_dev * 1e3, 4),
                      "bits_per_weight": round(job.bits_per_weight, 4)},
             "transcode_s_gpu": round(t_transcode_gpu, 4), "transcode_s_host": round(t_transcode, 2),

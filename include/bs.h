@@ -360,6 +360,20 @@ bs_status bs_fixed_info_get(const void* h_header, uint64_t header_len, uint64_t 
 bs_status bs_fixed_decode_async(const bs_fixed_info* info, const void* d_blob, void* d_out, uint64_t out_capacity,
                                 uint32_t* d_status, void* stream);
 
+/* Decode up to BS_FIXED_MANY_MAX fixed-width blobs in one kernel launch (a
+ * layer's tensors, say): blob i as bs_fixed_decode_async(&infos[i],
+ * d_blobs[i], d_outs[i], out_capacities[i], d_status ? d_status[i] : NULL).
+ * The launch's workgroups are shared among the blobs in proportion to their
+ * blocks (at least one each), so the blobs decode side by side and the
+ * launch ends once, with no tail per tensor.  Blobs with n = 0 are skipped;
+ * outputs must not overlap.  Every argument is checked before anything is
+ * enqueued.  Errors: BS_E_INVAL (count above BS_FIXED_MANY_MAX, NULL,
+ * alignment, an info not from bs_fixed_info_get), BS_E_NOSPACE, BS_E_HIP. */
+#define BS_FIXED_MANY_MAX 16
+bs_status bs_fixed_decode_many_async(const bs_fixed_info* infos, const void* const* d_blobs, void* const* d_outs,
+                                     const uint64_t* out_capacities, uint32_t* const* d_status, uint32_t count,
+                                     void* stream);
+
 /* Fused decode and matrix-vector product on a fixed-width blob [NVLC card,
  * runtime paragraphs: the compressed-only runtime multiplies with weights
  * decoded where they are used and keeps no decoded copy]: y[r] = sum over c

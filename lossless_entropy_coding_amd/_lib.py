@@ -22,6 +22,7 @@ BS_E_HIP = -6
 BS_E_CORRUPT = -7
 BS_E_MISMATCH = -8
 BS_E_EXISTS = -9
+FIXED_MANY_MAX = 16          # blobs per bs_fixed_decode_many_async call
 
 KIND_BF16 = 1
 KIND_RAW = 2
@@ -121,6 +122,8 @@ SIGNATURES = {
     "bs_fixed_info_get": (C.c_int, [C.c_void_p, C.c_uint64, C.c_uint64, C.POINTER(FixedInfo)]),
     "bs_fixed_decode_async": (C.c_int, [C.POINTER(FixedInfo), C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p,
                                         C.c_void_p]),
+    "bs_fixed_decode_many_async": (C.c_int, [C.POINTER(FixedInfo), C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
+                                             C.POINTER(C.c_uint64), C.POINTER(C.c_void_p), C.c_uint32, C.c_void_p]),
     "bs_fixed_gemv_async": (C.c_int, [C.POINTER(FixedInfo), C.c_void_p, C.c_uint64, C.c_uint64, C.c_void_p,
                                       C.c_void_p, C.c_void_p, C.c_void_p]),
     "bs_fixed_gemm_async": (C.c_int, [C.POINTER(FixedInfo), C.c_void_p, C.c_uint64, C.c_uint64, C.c_uint32,

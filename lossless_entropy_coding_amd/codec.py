@@ -448,6 +448,39 @@ class FixedPlan:
 
 
 # --------------------------------------------------------------------------- layer streaming
+def _many_args(plans, outs, status, stream):
+    k = len(plans)
+    if len(outs) != k:
+        raise ValueError("one output per blob")
+    infos = (L.FixedInfo * max(k, 1))(*[p.info for p in plans])
+    blobs = (C.c_void_p * max(k, 1))(*[p.dev.data_ptr() for p in plans])
+    dst = (C.c_void_p * max(k, 1))(*[o.data_ptr() for o in outs])
+    caps = (C.c_uint64 * max(k, 1))(*[o.numel() * o.element_size() for o in outs])
+    st = (C.c_void_p * max(k, 1))(*[p.status.data_ptr() for p in plans]) if status else None
+    args = (infos, blobs, dst, caps, st, C.c_uint32(k), C.c_void_p(_stream_handle(stream)))
+    return args, (infos, blobs, dst, caps, st, list(outs), [(p.dev, p.status) for p in plans])
+
+
+def fixed_decode_many(plans, outs, status: bool = True, stream=None) -> None:
+    """Enqueue the decode of up to FIXED_MANY_MAX fixed-width blobs (FixedPlan
+    objects) into their outputs in one launch (bs_fixed_decode_many_async)."""
+    args, _ = _many_args(plans, outs, status, stream)
+    L.check(L.lib().bs_fixed_decode_many_async(*args), "bs_fixed_decode_many_async")
+
+
+def bound_fixed_decode_many(plans, outs, status: bool = False, stream=None):
+    """fixed_decode_many with its ctypes arguments converted once."""
+    f = L.lib().bs_fixed_decode_many_async
+    args, keep = _many_args(plans, outs, status, stream)
+
+    def run():
+        rc = f(*args)
+        if rc:
+            L.check(rc, "bs_fixed_decode_many_async")
+        return keep
+    return run
+
+
 class Streamer:
     """Layers streamed on demand under a device-memory budget (bs_streamer_*):
     the containers live in the streamer's pinned host memory; acquire()

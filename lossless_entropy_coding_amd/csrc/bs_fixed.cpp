@@ -283,13 +283,59 @@ bs_status bs_fixed_decode_async(const bs_fixed_info* info, const void* d_blob, v
     return BS_OK;
 }
 
+static_assert(bsd::kFixManyMax == BS_FIXED_MANY_MAX, "the header's limit is the kernel's");
+
+bs_status bs_fixed_decode_many_async(const bs_fixed_info* infos, const void* const* d_blobs, void* const* d_outs,
+                                     const uint64_t* out_capacities, uint32_t* const* d_status, uint32_t count,
+                                     void* stream) {
+    if (count > bsd::kFixManyMax) { set_error("%u blobs in one call (at most %u)", count, bsd::kFixManyMax); return BS_E_INVAL; }
+    if (count && (!infos || !d_blobs || !d_outs || !out_capacities)) { set_error("NULL argument"); return BS_E_INVAL; }
+    bsd::FixedMany m;
+    memset(&m, 0, sizeof m);
+    uint64_t blocks = 0;
+    for (uint32_t i = 0; i < count; i++) {
+        const bs_fixed_info* info = &infos[i];
+        if (!d_outs[i] && info->n) { set_error("NULL output %u", i); return BS_E_INVAL; }
+        if ((uintptr_t)d_outs[i] & 15) { set_error("output %u must be 16-B aligned", i); return BS_E_INVAL; }
+        bsd::FixedArgs a;
+        const bs_status rc = fixed_args(info, d_blobs[i], a);
+        if (rc != BS_OK) return rc;
+        if (out_capacities[i] < 2 * info->n) {
+            set_error("output %u capacity %llu < %llu", i, (unsigned long long)out_capacities[i],
+                      (unsigned long long)(2 * info->n));
+            return BS_E_NOSPACE;
+        }
+        if (info->n == 0) continue;
+        a.out = (uint16_t*)d_outs[i];
+        a.status = d_status ? d_status[i] : nullptr;
+        m.a[m.count++] = a;
+        blocks += info->n_blocks;
+    }
+    if (m.count == 0) return BS_OK;
+    // workgroups in proportion to blocks: at least one per tensor, never more
+    // than its blocks need
+    const uint64_t total = fixed_groups(blocks);
+    uint32_t g = 0;
+    for (uint32_t k = 0; k < m.count; k++) {
+        const uint64_t nb = m.a[k].n_blocks;
+        const uint64_t need = (nb + bsd::kFixWaves - 1) / bsd::kFixWaves;
+        const uint64_t share = std::max<uint64_t>(1, (uint64_t)((unsigned __int128)total * nb / blocks));
+        m.wg_start[k] = g;
+        g += (uint32_t)std::min(need, share);
+    }
+    m.wg_start[m.count] = g;
+    const int e = bsk_fixed_decode_many(&m, stream);
+    if (e != 0) { set_error("fixed decode launch: %s", hipGetErrorString((hipError_t)e)); return BS_E_HIP; }
+    return BS_OK;
+}
+
 bs_status bs_fixed_gemv_async(const bs_fixed_info* info, const void* d_blob, uint64_t rows, uint64_t cols,
                               const void* d_x, float* d_y, uint32_t* d_status, void* stream) {
     bsd::FixedArgs a;
     const bs_status rc = fixed_args(info, d_blob, a);
     if (rc != BS_OK) return rc;
     if (!d_x || !d_y) { set_error("NULL argument"); return BS_E_INVAL; }
-    if (cols == 0 || cols % 32 || cols >= (1ull << 26) || rows * cols != info->n || rows > info->n) {
+    if (cols == 0 || cols % 32 || cols >= (1ull << 26) || info->n % cols || rows != info->n / cols) {
         set_error("a %llu x %llu matrix does not fit %llu weights with columns a multiple of 32 below 2^26",
                   (unsigned long long)rows, (unsigned long long)cols, (unsigned long long)info->n);
         return BS_E_INVAL;
@@ -326,7 +372,7 @@ bs_status bs_fixed_gemm_async(const bs_fixed_info* info, const void* d_blob, uin
     const bs_status rc = fixed_args(info, d_blob, a);
     if (rc != BS_OK) return rc;
     if (!d_x || !d_y) { set_error("NULL argument"); return BS_E_INVAL; }
-    if (cols == 0 || cols % bsd::kFixBlockW || cols >= (1ull << 26) || rows * cols != info->n || rows > info->n) {
+    if (cols == 0 || cols % bsd::kFixBlockW || cols >= (1ull << 26) || info->n % cols || rows != info->n / cols) {
         set_error("a %llu x %llu matrix does not fit %llu weights with columns a multiple of 2048 below 2^26",
                   (unsigned long long)rows, (unsigned long long)cols, (unsigned long long)info->n);
         return BS_E_INVAL;

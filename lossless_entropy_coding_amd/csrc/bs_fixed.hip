@@ -191,20 +191,11 @@ __device__ __forceinline__ void build_lut(const FixedArgs& a, uint32_t t, uint32
 }
 
 // decode: one wave per block at a time, out written with 16-B stores
-__global__ __launch_bounds__(64 * kFixWaves, 8) void fixed_decode_kernel(FixedArgs a) {
-    __shared__ uint32_t lut[256];
-    __shared__ __attribute__((aligned(16))) uint32_t stage[kFixWaves][kFixBlockW / 2];
-    __shared__ __attribute__((aligned(4))) uint16_t escl[kFixWaves][kFixEscLds];
-
-    const uint32_t t = threadIdx.x, lane = t & 63u;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    build_lut(a, t, lut);
-    __syncthreads();
-
-    uint32_t* st = stage[wave];
-    uint16_t* el = escl[wave];
-    for (uint64_t blk = (uint64_t)blockIdx.x * kFixWaves + wave; blk < a.n_blocks;
-         blk += (uint64_t)gridDim.x * kFixWaves) {
+// Blocks g*4 + wave, then every (ng*4)-th after, of one tensor: decoded,
+// staged in LDS and stored (the LUT of that tensor already in LDS).
+__device__ __forceinline__ void decode_blocks(const FixedArgs& a, uint32_t g, uint32_t ng, uint32_t wave,
+                                              uint32_t lane, const uint32_t* lut, uint32_t* st, uint16_t* el) {
+    for (uint64_t blk = (uint64_t)g * kFixWaves + wave; blk < a.n_blocks; blk += (uint64_t)ng * kFixWaves) {
         const uint32_t bad = finish_block(a, load_block(a, blk, lane), lane, lut, st, el);
         // out: 16-B pieces in order, 1 KiB per store instruction; the last,
         // partial block word by word
@@ -226,6 +217,39 @@ __global__ __launch_bounds__(64 * kFixWaves, 8) void fixed_decode_kernel(FixedAr
         }
         write_status(a, blk, bad, lane);
     }
+}
+
+__global__ __launch_bounds__(64 * kFixWaves, 8) void fixed_decode_kernel(FixedArgs a) {
+    __shared__ uint32_t lut[256];
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kFixWaves][kFixBlockW / 2];
+    __shared__ __attribute__((aligned(4))) uint16_t escl[kFixWaves][kFixEscLds];
+
+    const uint32_t t = threadIdx.x, lane = t & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    build_lut(a, t, lut);
+    __syncthreads();
+    decode_blocks(a, blockIdx.x, gridDim.x, wave, lane, lut, stage[wave], escl[wave]);
+}
+
+// Several tensors in one launch: tensor i owns workgroups wg_start[i] ..
+// wg_start[i + 1] - 1 (a share of the grid in proportion to its blocks), so
+// each workgroup builds one LUT and the tails of the tensors overlap instead
+// of each ending its own launch.
+__global__ __launch_bounds__(64 * kFixWaves, 8) void fixed_decode_many_kernel(const FixedMany m) {
+    __shared__ uint32_t lut[256];
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kFixWaves][kFixBlockW / 2];
+    __shared__ __attribute__((aligned(4))) uint16_t escl[kFixWaves][kFixEscLds];
+
+    uint32_t i = 0;
+    for (uint32_t k = 1; k < m.count; k++)
+        if (m.wg_start[k] <= blockIdx.x) i = k;
+    const FixedArgs& a = m.a[i];
+    const uint32_t t = threadIdx.x, lane = t & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    build_lut(a, t, lut);
+    __syncthreads();
+    decode_blocks(a, blockIdx.x - m.wg_start[i], m.wg_start[i + 1] - m.wg_start[i], wave, lane, lut, stage[wave],
+                  escl[wave]);
 }
 
 // The fused product: workgroup g takes row groups g, g + groups, ...: a
@@ -402,6 +426,13 @@ __global__ __launch_bounds__(64 * kGemmWaves) void fixed_gemm_kernel(FixedArgs a
 }
 
 }  // namespace
+
+extern "C" int bsk_fixed_decode_many(const FixedMany* m, void* stream) {
+    if (m->count == 0 || m->wg_start[m->count] == 0) return 0;
+    hipLaunchKernelGGL(fixed_decode_many_kernel, dim3(m->wg_start[m->count]), dim3(64 * kFixWaves), 0,
+                       (hipStream_t)stream, *m);
+    return (int)hipGetLastError();
+}
 
 extern "C" int bsk_fixed_gemm(const FixedArgs* args, uint32_t n_groups, void* stream) {
     if (n_groups == 0 || args->rows == 0) return 0;

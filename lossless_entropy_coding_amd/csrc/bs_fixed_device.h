@@ -41,6 +41,15 @@ struct FixedArgs {
     uint32_t reserved;
 };
 
+// several tensors decoded in one launch: tensor i takes workgroups
+// wg_start[i] .. wg_start[i + 1] - 1 (every tensor at least one)
+constexpr uint32_t kFixManyMax = 16;
+struct FixedMany {
+    FixedArgs a[kFixManyMax];
+    uint32_t wg_start[kFixManyMax + 1];
+    uint32_t count;
+};
+
 #ifndef BS_GEMM_WAVES
 #define BS_GEMM_WAVES 16
 #endif
@@ -54,6 +63,8 @@ extern "C" {
 // decode a fixed-width blob: n_groups workgroups of kFixWaves waves, each wave
 // striding over the blocks
 int bsk_fixed_decode(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
+// decode up to kFixManyMax blobs in one launch of wg_start[count] workgroups
+int bsk_fixed_decode_many(const bsd::FixedMany* m, void* stream);
 // the fused product of a fixed-width blob with a batch of vectors: one
 // workgroup of kGemmWaves waves per 16 rows (n_groups workgroups, striding)
 int bsk_fixed_gemm(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);

@@ -107,6 +107,63 @@ def test_fixed_writes_nothing_past_n():
     assert (h[words.size:] == 0x5A5A).all()
 
 
+MANY_SETS = {
+    # every case above in one launch (blobs from 1 weight to 655K), plus an empty one
+    "all_cases": [(nm, n) for nm, n in CASES] + [("zeros_empty", 0)],
+    # the most a call takes, all ragged: workgroups split 16 ways
+    "sixteen_ragged": [("gauss", 2048 * (3 * i + 1) + 7 * i + 1) for i in range(16)],
+    # one large tensor beside tiny ones: the tiny ones still get a workgroup
+    "skewed": [("gauss", 1), ("gauss", 2048 * 400 + 3), ("uniform", 5), ("wide", 2049)],
+}
+
+
+@pytest.mark.parametrize("set_name", list(MANY_SETS))
+def test_fixed_decode_many_matches_oracle(set_name):
+    say("fixed many", set_name)
+    plans, outs, expects, guards = [], [], [], []
+    for i, (nm, n) in enumerate(MANY_SETS[set_name]):
+        words = _case_words(nm, n, 1000 + i)
+        blob = codec.fixed_encode(words)
+        expect = O.fixed_decode(blob)
+        assert (expect == words).all()
+        plans.append(codec.FixedPlan(blob))
+        # 4 KiB of guard words past each output: nothing may be written there
+        outs.append(torch.full((n + 2048,), 0x5A5A, dtype=torch.int16, device="cuda"))
+        expects.append(expect)
+    codec.fixed_decode_many(plans, outs)
+    torch.cuda.synchronize()
+    for plan, out, expect in zip(plans, outs, expects):
+        h = out.cpu().numpy().view(np.uint16)
+        bad = np.flatnonzero(h[: expect.size] != expect)
+        assert bad.size == 0, (expect.size, bad[:8])
+        assert (h[expect.size:] == 0x5A5A).all()
+        assert (plan.block_status() == 0).all()
+    # the same launch again into dirty buffers, no status: the same words
+    for out in outs:
+        out.fill_(-1)
+    codec.fixed_decode_many(plans, outs, status=False)
+    torch.cuda.synchronize()
+    for out, expect in zip(outs, expects):
+        assert (out.cpu().numpy().view(np.uint16)[: expect.size] == expect).all()
+
+
+def test_fixed_decode_many_reports_a_corrupt_blob():
+    # the status words of a corrupted blob flag its block; the others stay clean
+    w0, w1 = _case_words("gauss", 3 * 2048, 1), _case_words("wide", 5 * 2048 + 9, 2)
+    plans = [codec.FixedPlan(codec.fixed_encode(w0)), codec.FixedPlan(codec.fixed_encode(w1))]
+    assert plans[1].info.n_esc > 0
+    blob1 = codec.fixed_encode(w1)
+    at = plans[1].info.esc_off - 4 * plans[1].info.n_blocks + 4 * 2   # block 2's first escape
+    _corrupt_device(plans[1], at, "<I", struct.unpack_from("<I", blob1, at)[0] + 1)
+    outs = [torch.empty(w.size, dtype=torch.int16, device="cuda") for w in (w0, w1)]
+    codec.fixed_decode_many(plans, outs)
+    torch.cuda.synchronize()
+    assert (outs[0].cpu().numpy().view(np.uint16) == w0).all()
+    assert (plans[0].block_status() == 0).all()
+    st = plans[1].block_status()
+    assert st[2] != 0
+
+
 def _corrupt_device(plan, off, fmt, value):
     b = bytearray(plan.dev.cpu().numpy().tobytes())
     struct.pack_into(fmt, b, off, value)

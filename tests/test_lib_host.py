@@ -263,6 +263,34 @@ def test_fixed_decode_argument_checks_before_launch():
     assert f(C.byref(empty), C.c_void_p(4096), None, 0, None, None) == L.BS_OK     # nothing to do
 
 
+def test_fixed_decode_many_argument_checks_before_launch():
+    import ctypes as C
+    w = _words(np.random.default_rng(6).standard_normal(5000) * 0.02)
+    info = codec.fixed_info(codec.fixed_encode(w))
+    empty = codec.fixed_info(codec.fixed_encode(np.zeros(0, np.uint16)))
+    f = L.lib().bs_fixed_decode_many_async
+
+    def call(infos, blobs, outs, caps, count=None):
+        k = len(infos)
+        ia = (L.FixedInfo * max(k, 1))(*infos)
+        ba = (C.c_void_p * max(k, 1))(*blobs)
+        oa = (C.c_void_p * max(k, 1))(*outs)
+        ca = (C.c_uint64 * max(k, 1))(*caps)
+        return f(ia, ba, oa, ca, None, k if count is None else count, None)
+
+    assert call([], [], [], []) == L.BS_OK                                        # nothing to do
+    assert call([empty, empty], [4096, 8192], [None, None], [0, 0]) == L.BS_OK
+    assert call([info], [4096], [4096], [10000], count=L.FIXED_MANY_MAX + 1) == L.BS_E_INVAL
+    assert f(None, None, None, None, None, 1, None) == L.BS_E_INVAL
+    assert call([empty, info], [4096, 4100], [4096, 8192], [0, 10000]) == L.BS_E_INVAL   # blob alignment
+    assert call([info, info], [4096, 8192], [4096, 8200], [10000, 10000]) == L.BS_E_INVAL  # output alignment
+    assert call([info, info], [4096, 8192], [4096, None], [10000, 10000]) == L.BS_E_INVAL  # NULL output
+    assert call([info, info], [4096, 8192], [4096, 8192], [10000, 9999]) == L.BS_E_NOSPACE
+    forged = L.FixedInfo.from_buffer_copy(info)
+    forged.esc_off += 4
+    assert call([info, forged], [4096, 8192], [4096, 8192], [10000, 10000]) == L.BS_E_INVAL
+
+
 def test_streamer_argument_checks_before_any_device_call():
     import ctypes as C
     f = L.lib().bs_streamer_create
