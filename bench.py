@@ -535,7 +535,7 @@ def stream_bench(a):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py measures one GPU only: this build decodes on a single MI355X and has no multi-GPU "
+        print(f"bench.py measures one GPU only: the library decodes on one MI355X and has no multi-GPU "
               f"path (asked for --gpus {a.gpus}). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch

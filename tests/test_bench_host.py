@@ -1,0 +1,63 @@
+"""bench.py host logic: the one-GPU refusal and the HBM traffic records.
+
+The traffic figure in a bench line comes from committed rocprofv3 counter
+passes; it is only reported while the kernel source it was measured on is
+unchanged.  These tests pin that the committed records match the current
+kernel sources (so the default bench line carries a measured figure) and
+that a changed source or an unknown workload gives null.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("args,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_more_than_one_gpu_exits_with_a_message(args, env):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                       env={**os.environ, **env}, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def _records():
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+        return json.load(f)
+
+
+def test_committed_traffic_records_match_the_kernel_sources():
+    rec = _records()
+    assert rec["workloads"], "no traffic records"
+    for key, w in rec["workloads"].items():
+        kind = "fixed" if key.startswith("fixed|") else "decode_kernel"
+        assert w["kernel_source_sha256"] == bench.kernel_source_sha256(kind), key
+        assert bench.measured_traffic(key, kind) == w["traffic_bytes"]
+        # counters close to the algorithmic bytes: nothing re-read
+        assert 1.0 <= w["traffic_bytes"] / w["alg_bytes"] < 1.03, key
+        assert w["traffic_bytes"] == w["fetch_bytes"] + w["write_bytes"]
+
+
+def test_default_workload_has_a_traffic_record():
+    keys = list(_records()["workloads"])
+    assert any(k.startswith("cfg2_4096x4096") for k in keys)
+
+
+def test_unknown_workload_or_changed_source_gives_null(monkeypatch):
+    assert bench.measured_traffic("no such workload") is None
+    key = next(k for k in _records()["workloads"] if not k.startswith("fixed|"))
+    monkeypatch.setattr(bench, "kernel_source_sha256", lambda kind: "0" * 64)
+    assert bench.measured_traffic(key) is None
+
+
+def test_copy_calibration_scales():
+    rec = _records()
+    # a plain copy reads back half its bytes in FETCH_SIZE and all of them in WRITE_SIZE
+    assert rec["fetch_scale"] == pytest.approx(2.0, abs=0.01)
+    assert rec["write_scale"] == pytest.approx(1.0, abs=0.01)
