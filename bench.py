@@ -192,10 +192,27 @@ def gemv_bench(a):
     def plain():
         torch.mv(W, x)
 
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if a.cold else None
+
     def timed(fn):
         for _ in range(a.warmup):
             fn()
         torch.cuda.synchronize()
+        if flush is not None:
+            # cold caches: a 1 GiB write before each step, outside the timing
+            wall_s, dev_s_ = 0.0, 0.0
+            for _ in range(a.steps):
+                flush.fill_(1)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                t_s = time.perf_counter()
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                wall_s += time.perf_counter() - t_s
+                dev_s_ += e0.elapsed_time(e1) * 1e-3
+            return wall_s / a.steps, dev_s_ / a.steps
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(a.steps):
@@ -381,7 +398,7 @@ def fixed_bench(a):
             "transcode_note": "GPU: device words to device blob, including the blob's read-back-free layout; host: "
                               "from host words (the copy to the host not included)", "gemv": gemv,
             "config": {"workload": job.name, "bf16_weights": n, "tensors": len(plans),
-                       "escapes": sum(p.info.n_esc for p in plans)}}
+                       "escapes": sum(p.info.n_esc for p in plans), "cold_cache": bool(a.cold)}}
     print(json.dumps(line))
 
 

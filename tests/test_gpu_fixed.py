@@ -147,6 +147,25 @@ def test_fixed_decode_many_matches_oracle(set_name):
         assert (out.cpu().numpy().view(np.uint16)[: expect.size] == expect).all()
 
 
+def test_fixed_decode_many_full_layer():
+    # the Gemma-2-9B-shaped layer at full size (7 matrices, 198M weights) in
+    # one launch, the configuration the fixed-width bench times: every word
+    # against the source tensors, and the oracle's decode of one whole blob
+    wl = synth.cfg3("cpu")
+    words = [synth.as_words(it.tensor).numpy().view(np.uint16) for it in wl.items if it.kind == "bf16"]
+    say("fixed many, full layer", [w.size for w in words])
+    blobs = [codec.fixed_encode(w) for w in words]
+    k = min(range(len(words)), key=lambda i: words[i].size)
+    assert (O.fixed_decode(blobs[k]) == words[k]).all()
+    plans = [codec.FixedPlan(b) for b in blobs]
+    outs = [torch.empty(w.size, dtype=torch.int16, device="cuda") for w in words]
+    codec.fixed_decode_many(plans, outs)
+    torch.cuda.synchronize()
+    for w, o, p in zip(words, outs, plans):
+        assert torch.equal(o, torch.from_numpy(w.view(np.int16)).cuda())
+        assert (p.block_status() == 0).all()
+
+
 def test_fixed_decode_many_reports_a_corrupt_blob():
     # the status words of a corrupted blob flag its block; the others stay clean
     w0, w1 = _case_words("gauss", 3 * 2048, 1), _case_words("wide", 5 * 2048 + 9, 2)
