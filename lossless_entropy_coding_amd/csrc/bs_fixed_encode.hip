@@ -25,14 +25,38 @@ using namespace bsd;
 
 namespace {
 
+// Eight interleaved copies of the 512 counters (copy k of bin b at 8 b + k;
+// lane l adds to copy l mod 8): the few hot symbols of a weight tensor then
+// spread over eight LDS banks instead of queueing on one.  Words are read 8
+// at a time (16-B loads; the words are 16-B aligned), the ragged tail one by
+// one.
+constexpr uint32_t kCountCopies = 8;
+
 __global__ __launch_bounds__(256) void sym_count_kernel(const uint16_t* w, uint64_t n, unsigned long long* counts) {
-    __shared__ uint32_t c[512];
-    for (uint32_t i = threadIdx.x; i < 512; i += 256) c[i] = 0;
+    __shared__ uint32_t c[512 * kCountCopies];
+    for (uint32_t i = threadIdx.x; i < 512 * kCountCopies; i += 256) c[i] = 0;
     __syncthreads();
-    for (uint64_t j = blockIdx.x * 256ull + threadIdx.x; j < n; j += 256ull * gridDim.x) atomicAdd(&c[w[j] >> 7], 1u);
+    uint32_t* mine = c + (threadIdx.x & (kCountCopies - 1));
+    const uint64_t n8 = n / 8, stride = 256ull * gridDim.x;
+    const uint4* w8 = (const uint4*)w;
+    for (uint64_t j = blockIdx.x * 256ull + threadIdx.x; j < n8; j += stride) {
+        const uint4 v = w8[j];
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            atomicAdd(mine + kCountCopies * ((d[k] >> 7) & 511u), 1u);   // low word's symbol
+            atomicAdd(mine + kCountCopies * (d[k] >> 23), 1u);            // high word's symbol
+        }
+    }
+    for (uint64_t j = 8 * n8 + blockIdx.x * 256ull + threadIdx.x; j < n; j += stride)
+        atomicAdd(mine + kCountCopies * (w[j] >> 7), 1u);
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < 512; i += 256)
-        if (c[i]) atomicAdd(counts + i, (unsigned long long)c[i]);
+    for (uint32_t i = threadIdx.x; i < 512; i += 256) {
+        uint32_t t = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kCountCopies; k++) t += c[kCountCopies * i + k];
+        if (t) atomicAdd(counts + i, (unsigned long long)t);
+    }
 }
 
 // escapes of each block (code 15 <-> code_of[s] == 15)
