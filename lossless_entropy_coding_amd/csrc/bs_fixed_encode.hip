@@ -69,9 +69,21 @@ __global__ __launch_bounds__(256) void block_esc_kernel(const uint16_t* w, uint6
     const uint64_t blk = blockIdx.x * 4ull + (threadIdx.x >> 6);
     if (blk >= n_blocks) return;
     uint32_t cnt = 0;
-    for (uint32_t i = 0; i < 32; i++) {
-        const uint64_t j = blk * kFixBlockW + 64ull * i + lane;     // coalesced: 64 consecutive weights per step
-        if (j < n) cnt += cmap[w[j] >> 7] == 15;
+#pragma unroll
+    for (uint32_t i = 0; i < 4; i++) {
+        // lane l takes words 8 l .. 8 l + 7 of each 512-word quarter: one
+        // 16-B load (the words are 16-B aligned), 1 KiB per load instruction
+        const uint64_t j = blk * kFixBlockW + 512ull * i + 8ull * lane;
+        if (j + 8 <= n) {
+            const uint4 v = *(const uint4*)(w + j);
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; k++)
+                cnt += (cmap[(d[k] >> 7) & 511u] == 15) + (cmap[d[k] >> 23] == 15);
+        } else {
+            for (uint32_t e = 0; e < 8; e++)
+                if (j + e < n) cnt += cmap[w[j + e] >> 7] == 15;
+        }
     }
     for (int off = 32; off; off >>= 1) cnt += __shfl_xor(cnt, off);
     if (lane == 0) esc[blk] = cnt;
