@@ -29,13 +29,25 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def cold_flush(buf) -> None:
+    """Leave the GPU caches cold and clean before a timed launch: write a
+    1 GiB buffer (evicting what the launch would find cached), then read it
+    back, so that the dirty lines of the write are written back here and not
+    during the timed launch.  Enqueued on the current stream without a host
+    synchronisation: the timed launch queues behind it, so the GPU is busy up
+    to the launch and no host launch latency enters the launch's events."""
+    import torch
+    buf.fill_(1)
+    buf.sum(dtype=torch.int64)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5"])
-    ap.add_argument("--cold", action="store_true", help="write a 1 GiB buffer between timed decodes (not in the timing)")
+    ap.add_argument("--cold", action="store_true", help="write and read back a 1 GiB buffer before each timed decode (not in the timing): cold, clean caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle baseline")
     ap.add_argument("--cfg5-layers", type=int, default=84, help="config 5: layers to build (84 = full checkpoint)")
@@ -192,27 +204,10 @@ def gemv_bench(a):
     def plain():
         torch.mv(W, x)
 
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if a.cold else None
-
     def timed(fn):
         for _ in range(a.warmup):
             fn()
         torch.cuda.synchronize()
-        if flush is not None:
-            # cold caches: a 1 GiB write before each step, outside the timing
-            wall_s, dev_s_ = 0.0, 0.0
-            for _ in range(a.steps):
-                flush.fill_(1)
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                t_s = time.perf_counter()
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                wall_s += time.perf_counter() - t_s
-                dev_s_ += e0.elapsed_time(e1) * 1e-3
-            return wall_s / a.steps, dev_s_ / a.steps
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(a.steps):
@@ -316,10 +311,25 @@ def fixed_bench(a):
                 log("FIXED DECODE MISMATCH")
                 sys.exit(1)
 
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if a.cold else None
+
     def timed(fn):
         for _ in range(a.warmup):
             fn()
         torch.cuda.synchronize()
+        if flush is not None:
+            # cold caches: a 1 GiB write and read-back before each step, outside the timing
+            # (device time only: the flushes run between the launches)
+            dev_s_ = 0.0
+            for _ in range(a.steps):
+                cold_flush(flush)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                dev_s_ += e0.elapsed_time(e1) * 1e-3
+            return dev_s_ / a.steps, dev_s_ / a.steps
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t_s = time.perf_counter()
         e0.record(stream)
@@ -721,20 +731,20 @@ def main():
         wall = time.perf_counter() - t_start
         avg_ms = e_start.elapsed_time(e_end) / a.steps
     else:
-        # cold HBM/L2: a 1 GiB write between steps, outside the timing
-        wall, dev_ms = 0.0, 0.0
+        # cold caches: a 1 GiB write and read-back between steps, outside the
+        # timing; the value is then from device time (the flushes run between
+        # the launches, so host time would count them)
+        dev_ms = 0.0
         for _ in range(a.steps):
-            flush.fill_(1)
-            torch.cuda.synchronize()
+            cold_flush(flush)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t_s = time.perf_counter()
             e0.record(stream)
             step()
             e1.record(stream)
             torch.cuda.synchronize()
-            wall += time.perf_counter() - t_s
             dev_ms += e0.elapsed_time(e1)
         avg_ms = dev_ms / a.steps
+        wall = dev_ms * 1e-3
     ok, detail = job.verify()
     if not ok:
         log("VERIFY FAILED after timing", detail)
