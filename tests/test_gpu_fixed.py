@@ -6,7 +6,8 @@ canonical model]; decoding it must give back every BF16 word bit for bit.
 Every blob here is built by the library's host transcoder, checked byte for
 byte against the oracle's encoder, and every GPU output is compared with the
 oracle's decode of the same blob.  All calls go through the C ABI
-(bs_fixed_info_get, bs_fixed_decode_async).
+(bs_fixed_info_get, bs_fixed_decode_async, bs_fixed_decode_many_async,
+bs_fixed_gemv_async, bs_fixed_gemm_async, bs_fixed_encode_device).
 """
 import struct
 import sys
