@@ -82,6 +82,14 @@ def test_normaliser_over_sum_reduction():
     assert q.tolist() == [14, 1, 1]
 
 
+def test_normaliser_over_sum_tie_takes_lower_index():
+    # 500:500:1:1:1 at M=4 (1003 words): floors 7,7,0,0,0 -> 7,7,1,1,1 = 17,
+    # one over; the two largest q tie at 7 and the lower index gives the slot up
+    assert O.normalise([500, 500, 1, 1, 1], 4).tolist() == [6, 7, 1, 1, 1]
+    # the same counts in reverse order: the tie again resolves to the lower index
+    assert O.normalise([1, 1, 1, 500, 500], 4).tolist() == [1, 1, 1, 6, 7]
+
+
 def test_context_choice_zero_spike_and_flat():
     cs = np.zeros(512, np.uint64)
     cf = np.zeros((512, 128), np.uint64)
@@ -130,6 +138,39 @@ def test_context_choice_respects_cmax_and_score_order():
     route, nt, qf = O.select_tables(cs, cf, 10, 6)
     assert nt == 6
     assert [int(route[e] > 0) for e in range(100, 108)] == [0, 0, 1, 1, 1, 1, 1, 1]
+
+
+def test_context_choice_score_tie_takes_lower_exponent():
+    # three exponents with identical skewed fraction counts have equal scores;
+    # with room for two tables the two lower exponents are chosen
+    cs = np.zeros(512, np.uint64)
+    cf = np.zeros((512, 128), np.uint64)
+    w = np.exp(-np.linspace(0, 3.0, 128))
+    c = np.round(w / w.sum() * 300000).astype(np.uint64)
+    for e in (100, 101, 102):
+        cf[e] = c
+        cs[e] = c.sum()
+    route, nt, qf = O.select_tables(cs, cf, 10, 2)
+    assert nt == 2
+    assert [int(route[e]) for e in (100, 101, 102)] == [1, 2, 0]
+
+
+def test_context_choice_candidates_reach_64_exponents():
+    # 39 exponents with exactly flat fractions (never eligible) outnumber one
+    # exponent whose 1000 words all share fraction 5 (eligible: 256 E > n^2 +
+    # 726784 n with E = 127 n^2).  That exponent ranks 40th by count, inside the
+    # 64 candidates, so it gets the only table.
+    cs = np.zeros(512, np.uint64)
+    cf = np.zeros((512, 128), np.uint64)
+    for e in range(60, 99):
+        cf[e, :] = 100
+        cs[e] = 12800
+    cf[20, 5] = 1000
+    cs[20] = 1000
+    route, nt, qf = O.select_tables(cs, cf, 10, 6)
+    assert nt == 1
+    assert route[20] == 1 and all(route[e] == 0 for e in range(60, 99))
+    assert qf[0, 5] == 1024
 
 
 def test_record_shape_rule():

@@ -51,6 +51,11 @@ MUTANTS = {
     "phase_order_swapped": ("for (int phase = 1; phase >= 0; phase--) {", "for (int phase = 0; phase <= 1; phase++) {"),
     "sign_in_wrong_place": ("return (uint16_t)((sign << 15) | (expo << 7) | f);", "return (uint16_t)((sign << 7) | (expo << 8) | f);"),
     "normalise_tie_high_index": ("(rem[ib] == rem[ibest] && ib < ibest)", "(rem[ib] == rem[ibest] && ib > ibest)"),
+    "normalise_over_sum_tie_high": ("if (q[i] > 1 && (best == A || q[i] > q[best])) best = i;",
+                                    "if (q[i] > 1 && (best == A || q[i] >= q[best])) best = i;"),
+    "context_score_tie_high": ("(score[k] == score[best] && cand[k] < cand[best])) best = (int)k;",
+                               "(score[k] == score[best] && cand[k] > cand[best])) best = (int)k;"),
+    "context_candidates_32": ("#define BSO_CANDIDATES 64u", "#define BSO_CANDIDATES 32u"),
     "normalise_no_floor_one": ("q[i] = (uint32_t)(v < 1 ? 1 : v);", "q[i] = (uint32_t)v;"),
     "table_always_eligible": ("eligible[k] = (256 * E > n * n + (unsigned __int128)726784 * n);", "eligible[k] = 1;"),
     "signs_not_merged": ("unsigned __int128 m = (unsigned __int128)cf[e * 128 + f] + cf[(256 + e) * 128 + f];",
