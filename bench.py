@@ -5,9 +5,13 @@ empirical conditional entropy.
 
 A step is one decode of the whole workload (bs_decode_async over every
 record: the rANS decode kernel plus the verbatim residual copy), with the
-container already resident in HBM and the output buffer preallocated.
-The default workload is the 4096x4096 BF16 matrix with log-normal row scales,
-0.1% outliers and 1% exact zeros, in 256 KiB chunks.
+containers already resident in HBM and the output buffer preallocated.
+The default workload is the largest: the synthetic 27.7B-weight checkpoint
+(1,199 tensors in 84 layer containers plus one of trailing vectors, about
+36 GB compressed, all resident), decoded layer by layer into one reused
+buffer; every layer is compared with its original bytes on the device before
+and after the timing, and the CPU oracle decodes a chunk of every tensor
+(and more, within its time budget), each compared with the original words.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1|2|3|4|5] [--cold]
 """
@@ -44,9 +48,10 @@ def cold_flush(buf) -> None:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 20 for the checkpoint, 200 for the other workloads)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5"])
+    ap.add_argument("--config", default="5", choices=["1", "2", "3", "4", "5"])
     ap.add_argument("--cold", action="store_true", help="write and read back a 1 GiB buffer before each timed decode (not in the timing): cold, clean caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle baseline")
@@ -71,7 +76,10 @@ def parse():
                          "(bs_streamer_*), against copying the uncompressed layers")
     ap.add_argument("--stream-layers", type=int, default=12, help="--stream: layers of the checkpoint to build")
     ap.add_argument("--stream-slots", type=int, default=3, help="--stream: decoded layers the budget holds")
-    return ap.parse_args()
+    a = ap.parse_args()
+    if a.steps is None:
+        a.steps = 20 if a.config == "5" and not (a.gemv or a.fixed or a.encode or a.stream) else 200
+    return a
 
 
 TRAFFIC_SOURCES = {"decode_kernel": ("bs_decode.hip", "bs_device.h"), "fixed": ("bs_fixed.hip", "bs_fixed_device.h")}
@@ -126,52 +134,95 @@ def model_build_rate(job):
             "what": "bs_build_tables wall time: one HIP histogram pass, the counts read back, host quantisation"}
 
 
-def cpu_baseline(job, seconds: float):
-    """The CPU oracle (plain scalar C, not tuned) decoding the same container
-    on the host, in two legs over the same chunks: one thread for a third of
-    the budget, then a pool of threads (the host cores available, at most 16)
-    that take chunks in turn, each chunk decoded by one scalar call.  Returns
-    the pool's decoded BF16 GB/s, with the one-thread figure beside it."""
-    import threading
-    from oracle import oracle as O
-    from lossless_entropy_coding_amd import codec
-    containers = job.containers() if hasattr(job, "containers") else [job.enc.container]
-    tasks = []
-    for c in containers:
-        for i in range(int.from_bytes(c[12:16], "little")):
-            ri = codec.record_info(c, i)
-            if ri.kind == 1:
-                tasks += [(c, i, ch, int(ri.chunk_weights)) for ch in range(ri.n_chunks)]
+def _oracle_sources(job):
+    """(host container, device original bytes) pairs the oracle decodes from:
+    every layer of the checkpoint, else the job's one container."""
+    import torch
+    if hasattr(job, "oracle_samples"):
+        return [(dev.cpu().numpy(), ref) for dev, ref in job.oracle_samples()]
+    return [(np.frombuffer(job.enc.container, np.uint8), job.ref)]
 
-    def leg(threads: int, budget: float):
+
+def cpu_baseline(job, seconds: float):
+    """The CPU oracle (plain scalar C, not tuned) decoding the same
+    containers on the host, every decoded chunk compared with the original
+    words.  The tasks are the chunks of every BF16 record: first one chunk of
+    every tensor (a parity pass over all of them), then further chunks spread
+    over the records.  Two legs: one thread for a third of the budget, then a
+    pool of host threads (the process's CPU share) that take tasks in turn,
+    one scalar call per chunk, for the rest of the budget, and at least
+    through the parity pass.  Returns the pool's decoded BF16 GB/s with the
+    one-thread figure beside it; exits non-zero on any mismatch."""
+    import threading
+    import torch
+    from oracle import oracle as O
+    from lossless_entropy_coding_amd import checkpoint, codec
+    sources = _oracle_sources(job)
+    first, rest = [], []
+    for si, (c, _) in enumerate(sources):
+        info = codec.container_info(c)
+        for i in range(info.n_records):
+            ri = codec.record_info(c, i)
+            if ri.kind != 1 or ri.n_chunks == 0:
+                continue
+            first.append((si, i, 0, int(ri.out_offset), int(ri.chunk_weights)))
+            # the rest of the record's chunks, strided so that a prefix of the
+            # list samples the whole record
+            order = list(range(1, ri.n_chunks))
+            step = max(1, len(order) // 7)
+            order = order[::step] + [ch for ch in order if (ch - 1) % step]
+            rest += [(r, si, i, ch, int(ri.out_offset), int(ri.chunk_weights)) for r, ch in enumerate(order)]
+    # interleave the records' further chunks so that any prefix spans them all
+    rest.sort(key=lambda t: t[:3])
+    tasks = first + [t[1:] for t in rest]
+    mismatches = []
+
+    def run_task(k):
+        si, i, ch, off, W = tasks[k]
+        c, ref = sources[si]
+        w = O.decode_chunk(c, i, ch)     # the C call releases the GIL
+        a = off + 2 * ch * W
+        want = ref[a: a + 2 * w.size].cpu().numpy().view(np.uint16)
+        if not np.array_equal(w, want):
+            mismatches.append((si, i, ch))
+        return 2 * w.size
+
+    def leg(threads: int, budget: float, at_least: int):
         nxt, decoded, lock = [0], [0], threading.Lock()
         t0 = time.perf_counter()
 
         def work():
-            while time.perf_counter() - t0 < budget:
+            while True:
                 with lock:
                     k = nxt[0]
+                    if k >= len(tasks) or (k >= at_least and time.perf_counter() - t0 > budget):
+                        return
                     nxt[0] += 1
-                if k >= len(tasks):
-                    return
-                w = O.decode_chunk(*tasks[k])     # the C call releases the GIL
+                b = run_task(k)
                 with lock:
-                    decoded[0] += 2 * w.size
+                    decoded[0] += b
         pool = [threading.Thread(target=work) for _ in range(threads)]
         for th in pool:
             th.start()
         for th in pool:
             th.join()
-        dt = time.perf_counter() - t0
-        return decoded[0], dt, min(nxt[0], len(tasks))
+        return decoded[0], time.perf_counter() - t0, min(nxt[0], len(tasks))
 
-    d1, t1, n1 = leg(1, seconds / 3)
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    dT, tT, nT = leg(cores, 2 * seconds / 3)
-    log(f"cpu baseline: 1 thread {d1 / 1e6:.1f} MB in {t1:.1f}s; {cores} threads {dT / 1e6:.1f} MB in {tT:.1f}s")
+    d1, t1, n1 = leg(1, seconds / 3, 1)
+    cores = checkpoint.host_threads()
+    dT, tT, nT = leg(cores, 2 * seconds / 3, len(first))
+    log(f"cpu baseline: 1 thread {d1 / 1e6:.1f} MB in {t1:.1f}s; {cores} threads {dT / 1e6:.1f} MB in {tT:.1f}s; "
+        f"{nT} chunks checked, {len(mismatches)} mismatches")
+    if mismatches:
+        log("ORACLE MISMATCH", mismatches[:5])
+        sys.exit(1)
+    n_tensors = len(first)
     return {"value": round(dT / tT / 1e9, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"leading chunks of the workload: {nT} of {len(tasks)} chunks ({dT / 2:.0f} weights) "
-                      f"on {cores} threads, one chunk per call",
+            "sample": f"{nT} of {len(tasks)} chunks ({dT / 2:.0f} weights): one chunk of each of the {n_tensors} "
+                      f"BF16 tensors, then chunks spread over every record; {cores} threads, one chunk per call; "
+                      f"every chunk equal to the original words",
+            "affinity_cores": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+            "chunks_checked": nT, "tensors_checked": n_tensors, "mismatches": 0,
             "single_thread": {"value": round(d1 / t1 / 1e9, 5), "chunks": n1, "seconds": round(t1, 2)},
             "seconds": round(t1 + tT, 2)}
 
@@ -673,6 +724,9 @@ def main():
         return
     L.lib()   # fails loudly if the HIP library is missing
     if a.gemv:
+        if a.cold:
+            print("--cold is not supported with --gemv (its timer runs back to back)", file=sys.stderr)
+            sys.exit(2)
         gemv_bench(a)
         return
     if a.fixed:
@@ -787,7 +841,8 @@ def main():
                    "m_s": job.m_s, "m_f": job.m_f,
                    "bits_per_weight": round(job.bits_per_weight, 5), "entropy_bits": round(job.entropy_bits, 5),
                    "bits_over_entropy_pct": round(100 * (job.bits_per_weight / job.entropy_bits - 1), 3),
-                   "cold_cache": bool(a.cold), "parallelism": "single GPU"},
+                   "cold_cache": bool(a.cold), "parallelism": "single GPU",
+                   "tensors": getattr(job, "n_tensors", None), "container_bytes": job.container_bytes},
         "roofline": roofline,
         "model_build": model,
         "cpu_baseline": cpu,

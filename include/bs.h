@@ -151,7 +151,12 @@ typedef struct {
 
 typedef struct bs_blob bs_blob; /* opaque, library-owned byte buffer */
 
-/* Encode tensors[0..n_tensors) into one container, in order, on host threads.
+/* Encode tensors[0..n_tensors) into one container, in order, on host threads
+ * [Qwen3.8-27B-BF16-NVLC-Lossless card, codec paragraph after the metrics
+ * table: each BF16 word split into its exact fields, the (sign, exponent)
+ * symbol rANS-coded with a per-tensor model, the fraction coded with the
+ * distribution that symbol selects, a residual for non-BF16 spans; the
+ * chunk, lane and byte layout are this library's own (header comment)].
  * Output offsets are assigned in order, each rounded up to 256 B.  A BF16
  * tensor with more than 256 distinct (sign, exponent) symbols is stored as a
  * RAW record of its bytes.  The result is deterministic (independent of the
@@ -254,7 +259,10 @@ bs_status bs_plan_rebind(bs_plan* plan, const void* d_container);
 uint64_t bs_plan_container_bytes(const bs_plan* plan);
 
 /* Decode records [first, first + count) into d_out, enqueued on `stream`
- * (no host synchronisation).  Record i is written at
+ * (no host synchronisation) [Qwen3.8-27B-BF16-NVLC-Lossless card, codec
+ * paragraph: the (sign, exponent) symbol is decoded first, it selects the
+ * fraction's distribution, and the fields are recombined bitwise into the
+ * original word; non-BF16 spans come back verbatim from the residual].  Record i is written at
  * d_out + out_offset(i) - out_offset(first); the bytes between records are not
  * written.  d_out must be 16-B aligned with at least the returned
  * bs_plan_out_bytes(plan, first, count) bytes of capacity; nothing outside
@@ -492,7 +500,11 @@ typedef struct {
 } bs_report;
 
 /* Synchronise `stream`, then check records [first, first + count) of a
- * decode made with the same plan and range.  d_ref (BS_VERIFY_COMPARE) holds
+ * decode made with the same plan and range [Gemma 2 9B Instruct -- Lossless
+ * Compressed card, "What lossless means": every tensor is hash-checked after
+ * decompression; Qwen3.8-27B-BF16-NVLC-Lossless card, metrics table and
+ * SHA256SUMS block: per-codec and full inverse verification, sha256
+ * digests].  d_ref (BS_VERIFY_COMPARE) holds
  * the expected bytes laid out like d_out.  Returns BS_OK when every requested
  * check passes, BS_E_CORRUPT when a chunk status is bad, BS_E_MISMATCH when
  * bytes or a digest differ; the report is filled in every case.  Errors:

@@ -176,12 +176,18 @@ def record_info(container: bytes, i: int) -> L.RecordInfo:
 class Plan:
     """A container resident in HBM plus its decode plan (opaque bs_plan)."""
 
-    def __init__(self, container: bytes, device: str = "cuda", stream=None):
+    def __init__(self, container: bytes, device: str = "cuda", stream=None, dev: torch.Tensor | None = None):
+        """container: host bytes (header, tables and index are read from it);
+        dev: a device copy of the same bytes to decode from (uint8, 16-B
+        aligned), or None to upload `container`."""
         self.host = container
         self.info = container_info(container)
         self.n_records = self.info.n_records
-        # 16-byte aligned device copy (torch allocations are 256-B aligned)
-        self.dev = torch.frombuffer(bytearray(container), dtype=torch.uint8).to(device)
+        if dev is None:
+            # 16-byte aligned device copy (torch allocations are 256-B aligned)
+            dev = torch.frombuffer(bytearray(container), dtype=torch.uint8).to(device)
+        assert dev.dtype == torch.uint8 and dev.numel() == len(container) and dev.data_ptr() % 16 == 0
+        self.dev = dev
         out = C.c_void_p()
         L.check(L.lib().bs_plan_create(container, len(container), C.c_void_p(self.dev.data_ptr()),
                                        C.c_void_p(_stream_handle(stream)), C.byref(out)), "bs_plan_create")
