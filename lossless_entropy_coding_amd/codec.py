@@ -161,15 +161,26 @@ def encode_device(tensors, p: L.Params | None = None, stream=None, tables=None, 
     return out[:size]
 
 
-def container_info(container: bytes) -> L.ContainerInfo:
+def _host_bytes(container):
+    """(pointer argument, length) of a host container given as bytes or as a
+    uint8 numpy array."""
+    if isinstance(container, np.ndarray):
+        assert container.dtype == np.uint8 and container.flags.c_contiguous
+        return C.c_void_p(container.ctypes.data), container.size
+    return container, len(container)
+
+
+def container_info(container) -> L.ContainerInfo:
     info = L.ContainerInfo()
-    L.check(L.lib().bs_container_info_get(container, len(container), C.byref(info)), "bs_container_info_get")
+    ptr, n = _host_bytes(container)
+    L.check(L.lib().bs_container_info_get(ptr, n, C.byref(info)), "bs_container_info_get")
     return info
 
 
-def record_info(container: bytes, i: int) -> L.RecordInfo:
+def record_info(container, i: int) -> L.RecordInfo:
     info = L.RecordInfo()
-    L.check(L.lib().bs_record_info_get(container, len(container), i, C.byref(info)), "bs_record_info_get")
+    ptr, n = _host_bytes(container)
+    L.check(L.lib().bs_record_info_get(ptr, n, i, C.byref(info)), "bs_record_info_get")
     return info
 
 

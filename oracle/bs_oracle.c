@@ -29,6 +29,18 @@
  *           x = q * floor(x / 2^M) + slot - cum
  * with a 32-bit state kept in [2^16, 2^32) by 16-bit renormalisation words.
  *
+ * Two record layouts (both this container's own definitions):
+ *   layout 1 (container version 1): per weight, s is coded with the s-table
+ *     and then the whole 7-bit fraction f with the table s selects; each of
+ *     the two symbols is followed by a renormalisation check.
+ *   layout 2 (container version 2): per weight, s (precision M_s) and the
+ *     fraction's high three bits h = f >> 4 (precision M_h = 16 - M_s, with
+ *     the table s selects) are coded back to back and followed by a single
+ *     renormalisation check: the two steps consume at most 16 bits of the
+ *     state, so one 16-bit word always restores it.  The low four bits
+ *     l = f & 15 are stored verbatim in a fixed-width plane of the chunk.
+ *     The fraction's distribution given s is thus P(h | s) * 2^-4.
+ *
  * Parity pins live in tests/test_oracle_*.py (hand-computed coder states,
  * a bit-stack reduction, brute force, normaliser invariants, round trips).
  */
@@ -38,7 +50,9 @@
 
 #define BSO_L          65536u          /* lower end of the state interval */
 #define BSO_MAGIC      "BF16RANS"
-#define BSO_VERSION    1u
+#define BSO_VERSION    1u              /* containers whose BF16 records use layout 1 */
+#define BSO_VERSION2   2u              /* containers with layout-2 BF16 records */
+#define BSO_MAX_HTABLES 31u            /* coded h tables per layout-2 record */
 #define BSO_HDR_BYTES  64u
 #define BSO_DIR_BYTES  96u
 #define BSO_KIND_BF16  1u
@@ -240,6 +254,90 @@ int bso_select_tables(const uint64_t* cs, const uint64_t* cf, uint32_t M_f, uint
 }
 
 /* ------------------------------------------------------------------------ */
+/* floor(65536 log2 q) for 1 <= q <= 65536 (container rule, integer only).   */
+/* Binary logarithm by repeated squaring: with q = 2^k r, r in [1, 2), each  */
+/* squaring of r doubles its logarithm; r >= 2 after a squaring means the   */
+/* next fraction bit is 1 (and r is halved).  r is held in fixed point with  */
+/* 62 fraction bits; the products are exact in 128 bits and truncated back. */
+/* ------------------------------------------------------------------------ */
+uint32_t bso_log2_q16(uint32_t q) {
+    if (q == 0) return 0;
+    uint32_t k = 0;
+    while ((q >> (k + 1)) != 0) k++;
+    unsigned __int128 r = (unsigned __int128)q << (62 - k);   /* q / 2^k in Q62 */
+    uint32_t bits = 0;
+    for (int i = 0; i < 16; i++) {
+        r = (r * r) >> 62;
+        bits <<= 1;
+        if (r >= ((unsigned __int128)2 << 62)) { bits |= 1; r >>= 1; }
+    }
+    return (k << 16) | bits;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Layout 2: choice of the coded tables for h = f >> 4 (container rule).      */
+/* Both signs of an exponent e share a context, with merged counts           */
+/*   n_e = cs[e] + cs[256+e],  m_e[h] = sum over f = 16h .. 16h+15 of         */
+/*   cf[e][f] + cf[256+e][f].                                                 */
+/* Candidate table: q_e = normalise(m_e, M_h) over the 8 values of h.        */
+/* Bits it saves against the flat table (q = 2^(M_h-3) for every h), in     */
+/* units of 2^-16 bit:                                                       */
+/*   D_e = sum over h with m_e[h] > 0 of m_e[h] (L(q_e[h]) - 65536 (M_h-3))  */
+/* with L(q) = floor(65536 log2 q).  Eligible iff D_e > 65536 * 64 (the      */
+/* table's 8 bytes).  Selected: up to cmax eligible exponents with the       */
+/* largest D_e (lower e on ties); ids 1..k in ascending e.  route[s] = id of */
+/* s mod 256 when selected, else 0.  qh[(id-1)*8 + h] = q_e[h].              */
+/* ------------------------------------------------------------------------ */
+int bso_select_htables(const uint64_t* cs, const uint64_t* cf, uint32_t M_h, uint32_t cmax,
+                       uint32_t* route /*512*/, uint32_t* n_tables, uint32_t* qh /*cmax*8*/) {
+    if (cmax > BSO_MAX_HTABLES || M_h < 4 || M_h > 5) return BSO_EINVAL;
+    __int128 saved[256];
+    int eligible[256];
+    uint32_t qe[256][8];
+    for (uint32_t e = 0; e < 256; e++) {
+        eligible[e] = 0;
+        saved[e] = 0;
+        uint64_t m[8];
+        uint64_t n_e = cs[e] + cs[256 + e];
+        for (uint32_t h = 0; h < 8; h++) {
+            m[h] = 0;
+            for (uint32_t f = 16 * h; f < 16 * h + 16; f++) m[h] += cf[e * 128 + f] + cf[(256 + e) * 128 + f];
+        }
+        if (n_e == 0) continue;
+        int rc = bso_normalise(m, 8, M_h, qe[e]);
+        if (rc) return rc;
+        for (uint32_t h = 0; h < 8; h++) {
+            if (m[h] == 0) continue;
+            saved[e] += (__int128)m[h] * ((int64_t)bso_log2_q16(qe[e][h]) - 65536 * (int64_t)(M_h - 3));
+        }
+        eligible[e] = saved[e] > (__int128)65536 * 64;
+    }
+    int picked[256];
+    for (uint32_t e = 0; e < 256; e++) picked[e] = 0;
+    for (uint32_t k = 0; k < cmax; k++) {
+        int best = -1;
+        for (uint32_t e = 0; e < 256; e++) {
+            if (!eligible[e] || picked[e]) continue;
+            if (best < 0 || saved[e] > saved[best]) best = (int)e;
+        }
+        if (best < 0) break;
+        picked[best] = 1;
+    }
+    uint32_t id_of[256];
+    uint32_t id = 0;
+    for (uint32_t e = 0; e < 256; e++) {
+        id_of[e] = 0;
+        if (!picked[e]) continue;
+        id++;
+        id_of[e] = id;
+        for (uint32_t h = 0; h < 8; h++) qh[(id - 1) * 8 + h] = qe[e][h];
+    }
+    for (uint32_t s = 0; s < 512; s++) route[s] = cs[s] ? id_of[s % 256] : 0;
+    *n_tables = id;
+    return BSO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Lane/chunk shape of a record (container rule).                            */
 /* Records of n >= Wmax weights use W = Wmax, K = Kmax.  A smaller record is */
 /* one chunk whose lane count is the smallest power of two that keeps the   */
@@ -431,6 +529,8 @@ typedef struct {
     uint32_t route[512];
     uint32_t n_tables;
     uint32_t qf[1 + BSO_MAX_TABLES][128]; /* [0] is the flat table */
+    uint32_t layout;                      /* 1 or 2 */
+    uint32_t qh[1 + BSO_MAX_HTABLES][8];  /* layout 2 (M_f holds M_h): [0] is the flat table */
 } bso_model;
 
 static int chunk_encode(const bso_model* md, const uint16_t* w, uint32_t n_c, uint32_t K,
@@ -516,6 +616,159 @@ static int chunk_decode(const bso_model* md, const uint32_t* states_in, const ui
 }
 
 /* ------------------------------------------------------------------------ */
+/* Layout 2: one chunk, one renormalisation per weight.                      */
+/* The lanes, groups, macro-steps, streams and word order are those of       */
+/* layout 1, with one sub-step per weight: (t, p).  In a sub-step a lane     */
+/* decodes s with the s-table (precision M_s) and then h = f >> 4 with the   */
+/* table route[s] (precision M_h = 16 - M_s), with no renormalisation in     */
+/* between; then, if its state is below L, it takes one word.  In its last  */
+/* group (c = min(8, weights left) weights) a lane decodes s only: the h of  */
+/* those c weights are the low 3c bits of its start state (the first weight */
+/* lowest) under a leading one at bit max(16, 3c), read off the state it     */
+/* ends in.  The low fraction bits l = f & 15 are not in the stream.         */
+/* ------------------------------------------------------------------------ */
+
+/* The rANS coding step of one symbol, without renormalisation. */
+static void code_step(uint32_t* x, const bso_table* t, uint32_t sym) {
+    uint32_t q = t->q[sym], cum = table_cum(t, sym);
+    *x = (*x / q) * (1u << t->M) + (*x % q) + cum;
+}
+
+/* Its inverse: the symbol in the low M bits of *x, and the state before it. */
+static int decode_step(uint32_t* x, const bso_table* t, uint32_t* sym) {
+    uint32_t slot = *x & ((1u << t->M) - 1u);
+    uint32_t cum = 0, s = 0;
+    while (s < t->A && !(cum <= slot && slot < cum + t->q[s])) { cum += t->q[s]; s++; }
+    if (s == t->A) return BSO_ECORRUPT;
+    *sym = s;
+    *x = t->q[s] * (*x >> t->M) + slot - cum;
+    return BSO_OK;
+}
+
+/* Encode the pair (s, h): one flush check for both symbols, with the joint */
+/* frequency q_s q_h at precision M_s + M_h; then h is coded, then s (the   */
+/* decoder takes s first).                                                   */
+static int enc_pair_words(uint32_t* x, const bso_table* ts, uint32_t s, const bso_table* th, uint32_t h,
+                          wordlist* out) {
+    uint64_t q = (uint64_t)ts->q[s] * th->q[h];
+    if (q == 0) return BSO_EINVAL;
+    uint64_t x_max = q << (32 - ts->M - th->M);
+    if ((uint64_t)*x >= x_max) {
+        int rc = wl_push(out, (uint16_t)(*x & 0xFFFFu));
+        if (rc) return rc;
+        *x >>= 16;
+    }
+    code_step(x, th, h);
+    code_step(x, ts, s);
+    return BSO_OK;
+}
+
+/* the lane's last group and the number of weights c in it (0: no weights) */
+static uint32_t lane_last_group(uint32_t n_c, uint32_t K, uint32_t l, uint64_t* g_last) {
+    uint64_t groups = ((uint64_t)n_c + 7) / 8;
+    *g_last = 0;
+    if (l >= groups) return 0;
+    uint64_t g = l + (uint64_t)K * ((groups - 1 - l) / K);
+    *g_last = g;
+    uint64_t end = 8 * g + 8 < n_c ? 8 * g + 8 : (uint64_t)n_c;
+    return (uint32_t)(end - 8 * g);
+}
+
+static uint32_t split_lead(uint32_t c) { return 3 * c > 16 ? 3 * c : 16; }
+
+static int chunk_encode_split(const bso_model* md, const uint16_t* w, uint32_t n_c, uint32_t K,
+                              uint32_t l0, uint32_t l1, uint32_t* states, wordlist* wl) {
+    bso_table ts = { md->M_s, 512, md->qs };
+    uint32_t groups = (n_c + 7) / 8;
+    uint32_t T = (groups + K - 1) / K;
+    for (uint32_t l = l0; l < l1; l++) {
+        uint64_t g;
+        uint32_t c = lane_last_group(n_c, K, l, &g);
+        uint32_t x = c ? 1u << split_lead(c) : BSO_L;
+        for (uint32_t i = 0; i < c; i++) x |= (bso_symbol_f(w[8 * g + i]) >> 4) << (3 * i);
+        states[l] = x;
+    }
+    for (int64_t t = (int64_t)T - 1; t >= 0; t--) {
+        for (int p = 7; p >= 0; p--) {
+            for (int64_t l = (int64_t)l1 - 1; l >= (int64_t)l0; l--) {
+                uint64_t j = 8 * ((uint64_t)t * K + (uint64_t)l) + (uint64_t)p;
+                if (j >= n_c) continue;
+                uint64_t g;
+                lane_last_group(n_c, K, (uint32_t)l, &g);
+                uint32_t s = bso_symbol_s(w[j]);
+                int rc;
+                if (j / 8 == g) {
+                    rc = enc_symbol(&states[l], &ts, s, wl);
+                } else {
+                    bso_table th = { md->M_f, 8, md->qh[md->route[s]] };
+                    rc = enc_pair_words(&states[l], &ts, s, &th, bso_symbol_f(w[j]) >> 4, wl);
+                }
+                if (rc) return rc;
+            }
+        }
+    }
+    return BSO_OK;
+}
+
+/* Decodes s and h of every weight of lanes [l0, l1) into out[j] = s << 7 |  */
+/* h << 4 (the low fraction bits are added by the caller from the plane).    */
+static int chunk_decode_split(const bso_model* md, const uint32_t* states_in, const uint16_t* words,
+                              uint64_t nw, uint32_t n_c, uint32_t K, uint32_t l0, uint32_t l1, uint16_t* out) {
+    bso_table ts = { md->M_s, 512, md->qs };
+    uint32_t groups = (n_c + 7) / 8;
+    uint32_t T = (groups + K - 1) / K;
+    uint32_t* x = (uint32_t*)malloc(sizeof(uint32_t) * K);
+    if (!x) return BSO_ENOMEM;
+    for (uint32_t l = l0; l < l1; l++) x[l] = states_in[l];
+    uint64_t pos = 0;
+    int rc = BSO_OK;
+    for (uint32_t t = 0; t < T && !rc; t++) {
+        for (uint32_t p = 0; p < 8 && !rc; p++) {
+            for (uint32_t l = l0; l < l1 && !rc; l++) {
+                uint64_t j = 8 * ((uint64_t)t * K + l) + p;
+                if (j >= n_c) continue;
+                uint64_t g;
+                lane_last_group(n_c, K, l, &g);
+                uint32_t s, h = 0;
+                rc = decode_step(&x[l], &ts, &s);
+                if (!rc && j / 8 != g) {
+                    bso_table th = { md->M_f, 8, md->qh[md->route[s]] };
+                    rc = decode_step(&x[l], &th, &h);
+                }
+                if (rc) break;
+                out[j] = (uint16_t)((s << 7) | (h << 4));
+                if (x[l] < BSO_L) {
+                    if (pos >= nw) { rc = BSO_ECORRUPT; break; }
+                    x[l] = (x[l] << 16) | words[pos++];
+                }
+            }
+        }
+    }
+    /* every lane ends at its start state: the leading one over the h of its
+       last group (nothing else set), or L for a lane without weights */
+    for (uint32_t l = l0; l < l1 && !rc; l++) {
+        uint64_t g;
+        uint32_t c = lane_last_group(n_c, K, l, &g);
+        if (c == 0) { if (x[l] != BSO_L) rc = BSO_ECORRUPT; continue; }
+        uint32_t lead = split_lead(c);
+        if ((x[l] >> lead) != 1u || (x[l] - (1u << lead)) >= (1u << (3 * c))) { rc = BSO_ECORRUPT; continue; }
+        for (uint32_t i = 0; i < c; i++) out[8 * g + i] = (uint16_t)(out[8 * g + i] | (((x[l] >> (3 * i)) & 7u) << 4));
+    }
+    if (!rc && pos != nw) rc = BSO_ECORRUPT;
+    free(x);
+    return rc;
+}
+
+/* The chunk's plane of low fraction bits: one 32-bit word per group of 8    */
+/* weights, group g at byte 4g; the low bits of position p of the group at  */
+/* bit 16 (p mod 2) + 4 (p div 2) (even positions in the low half, odd ones */
+/* in the high half); positions past the chunk's end hold 0.                */
+static uint32_t low_bit_pos(uint32_t p) { return 16 * (p % 2) + 4 * (p / 2); }
+
+/* bytes of a chunk's plane of low fraction bits, padded to 16 */
+static uint64_t plane_bytes(uint32_t n_c) { return round_up(4 * (((uint64_t)n_c + 7) / 8), 16); }
+
+/* ------------------------------------------------------------------------ */
 /* Byte buffer for the container                                             */
 /* ------------------------------------------------------------------------ */
 typedef struct { uint8_t* p; uint64_t n, cap; } bytebuf;
@@ -569,7 +822,7 @@ static uint32_t get_bits(const uint8_t* b, uint64_t off, uint32_t len) {
 /* Encode one BF16 record body.                                              */
 /* ------------------------------------------------------------------------ */
 static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32_t Kmax, uint32_t Pmax,
-                            uint32_t M_s, uint32_t M_f, uint32_t cmax, bytebuf* body) {
+                            uint32_t M_s, uint32_t M_f, uint32_t cmax, uint32_t layout, bytebuf* body) {
     uint32_t W, K;
     int rc = bso_record_shape(n, Wmax, Kmax, &W, &K);
     if (rc) return rc;
@@ -581,23 +834,25 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
     uint64_t* cs = (uint64_t*)calloc(512, sizeof(uint64_t));
     uint64_t* cf = (uint64_t*)calloc(512 * 128, sizeof(uint64_t));
     if (!md || !cs || !cf) { free(md); free(cs); free(cf); return BSO_ENOMEM; }
-    md->M_s = M_s; md->M_f = M_f;
+    md->M_s = M_s; md->M_f = M_f; md->layout = layout;
     uint32_t n_sym = 0;
     uint64_t n_chunks = n ? (n + W - 1) / W : 0;
     if (n) {
         bso_histogram(w, n, cs, cf);
         rc = bso_normalise(cs, 512, M_s, md->qs);
-        if (!rc) rc = bso_select_tables(cs, cf, M_f, cmax, md->route, &md->n_tables, &md->qf[1][0]);
+        if (!rc && layout == 1) rc = bso_select_tables(cs, cf, M_f, cmax, md->route, &md->n_tables, &md->qf[1][0]);
+        if (!rc && layout == 2) rc = bso_select_htables(cs, cf, M_f, cmax, md->route, &md->n_tables, &md->qh[1][0]);
         for (uint32_t s = 0; s < 512; s++) if (cs[s]) n_sym++;
     }
-    for (uint32_t f = 0; f < 128; f++) md->qf[0][f] = 1u << (M_f - 7);
+    if (layout == 1) for (uint32_t f = 0; f < 128; f++) md->qf[0][f] = 1u << (M_f - 7);
+    if (layout == 2) for (uint32_t h = 0; h < 8; h++) md->qh[0][h] = 1u << (M_f - 3);
     if (rc) goto done;
 
     /* fixed part, tables, chunk index and (S > 1) stream table */
     uint64_t off = 24;
     uint64_t tables_end = off + 4ull * n_sym;
     tables_end = round_up(tables_end + n_sym, 4);
-    tables_end += 256ull * md->n_tables;
+    tables_end += (layout == 1 ? 256ull : 8ull) * md->n_tables;
     uint64_t index_off = round_up(tables_end, 16);
     uint64_t stab_off = index_off + 16 * n_chunks;
     uint64_t payload_off = round_up(stab_off + 4ull * (S - 1) * n_chunks, 16);
@@ -607,7 +862,7 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
     uint8_t* b = body->p;
     put32(b + 0, W); put32(b + 4, K); put32(b + 8, (uint32_t)n_chunks);
     b[12] = (uint8_t)M_s; b[13] = (uint8_t)M_f; b[14] = (uint8_t)md->n_tables; b[15] = (uint8_t)log2S;
-    put32(b + 16, n_sym); put32(b + 20, 0);
+    put32(b + 16, n_sym); put32(b + 20, layout == 1 ? 0 : layout);
     uint64_t k = 0;
     for (uint32_t s = 0; s < 512; s++) {
         if (!cs[s]) continue;
@@ -617,8 +872,10 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
         k++;
     }
     uint64_t ft = round_up(off + 4ull * n_sym + n_sym, 4);
-    for (uint32_t t = 1; t <= md->n_tables; t++)
-        for (uint32_t f = 0; f < 128; f++) put16(b + ft + 256ull * (t - 1) + 2 * f, md->qf[t][f]);
+    for (uint32_t t = 1; t <= md->n_tables; t++) {
+        if (layout == 1) for (uint32_t f = 0; f < 128; f++) put16(b + ft + 256ull * (t - 1) + 2 * f, md->qf[t][f]);
+        else for (uint32_t h = 0; h < 8; h++) b[ft + 8ull * (t - 1) + h] = (uint8_t)md->qh[t][h];
+    }
 
     /* chunks: the K lanes' length codes, padded to 16 bytes, then the
        streams back to back, each the state bits of its P lanes (padded to a
@@ -633,8 +890,10 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
     for (uint64_t c = 0; c < n_chunks && !rc; c++) {
         uint32_t n_c = (uint32_t)((n - c * W) < W ? (n - c * W) : W);
         for (uint32_t st = 0; st < S; st++) wls[st].n = 0;
-        for (uint32_t st = 0; st < S && !rc; st++)
-            rc = chunk_encode(md, w + c * W, n_c, K, st * P, (st + 1) * P, states, &wls[st]);
+        for (uint32_t st = 0; st < S && !rc; st++) {
+            if (layout == 1) rc = chunk_encode(md, w + c * W, n_c, K, st * P, (st + 1) * P, states, &wls[st]);
+            else rc = chunk_encode_split(md, w + c * W, n_c, K, st * P, (st + 1) * P, states, &wls[st]);
+        }
         if (rc) break;
         uint64_t total = 0;
         for (uint32_t st = 0; st < S; st++) {
@@ -645,7 +904,9 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
             total += units[st];
         }
         uint64_t start = body->n;
-        uint64_t code_bytes = code_block_bytes(K);
+        /* layout 2: the plane of low fraction bits sits between the length
+           codes and the stream area */
+        uint64_t code_bytes = code_block_bytes(K) + (layout == 2 ? plane_bytes(n_c) : 0);
         uint64_t end = start + round_up(code_bytes + 2 * total, 16);
         rc = bb_reserve(body, end);
         if (rc) break;
@@ -655,6 +916,14 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
         put32(b + index_off + 16 * c + 8, (uint32_t)total);
         put32(b + index_off + 16 * c + 12, 0);
         for (uint32_t l = 0; l < K; l++) b[start + l / 2] |= (uint8_t)(state_code(states[l]) << (4 * (l % 2)));
+        if (layout == 2) {
+            uint8_t* plane = b + start + code_block_bytes(K);
+            for (uint32_t j = 0; j < n_c; j++) {
+                uint32_t g = j / 8, p = j % 8;
+                uint32_t v = get32(plane + 4 * g) | ((bso_symbol_f(w[c * W + j]) & 15u) << low_bit_pos(p));
+                put32(plane + 4 * g, v);
+            }
+        }
         uint64_t at = 0;   /* units from the start of the stream area */
         for (uint32_t st = 0; st < S; st++) {
             if (st > 0) put32(b + stab_off + 4 * ((S - 1) * c + st - 1), (uint32_t)at);
@@ -688,11 +957,16 @@ done:
 /* as a RAW record of its 2n bytes.                                          */
 /* On success *out points to malloc'ed bytes (free with bso_free).          */
 /* ------------------------------------------------------------------------ */
-int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* const* data,
-                         const uint64_t* n, const uint8_t* sha,
-                         uint32_t Wmax, uint32_t Kmax, uint32_t Pmax, uint32_t M_s, uint32_t M_f, uint32_t cmax,
-                         uint8_t** out, uint64_t* out_len) {
-    if (M_s < 9 || M_s > 12 || M_f < 8 || M_f > 10 || cmax > BSO_MAX_TABLES) return BSO_EINVAL;
+/* layout 1 writes a version-1 container, layout 2 a version-2 container    */
+/* (every BF16 record in that layout).  Layout 2: M_s is 11 or 12 and M_f    */
+/* holds M_h = 16 - M_s; cmax <= 31.                                         */
+int bso_encode_container2(uint32_t n_tensors, const uint32_t* kinds, const void* const* data,
+                          const uint64_t* n, const uint8_t* sha,
+                          uint32_t Wmax, uint32_t Kmax, uint32_t Pmax, uint32_t M_s, uint32_t M_f, uint32_t cmax,
+                          uint32_t layout, uint8_t** out, uint64_t* out_len) {
+    if (layout == 1 && (M_s < 9 || M_s > 12 || M_f < 8 || M_f > 10 || cmax > BSO_MAX_TABLES)) return BSO_EINVAL;
+    if (layout == 2 && (M_s < 11 || M_s > 12 || M_f != 16 - M_s || cmax > BSO_MAX_HTABLES)) return BSO_EINVAL;
+    if (layout != 1 && layout != 2) return BSO_EINVAL;
     if (!(Kmax <= 64 || Kmax == 128 || Kmax == 256 || Kmax == 512 || Kmax == 1024 || Kmax == 2048) || Kmax == 0) return BSO_EINVAL;
     if ((Kmax & (Kmax - 1)) != 0) return BSO_EINVAL;
     if (Pmax == 0 || (Pmax & (Pmax - 1)) != 0 || Pmax > Kmax || Pmax > 512) return BSO_EINVAL;
@@ -721,7 +995,7 @@ int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* 
             if (occ > BSO_MAX_SYMS) { kind = BSO_KIND_RAW; count = bytes; }
         }
         if (kind == BSO_KIND_BF16) {
-            rc = encode_bf16_body((const uint16_t*)data[i], n[i], Wmax, Kmax, Pmax, M_s, M_f, cmax, &body);
+            rc = encode_bf16_body((const uint16_t*)data[i], n[i], Wmax, Kmax, Pmax, M_s, M_f, cmax, layout, &body);
         } else if (kind == BSO_KIND_RAW) {
             rc = bb_reserve(&body, bytes ? bytes : 1);
             if (!rc) { if (bytes) memcpy(body.p, data[i], bytes); body.n = bytes; }
@@ -758,7 +1032,7 @@ int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* 
         if (e > out_len_bytes) out_len_bytes = e;
     }
     memcpy(c.p, BSO_MAGIC, 8);
-    put32(c.p + 8, BSO_VERSION);
+    put32(c.p + 8, layout == 1 ? BSO_VERSION : BSO_VERSION2);
     put32(c.p + 12, n_tensors);
     put64(c.p + 16, dir);
     put64(c.p + 24, total);
@@ -768,6 +1042,13 @@ int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* 
     return BSO_OK;
 }
 
+int bso_encode_container(uint32_t n_tensors, const uint32_t* kinds, const void* const* data,
+                         const uint64_t* n, const uint8_t* sha,
+                         uint32_t Wmax, uint32_t Kmax, uint32_t Pmax, uint32_t M_s, uint32_t M_f, uint32_t cmax,
+                         uint8_t** out, uint64_t* out_len) {
+    return bso_encode_container2(n_tensors, kinds, data, n, sha, Wmax, Kmax, Pmax, M_s, M_f, cmax, 1, out, out_len);
+}
+
 void bso_free(void* p) { free(p); }
 
 /* ------------------------------------------------------------------------ */
@@ -775,7 +1056,7 @@ void bso_free(void* p) { free(p); }
 /* rec_status[i] (may be NULL) receives 0 or the error of record i.          */
 /* Returns the first error, or 0.                                            */
 /* ------------------------------------------------------------------------ */
-static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md,
+static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, uint32_t version, bso_model* md,
                        uint32_t* W, uint32_t* K, uint32_t* S, uint64_t* n_chunks, uint64_t* index_off) {
     if (len < 24) return BSO_EFORMAT;
     *W = get32(b); *K = get32(b + 4);
@@ -784,7 +1065,13 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md
     if (b[15] > 9) return BSO_EFORMAT;
     *S = 1u << b[15];
     uint32_t n_sym = get32(b + 16);
-    if (md->M_s < 9 || md->M_s > 12 || md->M_f < 8 || md->M_f > 10 || md->n_tables > BSO_MAX_TABLES)
+    /* version 1: the word at +20 is 0 (layout 1); version 2: it names the layout */
+    uint32_t lw = get32(b + 20);
+    if (version == BSO_VERSION) { if (lw != 0) return BSO_EFORMAT; md->layout = 1; }
+    else { if (lw != 1 && lw != 2) return BSO_EFORMAT; md->layout = lw; }
+    if (md->layout == 1 && (md->M_s < 9 || md->M_s > 12 || md->M_f < 8 || md->M_f > 10 || md->n_tables > BSO_MAX_TABLES))
+        return BSO_EFORMAT;
+    if (md->layout == 2 && (md->M_s < 11 || md->M_s > 12 || md->M_f != 16 - md->M_s || md->n_tables > BSO_MAX_HTABLES))
         return BSO_EFORMAT;
     if (*K == 0 || *W == 0 || *W % (8 * *K)) return BSO_EFORMAT;
     if (!(*K <= 64 || *K == 128 || *K == 256 || *K == 512 || *K == 1024 || *K == 2048)) return BSO_EFORMAT;
@@ -793,7 +1080,7 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md
     if (n_sym > BSO_MAX_SYMS || (n_sym == 0) != (n == 0)) return BSO_EFORMAT;
     uint64_t off = 24;
     uint64_t ft = round_up(off + 4ull * n_sym + n_sym, 4);
-    uint64_t tab_end = ft + 256ull * md->n_tables;
+    uint64_t tab_end = ft + (md->layout == 1 ? 256ull : 8ull) * md->n_tables;
     *index_off = round_up(tab_end, 16);
     if (*index_off + 16 * *n_chunks + 4ull * (*S - 1) * *n_chunks > len) return BSO_EFORMAT;
     memset(md->qs, 0, sizeof(md->qs));
@@ -810,6 +1097,15 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, bso_model* md
         sum += q;
     }
     if (n_sym && sum != (1ull << md->M_s)) return BSO_EFORMAT;
+    if (md->layout == 2) {
+        for (uint32_t h = 0; h < 8; h++) md->qh[0][h] = 1u << (md->M_f - 3);
+        for (uint32_t t = 1; t <= md->n_tables; t++) {
+            uint64_t tsum = 0;
+            for (uint32_t h = 0; h < 8; h++) { md->qh[t][h] = b[ft + 8ull * (t - 1) + h]; tsum += md->qh[t][h]; }
+            if (tsum != (1ull << md->M_f)) return BSO_EFORMAT;
+        }
+        return BSO_OK;
+    }
     for (uint32_t f = 0; f < 128; f++) md->qf[0][f] = 1u << (md->M_f - 7);
     for (uint32_t t = 1; t <= md->n_tables; t++) {
         uint64_t tsum = 0;
@@ -824,7 +1120,8 @@ static int decode_one_chunk(const bso_model* md, const uint8_t* b, uint64_t rl, 
                             uint32_t S, uint64_t n_chunks, uint64_t ch, uint32_t n_c, uint16_t* out) {
     const uint8_t* e = b + io + 16 * ch;
     uint64_t po = get64(e), total = get32(e + 8);
-    uint64_t code_bytes = code_block_bytes(K);
+    /* layout 2: the plane of low fraction bits follows the length codes */
+    uint64_t code_bytes = code_block_bytes(K) + (md->layout == 2 ? plane_bytes(n_c) : 0);
     if (po % 16 || po > rl || code_bytes > rl - po || 2 * total > rl - po - code_bytes) return BSO_EFORMAT;
     const uint8_t* stab = b + io + 16 * n_chunks + 4 * (S - 1) * ch;
     uint32_t P = K / S;
@@ -854,16 +1151,23 @@ static int decode_one_chunk(const bso_model* md, const uint8_t* b, uint64_t rl, 
         uint16_t* words = (uint16_t*)malloc(sizeof(uint16_t) * (nws ? nws : 1));
         if (!words) { rc = BSO_ENOMEM; break; }
         for (uint64_t j = 0; j < nws; j++) words[j] = (uint16_t)get16(area + 2 * (mu + j));
-        rc = chunk_decode(md, st, words, nws, n_c, K, s * P, (s + 1) * P, out);
+        if (md->layout == 1) rc = chunk_decode(md, st, words, nws, n_c, K, s * P, (s + 1) * P, out);
+        else rc = chunk_decode_split(md, st, words, nws, n_c, K, s * P, (s + 1) * P, out);
         free(words);
     }
     free(st);
+    if (!rc && md->layout == 2) {
+        const uint8_t* plane = b + po + code_block_bytes(K);
+        for (uint32_t j = 0; j < n_c; j++)
+            out[j] = (uint16_t)(out[j] | ((get32(plane + 4 * (j / 8)) >> low_bit_pos(j % 8)) & 15u));
+    }
     return rc;
 }
 
 int bso_decode_container(const uint8_t* c, uint64_t len, uint8_t* out, uint64_t out_cap, int32_t* rec_status) {
     if (len < BSO_HDR_BYTES || memcmp(c, BSO_MAGIC, 8) != 0) return BSO_EFORMAT;
-    if (get32(c + 8) != BSO_VERSION) return BSO_EVERSION;
+    uint32_t version = get32(c + 8);
+    if (version != BSO_VERSION && version != BSO_VERSION2) return BSO_EVERSION;
     uint32_t n_rec = get32(c + 12);
     uint64_t dir = get64(c + 16);
     if (get64(c + 24) != len) return BSO_EFORMAT;
@@ -883,7 +1187,7 @@ int bso_decode_container(const uint8_t* c, uint64_t len, uint8_t* out, uint64_t 
             bso_model* md = (bso_model*)calloc(1, sizeof(bso_model));
             uint32_t W, K, S; uint64_t nch, io;
             if (!md) rc = BSO_ENOMEM;
-            if (!rc) rc = parse_model(c + ro, rl, n, md, &W, &K, &S, &nch, &io);
+            if (!rc) rc = parse_model(c + ro, rl, n, version, md, &W, &K, &S, &nch, &io);
             if (!rc && (oo + 2 * n > out_cap || oo % 16)) rc = BSO_EFORMAT;
             uint16_t* tmp = NULL;
             if (!rc && n) { tmp = (uint16_t*)malloc(sizeof(uint16_t) * W); if (!tmp) rc = BSO_ENOMEM; }
@@ -909,7 +1213,8 @@ int bso_decode_container(const uint8_t* c, uint64_t len, uint8_t* out, uint64_t 
 int bso_decode_chunk(const uint8_t* c, uint64_t len, uint32_t record, uint64_t chunk,
                      uint16_t* out, uint64_t out_cap, uint64_t* n_c_out) {
     if (len < BSO_HDR_BYTES || memcmp(c, BSO_MAGIC, 8) != 0) return BSO_EFORMAT;
-    if (get32(c + 8) != BSO_VERSION) return BSO_EVERSION;
+    uint32_t version = get32(c + 8);
+    if (version != BSO_VERSION && version != BSO_VERSION2) return BSO_EVERSION;
     uint32_t n_rec = get32(c + 12);
     uint64_t dir = get64(c + 16);
     if (record >= n_rec || dir + (uint64_t)BSO_DIR_BYTES * n_rec > len) return BSO_EINVAL;
@@ -920,7 +1225,7 @@ int bso_decode_chunk(const uint8_t* c, uint64_t len, uint32_t record, uint64_t c
     bso_model* md = (bso_model*)calloc(1, sizeof(bso_model));
     if (!md) return BSO_ENOMEM;
     uint32_t W, K, S; uint64_t nch, io;
-    int rc = parse_model(c + ro, rl, n, md, &W, &K, &S, &nch, &io);
+    int rc = parse_model(c + ro, rl, n, version, md, &W, &K, &S, &nch, &io);
     if (!rc && chunk >= nch) rc = BSO_EINVAL;
     uint64_t n_c = 0;
     if (!rc) {

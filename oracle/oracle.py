@@ -77,6 +77,13 @@ def lib():
                                            C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32,
                                            C.POINTER(C.POINTER(C.c_uint8)), u64p]
         l.bso_encode_container.restype = C.c_int
+        l.bso_encode_container2.argtypes = [C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                            C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32,
+                                            C.c_uint32, C.POINTER(C.POINTER(C.c_uint8)), u64p]
+        l.bso_encode_container2.restype = C.c_int
+        l.bso_log2_q16.argtypes = [C.c_uint32]; l.bso_log2_q16.restype = C.c_uint32
+        l.bso_select_htables.argtypes = [u64p, u64p, C.c_uint32, C.c_uint32, u32p, u32p, u32p]
+        l.bso_select_htables.restype = C.c_int
         l.bso_decode_container.argtypes = [C.c_void_p, C.c_uint64, C.c_void_p, C.c_uint64, C.c_void_p]
         l.bso_decode_container.restype = C.c_int
         l.bso_free.argtypes = [C.c_void_p]; l.bso_free.restype = None
@@ -147,6 +154,24 @@ def select_tables(cs, cf, M_f: int = 10, cmax: int = 6):
     if rc:
         raise OracleError(rc, "select_tables")
     return route, int(nt[0]), qf[: int(nt[0])].copy()
+
+
+def log2_q16(q: int) -> int:
+    """floor(65536 log2 q) as the container's layout-2 rule computes it."""
+    return int(lib().bso_log2_q16(q))
+
+
+def select_htables(cs, cf, M_h: int = 5, cmax: int = 31):
+    """Layout-2 coded tables of h = f >> 4: (route[512], n_tables, qh[cmax, 8])."""
+    cs = np.ascontiguousarray(cs, np.uint64)
+    cf = np.ascontiguousarray(cf, np.uint64).reshape(-1)
+    route = np.zeros(512, np.uint32)
+    nt = np.zeros(1, np.uint32)
+    qh = np.zeros(max(cmax, 1) * 8, np.uint32)
+    rc = lib().bso_select_htables(_u64p(cs), _u64p(cf), M_h, cmax, _u32p(route), _u32p(nt), _u32p(qh))
+    if rc:
+        raise OracleError(rc, "select_htables")
+    return route, int(nt[0]), qh.reshape(max(cmax, 1), 8)
 
 
 def record_shape(n: int, Wmax: int, Kmax: int):
@@ -242,9 +267,11 @@ def sha256(t: Tensor) -> bytes:
 
 
 def encode(tensors, W: int = 65536, K: int = 64, M_s: int = 12, M_f: int = 10, cmax: int = 6,
-           P: int | None = None) -> bytes:
+           P: int | None = None, layout: int = 1) -> bytes:
     """Container of the tensors: chunks of W weights with K lanes, split into
-    streams of P lanes (default: one stream of all K lanes)."""
+    streams of P lanes (default: one stream of all K lanes).  layout 1 gives a
+    version-1 container; layout 2 a version-2 one, with M_s 11 or 12, M_f
+    the precision of the h tables (16 - M_s) and cmax up to 31."""
     n = len(tensors)
     P = K if P is None else P
     kinds = np.array([t.kind for t in tensors] or [0], np.uint32)
@@ -254,8 +281,8 @@ def encode(tensors, W: int = 65536, K: int = 64, M_s: int = 12, M_f: int = 10, c
     sha = np.frombuffer(b"".join(sha256(t) for t in tensors) or b"\0" * 32, np.uint8).copy()
     out = C.POINTER(C.c_uint8)()
     out_len = C.c_uint64(0)
-    rc = lib().bso_encode_container(n, _ptr(kinds), ptrs, _ptr(counts), _ptr(sha), W, K, P, M_s, M_f, cmax,
-                                    C.byref(out), C.byref(out_len))
+    rc = lib().bso_encode_container2(n, _ptr(kinds), ptrs, _ptr(counts), _ptr(sha), W, K, P, M_s, M_f, cmax,
+                                     layout, C.byref(out), C.byref(out_len))
     if rc:
         raise OracleError(rc, "encode")
     try:

@@ -136,10 +136,10 @@ def test_corruption_and_header_errors():
     # truncation
     rc, _, _ = O.decode_status(bytes(c[:-16]))
     assert rc == -2
-    # unknown version
-    v2 = bytearray(c)
-    v2[8:12] = struct.pack("<I", 2)
-    rc, _, _ = O.decode_status(bytes(v2))
+    # unknown version (1 and 2 are defined)
+    v3 = bytearray(c)
+    v3[8:12] = struct.pack("<I", 3)
+    rc, _, _ = O.decode_status(bytes(v3))
     assert rc == -3
     # output too small
     rc, _, _ = O.decode_status(bytes(c), out_cap=100)

@@ -72,11 +72,40 @@ MUTANTS = {
     "shape_rounding": ("*W = (uint32_t)round_up(n ? n : 1, 8 * (uint64_t)k);", "*W = (uint32_t)round_up(n ? n : 1, 8);"),
 }
 
+# planted mistakes in layout 2 (one renormalisation per weight), checked
+# against the layout-2 pins only
+PINS2 = ["tests/test_oracle_layout2.py"]
+MUTANTS2 = {
+    "split_pair_order_swapped": ("    code_step(x, th, h);\n    code_step(x, ts, s);", "    code_step(x, ts, s);\n    code_step(x, th, h);"),
+    "split_flush_bound_s_only": ("uint64_t q = (uint64_t)ts->q[s] * th->q[h];", "uint64_t q = (uint64_t)ts->q[s] * (1u << th->M) / 8;"),
+    "split_lead_always_16": ("static uint32_t split_lead(uint32_t c) { return 3 * c > 16 ? 3 * c : 16; }",
+                             "static uint32_t split_lead(uint32_t c) { return 16 + 0 * c; }"),
+    "split_start_h_reversed": ("x |= (bso_symbol_f(w[8 * g + i]) >> 4) << (3 * i);", "x |= (bso_symbol_f(w[8 * g + i]) >> 4) << (3 * (c - 1 - i));"),
+    "split_plane_even_odd_swapped": ("static uint32_t low_bit_pos(uint32_t p) { return 16 * (p % 2) + 4 * (p / 2); }",
+                                     "static uint32_t low_bit_pos(uint32_t p) { return 16 * (1 - p % 2) + 4 * (p / 2); }"),
+    "split_last_group_paired": ("                if (j / 8 == g) {\n                    rc = enc_symbol(&states[l], &ts, s, wl);",
+                                "                if (0) {\n                    rc = enc_symbol(&states[l], &ts, s, wl);"),
+    "split_h_four_bits": ("rc = enc_pair_words(&states[l], &ts, s, &th, bso_symbol_f(w[j]) >> 4, wl);",
+                          "rc = enc_pair_words(&states[l], &ts, s, &th, (bso_symbol_f(w[j]) >> 4) ^ (j & 1), wl);"),
+    "split_refill_between_steps": ("                rc = decode_step(&x[l], &ts, &s);\n                if (!rc && j / 8 != g) {",
+                                   "                rc = decode_step(&x[l], &ts, &s);\n                if (x[l] < BSO_L && pos < nw) x[l] = (x[l] << 16) | words[pos++];\n                if (!rc && j / 8 != g) {"),
+    "htable_threshold_zero": ("eligible[e] = saved[e] > (__int128)65536 * 64;", "eligible[e] = saved[e] > 0;"),
+    "htable_tie_high": ("if (best < 0 || saved[e] > saved[best]) best = (int)e;", "if (best < 0 || saved[e] >= saved[best]) best = (int)e;"),
+    "htable_signs_not_merged": ("for (uint32_t f = 16 * h; f < 16 * h + 16; f++) m[h] += cf[e * 128 + f] + cf[(256 + e) * 128 + f];",
+                                "for (uint32_t f = 16 * h; f < 16 * h + 16; f++) m[h] += cf[e * 128 + f];"),
+    "htable_ids_by_saving": ("        id++;\n        id_of[e] = id;\n        for (uint32_t h = 0; h < 8; h++) qh[(id - 1) * 8 + h] = qe[e][h];",
+                             "        id++;\n        id_of[e] = (id % 2) ? id + 1 : id - 1;\n        for (uint32_t h = 0; h < 8; h++) qh[(id - 1) * 8 + h] = qe[e][h];"),
+    "log2_square_shift": ("        r = (r * r) >> 62;", "        r = (r * r) >> 61;"),
+    "log2_bit_compare": ("if (r >= ((unsigned __int128)2 << 62)) { bits |= 1; r >>= 1; }", "if (r > ((unsigned __int128)3 << 61)) { bits |= 1; r >>= 1; }"),
+    "version2_accepts_layout0": ("else { if (lw != 1 && lw != 2) return BSO_EFORMAT; md->layout = lw; }",
+                                 "else { if (lw > 2) return BSO_EFORMAT; md->layout = lw ? lw : 1; }"),
+}
 
-def _run_pins(lib_path):
+
+def _run_pins(lib_path, pins=PINS):
     env = dict(os.environ)
     env["BSO_ORACLE_LIB"] = lib_path
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PINS, *SELECT],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *pins, *SELECT],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return r.returncode, r.stdout[-2000:]
 
@@ -102,4 +131,20 @@ def test_mutant_is_caught(name, tmp_path):
     assert text.count(old) >= 1, f"mutation anchor not found: {name}"
     so = _build(text.replace(old, new, 1), tmp_path, name)
     rc, out = _run_pins(so)
+    assert rc != 0, f"planted mistake {name} was not caught:\n{out}"
+
+
+def test_unmodified_oracle_passes_layout2_selection(tmp_path):
+    so = _build(open(SRC).read(), tmp_path, "clean2")
+    rc, out = _run_pins(so, PINS2)
+    assert rc == 0, out
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS2))
+def test_layout2_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS2[name]
+    text = open(SRC).read()
+    assert text.count(old) >= 1, f"mutation anchor not found: {name}"
+    so = _build(text.replace(old, new, 1), tmp_path, name)
+    rc, out = _run_pins(so, PINS2)
     assert rc != 0, f"planted mistake {name} was not caught:\n{out}"
