@@ -11,7 +11,9 @@
  * Instruct -- Lossless Compressed card, "What lossless means"; NVLC card,
  * SHA256SUMS verification block] (sha256 here).
  *
- * Container ("BF16RANS", version 1, little-endian) -- this library's own layout:
+ * Container ("BF16RANS", version 1 or 2, little-endian) -- this library's own
+ * layout.  Version 1 holds layout-1 records only; version 2 adds layout 2
+ * (below) and names each BF16 record's layout in its fixed part:
  *   header 64 B: magic[8] "BF16RANS", u32 version, u32 n_records,
  *                u64 dir_offset, u64 total_len, u64 out_len, u32 flags, 20 B zero
  *   directory, 96 B per record: u32 kind (1 = BF16 rANS, 2 = RAW verbatim),
@@ -19,7 +21,8 @@
  *                u64 rec_offset, u64 rec_len, u8 sha256[32], 24 B zero
  *   BF16 record body: u32 W (weights per chunk), u32 K (lanes), u32 n_chunks,
  *                u8 M_s, u8 M_f, u8 n_tables, u8 log2 S (word streams per
- *                chunk), u32 n_sym, u32 0;
+ *                chunk), u32 n_sym, u32 layout (version 1: 0, meaning layout
+ *                1; version 2: 1 or 2); the rest of a layout-1 body:
  *                s-table n_sym x (u16 s, u16 q) ascending s (sum q = 2^M_s);
  *                route: n_sym bytes (fraction table of each s: 0 = flat,
  *                1..n_tables), padded to 4 B; n_tables x 128 x u16 q_f
@@ -49,6 +52,29 @@
  *   lowest) under a leading one at bit max(16, 7m), so the decoder reads them
  *   off the state it ends in.  A lane without weights starts and ends at
  *   2^16.  Fraction tables with id 0 are flat (q = 2^(M_f - 7) for every f).
+ *
+ * Layout 2 (one renormalisation per weight): the fraction f = h << 4 | l is
+ * split into its high three bits h, coded with the distribution s selects,
+ * and its low four bits l, stored verbatim.  Per weight a lane decodes s
+ * (precision M_s, 11 or 12) and then h (precision M_h = 16 - M_s, held in
+ * the M_f byte) with the table route[s], and only then renormalises: the two
+ * steps use at most 16 bits of the state, so one 16-bit word restores it.
+ * Body after the fixed part: the s-table and route bytes as in layout 1
+ * (padded to 4 B), then n_tables (<= 31) x 8 x u8 q_h (each sums to 2^M_h;
+ * table 0 is flat, q_h = 2^(M_h - 3)), padded to 16 B; chunk index and stream
+ * table as in layout 1.  A chunk payload is the length codes (padded to
+ * 16 B), then the plane of low bits, one u32 per group of 8 weights (group g
+ * at byte 4 g, padded to 16 B; the l of position p of a group at bit
+ * 16 (p mod 2) + 4 (p div 2), 0 past the chunk's end), then the stream area
+ * as in layout 1 (its units counted in the chunk index).  Sub-steps are one
+ * per weight, (macro-step, position), lanes ascending inside each.  In its
+ * last group (c = min(8, weights left) weights) a lane decodes s only: the h
+ * of those c weights are the low 3c bits of its start state (first weight
+ * lowest) under a leading one at bit max(16, 3c).  A table id > 0 is given to
+ * an exponent (both signs share it) when quantising its h counts saves more
+ * than 64 bits against the flat table, counted with floor(65536 log2 q);
+ * at most max_tables of them, the largest savings first (lower exponent on
+ * ties), ids in ascending exponent order.
  *
  * Conventions:
  *   - Every function returns a bs_status (0 = BS_OK); none throws or aborts.
@@ -89,9 +115,12 @@ enum { BS_KIND_BF16 = 1, BS_KIND_RAW = 2 };
  * is a power of two: 1..64, 128, 256, 512, 1024 or 2048; stream_lanes P
  * (0 = K) is a power of two <= K and <= 512: each chunk's lanes are split into
  * word streams of P lanes (fewer when a small record gets fewer lanes), which
- * the decoder runs on separate wavefronts; 9 <= m_s <= 12; 8 <= m_f <= 10 (the decoder multiplies
- * x >> m in 24 bits, so m >= 8); max_tables <= 6;
- * threads = host encoder threads (0 = hardware count). */
+ * the decoder runs on separate wavefronts; threads = host encoder threads
+ * (0 = hardware count).  layout 1: 9 <= m_s <= 12, 8 <= m_f <= 10 (the
+ * decoder multiplies x >> m in 24 bits, so m >= 8), max_tables <= 6; the
+ * container is version 1.  layout 2: m_s 11 or 12, m_f = 16 - m_s (the
+ * precision of the h tables), max_tables <= 31; the container is version 2,
+ * and the GPU decode takes at most 256 lanes per word stream. */
 typedef struct {
     uint32_t chunk_weights;
     uint32_t lanes;
@@ -100,10 +129,12 @@ typedef struct {
     uint32_t max_tables;
     uint32_t threads;
     uint32_t stream_lanes;
+    uint32_t layout;
 } bs_params;
 
-/* Fill *p with the defaults: W = 65536, K = 128, m_s = 12, m_f = 10,
- * max_tables = 6, threads = 0, stream_lanes = 0 (one stream per chunk). */
+/* Fill *p with the defaults: W = 65536, K = 128, layout 2, m_s = 11,
+ * m_f = 5, max_tables = 31, threads = 0, stream_lanes = 0 (one stream per
+ * chunk). */
 void bs_params_default(bs_params* p);
 
 /* ---------------------------------------------------------------- model */
@@ -130,9 +161,13 @@ void bs_tables_free(bs_tables* t);
 
 /* Read back a model (for inspection and tests).  Arrays are caller-owned:
  * counts_s[512] (u64, may be NULL), q_s[512], route[512] (table id of each s),
- * q_f[6*128] (row t-1 = table t); *n_tables, *m_s, *m_f, *n_weights. */
+ * q_f[6*128] (layout 1: row t-1 = table t); *n_tables, *m_s, *m_f, *n_weights. */
 bs_status bs_tables_get(const bs_tables* t, uint64_t* counts_s, uint32_t* q_s, uint32_t* route,
                         uint32_t* q_f, uint32_t* n_tables, uint32_t* m_s, uint32_t* m_f, uint64_t* n_weights);
+
+/* The model's layout (1 or 2) and, for layout 2, its h tables: q_h[31*8]
+ * (row t-1 = table t; may be NULL). */
+bs_status bs_tables_get_layout(const bs_tables* t, uint32_t* layout, uint32_t* q_h);
 
 /* ---------------------------------------------------------------- encode */
 
@@ -224,7 +259,7 @@ typedef struct {
     uint8_t sha256[32];
     uint64_t stream_base;   /* status index of the record's first stream */
     uint32_t streams;       /* word streams per chunk */
-    uint32_t reserved;
+    uint32_t layout;        /* BF16 records: 1 or 2 */
 } bs_record_info;
 
 /* Validate a host copy of a container and describe it.  Errors: BS_E_FORMAT,

@@ -35,7 +35,7 @@ VERIFY_SHA256 = 4
 class Params(C.Structure):
     _fields_ = [("chunk_weights", C.c_uint32), ("lanes", C.c_uint32), ("m_s", C.c_uint32),
                 ("m_f", C.c_uint32), ("max_tables", C.c_uint32), ("threads", C.c_uint32),
-                ("stream_lanes", C.c_uint32)]
+                ("stream_lanes", C.c_uint32), ("layout", C.c_uint32)]
 
 
 class Tensor(C.Structure):
@@ -59,7 +59,7 @@ class RecordInfo(C.Structure):
                 ("n_chunks", C.c_uint32), ("m_s", C.c_uint32), ("m_f", C.c_uint32), ("n_tables", C.c_uint32),
                 ("n_sym", C.c_uint32), ("n", C.c_uint64), ("out_offset", C.c_uint64), ("rec_offset", C.c_uint64),
                 ("rec_len", C.c_uint64), ("chunk_base", C.c_uint64), ("sha256", C.c_uint8 * 32),
-                ("stream_base", C.c_uint64), ("streams", C.c_uint32), ("reserved", C.c_uint32)]
+                ("stream_base", C.c_uint64), ("streams", C.c_uint32), ("layout", C.c_uint32)]
 
 
 class Report(C.Structure):
@@ -84,6 +84,7 @@ class StreamerStats(C.Structure):
 SIGNATURES = {
     "bs_params_default": (None, [C.POINTER(Params)]),
     "bs_build_tables": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(Params), C.c_void_p, C.POINTER(C.c_void_p)]),
+    "bs_tables_get_layout": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_void_p]),
     "bs_build_tables_host": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(Params), C.POINTER(C.c_void_p)]),
     "bs_tables_free": (None, [C.c_void_p]),
     "bs_tables_get": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(C.c_uint32),

@@ -29,14 +29,23 @@ def _stream_handle(stream) -> int:
 
 
 def params(chunk_weights: int = 65536, lanes: int = 128, m_s: int = 12, m_f: int = 10, max_tables: int = 6,
-           threads: int = 0, stream_lanes: int = 0) -> L.Params:
-    """Encoder parameters; stream_lanes 0 keeps each chunk one word stream."""
+           threads: int = 0, stream_lanes: int = 0, layout: int = 1) -> L.Params:
+    """Encoder parameters; stream_lanes 0 keeps each chunk one word stream.
+    layout 2 (one renormalisation per weight) takes m_s 11 or 12, m_f =
+    16 - m_s and up to 31 tables: see params2."""
     p = L.Params()
     L.lib().bs_params_default(C.byref(p))
     p.chunk_weights, p.lanes, p.m_s, p.m_f, p.max_tables, p.threads = (chunk_weights, lanes, m_s, m_f,
                                                                        max_tables, threads)
     p.stream_lanes = stream_lanes
+    p.layout = layout
     return p
+
+
+def params2(chunk_weights: int = 65536, lanes: int = 128, m_s: int = 11, threads: int = 0,
+            stream_lanes: int = 0, max_tables: int = 31) -> L.Params:
+    """Layout-2 encoder parameters (the library's default layout)."""
+    return params(chunk_weights, lanes, m_s, 16 - m_s, max_tables, threads, stream_lanes, layout=2)
 
 
 class Tables:
@@ -60,8 +69,16 @@ class Tables:
         L.check(L.lib().bs_tables_get(self.handle, cs.ctypes.data, qs.ctypes.data, route.ctypes.data,
                                       qf.ctypes.data, C.byref(nt), C.byref(ms), C.byref(mf), C.byref(n)),
                 "bs_tables_get")
-        return {"counts_s": cs, "q_s": qs, "route": route, "n_tables": nt.value, "q_f": qf[: nt.value].copy(),
-                "m_s": ms.value, "m_f": mf.value, "n": n.value}
+        layout = C.c_uint32()
+        qh = np.zeros((31, 8), np.uint32)
+        L.check(L.lib().bs_tables_get_layout(self.handle, C.byref(layout), qh.ctypes.data), "bs_tables_get_layout")
+        d = {"counts_s": cs, "q_s": qs, "route": route, "n_tables": nt.value, "m_s": ms.value, "m_f": mf.value,
+             "n": n.value, "layout": layout.value}
+        if layout.value == 1:
+            d["q_f"] = qf[: nt.value].copy()
+        else:
+            d["q_h"] = qh[: nt.value].copy()
+        return d
 
 
 def build_tables(words: torch.Tensor, p: L.Params | None = None, stream=None) -> Tables:

@@ -40,13 +40,16 @@ struct EncSym {
 };
 
 struct EncModel {
-    uint32_t m_s, m_f;
+    uint32_t layout;
+    uint32_t m_s, m_f;                 // layout 2: m_f is M_h
     EncSym s[512];
-    EncSym f[kMaxTables + 1][128];
+    EncSym f[kMaxTables + 1][128];     // layout 1
+    EncSym h[kMaxHTables + 1][8];      // layout 2 (x_max unused: a pair's bound is joint)
     uint8_t route[512];
 };
 
 void make_enc(const Model& md, EncModel& em) {
+    em.layout = md.layout;
     em.m_s = md.m_s;
     em.m_f = md.m_f;
     uint32_t cum = 0;
@@ -54,6 +57,17 @@ void make_enc(const Model& md, EncModel& em) {
         em.s[s] = {(uint64_t)md.q_s[s] << (32 - md.m_s), md.q_s[s], cum};
         cum += md.q_s[s];
         em.route[s] = (uint8_t)md.route[s];
+    }
+    if (md.layout == 2) {
+        for (uint32_t t = 0; t <= md.n_tables; t++) {
+            cum = 0;
+            for (uint32_t h = 0; h < 8; h++) {
+                const uint32_t q = t == 0 ? (1u << (md.m_f - 3)) : md.q_h[t - 1][h];
+                em.h[t][h] = {0, q, cum};
+                cum += q;
+            }
+        }
+        return;
     }
     for (uint32_t t = 0; t <= md.n_tables; t++) {
         cum = 0;
@@ -131,6 +145,57 @@ uint64_t encode_stream(const EncModel& em, const uint16_t* w, uint32_t n_c, uint
     return (uint64_t)(sink - scratch);
 }
 
+// Layout 2: one stream of the lanes [l0, l1) of a chunk, one renormalisation
+// per weight.  A lane's weight outside its last group is the pair (s, h =
+// f >> 4): one flush check against the joint bound q_s q_h 2^(32 - M_s - M_h)
+// = q_s q_h 2^16, then h is coded, then s (the decoder takes s first).  In
+// its last group (c weights) a lane codes s only; the h of those weights
+// start the lane's state: the low 3c bits under a leading one at bit
+// max(16, 3c).  The low fraction bits go to the chunk's plane, not here.
+uint64_t encode_stream2(const EncModel& em, const uint16_t* w, uint32_t n_c, uint32_t K, uint32_t l0, uint32_t l1,
+                        uint32_t* x, uint16_t* scratch) {
+    const uint64_t groups = ((uint64_t)n_c + 7) / 8;
+    uint64_t last[512];
+    for (uint32_t l = l0; l < l1; l++) {
+        if (l >= groups) {
+            x[l] = kL;
+            last[l - l0] = UINT64_MAX;
+            continue;
+        }
+        const uint64_t g = l + (uint64_t)K * ((groups - 1 - l) / K);
+        const uint32_t c = (uint32_t)std::min<uint64_t>(8, n_c - 8 * g);
+        uint32_t v = 1u << std::max(16u, 3 * c);
+        for (uint32_t i = 0; i < c; i++) v |= ((w[8 * g + i] & 127u) >> 4) << (3 * i);
+        x[l] = v;
+        last[l - l0] = g;
+    }
+    uint16_t* sink = scratch;
+    const uint32_t T = (uint32_t)((groups + K - 1) / K);
+    for (uint32_t t = T; t-- > 0;) {
+        for (int p = 7; p >= 0; p--) {
+            for (uint32_t l = l1; l-- > l0;) {
+                const uint64_t j = 8ull * ((uint64_t)t * K + l) + (uint64_t)p;
+                if (j >= n_c) continue;
+                const uint32_t v = w[j];
+                const EncSym& es = em.s[v >> 7];
+                if (j / 8 == last[l - l0]) {
+                    put(x[l], es, em.m_s, sink);
+                    continue;
+                }
+                const EncSym& eh = em.h[em.route[v >> 7]][(v & 127u) >> 4];
+                uint32_t& xl = x[l];
+                if (xl >= ((uint64_t)es.q * eh.q) << (32 - em.m_s - em.m_f)) {
+                    *sink++ = (uint16_t)xl;
+                    xl >>= 16;
+                }
+                xl = ((xl / eh.q) << em.m_f) + xl % eh.q + eh.cum;
+                xl = ((xl / es.q) << em.m_s) + xl % es.q + es.cum;
+            }
+        }
+    }
+    return (uint64_t)(sink - scratch);
+}
+
 void record_shape(uint64_t n, uint32_t W, uint32_t K, uint32_t& w_out, uint32_t& k_out) {
     if (n >= W) { w_out = W; k_out = K; return; }
     const uint64_t per_lane = W / K;
@@ -151,6 +216,7 @@ inline uint64_t state_units(uint32_t P, uint64_t esum) { return (16ull * P + esu
 
 struct ChunkOut {
     std::vector<uint32_t> states;
+    std::vector<uint32_t> plane;                // layout 2: the low fraction bits, a u32 per group
     std::vector<std::vector<uint16_t>> words;   // per stream, decode order
     std::vector<uint64_t> mu;                   // per stream, units of its state bits
     uint64_t units(uint32_t st) const { return mu[st] + words[st].size(); }
@@ -163,7 +229,9 @@ struct ChunkOut {
 
 // chunk payload bytes: the length codes padded to 16 bytes, then the streams
 // back to back (state bits, then words), the whole padded to 16 bytes
-uint64_t payload_bytes(const ChunkOut& co, uint32_t K) { return align_up(code_bytes(K) + 2 * co.total(), 16); }
+uint64_t payload_bytes(const ChunkOut& co, uint32_t K) {
+    return align_up(code_bytes(K) + 4 * co.plane.size() + 2 * co.total(), 16);
+}
 
 struct EncRecord {
     uint32_t kind = 0;
@@ -185,7 +253,7 @@ void build_head(EncRecord& r) {
     const uint64_t stab = 24;
     const uint64_t route_off = stab + 4ull * md.n_sym;
     const uint64_t ftab = align_up(route_off + md.n_sym, 4);
-    const uint64_t tab_end = ftab + 256ull * md.n_tables;
+    const uint64_t tab_end = ftab + (md.layout == 2 ? 8ull : 256ull) * md.n_tables;
     r.index_off = align_up(tab_end, 16);
     r.stab_off = r.index_off + 16ull * r.n_chunks;
     r.head.assign(align_up(r.stab_off + 4ull * (r.S - 1) * r.n_chunks, 16), 0);
@@ -200,6 +268,7 @@ void build_head(EncRecord& r) {
     while ((1u << log2s) < r.S) log2s++;
     b[15] = (uint8_t)log2s;
     wr32(b + 16, md.n_sym);
+    wr32(b + 20, md.layout == 2 ? 2u : 0u);   // version 1 (layout 1 only) keeps 0 here
     uint32_t k = 0;
     for (uint32_t s = 0; s < 512; s++) {
         if (!md.counts_s[s]) continue;
@@ -208,8 +277,13 @@ void build_head(EncRecord& r) {
         b[route_off + k] = (uint8_t)md.route[s];
         k++;
     }
-    for (uint32_t t = 0; t < md.n_tables; t++)
-        for (uint32_t f = 0; f < 128; f++) wr16(b + ftab + 256 * t + 2 * f, md.q_f[t][f]);
+    for (uint32_t t = 0; t < md.n_tables; t++) {
+        if (md.layout == 2) {
+            for (uint32_t h = 0; h < 8; h++) b[ftab + 8 * t + h] = (uint8_t)md.q_h[t][h];
+        } else {
+            for (uint32_t f = 0; f < 128; f++) wr16(b + ftab + 256 * t + 2 * f, md.q_f[t][f]);
+        }
+    }
 }
 
 }  // namespace
@@ -221,8 +295,10 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         set_error("not a BF16RANS container");
         return BS_E_FORMAT;
     }
-    if (rd32(h + 8) != kVersion) {
-        set_error("container version %u is not supported (this library reads version %u)", rd32(h + 8), kVersion);
+    const uint32_t version = rd32(h + 8);
+    if (version != kVersion && version != kVersion2) {
+        set_error("container version %u is not supported (this library reads versions %u and %u)", version, kVersion,
+                  kVersion2);
         return BS_E_VERSION;
     }
     c.n_records = rd32(h + 12);
@@ -266,6 +342,10 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         r.m_f = b[13];
         r.n_tables = b[14];
         r.n_sym = rd32(b + 16);
+        // version 1: the word at +20 is 0 (layout 1); version 2: it names the layout
+        const uint32_t lw = rd32(b + 20);
+        if (version == kVersion ? lw != 0 : (lw != 1 && lw != 2)) { set_error("record %u: bad layout word %u", i, lw); return BS_E_FORMAT; }
+        r.layout = version == kVersion ? 1 : lw;
         const uint32_t K = r.K;
         if (b[15] > 9 || (1u << b[15]) > K) { set_error("record %u: bad stream count", i); return BS_E_FORMAT; }
         r.S = 1u << b[15];
@@ -274,7 +354,8 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
             set_error("record %u: bad chunk shape W=%u K=%u", i, r.W, K);
             return BS_E_FORMAT;
         }
-        if (r.m_s < 9 || r.m_s > 12 || r.m_f < 8 || r.m_f > 10 || r.n_tables > kMaxTables) {
+        if (r.layout == 1 ? (r.m_s < 9 || r.m_s > 12 || r.m_f < 8 || r.m_f > 10 || r.n_tables > kMaxTables)
+                          : (r.m_s < 11 || r.m_s > 12 || r.m_f != 16 - r.m_s || r.n_tables > kMaxHTables)) {
             set_error("record %u: bad table parameters", i);
             return BS_E_FORMAT;
         }
@@ -283,7 +364,7 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         r.stab_off = 24;
         r.route_off = 24 + 4 * r.n_sym;
         r.ftab_off = (uint32_t)align_up(r.route_off + r.n_sym, 4);
-        r.index_off = align_up(r.ftab_off + 256ull * r.n_tables, 16);
+        r.index_off = align_up(r.ftab_off + (r.layout == 2 ? 8ull : 256ull) * r.n_tables, 16);
         if (r.index_off + 16ull * r.n_chunks + 4ull * (r.S - 1) * r.n_chunks > r.rec_len) {
             set_error("record %u: chunk index or stream table out of bounds", i);
             return BS_E_FORMAT;
@@ -302,16 +383,22 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         if (r.n_sym && sum != (1ull << r.m_s)) { set_error("record %u: sign/exponent frequencies do not sum to 2^%u", i, r.m_s); return BS_E_FORMAT; }
         for (uint32_t t = 0; t < r.n_tables; t++) {
             uint64_t fs = 0;
-            for (uint32_t f = 0; f < 128; f++) fs += rd16(b + r.ftab_off + 256 * t + 2 * f);
+            if (r.layout == 2) {
+                for (uint32_t h = 0; h < 8; h++) fs += b[r.ftab_off + 8 * t + h];
+            } else {
+                for (uint32_t f = 0; f < 128; f++) fs += rd16(b + r.ftab_off + 256 * t + 2 * f);
+            }
             if (fs != (1ull << r.m_f)) { set_error("record %u: fraction table %u does not sum to 2^%u", i, t + 1, r.m_f); return BS_E_FORMAT; }
         }
-        const uint64_t cbytes = code_bytes(K);
         const uint32_t P = K / r.S;
         const uint8_t* stab = b + r.index_off + 16ull * r.n_chunks;
         for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
             const uint8_t* e = b + r.index_off + 16ull * ch;
             const uint64_t po = rd64(e);
             const uint64_t total = rd32(e + 8);
+            // layout 2: the plane of low fraction bits sits between the codes and the streams
+            const uint64_t n_c = std::min<uint64_t>(r.W, r.n - (uint64_t)ch * r.W);
+            const uint64_t cbytes = code_bytes(K) + (r.layout == 2 ? plane_bytes(n_c) : 0);
             // the payload (codes and stream area, padded to 16 bytes) within
             // the record; the streams' starts ascend within the area and each
             // stream holds at least its state bits
@@ -361,7 +448,8 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
             }
             if (t.kind == BS_KIND_RAW) continue;
             if (t.tables) {
-                if (t.tables->n != t.n || t.tables->m_s != p->m_s || t.tables->m_f != p->m_f) {
+                if (t.tables->n != t.n || t.tables->m_s != p->m_s || t.tables->m_f != p->m_f ||
+                    t.tables->layout != p->layout) {
                     set_error("tensor %u: model was built for other data or parameters", i);
                     return BS_E_INVAL;
                 }
@@ -412,9 +500,16 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
             co.words.resize(r.S);
             const uint32_t P = r.K / r.S;
             co.mu.resize(r.S);
+            const uint16_t* wc = (const uint16_t*)r.data + c0;
+            if (r.em.layout == 2) {
+                // the plane of low fraction bits, padded to 16 bytes
+                co.plane.assign(align_up((n_c + 7) / 8, 4), 0u);
+                for (uint32_t j = 0; j < n_c; j++) co.plane[j / 8] |= (wc[j] & 15u) << low_bit_pos(j % 8);
+            }
             for (uint32_t st = 0; st < r.S; st++) {
-                const uint64_t nw = encode_stream(r.em, (const uint16_t*)r.data + c0, n_c, r.K, st * P, (st + 1) * P,
-                                                  co.states.data(), buf.data());
+                const uint64_t nw = r.em.layout == 2
+                                        ? encode_stream2(r.em, wc, n_c, r.K, st * P, (st + 1) * P, co.states.data(), buf.data())
+                                        : encode_stream(r.em, wc, n_c, r.K, st * P, (st + 1) * P, co.states.data(), buf.data());
                 std::vector<uint16_t>& v = co.words[st];
                 v.resize(nw);
                 for (uint64_t i = 0; i < nw; i++) v[i] = buf[nw - 1 - i];
@@ -458,7 +553,7 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
         blob->bytes.assign(pos, 0);
         uint8_t* c = blob->bytes.data();
         memcpy(c, kMagic, 8);
-        wr32(c + 8, kVersion);
+        wr32(c + 8, p->layout == 2 ? kVersion2 : kVersion);
         wr32(c + 12, n_tensors);
         wr64(c + 16, kHeaderBytes);
         wr64(c + 24, pos);
@@ -486,7 +581,8 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
                 // length codes, then each stream: its lanes' state bits, then
                 // its words (the buffer is zero-filled)
                 for (uint32_t l = 0; l < r.K; l++) pp[l / 2] |= (uint8_t)(state_code(co.states[l]) << (4 * (l % 2)));
-                uint8_t* area = pp + sb;
+                for (uint64_t g = 0; g < co.plane.size(); g++) wr32(pp + sb + 4 * g, co.plane[g]);
+                uint8_t* area = pp + sb + 4 * co.plane.size();
                 for (uint32_t st = 0; st < r.S; st++) {
                     uint64_t moff = 0;
                     for (uint32_t l = st * P; l < (st + 1) * P; l++) {
@@ -524,7 +620,7 @@ bs_status bs_container_info_get(const void* h, uint64_t len, bs_container_info* 
     bs_status rc = parse_container((const uint8_t*)h, len, c);
     if (rc) return rc;
     memset(info, 0, sizeof(*info));
-    info->version = kVersion;
+    info->version = rd32((const uint8_t*)h + 8);
     info->n_records = c.n_records;
     info->total_len = c.total_len;
     info->out_len = c.out_len;
@@ -563,6 +659,7 @@ bs_status bs_record_info_get(const void* h, uint64_t len, uint32_t index, bs_rec
     info->rec_offset = r.rec_offset;
     info->rec_len = r.rec_len;
     info->chunk_base = r.chunk_base;
+    info->layout = r.kind == BS_KIND_BF16 ? r.layout : 0;
     memcpy(info->sha256, r.sha, 32);
     info->stream_base = r.stream_base;
     info->streams = r.S;
@@ -603,7 +700,7 @@ const char* bs_strerror(bs_status s) {
 }
 
 const char* bs_last_error(void) { return last_error(); }
-const char* bs_version(void) { return "bs 1.0 (container version 1, gfx950)"; }
+const char* bs_version(void) { return "bs 1.1 (container versions 1 and 2, gfx950)"; }
 
 }  // extern "C"
 
@@ -681,6 +778,7 @@ bs_status bs_encode_device_begin(const bs_dtensor* tensors, uint32_t n_tensors, 
     if (!out || (!tensors && n_tensors)) { set_error("NULL argument"); return BS_E_INVAL; }
     *out = nullptr;
     if (!params_ok(p)) return BS_E_INVAL;
+    if (p->layout != 1) { set_error("the GPU encoder writes layout 1 only"); return BS_E_INVAL; }
     hipStream_t hs = (hipStream_t)stream;
     bs_dencoder* e = new (std::nothrow) bs_dencoder();
     if (!e) return BS_E_NOMEM;
@@ -714,7 +812,8 @@ bs_status bs_encode_device_begin(const bs_dtensor* tensors, uint32_t n_tensors, 
             }
             if (t.kind == BS_KIND_RAW) continue;
             if (t.tables) {
-                if (t.tables->n != t.n || t.tables->m_s != p->m_s || t.tables->m_f != p->m_f) {
+                if (t.tables->n != t.n || t.tables->m_s != p->m_s || t.tables->m_f != p->m_f ||
+                    t.tables->layout != p->layout) {
                     set_error("tensor %u: model was built for other data or parameters", i);
                     return fail(BS_E_INVAL);
                 }

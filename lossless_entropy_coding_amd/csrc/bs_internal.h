@@ -14,12 +14,14 @@ namespace bs {
 
 // container constants (the layout is documented in bs.h)
 constexpr char kMagic[8] = {'B', 'F', '1', '6', 'R', 'A', 'N', 'S'};
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 1;           // containers of layout-1 records
+constexpr uint32_t kVersion2 = 2;          // containers that name each record's layout (1 or 2)
 constexpr uint64_t kHeaderBytes = 64;
 constexpr uint64_t kDirEntryBytes = 96;
 constexpr uint64_t kOutAlign = 256;
 constexpr uint32_t kCandidates = 64;        // exponents whose fraction counts are gathered
 constexpr uint32_t kMaxTables = 6;
+constexpr uint32_t kMaxHTables = 31;       // coded h tables of a layout-2 record
 constexpr uint32_t kMaxSyms = 256;
 
 void set_error(const char* fmt, ...);
@@ -68,6 +70,7 @@ struct Record {
     uint8_t sha[32] = {0};
     // BF16 records
     uint32_t W = 0, K = 0, n_chunks = 0, m_s = 0, m_f = 0, n_tables = 0, n_sym = 0;
+    uint32_t layout = 1;            // 2: s and h = f >> 4 coded, l = f & 15 in a plane (m_f holds M_h)
     uint32_t S = 1;                 // word streams per chunk (K / S lanes each)
     uint32_t stab_off = 0, route_off = 0, ftab_off = 0;
     uint64_t index_off = 0;
@@ -92,6 +95,11 @@ uint32_t plan_records(const bs_plan* plan);
 bs_status parse_container(const uint8_t* h, uint64_t len, Container& c);
 
 }  // namespace bs
+
+// Layout 2: bytes of a chunk's plane of low fraction bits (a u32 per group of
+// 8 weights, padded to 16 B), and the bit of position p's low bits in it.
+inline uint64_t plane_bytes(uint64_t n_c) { return bs::align_up(4 * ((n_c + 7) / 8), 16); }
+inline uint32_t low_bit_pos(uint32_t p) { return 16 * (p & 1) + 4 * (p >> 1); }
 
 // the library's opaque byte buffer
 struct bs_blob {

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <array>
+#include <cmath>
 #include <new>
 #include <numeric>
 #include <vector>
@@ -57,12 +58,28 @@ bool params_ok(const bs_params* p) {
         set_error("chunk_weights must be a positive multiple of 8*lanes (got %u)", p->chunk_weights);
         return false;
     }
-    if (p->m_s < 9 || p->m_s > 12 || p->m_f < 8 || p->m_f > 10 || p->max_tables > kMaxTables) {
-        set_error("need 9 <= m_s <= 12, 8 <= m_f <= 10, max_tables <= %u", kMaxTables);
+    if (p->layout == 1) {
+        if (p->m_s < 9 || p->m_s > 12 || p->m_f < 8 || p->m_f > 10 || p->max_tables > kMaxTables) {
+            set_error("layout 1 needs 9 <= m_s <= 12, 8 <= m_f <= 10, max_tables <= %u", kMaxTables);
+            return false;
+        }
+    } else if (p->layout == 2) {
+        if (p->m_s < 11 || p->m_s > 12 || p->m_f != 16 - p->m_s || p->max_tables > kMaxHTables) {
+            set_error("layout 2 needs m_s 11 or 12, m_f = 16 - m_s, max_tables <= %u", kMaxHTables);
+            return false;
+        }
+    } else {
+        set_error("layout must be 1 or 2 (got %u)", p->layout);
         return false;
     }
     return true;
 }
+
+// floor(65536 log2 q) for the table rule of layout 2 (q <= 2^m_f <= 32 there).
+// The double logarithm of an integer is within an ulp of the exact value, and
+// no 65536 log2 q for q <= 2^16 lies that close to an integer without being
+// one (q a power of two, where the logarithm is exact).
+uint32_t log2_q16(uint32_t q) { return (uint32_t)std::floor(std::log2((double)q) * 65536.0); }
 
 // counts -> frequencies summing to 2^M; integer rule documented in bs.h
 bool quantise(const uint64_t* counts, uint32_t A, uint32_t M, uint32_t* q) {
@@ -131,6 +148,37 @@ void choose_contexts(const uint64_t exp_counts[256], const std::vector<uint32_t>
     for (uint32_t s = 0; s < 512; s++) md.route[s] = md.counts_s[s] ? id[s & 255] : 0;
 }
 
+// Layout 2: the coded h tables.  hc[e][h] = counts of h = f >> 4 over both
+// signs of exponent e.  An exponent is eligible when quantising its counts
+// saves more than 64 bits against the flat table (bits counted in units of
+// 2^-16 with floor(65536 log2 q)); the max_tables largest savings win (lower
+// exponent on ties); ids ascend with the exponent.
+void choose_htables(const std::array<std::array<uint64_t, 8>, 256>& hc, uint32_t m_h, uint32_t max_tables, Model& md) {
+    struct Cand { __int128 saved; uint32_t e; std::array<uint32_t, 8> q; };
+    std::vector<Cand> ok;
+    const int64_t flat = 65536 * (int64_t)(m_h - 3);
+    for (uint32_t e = 0; e < 256; e++) {
+        uint64_t n_e = 0;
+        for (uint32_t h = 0; h < 8; h++) n_e += hc[e][h];
+        if (!n_e) continue;
+        Cand c{0, e, {}};
+        quantise(hc[e].data(), 8, m_h, c.q.data());
+        for (uint32_t h = 0; h < 8; h++)
+            if (hc[e][h]) c.saved += (__int128)hc[e][h] * ((int64_t)log2_q16(c.q[h]) - flat);
+        if (c.saved > (__int128)65536 * 64) ok.push_back(c);
+    }
+    std::stable_sort(ok.begin(), ok.end(), [](const Cand& a, const Cand& b) { return a.saved > b.saved; });
+    if (ok.size() > max_tables) ok.resize(max_tables);
+    std::sort(ok.begin(), ok.end(), [](const Cand& a, const Cand& b) { return a.e < b.e; });
+    md.n_tables = (uint32_t)ok.size();
+    std::array<uint32_t, 256> id{};
+    for (uint32_t t = 0; t < ok.size(); t++) {
+        id[ok[t].e] = t + 1;
+        md.q_h[t] = ok[t].q;
+    }
+    for (uint32_t s = 0; s < 512; s++) md.route[s] = md.counts_s[s] ? id[s & 255] : 0;
+}
+
 std::vector<uint32_t> candidates(const uint64_t exp_counts[256]) {
     std::vector<uint32_t> es;
     for (uint32_t e = 0; e < 256; e++)
@@ -141,9 +189,11 @@ std::vector<uint32_t> candidates(const uint64_t exp_counts[256]) {
 }
 
 bool finish_model(Model& md, const bs_params* p, const std::vector<uint32_t>& cand,
-                  const std::vector<std::array<uint64_t, 128>>& merged) {
+                  const std::vector<std::array<uint64_t, 128>>& merged,
+                  const std::array<std::array<uint64_t, 8>, 256>& hc) {
     md.m_s = p->m_s;
     md.m_f = p->m_f;
+    md.layout = p->layout;
     md.n_sym = 0;
     for (uint32_t s = 0; s < 512; s++) md.n_sym += md.counts_s[s] != 0;
     md.n_tables = 0;
@@ -153,6 +203,10 @@ bool finish_model(Model& md, const bs_params* p, const std::vector<uint32_t>& ca
     if (!quantise(md.counts_s.data(), 512, md.m_s, md.q_s.data())) {
         set_error("cannot quantise the sign/exponent counts");
         return false;
+    }
+    if (md.layout == 2) {
+        choose_htables(hc, md.m_f, p->max_tables, md);
+        return true;
     }
     uint64_t ec[256];
     for (uint32_t e = 0; e < 256; e++) ec[e] = md.counts_s[e] + md.counts_s[256 + e];
@@ -172,11 +226,12 @@ void bs_params_default(bs_params* p) {
     if (!p) return;
     p->chunk_weights = 65536;
     p->lanes = 128;
-    p->m_s = 12;
-    p->m_f = 10;
-    p->max_tables = 6;
+    p->m_s = 11;
+    p->m_f = 5;
+    p->max_tables = 31;
     p->threads = 0;
     p->stream_lanes = 0;
+    p->layout = 2;
 }
 
 bs_status bs_build_tables_host(const uint16_t* h, uint64_t n, const bs_params* p, bs_tables** out) {
@@ -199,7 +254,10 @@ bs_status bs_build_tables_host(const uint16_t* h, uint64_t n, const bs_params* p
     std::vector<std::array<uint64_t, 128>> merged(cand.size());
     for (uint32_t c = 0; c < cand.size(); c++)
         for (uint32_t f = 0; f < 128; f++) merged[c][f] = cf[(cand[c] << 7) | f] + cf[((256 + cand[c]) << 7) | f];
-    if (!finish_model(*t, p, cand, merged)) { delete t; return BS_E_INVAL; }
+    std::array<std::array<uint64_t, 8>, 256> hc{};
+    for (uint32_t e = 0; e < 256; e++)
+        for (uint32_t f = 0; f < 128; f++) hc[e][f >> 4] += cf[(e << 7) | f] + cf[((256 + e) << 7) | f];
+    if (!finish_model(*t, p, cand, merged, hc)) { delete t; return BS_E_INVAL; }
     *out = t;
     return BS_OK;
 }
@@ -217,6 +275,7 @@ bs_status bs_build_tables(const void* d_bf16, uint64_t n, const bs_params* p, vo
     bs_status rc = BS_OK;
     std::vector<uint32_t> cand;
     std::vector<std::array<uint64_t, 128>> merged;
+    std::array<std::array<uint64_t, 8>, 256> hc{};
     constexpr size_t kCounters = 256 * 128 + 256;
     auto hip_fail = [&](hipError_t e, const char* what) {
         set_error("%s: %s", what, hipGetErrorString(e));
@@ -247,8 +306,10 @@ bs_status bs_build_tables(const void* d_bf16, uint64_t n, const bs_params* p, vo
         merged.resize(cand.size());
         for (uint32_t c = 0; c < cand.size(); c++)
             for (uint32_t f = 0; f < 128; f++) merged[c][f] = cnt[cand[c] * 128 + f];
+        for (uint32_t x = 0; x < 256; x++)
+            for (uint32_t f = 0; f < 128; f++) hc[x][f >> 4] += cnt[x * 128 + f];
     }
-    if (!finish_model(*t, p, cand, merged)) rc = BS_E_INVAL;
+    if (!finish_model(*t, p, cand, merged, hc)) rc = BS_E_INVAL;
 done:
     if (d_cnt) (void)hipFree(d_cnt);
     if (rc != BS_OK) { delete t; return rc; }
@@ -270,6 +331,14 @@ bs_status bs_tables_get(const bs_tables* t, uint64_t* counts_s, uint32_t* q_s, u
     if (m_s) *m_s = t->m_s;
     if (m_f) *m_f = t->m_f;
     if (n_weights) *n_weights = t->n;
+    return BS_OK;
+}
+
+bs_status bs_tables_get_layout(const bs_tables* t, uint32_t* layout, uint32_t* q_h) {
+    if (!t) { set_error("NULL tables"); return BS_E_INVAL; }
+    if (layout) *layout = t->layout;
+    if (q_h)
+        for (uint32_t k = 0; k < kMaxHTables; k++) memcpy(q_h + 8 * k, t->q_h[k].data(), 8 * 4);
     return BS_OK;
 }
 

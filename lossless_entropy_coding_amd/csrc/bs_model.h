@@ -18,7 +18,9 @@ struct Model {
     std::array<uint64_t, 512> counts_s{};        // cs[s]
     std::array<uint32_t, 512> q_s{};             // sums to 2^m_s
     std::array<uint32_t, 512> route{};           // fraction table id of each occupied s (0 = flat)
-    std::array<std::array<uint32_t, 128>, kMaxTables> q_f{};  // table t at index t-1, sums to 2^m_f
+    std::array<std::array<uint32_t, 128>, kMaxTables> q_f{};  // layout 1: table t at index t-1, sums to 2^m_f
+    uint32_t layout = 1;                         // 2: m_f is M_h = 16 - m_s
+    std::array<std::array<uint32_t, 8>, kMaxHTables> q_h{};   // layout 2: table t at index t-1, sums to 2^m_f
 };
 
 bool params_ok(const bs_params* p);

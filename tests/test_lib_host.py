@@ -126,10 +126,15 @@ def test_validation_errors():
     c = codec.encode([codec.bf16(w)], codec.params(chunk_weights=4096, lanes=8))
     codec.container_info(c)
     bad = bytearray(c)
-    bad[8:12] = struct.pack("<I", 2)
+    bad[8:12] = struct.pack("<I", 3)
     with pytest.raises(L.BSError) as e:
         codec.container_info(bytes(bad))
     assert e.value.rc == L.BS_E_VERSION
+    # version 2 names every BF16 record's layout: a version-1 record's 0 is malformed there
+    bad[8:12] = struct.pack("<I", 2)
+    with pytest.raises(L.BSError) as e:
+        codec.container_info(bytes(bad))
+    assert e.value.rc == L.BS_E_FORMAT
     with pytest.raises(L.BSError) as e:
         codec.container_info(c[:-16])
     assert e.value.rc == L.BS_E_FORMAT
@@ -320,3 +325,71 @@ def test_fixed_device_transcoder_argument_checks():
     assert f(C.c_void_p(4096), 10, C.c_void_p(8192), 1 << 20, None, None) == L.BS_E_INVAL          # no out_len
     assert f(C.c_void_p(4098), 10, C.c_void_p(8192), 1 << 20, C.byref(ln), None) == L.BS_E_INVAL  # misaligned
     assert f(None, 10, C.c_void_p(8192), 1 << 20, C.byref(ln), None) == L.BS_E_INVAL              # no words
+
+
+# ------------------------------------------------------------------ layout 2
+@pytest.mark.parametrize("seed,n,W,K,P,M_s", [(30, 100000, 4096, 8, 4, 11), (31, 33333, 65536, 128, 64, 12),
+                                              (32, 8, 64, 1, 1, 11), (33, 0, 64, 2, 2, 11),
+                                              (34, 300000, 131072, 2048, 64, 11), (35, 262144 * 2 + 5, 65536, 512, 256, 11),
+                                              (36, 5000, 65536, 256, 256, 12), (37, 70001, 65536, 128, 128, 11)])
+def test_layout2_encoder_bytes_match_oracle(seed, n, W, K, P, M_s):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(n) * rng.choice([0.004, 0.02, 0.1])
+    x[rng.random(n) < 0.01] = 0.0
+    w = _words(x)
+    a = O.encode([O.bf16(w)], W=W, K=K, M_s=M_s, M_f=16 - M_s, cmax=31, P=P, layout=2)
+    b = codec.encode([codec.bf16(w)], codec.params2(chunk_weights=W, lanes=K, m_s=M_s, stream_lanes=P))
+    assert a == b
+    assert codec.container_info(b).version == 2 and codec.record_info(b, 0).layout == 2
+
+
+def test_layout2_models_match_oracle():
+    rng = np.random.default_rng(13)
+    for scale in (0.003, 0.02, 0.3):
+        x = rng.standard_normal(200000) * scale
+        x[rng.random(x.size) < 0.02] = 0.0
+        w = _words(x)
+        for M_s, cmax in [(11, 31), (12, 31), (11, 3)]:
+            t = codec.build_tables_host(w, codec.params2(m_s=M_s, max_tables=cmax)).get()
+            cs, cf = O.histogram(w)
+            assert t["layout"] == 2 and (t["q_s"] == O.normalise(cs, M_s)).all()
+            route, nt, qh = O.select_htables(cs, cf, 16 - M_s, cmax)
+            assert nt == t["n_tables"] and (route == t["route"]).all() and (qh[:nt] == t["q_h"]).all()
+
+
+def test_layout2_mixed_records_and_raw():
+    rng = np.random.default_rng(14)
+    a = _words(rng.standard_normal(70000) * 0.02)
+    b = np.full(5000, 0x3F80, np.uint16)
+    raw = np.arange(999, dtype=np.uint8)
+    o = O.encode([O.bf16(a), O.raw(raw), O.bf16(b)], W=65536, K=128, M_s=11, M_f=5, cmax=31, P=64, layout=2)
+    l = codec.encode([codec.bf16(a), codec.raw(raw), codec.bf16(b)], codec.params2(lanes=128, stream_lanes=64))
+    assert o == l
+
+
+def test_layout2_params_rejected():
+    w = np.zeros(100, np.uint16)
+    for kw in [dict(m_s=10), dict(m_s=13), dict(max_tables=32)]:
+        with pytest.raises(L.BSError) as e:
+            codec.encode([codec.bf16(w)], codec.params2(**kw))
+        assert e.value.rc == L.BS_E_INVAL
+    for m_f in (4, 6):   # m_f must be 16 - m_s
+        p = codec.params2(m_s=11)
+        p.m_f = m_f
+        with pytest.raises(L.BSError):
+            codec.encode([codec.bf16(w)], p)
+    p = codec.params2()
+    p.layout = 3
+    with pytest.raises(L.BSError):
+        codec.encode([codec.bf16(w)], p)
+    # a model built for one layout cannot encode the other
+    t = codec.build_tables_host(_words(np.ones(64)), codec.params())
+    with pytest.raises(L.BSError):
+        codec.encode([codec.bf16(_words(np.ones(64)), t)], codec.params2())
+
+
+def test_layout2_is_the_library_default():
+    import ctypes
+    p = L.Params()
+    L.lib().bs_params_default(ctypes.byref(p))
+    assert (p.layout, p.m_s, p.m_f, p.max_tables, p.lanes, p.chunk_weights) == (2, 11, 5, 31, 128, 65536)
