@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--stream-lanes", type=int, default=None, help="override the lanes per word stream")
     ap.add_argument("--m-s", type=int, default=None, help="override the (sign, exponent) table precision")
     ap.add_argument("--m-f", type=int, default=None, help="override the fraction table precision")
+    ap.add_argument("--layout", type=int, default=None, choices=[1, 2],
+                    help="override the record layout (2: one renormalisation per weight; the default except for "
+                         "the 4096x4096 matrix)")
     ap.add_argument("--gemv", action="store_true",
                     help="time the fused decode and matrix-vector product (bs_gemv_async) of the 4096x4096 "
                          "workload against decode-then-GEMV and a GEMV on the uncompressed matrix")
@@ -82,7 +85,9 @@ def parse():
     return a
 
 
-TRAFFIC_SOURCES = {"decode_kernel": ("bs_decode.hip", "bs_device.h"), "fixed": ("bs_fixed.hip", "bs_fixed_device.h")}
+TRAFFIC_SOURCES = {"decode_kernel": ("bs_decode.hip", "bs_decode_common.h", "bs_device.h"),
+                   "decode2_kernel": ("bs_decode2.hip", "bs_decode_common.h", "bs_device.h"),
+                   "fixed": ("bs_fixed.hip", "bs_fixed_device.h")}
 
 
 def kernel_source_sha256(kind: str) -> str:
@@ -752,7 +757,7 @@ def main():
         gen_dev = "cuda" if a.config == "4" else "cpu"
         enc = workloads.encode_config(a.config, device=gen_dev, keep_reference=False, keep_device_reference=True,
                                       lanes=a.lanes, chunk_weights=a.chunk_weights, stream_lanes=a.stream_lanes,
-                                      m_s=a.m_s, m_f=a.m_f)
+                                      m_s=a.m_s, m_f=a.m_f, layout=a.layout)
         job = workloads.DecodeJob(enc)
     log(f"workload {job.name}: {job.n_weights} BF16 weights, container {job.container_bytes / 1e6:.1f} MB, "
         f"built in {time.time() - t0:.1f}s")
@@ -810,7 +815,9 @@ def main():
     # records: tables, index, states, words; verbatim spans) + the bytes written
     alg_bytes = job.read_bytes + out_bytes
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(f"{job.name}|W={job.chunk_weights}|K={job.lanes}|P={job.stream_lanes}")
+    layout = getattr(job, "layout", 1)
+    traffic = measured_traffic(f"{job.name}|W={job.chunk_weights}|K={job.lanes}|P={job.stream_lanes}|L={layout}",
+                               "decode2_kernel" if layout == 2 else "decode_kernel")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
@@ -838,7 +845,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": job.name, "bf16_weights": job.n_weights, "raw_bytes": job.raw_bytes,
                    "chunk_weights": job.chunk_weights, "lanes": job.lanes, "stream_lanes": job.stream_lanes,
-                   "m_s": job.m_s, "m_f": job.m_f,
+                   "m_s": job.m_s, "m_f": job.m_f, "layout": getattr(job, "layout", 1),
                    "bits_per_weight": round(job.bits_per_weight, 5), "entropy_bits": round(job.entropy_bits, 5),
                    "bits_over_entropy_pct": round(100 * (job.bits_per_weight / job.entropy_bits - 1), 3),
                    "cold_cache": bool(a.cold), "parallelism": "single GPU",

@@ -7,6 +7,7 @@ namespace bsd {
 
 constexpr uint32_t kStateLow = 65536u;      // lower end of the rANS state interval
 constexpr uint32_t kMaxTables = 6;          // coded fraction tables per record
+constexpr uint32_t kMaxHTablesDev = 31;     // coded h tables per layout-2 record
 constexpr uint32_t kMaxSyms = 256;          // occupied (sign, exponent) symbols per BF16 record
 
 // Two LDS layouts of a decode workgroup (bytes):
@@ -41,6 +42,14 @@ static_assert(lut_lds(true) + 16 * ring_bytes(4, true) + 8 <= 81920, "compact la
 static_assert(lut_lds(false) + 16 * ring_bytes(4, false) + 8 <= 163840, "full layout must fit in 160 KiB");
 static_assert(lut_lds(false) + 8 * ring_bytes(8, false) + 8 <= 163840, "full layout must fit in 160 KiB");
 
+// Layout 2 lookup-table image of one record (built once per plan):
+//   s part: 2^M_s x 16 B {q_s, slot - cum_s, LDS address of the h page of
+//     route[s] (65536 + 256 route[s]), s}
+//   h part: (n_tables + 1) pages of 256 B (page 0 flat), each 2^M_h x 8 B
+//     {q_h | h << 29, slot - cum_h}
+constexpr uint32_t kHPageBytes = 256;
+constexpr uint32_t kHPagesAt = 65536;      // LDS address of h page 0 in a layout-2 workgroup
+
 // Device lookup-table image of one record (built once per plan):
 //   s part: 2^M_s x {A, B}
 //     A = q_s | (page << 24), page = LDS address of the routed fraction table >> 11
@@ -66,7 +75,8 @@ struct RecDev {
     uint32_t n_sym;
     uint32_t stab_off;      // byte offset (from body) of the s-table
     uint32_t route_off;     // byte offset (from body) of the route bytes
-    uint32_t ftab_off;      // byte offset (from body) of the fraction tables
+    uint32_t ftab_off;      // byte offset (from body) of the fraction tables (layout 2: the h tables)
+    uint32_t layout;        // 1, or 2: s and h = f >> 4 coded (m_f holds M_h), l = f & 15 in a plane
 };
 
 // One launch class of a plan (lanes per thread 1, 2 or 4; or 8): its BF16 records in container order
@@ -116,6 +126,9 @@ int bsk_build_luts(const uint8_t* d_container, const bsd::RecDev* d_recs, uint32
 // thread; variant 0: a mix of 1 and 2; variant 3: a mix of 1, 2 and 4.
 // compact: the records use the compact LDS layout (not with variant 8).
 int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, bool compact, void* stream);
+// layout-2 records: variant 1, 2 or 4 (every record of the launch has that
+// many lanes per thread), 0 (a mix of 1 and 2) or 3 (a mix with 4)
+int bsk_decode2(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream);
 // the fused matrix-vector product of one record (full layout, variant 1, 2 or 4), y zeroed first
 int bsk_gemv(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream);
 int bsk_raw_copy(const uint8_t* d_container, const bsd::RawDev* d_raw, uint32_t n_raw, uint8_t* d_out,

@@ -107,6 +107,45 @@ __global__ __launch_bounds__(256) void lut_kernel(const uint8_t* __restrict__ c,
         route[s] = body[r.route_off + k];
     }
     const uint32_t nt = r.n_tables + 1;
+    if (r.layout == 2) {
+        // layout 2: 16-byte s entries {q_s, slot - cum_s, LDS address of the
+        // h page, s} and 256-byte h pages of 8-byte entries {q_h | h << 29,
+        // slot - cum_h}; page 0 is flat (q_h = 2^(M_h - 3))
+        __shared__ uint32_t qh[kMaxHTablesDev + 1][8], cumh[kMaxHTablesDev + 1][8];
+        for (uint32_t i = threadIdx.x; i < nt * 8; i += blockDim.x) {
+            const uint32_t t = i / 8, h = i % 8;
+            qh[t][h] = t == 0 ? (1u << (r.m_f - 3)) : body[r.ftab_off + 8 * (t - 1) + h];
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t a = 0;
+            for (int s = 0; s < 512; s++) { cums[s] = a; a += qs[s]; }
+        }
+        if (threadIdx.x >= 64 && threadIdx.x < 64 + nt) {
+            const uint32_t t = threadIdx.x - 64;
+            uint32_t a = 0;
+            for (int h = 0; h < 8; h++) { cumh[t][h] = a; a += qh[t][h]; }
+        }
+        __syncthreads();
+        uint4* so = (uint4*)(luts + r.lut_off);
+        const uint32_t ns = 1u << r.m_s;
+        for (uint32_t slot = threadIdx.x; slot < ns; slot += blockDim.x) {
+            const uint32_t s = last_le(cums, 512, slot);
+            so[slot] = make_uint4(qs[s], slot - cums[s], kHPagesAt + route[s] * kHPageBytes, s);
+        }
+        uint2* ho = (uint2*)(luts + r.lut_off + 16ull * ns);
+        const uint32_t nh = 1u << r.m_f;
+        for (uint32_t i = threadIdx.x; i < nt * (kHPageBytes / 8); i += blockDim.x) {
+            const uint32_t t = i / (kHPageBytes / 8), slot = i % (kHPageBytes / 8);
+            uint2 v = make_uint2(0, 0);
+            if (slot < nh) {
+                const uint32_t h = last_le(cumh[t], 8, slot);
+                v = make_uint2(qh[t][h] | (h << 29), slot - cumh[t][h]);
+            }
+            ho[i] = v;
+        }
+        return;
+    }
     for (uint32_t i = threadIdx.x; i < nt * 128; i += blockDim.x) {
         uint32_t t = i / 128, f = i % 128;
         qf[t][f] = t == 0 ? (1u << (r.m_f - 7)) : ld16(body + r.ftab_off + 256 * (t - 1) + 2 * f);

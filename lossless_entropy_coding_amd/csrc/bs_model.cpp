@@ -68,6 +68,10 @@ bool params_ok(const bs_params* p) {
             set_error("layout 2 needs m_s 11 or 12, m_f = 16 - m_s, max_tables <= %u", kMaxHTables);
             return false;
         }
+        if ((p->stream_lanes ? p->stream_lanes : K) > 256) {
+            set_error("layout 2 decodes with at most 256 lanes per word stream: set stream_lanes");
+            return false;
+        }
     } else {
         set_error("layout must be 1 or 2 (got %u)", p->layout);
         return false;

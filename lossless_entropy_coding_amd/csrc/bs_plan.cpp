@@ -32,9 +32,12 @@ struct bs_plan {
     // one record list per launch class: records with 1, 2 or 4 lanes per
     // thread share one kernel (16-wave workgroups), in the full or the compact
     // LDS layout; eight lanes per thread have their own (8-wave workgroups)
-    static constexpr int kClasses = 3;
-    static constexpr uint32_t kMaxR[kClasses] = {4, 4, 8};
-    static constexpr bool kCompact[kClasses] = {false, true, false};
+    // layout; records of layout 2 (one renormalisation per weight) form the
+    // fourth class, with their own kernel
+    static constexpr int kClasses = 4;
+    static constexpr uint32_t kMaxR[kClasses] = {4, 4, 8, 4};
+    static constexpr bool kCompact[kClasses] = {false, true, false, false};
+    static constexpr int kLayout2 = 3;
     int cus = 256;
     std::vector<uint32_t> dev_index;   // record -> index in d_recs (BF16) or d_raws (RAW)
     std::vector<uint32_t> rclass;      // record -> class (BF16)
@@ -44,8 +47,8 @@ struct bs_plan {
     std::vector<bsd::RawDev> raws;
     std::vector<bsd::RecDev> h_recs;   // host copy of d_recs (a launch of one record passes it by value)
     bsd::RecDev* d_recs = nullptr;
-    uint32_t* d_cls_recs[kClasses] = {nullptr, nullptr, nullptr};
-    uint32_t* d_cls_start[kClasses] = {nullptr, nullptr, nullptr};
+    uint32_t* d_cls_recs[kClasses] = {};
+    uint32_t* d_cls_start[kClasses] = {};
     bsd::RawDev* d_raws = nullptr;
     uint8_t* d_luts = nullptr;
     unsigned long long* d_cmp = nullptr;   // compare results (2 words)
@@ -77,7 +80,7 @@ bs_status hip_err(hipError_t e, const char* what) {
 void ranges(const bs_plan* p, uint32_t first, uint32_t count, uint32_t* e0, uint32_t* e1, uint32_t& r0,
             uint32_t& r1) {
     r0 = r1 = 0;
-    bool have_e[bs_plan::kClasses] = {false, false, false}, have_r = false;
+    bool have_e[bs_plan::kClasses] = {}, have_r = false;
     for (int k = 0; k < bs_plan::kClasses; k++) e0[k] = e1[k] = 0;
     for (uint32_t i = first; i < first + count; i++) {
         const Record& r = p->c.recs[i];
@@ -196,9 +199,22 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
         d.route_off = r.route_off;
         d.ftab_off = r.ftab_off;
         const uint32_t R = d.lanes_per_thread;
-        d.compact = R <= 4 && r.m_s <= 11 && r.m_f <= 9;
-        lut_bytes += (8ull << r.m_s) + (r.n_tables + 1ull) * bsd::fpage_bytes(d.compact);
-        const uint32_t k = R == 8 ? 2 : d.compact ? 1 : 0;
+        d.layout = r.layout;
+        uint32_t k;
+        if (r.layout == 2) {
+            if (R > 4) {
+                plan_free(p);
+                set_error("record %u: layout 2 decodes with at most 256 lanes per word stream (it has %u)", i, d.P);
+                return BS_E_INVAL;
+            }
+            d.compact = 0;
+            lut_bytes += (16ull << r.m_s) + (r.n_tables + 1ull) * bsd::kHPageBytes;
+            k = bs_plan::kLayout2;
+        } else {
+            d.compact = R <= 4 && r.m_s <= 11 && r.m_f <= 9;
+            lut_bytes += (8ull << r.m_s) + (r.n_tables + 1ull) * bsd::fpage_bytes(d.compact);
+            k = R == 8 ? 2 : d.compact ? 1 : 0;
+        }
         p->rclass[i] = k;
         p->cls_pos[i] = (uint32_t)p->cls_recs[k].size();
         p->cls_recs[k].push_back((uint32_t)recs.size());
@@ -316,7 +332,8 @@ bs_status bs_decode_async(const bs_plan* p, uint32_t first, uint32_t count, void
             rmax = std::max(rmax, R);
         }
         const uint32_t variant = rmin == rmax ? rmax : rmax <= 2 ? 0 : 3;
-        int e = bsk_decode(&a, groups, variant, bs_plan::kCompact[k], stream);
+        int e = k == bs_plan::kLayout2 ? bsk_decode2(&a, groups, variant, stream)
+                                       : bsk_decode(&a, groups, variant, bs_plan::kCompact[k], stream);
         if (e) return hip_err((hipError_t)e, "decode launch");
     }
     if (r1 > r0) {
@@ -339,6 +356,7 @@ bs_status bs_gemv_async(const bs_plan* p, uint32_t record, uint64_t rows, uint64
     }
     if (((uintptr_t)d_x & 15) || ((uintptr_t)d_y & 3)) { set_error("x must be 16-byte aligned, y 4-byte aligned"); return BS_E_INVAL; }
     const int k = (int)p->rclass[record];
+    if (k == bs_plan::kLayout2) { set_error("record %u: the fused product reads layout-1 records", record); return BS_E_INVAL; }
     if (bs_plan::kCompact[k] || bs_plan::kMaxR[k] > 4) {
         set_error("the fused product runs on records in the full table layout with at most 4 lanes per thread");
         return BS_E_INVAL;

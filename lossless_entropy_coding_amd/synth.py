@@ -35,7 +35,8 @@ class Workload:
     lanes: int = 64
     stream_lanes: int = 0     # lanes per word stream (0: one stream per chunk)
     m_s: int = 12             # precision of the (sign, exponent) table
-    m_f: int = 10             # precision of the fraction tables
+    m_f: int = 10             # precision of the fraction tables (layout 2: of the h tables, 16 - m_s)
+    layout: int = 1           # record layout: 2 codes s and f >> 4 with one renormalisation per weight
 
     @property
     def n_bf16(self) -> int:

@@ -47,7 +47,7 @@ class Encoded:
 def encode_workload(wl: synth.Workload, device: str = "cpu", keep_reference: bool = True,
                     keep_device_reference: bool = False, threads: int = 0) -> Encoded:
     p = codec.params(chunk_weights=wl.chunk_weights, lanes=wl.lanes, threads=threads, stream_lanes=wl.stream_lanes,
-                     m_s=wl.m_s, m_f=wl.m_f)
+                     m_s=wl.m_s, m_f=wl.m_f, max_tables=31 if wl.layout == 2 else 6, layout=wl.layout)
     tensors = []
     ent_sum, n_bf16 = 0.0, 0
     for it in wl.items:
@@ -66,7 +66,7 @@ def encode_workload(wl: synth.Workload, device: str = "cpu", keep_reference: boo
                   entropy_bits=ent_sum / n_bf16 if n_bf16 else math.nan,
                   bits_per_weight=8.0 * info.bf16_bytes / info.bf16_weights if info.bf16_weights else math.nan,
                   params=dict(chunk_weights=wl.chunk_weights, lanes=wl.lanes, stream_lanes=wl.stream_lanes or wl.lanes,
-                              m_s=wl.m_s, m_f=wl.m_f, max_tables=6))
+                              m_s=wl.m_s, m_f=wl.m_f, max_tables=31 if wl.layout == 2 else 6, layout=wl.layout))
     if keep_reference or keep_device_reference:
         ref = np.zeros(info.out_len, np.uint8)
         for i, t in enumerate(tensors):
@@ -94,16 +94,27 @@ def _with_streams(wl: synth.Workload, stream_lanes: int) -> synth.Workload:
 # (64 weights per lane) still keep the lane-state overhead inside the 1% size
 # budget, and streams of 64 lanes let 32 wavefronts decode each chunk, so
 # that 4096 wavefronts share the GPU.
+def _layout2(wl: synth.Workload, m_s: int = 11) -> synth.Workload:
+    wl.layout, wl.m_s, wl.m_f = 2, m_s, 16 - m_s
+    return wl
+
+
+# Layout 2 (one renormalisation per weight, the low fraction bits in a plane)
+# for every workload but the 4096x4096 matrix: its 1% exact zeros each pay
+# the four verbatim low bits, and it needs 2048 lanes per chunk to fill the
+# GPU, which together would exceed the 1% size budget in layout 2; it keeps
+# layout 1 (a version-1 container).
 CONFIG_BUILDERS = {
-    "1": lambda device: synth.cfg1(device),
+    "1": lambda device: _layout2(synth.cfg1(device)),
     "2": lambda device: _with_streams(synth.cfg2(device, lanes=2048), 64),
-    "3": lambda device: synth.cfg3(device, lanes=256),
-    "4": lambda device: synth.cfg4(device),
+    "3": lambda device: _layout2(synth.cfg3(device, lanes=256)),
+    "4": lambda device: _layout2(synth.cfg4(device)),
 }
 
 
 def encode_config(cfg: str, device: str = "cpu", lanes: int | None = None, chunk_weights: int | None = None,
-                  stream_lanes: int | None = None, m_s: int | None = None, m_f: int | None = None, **kw) -> Encoded:
+                  stream_lanes: int | None = None, m_s: int | None = None, m_f: int | None = None,
+                  layout: int | None = None, **kw) -> Encoded:
     wl = CONFIG_BUILDERS[cfg](device)
     if lanes:
         wl.lanes = lanes
@@ -112,8 +123,16 @@ def encode_config(cfg: str, device: str = "cpu", lanes: int | None = None, chunk
         wl.chunk_weights = chunk_weights
     if stream_lanes is not None:
         wl.stream_lanes = stream_lanes
+    if layout:
+        wl.layout = layout
+        if layout == 2 and not m_s:
+            wl.m_s, wl.m_f = 11, 5
+        elif layout == 1 and not m_s:
+            wl.m_s, wl.m_f = 12, 10
     if m_s:
         wl.m_s = m_s
+        if wl.layout == 2:
+            wl.m_f = 16 - m_s
     if m_f:
         wl.m_f = m_f
     if cfg == "4":
@@ -138,9 +157,13 @@ class DecodeJob:
         self.stream_lanes = enc.params["stream_lanes"]
         self.lanes_per_thread = max(1, self.stream_lanes // 64)
         self.m_s, self.m_f = enc.params["m_s"], enc.params["m_f"]
+        self.layout = enc.params["layout"]
         # the decode kernel instance the workload's large records run on
-        compact = self.lanes_per_thread <= 4 and self.m_s <= 11 and self.m_f <= 9
-        self.kernel_name = "decode_kernel<%d, %s>" % (self.lanes_per_thread, "true" if compact else "false")
+        if self.layout == 2:
+            self.kernel_name = "decode2_kernel<%d>" % self.lanes_per_thread
+        else:
+            compact = self.lanes_per_thread <= 4 and self.m_s <= 11 and self.m_f <= 9
+            self.kernel_name = "decode_kernel<%d, %s>" % (self.lanes_per_thread, "true" if compact else "false")
         self.container_bytes = len(enc.container)
         info = codec.container_info(enc.container)
         # bytes a decode reads: BF16 record bytes (tables, index, states, words) and verbatim spans

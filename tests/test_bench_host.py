@@ -36,7 +36,7 @@ def test_committed_traffic_records_match_the_kernel_sources():
     rec = _records()
     assert rec["workloads"], "no traffic records"
     for key, w in rec["workloads"].items():
-        kind = "fixed" if key.startswith("fixed|") else "decode_kernel"
+        kind = "fixed" if key.startswith("fixed|") else "decode2_kernel" if key.endswith("|L=2") else "decode_kernel"
         assert w["kernel_source_sha256"] == bench.kernel_source_sha256(kind), key
         assert bench.measured_traffic(key, kind) == w["traffic_bytes"]
         # counters close to the algorithmic bytes: nothing re-read
@@ -44,16 +44,18 @@ def test_committed_traffic_records_match_the_kernel_sources():
         assert w["traffic_bytes"] == w["fetch_bytes"] + w["write_bytes"]
 
 
-def test_default_workload_has_a_traffic_record():
-    keys = list(_records()["workloads"])
-    assert any(k.startswith("cfg2_4096x4096") for k in keys)
+def test_traffic_keys_name_the_layout():
+    for key in _records()["workloads"]:
+        assert key.startswith("fixed|") or key.endswith(("|L=1", "|L=2")), key
 
 
 def test_unknown_workload_or_changed_source_gives_null(monkeypatch):
     assert bench.measured_traffic("no such workload") is None
-    key = next(k for k in _records()["workloads"] if not k.startswith("fixed|"))
+    key = next(iter(_records()["workloads"]))
+    kind = "fixed" if key.startswith("fixed|") else "decode2_kernel" if key.endswith("|L=2") else "decode_kernel"
+    assert bench.measured_traffic(key, kind) is not None
     monkeypatch.setattr(bench, "kernel_source_sha256", lambda kind: "0" * 64)
-    assert bench.measured_traffic(key) is None
+    assert bench.measured_traffic(key, kind) is None
 
 
 def test_copy_calibration_scales():
