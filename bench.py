@@ -126,8 +126,11 @@ def model_build_rate(job):
     if ri is None or ri.kind != 1 or ri.n == 0:
         return None
     words = job.ref[ri.out_offset: ri.out_offset + 2 * ri.n].view(torch.int16)
-    p = codec.params(chunk_weights=job.chunk_weights, lanes=job.lanes, m_s=job.m_s, m_f=job.m_f,
-                     stream_lanes=job.stream_lanes)
+    if getattr(job, "layout", 1) == 2:
+        p = codec.params2(chunk_weights=job.chunk_weights, lanes=job.lanes, m_s=job.m_s, stream_lanes=job.stream_lanes)
+    else:
+        p = codec.params(chunk_weights=job.chunk_weights, lanes=job.lanes, m_s=job.m_s, m_f=job.m_f,
+                         stream_lanes=job.stream_lanes)
     codec.build_tables(words, p)          # warm-up
     best = float("inf")
     for _ in range(3):
@@ -751,7 +754,7 @@ def main():
     if a.config == "5":
         from lossless_entropy_coding_amd import checkpoint
         over = {k: v for k, v in (("m_s", a.m_s), ("m_f", a.m_f), ("lanes", a.lanes), ("chunk_weights", a.chunk_weights),
-                                  ("stream_lanes", a.stream_lanes)) if v}
+                                  ("stream_lanes", a.stream_lanes), ("layout", a.layout)) if v}
         job = checkpoint.build_job(layers=a.cfg5_layers, log=log, **over)
     else:
         gen_dev = "cuda" if a.config == "4" else "cpu"

@@ -48,25 +48,35 @@ class CheckpointJob:
     """One Plan per layer container; decode() decodes every layer in order."""
 
     def __init__(self, layers: int = 84, chunk_weights: int = 65536, lanes: int = 512, log=print,
-                 device: str = "cuda", m_s: int = 12, m_f: int = 10, stream_lanes: int = 256):
-        layout = synth.cfg5_layout(layers=layers)
-        self.name = "cfg5_checkpoint_%dlayers_%dtensors" % (layers, len(layout))
+                 device: str = "cuda", m_s: int = 11, m_f: int | None = None, stream_lanes: int = 256,
+                 layout: int = 2):
+        tensors = synth.cfg5_layout(layers=layers)
+        self.name = "cfg5_checkpoint_%dlayers_%dtensors" % (layers, len(tensors))
         self.chunk_weights, self.lanes, self.stream_lanes = chunk_weights, lanes, stream_lanes or lanes
-        self.m_s, self.m_f = m_s, m_f
+        # record layout 2 codes the fraction's high three bits at M_h = 16 - M_s
+        if m_f is None:
+            m_f = 16 - m_s if layout == 2 else 10
+        self.m_s, self.m_f, self.layout = m_s, m_f, layout
         self.lanes_per_thread = max(1, self.stream_lanes // 64)
         # one mixed launch per layer: matrices (several lanes per thread) and vectors (one)
-        self.kernel_name = "decode_kernel<%d, %s>" % (0 if self.lanes_per_thread <= 2 else 3,
-                                                      "true" if m_s <= 11 and m_f <= 9 else "false")
+        variant = 0 if self.lanes_per_thread <= 2 else 3
+        if layout == 2:
+            self.kernel_name = "decode2_kernel<%d>" % variant
+        else:
+            self.kernel_name = "decode_kernel<%d, %s>" % (variant, "true" if m_s <= 11 and m_f <= 9 else "false")
         self.plans, self.refs = [], []
         self.n_weights = self.raw_bytes = self.read_bytes = self.container_bytes = 0
         self.n_tensors = 0
         bits = ent = 0.0
-        p = codec.params(chunk_weights=chunk_weights, lanes=lanes, m_s=m_s, m_f=m_f, stream_lanes=stream_lanes)
+        if layout == 2:
+            p = codec.params2(chunk_weights=chunk_weights, lanes=lanes, m_s=m_s, stream_lanes=stream_lanes)
+        else:
+            p = codec.params(chunk_weights=chunk_weights, lanes=lanes, m_s=m_s, m_f=m_f, stream_lanes=stream_lanes)
         pool = cf.ThreadPoolExecutor(max_workers=host_threads())
         t0 = time.time()
         out_max = 16
         for layer in range(layers + 1):
-            wl = synth.cfg5_layer(layer, device=device, chunk_weights=chunk_weights, lanes=lanes, layout=layout)
+            wl = synth.cfg5_layer(layer, device=device, chunk_weights=chunk_weights, lanes=lanes, layout=tensors)
             words = [synth.as_words(it.tensor) for it in wl.items]
             digests = list(pool.map(_digest, words))
             dev = codec.encode_device([("bf16", w) for w in words], p, digests=digests)

@@ -748,6 +748,11 @@ void fill_enc_tab(const bs::EncModel& em, bsd::EncTabDev& t) {
         t.s_qc[s] = em.s[s].q | em.s[s].cum << 16;
         t.route[s] = em.route[s];
     }
+    if (em.layout == 2) {
+        for (uint32_t k = 0; k <= bs::kMaxHTables; k++)
+            for (uint32_t h = 0; h < 8; h++) t.h_qc[k * 8 + h] = em.h[k][h].q | em.h[k][h].cum << 16;
+        return;
+    }
     for (uint32_t k = 0; k <= bs::kMaxTables; k++)
         for (uint32_t f = 0; f < 128; f++) t.f_qc[k * 128 + f] = em.f[k][f].q | em.f[k][f].cum << 16;
 }
@@ -759,6 +764,7 @@ bsd::EncArgs enc_args(const bs_dencoder* e, const bs_dencoder::Rec& r) {
     a.n = r.n;
     a.W = r.W; a.K = r.K; a.S = r.S; a.P = r.P;
     a.n_chunks = r.n_chunks; a.m_s = r.em.m_s; a.m_f = r.em.m_f;
+    a.layout = r.em.layout;
     a.tab = (const bsd::EncTabDev*)(e->d_scratch + r.o_tab);
     a.words = (uint16_t*)(e->d_scratch + r.o_words);
     a.states = (uint32_t*)(e->d_scratch + r.o_states);
@@ -778,7 +784,6 @@ bs_status bs_encode_device_begin(const bs_dtensor* tensors, uint32_t n_tensors, 
     if (!out || (!tensors && n_tensors)) { set_error("NULL argument"); return BS_E_INVAL; }
     *out = nullptr;
     if (!params_ok(p)) return BS_E_INVAL;
-    if (p->layout != 1) { set_error("the GPU encoder writes layout 1 only"); return BS_E_INVAL; }
     hipStream_t hs = (hipStream_t)stream;
     bs_dencoder* e = new (std::nothrow) bs_dencoder();
     if (!e) return BS_E_NOMEM;
@@ -898,7 +903,8 @@ bs_status bs_encode_device_begin(const bs_dtensor* tensors, uint32_t n_tensors, 
                     wr64(r.head.data() + r.index_off + 16ull * ch, len);
                     wr32(r.head.data() + r.index_off + 16ull * ch + 8, (uint32_t)at);
                     r.chunk_off[ch] = len;
-                    len += align_up(code_bytes(r.K) + 2 * at, 16);
+                    const uint64_t n_c = std::min<uint64_t>(r.W, r.n - (uint64_t)ch * r.W);
+                    len += align_up(code_bytes(r.K) + (r.em.layout == 2 ? plane_bytes(n_c) : 0) + 2 * at, 16);
                 }
             }
             r.rec_len = len;
@@ -912,7 +918,7 @@ bs_status bs_encode_device_begin(const bs_dtensor* tensors, uint32_t n_tensors, 
         e->top.assign(align_up(kHeaderBytes + kDirEntryBytes * n_tensors, 16), 0);
         uint8_t* c = e->top.data();
         memcpy(c, kMagic, 8);
-        wr32(c + 8, kVersion);
+        wr32(c + 8, p->layout == 2 ? kVersion2 : kVersion);
         wr32(c + 12, n_tensors);
         wr64(c + 16, kHeaderBytes);
         wr64(c + 24, pos);

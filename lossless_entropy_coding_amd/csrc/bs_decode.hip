@@ -340,7 +340,7 @@ __device__ __forceinline__ void run_units(const DecodeArgs& a, const RecDev& r, 
     }
     Unit<R, C> un;
     uint32_t u = u0 + wave;
-    if (u < u1) unit_open<R, C, lut_lds(C), false>(a, r, u, wave, lds, un);
+    if (u < u1) unit_open<R, C, false>(a, r, u, wave, lds, lut_lds(C), un);
 #pragma unroll
     for (int k = 0; k < kStageBatch; k++) {
         const uint32_t i = threadIdx.x + k * blockDim.x;
@@ -361,7 +361,7 @@ __device__ __forceinline__ void run_units(const DecodeArgs& a, const RecDev& r, 
     }
     __syncthreads();
     for (; u < u1; u += a.waves) {
-        if (u != u0 + wave) unit_open<R, C, lut_lds(C), false>(a, r, u, wave, lds, un);
+        if (u != u0 + wave) unit_open<R, C, false>(a, r, u, wave, lds, lut_lds(C), un);
         unit_decode<R, C, V>(a, r, lds, un, u1 - u0 <= a.waves);
     }
 }

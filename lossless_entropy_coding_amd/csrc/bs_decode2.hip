@@ -26,27 +26,28 @@ using namespace bsd;
 
 namespace {
 
-// Static LDS layout of a workgroup (bytes):
-//   s table at 0: 2^M_s entries of 16 B {q_s, slot - cum_s, LDS address of
-//     the h page that route[s] names, s} (M_s <= 12: at most 64 KiB);
-//   h pages from 64 KiB, 256 B apart: page t (0 = flat) holds 2^M_h entries
-//     of 8 B {q_h | h << 29, slot - cum_h} (M_h <= 5; at most 32 pages);
-//   the waves' stream rings from 72 KiB.
-constexpr uint32_t kS2 = 65536, kHPage = 256, kLut2 = kS2 + 32 * kHPage;
-static_assert(kLut2 + 16 * ring_bytes(4, false) + 8 <= 163840, "layout-2 workgroup must fit in 160 KiB of LDS");
-
+// LDS of a workgroup (bytes): the record's table image as built (s table
+// of 2^M_s 16-byte entries at 0, then its 2 KiB h pages, each indexed by the
+// state's low 8 bits), then one stream ring per wave.  The image's size
+// depends on M_s and the number of h tables, so the rings start at a
+// per-record offset and the launch takes as many waves as fit.
 struct Model2 {
-    uint32_t m_s, m_h;
-    uint32_t smask, hmask;    // 2^M - 1
+    uint32_t m_s;
+    uint32_t smask;    // 2^M_s - 1
 };
 
 __device__ __forceinline__ uint4 s_entry(const uint8_t* lds, uint32_t x, const Model2& md) {
     return *(const uint4*)(lds + ((x & md.smask) << 4));
 }
 
-__device__ __forceinline__ uint2 h_entry(const uint8_t* lds, uint32_t page, uint32_t x, const Model2& md) {
-    return *(const uint2*)(lds + page + ((x & md.hmask) << 3));
+__device__ __forceinline__ uint2 h_entry(const uint8_t* lds, uint32_t page, uint32_t x) {
+    return *(const uint2*)(lds + page + ((x & 255u) << 3));
 }
+
+// the h step on the state after the s step: q_h (x >> M_h) + slot - cum_h,
+// taken as (x >> 8) (q_h << (8 - M_h)) + entry so that both multiply
+// operands fit 24 bits
+__device__ __forceinline__ uint32_t h_step(uint32_t x, uint2 f) { return __umul24(x >> 8, f.x) + f.y; }
 
 // One group of 8 weights per lane group q, each the pair (s, h), with one
 // renormalisation per weight.  o receives the words' high twelve bits,
@@ -64,11 +65,11 @@ __device__ __forceinline__ void group_pairs(uint32_t (&x)[R], uint32_t (&o)[R][4
         for (int q = 0; q < R; q++) x[q] = __umul24(x[q] >> md.m_s, e[q].x) + e[q].y;
         uint2 f[R];
 #pragma unroll
-        for (int q = 0; q < R; q++) f[q] = h_entry(lds, e[q].z, x[q], md);
+        for (int q = 0; q < R; q++) f[q] = h_entry(lds, e[q].z, x[q]);
         uint32_t w[R];
 #pragma unroll
         for (int q = 0; q < R; q++) {
-            x[q] = __umul24(x[q] >> md.m_h, f[q].x) + f[q].y;
+            x[q] = h_step(x[q], f[q]);
             // (s << 7) | (f.x >> 25), and f.x >> 25 = h << 4
             w[q] = __builtin_amdgcn_alignbit(e[q].w, f[q].x, 25);
         }
@@ -107,7 +108,7 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
     uint32_t (&x)[R] = u.x;
     const uint32_t K = r.K, P = r.P, LB = u.st * P;
     const uint32_t n_c = u.n_c, ch = u.ch, unit = u.unit, nw = u.nw, skip = u.skip;
-    const Model2 md{r.m_s, r.m_f, (1u << r.m_s) - 1, (1u << r.m_f) - 1};
+    const Model2 md{r.m_s, (1u << r.m_s) - 1};
     uint32_t pos = u.pos;
     uint8_t* out = a.out + (r.out_off - a.out_base) + 2ull * ch * r.W;
 
@@ -223,8 +224,8 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
                 const uint4 e = s_entry(lds, xs, md);
                 xs = __umul24(xs >> md.m_s, e.x) + e.y;
                 uint32_t xh = xs;
-                const uint2 f = h_entry(lds, e.z, xh, md);
-                xh = __umul24(xh >> md.m_h, f.x) + f.y;
+                const uint2 f = h_entry(lds, e.z, xh);
+                xh = h_step(xh, f);
                 const uint32_t w = fin[q] ? e.w << 7 : __builtin_amdgcn_alignbit(e.w, f.x, 25);
                 if (act[q]) x[q] = fin[q] ? xs : xh;
                 // shift the 128-bit register right by 16 and insert w on top
@@ -263,8 +264,8 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
     if (lane == 0) a.status[r.status_base + unit] = (badm ? 1u : 0u) | (pos - skip != nw ? 2u : 0u);
 }
 
-// Stage one record's tables into LDS (all threads of the workgroup): the
-// image's s part to 0, its h pages to 64 KiB.  Each thread moves up to
+// Stage one record's table image into LDS (all threads of the workgroup),
+// as it is.  Each thread moves up to
 // kStage2 16-byte pieces per round trip; the first batch's loads are issued
 // before a wave opens its first unit, so that the two overlap.
 constexpr int kStage2 = 8;
@@ -274,9 +275,8 @@ __device__ __forceinline__ void run_units2(const DecodeArgs& a, const RecDev& r,
                                            uint8_t* lds) {
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
     const v4u* src = (const v4u*)(a.luts + r.lut_off);
-    const uint32_t ns16 = 1u << r.m_s;                       // 16-B s entries
-    const uint32_t n16 = ns16 + (r.n_tables + 1) * (kHPage / 16);
-    const uint32_t gap16 = kS2 / 16 - ns16;                  // the h pages land at 64 KiB
+    const uint32_t rb = l2_ring_base(r.m_s, r.n_tables);
+    const uint32_t n16 = rb / 16;
     const uint32_t step = kStage2 * blockDim.x;
     v4u* dst = (v4u*)lds;
     v4u sv[kStage2];
@@ -287,11 +287,11 @@ __device__ __forceinline__ void run_units2(const DecodeArgs& a, const RecDev& r,
     }
     Unit<R, false> un;
     uint32_t u = u0 + wave;
-    if (u < u1) unit_open<R, false, kLut2, true>(a, r, u, wave, lds, un);
+    if (u < u1) unit_open<R, false, true>(a, r, u, wave, lds, rb, un);
 #pragma unroll
     for (int k = 0; k < kStage2; k++) {
         const uint32_t i = threadIdx.x + k * blockDim.x;
-        if (i < n16) dst[i < ns16 ? i : i + gap16] = sv[k];
+        if (i < n16) dst[i] = sv[k];
     }
     for (uint32_t base = threadIdx.x + step; base < n16; base += step) {
         v4u t[kStage2];
@@ -303,12 +303,12 @@ __device__ __forceinline__ void run_units2(const DecodeArgs& a, const RecDev& r,
 #pragma unroll
         for (int k = 0; k < kStage2; k++) {
             const uint32_t i = base + k * blockDim.x;
-            if (i < n16) dst[i < ns16 ? i : i + gap16] = t[k];
+            if (i < n16) dst[i] = t[k];
         }
     }
     __syncthreads();
     for (; u < u1; u += a.waves) {
-        if (u != u0 + wave) unit_open<R, false, kLut2, true>(a, r, u, wave, lds, un);
+        if (u != u0 + wave) unit_open<R, false, true>(a, r, u, wave, lds, rb, un);
         unit_decode2<R>(a, r, lds, un, u1 - u0 <= a.waves);
     }
 }
@@ -334,7 +334,7 @@ __device__ __forceinline__ void run_record2(const DecodeArgs& a, const RecDev& r
 // (1, 2 or 4), 0 for a mix of 1 and 2, 3 for a mix that includes 4.
 template <int G>
 __global__ __launch_bounds__(1024) void decode2_kernel(const DecodeArgs a) {
-    __shared__ __align__(16) uint8_t lds[kLut2 + 16 * ring_bytes(1, false)];
+    __shared__ __align__(16) uint8_t lds[kLds2];
     __shared__ uint32_t pick[2];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t b = blockIdx.x;

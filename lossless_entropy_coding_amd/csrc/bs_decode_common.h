@@ -156,12 +156,12 @@ struct Unit {
     uint32_t unit;
 };
 
-// RB: LDS byte offset of the first ring (after the lookup tables); L2: the
-// record has layout 2, whose chunk payload holds the plane of low fraction
-// bits between the length codes and the stream area.
-template <int R, bool C, uint32_t RB, bool L2>
+// L2: the record has layout 2, whose chunk payload holds the plane of low
+// fraction bits between the length codes and the stream area; rb: LDS byte
+// offset of the first wave's ring (after the lookup tables, uniform).
+template <int R, bool C, bool L2>
 __device__ __forceinline__ void unit_open(const DecodeArgs& a, const RecDev& r, uint32_t unit, uint32_t wave, uint8_t* lds,
-                                          Unit<R, C>& u) {
+                                          uint32_t rb, Unit<R, C>& u) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t ch = unit >> r.streams_log2;
     const uint32_t st = unit & ((1u << r.streams_log2) - 1);
@@ -201,7 +201,7 @@ __device__ __forceinline__ void unit_open(const DecodeArgs& a, const RecDev& r, 
     // length codes
     constexpr uint32_t RW = ring_words(R, C);
     Ring<RW>& g = u.g;
-    g.base = (uint16_t*)(lds + RB + wave * ring_bytes(R, C));
+    g.base = (uint16_t*)(lds + rb + wave * ring_bytes(R, C));
     g.words = payload + w16;
     g.bytes = aend16 - w16;
     uint4 first[Ring<RW>::kPieces];

@@ -42,13 +42,28 @@ static_assert(lut_lds(true) + 16 * ring_bytes(4, true) + 8 <= 81920, "compact la
 static_assert(lut_lds(false) + 16 * ring_bytes(4, false) + 8 <= 163840, "full layout must fit in 160 KiB");
 static_assert(lut_lds(false) + 8 * ring_bytes(8, false) + 8 <= 163840, "full layout must fit in 160 KiB");
 
-// Layout 2 lookup-table image of one record (built once per plan):
-//   s part: 2^M_s x 16 B {q_s, slot - cum_s, LDS address of the h page of
-//     route[s] (65536 + 256 route[s]), s}
-//   h part: (n_tables + 1) pages of 256 B (page 0 flat), each 2^M_h x 8 B
-//     {q_h | h << 29, slot - cum_h}
-constexpr uint32_t kHPageBytes = 256;
-constexpr uint32_t kHPagesAt = 65536;      // LDS address of h page 0 in a layout-2 workgroup
+// Layout 2 lookup-table image of one record (built once per plan), copied
+// as it is to the start of the workgroup's LDS:
+//   s part at 0: 2^M_s x 16 B {q_s, slot - cum_s, LDS address of the h page
+//     of route[s], s}
+//   h part at 16 * 2^M_s: (n_tables + 1) pages of 2 KiB (page 0 flat).  A
+//     page is indexed by the low 8 bits i of the state after the s step (not
+//     by the M_h-bit slot alone): entry i = {q_h << (8 - M_h) | h << 29,
+//     q_h * (i >> M_h) + (i mod 2^M_h) - cum_h} for the h whose interval holds
+//     the slot i mod 2^M_h.  Then x -> q_h (x >> M_h) + slot - cum_h becomes
+//     x -> (x >> 8) * (q_h << (8 - M_h)) + entry, whose operands fit the
+//     24-bit multiply (x >> 8 < 2^24, q_h << (8 - M_h) <= 256), while x >> M_h
+//     itself can need 27 bits: the state is not renormalised between s and h.
+//   the waves' stream rings after the h part.
+constexpr uint32_t kHPageBytes = 2048;
+constexpr uint32_t kLds2 = 163840 - 16;    // a layout-2 workgroup's LDS (the rest: two words of record lookup)
+constexpr uint32_t l2_ring_base(uint32_t m_s, uint32_t n_tables) { return (16u << m_s) + (n_tables + 1) * kHPageBytes; }
+// waves of a layout-2 workgroup whose records' rings start at `ring_base` at most
+constexpr uint32_t l2_max_waves(uint32_t ring_base) {
+    return ring_base >= kLds2 ? 0u : ((kLds2 - ring_base) / ring_bytes(4, false) < kMaxWaves ? (kLds2 - ring_base) / ring_bytes(4, false) : kMaxWaves);
+}
+static_assert(l2_max_waves(l2_ring_base(12, kMaxHTablesDev)) >= 7 && l2_max_waves(l2_ring_base(11, 29)) == 16,
+              "layout-2 workgroup sizes");
 
 // Device lookup-table image of one record (built once per plan):
 //   s part: 2^M_s x {A, B}

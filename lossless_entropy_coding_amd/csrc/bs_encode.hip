@@ -146,6 +146,114 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncArgs a) {
     }
 }
 
+// Layout 2: code the weight of one sub-step for a lane: outside its last
+// group the pair (h first, then s; the decoder takes s first) with one flush
+// check against the joint bound q_s q_h 2^(32 - M_s - M_h), inside it s alone
+// (bound q_s 2^(32 - M_s)).  Flushing lanes take word slots as in put_symbol.
+__device__ __forceinline__ void put_weight2(bool act, bool pair, uint32_t& x, uint32_t sqc, uint32_t hqc, uint32_t m_s,
+                                           uint32_t m_h, uint16_t* sink, uint32_t& base, uint32_t lane) {
+    const uint32_t qs = sqc & 0xFFFFu, cs = sqc >> 16, qh = hqc & 0xFFFFu, ch = hqc >> 16;
+    const bool flush = act && (pair ? (x >> (32 - m_s - m_h)) >= qs * qh : (x >> (32 - m_s)) >= qs);
+    const uint64_t b = __builtin_amdgcn_ballot_w64(flush);
+    if (flush) {
+        const uint32_t above = (uint32_t)__builtin_popcountll(lane == 63 ? 0ull : b >> (lane + 1));
+        sink[base + above] = (uint16_t)x;
+        x >>= 16;
+    }
+    base += (uint32_t)__builtin_popcountll(b);
+    if (act) {
+        if (pair) x = ((x / qh) << m_h) + x % qh + ch;
+        x = ((x / qs) << m_s) + x % qs + cs;
+    }
+}
+
+// Layout 2: one wavefront per word stream, one sub-step per weight, run
+// backwards.  A lane's start state carries the h of its last group's c
+// weights (the low 3c bits under a leading one at bit max(16, 3c)).
+template <int R>
+__global__ __launch_bounds__(64 * kEncWaves) void encode2_kernel(EncArgs a) {
+    __shared__ uint32_t s_qc[512];
+    __shared__ uint32_t h_qc[(kMaxHTablesDev + 1) * 8];
+    __shared__ uint8_t route[512];
+    for (uint32_t i = threadIdx.x; i < 512; i += 64 * kEncWaves) {
+        s_qc[i] = a.tab->s_qc[i];
+        route[i] = a.tab->route[i];
+    }
+    for (uint32_t i = threadIdx.x; i < (kMaxHTablesDev + 1) * 8; i += 64 * kEncWaves) h_qc[i] = a.tab->h_qc[i];
+    __syncthreads();
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t u = (uint64_t)blockIdx.x * kEncWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (u >= (uint64_t)a.n_chunks * a.S) return;
+    const uint32_t c = (uint32_t)(u / a.S), st = (uint32_t)(u % a.S);
+    const uint64_t c0 = (uint64_t)c * a.W;
+    const uint32_t n_c = (uint32_t)std::min<uint64_t>(a.W, a.n - c0);
+    const uint16_t* w = a.w + c0;
+    const uint32_t K = a.K, l0 = st * a.P;
+    const uint32_t groups = (n_c + 7) / 8, T = (groups + K - 1) / K;
+
+    uint32_t x[R], glast[R];
+    bool lv[R];
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        const uint32_t l = l0 + 64 * q + lane;
+        lv[q] = 64 * q + lane < a.P;
+        x[q] = 65536u;
+        glast[q] = UINT32_MAX;
+        if (lv[q] && l < groups) {
+            const uint32_t g = l + K * ((groups - 1 - l) / K);
+            const uint32_t cnt = std::min(n_c - 8 * g, 8u);
+            uint32_t v = 1u << std::max(16u, 3 * cnt);
+            for (uint32_t i = 0; i < cnt; i++) v |= (uint32_t)((w[8 * g + i] & 127u) >> 4) << (3 * i);
+            x[q] = v;
+            glast[q] = g;
+        }
+    }
+    uint16_t* sink = a.words + u * 2ull * (a.W / a.S);
+    uint32_t base = 0;
+    for (int t = (int)T - 1; t >= 0; t--) {
+        uint32_t gw[R][4];
+        uint32_t g[R];
+#pragma unroll
+        for (int q = 0; q < R; q++) {
+            g[q] = (uint32_t)t * K + l0 + 64 * q + lane;
+            gw[q][0] = gw[q][1] = gw[q][2] = gw[q][3] = 0;
+            if (lv[q] && g[q] < groups) {
+                if (8 * g[q] + 8 <= n_c) {
+                    const uint4 v = *(const uint4*)(w + 8 * g[q]);
+                    gw[q][0] = v.x; gw[q][1] = v.y; gw[q][2] = v.z; gw[q][3] = v.w;
+                } else {
+                    for (uint32_t i = 0; 8 * g[q] + i < n_c; i++) gw[q][i >> 1] |= (uint32_t)w[8 * g[q] + i] << (16 * (i & 1));
+                }
+            }
+        }
+#pragma unroll 1
+        for (int p = 7; p >= 0; p--) {
+#pragma unroll
+            for (int q = R - 1; q >= 0; q--) {
+                const uint32_t j = 8 * g[q] + p;
+                const bool act = lv[q] && j < n_c;
+                const uint32_t v = (gw[q][p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
+                put_weight2(act, g[q] != glast[q], x[q], s_qc[v >> 7], h_qc[route[v >> 7] * 8u + ((v & 127u) >> 4)],
+                            a.m_s, a.m_f, sink, base, lane);
+            }
+        }
+    }
+    uint32_t esum = 0;
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        if (lv[q]) {
+            a.states[(uint64_t)c * K + l0 + 64 * q + lane] = x[q];
+            esum += 31u - (uint32_t)__builtin_clz(x[q]) - 16u;
+        }
+    }
+    for (int off = 32; off; off >>= 1) esum += __shfl_xor(esum, off);
+    if (lane == 0) {
+        a.counts[2 * u] = base;
+        a.counts[2 * u + 1] = esum;
+    }
+}
+
 __global__ __launch_bounds__(64 * kEncWaves) void assemble_kernel(EncArgs a) {
     __shared__ uint32_t bits[kEncWaves][512];   // a stream's state bits: at most 512 lanes x 31 bits
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
@@ -163,7 +271,29 @@ __global__ __launch_bounds__(64 * kEncWaves) void assemble_kernel(EncArgs a) {
             pay[b] = (uint8_t)v;
         }
     }
-    uint16_t* area = (uint16_t*)(pay + ((K + 1ull) / 2 + 15) / 16 * 16);
+    const uint64_t code_bytes = ((K + 1ull) / 2 + 15) / 16 * 16;
+    uint64_t plane = 0;
+    if (a.layout == 2) {
+        // layout 2: the plane of low fraction bits between the codes and the
+        // streams; this stream's wave writes its lanes' groups (position p of
+        // a group at bit 16 (p mod 2) + 4 (p div 2) of the group's word)
+        const uint64_t c0 = (uint64_t)c * a.W;
+        const uint32_t n_c = (uint32_t)std::min<uint64_t>(a.W, a.n - c0);
+        const uint32_t groups = (n_c + 7) / 8;
+        plane = (4ull * groups + 15) / 16 * 16;
+        uint32_t* pw = (uint32_t*)(pay + code_bytes);
+        for (uint32_t t = 0; (uint64_t)t * K < groups; t++) {
+            for (uint32_t l = lane; l < P; l += 64) {
+                const uint32_t gg = t * K + l0 + l;
+                if (gg >= groups) continue;
+                uint32_t v = 0;
+                for (uint32_t i = 0; i < 8 && 8 * gg + i < n_c; i++)
+                    v |= (uint32_t)(a.w[c0 + 8 * gg + i] & 15u) << (16 * (i & 1) + 4 * (i >> 1));
+                pw[gg] = v;
+            }
+        }
+    }
+    uint16_t* area = (uint16_t*)(pay + code_bytes + plane);
     uint16_t* dst = area + a.unit_start[u];
     // state bits: each lane's 16 + e bits below its leading one, in lane order from bit 0
     uint32_t* bb = bits[wave];
@@ -211,6 +341,15 @@ int bsk_encode(const EncArgs* args, uint32_t R, void* stream) {
     if (units == 0) return 0;
     const dim3 grid((uint32_t)((units + kEncWaves - 1) / kEncWaves)), block(64 * kEncWaves);
     hipStream_t st = (hipStream_t)stream;
+    if (args->layout == 2) {
+        switch (R) {
+            case 1: hipLaunchKernelGGL(encode2_kernel<1>, grid, block, 0, st, *args); break;
+            case 2: hipLaunchKernelGGL(encode2_kernel<2>, grid, block, 0, st, *args); break;
+            case 4: hipLaunchKernelGGL(encode2_kernel<4>, grid, block, 0, st, *args); break;
+            default: return (int)hipErrorInvalidValue;
+        }
+        return (int)hipGetLastError();
+    }
     switch (R) {
         case 1: hipLaunchKernelGGL(encode_kernel<1>, grid, block, 0, st, *args); break;
         case 2: hipLaunchKernelGGL(encode_kernel<2>, grid, block, 0, st, *args); break;

@@ -14,6 +14,7 @@ struct EncTabDev {
     uint32_t s_qc[512];
     uint32_t f_qc[(kMaxTables + 1) * 128];
     uint8_t route[512];
+    uint32_t h_qc[(kMaxHTablesDev + 1) * 8];   // layout 2: q | cum << 16 of each h table (0 = flat) and h
 };
 
 // One BF16 record to encode: its chunks' streams (chunk c, stream st = unit
@@ -22,8 +23,8 @@ struct EncArgs {
     const uint16_t* w;          // n weights, 16-B aligned
     uint64_t n;
     uint32_t W, K, S, P;        // P = K / S lanes per stream
-    uint32_t n_chunks, m_s, m_f;
-    uint32_t reserved;
+    uint32_t n_chunks, m_s, m_f;   // layout 2: m_f is M_h
+    uint32_t layout;
     const EncTabDev* tab;
     uint16_t* words;            // unit u's words (in emission order) at words + u * 2 * (W / S)
     uint32_t* states;           // chunk c lane l at states + c * K + l

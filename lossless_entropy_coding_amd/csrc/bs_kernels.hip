@@ -108,9 +108,9 @@ __global__ __launch_bounds__(256) void lut_kernel(const uint8_t* __restrict__ c,
     }
     const uint32_t nt = r.n_tables + 1;
     if (r.layout == 2) {
-        // layout 2: 16-byte s entries {q_s, slot - cum_s, LDS address of the
-        // h page, s} and 256-byte h pages of 8-byte entries {q_h | h << 29,
-        // slot - cum_h}; page 0 is flat (q_h = 2^(M_h - 3))
+        // layout 2 (the image layout is described with kHPageBytes): 16-byte s
+        // entries, then 2 KiB h pages indexed by 8 state bits; page 0 is
+        // flat (q_h = 2^(M_h - 3))
         __shared__ uint32_t qh[kMaxHTablesDev + 1][8], cumh[kMaxHTablesDev + 1][8];
         for (uint32_t i = threadIdx.x; i < nt * 8; i += blockDim.x) {
             const uint32_t t = i / 8, h = i % 8;
@@ -131,18 +131,14 @@ __global__ __launch_bounds__(256) void lut_kernel(const uint8_t* __restrict__ c,
         const uint32_t ns = 1u << r.m_s;
         for (uint32_t slot = threadIdx.x; slot < ns; slot += blockDim.x) {
             const uint32_t s = last_le(cums, 512, slot);
-            so[slot] = make_uint4(qs[s], slot - cums[s], kHPagesAt + route[s] * kHPageBytes, s);
+            so[slot] = make_uint4(qs[s], slot - cums[s], 16u * ns + route[s] * kHPageBytes, s);
         }
         uint2* ho = (uint2*)(luts + r.lut_off + 16ull * ns);
-        const uint32_t nh = 1u << r.m_f;
-        for (uint32_t i = threadIdx.x; i < nt * (kHPageBytes / 8); i += blockDim.x) {
-            const uint32_t t = i / (kHPageBytes / 8), slot = i % (kHPageBytes / 8);
-            uint2 v = make_uint2(0, 0);
-            if (slot < nh) {
-                const uint32_t h = last_le(cumh[t], 8, slot);
-                v = make_uint2(qh[t][h] | (h << 29), slot - cumh[t][h]);
-            }
-            ho[i] = v;
+        const uint32_t hmask = (1u << r.m_f) - 1;
+        for (uint32_t i = threadIdx.x; i < nt * 256; i += blockDim.x) {
+            const uint32_t t = i / 256, b = i % 256, slot = b & hmask;
+            const uint32_t h = last_le(cumh[t], 8, slot);
+            ho[i] = make_uint2((qh[t][h] << (8 - r.m_f)) | (h << 29), qh[t][h] * (b >> r.m_f) + slot - cumh[t][h]);
         }
         return;
     }

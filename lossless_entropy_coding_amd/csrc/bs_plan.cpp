@@ -128,6 +128,16 @@ void launch_shape(const bs_plan* p, int k, uint32_t e0, uint32_t e1, uint32_t& w
     }
     groups = (uint32_t)count(run);
     waves = std::min<uint32_t>(bsd::max_waves(bs_plan::kMaxR[k]), run);
+    if (k == bs_plan::kLayout2) {
+        // a layout-2 workgroup's rings follow its records' table image, whose
+        // size varies: take as many waves as fit after the largest
+        uint32_t rb = 0;
+        for (uint32_t e = e0; e < e1; e++) {
+            const bsd::RecDev& d = p->h_recs[p->cls_recs[k][e]];
+            rb = std::max(rb, bsd::l2_ring_base(d.m_s, d.n_tables));
+        }
+        waves = std::min(waves, bsd::l2_max_waves(rb));
+    }
 }
 
 uint64_t out_extent(const bs_plan* p, uint32_t first, uint32_t count) {
@@ -208,7 +218,7 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
                 return BS_E_INVAL;
             }
             d.compact = 0;
-            lut_bytes += (16ull << r.m_s) + (r.n_tables + 1ull) * bsd::kHPageBytes;
+            lut_bytes += bsd::l2_ring_base(r.m_s, r.n_tables);
             k = bs_plan::kLayout2;
         } else {
             d.compact = R <= 4 && r.m_s <= 11 && r.m_f <= 9;

@@ -158,7 +158,10 @@ def test_layout2_many_records_mixed_lane_classes(stream_lanes, ms):
     c = _encode_both(t_o, t_l, 131072, 256, stream_lanes or 256, ms)
     info = codec.container_info(c)
     bf = [ri for ri in (codec.record_info(c, i) for i in range(info.n_records)) if ri.kind == L.KIND_BF16 and ri.n]
-    assert len({max(ri.lanes // max(ri.streams, 1) // 64, 1) for ri in bf}) >= 2
+    classes = {max(ri.lanes // max(ri.streams, 1) // 64, 1) for ri in bf}
+    # 64 lanes per stream put every record at one lane per thread; wider
+    # streams leave the small records with fewer lanes than the large ones
+    assert len(classes) >= (1 if stream_lanes == 64 else 2), classes
     expect = _oracle_bytes(c)
     plan = codec.Plan(c)
     out = plan.decode()

@@ -104,3 +104,45 @@ def test_device_encoder_errors():
     assert L.lib().bs_encode_device_finish(enc, C.c_void_p(out.data_ptr()), size, None) == L.BS_OK
     L.lib().bs_encode_device_free(enc)
     assert out.cpu().numpy().tobytes() == codec.encode([codec.bf16(np.zeros(4096, np.uint16))], p)
+
+
+CASES2 = [
+    # layout 2 (version-2 containers): (name, sizes, chunk weights, lanes, lanes per stream, M_s)
+    ("l2_k64_p32_two_streams", [5000, 70001], 4096, 64, 32, 11),
+    ("l2_k128_full_and_ragged", [6 * 65536, 65536 + 1025], 65536, 128, 128, 11),
+    ("l2_k256_p128_ms12", [131072 + 2049 + 7], 131072, 256, 128, 12),
+    ("l2_k512_p256_checkpoint_shape", [3 * 65536 + 5, 5120], 65536, 512, 256, 11),
+    ("l2_k2048_p64", [2 * 131072 + 8 * 333 + 3], 131072, 2048, 64, 11),
+    ("l2_k1_tiny", [1, 8, 9], 64, 1, 1, 11),
+]
+
+
+@pytest.mark.parametrize("name,sizes,W,K,P,ms", CASES2, ids=[c[0] for c in CASES2])
+def test_device_container_equals_host_container_layout2(name, sizes, W, K, P, ms):
+    say("encode case", name)
+    rng = np.random.default_rng(len(name) + 100)
+    words = []
+    for i, n in enumerate(sizes):
+        x = rng.standard_normal(n) * (0.02 if i % 2 == 0 else 1.0)
+        x[rng.random(n) < 0.001] *= 60.0
+        x[rng.random(n) < 0.01] = 0.0
+        words.append(_bf16(x))
+    raw = rng.integers(0, 256, 777, dtype=np.uint8)
+    p = codec.params2(chunk_weights=W, lanes=K, stream_lanes=P, m_s=ms)
+    host = codec.encode([codec.bf16(w) for w in words] + [codec.raw(raw)], p)
+    assert host == O.encode([O.bf16(w) for w in words] + [O.raw(raw)], W=W, K=K, P=P, M_s=ms, M_f=16 - ms, cmax=31,
+                            layout=2)
+    dev_tensors = [("bf16", torch.from_numpy(w.view(np.int16).copy()).cuda()) for w in words]
+    dev_tensors.append(("raw", torch.from_numpy(raw.copy()).cuda()))
+    digests = [hashlib.sha256(w.tobytes()).digest() for w in words] + [None]
+    dc = codec.encode_device(dev_tensors, p, digests=digests)
+    torch.cuda.synchronize()
+    got = dc.cpu().numpy().tobytes()
+    assert len(got) == len(host)
+    if got != host:
+        diff = np.flatnonzero(np.frombuffer(got, np.uint8) != np.frombuffer(host, np.uint8))
+        pytest.fail(f"{diff.size} bytes differ, first at {diff[:8]}")
+    plan = codec.Plan(got)
+    out = plan.decode()
+    rc, rep = plan.verify(out, flags=L.VERIFY_STATUS | L.VERIFY_SHA256)
+    assert rc == L.BS_OK, rep
