@@ -48,12 +48,14 @@ class CheckpointJob:
     """One Plan per layer container; decode() decodes every layer in order."""
 
     def __init__(self, layers: int = 84, chunk_weights: int = 65536, lanes: int = 512, log=print,
-                 device: str = "cuda", m_s: int = 11, m_f: int | None = None, stream_lanes: int = 256,
+                 device: str = "cuda", m_s: int | None = None, m_f: int | None = None, stream_lanes: int = 256,
                  layout: int = 2):
         tensors = synth.cfg5_layout(layers=layers)
         self.name = "cfg5_checkpoint_%dlayers_%dtensors" % (layers, len(tensors))
         self.chunk_weights, self.lanes, self.stream_lanes = chunk_weights, lanes, stream_lanes or lanes
         # record layout 2 codes the fraction's high three bits at M_h = 16 - M_s
+        if m_s is None:
+            m_s = 11 if layout == 2 else 12
         if m_f is None:
             m_f = 16 - m_s if layout == 2 else 10
         self.m_s, self.m_f, self.layout = m_s, m_f, layout
