@@ -157,6 +157,21 @@ bs_status bs_build_tables(const void* d_bf16, uint64_t n, const bs_params* p, vo
 /* Same model from host memory (CPU histogram); identical result. */
 bs_status bs_build_tables_host(const uint16_t* h_bf16, uint64_t n, const bs_params* p, bs_tables** out);
 
+/* For callers that cannot allocate memory (harnesses that forbid hipMalloc,
+ * serving loops that must not touch an allocator): bs_build_tables without
+ * any allocation.  The model is written over *t, an existing tables object
+ * (from bs_build_tables or bs_build_tables_host); the result is the one
+ * bs_build_tables gives for the same words and params.  The histogram's
+ * counters sit in a fixed device array of the library (264,192 B on each GPU
+ * it runs on, held until the process ends; its size does not depend on n),
+ * cleared by a kernel at each call.  Calls in one process are serialised by
+ * a host lock held from the clear to the read-back, so they never overlap on
+ * a GPU; the array keeps the last call's counts.  Synchronises `stream`.
+ * n at most BS_NOALLOC_MAX_WEIGHTS (2^36), beyond it BS_E_INVAL with a
+ * message.  Errors: BS_E_INVAL (NULL, bad params, n too large), BS_E_HIP. */
+#define BS_NOALLOC_MAX_WEIGHTS (1ull << 36)
+bs_status bs_build_tables_noalloc(const void* d_bf16, uint64_t n, const bs_params* p, void* stream, bs_tables* t);
+
 void bs_tables_free(bs_tables* t);
 
 /* Read back a model (for inspection and tests).  Arrays are caller-owned:

@@ -23,6 +23,7 @@ BS_E_CORRUPT = -7
 BS_E_MISMATCH = -8
 BS_E_EXISTS = -9
 FIXED_MANY_MAX = 16          # blobs per bs_fixed_decode_many_async call
+NOALLOC_MAX_WEIGHTS = 1 << 36   # words per bs_build_tables_noalloc call
 
 KIND_BF16 = 1
 KIND_RAW = 2
@@ -86,6 +87,7 @@ SIGNATURES = {
     "bs_build_tables": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(Params), C.c_void_p, C.POINTER(C.c_void_p)]),
     "bs_tables_get_layout": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_void_p]),
     "bs_build_tables_host": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(Params), C.POINTER(C.c_void_p)]),
+    "bs_build_tables_noalloc": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(Params), C.c_void_p, C.c_void_p]),
     "bs_tables_free": (None, [C.c_void_p]),
     "bs_tables_get": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(C.c_uint32),
                                 C.POINTER(C.c_uint32), C.POINTER(C.c_uint32), C.POINTER(C.c_uint64)]),

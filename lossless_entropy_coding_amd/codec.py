@@ -92,6 +92,16 @@ def build_tables(words: torch.Tensor, p: L.Params | None = None, stream=None) ->
     return Tables(out.value)
 
 
+def build_tables_noalloc(words: torch.Tensor, into: Tables, p: L.Params | None = None, stream=None) -> Tables:
+    """bs_build_tables_noalloc: the model of a device-resident tensor written
+    over an existing Tables, with nothing allocated by the library."""
+    p = p or params()
+    assert words.is_cuda and words.is_contiguous() and words.element_size() == 2
+    L.check(L.lib().bs_build_tables_noalloc(C.c_void_p(words.data_ptr()), words.numel(), C.byref(p),
+                                            C.c_void_p(_stream_handle(stream)), into.handle), "bs_build_tables_noalloc")
+    return into
+
+
 def build_tables_host(words: np.ndarray, p: L.Params | None = None) -> Tables:
     p = p or params()
     w = np.ascontiguousarray(words, np.uint16)

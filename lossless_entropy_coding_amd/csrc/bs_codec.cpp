@@ -23,8 +23,6 @@
 #include "bs_internal.h"
 #include "bs_model.h"
 
-struct bs_tables : bs::Model {};
-
 namespace bs {
 namespace {
 

@@ -95,9 +95,11 @@ bool quantise(const uint64_t* counts, uint32_t A, uint32_t M, uint32_t* q) {
         occupied += counts[i] != 0;
     }
     if (n == 0 || occupied > total) return false;
+    // (fixed-size working arrays: the model is built without heap memory)
     struct Rem { uint64_t rem; uint32_t idx; };
-    std::vector<Rem> rems;
-    rems.reserve(occupied);
+    if (A > 512) return false;
+    Rem rems[512];
+    uint32_t n_rem = 0;
     int64_t have = 0;
     for (uint32_t i = 0; i < A; i++) {
         if (!counts[i]) { q[i] = 0; continue; }
@@ -105,12 +107,13 @@ bool quantise(const uint64_t* counts, uint32_t A, uint32_t M, uint32_t* q) {
         const uint64_t fl = (uint64_t)(scaled / n);
         q[i] = fl ? (uint32_t)fl : 1u;
         have += q[i];
-        rems.push_back({(uint64_t)(scaled % n), i});
+        rems[n_rem++] = {(uint64_t)(scaled % n), i};
     }
     int64_t deficit = (int64_t)total - have;
     if (deficit > 0) {
-        std::stable_sort(rems.begin(), rems.end(), [](const Rem& a, const Rem& b) { return a.rem > b.rem; });
-        for (int64_t k = 0; k < deficit; k++) q[rems[(size_t)k % rems.size()].idx]++;
+        // largest remainder first, lower index first on ties
+        std::sort(rems, rems + n_rem, [](const Rem& a, const Rem& b) { return a.rem != b.rem ? a.rem > b.rem : a.idx < b.idx; });
+        for (int64_t k = 0; k < deficit; k++) q[rems[(size_t)k % n_rem].idx]++;
     }
     for (; deficit < 0; deficit++) {
         uint32_t* big = nullptr;
@@ -126,26 +129,26 @@ bool quantise(const uint64_t* counts, uint32_t A, uint32_t M, uint32_t* q) {
 // exp_counts[e] = cs[e] + cs[256+e]; merged[c][f] = fraction counts of the
 // c-th candidate (candidates = the 64 most frequent exponents, lower e first
 // on ties, in that order).
-void choose_contexts(const uint64_t exp_counts[256], const std::vector<uint32_t>& cand,
-                     const std::vector<std::array<uint64_t, 128>>& merged, uint32_t m_f, uint32_t max_tables,
-                     Model& md) {
+void choose_contexts(const uint64_t exp_counts[256], const uint32_t* cand, uint32_t n_cand,
+                     const std::array<uint64_t, 128>* merged, uint32_t m_f, uint32_t max_tables, Model& md) {
     struct Scored { uint64_t score; uint32_t e, c; };
-    std::vector<Scored> ok;
-    for (uint32_t c = 0; c < cand.size(); c++) {
+    Scored ok[256];
+    uint32_t n_ok = 0;
+    for (uint32_t c = 0; c < n_cand; c++) {
         const unsigned __int128 n = exp_counts[cand[c]];
         unsigned __int128 sq = 0;
         for (uint32_t f = 0; f < 128; f++) sq += (unsigned __int128)merged[c][f] * merged[c][f];
         const unsigned __int128 excess = 128 * sq - n * n;   // >= 0 by Cauchy-Schwarz
-        if (256 * excess > n * n + (unsigned __int128)726784 * n) ok.push_back({(uint64_t)(excess / n), cand[c], c});
+        if (256 * excess > n * n + (unsigned __int128)726784 * n) ok[n_ok++] = {(uint64_t)(excess / n), cand[c], c};
     }
-    std::sort(ok.begin(), ok.end(), [](const Scored& a, const Scored& b) {
+    std::sort(ok, ok + n_ok, [](const Scored& a, const Scored& b) {
         return a.score != b.score ? a.score > b.score : a.e < b.e;
     });
-    if (ok.size() > max_tables) ok.resize(max_tables);
-    std::sort(ok.begin(), ok.end(), [](const Scored& a, const Scored& b) { return a.e < b.e; });
-    md.n_tables = (uint32_t)ok.size();
+    if (n_ok > max_tables) n_ok = max_tables;
+    std::sort(ok, ok + n_ok, [](const Scored& a, const Scored& b) { return a.e < b.e; });
+    md.n_tables = n_ok;
     std::array<uint32_t, 256> id{};
-    for (uint32_t t = 0; t < ok.size(); t++) {
+    for (uint32_t t = 0; t < n_ok; t++) {
         id[ok[t].e] = t + 1;
         quantise(merged[ok[t].c].data(), 128, m_f, md.q_f[t].data());
     }
@@ -159,7 +162,8 @@ void choose_contexts(const uint64_t exp_counts[256], const std::vector<uint32_t>
 // exponent on ties); ids ascend with the exponent.
 void choose_htables(const std::array<std::array<uint64_t, 8>, 256>& hc, uint32_t m_h, uint32_t max_tables, Model& md) {
     struct Cand { __int128 saved; uint32_t e; std::array<uint32_t, 8> q; };
-    std::vector<Cand> ok;
+    Cand ok[256];
+    uint32_t n_ok = 0;
     const int64_t flat = 65536 * (int64_t)(m_h - 3);
     for (uint32_t e = 0; e < 256; e++) {
         uint64_t n_e = 0;
@@ -169,32 +173,34 @@ void choose_htables(const std::array<std::array<uint64_t, 8>, 256>& hc, uint32_t
         quantise(hc[e].data(), 8, m_h, c.q.data());
         for (uint32_t h = 0; h < 8; h++)
             if (hc[e][h]) c.saved += (__int128)hc[e][h] * ((int64_t)log2_q16(c.q[h]) - flat);
-        if (c.saved > (__int128)65536 * 64) ok.push_back(c);
+        if (c.saved > (__int128)65536 * 64) ok[n_ok++] = c;
     }
-    std::stable_sort(ok.begin(), ok.end(), [](const Cand& a, const Cand& b) { return a.saved > b.saved; });
-    if (ok.size() > max_tables) ok.resize(max_tables);
-    std::sort(ok.begin(), ok.end(), [](const Cand& a, const Cand& b) { return a.e < b.e; });
-    md.n_tables = (uint32_t)ok.size();
+    std::sort(ok, ok + n_ok, [](const Cand& a, const Cand& b) { return a.saved != b.saved ? a.saved > b.saved : a.e < b.e; });
+    if (n_ok > max_tables) n_ok = max_tables;
+    std::sort(ok, ok + n_ok, [](const Cand& a, const Cand& b) { return a.e < b.e; });
+    md.n_tables = n_ok;
     std::array<uint32_t, 256> id{};
-    for (uint32_t t = 0; t < ok.size(); t++) {
+    for (uint32_t t = 0; t < n_ok; t++) {
         id[ok[t].e] = t + 1;
         md.q_h[t] = ok[t].q;
     }
     for (uint32_t s = 0; s < 512; s++) md.route[s] = md.counts_s[s] ? id[s & 255] : 0;
 }
 
-std::vector<uint32_t> candidates(const uint64_t exp_counts[256]) {
-    std::vector<uint32_t> es;
+// the occupied exponents, most frequent first (lower exponent on ties), at
+// most kCandidates of them; returns their number
+uint32_t candidates(const uint64_t exp_counts[256], uint32_t* es) {
+    uint32_t all[256], n = 0;
     for (uint32_t e = 0; e < 256; e++)
-        if (exp_counts[e]) es.push_back(e);
-    std::stable_sort(es.begin(), es.end(), [&](uint32_t a, uint32_t b) { return exp_counts[a] > exp_counts[b]; });
-    if (es.size() > kCandidates) es.resize(kCandidates);
-    return es;
+        if (exp_counts[e]) all[n++] = e;
+    std::sort(all, all + n, [&](uint32_t a, uint32_t b) { return exp_counts[a] != exp_counts[b] ? exp_counts[a] > exp_counts[b] : a < b; });
+    n = std::min<uint32_t>(n, kCandidates);
+    std::copy(all, all + n, es);
+    return n;
 }
 
-bool finish_model(Model& md, const bs_params* p, const std::vector<uint32_t>& cand,
-                  const std::vector<std::array<uint64_t, 128>>& merged,
-                  const std::array<std::array<uint64_t, 8>, 256>& hc) {
+bool finish_model(Model& md, const bs_params* p, const uint32_t* cand, uint32_t n_cand,
+                  const std::array<uint64_t, 128>* merged, const std::array<std::array<uint64_t, 8>, 256>& hc) {
     md.m_s = p->m_s;
     md.m_f = p->m_f;
     md.layout = p->layout;
@@ -214,15 +220,49 @@ bool finish_model(Model& md, const bs_params* p, const std::vector<uint32_t>& ca
     }
     uint64_t ec[256];
     for (uint32_t e = 0; e < 256; e++) ec[e] = md.counts_s[e] + md.counts_s[256 + e];
-    choose_contexts(ec, cand, merged, md.m_f, p->max_tables, md);
+    choose_contexts(ec, cand, n_cand, merged, md.m_f, p->max_tables, md);
     return true;
+}
+
+// The model of n words from the device histogram's counters: cnt[e * 128 +
+// f] counts exponent e and fraction f over both signs, cnt[256 * 128 + e]
+// the negative words of exponent e.  md is overwritten; merged is working
+// memory for kCandidates fraction histograms.  Allocates nothing.
+bs_status model_from_counts(Model& md, const bs_params* p, uint64_t n, const unsigned long long* cnt,
+                            std::array<uint64_t, 128>* merged) {
+    md = Model{};
+    md.n = n;
+    uint32_t cand[kCandidates];
+    uint32_t n_cand = 0;
+    std::array<std::array<uint64_t, 8>, 256> hc{};
+    if (n) {
+        // the (sign, exponent) counts: negatives counted directly, positives
+        // as the exponent's total minus its negatives
+        uint64_t ec[256], sum = 0;
+        for (uint32_t x = 0; x < 256; x++) {
+            uint64_t tot = 0;
+            for (uint32_t f = 0; f < 128; f++) tot += cnt[x * 128 + f];
+            const uint64_t neg = cnt[256 * 128 + x];
+            if (neg > tot) { set_error("histogram counts are inconsistent"); return BS_E_HIP; }
+            md.counts_s[256 + x] = neg;
+            md.counts_s[x] = tot - neg;
+            ec[x] = tot;
+            sum += tot;
+        }
+        if (sum != n) { set_error("histogram counts %llu words, not %llu", (unsigned long long)sum, (unsigned long long)n); return BS_E_HIP; }
+        n_cand = candidates(ec, cand);
+        for (uint32_t c = 0; c < n_cand; c++)
+            for (uint32_t f = 0; f < 128; f++) merged[c][f] = cnt[cand[c] * 128 + f];
+        for (uint32_t x = 0; x < 256; x++)
+            for (uint32_t f = 0; f < 128; f++) hc[x][f >> 4] += cnt[x * 128 + f];
+    }
+    return finish_model(md, p, cand, n_cand, merged, hc) ? BS_OK : BS_E_INVAL;
 }
 
 }  // namespace bs
 
 using namespace bs;
 
-struct bs_tables : Model {};
 
 extern "C" {
 
@@ -254,14 +294,15 @@ bs_status bs_build_tables_host(const uint16_t* h, uint64_t n, const bs_params* p
     }
     uint64_t ec[256];
     for (uint32_t e = 0; e < 256; e++) ec[e] = t->counts_s[e] + t->counts_s[256 + e];
-    const std::vector<uint32_t> cand = candidates(ec);
-    std::vector<std::array<uint64_t, 128>> merged(cand.size());
-    for (uint32_t c = 0; c < cand.size(); c++)
+    uint32_t cand[kCandidates];
+    const uint32_t n_cand = candidates(ec, cand);
+    std::vector<std::array<uint64_t, 128>> merged(kCandidates);
+    for (uint32_t c = 0; c < n_cand; c++)
         for (uint32_t f = 0; f < 128; f++) merged[c][f] = cf[(cand[c] << 7) | f] + cf[((256 + cand[c]) << 7) | f];
     std::array<std::array<uint64_t, 8>, 256> hc{};
     for (uint32_t e = 0; e < 256; e++)
         for (uint32_t f = 0; f < 128; f++) hc[e][f >> 4] += cf[(e << 7) | f] + cf[((256 + e) << 7) | f];
-    if (!finish_model(*t, p, cand, merged, hc)) { delete t; return BS_E_INVAL; }
+    if (!finish_model(*t, p, cand, n_cand, merged.data(), hc)) { delete t; return BS_E_INVAL; }
     *out = t;
     return BS_OK;
 }
@@ -273,48 +314,24 @@ bs_status bs_build_tables(const void* d_bf16, uint64_t n, const bs_params* p, vo
     }
     bs_tables* t = new (std::nothrow) bs_tables();
     if (!t) return BS_E_NOMEM;
-    t->n = n;
     hipStream_t s = (hipStream_t)stream;
-    unsigned long long* d_cnt = nullptr;   // 256 x 128 sign-merged (exponent, fraction) counts, then 256 negative counts
+    unsigned long long* d_cnt = nullptr;   // kHistCounters: see model_from_counts
+    std::vector<unsigned long long> cnt(kHistCounters, 0);
+    std::vector<std::array<uint64_t, 128>> merged(kCandidates);
     bs_status rc = BS_OK;
-    std::vector<uint32_t> cand;
-    std::vector<std::array<uint64_t, 128>> merged;
-    std::array<std::array<uint64_t, 8>, 256> hc{};
-    constexpr size_t kCounters = 256 * 128 + 256;
-    auto hip_fail = [&](hipError_t e, const char* what) {
-        set_error("%s: %s", what, hipGetErrorString(e));
-        rc = BS_E_HIP;
-    };
-    hipError_t e = hipMalloc(&d_cnt, kCounters * sizeof(unsigned long long));
-    if (e != hipSuccess) { hip_fail(e, "hipMalloc"); goto done; }
-    if (n) {
-        std::vector<unsigned long long> cnt(kCounters);
-        e = hipMemsetAsync(d_cnt, 0, kCounters * sizeof(unsigned long long), s);
+    hipError_t e = hipMalloc(&d_cnt, kHistCounters * sizeof(unsigned long long));
+    if (e == hipSuccess && n) {
+        e = hipMemsetAsync(d_cnt, 0, kHistCounters * sizeof(unsigned long long), s);
         if (e == hipSuccess) e = (hipError_t)bsk_hist((const uint16_t*)d_bf16, n, d_cnt, d_cnt + 256 * 128, stream);
-        if (e == hipSuccess) e = hipMemcpyAsync(cnt.data(), d_cnt, kCounters * 8, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipMemcpyAsync(cnt.data(), d_cnt, kHistCounters * 8, hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
-        if (e != hipSuccess) { hip_fail(e, "histogram"); goto done; }
-        // the (sign, exponent) counts: negatives counted directly, positives
-        // as the exponent's total minus its negatives
-        uint64_t ec[256];
-        for (uint32_t x = 0; x < 256; x++) {
-            uint64_t tot = 0;
-            for (uint32_t f = 0; f < 128; f++) tot += cnt[x * 128 + f];
-            const uint64_t neg = cnt[256 * 128 + x];
-            if (neg > tot) { set_error("histogram counts are inconsistent"); rc = BS_E_HIP; goto done; }
-            t->counts_s[256 + x] = neg;
-            t->counts_s[x] = tot - neg;
-            ec[x] = tot;
-        }
-        cand = candidates(ec);
-        merged.resize(cand.size());
-        for (uint32_t c = 0; c < cand.size(); c++)
-            for (uint32_t f = 0; f < 128; f++) merged[c][f] = cnt[cand[c] * 128 + f];
-        for (uint32_t x = 0; x < 256; x++)
-            for (uint32_t f = 0; f < 128; f++) hc[x][f >> 4] += cnt[x * 128 + f];
     }
-    if (!finish_model(*t, p, cand, merged, hc)) rc = BS_E_INVAL;
-done:
+    if (e != hipSuccess) {
+        set_error("histogram: %s", hipGetErrorString(e));
+        rc = BS_E_HIP;
+    } else {
+        rc = model_from_counts(*t, p, n, cnt.data(), merged.data());
+    }
     if (d_cnt) (void)hipFree(d_cnt);
     if (rc != BS_OK) { delete t; return rc; }
     *out = t;

@@ -24,7 +24,15 @@ struct Model {
 };
 
 bool params_ok(const bs_params* p);
+// counters of the device histogram (hist kernel): 256 x 128 sign-merged
+// (exponent, fraction) counts, then 256 negative counts per exponent
+constexpr size_t kHistCounters = 256 * 128 + 256;
+bs_status model_from_counts(Model& md, const bs_params* p, uint64_t n, const unsigned long long* cnt,
+                            std::array<uint64_t, 128>* merged);
 bool quantise(const uint64_t* counts, uint32_t A, uint32_t M, uint32_t* q);
 const char* last_error();
 
 }  // namespace bs
+
+// the public opaque type of bs.h
+struct bs_tables : bs::Model {};

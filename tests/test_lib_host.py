@@ -4,6 +4,7 @@ The library's encoder, model building, container validation and sha256 are
 host C++ written independently of the oracle; the container is a
 deterministic encoding, so the two must agree byte for byte.
 """
+import ctypes as C
 import hashlib
 import os
 import re
@@ -393,3 +394,20 @@ def test_layout2_is_the_library_default():
     p = L.Params()
     L.lib().bs_params_default(ctypes.byref(p))
     assert (p.layout, p.m_s, p.m_f, p.max_tables, p.lanes, p.chunk_weights) == (2, 11, 5, 31, 128, 65536)
+
+
+def test_noalloc_tables_refuses_bad_arguments_on_the_host():
+    """bs_build_tables_noalloc checks its arguments before any device work
+    (so this runs without a GPU): NULL tables, NULL words, and more words than
+    its maximum are refused with BS_E_INVAL and a message."""
+    p = codec.params2()
+    into = codec.build_tables_host(np.zeros(0, np.uint16), p)
+    fake = C.c_void_p(1 << 20)   # never dereferenced: every call below is refused first
+    lib = L.lib()
+    assert lib.bs_build_tables_noalloc(fake, 8, C.byref(p), None, None) == L.BS_E_INVAL
+    assert lib.bs_build_tables_noalloc(None, 8, C.byref(p), None, into.handle) == L.BS_E_INVAL
+    assert lib.bs_build_tables_noalloc(fake, L.NOALLOC_MAX_WEIGHTS + 1, C.byref(p), None, into.handle) == L.BS_E_INVAL
+    assert b"maximum" in lib.bs_last_error()
+    bad = codec.params2()
+    bad.m_s = 13
+    assert lib.bs_build_tables_noalloc(fake, 8, C.byref(bad), None, into.handle) == L.BS_E_INVAL
