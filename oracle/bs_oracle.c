@@ -39,7 +39,9 @@
  *     renormalisation check: the two steps consume at most 16 bits of the
  *     state, so one 16-bit word always restores it.  The low four bits
  *     l = f & 15 are stored verbatim in a fixed-width plane of the chunk.
- *     The fraction's distribution given s is thus P(h | s) * 2^-4.
+ *     The fraction's distribution given s is thus P(h | s) * 2^-4.  An
+ *     exponent without a coded h table of its own shares the table (flat or
+ *     coded) that codes its h counts in the fewest bits (bso_share_hroutes).
  *
  * Parity pins live in tests/test_oracle_*.py (hand-computed coder states,
  * a bit-stack reduction, brute force, normaliser invariants, round trips).
@@ -819,6 +821,52 @@ static uint32_t get_bits(const uint8_t* b, uint64_t off, uint32_t len) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* Layout 2: shared routing (container rule, integer only).                  */
+/* [NVLC card, codec paragraph: the fraction distribution is routed from the */
+/*  decoded symbol; the route byte may name any of the record's tables]      */
+/* After the coded tables are chosen, each occupied exponent e that did not  */
+/* get a table of its own (route 0) is routed to the table t -- the flat     */
+/* table 0 or a coded table 1..n_tables -- that codes its merged h counts    */
+/* m_e[h] in the fewest bits, counted in units of 2^-16 bit:                 */
+/*   cost_t(e) = sum over h with m_e[h] > 0 of m_e[h] (65536 M_h - L(q_t[h])) */
+/* with L(q) = floor(65536 log2 q).  A table with q_t[h] = 0 for an h that  */
+/* e uses cannot code e.  The lowest cost wins, the lower id on ties (so    */
+/* the flat table keeps e unless a coded table is strictly cheaper).  Both  */
+/* signs of e follow: route[s] for the occupied s of exponent e.             */
+/* qh holds the coded tables only: qh[(t-1)*8 + h] for t = 1..n_tables.     */
+/* ------------------------------------------------------------------------ */
+int bso_share_hroutes(const uint64_t* cs, const uint64_t* cf, uint32_t M_h, uint32_t n_tables, const uint32_t* qh,
+                      uint32_t* route /*512*/) {
+    if (M_h < 4 || M_h > 5 || n_tables > BSO_MAX_HTABLES) return BSO_EINVAL;
+    for (uint32_t e = 0; e < 256; e++) {
+        if (cs[e] + cs[256 + e] == 0) continue;
+        if ((cs[e] && route[e]) || (cs[256 + e] && route[256 + e])) continue;   /* has its own table */
+        uint64_t m[8];
+        for (uint32_t h = 0; h < 8; h++) {
+            m[h] = 0;
+            for (uint32_t f = 16 * h; f < 16 * h + 16; f++) m[h] += cf[e * 128 + f] + cf[(256 + e) * 128 + f];
+        }
+        uint32_t best = 0;
+        unsigned __int128 best_cost = 0;
+        for (uint32_t t = 0; t <= n_tables; t++) {
+            unsigned __int128 cost = 0;
+            int usable = 1;
+            for (uint32_t h = 0; h < 8; h++) {
+                if (m[h] == 0) continue;
+                uint32_t q = t == 0 ? (1u << (M_h - 3)) : qh[(t - 1) * 8 + h];
+                if (q == 0) { usable = 0; break; }
+                cost += (unsigned __int128)m[h] * (65536u * M_h - bso_log2_q16(q));
+            }
+            if (!usable) continue;
+            if (t == 0 || cost < best_cost) { best = t; best_cost = cost; }
+        }
+        if (cs[e]) route[e] = best;
+        if (cs[256 + e]) route[256 + e] = best;
+    }
+    return BSO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Encode one BF16 record body.                                              */
 /* ------------------------------------------------------------------------ */
 static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32_t Kmax, uint32_t Pmax,
@@ -842,6 +890,7 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
         rc = bso_normalise(cs, 512, M_s, md->qs);
         if (!rc && layout == 1) rc = bso_select_tables(cs, cf, M_f, cmax, md->route, &md->n_tables, &md->qf[1][0]);
         if (!rc && layout == 2) rc = bso_select_htables(cs, cf, M_f, cmax, md->route, &md->n_tables, &md->qh[1][0]);
+        if (!rc && layout == 2) rc = bso_share_hroutes(cs, cf, M_f, md->n_tables, &md->qh[1][0], md->route);
         for (uint32_t s = 0; s < 512; s++) if (cs[s]) n_sym++;
     }
     if (layout == 1) for (uint32_t f = 0; f < 128; f++) md->qf[0][f] = 1u << (M_f - 7);

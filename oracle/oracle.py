@@ -84,6 +84,8 @@ def lib():
         l.bso_log2_q16.argtypes = [C.c_uint32]; l.bso_log2_q16.restype = C.c_uint32
         l.bso_select_htables.argtypes = [u64p, u64p, C.c_uint32, C.c_uint32, u32p, u32p, u32p]
         l.bso_select_htables.restype = C.c_int
+        l.bso_share_hroutes.argtypes = [u64p, u64p, C.c_uint32, C.c_uint32, u32p, u32p]
+        l.bso_share_hroutes.restype = C.c_int
         l.bso_decode_container.argtypes = [C.c_void_p, C.c_uint64, C.c_void_p, C.c_uint64, C.c_void_p]
         l.bso_decode_container.restype = C.c_int
         l.bso_free.argtypes = [C.c_void_p]; l.bso_free.restype = None
@@ -172,6 +174,20 @@ def select_htables(cs, cf, M_h: int = 5, cmax: int = 31):
     if rc:
         raise OracleError(rc, "select_htables")
     return route, int(nt[0]), qh.reshape(max(cmax, 1), 8)
+
+
+def share_hroutes(cs, cf, qh, route, M_h: int = 5):
+    """Layout-2 shared routing: route[] after every exponent without a table
+    of its own is sent to the cheapest of the flat and the coded tables qh
+    (n_tables rows of 8)."""
+    cs = np.ascontiguousarray(cs, np.uint64)
+    cf = np.ascontiguousarray(cf, np.uint64).reshape(-1)
+    qh = np.ascontiguousarray(qh, np.uint32).reshape(-1, 8)
+    r = np.ascontiguousarray(route, np.uint32).copy()
+    rc = lib().bso_share_hroutes(_u64p(cs), _u64p(cf), M_h, qh.shape[0], _u32p(qh.reshape(-1)), _u32p(r))
+    if rc:
+        raise OracleError(rc, "share_hroutes")
+    return r
 
 
 def record_shape(n: int, Wmax: int, Kmax: int):

@@ -74,7 +74,7 @@ MUTANTS = {
 
 # planted mistakes in layout 2 (one renormalisation per weight), checked
 # against the layout-2 pins only
-PINS2 = ["tests/test_oracle_layout2.py"]
+PINS2 = ["tests/test_oracle_layout2.py", "tests/test_oracle_shared_routing.py"]
 MUTANTS2 = {
     "split_pair_order_swapped": ("    code_step(x, th, h);\n    code_step(x, ts, s);", "    code_step(x, ts, s);\n    code_step(x, th, h);"),
     "split_flush_bound_s_only": ("uint64_t q = (uint64_t)ts->q[s] * th->q[h];", "uint64_t q = (uint64_t)ts->q[s] * (1u << th->M) / 8;"),
@@ -97,6 +97,17 @@ MUTANTS2 = {
                              "        id++;\n        id_of[e] = (id % 2) ? id + 1 : id - 1;\n        for (uint32_t h = 0; h < 8; h++) qh[(id - 1) * 8 + h] = qe[e][h];"),
     "log2_square_shift": ("        r = (r * r) >> 62;", "        r = (r * r) >> 61;"),
     "log2_bit_compare": ("if (r >= ((unsigned __int128)2 << 62)) { bits |= 1; r >>= 1; }", "if (r > ((unsigned __int128)3 << 61)) { bits |= 1; r >>= 1; }"),
+    "share_not_applied": ("        if (!rc && layout == 2) rc = bso_share_hroutes(cs, cf, M_f, md->n_tables, &md->qh[1][0], md->route);\n", ""),
+    "share_tie_high": ("if (t == 0 || cost < best_cost) { best = t; best_cost = cost; }",
+                       "if (t == 0 || cost <= best_cost) { best = t; best_cost = cost; }"),
+    "share_zero_q_usable": ("if (q == 0) { usable = 0; break; }", "if (q == 0) { usable = 1; }"),
+    "share_one_sign": ("        if (cs[256 + e]) route[256 + e] = best;\n", ""),
+    "share_selected_too": ("if ((cs[e] && route[e]) || (cs[256 + e] && route[256 + e])) continue;   /* has its own table */",
+                           "if (0) continue;"),
+    "share_flat_value": ("uint32_t q = t == 0 ? (1u << (M_h - 3)) : qh[(t - 1) * 8 + h];",
+                         "uint32_t q = t == 0 ? (1u << (M_h - 2)) : qh[(t - 1) * 8 + h];"),
+    "share_positive_counts": ("for (uint32_t f = 16 * h; f < 16 * h + 16; f++) m[h] += cf[e * 128 + f] + cf[(256 + e) * 128 + f];\n        }\n        uint32_t best = 0;",
+                              "for (uint32_t f = 16 * h; f < 16 * h + 16; f++) m[h] += cf[e * 128 + f];\n        }\n        uint32_t best = 0;"),
     "version2_accepts_layout0": ("else { if (lw != 1 && lw != 2) return BSO_EFORMAT; md->layout = lw; }",
                                  "else { if (lw > 2) return BSO_EFORMAT; md->layout = lw ? lw : 1; }"),
 }
