@@ -74,7 +74,12 @@
  * an exponent (both signs share it) when quantising its h counts saves more
  * than 64 bits against the flat table, counted with floor(65536 log2 q);
  * at most max_tables of them, the largest savings first (lower exponent on
- * ties), ids in ascending exponent order.
+ * ties), ids in ascending exponent order.  Every other occupied exponent is
+ * routed to the table, flat or coded, that codes its h counts in the fewest
+ * bits (sum of m[h] (65536 M_h - floor(65536 log2 q[h])); a table with q = 0
+ * for a used h is excluded; the lower id wins ties), so tables are shared
+ * between contexts [NVLC card, codec paragraph: "soft-routed fraction
+ * distribution", read as a route to a shared table].
  *
  * Conventions:
  *   - Every function returns a bs_status (0 = BS_OK); none throws or aborts.

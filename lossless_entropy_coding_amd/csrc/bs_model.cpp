@@ -184,6 +184,30 @@ void choose_htables(const std::array<std::array<uint64_t, 8>, 256>& hc, uint32_t
         id[ok[t].e] = t + 1;
         md.q_h[t] = ok[t].q;
     }
+    // Shared routing: an exponent without a table of its own goes to the
+    // table (flat or coded) that codes its h counts in the fewest 2^-16 bits,
+    // sum of m[h] (65536 M_h - floor(65536 log2 q_t[h])); a table with q = 0
+    // for a used h cannot take it; the lower id wins ties, so flat stays
+    // unless a coded table is strictly cheaper.
+    for (uint32_t e = 0; e < 256; e++) {
+        uint64_t n_e = 0;
+        for (uint32_t h = 0; h < 8; h++) n_e += hc[e][h];
+        if (!n_e || id[e]) continue;
+        uint32_t best = 0;
+        unsigned __int128 best_cost = 0;
+        for (uint32_t t = 0; t <= n_ok; t++) {
+            unsigned __int128 cost = 0;
+            bool usable = true;
+            for (uint32_t h = 0; h < 8 && usable; h++) {
+                if (!hc[e][h]) continue;
+                const uint32_t q = t == 0 ? 1u << (m_h - 3) : md.q_h[t - 1][h];
+                if (!q) { usable = false; break; }
+                cost += (unsigned __int128)hc[e][h] * (65536u * m_h - log2_q16(q));
+            }
+            if (usable && (t == 0 || cost < best_cost)) { best = t; best_cost = cost; }
+        }
+        id[e] = best;
+    }
     for (uint32_t s = 0; s < 512; s++) md.route[s] = md.counts_s[s] ? id[s & 255] : 0;
 }
 

@@ -232,3 +232,37 @@ def test_layout2_record_with_512_lane_streams_is_refused():
     with pytest.raises(L.BSError) as e:
         codec.Plan(c)
     assert e.value.rc == L.BS_E_INVAL
+
+
+def test_layout2_shared_routes():
+    """Shared routing: exponents without a table of their own routed to a
+    coded table (the route byte names it), decoded on the GPU bit for bit;
+    the GPU encoder's container equals the host's with the same routes."""
+    say("layout 2, shared routes")
+    rng = np.random.default_rng(21)
+    words = []
+    # exponent 120 earns a table; 100 and 99 (rare, h mostly 0 or 7) share it;
+    # 101 uses an h that table has no room for and stays flat
+    for e, hs, n in ((120, [0] * 90 + [7] * 7, 200000), (100, [0, 0, 0, 7], 12), (99, [0, 7, 7], 9),
+                     (101, [0, 1], 10), (121, list(range(8)), 50000)):
+        for _ in range(n):
+            h = hs[int(rng.integers(len(hs)))]
+            words.append((int(rng.integers(2)) << 15) | (e << 7) | (h << 4) | int(rng.integers(16)))
+    w = np.array(words, np.uint16)
+    rng.shuffle(w)
+    t = codec.build_tables_host(w, codec.params2()).get()
+    assert t["n_tables"] == 1 and t["route"][120] == 1
+    assert t["route"][100] == 1 and t["route"][99] == 1 and t["route"][101] == 0 and t["route"][121] == 0
+    cs, cf = O.histogram(w)
+    route, nt, qh = O.select_htables(cs, cf, 5, 31)
+    assert route[100] == 0 and route[99] == 0            # no table of their own: routed by sharing
+    c = _encode_both([O.bf16(w)], [codec.bf16(w)], 65536, 128, 128)
+    plan = codec.Plan(c)
+    out = plan.decode()
+    torch.cuda.synchronize()
+    assert out[: 2 * w.size].cpu().numpy().view(np.uint16).tolist() == w.tolist()
+    assert out[: 2 * w.size].cpu().numpy().tobytes() == _oracle_bytes(c)[: 2 * w.size]
+    rc, rep = plan.verify(out, flags=L.VERIFY_STATUS | L.VERIFY_SHA256)
+    assert rc == L.BS_OK, rep
+    dev = codec.encode_device([("bf16", torch.from_numpy(w.view(np.int16)).cuda())], codec.params2(lanes=128, stream_lanes=128))
+    assert dev.cpu().numpy().tobytes() == c

@@ -355,6 +355,7 @@ def test_layout2_models_match_oracle():
             cs, cf = O.histogram(w)
             assert t["layout"] == 2 and (t["q_s"] == O.normalise(cs, M_s)).all()
             route, nt, qh = O.select_htables(cs, cf, 16 - M_s, cmax)
+            route = O.share_hroutes(cs, cf, qh[:nt], route, 16 - M_s)
             assert nt == t["n_tables"] and (route == t["route"]).all() and (qh[:nt] == t["q_h"]).all()
 
 
