@@ -47,10 +47,16 @@ def host_threads() -> int:
 class CheckpointJob:
     """One Plan per layer container; decode() decodes every layer in order."""
 
-    def __init__(self, layers: int = 84, chunk_weights: int = 65536, lanes: int = 512, log=print,
-                 device: str = "cuda", m_s: int | None = None, m_f: int | None = None, stream_lanes: int = 256,
-                 layout: int = 2):
+    def __init__(self, layers: int = 84, chunk_weights: int = 65536, lanes: int | None = None, log=print,
+                 device: str = "cuda", m_s: int | None = None, m_f: int | None = None,
+                 stream_lanes: int | None = None, layout: int = 2):
         tensors = synth.cfg5_layout(layers=layers)
+        # chunk shape: K = 256 lanes in streams of 128 for layout 2 (as fast as
+        # 512 lanes here, at 0.2% less size); 512 in streams of 256 for layout 1
+        if lanes is None:
+            lanes = 256 if layout == 2 else 512
+        if stream_lanes is None:
+            stream_lanes = 128 if layout == 2 else 256
         self.name = "cfg5_checkpoint_%dlayers_%dtensors" % (layers, len(tensors))
         self.chunk_weights, self.lanes, self.stream_lanes = chunk_weights, lanes, stream_lanes or lanes
         # record layout 2 codes the fraction's high three bits at M_h = 16 - M_s
