@@ -27,7 +27,7 @@ using namespace bsd;
 namespace {
 
 // LDS of a workgroup (bytes): the record's table image as built (s table
-// of 2^M_s 16-byte entries at 0, then its 2 KiB h pages, each indexed by the
+// of 2^M_s 8-byte entries at 0, then its 2 KiB h pages, each indexed by the
 // state's low 8 bits), then one stream ring per wave.  The image's size
 // depends on M_s and the number of h tables, so the rings start at a
 // per-record offset and the launch takes as many waves as fit.
@@ -36,12 +36,19 @@ struct Model2 {
     uint32_t smask;    // 2^M_s - 1
 };
 
-__device__ __forceinline__ uint4 s_entry(const uint8_t* lds, uint32_t x, const Model2& md) {
-    return *(const uint4*)(lds + ((x & md.smask) << 4));
+// s entry {A = q_s | P << 24, B = s | (slot - cum_s) << 16}
+__device__ __forceinline__ uint2 s_entry(const uint8_t* lds, uint32_t x, const Model2& md) {
+    return *(const uint2*)(lds + ((x & md.smask) << 3));
 }
 
-__device__ __forceinline__ uint2 h_entry(const uint8_t* lds, uint32_t page, uint32_t x) {
-    return *(const uint2*)(lds + page + ((x & 255u) << 3));
+// the s step: q_s (x >> M_s) + slot - cum_s
+__device__ __forceinline__ uint32_t s_step(uint32_t x, uint2 e, const Model2& md) {
+    return __umul24(x >> md.m_s, e.x) + (e.y >> 16);
+}
+
+// the h entry of state x (after the s step) in the page that e names
+__device__ __forceinline__ uint2 h_entry(const uint8_t* lds, uint2 e, uint32_t x) {
+    return *(const uint2*)(lds + (((e.x >> 16) + (x & 255u)) << 3));
 }
 
 // the h step on the state after the s step: q_h (x >> M_h) + slot - cum_h,
@@ -58,20 +65,20 @@ __device__ __forceinline__ void group_pairs(uint32_t (&x)[R], uint32_t (&o)[R][4
 #pragma unroll
     for (int p = 0; p < 8; p++) {
         if (p % top_up_every(R, false) == 0) ring_top_up(g, pos);
-        uint4 e[R];
+        uint2 e[R];
 #pragma unroll
         for (int q = 0; q < R; q++) e[q] = s_entry(lds, x[q], md);
 #pragma unroll
-        for (int q = 0; q < R; q++) x[q] = __umul24(x[q] >> md.m_s, e[q].x) + e[q].y;
+        for (int q = 0; q < R; q++) x[q] = s_step(x[q], e[q], md);
         uint2 f[R];
 #pragma unroll
-        for (int q = 0; q < R; q++) f[q] = h_entry(lds, e[q].z, x[q]);
+        for (int q = 0; q < R; q++) f[q] = h_entry(lds, e[q], x[q]);
         uint32_t w[R];
 #pragma unroll
         for (int q = 0; q < R; q++) {
             x[q] = h_step(x[q], f[q]);
-            // (s << 7) | (f.x >> 25), and f.x >> 25 = h << 4
-            w[q] = __builtin_amdgcn_alignbit(e[q].w, f[q].x, 25);
+            // low half: (s << 7) | (f.x >> 25), and f.x >> 25 = h << 4
+            w[q] = __builtin_amdgcn_alignbit(e[q].y, f[q].x, 25);
         }
         refill_all<R, RW>(x, all_on, g, pos);
 #pragma unroll
@@ -157,15 +164,15 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
 #pragma unroll
         for (int p = 0; p < 8; p++) {
             if (p % top_up_every(R, false) == 0) ring_top_up(g, pos);
-            uint4 e[R];
+            uint2 e[R];
 #pragma unroll
             for (int q = 0; q < R; q++) e[q] = s_entry(lds, x[q], md);
 #pragma unroll
-            for (int q = 0; q < R; q++) x[q] = __umul24(x[q] >> md.m_s, e[q].x) + e[q].y;
+            for (int q = 0; q < R; q++) x[q] = s_step(x[q], e[q], md);
             refill_all<R, RW>(x, all_on, g, pos);
 #pragma unroll
             for (int q = 0; q < R; q++) {
-                const uint32_t w = e[q].w << 7;
+                const uint32_t w = e[q].y << 7;   // low half s << 7
                 if (p & 1) o[q][p >> 1] = __builtin_amdgcn_perm(w, o[q][p >> 1], 0x05040100u);
                 else o[q][p >> 1] = w;
             }
@@ -221,12 +228,12 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
             for (int q = 0; q < R; q++) {
                 act[q] = p < cnt[q];
                 uint32_t xs = x[q];
-                const uint4 e = s_entry(lds, xs, md);
-                xs = __umul24(xs >> md.m_s, e.x) + e.y;
+                const uint2 e = s_entry(lds, xs, md);
+                xs = s_step(xs, e, md);
                 uint32_t xh = xs;
-                const uint2 f = h_entry(lds, e.z, xh);
+                const uint2 f = h_entry(lds, e, xh);
                 xh = h_step(xh, f);
-                const uint32_t w = fin[q] ? e.w << 7 : __builtin_amdgcn_alignbit(e.w, f.x, 25);
+                const uint32_t w = fin[q] ? e.y << 7 : __builtin_amdgcn_alignbit(e.y, f.x, 25);
                 if (act[q]) x[q] = fin[q] ? xs : xh;
                 // shift the 128-bit register right by 16 and insert w on top
                 o[q][0] = __builtin_amdgcn_alignbit(o[q][1], o[q][0], 16);

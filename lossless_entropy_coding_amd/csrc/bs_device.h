@@ -44,9 +44,11 @@ static_assert(lut_lds(false) + 8 * ring_bytes(8, false) + 8 <= 163840, "full lay
 
 // Layout 2 lookup-table image of one record (built once per plan), copied
 // as it is to the start of the workgroup's LDS:
-//   s part at 0: 2^M_s x 16 B {q_s, slot - cum_s, LDS address of the h page
-//     of route[s], s}
-//   h part at 16 * 2^M_s: (n_tables + 1) pages of 2 KiB (page 0 flat).  A
+//   s part at 0: 2^M_s x 8 B {A, B}, A = q_s | P << 24 with P the LDS
+//     address of the h page of route[s] divided by 2048, B = s | (slot -
+//     cum_s) << 16 (s below bit 9, so the output word s << 7 | h << 4 comes
+//     from one funnel shift of B and the h entry)
+//   h part at 8 * 2^M_s: (n_tables + 1) pages of 2 KiB (page 0 flat).  A
 //     page is indexed by the low 8 bits i of the state after the s step (not
 //     by the M_h-bit slot alone): entry i = {q_h << (8 - M_h) | h << 29,
 //     q_h * (i >> M_h) + (i mod 2^M_h) - cum_h} for the h whose interval holds
@@ -55,14 +57,16 @@ static_assert(lut_lds(false) + 8 * ring_bytes(8, false) + 8 <= 163840, "full lay
 //     24-bit multiply (x >> 8 < 2^24, q_h << (8 - M_h) <= 256), while x >> M_h
 //     itself can need 27 bits: the state is not renormalised between s and h.
 //   the waves' stream rings after the h part.
+// The h entry of state x after the s step sits at LDS address
+// ((A >> 16) + (x mod 256)) * 8.
 constexpr uint32_t kHPageBytes = 2048;
 constexpr uint32_t kLds2 = 163840 - 16;    // a layout-2 workgroup's LDS (the rest: two words of record lookup)
-constexpr uint32_t l2_ring_base(uint32_t m_s, uint32_t n_tables) { return (16u << m_s) + (n_tables + 1) * kHPageBytes; }
+constexpr uint32_t l2_ring_base(uint32_t m_s, uint32_t n_tables) { return (8u << m_s) + (n_tables + 1) * kHPageBytes; }
 // waves of a layout-2 workgroup whose records' rings start at `ring_base` at most
 constexpr uint32_t l2_max_waves(uint32_t ring_base) {
     return ring_base >= kLds2 ? 0u : ((kLds2 - ring_base) / ring_bytes(4, false) < kMaxWaves ? (kLds2 - ring_base) / ring_bytes(4, false) : kMaxWaves);
 }
-static_assert(l2_max_waves(l2_ring_base(12, kMaxHTablesDev)) >= 7 && l2_max_waves(l2_ring_base(11, 29)) == 16,
+static_assert(l2_max_waves(l2_ring_base(12, kMaxHTablesDev)) == 15 && l2_max_waves(l2_ring_base(11, kMaxHTablesDev)) == 16,
               "layout-2 workgroup sizes");
 
 // Device lookup-table image of one record (built once per plan):

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void lut_kernel(const uint8_t* __restrict__ c,
     }
     const uint32_t nt = r.n_tables + 1;
     if (r.layout == 2) {
-        // layout 2 (the image layout is described with kHPageBytes): 16-byte s
+        // layout 2 (the image layout is described with kHPageBytes): 8-byte s
         // entries, then 2 KiB h pages indexed by 8 state bits; page 0 is
         // flat (q_h = 2^(M_h - 3))
         __shared__ uint32_t qh[kMaxHTablesDev + 1][8], cumh[kMaxHTablesDev + 1][8];
@@ -127,13 +127,14 @@ __global__ __launch_bounds__(256) void lut_kernel(const uint8_t* __restrict__ c,
             for (int h = 0; h < 8; h++) { cumh[t][h] = a; a += qh[t][h]; }
         }
         __syncthreads();
-        uint4* so = (uint4*)(luts + r.lut_off);
+        uint2* so = (uint2*)(luts + r.lut_off);
         const uint32_t ns = 1u << r.m_s;
         for (uint32_t slot = threadIdx.x; slot < ns; slot += blockDim.x) {
             const uint32_t s = last_le(cums, 512, slot);
-            so[slot] = make_uint4(qs[s], slot - cums[s], 16u * ns + route[s] * kHPageBytes, s);
+            const uint32_t page = (8u * ns + route[s] * kHPageBytes) / 2048;
+            so[slot] = make_uint2(qs[s] | page << 24, s | (slot - cums[s]) << 16);
         }
-        uint2* ho = (uint2*)(luts + r.lut_off + 16ull * ns);
+        uint2* ho = (uint2*)(luts + r.lut_off + 8ull * ns);
         const uint32_t hmask = (1u << r.m_f) - 1;
         for (uint32_t i = threadIdx.x; i < nt * 256; i += blockDim.x) {
             const uint32_t t = i / 256, b = i % 256, slot = b & hmask;
