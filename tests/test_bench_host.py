@@ -63,3 +63,11 @@ def test_copy_calibration_scales():
     # a plain copy reads back half its bytes in FETCH_SIZE and all of them in WRITE_SIZE
     assert rec["fetch_scale"] == pytest.approx(2.0, abs=0.01)
     assert rec["write_scale"] == pytest.approx(1.0, abs=0.01)
+
+
+def test_default_workload_has_a_traffic_record():
+    """The default bench line (the 84-layer checkpoint in layout 2, 256 lanes
+    per chunk in streams of 128) reports a measured traffic figure."""
+    from lossless_entropy_coding_amd import synth
+    key = f"cfg5_checkpoint_84layers_{len(synth.cfg5_layout(layers=84))}tensors|W=65536|K=256|P=128|L=2"
+    assert bench.measured_traffic(key, "decode2_kernel") is not None, key
