@@ -46,9 +46,14 @@ __device__ __forceinline__ uint32_t s_step(uint32_t x, uint2 e, const Model2& md
     return __umul24(x >> md.m_s, e.x) + (e.y >> 16);
 }
 
-// the h entry of state x (after the s step) in the page that e names
+// the h entry of state x (after the s step) in the page that e names: index
+// (A >> 16) + (x mod 256), taken in one add whose operand selects pick the
+// high half of A and the low byte of x (an ALU instruction only)
 __device__ __forceinline__ uint2 h_entry(const uint8_t* lds, uint2 e, uint32_t x) {
-    return *(const uint2*)(lds + (((e.x >> 16) + (x & 255u)) << 3));
+    uint32_t i;
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 src1_sel:BYTE_0"
+        : "=v"(i) : "v"(e.x), "v"(x));
+    return *(const uint2*)(lds + (i << 3));
 }
 
 // the h step on the state after the s step: q_h (x >> M_h) + slot - cum_h,
