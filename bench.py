@@ -243,7 +243,7 @@ def gemv_bench(a):
     from lossless_entropy_coding_amd import workloads
     enc = workloads.encode_config(a.config, device="cpu", keep_reference=False, keep_device_reference=True,
                                   lanes=a.lanes, chunk_weights=a.chunk_weights, stream_lanes=a.stream_lanes,
-                                  m_s=a.m_s, m_f=a.m_f)
+                                  m_s=a.m_s, m_f=a.m_f, layout=a.layout)
     assert a.config == "2", "the fused product is timed on the 4096x4096 workload"
     rows = cols = 4096
     job = workloads.DecodeJob(enc)
@@ -288,7 +288,7 @@ def gemv_bench(a):
             "plain_GB_s_of_bf16_weights": round(2 * rows * cols / t_plain / 1e3, 1),
             "max_rel_diff_vs_fp32_product": err, "steps": a.steps, "data": "synthetic",
             "config": {"workload": job.name, "lanes": job.lanes, "stream_lanes": job.stream_lanes,
-                       "chunk_weights": job.chunk_weights}}
+                       "chunk_weights": job.chunk_weights, "layout": job.layout}}
     print(json.dumps(line))
 
 

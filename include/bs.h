@@ -342,9 +342,10 @@ bs_status bs_decode_async(const bs_plan* plan, uint32_t first, uint32_t count, v
  * clears it first, then the products are added in fp32, in an order that
  * varies from run to run, so the result matches the exact sum within the
  * usual fp32 summation bound, not bit for bit).  d_status as for
- * bs_decode_async (only the record's entries are written).  Records in the
- * compact table layout or with more than 4 lanes per thread are rejected
- * (BS_E_INVAL).  Enqueued on `stream`; nothing is allocated. */
+ * bs_decode_async (only the record's entries are written).  Records of
+ * either layout are accepted; layout-1 records in the compact table layout
+ * or with more than 4 lanes per thread are rejected (BS_E_INVAL).  Enqueued
+ * on `stream`; nothing is allocated. */
 bs_status bs_gemv_async(const bs_plan* plan, uint32_t record, uint64_t rows, uint64_t cols, const void* d_x, float* d_y,
                         uint32_t* d_status, void* stream);
 

@@ -13,7 +13,9 @@
 // One wavefront decodes one word stream of a chunk, as in layout 1: lane
 // states in VGPRs, the record's tables in LDS, a per-wave LDS ring of stream
 // words, one refill per weight addressed by a wavefront prefix count, the
-// plane read one 32-bit word per lane and group, 128-bit output stores.
+// plane read one 32-bit word per lane and group, 128-bit output stores.  The
+// instances with V set are the fused matrix-vector product: each group of 8
+// decoded weights goes into a dot product with x instead of memory.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -111,7 +113,7 @@ __device__ __forceinline__ bool lane_bad(uint32_t x, bool has, uint32_t c) {
     return has ? ((x >> lead) != 1u || ((x - (1u << lead)) >> (3 * c)) != 0u) : x != kStateLow;
 }
 
-template <int R>
+template <int R, bool V>
 __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& r, const uint8_t* lds, Unit<R, false>& u,
                                              bool fair) {
     const uint32_t lane = threadIdx.x & 63;
@@ -123,6 +125,15 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
     const Model2 md{r.m_s, (1u << r.m_s) - 1};
     uint32_t pos = u.pos;
     uint8_t* out = a.out + (r.out_off - a.out_base) + 2ull * ch * r.W;
+    // the fused product: matrix position of the stream's first group
+    MatPos mpos{0, 0};
+    if (V) {
+        const uint64_t e = (uint64_t)ch * r.W + 8ull * LB;
+        const uint64_t row = e / a.gcols;
+        mpos.row = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(row >> 32)) << 32) |
+                   __builtin_amdgcn_readfirstlane((uint32_t)row);
+        mpos.col = __builtin_amdgcn_readfirstlane((uint32_t)(e - row * a.gcols));
+    }
 
     // the plane of low bits: one 32-bit word per group, group t K + l for
     // lane l at macro-step t; loads past its end return 0
@@ -156,9 +167,15 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
 #pragma unroll
         for (int q = 0; q < R; q++) {
             add_low_bits(o[q], d[q]);
-            v4o* op = (v4o*)out + (uint64_t)t * K + LB + 64 * q + lane;
-            __builtin_nontemporal_store(v4o{o[q][0], o[q][1], o[q][2], o[q][3]}, op);
+            if (!V) {
+                v4o* op = (v4o*)out + (uint64_t)t * K + LB + 64 * q + lane;
+                __builtin_nontemporal_store(v4o{o[q][0], o[q][1], o[q][2], o[q][3]}, op);
+            }
             d[q] = dn[q];
+        }
+        if (V) {
+            gemv_step<R>(a, o, nullptr, mpos, lane);
+            mpos.advance(8 * K, (uint32_t)a.gcols);
         }
     }
     if (whole) {
@@ -189,10 +206,13 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
             for (int k = 0; k < 4; k++)
                 o[q][k] |= ((x[q] >> (6 * k)) & 7u) << 4 | ((x[q] >> (6 * k + 3)) & 7u) << 20;
             add_low_bits(o[q], d[q]);
-            v4o* op = (v4o*)out + (uint64_t)T_main * K + LB + 64 * q + lane;
-            __builtin_nontemporal_store(v4o{o[q][0], o[q][1], o[q][2], o[q][3]}, op);
+            if (!V) {
+                v4o* op = (v4o*)out + (uint64_t)T_main * K + LB + 64 * q + lane;
+                __builtin_nontemporal_store(v4o{o[q][0], o[q][1], o[q][2], o[q][3]}, op);
+            }
             bad |= lane_bad(x[q], true, 8);
         }
+        if (V) gemv_step<R>(a, o, nullptr, mpos, lane);
         const uint64_t badm = __builtin_amdgcn_ballot_w64(bad);
         if (lane == 0) a.status[r.status_base + unit] = (badm ? 1u : 0u) | (pos - skip != nw ? 2u : 0u);
         return;
@@ -259,7 +279,9 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
             }
             add_low_bits(o[q], dt[q]);
             const uint64_t g16 = (uint64_t)t * K + LB + 64 * q + lane;
-            if (cnt[q] == 8) {
+            if (V) {
+                // below, after the R groups
+            } else if (cnt[q] == 8) {
                 __builtin_nontemporal_store(v4o{o[q][0], o[q][1], o[q][2], o[q][3]}, (v4o*)out + g16);
             } else if (cnt[q] > 0) {
                 uint16_t* o16 = (uint16_t*)out + 8 * g16;
@@ -267,6 +289,10 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
                 for (int k = 0; k < 8; k++)
                     if (k < cnt[q]) o16[k] = (uint16_t)(o[q][k >> 1] >> (16 * (k & 1)));
             }
+        }
+        if (V) {
+            gemv_step<R>(a, o, cnt, mpos, lane);
+            mpos.advance(8 * K, (uint32_t)a.gcols);
         }
     }
     bool bad = false;
@@ -282,7 +308,7 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
 // before a wave opens its first unit, so that the two overlap.
 constexpr int kStage2 = 8;
 
-template <int R>
+template <int R, bool V>
 __device__ __forceinline__ void run_units2(const DecodeArgs& a, const RecDev& r, uint32_t u0, uint32_t u1, uint32_t wave,
                                            uint8_t* lds) {
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -321,30 +347,31 @@ __device__ __forceinline__ void run_units2(const DecodeArgs& a, const RecDev& r,
     __syncthreads();
     for (; u < u1; u += a.waves) {
         if (u != u0 + wave) unit_open<R, false, true>(a, r, u, wave, lds, rb, un);
-        unit_decode2<R>(a, r, lds, un, u1 - u0 <= a.waves);
+        unit_decode2<R, V>(a, r, lds, un, u1 - u0 <= a.waves);
     }
 }
 
-template <int G>
+template <int G, bool V>
 __device__ __forceinline__ void run_record2(const DecodeArgs& a, const RecDev& r, uint32_t u0, uint32_t wave, uint8_t* lds) {
     const uint32_t u1 = min(r.n_chunks << r.streams_log2, u0 + a.run);
     if (G == 1 || G == 2 || G == 4) {
         constexpr int R = (G == 1 || G == 2 || G == 4) ? G : 1;
-        run_units2<R>(a, r, u0, u1, wave, lds);
+        run_units2<R, V>(a, r, u0, u1, wave, lds);
     } else if (r.lanes_per_thread == 1) {
-        run_units2<1>(a, r, u0, u1, wave, lds);
+        run_units2<1, V>(a, r, u0, u1, wave, lds);
     } else if (G == 0 || r.lanes_per_thread == 2) {
-        run_units2<2>(a, r, u0, u1, wave, lds);
+        run_units2<2, V>(a, r, u0, u1, wave, lds);
     } else {
-        run_units2<4>(a, r, u0, u1, wave, lds);
+        run_units2<4, V>(a, r, u0, u1, wave, lds);
     }
 }
 
 // Workgroup b decodes one run of units inside one record, as the layout-1
 // kernel does (record lookup by a prefix sum over the records' run counts
 // when the launch has several).  G: the lanes per thread of every record
-// (1, 2 or 4), 0 for a mix of 1 and 2, 3 for a mix that includes 4.
-template <int G>
+// (1, 2 or 4), 0 for a mix of 1 and 2, 3 for a mix that includes 4.  V:
+// the fused product (one record, G = 1, 2 or 4).
+template <int G, bool V = false>
 __global__ __launch_bounds__(1024) void decode2_kernel(const DecodeArgs a) {
     __shared__ __align__(16) uint8_t lds[kLds2];
     __shared__ uint32_t pick[2];
@@ -353,7 +380,7 @@ __global__ __launch_bounds__(1024) void decode2_kernel(const DecodeArgs a) {
     if (a.i1 - a.i0 == 1) {
         const uint32_t u0 = b * a.run;
         if (u0 >= (a.one.n_chunks << a.one.streams_log2)) return;
-        run_record2<G>(a, a.one, u0, wave, lds);
+        run_record2<G, V>(a, a.one, u0, wave, lds);
         return;
     }
     if (wave == 0) {
@@ -380,7 +407,7 @@ __global__ __launch_bounds__(1024) void decode2_kernel(const DecodeArgs a) {
     const uint32_t e = __builtin_amdgcn_readfirstlane(pick[0]);
     if (e == UINT32_MAX) return;
     const RecDev r = a.recs[a.cls.recs[e]];
-    run_record2<G>(a, r, __builtin_amdgcn_readfirstlane(pick[1]) * a.run, wave, lds);
+    run_record2<G, V>(a, r, __builtin_amdgcn_readfirstlane(pick[1]) * a.run, wave, lds);
 }
 
 }  // namespace
@@ -398,6 +425,24 @@ int bsk_decode2(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, voi
         case 1: hipLaunchKernelGGL((decode2_kernel<1>), grid, block, 0, st, *args); break;
         case 2: hipLaunchKernelGGL((decode2_kernel<2>), grid, block, 0, st, *args); break;
         case 4: hipLaunchKernelGGL((decode2_kernel<4>), grid, block, 0, st, *args); break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+int bsk_gemv2(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    if (rows) {
+        const int e = bsk_zero_f32(args->gy, rows, stream);
+        if (e) return e;
+    }
+    if (n_groups == 0) return (int)hipGetLastError();
+    const dim3 grid(n_groups), block(64 * args->waves);
+    if (args->waves == 0 || args->waves > 16) return (int)hipErrorInvalidValue;
+    switch (variant) {
+        case 1: hipLaunchKernelGGL((decode2_kernel<1, true>), grid, block, 0, st, *args); break;
+        case 2: hipLaunchKernelGGL((decode2_kernel<2, true>), grid, block, 0, st, *args); break;
+        case 4: hipLaunchKernelGGL((decode2_kernel<4, true>), grid, block, 0, st, *args); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();

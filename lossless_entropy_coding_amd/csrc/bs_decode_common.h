@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "bs_device.h"
+#include "bs_wave.h"
 
 namespace bsd {
 
@@ -243,6 +244,65 @@ __device__ __forceinline__ void unit_open(const DecodeArgs& a, const RecDev& r, 
     u.n_c = n_c;
     u.unit = unit;
     u.payload = payload;
+}
+
+// ------------------------------------------------------------------ fused product
+
+// The fused product's epilogue for one group of 8 weights per lane (cnt of
+// them present).  The wave's groups are 512 consecutive record elements from
+// (row0, c0), 8 per lane in lane order, so with gcols >= 512 they span at most
+// two matrix rows.  Each lane takes the dot product of its weights with the
+// matching x (packed BF16 pairs, v_dot2 with fp32 accumulation), the wave
+// sums the products per row (DPP steps, no LDS), and lane 0 adds the sums
+// into y.
+__device__ __forceinline__ void gemv_group(const DecodeArgs& a, const uint32_t (&o)[4], uint32_t cnt, uint64_t row0,
+                                           uint32_t c0, uint32_t lane) {
+    const uint32_t cols = (uint32_t)a.gcols;
+    const uint32_t c = c0 + 8 * lane;
+    const bool wrap = c >= cols;
+    const uint32_t col = wrap ? c - cols : c;
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u xv = *(const v4u*)(a.gx + col);
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        // weights 2k and 2k + 1 of the group, the upper one dropped when absent
+        const uint32_t w = 2 * k + 1 < (int)cnt ? o[k] : 2 * k < (int)cnt ? (o[k] & 0xFFFFu) : 0u;
+        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, xw[k]), sum,
+                                              false);
+    }
+    const float s0 = wave_sum_dpp(wrap ? 0.f : sum);
+    const float s1 = wave_sum_dpp(wrap ? sum : 0.f);
+    const uint64_t wrapped = __builtin_amdgcn_ballot_w64(wrap && cnt > 0);
+    const uint64_t here = __builtin_amdgcn_ballot_w64(!wrap && cnt > 0);
+    if (lane == 0) {
+        if (here) __hip_atomic_fetch_add(a.gy + row0, s0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (wrapped) __hip_atomic_fetch_add(a.gy + row0 + 1, s1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Matrix position (row, column) of a group start, advanced by whole groups
+// without dividing (uniform values, kept in scalar registers).
+struct MatPos {
+    uint64_t row;
+    uint32_t col;
+    __device__ __forceinline__ void advance(uint32_t by, uint32_t cols) {
+        col += by;
+        while (col >= cols) { col -= cols; row++; }
+    }
+};
+
+// the product of one group per lane group q of the macro-step that starts at p
+template <int R>
+__device__ __forceinline__ void gemv_step(const DecodeArgs& a, const uint32_t (&o)[R][4], const int32_t* cnt,
+                                          MatPos p, uint32_t lane) {
+    const uint32_t cols = (uint32_t)a.gcols;
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        gemv_group(a, o[q], cnt ? (uint32_t)cnt[q] : 8u, p.row, p.col, lane);
+        p.advance(512, cols);
+    }
 }
 
 }  // namespace bsd

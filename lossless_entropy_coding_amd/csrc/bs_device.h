@@ -150,6 +150,10 @@ int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant,
 int bsk_decode2(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream);
 // the fused matrix-vector product of one record (full layout, variant 1, 2 or 4), y zeroed first
 int bsk_gemv(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream);
+// the same for a layout-2 record
+int bsk_gemv2(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream);
+// fill n floats at y with 0 (a kernel, so that the work stays capturable)
+int bsk_zero_f32(float* y, uint64_t n, void* stream);
 int bsk_raw_copy(const uint8_t* d_container, const bsd::RawDev* d_raw, uint32_t n_raw, uint8_t* d_out,
                  uint64_t out_base, void* stream);
 int bsk_compare(const uint8_t* a, const uint8_t* b, uint64_t n, unsigned long long* d_result /*2*/, void* stream);

@@ -366,7 +366,6 @@ bs_status bs_gemv_async(const bs_plan* p, uint32_t record, uint64_t rows, uint64
     }
     if (((uintptr_t)d_x & 15) || ((uintptr_t)d_y & 3)) { set_error("x must be 16-byte aligned, y 4-byte aligned"); return BS_E_INVAL; }
     const int k = (int)p->rclass[record];
-    if (k == bs_plan::kLayout2) { set_error("record %u: the fused product reads layout-1 records", record); return BS_E_INVAL; }
     if (bs_plan::kCompact[k] || bs_plan::kMaxR[k] > 4) {
         set_error("the fused product runs on records in the full table layout with at most 4 lanes per thread");
         return BS_E_INVAL;
@@ -392,7 +391,8 @@ bs_status bs_gemv_async(const bs_plan* p, uint32_t record, uint64_t rows, uint64
     uint32_t groups;
     launch_shape(p, k, e, e + 1, a.waves, a.run, groups);
     if (p->cls_start[k][e + 1] == p->cls_start[k][e]) groups = 0;
-    const int err = bsk_gemv(&a, groups, p->cls_R[k][e], rows, stream);
+    const int err = k == bs_plan::kLayout2 ? bsk_gemv2(&a, groups, p->cls_R[k][e], rows, stream)
+                                           : bsk_gemv(&a, groups, p->cls_R[k][e], rows, stream);
     if (err) return hip_err((hipError_t)err, "fused product launch");
     return BS_OK;
 }

@@ -1,5 +1,5 @@
 """GPU: the fused decode and matrix-vector product against an fp64 product of
-the oracle's decode.
+the oracle's decode, on records of both layouts.
 
 The weights are decoded in registers and multiplied into y without being
 written out [Qwen3.8-27B-BF16-NVLC-Lossless card, runtime paragraphs: the
@@ -49,16 +49,20 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", [1, 2])
 @pytest.mark.parametrize("name,rows,cols,W,K,P", CASES, ids=[c[0] for c in CASES])
-def test_gemv_matches_fp64_product_of_oracle_decode(name, rows, cols, W, K, P):
-    say("gemv case", name, rows, cols, W, K, P)
+def test_gemv_matches_fp64_product_of_oracle_decode(name, rows, cols, W, K, P, layout):
+    say("gemv case", name, rows, cols, W, K, P, "layout", layout)
     rng = np.random.default_rng(rows * 7 + cols)
     w = rng.standard_normal(rows * cols) * 0.02
     w[rng.random(w.size) < 0.001] *= 50.0
     w[rng.random(w.size) < 0.01] = 0.0
     words = _bf16_words(w)
     xw = _bf16_words(rng.standard_normal(cols))
-    c = codec.encode([codec.bf16(words)], codec.params(chunk_weights=W, lanes=K, stream_lanes=P))
+    p = (codec.params2(chunk_weights=W, lanes=K, stream_lanes=P) if layout == 2
+         else codec.params(chunk_weights=W, lanes=K, stream_lanes=P))
+    c = codec.encode([codec.bf16(words)], p)
+    assert codec.record_info(c, 0).layout == layout
     out, st = O.decode(c)
     assert st == [0]
     W64 = _as_f64(np.frombuffer(out[: 2 * words.size], np.uint16)).reshape(rows, cols)
