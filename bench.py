@@ -51,7 +51,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: 20 for the checkpoint, 200 for the other workloads)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="5", choices=["1", "2", "3", "4", "5"])
+    ap.add_argument("--config", default=None, choices=["1", "2", "3", "4", "5"],
+                    help="workload (default: 5, the checkpoint; 2, the 4096x4096 matrix, with --gemv, and for the "
+                         "products in --fixed)")
     ap.add_argument("--cold", action="store_true", help="write and read back a 1 GiB buffer before each timed decode (not in the timing): cold, clean caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle baseline")
@@ -80,6 +82,8 @@ def parse():
     ap.add_argument("--stream-layers", type=int, default=12, help="--stream: layers of the checkpoint to build")
     ap.add_argument("--stream-slots", type=int, default=3, help="--stream: decoded layers the budget holds")
     a = ap.parse_args()
+    if a.config is None:
+        a.config = "2" if a.gemv else "5"
     if a.steps is None:
         a.steps = 20 if a.config == "5" and not (a.gemv or a.fixed or a.encode or a.stream) else 200
     return a
