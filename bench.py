@@ -121,15 +121,22 @@ def measured_traffic(key: str, kind: str = "decode_kernel"):
 
 def model_build_rate(job):
     """bs_build_tables (the HIP histogram pass + host quantisation) on the
-    workload's first BF16 tensor, already in HBM: wall time per call."""
+    workload's first BF16 tensor (the checkpoint: its first layer's largest),
+    already in HBM: wall time per call."""
     import torch
     from lossless_entropy_coding_amd import codec
-    if not hasattr(job, "ref") or not hasattr(job, "plan"):
-        return None
-    ri = codec.record_info(job.plan.host, 0) if job.plan.host is not None else None
-    if ri is None or ri.kind != 1 or ri.n == 0:
-        return None
-    words = job.ref[ri.out_offset: ri.out_offset + 2 * ri.n].view(torch.int16)
+    if getattr(job, "model_sample", None) is not None:
+        # the checkpoint: the first layer's largest tensor
+        words = job.model_sample.view(torch.int16).reshape(-1)
+        n = words.numel()
+    else:
+        if not hasattr(job, "ref") or not hasattr(job, "plan"):
+            return None
+        ri = codec.record_info(job.plan.host, 0) if job.plan.host is not None else None
+        if ri is None or ri.kind != 1 or ri.n == 0:
+            return None
+        words = job.ref[ri.out_offset: ri.out_offset + 2 * ri.n].view(torch.int16)
+        n = ri.n
     if getattr(job, "layout", 1) == 2:
         p = codec.params2(chunk_weights=job.chunk_weights, lanes=job.lanes, m_s=job.m_s, stream_lanes=job.stream_lanes)
     else:
@@ -142,7 +149,7 @@ def model_build_rate(job):
         t0 = time.perf_counter()
         codec.build_tables(words, p)
         best = min(best, time.perf_counter() - t0)
-    return {"weights": int(ri.n), "ms": round(best * 1e3, 3), "read_GB_s": round(2 * ri.n / best / 1e9, 1),
+    return {"weights": int(n), "ms": round(best * 1e3, 3), "read_GB_s": round(2 * n / best / 1e9, 1),
             "what": "bs_build_tables wall time: one HIP histogram pass, the counts read back, host quantisation"}
 
 
@@ -576,8 +583,11 @@ def encode_bench(a):
     import torch
     from lossless_entropy_coding_amd import codec, synth, workloads
     wl = workloads.CONFIG_BUILDERS[a.config]("cuda")
+    layout = a.layout or wl.layout
     p = codec.params(chunk_weights=a.chunk_weights or wl.chunk_weights, lanes=a.lanes or wl.lanes,
-                     stream_lanes=a.stream_lanes if a.stream_lanes is not None else wl.stream_lanes)
+                     stream_lanes=a.stream_lanes if a.stream_lanes is not None else wl.stream_lanes,
+                     m_s=11 if layout == 2 else 12, m_f=5 if layout == 2 else 10,
+                     max_tables=31 if layout == 2 else 6, layout=layout)
     dev, host, digests = [], [], []
     n_bf16 = 0
     for it in wl.items:
@@ -617,7 +627,7 @@ def encode_bench(a):
             "host_threads": os.cpu_count(), "speedup_vs_host": round(host_s / gs, 1),
             "identical_bytes": same, "container_bytes": len(hc),
             "config": {"workload": wl.name, "bf16_weights": n_bf16, "chunk_weights": p.chunk_weights, "lanes": p.lanes,
-                       "stream_lanes": p.stream_lanes}}
+                       "stream_lanes": p.stream_lanes, "layout": p.layout}}
     print(json.dumps(line))
 
 
@@ -636,8 +646,10 @@ def stream_bench(a):
     containers, refs = [], []
     t0 = time.time()
     for layer in range(a.stream_layers):
-        wl = synth.cfg5_layer(layer, device="cuda", chunk_weights=65536, lanes=512, layout=layout)
-        wl.stream_lanes = 256
+        # the checkpoint's chunk shape and record layout (layout 2: K 256 in
+        # streams of 128)
+        wl = synth.cfg5_layer(layer, device="cuda", chunk_weights=65536, lanes=256, layout=layout)
+        wl.stream_lanes, wl.layout, wl.m_s, wl.m_f = 128, 2, 11, 5
         enc = workloads.encode_workload(wl, device="cuda", keep_reference=False, keep_device_reference=True)
         containers.append(enc.container)
         refs.append(enc.reference_device)
@@ -709,7 +721,7 @@ def stream_bench(a):
                          "vram_budget": budget, "misses_per_pass": (after["misses"] - before["misses"]) // len(walls),
                          "hits_per_pass": (after["hits"] - before["hits"]) // len(walls)},
             "config": {"workload": f"cfg5_checkpoint_first_{len(containers)}_layers", "bf16_bytes": decoded,
-                       "container_bytes": compressed}}
+                       "container_bytes": compressed, "layout": 2}}
     print(json.dumps(line))
 
 

@@ -73,6 +73,7 @@ class CheckpointJob:
         else:
             self.kernel_name = "decode_kernel<%d, %s>" % (variant, "true" if m_s <= 11 and m_f <= 9 else "false")
         self.plans, self.refs = [], []
+        self.model_sample = None
         self.n_weights = self.raw_bytes = self.read_bytes = self.container_bytes = 0
         self.n_tensors = 0
         bits = ent = 0.0
@@ -80,12 +81,16 @@ class CheckpointJob:
             p = codec.params2(chunk_weights=chunk_weights, lanes=lanes, m_s=m_s, stream_lanes=stream_lanes)
         else:
             p = codec.params(chunk_weights=chunk_weights, lanes=lanes, m_s=m_s, m_f=m_f, stream_lanes=stream_lanes)
+        self.params = p
         pool = cf.ThreadPoolExecutor(max_workers=host_threads())
         t0 = time.time()
         out_max = 16
         for layer in range(layers + 1):
             wl = synth.cfg5_layer(layer, device=device, chunk_weights=chunk_weights, lanes=lanes, layout=tensors)
             words = [synth.as_words(it.tensor) for it in wl.items]
+            if layer == 0:
+                # the first layer's largest tensor, kept to time the model build
+                self.model_sample = max(words, key=lambda t: t.numel())
             digests = list(pool.map(_digest, words))
             dev = codec.encode_device([("bf16", w) for w in words], p, digests=digests)
             host = dev.cpu().numpy().tobytes()
