@@ -266,3 +266,55 @@ def test_layout2_shared_routes():
     assert rc == L.BS_OK, rep
     dev = codec.encode_device([("bf16", torch.from_numpy(w.view(np.int16)).cuda())], codec.params2(lanes=128, stream_lanes=128))
     assert dev.cpu().numpy().tobytes() == c
+
+
+def _words_31_tables(seed: int) -> np.ndarray:
+    """40 exponents of 6,000 weights each, each with a different dominant h:
+    more eligible h tables than the 31 a record may hold."""
+    rng = np.random.default_rng(seed)
+    parts = []
+    for k, e in enumerate(range(90, 130)):
+        p = np.full(8, 0.2 / 7)
+        p[k % 8] = 0.8
+        h = rng.choice(8, size=6000, p=p)
+        sign = rng.integers(0, 2, 6000)
+        parts.append((sign << 15) | (e << 7) | (h << 4) | rng.integers(0, 16, 6000))
+    w = np.concatenate(parts).astype(np.uint16)
+    rng.shuffle(w)
+    return w
+
+
+@pytest.mark.parametrize("ms,P", [(12, 256), (11, 256), (12, 128)])
+def test_layout2_largest_table_image(ms, P):
+    """31 coded h tables: the largest table image a record can have (with
+    M_s = 12, 96 KiB of LDS before the rings, so a workgroup runs fewer
+    waves), decoded bit for bit."""
+    say("layout 2, 31 h tables, m_s", ms, "stream lanes", P)
+    w = _words_31_tables(5)
+    c = _encode_both([O.bf16(w)], [codec.bf16(w)], 16384, 256, P, ms)
+    assert codec.record_info(c, 0).n_tables == 31
+    plan = codec.Plan(c)
+    for _ in range(2):
+        out = plan.decode()
+        rc, rep = plan.verify(out, flags=L.VERIFY_STATUS | L.VERIFY_SHA256)
+        assert rc == L.BS_OK, rep
+        assert out[: 2 * w.size].cpu().numpy().tobytes() == w.tobytes()
+
+
+@pytest.mark.parametrize("ms,waves", [(12, 15), (11, 16)])
+def test_layout2_largest_table_image_full_workgroups(ms, waves):
+    """The same tables over enough chunks (about 65M weights) that every
+    workgroup runs as many waves as fit after the table image: 15 with
+    M_s = 12 (96 KiB of tables), 16 with M_s = 11; compared with the original
+    words on the device and through the record digest."""
+    say("layout 2, 31 h tables, full workgroups, m_s", ms)
+    w = np.tile(_words_31_tables(5), 270)
+    c = codec.encode([codec.bf16(w)], codec.params2(chunk_weights=16384, lanes=256, stream_lanes=256, m_s=ms))
+    assert codec.record_info(c, 0).n_tables == 31
+    plan = codec.Plan(c)
+    assert plan.waves_per_block == waves
+    out = plan.decode()
+    rc, rep = plan.verify(out, flags=L.VERIFY_STATUS | L.VERIFY_SHA256)
+    assert rc == L.BS_OK, rep
+    ref = torch.from_numpy(w.view(np.int16)).cuda()
+    assert torch.equal(out[: 2 * w.size].view(torch.int16), ref)
