@@ -3,9 +3,11 @@
 Each case copies oracle/bs_oracle.c, changes one expression the way a
 plausible bug would (a dropped term, a wrong comparison, a reversed order),
 compiles the copy with gcc into a temporary directory and runs the quick pin
-tests against it in a child process.  The pins must fail for every mutant;
-the unmodified oracle must pass the same selection.
+tests against it in a child process (the cases run concurrently, each in its
+own process).  The pins must fail for every mutant; the unmodified oracle
+must pass the same selection.
 """
+import concurrent.futures as cf
 import os
 import subprocess
 import sys
@@ -121,41 +123,53 @@ def _run_pins(lib_path, pins=PINS):
     return r.returncode, r.stdout[-2000:]
 
 
-def _build(src_text, tmp_path, name):
-    c = tmp_path / f"{name}.c"
-    so = tmp_path / f"{name}.so"
-    c.write_text(src_text)
-    subprocess.check_call(["gcc", "-O1", "-std=gnu11", "-fPIC", "-shared", "-o", str(so), str(c)])
-    return str(so)
+def _run_one(job, base_dir):
+    """Build one oracle copy (name, source text) and run its pin selection."""
+    name, text, pins = job
+    d = os.path.join(base_dir, name)
+    os.makedirs(d, exist_ok=True)
+    c = os.path.join(d, f"{name}.c")
+    so = os.path.join(d, f"{name}.so")
+    with open(c, "w") as f:
+        f.write(text)
+    subprocess.check_call(["gcc", "-O1", "-std=gnu11", "-fPIC", "-shared", "-o", so, c])
+    return _run_pins(so, pins)
 
 
-def test_unmodified_oracle_passes_selection(tmp_path):
-    so = _build(open(SRC).read(), tmp_path, "clean")
-    rc, out = _run_pins(so)
+@pytest.fixture(scope="module")
+def outcomes(tmp_path_factory):
+    """Every planted mistake (and the unmodified oracle, once per pin set),
+    built and run concurrently: each case is an independent child process."""
+    base = str(tmp_path_factory.mktemp("mutants"))
+    src = open(SRC).read()
+    jobs = [("clean", src, PINS), ("clean2", src, PINS2)]
+    for table, pins, tag in ((MUTANTS, PINS, "m1"), (MUTANTS2, PINS2, "m2")):
+        for name, (old, new) in table.items():
+            assert src.count(old) >= 1, f"mutation anchor not found: {name}"
+            jobs.append((f"{tag}_{name}", src.replace(old, new, 1), pins))
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with cf.ThreadPoolExecutor(max_workers=workers) as pool:
+        results = list(pool.map(lambda j: _run_one(j, base), jobs))
+    return {j[0]: r for j, r in zip(jobs, results)}
+
+
+def test_unmodified_oracle_passes_selection(outcomes):
+    rc, out = outcomes["clean"]
     assert rc == 0, out
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_mutant_is_caught(name, tmp_path):
-    old, new = MUTANTS[name]
-    text = open(SRC).read()
-    assert text.count(old) >= 1, f"mutation anchor not found: {name}"
-    so = _build(text.replace(old, new, 1), tmp_path, name)
-    rc, out = _run_pins(so)
+def test_mutant_is_caught(name, outcomes):
+    rc, out = outcomes[f"m1_{name}"]
     assert rc != 0, f"planted mistake {name} was not caught:\n{out}"
 
 
-def test_unmodified_oracle_passes_layout2_selection(tmp_path):
-    so = _build(open(SRC).read(), tmp_path, "clean2")
-    rc, out = _run_pins(so, PINS2)
+def test_unmodified_oracle_passes_layout2_selection(outcomes):
+    rc, out = outcomes["clean2"]
     assert rc == 0, out
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS2))
-def test_layout2_mutant_is_caught(name, tmp_path):
-    old, new = MUTANTS2[name]
-    text = open(SRC).read()
-    assert text.count(old) >= 1, f"mutation anchor not found: {name}"
-    so = _build(text.replace(old, new, 1), tmp_path, name)
-    rc, out = _run_pins(so, PINS2)
+def test_layout2_mutant_is_caught(name, outcomes):
+    rc, out = outcomes[f"m2_{name}"]
     assert rc != 0, f"planted mistake {name} was not caught:\n{out}"
