@@ -42,6 +42,14 @@
  *     The fraction's distribution given s is thus P(h | s) * 2^-4.  An
  *     exponent without a coded h table of its own shares the table (flat or
  *     coded) that codes its h counts in the fewest bits (bso_share_hroutes).
+ *   layout 3 (container version 3): as layout 2, except that s and h are
+ *     coded as one joint symbol t = 8 s + h with a single per-tensor table
+ *     of precision M_t = 13 (the normaliser applied to the joint counts):
+ *     one coding step and one renormalisation check per weight.  The joint
+ *     table holds P(s) P(h | s) as counted, so every s has its own h
+ *     distribution.  A lane's last group codes s alone (the s-table, M_s),
+ *     with its h values in the start state, and the low four bits sit in
+ *     the plane, both as in layout 2.
  *
  * Parity pins live in tests/test_oracle_*.py (hand-computed coder states,
  * a bit-stack reduction, brute force, normaliser invariants, round trips).
@@ -54,6 +62,8 @@
 #define BSO_MAGIC      "BF16RANS"
 #define BSO_VERSION    1u              /* containers whose BF16 records use layout 1 */
 #define BSO_VERSION2   2u              /* containers with layout-2 BF16 records */
+#define BSO_VERSION3   3u              /* containers with layout-3 BF16 records */
+#define BSO_MT         13u             /* precision of the joint (s, h) table of layout 3 */
 #define BSO_MAX_HTABLES 31u            /* coded h tables per layout-2 record */
 #define BSO_HDR_BYTES  64u
 #define BSO_DIR_BYTES  96u
@@ -531,8 +541,9 @@ typedef struct {
     uint32_t route[512];
     uint32_t n_tables;
     uint32_t qf[1 + BSO_MAX_TABLES][128]; /* [0] is the flat table */
-    uint32_t layout;                      /* 1 or 2 */
+    uint32_t layout;                      /* 1, 2 or 3 */
     uint32_t qh[1 + BSO_MAX_HTABLES][8];  /* layout 2 (M_f holds M_h): [0] is the flat table */
+    uint32_t qt[512 * 8];                 /* layout 3 (M_f holds M_t): q of t = 8 s + h */
 } bso_model;
 
 static int chunk_encode(const bso_model* md, const uint16_t* w, uint32_t n_c, uint32_t K,
@@ -678,11 +689,55 @@ static uint32_t lane_last_group(uint32_t n_c, uint32_t K, uint32_t l, uint64_t* 
 
 static uint32_t split_lead(uint32_t c) { return 3 * c > 16 ? 3 * c : 16; }
 
+/* Layout 3: the joint table's cumulative frequencies in t order and its     */
+/* slot -> symbol map (the slots of t are cum[t] .. cum[t] + q[t] - 1),      */
+/* built once per chunk from qt (whose sum is 2^M_t).                        */
+typedef struct {
+    uint32_t cum[512 * 8];
+    uint16_t sym[1u << BSO_MT];
+} joint_tab;
+
+static void joint_build(const bso_model* md, joint_tab* jt) {
+    uint32_t c = 0;
+    for (uint32_t t = 0; t < 512 * 8; t++) {
+        jt->cum[t] = c;
+        for (uint32_t k = 0; k < md->qt[t] && c + k < (1u << BSO_MT); k++) jt->sym[c + k] = (uint16_t)t;
+        c += md->qt[t];
+    }
+}
+
+/* Encode the joint symbol t: the flush check with its own q at M_t, then    */
+/* the coding step (as enc_symbol, with the cumulative frequency looked up). */
+static int enc_joint(uint32_t* x, const bso_model* md, const joint_tab* jt, uint32_t t, wordlist* out) {
+    uint32_t q = md->qt[t];
+    if (q == 0) return BSO_EINVAL;
+    if ((uint64_t)*x >= ((uint64_t)q << (32 - BSO_MT))) {
+        int rc = wl_push(out, (uint16_t)(*x & 0xFFFFu));
+        if (rc) return rc;
+        *x >>= 16;
+    }
+    *x = (*x / q) * (1u << BSO_MT) + (*x % q) + jt->cum[t];
+    return BSO_OK;
+}
+
+/* Its inverse: t from the low M_t bits of *x, and the state before it. */
+static void dec_joint(uint32_t* x, const bso_model* md, const joint_tab* jt, uint32_t* t) {
+    uint32_t slot = *x & ((1u << BSO_MT) - 1u);
+    *t = jt->sym[slot];
+    *x = md->qt[*t] * (*x >> BSO_MT) + slot - jt->cum[*t];
+}
+
 static int chunk_encode_split(const bso_model* md, const uint16_t* w, uint32_t n_c, uint32_t K,
                               uint32_t l0, uint32_t l1, uint32_t* states, wordlist* wl) {
     bso_table ts = { md->M_s, 512, md->qs };
     uint32_t groups = (n_c + 7) / 8;
     uint32_t T = (groups + K - 1) / K;
+    joint_tab* jt = NULL;
+    if (md->layout == 3) {
+        jt = (joint_tab*)malloc(sizeof(joint_tab));
+        if (!jt) return BSO_ENOMEM;
+        joint_build(md, jt);
+    }
     for (uint32_t l = l0; l < l1; l++) {
         uint64_t g;
         uint32_t c = lane_last_group(n_c, K, l, &g);
@@ -701,14 +756,17 @@ static int chunk_encode_split(const bso_model* md, const uint16_t* w, uint32_t n
                 int rc;
                 if (j / 8 == g) {
                     rc = enc_symbol(&states[l], &ts, s, wl);
+                } else if (md->layout == 3) {
+                    rc = enc_joint(&states[l], md, jt, 8 * s + (bso_symbol_f(w[j]) >> 4), wl);
                 } else {
                     bso_table th = { md->M_f, 8, md->qh[md->route[s]] };
                     rc = enc_pair_words(&states[l], &ts, s, &th, bso_symbol_f(w[j]) >> 4, wl);
                 }
-                if (rc) return rc;
+                if (rc) { free(jt); return rc; }
             }
         }
     }
+    free(jt);
     return BSO_OK;
 }
 
@@ -720,7 +778,9 @@ static int chunk_decode_split(const bso_model* md, const uint32_t* states_in, co
     uint32_t groups = (n_c + 7) / 8;
     uint32_t T = (groups + K - 1) / K;
     uint32_t* x = (uint32_t*)malloc(sizeof(uint32_t) * K);
-    if (!x) return BSO_ENOMEM;
+    joint_tab* jt = md->layout == 3 ? (joint_tab*)malloc(sizeof(joint_tab)) : NULL;
+    if (!x || (md->layout == 3 && !jt)) { free(x); free(jt); return BSO_ENOMEM; }
+    if (jt) joint_build(md, jt);
     for (uint32_t l = l0; l < l1; l++) x[l] = states_in[l];
     uint64_t pos = 0;
     int rc = BSO_OK;
@@ -732,10 +792,17 @@ static int chunk_decode_split(const bso_model* md, const uint32_t* states_in, co
                 uint64_t g;
                 lane_last_group(n_c, K, l, &g);
                 uint32_t s, h = 0;
-                rc = decode_step(&x[l], &ts, &s);
-                if (!rc && j / 8 != g) {
-                    bso_table th = { md->M_f, 8, md->qh[md->route[s]] };
-                    rc = decode_step(&x[l], &th, &h);
+                if (md->layout == 3 && j / 8 != g) {
+                    uint32_t t;
+                    dec_joint(&x[l], md, jt, &t);
+                    s = t >> 3;
+                    h = t & 7u;
+                } else {
+                    rc = decode_step(&x[l], &ts, &s);
+                    if (!rc && j / 8 != g) {
+                        bso_table th = { md->M_f, 8, md->qh[md->route[s]] };
+                        rc = decode_step(&x[l], &th, &h);
+                    }
                 }
                 if (rc) break;
                 out[j] = (uint16_t)((s << 7) | (h << 4));
@@ -758,6 +825,7 @@ static int chunk_decode_split(const bso_model* md, const uint32_t* states_in, co
     }
     if (!rc && pos != nw) rc = BSO_ECORRUPT;
     free(x);
+    free(jt);
     return rc;
 }
 
@@ -891,6 +959,16 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
         if (!rc && layout == 1) rc = bso_select_tables(cs, cf, M_f, cmax, md->route, &md->n_tables, &md->qf[1][0]);
         if (!rc && layout == 2) rc = bso_select_htables(cs, cf, M_f, cmax, md->route, &md->n_tables, &md->qh[1][0]);
         if (!rc && layout == 2) rc = bso_share_hroutes(cs, cf, M_f, md->n_tables, &md->qh[1][0], md->route);
+        if (!rc && layout == 3) {
+            /* the joint counts of t = 8 s + h: the fraction counts of s summed
+               over the low four bits */
+            uint64_t* ct = (uint64_t*)calloc(512 * 8, sizeof(uint64_t));
+            if (!ct) rc = BSO_ENOMEM;
+            for (uint32_t t = 0; !rc && t < 512 * 8; t++)
+                for (uint32_t lo = 0; lo < 16; lo++) ct[t] += cf[(t >> 3) * 128 + 16 * (t & 7u) + lo];
+            if (!rc) rc = bso_normalise(ct, 512 * 8, BSO_MT, md->qt);
+            free(ct);
+        }
         for (uint32_t s = 0; s < 512; s++) if (cs[s]) n_sym++;
     }
     if (layout == 1) for (uint32_t f = 0; f < 128; f++) md->qf[0][f] = 1u << (M_f - 7);
@@ -901,7 +979,7 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
     uint64_t off = 24;
     uint64_t tables_end = off + 4ull * n_sym;
     tables_end = round_up(tables_end + n_sym, 4);
-    tables_end += (layout == 1 ? 256ull : 8ull) * md->n_tables;
+    tables_end += layout == 3 ? 16ull * n_sym : (layout == 1 ? 256ull : 8ull) * md->n_tables;
     uint64_t index_off = round_up(tables_end, 16);
     uint64_t stab_off = index_off + 16 * n_chunks;
     uint64_t payload_off = round_up(stab_off + 4ull * (S - 1) * n_chunks, 16);
@@ -924,6 +1002,16 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
     for (uint32_t t = 1; t <= md->n_tables; t++) {
         if (layout == 1) for (uint32_t f = 0; f < 128; f++) put16(b + ft + 256ull * (t - 1) + 2 * f, md->qf[t][f]);
         else for (uint32_t h = 0; h < 8; h++) b[ft + 8ull * (t - 1) + h] = (uint8_t)md->qh[t][h];
+    }
+    /* layout 3: the joint table, eight 16-bit q (h = 0..7) per occupied s in
+       the order of the s list */
+    if (layout == 3) {
+        uint64_t kk = 0;
+        for (uint32_t sy = 0; sy < 512; sy++) {
+            if (!cs[sy]) continue;
+            for (uint32_t h = 0; h < 8; h++) put16(b + ft + 16 * kk + 2 * h, md->qt[8 * sy + h]);
+            kk++;
+        }
     }
 
     /* chunks: the K lanes' length codes, padded to 16 bytes, then the
@@ -955,7 +1043,7 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
         uint64_t start = body->n;
         /* layout 2: the plane of low fraction bits sits between the length
            codes and the stream area */
-        uint64_t code_bytes = code_block_bytes(K) + (layout == 2 ? plane_bytes(n_c) : 0);
+        uint64_t code_bytes = code_block_bytes(K) + (layout >= 2 ? plane_bytes(n_c) : 0);
         uint64_t end = start + round_up(code_bytes + 2 * total, 16);
         rc = bb_reserve(body, end);
         if (rc) break;
@@ -965,7 +1053,7 @@ static int encode_bf16_body(const uint16_t* w, uint64_t n, uint32_t Wmax, uint32
         put32(b + index_off + 16 * c + 8, (uint32_t)total);
         put32(b + index_off + 16 * c + 12, 0);
         for (uint32_t l = 0; l < K; l++) b[start + l / 2] |= (uint8_t)(state_code(states[l]) << (4 * (l % 2)));
-        if (layout == 2) {
+        if (layout >= 2) {
             uint8_t* plane = b + start + code_block_bytes(K);
             for (uint32_t j = 0; j < n_c; j++) {
                 uint32_t g = j / 8, p = j % 8;
@@ -1006,16 +1094,18 @@ done:
 /* as a RAW record of its 2n bytes.                                          */
 /* On success *out points to malloc'ed bytes (free with bso_free).          */
 /* ------------------------------------------------------------------------ */
-/* layout 1 writes a version-1 container, layout 2 a version-2 container    */
-/* (every BF16 record in that layout).  Layout 2: M_s is 11 or 12 and M_f    */
-/* holds M_h = 16 - M_s; cmax <= 31.                                         */
+/* layout 1 writes a version-1 container, layout 2 a version-2 container,   */
+/* layout 3 a version-3 one (every BF16 record in that layout).  Layout 2:   */
+/* M_s is 11 or 12 and M_f holds M_h = 16 - M_s; cmax <= 31.  Layout 3: M_s  */
+/* is 11 or 12 and M_f holds M_t = 13; cmax is not used.                     */
 int bso_encode_container2(uint32_t n_tensors, const uint32_t* kinds, const void* const* data,
                           const uint64_t* n, const uint8_t* sha,
                           uint32_t Wmax, uint32_t Kmax, uint32_t Pmax, uint32_t M_s, uint32_t M_f, uint32_t cmax,
                           uint32_t layout, uint8_t** out, uint64_t* out_len) {
     if (layout == 1 && (M_s < 9 || M_s > 12 || M_f < 8 || M_f > 10 || cmax > BSO_MAX_TABLES)) return BSO_EINVAL;
     if (layout == 2 && (M_s < 11 || M_s > 12 || M_f != 16 - M_s || cmax > BSO_MAX_HTABLES)) return BSO_EINVAL;
-    if (layout != 1 && layout != 2) return BSO_EINVAL;
+    if (layout == 3 && (M_s < 11 || M_s > 12 || M_f != BSO_MT)) return BSO_EINVAL;
+    if (layout < 1 || layout > 3) return BSO_EINVAL;
     if (!(Kmax <= 64 || Kmax == 128 || Kmax == 256 || Kmax == 512 || Kmax == 1024 || Kmax == 2048) || Kmax == 0) return BSO_EINVAL;
     if ((Kmax & (Kmax - 1)) != 0) return BSO_EINVAL;
     if (Pmax == 0 || (Pmax & (Pmax - 1)) != 0 || Pmax > Kmax || Pmax > 512) return BSO_EINVAL;
@@ -1081,7 +1171,7 @@ int bso_encode_container2(uint32_t n_tensors, const uint32_t* kinds, const void*
         if (e > out_len_bytes) out_len_bytes = e;
     }
     memcpy(c.p, BSO_MAGIC, 8);
-    put32(c.p + 8, layout == 1 ? BSO_VERSION : BSO_VERSION2);
+    put32(c.p + 8, layout == 1 ? BSO_VERSION : layout == 2 ? BSO_VERSION2 : BSO_VERSION3);
     put32(c.p + 12, n_tensors);
     put64(c.p + 16, dir);
     put64(c.p + 24, total);
@@ -1114,14 +1204,16 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, uint32_t vers
     if (b[15] > 9) return BSO_EFORMAT;
     *S = 1u << b[15];
     uint32_t n_sym = get32(b + 16);
-    /* version 1: the word at +20 is 0 (layout 1); version 2: it names the layout */
+    /* version 1: the word at +20 is 0 (layout 1); versions 2 and 3 name the
+       layout there (1 or 2; version 3 also 3) */
     uint32_t lw = get32(b + 20);
     if (version == BSO_VERSION) { if (lw != 0) return BSO_EFORMAT; md->layout = 1; }
-    else { if (lw != 1 && lw != 2) return BSO_EFORMAT; md->layout = lw; }
+    else { if (lw < 1 || lw > (version == BSO_VERSION3 ? 3u : 2u)) return BSO_EFORMAT; md->layout = lw; }
     if (md->layout == 1 && (md->M_s < 9 || md->M_s > 12 || md->M_f < 8 || md->M_f > 10 || md->n_tables > BSO_MAX_TABLES))
         return BSO_EFORMAT;
     if (md->layout == 2 && (md->M_s < 11 || md->M_s > 12 || md->M_f != 16 - md->M_s || md->n_tables > BSO_MAX_HTABLES))
         return BSO_EFORMAT;
+    if (md->layout == 3 && (md->M_s < 11 || md->M_s > 12 || md->M_f != BSO_MT || md->n_tables != 0)) return BSO_EFORMAT;
     if (*K == 0 || *W == 0 || *W % (8 * *K)) return BSO_EFORMAT;
     if (!(*K <= 64 || *K == 128 || *K == 256 || *K == 512 || *K == 1024 || *K == 2048)) return BSO_EFORMAT;
     if (*K % *S || *K / *S > 512) return BSO_EFORMAT;
@@ -1129,7 +1221,7 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, uint32_t vers
     if (n_sym > BSO_MAX_SYMS || (n_sym == 0) != (n == 0)) return BSO_EFORMAT;
     uint64_t off = 24;
     uint64_t ft = round_up(off + 4ull * n_sym + n_sym, 4);
-    uint64_t tab_end = ft + (md->layout == 1 ? 256ull : 8ull) * md->n_tables;
+    uint64_t tab_end = ft + (md->layout == 3 ? 16ull * n_sym : (md->layout == 1 ? 256ull : 8ull) * md->n_tables);
     *index_off = round_up(tab_end, 16);
     if (*index_off + 16 * *n_chunks + 4ull * (*S - 1) * *n_chunks > len) return BSO_EFORMAT;
     memset(md->qs, 0, sizeof(md->qs));
@@ -1146,6 +1238,17 @@ static int parse_model(const uint8_t* b, uint64_t len, uint64_t n, uint32_t vers
         sum += q;
     }
     if (n_sym && sum != (1ull << md->M_s)) return BSO_EFORMAT;
+    if (md->layout == 3) {
+        /* eight joint frequencies per listed s, summing to 2^M_t over all */
+        memset(md->qt, 0, sizeof(md->qt));
+        uint64_t tsum = 0;
+        for (uint32_t k = 0; k < n_sym; k++) {
+            uint32_t sy = get16(b + off + 4ull * k);
+            for (uint32_t h = 0; h < 8; h++) { md->qt[8 * sy + h] = get16(b + ft + 16ull * k + 2 * h); tsum += md->qt[8 * sy + h]; }
+        }
+        if (n_sym && tsum != (1ull << BSO_MT)) return BSO_EFORMAT;
+        return BSO_OK;
+    }
     if (md->layout == 2) {
         for (uint32_t h = 0; h < 8; h++) md->qh[0][h] = 1u << (md->M_f - 3);
         for (uint32_t t = 1; t <= md->n_tables; t++) {
@@ -1169,8 +1272,8 @@ static int decode_one_chunk(const bso_model* md, const uint8_t* b, uint64_t rl, 
                             uint32_t S, uint64_t n_chunks, uint64_t ch, uint32_t n_c, uint16_t* out) {
     const uint8_t* e = b + io + 16 * ch;
     uint64_t po = get64(e), total = get32(e + 8);
-    /* layout 2: the plane of low fraction bits follows the length codes */
-    uint64_t code_bytes = code_block_bytes(K) + (md->layout == 2 ? plane_bytes(n_c) : 0);
+    /* layouts 2 and 3: the plane of low fraction bits follows the length codes */
+    uint64_t code_bytes = code_block_bytes(K) + (md->layout >= 2 ? plane_bytes(n_c) : 0);
     if (po % 16 || po > rl || code_bytes > rl - po || 2 * total > rl - po - code_bytes) return BSO_EFORMAT;
     const uint8_t* stab = b + io + 16 * n_chunks + 4 * (S - 1) * ch;
     uint32_t P = K / S;
@@ -1205,7 +1308,7 @@ static int decode_one_chunk(const bso_model* md, const uint8_t* b, uint64_t rl, 
         free(words);
     }
     free(st);
-    if (!rc && md->layout == 2) {
+    if (!rc && md->layout >= 2) {
         const uint8_t* plane = b + po + code_block_bytes(K);
         for (uint32_t j = 0; j < n_c; j++)
             out[j] = (uint16_t)(out[j] | ((get32(plane + 4 * (j / 8)) >> low_bit_pos(j % 8)) & 15u));
@@ -1216,7 +1319,7 @@ static int decode_one_chunk(const bso_model* md, const uint8_t* b, uint64_t rl, 
 int bso_decode_container(const uint8_t* c, uint64_t len, uint8_t* out, uint64_t out_cap, int32_t* rec_status) {
     if (len < BSO_HDR_BYTES || memcmp(c, BSO_MAGIC, 8) != 0) return BSO_EFORMAT;
     uint32_t version = get32(c + 8);
-    if (version != BSO_VERSION && version != BSO_VERSION2) return BSO_EVERSION;
+    if (version != BSO_VERSION && version != BSO_VERSION2 && version != BSO_VERSION3) return BSO_EVERSION;
     uint32_t n_rec = get32(c + 12);
     uint64_t dir = get64(c + 16);
     if (get64(c + 24) != len) return BSO_EFORMAT;
@@ -1263,7 +1366,7 @@ int bso_decode_chunk(const uint8_t* c, uint64_t len, uint32_t record, uint64_t c
                      uint16_t* out, uint64_t out_cap, uint64_t* n_c_out) {
     if (len < BSO_HDR_BYTES || memcmp(c, BSO_MAGIC, 8) != 0) return BSO_EFORMAT;
     uint32_t version = get32(c + 8);
-    if (version != BSO_VERSION && version != BSO_VERSION2) return BSO_EVERSION;
+    if (version != BSO_VERSION && version != BSO_VERSION2 && version != BSO_VERSION3) return BSO_EVERSION;
     uint32_t n_rec = get32(c + 12);
     uint64_t dir = get64(c + 16);
     if (record >= n_rec || dir + (uint64_t)BSO_DIR_BYTES * n_rec > len) return BSO_EINVAL;

@@ -287,7 +287,9 @@ def encode(tensors, W: int = 65536, K: int = 64, M_s: int = 12, M_f: int = 10, c
     """Container of the tensors: chunks of W weights with K lanes, split into
     streams of P lanes (default: one stream of all K lanes).  layout 1 gives a
     version-1 container; layout 2 a version-2 one, with M_s 11 or 12, M_f
-    the precision of the h tables (16 - M_s) and cmax up to 31."""
+    the precision of the h tables (16 - M_s) and cmax up to 31; layout 3 a
+    version-3 one, with M_s 11 or 12 and M_f the precision of the joint
+    (s, h) table (13)."""
     n = len(tensors)
     P = K if P is None else P
     kinds = np.array([t.kind for t in tensors] or [0], np.uint32)

@@ -127,7 +127,7 @@ def test_validation_errors():
     c = codec.encode([codec.bf16(w)], codec.params(chunk_weights=4096, lanes=8))
     codec.container_info(c)
     bad = bytearray(c)
-    bad[8:12] = struct.pack("<I", 3)
+    bad[8:12] = struct.pack("<I", 4)
     with pytest.raises(L.BSError) as e:
         codec.container_info(bytes(bad))
     assert e.value.rc == L.BS_E_VERSION

@@ -136,9 +136,9 @@ def test_corruption_and_header_errors():
     # truncation
     rc, _, _ = O.decode_status(bytes(c[:-16]))
     assert rc == -2
-    # unknown version (1 and 2 are defined)
+    # unknown version (1, 2 and 3 are defined)
     v3 = bytearray(c)
-    v3[8:12] = struct.pack("<I", 3)
+    v3[8:12] = struct.pack("<I", 4)
     rc, _, _ = O.decode_status(bytes(v3))
     assert rc == -3
     # output too small

@@ -360,9 +360,9 @@ def test_corruption_and_format_errors():
     c1[8:12] = (2).to_bytes(4, "little")
     rc, out, st = O.decode_status(bytes(c1))
     assert st[0] == -2
-    # an unknown container version
+    # an unknown container version (3 is layout 3's)
     bad = bytearray(c)
-    bad[8:12] = (3).to_bytes(4, "little")
+    bad[8:12] = (4).to_bytes(4, "little")
     rc, out, st = O.decode_status(bytes(bad))
     assert rc == -3
 

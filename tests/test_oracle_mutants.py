@@ -89,8 +89,8 @@ MUTANTS2 = {
                                 "                if (0) {\n                    rc = enc_symbol(&states[l], &ts, s, wl);"),
     "split_h_four_bits": ("rc = enc_pair_words(&states[l], &ts, s, &th, bso_symbol_f(w[j]) >> 4, wl);",
                           "rc = enc_pair_words(&states[l], &ts, s, &th, (bso_symbol_f(w[j]) >> 4) ^ (j & 1), wl);"),
-    "split_refill_between_steps": ("                rc = decode_step(&x[l], &ts, &s);\n                if (!rc && j / 8 != g) {",
-                                   "                rc = decode_step(&x[l], &ts, &s);\n                if (x[l] < BSO_L && pos < nw) x[l] = (x[l] << 16) | words[pos++];\n                if (!rc && j / 8 != g) {"),
+    "split_refill_between_steps": ("                    rc = decode_step(&x[l], &ts, &s);\n                    if (!rc && j / 8 != g) {",
+                                   "                    rc = decode_step(&x[l], &ts, &s);\n                    if (x[l] < BSO_L && pos < nw) x[l] = (x[l] << 16) | words[pos++];\n                    if (!rc && j / 8 != g) {"),
     "htable_threshold_zero": ("eligible[e] = saved[e] > (__int128)65536 * 64;", "eligible[e] = saved[e] > 0;"),
     "htable_tie_high": ("if (best < 0 || saved[e] > saved[best]) best = (int)e;", "if (best < 0 || saved[e] >= saved[best]) best = (int)e;"),
     "htable_signs_not_merged": ("for (uint32_t f = 16 * h; f < 16 * h + 16; f++) m[h] += cf[e * 128 + f] + cf[(256 + e) * 128 + f];",
@@ -110,8 +110,30 @@ MUTANTS2 = {
                          "uint32_t q = t == 0 ? (1u << (M_h - 2)) : qh[(t - 1) * 8 + h];"),
     "share_positive_counts": ("for (uint32_t f = 16 * h; f < 16 * h + 16; f++) m[h] += cf[e * 128 + f] + cf[(256 + e) * 128 + f];\n        }\n        uint32_t best = 0;",
                               "for (uint32_t f = 16 * h; f < 16 * h + 16; f++) m[h] += cf[e * 128 + f];\n        }\n        uint32_t best = 0;"),
-    "version2_accepts_layout0": ("else { if (lw != 1 && lw != 2) return BSO_EFORMAT; md->layout = lw; }",
-                                 "else { if (lw > 2) return BSO_EFORMAT; md->layout = lw ? lw : 1; }"),
+    "version2_accepts_layout0": ("else { if (lw < 1 || lw > (version == BSO_VERSION3 ? 3u : 2u)) return BSO_EFORMAT; md->layout = lw; }",
+                                 "else { if (lw > (version == BSO_VERSION3 ? 3u : 2u)) return BSO_EFORMAT; md->layout = lw ? lw : 1; }"),
+}
+
+# planted mistakes in layout 3 (the joint (s, h) symbol), checked against the
+# layout-3 pins only
+PINS3 = ["tests/test_oracle_layout3.py"]
+MUTANTS3 = {
+    "joint_flush_uses_M_s": ("if ((uint64_t)*x >= ((uint64_t)q << (32 - BSO_MT))) {",
+                             "if ((uint64_t)*x >= ((uint64_t)q << (32 - md->M_s))) {"),
+    "joint_precision_12": ("#define BSO_MT         13u", "#define BSO_MT         12u"),
+    "joint_counts_drop_low15": ("for (uint32_t lo = 0; lo < 16; lo++) ct[t] +=", "for (uint32_t lo = 0; lo < 15; lo++) ct[t] +="),
+    "joint_counts_h_stride_8": ("ct[t] += cf[(t >> 3) * 128 + 16 * (t & 7u) + lo];", "ct[t] += cf[(t >> 3) * 128 + 8 * (t & 7u) + lo];"),
+    "joint_counts_one_sign": ("for (uint32_t t = 0; !rc && t < 512 * 8; t++)", "for (uint32_t t = 0; !rc && t < 256 * 8; t++)"),
+    "joint_index_h_major": ("rc = enc_joint(&states[l], md, jt, 8 * s + (bso_symbol_f(w[j]) >> 4), wl);",
+                            "rc = enc_joint(&states[l], md, jt, s + 512 * (bso_symbol_f(w[j]) >> 4), wl);"),
+    "joint_last_group_joint": ("                if (j / 8 == g) {\n                    rc = enc_symbol(&states[l], &ts, s, wl);",
+                               "                if (j / 8 == g && md->layout != 3) {\n                    rc = enc_symbol(&states[l], &ts, s, wl);"),
+    "joint_table_h_reversed": ("for (uint32_t h = 0; h < 8; h++) put16(b + ft + 16 * kk + 2 * h, md->qt[8 * sy + h]);",
+                               "for (uint32_t h = 0; h < 8; h++) put16(b + ft + 16 * kk + 2 * (7 - h), md->qt[8 * sy + h]);"),
+    "joint_decoded_h_shifted": ("                    h = t & 7u;", "                    h = (t >> 1) & 7u;"),
+    "joint_no_sum_check": ("if (n_sym && tsum != (1ull << BSO_MT)) return BSO_EFORMAT;", "if (0) return BSO_EFORMAT;"),
+    "layout3_plane_missing": ("uint64_t code_bytes = code_block_bytes(K) + (md->layout >= 2 ? plane_bytes(n_c) : 0);",
+                              "uint64_t code_bytes = code_block_bytes(K) + (md->layout == 2 ? plane_bytes(n_c) : 0);"),
 }
 
 
@@ -142,8 +164,8 @@ def outcomes(tmp_path_factory):
     built and run concurrently: each case is an independent child process."""
     base = str(tmp_path_factory.mktemp("mutants"))
     src = open(SRC).read()
-    jobs = [("clean", src, PINS), ("clean2", src, PINS2)]
-    for table, pins, tag in ((MUTANTS, PINS, "m1"), (MUTANTS2, PINS2, "m2")):
+    jobs = [("clean", src, PINS), ("clean2", src, PINS2), ("clean3", src, PINS3)]
+    for table, pins, tag in ((MUTANTS, PINS, "m1"), (MUTANTS2, PINS2, "m2"), (MUTANTS3, PINS3, "m3")):
         for name, (old, new) in table.items():
             assert src.count(old) >= 1, f"mutation anchor not found: {name}"
             jobs.append((f"{tag}_{name}", src.replace(old, new, 1), pins))
@@ -172,4 +194,15 @@ def test_unmodified_oracle_passes_layout2_selection(outcomes):
 @pytest.mark.parametrize("name", sorted(MUTANTS2))
 def test_layout2_mutant_is_caught(name, outcomes):
     rc, out = outcomes[f"m2_{name}"]
+    assert rc != 0, f"planted mistake {name} was not caught:\n{out}"
+
+
+def test_unmodified_oracle_passes_layout3_selection(outcomes):
+    rc, out = outcomes["clean3"]
+    assert rc == 0, out
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS3))
+def test_layout3_mutant_is_caught(name, outcomes):
+    rc, out = outcomes[f"m3_{name}"]
     assert rc != 0, f"planted mistake {name} was not caught:\n{out}"
