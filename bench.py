@@ -65,9 +65,9 @@ def parse():
     ap.add_argument("--stream-lanes", type=int, default=None, help="override the lanes per word stream")
     ap.add_argument("--m-s", type=int, default=None, help="override the (sign, exponent) table precision")
     ap.add_argument("--m-f", type=int, default=None, help="override the fraction table precision")
-    ap.add_argument("--layout", type=int, default=None, choices=[1, 2],
-                    help="override the record layout (2: one renormalisation per weight; the default except for "
-                         "the 4096x4096 matrix)")
+    ap.add_argument("--layout", type=int, default=None, choices=[1, 2, 3],
+                    help="override the record layout (2: one renormalisation per weight; 3: the same with s and "
+                         "the fraction's high bits one joint symbol)")
     ap.add_argument("--gemv", action="store_true",
                     help="time the fused decode and matrix-vector product (bs_gemv_async) of the 4096x4096 "
                          "workload against decode-then-GEMV and a GEMV on the uncompressed matrix")
@@ -91,6 +91,7 @@ def parse():
 
 TRAFFIC_SOURCES = {"decode_kernel": ("bs_decode.hip", "bs_decode_common.h", "bs_device.h"),
                    "decode2_kernel": ("bs_decode2.hip", "bs_decode_common.h", "bs_device.h"),
+                   "decode3_kernel": ("bs_decode2.hip", "bs_decode_common.h", "bs_device.h"),
                    "fixed": ("bs_fixed.hip", "bs_fixed_device.h")}
 
 
@@ -137,7 +138,9 @@ def model_build_rate(job):
             return None
         words = job.ref[ri.out_offset: ri.out_offset + 2 * ri.n].view(torch.int16)
         n = ri.n
-    if getattr(job, "layout", 1) == 2:
+    if getattr(job, "layout", 1) == 3:
+        p = codec.params3(chunk_weights=job.chunk_weights, lanes=job.lanes, m_s=job.m_s, stream_lanes=job.stream_lanes)
+    elif getattr(job, "layout", 1) == 2:
         p = codec.params2(chunk_weights=job.chunk_weights, lanes=job.lanes, m_s=job.m_s, stream_lanes=job.stream_lanes)
     else:
         p = codec.params(chunk_weights=job.chunk_weights, lanes=job.lanes, m_s=job.m_s, m_f=job.m_f,
@@ -586,7 +589,7 @@ def encode_bench(a):
     layout = a.layout or wl.layout
     p = codec.params(chunk_weights=a.chunk_weights or wl.chunk_weights, lanes=a.lanes or wl.lanes,
                      stream_lanes=a.stream_lanes if a.stream_lanes is not None else wl.stream_lanes,
-                     m_s=11 if layout == 2 else 12, m_f=5 if layout == 2 else 10,
+                     m_s=11 if layout >= 2 else 12, m_f={1: 10, 2: 5, 3: codec.JOINT_BITS}[layout],
                      max_tables=31 if layout == 2 else 6, layout=layout)
     dev, host, digests = [], [], []
     n_bf16 = 0
@@ -836,7 +839,7 @@ def main():
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
     layout = getattr(job, "layout", 1)
     traffic = measured_traffic(f"{job.name}|W={job.chunk_weights}|K={job.lanes}|P={job.stream_lanes}|L={layout}",
-                               "decode2_kernel" if layout == 2 else "decode_kernel")
+                               {2: "decode2_kernel", 3: "decode3_kernel"}.get(layout, "decode_kernel"))
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",

@@ -11,9 +11,10 @@
  * Instruct -- Lossless Compressed card, "What lossless means"; NVLC card,
  * SHA256SUMS verification block] (sha256 here).
  *
- * Container ("BF16RANS", version 1 or 2, little-endian) -- this library's own
- * layout.  Version 1 holds layout-1 records only; version 2 adds layout 2
- * (below) and names each BF16 record's layout in its fixed part:
+ * Container ("BF16RANS", version 1, 2 or 3, little-endian) -- this library's
+ * own layout.  Version 1 holds layout-1 records only; version 2 adds layout 2
+ * (below) and names each BF16 record's layout in its fixed part; version 3
+ * also allows layout 3 (below):
  *   header 64 B: magic[8] "BF16RANS", u32 version, u32 n_records,
  *                u64 dir_offset, u64 total_len, u64 out_len, u32 flags, 20 B zero
  *   directory, 96 B per record: u32 kind (1 = BF16 rANS, 2 = RAW verbatim),
@@ -22,7 +23,7 @@
  *   BF16 record body: u32 W (weights per chunk), u32 K (lanes), u32 n_chunks,
  *                u8 M_s, u8 M_f, u8 n_tables, u8 log2 S (word streams per
  *                chunk), u32 n_sym, u32 layout (version 1: 0, meaning layout
- *                1; version 2: 1 or 2); the rest of a layout-1 body:
+ *                1; version 2: 1 or 2; version 3: 1, 2 or 3); the rest of a layout-1 body:
  *                s-table n_sym x (u16 s, u16 q) ascending s (sum q = 2^M_s);
  *                route: n_sym bytes (fraction table of each s: 0 = flat,
  *                1..n_tables), padded to 4 B; n_tables x 128 x u16 q_f
@@ -81,6 +82,23 @@
  * between contexts [NVLC card, codec paragraph: "soft-routed fraction
  * distribution", read as a route to a shared table].
  *
+ * Layout 3 (one joint symbol per weight): as layout 2, except that outside
+ * a lane's last group s and h are coded as one symbol t = 8 s + h with a
+ * per-tensor table of precision M_t = 13 (held in the M_f byte; n_tables 0):
+ * one coding step and one renormalisation check per weight.  Each s thus
+ * has its own h distribution [NVLC card, codec paragraph: the decoded
+ * symbol selects the fraction's distribution].  Body after the fixed part:
+ * the s-table and route bytes (all 0) as in layout 1, padded to 4 B, then
+ * n_sym x 8 x u16 q_t, the joint frequencies of (s, h = 0..7) for each s of
+ * the s-table in its order (all summing to 2^13), padded to 16 B; chunk
+ * index, stream table, payloads (with the plane), sub-steps and the last
+ * group (s alone, h in the start state) as in layout 2.  Frequencies (the
+ * s-table's and the joint table's) quantise counts c of n words to 2^M:
+ * q = max(1, floor(c 2^M / n)) for c > 0; a shortfall is added one by one
+ * in order of the remainder (c 2^M mod n) descending, lower index first,
+ * cycling; an excess is taken one at a time from the largest q > 1, lower
+ * index first.
+ *
  * Conventions:
  *   - Every function returns a bs_status (0 = BS_OK); none throws or aborts.
  *     bs_last_error() gives a thread-local message for the last failure.
@@ -125,7 +143,9 @@ enum { BS_KIND_BF16 = 1, BS_KIND_RAW = 2 };
  * decoder multiplies x >> m in 24 bits, so m >= 8), max_tables <= 6; the
  * container is version 1.  layout 2: m_s 11 or 12, m_f = 16 - m_s (the
  * precision of the h tables), max_tables <= 31; the container is version 2,
- * and the GPU decode takes at most 256 lanes per word stream. */
+ * and the GPU decode takes at most 256 lanes per word stream.  layout 3: m_s
+ * 11 or 12, m_f = 13 (the joint table's precision), max_tables unused; the
+ * container is version 3, at most 256 lanes per word stream as in layout 2. */
 typedef struct {
     uint32_t chunk_weights;
     uint32_t lanes;
@@ -150,9 +170,10 @@ typedef struct bs_tables bs_tables; /* opaque, library-owned */
  * [NVLC card, codec paragraph: the sign/exponent model is per tensor, the
  * fraction distribution is selected by the decoded symbol].
  * One HIP histogram pass with LDS-privatised counters (fraction counts per
- * exponent over both signs, and negative words per exponent), then host
- * quantisation of the counts to 2^m_s and 2^m_f and the choice of coded
- * fraction contexts.
+ * exponent over both signs, and negative words per exponent and high
+ * fraction bits), then host quantisation of the counts to 2^m_s and 2^m_f
+ * (layout 3: of the joint counts to 2^13) and the choice of coded fraction
+ * contexts.
  * d_bf16: n little-endian 16-bit words in device memory (any alignment of 2).
  * Synchronises `stream`.  *out receives a new bs_tables (free with
  * bs_tables_free).  Errors: BS_E_INVAL (bad params / NULL), BS_E_HIP,
@@ -167,7 +188,7 @@ bs_status bs_build_tables_host(const uint16_t* h_bf16, uint64_t n, const bs_para
  * any allocation.  The model is written over *t, an existing tables object
  * (from bs_build_tables or bs_build_tables_host); the result is the one
  * bs_build_tables gives for the same words and params.  The histogram's
- * counters sit in a fixed device array of the library (264,192 B on each GPU
+ * counters sit in a fixed device array of the library (278,528 B on each GPU
  * it runs on, held until the process ends; its size does not depend on n),
  * cleared by a kernel at each call.  Calls in one process are serialised by
  * a host lock held from the clear to the read-back, so they never overlap on
@@ -185,9 +206,15 @@ void bs_tables_free(bs_tables* t);
 bs_status bs_tables_get(const bs_tables* t, uint64_t* counts_s, uint32_t* q_s, uint32_t* route,
                         uint32_t* q_f, uint32_t* n_tables, uint32_t* m_s, uint32_t* m_f, uint64_t* n_weights);
 
-/* The model's layout (1 or 2) and, for layout 2, its h tables: q_h[31*8]
+/* The model's layout (1, 2 or 3) and, for layout 2, its h tables: q_h[31*8]
  * (row t-1 = table t; may be NULL). */
 bs_status bs_tables_get_layout(const bs_tables* t, uint32_t* layout, uint32_t* q_h);
+
+/* A layout-3 model's joint table: q_t[4096] receives the frequency of each
+ * joint symbol 8 s + h (sum 2^13; zeros for a model of another layout)
+ * [NVLC card, codec paragraph: the fraction's distribution is selected by
+ * the decoded symbol].  Errors: BS_E_INVAL (NULL). */
+bs_status bs_tables_get_joint(const bs_tables* t, uint32_t* q_t);
 
 /* ---------------------------------------------------------------- encode */
 
@@ -279,7 +306,7 @@ typedef struct {
     uint8_t sha256[32];
     uint64_t stream_base;   /* status index of the record's first stream */
     uint32_t streams;       /* word streams per chunk */
-    uint32_t layout;        /* BF16 records: 1 or 2 */
+    uint32_t layout;        /* BF16 records: 1, 2 or 3 */
 } bs_record_info;
 
 /* Validate a host copy of a container and describe it.  Errors: BS_E_FORMAT,

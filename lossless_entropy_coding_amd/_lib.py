@@ -86,6 +86,7 @@ SIGNATURES = {
     "bs_params_default": (None, [C.POINTER(Params)]),
     "bs_build_tables": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(Params), C.c_void_p, C.POINTER(C.c_void_p)]),
     "bs_tables_get_layout": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_void_p]),
+    "bs_tables_get_joint": (C.c_int, [C.c_void_p, C.c_void_p]),
     "bs_build_tables_host": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(Params), C.POINTER(C.c_void_p)]),
     "bs_build_tables_noalloc": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(Params), C.c_void_p, C.c_void_p]),
     "bs_tables_free": (None, [C.c_void_p]),

@@ -49,27 +49,29 @@ class CheckpointJob:
 
     def __init__(self, layers: int = 84, chunk_weights: int = 65536, lanes: int | None = None, log=print,
                  device: str = "cuda", m_s: int | None = None, m_f: int | None = None,
-                 stream_lanes: int | None = None, layout: int = 2):
+                 stream_lanes: int | None = None, layout: int = 3):
         tensors = synth.cfg5_layout(layers=layers)
-        # chunk shape: K = 256 lanes in streams of 128 for layout 2 (as fast as
-        # 512 lanes here, at 0.2% less size); 512 in streams of 256 for layout 1
+        # chunk shape: K = 256 lanes in streams of 128 for layouts 2 and 3 (as
+        # fast as 512 lanes here, at 0.2% less size); 512 in streams of 256 for
+        # layout 1
         if lanes is None:
-            lanes = 256 if layout == 2 else 512
+            lanes = 256 if layout >= 2 else 512
         if stream_lanes is None:
-            stream_lanes = 128 if layout == 2 else 256
+            stream_lanes = 128 if layout >= 2 else 256
         self.name = "cfg5_checkpoint_%dlayers_%dtensors" % (layers, len(tensors))
         self.chunk_weights, self.lanes, self.stream_lanes = chunk_weights, lanes, stream_lanes or lanes
-        # record layout 2 codes the fraction's high three bits at M_h = 16 - M_s
+        # record layout 2 codes the fraction's high three bits at M_h = 16 - M_s,
+        # layout 3 the joint (s, h) symbol at 13 bits
         if m_s is None:
-            m_s = 11 if layout == 2 else 12
+            m_s = 11 if layout >= 2 else 12
         if m_f is None:
-            m_f = 16 - m_s if layout == 2 else 10
+            m_f = {1: 10, 2: 16 - m_s, 3: codec.JOINT_BITS}[layout]
         self.m_s, self.m_f, self.layout = m_s, m_f, layout
         self.lanes_per_thread = max(1, self.stream_lanes // 64)
         # one mixed launch per layer: matrices (several lanes per thread) and vectors (one)
         variant = 0 if self.lanes_per_thread <= 2 else 3
-        if layout == 2:
-            self.kernel_name = "decode2_kernel<%d>" % variant
+        if layout >= 2:
+            self.kernel_name = "decode%d_kernel<%d>" % (layout, variant)
         else:
             self.kernel_name = "decode_kernel<%d, %s>" % (variant, "true" if m_s <= 11 and m_f <= 9 else "false")
         self.plans, self.refs = [], []
@@ -77,7 +79,9 @@ class CheckpointJob:
         self.n_weights = self.raw_bytes = self.read_bytes = self.container_bytes = 0
         self.n_tensors = 0
         bits = ent = 0.0
-        if layout == 2:
+        if layout == 3:
+            p = codec.params3(chunk_weights=chunk_weights, lanes=lanes, m_s=m_s, stream_lanes=stream_lanes)
+        elif layout == 2:
             p = codec.params2(chunk_weights=chunk_weights, lanes=lanes, m_s=m_s, stream_lanes=stream_lanes)
         else:
             p = codec.params(chunk_weights=chunk_weights, lanes=lanes, m_s=m_s, m_f=m_f, stream_lanes=stream_lanes)

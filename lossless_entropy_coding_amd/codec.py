@@ -48,6 +48,15 @@ def params2(chunk_weights: int = 65536, lanes: int = 128, m_s: int = 11, threads
     return params(chunk_weights, lanes, m_s, 16 - m_s, max_tables, threads, stream_lanes, layout=2)
 
 
+JOINT_BITS = 13   # precision of a layout-3 record's joint (s, h) table
+
+
+def params3(chunk_weights: int = 65536, lanes: int = 128, m_s: int = 11, threads: int = 0,
+            stream_lanes: int = 0) -> L.Params:
+    """Layout-3 encoder parameters: s and h coded as one joint symbol."""
+    return params(chunk_weights, lanes, m_s, JOINT_BITS, 0, threads, stream_lanes, layout=3)
+
+
 class Tables:
     """A per-tensor model (opaque bs_tables), freed with the object."""
 
@@ -76,8 +85,12 @@ class Tables:
              "n": n.value, "layout": layout.value}
         if layout.value == 1:
             d["q_f"] = qf[: nt.value].copy()
-        else:
+        elif layout.value == 2:
             d["q_h"] = qh[: nt.value].copy()
+        else:
+            qt = np.zeros(512 * 8, np.uint32)
+            L.check(L.lib().bs_tables_get_joint(self.handle, qt.ctypes.data), "bs_tables_get_joint")
+            d["q_t"] = qt
         return d
 
 

@@ -43,6 +43,7 @@ struct EncModel {
     EncSym s[512];
     EncSym f[kMaxTables + 1][128];     // layout 1
     EncSym h[kMaxHTables + 1][8];      // layout 2 (x_max unused: a pair's bound is joint)
+    EncSym t[512 * 8];                 // layout 3: the joint symbol 8 s + h at precision kMt
     uint8_t route[512];
 };
 
@@ -55,6 +56,14 @@ void make_enc(const Model& md, EncModel& em) {
         em.s[s] = {(uint64_t)md.q_s[s] << (32 - md.m_s), md.q_s[s], cum};
         cum += md.q_s[s];
         em.route[s] = (uint8_t)md.route[s];
+    }
+    if (md.layout == 3) {
+        cum = 0;
+        for (uint32_t t = 0; t < 512 * 8; t++) {
+            em.t[t] = {(uint64_t)md.q_t[t] << (32 - kMt), md.q_t[t], cum};
+            cum += md.q_t[t];
+        }
+        return;
     }
     if (md.layout == 2) {
         for (uint32_t t = 0; t <= md.n_tables; t++) {
@@ -143,13 +152,15 @@ uint64_t encode_stream(const EncModel& em, const uint16_t* w, uint32_t n_c, uint
     return (uint64_t)(sink - scratch);
 }
 
-// Layout 2: one stream of the lanes [l0, l1) of a chunk, one renormalisation
-// per weight.  A lane's weight outside its last group is the pair (s, h =
-// f >> 4): one flush check against the joint bound q_s q_h 2^(32 - M_s - M_h)
-// = q_s q_h 2^16, then h is coded, then s (the decoder takes s first).  In
-// its last group (c weights) a lane codes s only; the h of those weights
-// start the lane's state: the low 3c bits under a leading one at bit
-// max(16, 3c).  The low fraction bits go to the chunk's plane, not here.
+// Layouts 2 and 3: one stream of the lanes [l0, l1) of a chunk, one
+// renormalisation per weight.  Layout 2: a lane's weight outside its last
+// group is the pair (s, h = f >> 4): one flush check against the joint bound
+// q_s q_h 2^(32 - M_s - M_h) = q_s q_h 2^16, then h is coded, then s (the
+// decoder takes s first).  Layout 3: that weight is the one joint symbol
+// 8 s + h (precision kMt).  In its last group (c weights) a lane codes s
+// only; the h of those weights start the lane's state: the low 3c bits under
+// a leading one at bit max(16, 3c).  The low fraction bits go to the chunk's
+// plane, not here.
 uint64_t encode_stream2(const EncModel& em, const uint16_t* w, uint32_t n_c, uint32_t K, uint32_t l0, uint32_t l1,
                         uint32_t* x, uint16_t* scratch) {
     const uint64_t groups = ((uint64_t)n_c + 7) / 8;
@@ -178,6 +189,10 @@ uint64_t encode_stream2(const EncModel& em, const uint16_t* w, uint32_t n_c, uin
                 const EncSym& es = em.s[v >> 7];
                 if (j / 8 == last[l - l0]) {
                     put(x[l], es, em.m_s, sink);
+                    continue;
+                }
+                if (em.layout == 3) {
+                    put(x[l], em.t[8 * (v >> 7) + ((v & 127u) >> 4)], kMt, sink);
                     continue;
                 }
                 const EncSym& eh = em.h[em.route[v >> 7]][(v & 127u) >> 4];
@@ -251,7 +266,7 @@ void build_head(EncRecord& r) {
     const uint64_t stab = 24;
     const uint64_t route_off = stab + 4ull * md.n_sym;
     const uint64_t ftab = align_up(route_off + md.n_sym, 4);
-    const uint64_t tab_end = ftab + (md.layout == 2 ? 8ull : 256ull) * md.n_tables;
+    const uint64_t tab_end = md.layout == 3 ? ftab + 16ull * md.n_sym : ftab + (md.layout == 2 ? 8ull : 256ull) * md.n_tables;
     r.index_off = align_up(tab_end, 16);
     r.stab_off = r.index_off + 16ull * r.n_chunks;
     r.head.assign(align_up(r.stab_off + 4ull * (r.S - 1) * r.n_chunks, 16), 0);
@@ -266,13 +281,16 @@ void build_head(EncRecord& r) {
     while ((1u << log2s) < r.S) log2s++;
     b[15] = (uint8_t)log2s;
     wr32(b + 16, md.n_sym);
-    wr32(b + 20, md.layout == 2 ? 2u : 0u);   // version 1 (layout 1 only) keeps 0 here
+    wr32(b + 20, md.layout == 1 ? 0u : md.layout);   // version 1 (layout 1 only) keeps 0 here
     uint32_t k = 0;
     for (uint32_t s = 0; s < 512; s++) {
         if (!md.counts_s[s]) continue;
         wr16(b + stab + 4 * k, s);
         wr16(b + stab + 4 * k + 2, md.q_s[s]);
         b[route_off + k] = (uint8_t)md.route[s];
+        // layout 3: the eight joint frequencies of s, in the order of the s list
+        if (md.layout == 3)
+            for (uint32_t h = 0; h < 8; h++) wr16(b + ftab + 16 * k + 2 * h, md.q_t[8 * s + h]);
         k++;
     }
     for (uint32_t t = 0; t < md.n_tables; t++) {
@@ -294,9 +312,9 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         return BS_E_FORMAT;
     }
     const uint32_t version = rd32(h + 8);
-    if (version != kVersion && version != kVersion2) {
-        set_error("container version %u is not supported (this library reads versions %u and %u)", version, kVersion,
-                  kVersion2);
+    if (version != kVersion && version != kVersion2 && version != kVersion3) {
+        set_error("container version %u is not supported (this library reads versions %u to %u)", version, kVersion,
+                  kVersion3);
         return BS_E_VERSION;
     }
     c.n_records = rd32(h + 12);
@@ -340,9 +358,13 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         r.m_f = b[13];
         r.n_tables = b[14];
         r.n_sym = rd32(b + 16);
-        // version 1: the word at +20 is 0 (layout 1); version 2: it names the layout
+        // version 1: the word at +20 is 0 (layout 1); versions 2 and 3 name
+        // the layout there (1 or 2; version 3 also 3)
         const uint32_t lw = rd32(b + 20);
-        if (version == kVersion ? lw != 0 : (lw != 1 && lw != 2)) { set_error("record %u: bad layout word %u", i, lw); return BS_E_FORMAT; }
+        if (version == kVersion ? lw != 0 : (lw < 1 || lw > (version == kVersion3 ? 3u : 2u))) {
+            set_error("record %u: bad layout word %u", i, lw);
+            return BS_E_FORMAT;
+        }
         r.layout = version == kVersion ? 1 : lw;
         const uint32_t K = r.K;
         if (b[15] > 9 || (1u << b[15]) > K) { set_error("record %u: bad stream count", i); return BS_E_FORMAT; }
@@ -352,8 +374,9 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
             set_error("record %u: bad chunk shape W=%u K=%u", i, r.W, K);
             return BS_E_FORMAT;
         }
-        if (r.layout == 1 ? (r.m_s < 9 || r.m_s > 12 || r.m_f < 8 || r.m_f > 10 || r.n_tables > kMaxTables)
-                          : (r.m_s < 11 || r.m_s > 12 || r.m_f != 16 - r.m_s || r.n_tables > kMaxHTables)) {
+        if (r.layout == 1   ? (r.m_s < 9 || r.m_s > 12 || r.m_f < 8 || r.m_f > 10 || r.n_tables > kMaxTables)
+            : r.layout == 2 ? (r.m_s < 11 || r.m_s > 12 || r.m_f != 16 - r.m_s || r.n_tables > kMaxHTables)
+                            : (r.m_s < 11 || r.m_s > 12 || r.m_f != kMt || r.n_tables != 0)) {
             set_error("record %u: bad table parameters", i);
             return BS_E_FORMAT;
         }
@@ -362,7 +385,7 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
         r.stab_off = 24;
         r.route_off = 24 + 4 * r.n_sym;
         r.ftab_off = (uint32_t)align_up(r.route_off + r.n_sym, 4);
-        r.index_off = align_up(r.ftab_off + (r.layout == 2 ? 8ull : 256ull) * r.n_tables, 16);
+        r.index_off = align_up(r.layout == 3 ? r.ftab_off + 16ull * r.n_sym : r.ftab_off + (r.layout == 2 ? 8ull : 256ull) * r.n_tables, 16);
         if (r.index_off + 16ull * r.n_chunks + 4ull * (r.S - 1) * r.n_chunks > r.rec_len) {
             set_error("record %u: chunk index or stream table out of bounds", i);
             return BS_E_FORMAT;
@@ -379,6 +402,11 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
             sum += q;
         }
         if (r.n_sym && sum != (1ull << r.m_s)) { set_error("record %u: sign/exponent frequencies do not sum to 2^%u", i, r.m_s); return BS_E_FORMAT; }
+        if (r.layout == 3) {
+            uint64_t ts = 0;
+            for (uint32_t k = 0; k < 8 * r.n_sym; k++) ts += rd16(b + r.ftab_off + 2 * k);
+            if (r.n_sym && ts != (1ull << kMt)) { set_error("record %u: joint frequencies do not sum to 2^%u", i, kMt); return BS_E_FORMAT; }
+        }
         for (uint32_t t = 0; t < r.n_tables; t++) {
             uint64_t fs = 0;
             if (r.layout == 2) {
@@ -394,9 +422,9 @@ bs_status parse_container(const uint8_t* h, uint64_t len, Container& c) {
             const uint8_t* e = b + r.index_off + 16ull * ch;
             const uint64_t po = rd64(e);
             const uint64_t total = rd32(e + 8);
-            // layout 2: the plane of low fraction bits sits between the codes and the streams
+            // layouts 2 and 3: the plane of low fraction bits sits between the codes and the streams
             const uint64_t n_c = std::min<uint64_t>(r.W, r.n - (uint64_t)ch * r.W);
-            const uint64_t cbytes = code_bytes(K) + (r.layout == 2 ? plane_bytes(n_c) : 0);
+            const uint64_t cbytes = code_bytes(K) + (r.layout >= 2 ? plane_bytes(n_c) : 0);
             // the payload (codes and stream area, padded to 16 bytes) within
             // the record; the streams' starts ascend within the area and each
             // stream holds at least its state bits
@@ -499,13 +527,13 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
             const uint32_t P = r.K / r.S;
             co.mu.resize(r.S);
             const uint16_t* wc = (const uint16_t*)r.data + c0;
-            if (r.em.layout == 2) {
+            if (r.em.layout >= 2) {
                 // the plane of low fraction bits, padded to 16 bytes
                 co.plane.assign(align_up((n_c + 7) / 8, 4), 0u);
                 for (uint32_t j = 0; j < n_c; j++) co.plane[j / 8] |= (wc[j] & 15u) << low_bit_pos(j % 8);
             }
             for (uint32_t st = 0; st < r.S; st++) {
-                const uint64_t nw = r.em.layout == 2
+                const uint64_t nw = r.em.layout >= 2
                                         ? encode_stream2(r.em, wc, n_c, r.K, st * P, (st + 1) * P, co.states.data(), buf.data())
                                         : encode_stream(r.em, wc, n_c, r.K, st * P, (st + 1) * P, co.states.data(), buf.data());
                 std::vector<uint16_t>& v = co.words[st];
@@ -551,7 +579,7 @@ bs_status bs_encode_host(const bs_tensor* tensors, uint32_t n_tensors, const bs_
         blob->bytes.assign(pos, 0);
         uint8_t* c = blob->bytes.data();
         memcpy(c, kMagic, 8);
-        wr32(c + 8, p->layout == 2 ? kVersion2 : kVersion);
+        wr32(c + 8, p->layout == 1 ? kVersion : p->layout == 2 ? kVersion2 : kVersion3);
         wr32(c + 12, n_tensors);
         wr64(c + 16, kHeaderBytes);
         wr64(c + 24, pos);
@@ -746,6 +774,10 @@ void fill_enc_tab(const bs::EncModel& em, bsd::EncTabDev& t) {
         t.s_qc[s] = em.s[s].q | em.s[s].cum << 16;
         t.route[s] = em.route[s];
     }
+    if (em.layout == 3) {
+        for (uint32_t k = 0; k < 512 * 8; k++) t.t_qc[k] = em.t[k].q | em.t[k].cum << 16;
+        return;
+    }
     if (em.layout == 2) {
         for (uint32_t k = 0; k <= bs::kMaxHTables; k++)
             for (uint32_t h = 0; h < 8; h++) t.h_qc[k * 8 + h] = em.h[k][h].q | em.h[k][h].cum << 16;
@@ -902,7 +934,7 @@ bs_status bs_encode_device_begin(const bs_dtensor* tensors, uint32_t n_tensors, 
                     wr32(r.head.data() + r.index_off + 16ull * ch + 8, (uint32_t)at);
                     r.chunk_off[ch] = len;
                     const uint64_t n_c = std::min<uint64_t>(r.W, r.n - (uint64_t)ch * r.W);
-                    len += align_up(code_bytes(r.K) + (r.em.layout == 2 ? plane_bytes(n_c) : 0) + 2 * at, 16);
+                    len += align_up(code_bytes(r.K) + (r.em.layout >= 2 ? plane_bytes(n_c) : 0) + 2 * at, 16);
                 }
             }
             r.rec_len = len;
@@ -916,7 +948,7 @@ bs_status bs_encode_device_begin(const bs_dtensor* tensors, uint32_t n_tensors, 
         e->top.assign(align_up(kHeaderBytes + kDirEntryBytes * n_tensors, 16), 0);
         uint8_t* c = e->top.data();
         memcpy(c, kMagic, 8);
-        wr32(c + 8, p->layout == 2 ? kVersion2 : kVersion);
+        wr32(c + 8, p->layout == 1 ? kVersion : p->layout == 2 ? kVersion2 : kVersion3);
         wr32(c + 12, n_tensors);
         wr64(c + 16, kHeaderBytes);
         wr64(c + 24, pos);

@@ -1,4 +1,4 @@
-// bs_decode2.hip -- the decode kernel (gfx950) for records of layout 2.
+// bs_decode2.hip -- the decode kernel (gfx950) for records of layouts 2 and 3.
 //
 // What is decoded [Qwen3.8-27B-BF16-NVLC-Lossless model card, codec
 // paragraph]: each BF16 word w = s << 7 | f; the joint (sign, exponent)
@@ -16,6 +16,10 @@
 // plane read one 32-bit word per lane and group, 128-bit output stores.  The
 // instances with V set are the fused matrix-vector product: each group of 8
 // decoded weights goes into a dot product with x instead of memory.
+//
+// Layout 3 (the instances with J set) decodes s and h as one joint symbol:
+// one table read and one step per weight instead of two, whose entry also
+// holds the output word's high twelve bits.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,29 +67,53 @@ __device__ __forceinline__ uint2 h_entry(const uint8_t* lds, uint2 e, uint32_t x
 // operands fit 24 bits
 __device__ __forceinline__ uint32_t h_step(uint32_t x, uint2 f) { return __umul24(x >> 8, f.x) + f.y; }
 
-// One group of 8 weights per lane group q, each the pair (s, h), with one
-// renormalisation per weight.  o receives the words' high twelve bits,
-// weight p at 16-bit half p of the four dwords.
-template <int R, uint32_t RW>
+// Layout 3: the joint entry of state x, at LDS address (x mod 2^13) * 8,
+// which is the low half of x << 3: one shift whose result keeps its low 16
+// bits (an ALU instruction only).
+__device__ __forceinline__ uint2 joint_entry(const uint8_t* lds, uint32_t x) {
+    uint32_t a;
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD"
+        : "=v"(a) : "v"(x));
+    return *(const uint2*)(lds + a);
+}
+
+// the joint step: q_t (x >> 13) + slot - cum_t
+__device__ __forceinline__ uint32_t joint_step(uint32_t x, uint2 e) { return __umul24(x >> kJointBits, e.x) + (e.y >> 16); }
+
+// One group of 8 weights per lane group q, each the pair (s, h) (J: the
+// joint symbol), with one renormalisation per weight.  o receives the words'
+// high twelve bits, weight p at 16-bit half p of the four dwords.
+template <int R, uint32_t RW, bool J>
 __device__ __forceinline__ void group_pairs(uint32_t (&x)[R], uint32_t (&o)[R][4], const uint8_t* lds, const Model2& md,
                                             Ring<RW>& g, uint32_t& pos, const bool (&all_on)[R]) {
 #pragma unroll
     for (int p = 0; p < 8; p++) {
         if (p % top_up_every(R, false) == 0) ring_top_up(g, pos);
-        uint2 e[R];
-#pragma unroll
-        for (int q = 0; q < R; q++) e[q] = s_entry(lds, x[q], md);
-#pragma unroll
-        for (int q = 0; q < R; q++) x[q] = s_step(x[q], e[q], md);
-        uint2 f[R];
-#pragma unroll
-        for (int q = 0; q < R; q++) f[q] = h_entry(lds, e[q], x[q]);
         uint32_t w[R];
+        if (J) {
+            uint2 e[R];
 #pragma unroll
-        for (int q = 0; q < R; q++) {
-            x[q] = h_step(x[q], f[q]);
-            // low half: (s << 7) | (f.x >> 25), and f.x >> 25 = h << 4
-            w[q] = __builtin_amdgcn_alignbit(e[q].y, f[q].x, 25);
+            for (int q = 0; q < R; q++) e[q] = joint_entry(lds, x[q]);
+#pragma unroll
+            for (int q = 0; q < R; q++) {
+                x[q] = joint_step(x[q], e[q]);
+                w[q] = e[q].y;   // low half: s << 7 | h << 4
+            }
+        } else {
+            uint2 e[R];
+#pragma unroll
+            for (int q = 0; q < R; q++) e[q] = s_entry(lds, x[q], md);
+#pragma unroll
+            for (int q = 0; q < R; q++) x[q] = s_step(x[q], e[q], md);
+            uint2 f[R];
+#pragma unroll
+            for (int q = 0; q < R; q++) f[q] = h_entry(lds, e[q], x[q]);
+#pragma unroll
+            for (int q = 0; q < R; q++) {
+                x[q] = h_step(x[q], f[q]);
+                // low half: (s << 7) | (f.x >> 25), and f.x >> 25 = h << 4
+                w[q] = __builtin_amdgcn_alignbit(e[q].y, f[q].x, 25);
+            }
         }
         refill_all<R, RW>(x, all_on, g, pos);
 #pragma unroll
@@ -113,9 +141,12 @@ __device__ __forceinline__ bool lane_bad(uint32_t x, bool has, uint32_t c) {
     return has ? ((x >> lead) != 1u || ((x - (1u << lead)) >> (3 * c)) != 0u) : x != kStateLow;
 }
 
-template <int R, bool V>
+template <int R, bool V, bool J>
 __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& r, const uint8_t* lds, Unit<R, false>& u,
                                              bool fair) {
+    // the s entries of the lanes' last groups: at 0 in layout 2, after the
+    // joint entries in layout 3
+    const uint8_t* lds_s = J ? lds + kJointBytes : lds;
     const uint32_t lane = threadIdx.x & 63;
     constexpr uint32_t RW = ring_words(R, false);
     Ring<RW>& g = u.g;
@@ -163,7 +194,7 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
         for (int q = 0; q < R; q++)
             dn[q] = __builtin_amdgcn_raw_buffer_load_b32(plane, 4 * ((t + 1) * K + LB + 64 * q + lane), 0, 0);
         uint32_t o[R][4];
-        group_pairs<R, RW>(x, o, lds, md, g, pos, all_on);
+        group_pairs<R, RW, J>(x, o, lds, md, g, pos, all_on);
 #pragma unroll
         for (int q = 0; q < R; q++) {
             add_low_bits(o[q], d[q]);
@@ -188,7 +219,7 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
             if (p % top_up_every(R, false) == 0) ring_top_up(g, pos);
             uint2 e[R];
 #pragma unroll
-            for (int q = 0; q < R; q++) e[q] = s_entry(lds, x[q], md);
+            for (int q = 0; q < R; q++) e[q] = s_entry(lds_s, x[q], md);
 #pragma unroll
             for (int q = 0; q < R; q++) x[q] = s_step(x[q], e[q], md);
             refill_all<R, RW>(x, all_on, g, pos);
@@ -253,12 +284,20 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
             for (int q = 0; q < R; q++) {
                 act[q] = p < cnt[q];
                 uint32_t xs = x[q];
-                const uint2 e = s_entry(lds, xs, md);
+                const uint2 e = s_entry(lds_s, xs, md);
                 xs = s_step(xs, e, md);
-                uint32_t xh = xs;
-                const uint2 f = h_entry(lds, e, xh);
-                xh = h_step(xh, f);
-                const uint32_t w = fin[q] ? e.y << 7 : __builtin_amdgcn_alignbit(e.y, f.x, 25);
+                uint32_t xh, wh;
+                if (J) {
+                    const uint2 ej = joint_entry(lds, x[q]);
+                    xh = joint_step(x[q], ej);
+                    wh = ej.y;
+                } else {
+                    xh = xs;
+                    const uint2 f = h_entry(lds, e, xh);
+                    xh = h_step(xh, f);
+                    wh = __builtin_amdgcn_alignbit(e.y, f.x, 25);
+                }
+                const uint32_t w = fin[q] ? e.y << 7 : wh;
                 if (act[q]) x[q] = fin[q] ? xs : xh;
                 // shift the 128-bit register right by 16 and insert w on top
                 o[q][0] = __builtin_amdgcn_alignbit(o[q][1], o[q][0], 16);
@@ -308,12 +347,12 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
 // before a wave opens its first unit, so that the two overlap.
 constexpr int kStage2 = 8;
 
-template <int R, bool V>
+template <int R, bool V, bool J>
 __device__ __forceinline__ void run_units2(const DecodeArgs& a, const RecDev& r, uint32_t u0, uint32_t u1, uint32_t wave,
                                            uint8_t* lds) {
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
     const v4u* src = (const v4u*)(a.luts + r.lut_off);
-    const uint32_t rb = l2_ring_base(r.m_s, r.n_tables);
+    const uint32_t rb = J ? l3_ring_base(r.m_s) : l2_ring_base(r.m_s, r.n_tables);
     const uint32_t n16 = rb / 16;
     const uint32_t step = kStage2 * blockDim.x;
     v4u* dst = (v4u*)lds;
@@ -347,22 +386,22 @@ __device__ __forceinline__ void run_units2(const DecodeArgs& a, const RecDev& r,
     __syncthreads();
     for (; u < u1; u += a.waves) {
         if (u != u0 + wave) unit_open<R, false, true>(a, r, u, wave, lds, rb, un);
-        unit_decode2<R, V>(a, r, lds, un, u1 - u0 <= a.waves);
+        unit_decode2<R, V, J>(a, r, lds, un, u1 - u0 <= a.waves);
     }
 }
 
-template <int G, bool V>
+template <int G, bool V, bool J>
 __device__ __forceinline__ void run_record2(const DecodeArgs& a, const RecDev& r, uint32_t u0, uint32_t wave, uint8_t* lds) {
     const uint32_t u1 = min(r.n_chunks << r.streams_log2, u0 + a.run);
     if (G == 1 || G == 2 || G == 4) {
         constexpr int R = (G == 1 || G == 2 || G == 4) ? G : 1;
-        run_units2<R, V>(a, r, u0, u1, wave, lds);
+        run_units2<R, V, J>(a, r, u0, u1, wave, lds);
     } else if (r.lanes_per_thread == 1) {
-        run_units2<1, V>(a, r, u0, u1, wave, lds);
+        run_units2<1, V, J>(a, r, u0, u1, wave, lds);
     } else if (G == 0 || r.lanes_per_thread == 2) {
-        run_units2<2, V>(a, r, u0, u1, wave, lds);
+        run_units2<2, V, J>(a, r, u0, u1, wave, lds);
     } else {
-        run_units2<4, V>(a, r, u0, u1, wave, lds);
+        run_units2<4, V, J>(a, r, u0, u1, wave, lds);
     }
 }
 
@@ -370,9 +409,9 @@ __device__ __forceinline__ void run_record2(const DecodeArgs& a, const RecDev& r
 // kernel does (record lookup by a prefix sum over the records' run counts
 // when the launch has several).  G: the lanes per thread of every record
 // (1, 2 or 4), 0 for a mix of 1 and 2, 3 for a mix that includes 4.  V:
-// the fused product (one record, G = 1, 2 or 4).
-template <int G, bool V = false>
-__global__ __launch_bounds__(1024) void decode2_kernel(const DecodeArgs a) {
+// the fused product (one record, G = 1, 2 or 4).  J: layout-3 records.
+template <int G, bool V, bool J>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     __shared__ __align__(16) uint8_t lds[kLds2];
     __shared__ uint32_t pick[2];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -380,7 +419,7 @@ __global__ __launch_bounds__(1024) void decode2_kernel(const DecodeArgs a) {
     if (a.i1 - a.i0 == 1) {
         const uint32_t u0 = b * a.run;
         if (u0 >= (a.one.n_chunks << a.one.streams_log2)) return;
-        run_record2<G, V>(a, a.one, u0, wave, lds);
+        run_record2<G, V, J>(a, a.one, u0, wave, lds);
         return;
     }
     if (wave == 0) {
@@ -407,30 +446,44 @@ __global__ __launch_bounds__(1024) void decode2_kernel(const DecodeArgs a) {
     const uint32_t e = __builtin_amdgcn_readfirstlane(pick[0]);
     if (e == UINT32_MAX) return;
     const RecDev r = a.recs[a.cls.recs[e]];
-    run_record2<G, V>(a, r, __builtin_amdgcn_readfirstlane(pick[1]) * a.run, wave, lds);
+    run_record2<G, V, J>(a, r, __builtin_amdgcn_readfirstlane(pick[1]) * a.run, wave, lds);
 }
 
-}  // namespace
+// the kernels: layout 2 (decode2_kernel) and layout 3 (decode3_kernel)
+template <int G, bool V = false>
+__global__ __launch_bounds__(1024) void decode2_kernel(const DecodeArgs a) { decode_body<G, V, false>(a); }
 
-extern "C" {
+template <int G, bool V = false>
+__global__ __launch_bounds__(1024) void decode3_kernel(const DecodeArgs a) { decode_body<G, V, true>(a); }
 
-int bsk_decode2(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream) {
+// the decode of a launch's records (J: layout 3) with the instance for its
+// lanes per thread
+template <int G, bool V, bool J>
+void launch_one(dim3 grid, dim3 block, hipStream_t st, const DecodeArgs* args) {
+    if (J) hipLaunchKernelGGL((decode3_kernel<G, V>), grid, block, 0, st, *args);
+    else hipLaunchKernelGGL((decode2_kernel<G, V>), grid, block, 0, st, *args);
+}
+
+template <bool J>
+int launch_decode2(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream) {
     if (n_groups == 0) return 0;
     const dim3 grid(n_groups), block(64 * args->waves);
     hipStream_t st = (hipStream_t)stream;
     if (args->waves == 0 || args->waves > 16) return (int)hipErrorInvalidValue;
     switch (variant) {
-        case 0: hipLaunchKernelGGL((decode2_kernel<0>), grid, block, 0, st, *args); break;
-        case 3: hipLaunchKernelGGL((decode2_kernel<3>), grid, block, 0, st, *args); break;
-        case 1: hipLaunchKernelGGL((decode2_kernel<1>), grid, block, 0, st, *args); break;
-        case 2: hipLaunchKernelGGL((decode2_kernel<2>), grid, block, 0, st, *args); break;
-        case 4: hipLaunchKernelGGL((decode2_kernel<4>), grid, block, 0, st, *args); break;
+        case 0: launch_one<0, false, J>(grid, block, st, args); break;
+        case 3: launch_one<3, false, J>(grid, block, st, args); break;
+        case 1: launch_one<1, false, J>(grid, block, st, args); break;
+        case 2: launch_one<2, false, J>(grid, block, st, args); break;
+        case 4: launch_one<4, false, J>(grid, block, st, args); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
 }
 
-int bsk_gemv2(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream) {
+// the fused product of one record: y zeroed, then the decode with V set
+template <bool J>
+int launch_gemv2(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream) {
     hipStream_t st = (hipStream_t)stream;
     if (rows) {
         const int e = bsk_zero_f32(args->gy, rows, stream);
@@ -440,12 +493,32 @@ int bsk_gemv2(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint6
     const dim3 grid(n_groups), block(64 * args->waves);
     if (args->waves == 0 || args->waves > 16) return (int)hipErrorInvalidValue;
     switch (variant) {
-        case 1: hipLaunchKernelGGL((decode2_kernel<1, true>), grid, block, 0, st, *args); break;
-        case 2: hipLaunchKernelGGL((decode2_kernel<2, true>), grid, block, 0, st, *args); break;
-        case 4: hipLaunchKernelGGL((decode2_kernel<4, true>), grid, block, 0, st, *args); break;
+        case 1: launch_one<1, true, J>(grid, block, st, args); break;
+        case 2: launch_one<2, true, J>(grid, block, st, args); break;
+        case 4: launch_one<4, true, J>(grid, block, st, args); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsk_decode2(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream) {
+    return launch_decode2<false>(args, n_groups, variant, stream);
+}
+
+int bsk_decode3(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream) {
+    return launch_decode2<true>(args, n_groups, variant, stream);
+}
+
+int bsk_gemv2(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream) {
+    return launch_gemv2<false>(args, n_groups, variant, rows, stream);
+}
+
+int bsk_gemv3(const DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream) {
+    return launch_gemv2<true>(args, n_groups, variant, rows, stream);
 }
 
 }  // extern "C"

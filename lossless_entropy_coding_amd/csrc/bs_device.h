@@ -69,6 +69,22 @@ constexpr uint32_t l2_max_waves(uint32_t ring_base) {
 static_assert(l2_max_waves(l2_ring_base(12, kMaxHTablesDev)) == 15 && l2_max_waves(l2_ring_base(11, kMaxHTablesDev)) == 16,
               "layout-2 workgroup sizes");
 
+// Layout-3 lookup-table image (LDS of a workgroup, in this order):
+//   joint part at 0: 2^13 x 8-byte entries, entry i for state slot i (the
+//     state's low 13 bits) of the joint symbol t = 8 s + h with
+//     cum_t <= i < cum_t + q_t:
+//       {A = q_t, B = (s << 7 | h << 4) | (i - cum_t) << 16}
+//     so one step is x -> q_t (x >> 13) + (B >> 16), and the low half of B is
+//     the output word's high twelve bits; its address (x mod 2^13) * 8 is the
+//     low 16 bits of x << 3.
+//   s part at 65536: 2^M_s entries {q_s, s | (slot - cum_s) << 16} for the
+//     lanes' last groups (s alone), as layout 2's s part without a page;
+//   the waves' stream rings after it.
+constexpr uint32_t kJointBits = 13;
+constexpr uint32_t kJointBytes = 8u << kJointBits;
+constexpr uint32_t l3_ring_base(uint32_t m_s) { return kJointBytes + (8u << m_s); }
+static_assert(l2_max_waves(l3_ring_base(11)) == 16 && l2_max_waves(l3_ring_base(12)) == 15, "layout-3 workgroup sizes");
+
 // Device lookup-table image of one record (built once per plan):
 //   s part: 2^M_s x {A, B}
 //     A = q_s | (page << 24), page = LDS address of the routed fraction table >> 11
@@ -95,7 +111,8 @@ struct RecDev {
     uint32_t stab_off;      // byte offset (from body) of the s-table
     uint32_t route_off;     // byte offset (from body) of the route bytes
     uint32_t ftab_off;      // byte offset (from body) of the fraction tables (layout 2: the h tables)
-    uint32_t layout;        // 1, or 2: s and h = f >> 4 coded (m_f holds M_h), l = f & 15 in a plane
+    uint32_t layout;        // 1; 2: s and h = f >> 4 coded (m_f holds M_h), l = f & 15 in a plane;
+                            // 3: as 2 with s and h one joint symbol (m_f holds M_t = 13)
 };
 
 // One launch class of a plan (lanes per thread 1, 2 or 4; or 8): its BF16 records in container order
@@ -136,8 +153,9 @@ struct DecodeArgs {
 
 // Launchers (bs_kernels.hip).  All return a hipError_t as int.
 extern "C" {
-// d_cf: 256 x 128 counters (exponent, fraction; both signs), d_cneg: 256
-// counters (negative words per exponent); both zeroed by the caller
+// d_cf: 256 x 128 counters (exponent, fraction; both signs), d_cneg: 256 x 8
+// counters (negative words per exponent e and high fraction bits h, at
+// 8 e + h); both zeroed by the caller
 int bsk_hist(const uint16_t* d_w, uint64_t n, unsigned long long* d_cf, unsigned long long* d_cneg, void* stream);
 int bsk_build_luts(const uint8_t* d_container, const bsd::RecDev* d_recs, uint32_t n_recs, uint8_t* d_luts,
                    void* stream);
@@ -148,10 +166,13 @@ int bsk_decode(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant,
 // layout-2 records: variant 1, 2 or 4 (every record of the launch has that
 // many lanes per thread), 0 (a mix of 1 and 2) or 3 (a mix with 4)
 int bsk_decode2(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream);
+// the same for layout-3 records
+int bsk_decode3(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, void* stream);
 // the fused matrix-vector product of one record (full layout, variant 1, 2 or 4), y zeroed first
 int bsk_gemv(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream);
-// the same for a layout-2 record
+// the same for a layout-2 record, and for a layout-3 record
 int bsk_gemv2(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream);
+int bsk_gemv3(const bsd::DecodeArgs* args, uint32_t n_groups, uint32_t variant, uint64_t rows, void* stream);
 // fill n floats at y with 0 (a kernel, so that the work stays capturable)
 int bsk_zero_f32(float* y, uint64_t n, void* stream);
 int bsk_raw_copy(const uint8_t* d_container, const bsd::RawDev* d_raw, uint32_t n_raw, uint8_t* d_out,

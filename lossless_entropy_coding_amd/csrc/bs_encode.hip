@@ -167,19 +167,37 @@ __device__ __forceinline__ void put_weight2(bool act, bool pair, uint32_t& x, ui
     }
 }
 
-// Layout 2: one wavefront per word stream, one sub-step per weight, run
-// backwards.  A lane's start state carries the h of its last group's c
-// weights (the low 3c bits under a leading one at bit max(16, 3c)).
-template <int R>
+// Layout 3: the same sub-step, with the joint symbol 8 s + h outside the
+// last group (one flush check against q_t 2^(32 - 13), one coding step).
+__device__ __forceinline__ void put_weight3(bool act, bool joint, uint32_t& x, uint32_t sqc, uint32_t tqc, uint32_t m_s,
+                                           uint16_t* sink, uint32_t& base, uint32_t lane) {
+    const uint32_t q = joint ? tqc & 0xFFFFu : sqc & 0xFFFFu, cum = joint ? tqc >> 16 : sqc >> 16;
+    const uint32_t m = joint ? kJointBits : m_s;
+    const bool flush = act && (x >> (32 - m)) >= q;
+    const uint64_t b = __builtin_amdgcn_ballot_w64(flush);
+    if (flush) {
+        const uint32_t above = (uint32_t)__builtin_popcountll(lane == 63 ? 0ull : b >> (lane + 1));
+        sink[base + above] = (uint16_t)x;
+        x >>= 16;
+    }
+    base += (uint32_t)__builtin_popcountll(b);
+    if (act) x = ((x / q) << m) + x % q + cum;
+}
+
+// Layouts 2 and 3 (J): one wavefront per word stream, one sub-step per
+// weight, run backwards.  A lane's start state carries the h of its last
+// group's c weights (the low 3c bits under a leading one at bit max(16, 3c)).
+template <int R, bool J>
 __global__ __launch_bounds__(64 * kEncWaves) void encode2_kernel(EncArgs a) {
+    constexpr uint32_t NH = J ? 512 * 8 : (kMaxHTablesDev + 1) * 8;
     __shared__ uint32_t s_qc[512];
-    __shared__ uint32_t h_qc[(kMaxHTablesDev + 1) * 8];
+    __shared__ uint32_t h_qc[NH];   // J: the joint table's q | cum << 16
     __shared__ uint8_t route[512];
     for (uint32_t i = threadIdx.x; i < 512; i += 64 * kEncWaves) {
         s_qc[i] = a.tab->s_qc[i];
         route[i] = a.tab->route[i];
     }
-    for (uint32_t i = threadIdx.x; i < (kMaxHTablesDev + 1) * 8; i += 64 * kEncWaves) h_qc[i] = a.tab->h_qc[i];
+    for (uint32_t i = threadIdx.x; i < NH; i += 64 * kEncWaves) h_qc[i] = J ? a.tab->t_qc[i] : a.tab->h_qc[i];
     __syncthreads();
 
     const uint32_t lane = threadIdx.x & 63u;
@@ -234,8 +252,12 @@ __global__ __launch_bounds__(64 * kEncWaves) void encode2_kernel(EncArgs a) {
                 const uint32_t j = 8 * g[q] + p;
                 const bool act = lv[q] && j < n_c;
                 const uint32_t v = (gw[q][p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
-                put_weight2(act, g[q] != glast[q], x[q], s_qc[v >> 7], h_qc[route[v >> 7] * 8u + ((v & 127u) >> 4)],
-                            a.m_s, a.m_f, sink, base, lane);
+                if (J)
+                    put_weight3(act, g[q] != glast[q], x[q], s_qc[v >> 7], h_qc[8u * (v >> 7) + ((v & 127u) >> 4)], a.m_s,
+                                sink, base, lane);
+                else
+                    put_weight2(act, g[q] != glast[q], x[q], s_qc[v >> 7], h_qc[route[v >> 7] * 8u + ((v & 127u) >> 4)],
+                                a.m_s, a.m_f, sink, base, lane);
             }
         }
     }
@@ -273,8 +295,8 @@ __global__ __launch_bounds__(64 * kEncWaves) void assemble_kernel(EncArgs a) {
     }
     const uint64_t code_bytes = ((K + 1ull) / 2 + 15) / 16 * 16;
     uint64_t plane = 0;
-    if (a.layout == 2) {
-        // layout 2: the plane of low fraction bits between the codes and the
+    if (a.layout >= 2) {
+        // layouts 2 and 3: the plane of low fraction bits between the codes and the
         // streams; this stream's wave writes its lanes' groups (position p of
         // a group at bit 16 (p mod 2) + 4 (p div 2) of the group's word)
         const uint64_t c0 = (uint64_t)c * a.W;
@@ -341,11 +363,15 @@ int bsk_encode(const EncArgs* args, uint32_t R, void* stream) {
     if (units == 0) return 0;
     const dim3 grid((uint32_t)((units + kEncWaves - 1) / kEncWaves)), block(64 * kEncWaves);
     hipStream_t st = (hipStream_t)stream;
-    if (args->layout == 2) {
-        switch (R) {
-            case 1: hipLaunchKernelGGL(encode2_kernel<1>, grid, block, 0, st, *args); break;
-            case 2: hipLaunchKernelGGL(encode2_kernel<2>, grid, block, 0, st, *args); break;
-            case 4: hipLaunchKernelGGL(encode2_kernel<4>, grid, block, 0, st, *args); break;
+    if (args->layout == 2 || args->layout == 3) {
+        const uint32_t v = R | (args->layout == 3 ? 8u : 0u);
+        switch (v) {
+            case 1: hipLaunchKernelGGL((encode2_kernel<1, false>), grid, block, 0, st, *args); break;
+            case 2: hipLaunchKernelGGL((encode2_kernel<2, false>), grid, block, 0, st, *args); break;
+            case 4: hipLaunchKernelGGL((encode2_kernel<4, false>), grid, block, 0, st, *args); break;
+            case 9: hipLaunchKernelGGL((encode2_kernel<1, true>), grid, block, 0, st, *args); break;
+            case 10: hipLaunchKernelGGL((encode2_kernel<2, true>), grid, block, 0, st, *args); break;
+            case 12: hipLaunchKernelGGL((encode2_kernel<4, true>), grid, block, 0, st, *args); break;
             default: return (int)hipErrorInvalidValue;
         }
         return (int)hipGetLastError();

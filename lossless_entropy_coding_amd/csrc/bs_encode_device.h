@@ -15,6 +15,7 @@ struct EncTabDev {
     uint32_t f_qc[(kMaxTables + 1) * 128];
     uint8_t route[512];
     uint32_t h_qc[(kMaxHTablesDev + 1) * 8];   // layout 2: q | cum << 16 of each h table (0 = flat) and h
+    uint32_t t_qc[512 * 8];                    // layout 3: q | cum << 16 of the joint symbol 8 s + h
 };
 
 // One BF16 record to encode: its chunks' streams (chunk c, stream st = unit

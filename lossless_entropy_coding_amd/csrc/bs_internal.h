@@ -16,12 +16,14 @@ namespace bs {
 constexpr char kMagic[8] = {'B', 'F', '1', '6', 'R', 'A', 'N', 'S'};
 constexpr uint32_t kVersion = 1;           // containers of layout-1 records
 constexpr uint32_t kVersion2 = 2;          // containers that name each record's layout (1 or 2)
+constexpr uint32_t kVersion3 = 3;          // the same with layout 3 allowed (1, 2 or 3)
 constexpr uint64_t kHeaderBytes = 64;
 constexpr uint64_t kDirEntryBytes = 96;
 constexpr uint64_t kOutAlign = 256;
 constexpr uint32_t kCandidates = 64;        // exponents whose fraction counts are gathered
 constexpr uint32_t kMaxTables = 6;
 constexpr uint32_t kMaxHTables = 31;       // coded h tables of a layout-2 record
+constexpr uint32_t kMt = 13;               // precision of a layout-3 record's joint (s, h) table
 constexpr uint32_t kMaxSyms = 256;
 
 void set_error(const char* fmt, ...);

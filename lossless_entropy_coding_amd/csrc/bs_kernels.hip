@@ -28,12 +28,14 @@ constexpr int kHistThreads = 1024;
 
 // One pass over the words of a tensor.  cf[e * 128 + f] counts exponent e and
 // fraction f over both signs (the sign-merged fraction counts that the choice
-// of coded contexts needs), and cneg[e] counts the negative words of exponent
-// e, from which the sign split of the (sign, exponent) histogram follows:
-// cs[256 + e] = cneg[e], cs[e] = sum_f cf[e][f] - cneg[e].  The counters are
-// privatised in LDS per workgroup (128 KiB + 8 KiB); the negative counts are
-// spread over 8 sub-bins by f mod 8, because a tensor's exponents concentrate
-// on a few values and same-address LDS atomics serialise.
+// of coded contexts needs), and cneg[8 e + h] counts the negative words of
+// exponent e whose fraction has high three bits h, from which the sign split
+// follows: the (sign, exponent) counts cs[256 + e] = sum_h cneg[8 e + h],
+// cs[e] = sum_f cf[e][f] - cs[256 + e], and the joint (sign, exponent, h)
+// counts of layout 3.  The counters are privatised in LDS per workgroup
+// (128 KiB + 8 KiB); keyed by h, the negative counts of one exponent also
+// fall in 8 bins, because a tensor's exponents concentrate on a few values
+// and same-address LDS atomics serialise.
 __global__ __launch_bounds__(kHistThreads) void hist_kernel(const uint16_t* __restrict__ w, uint64_t n,
                                                              unsigned long long* __restrict__ cf,
                                                              unsigned long long* __restrict__ cneg) {
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(kHistThreads) void hist_kernel(const uint16_t* __re
         for (int k = 0; k < 8; k++) {
             const uint32_t x = (d[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
             atomicAdd(&hb[x & 0x7FFFu], 1u);
-            if (x & 0x8000u) atomicAdd(&hn[((x >> 4) & 0x7F8u) | (x & 7u)], 1u);
+            if (x & 0x8000u) atomicAdd(&hn[(x >> 4) & 0x7FFu], 1u);
         }
     }
     const uint64_t rest0 = head + body * 8;
@@ -65,16 +67,13 @@ __global__ __launch_bounds__(kHistThreads) void hist_kernel(const uint16_t* __re
         const uint64_t j = i < head ? i : rest0 + (i - head);
         const uint32_t x = w[j];
         atomicAdd(&hb[x & 0x7FFFu], 1u);
-        if (x & 0x8000u) atomicAdd(&hn[((x >> 4) & 0x7F8u) | (x & 7u)], 1u);
+        if (x & 0x8000u) atomicAdd(&hn[(x >> 4) & 0x7FFu], 1u);
     }
     __syncthreads();
     for (uint32_t b = threadIdx.x; b < 256 * 128; b += blockDim.x)
         if (hb[b]) atomicAdd(&cf[b], (unsigned long long)hb[b]);
-    for (uint32_t e = threadIdx.x; e < 256; e += blockDim.x) {
-        uint32_t t = 0;
-        for (int k = 0; k < 8; k++) t += hn[e * 8 + k];
-        if (t) atomicAdd(&cneg[e], (unsigned long long)t);
-    }
+    for (uint32_t b = threadIdx.x; b < 256 * 8; b += blockDim.x)
+        if (hn[b]) atomicAdd(&cneg[b], (unsigned long long)hn[b]);
 }
 
 // ------------------------------------------------------------------ lookup tables
@@ -107,6 +106,37 @@ __global__ __launch_bounds__(256) void lut_kernel(const uint8_t* __restrict__ c,
         route[s] = body[r.route_off + k];
     }
     const uint32_t nt = r.n_tables + 1;
+    if (r.layout == 3) {
+        // layout 3 (image layout with kJointBytes): the joint (s, h) entries,
+        // then the s entries of the lanes' last groups
+        __shared__ uint32_t cumt[512 * 8];
+        __shared__ uint32_t qtl[512 * 8];
+        for (uint32_t i = threadIdx.x; i < 512 * 8; i += blockDim.x) qtl[i] = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < 8 * r.n_sym; i += blockDim.x) {
+            const uint32_t k = i / 8, h = i % 8;
+            qtl[8 * ld16(body + r.stab_off + 4 * k) + h] = ld16(body + r.ftab_off + 2 * i);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t a = 0;
+            for (int s = 0; s < 512; s++) { cums[s] = a; a += qs[s]; }
+            a = 0;
+            for (int t = 0; t < 512 * 8; t++) { cumt[t] = a; a += qtl[t]; }
+        }
+        __syncthreads();
+        uint2* jo = (uint2*)(luts + r.lut_off);
+        for (uint32_t i = threadIdx.x; i < (1u << kJointBits); i += blockDim.x) {
+            const uint32_t t = last_le(cumt, 512 * 8, i);
+            jo[i] = make_uint2(qtl[t], ((t >> 3) << 7 | (t & 7u) << 4) | (i - cumt[t]) << 16);
+        }
+        uint2* so = (uint2*)(luts + r.lut_off + kJointBytes);
+        for (uint32_t slot = threadIdx.x; slot < (1u << r.m_s); slot += blockDim.x) {
+            const uint32_t s = last_le(cums, 512, slot);
+            so[slot] = make_uint2(qs[s], s | (slot - cums[s]) << 16);
+        }
+        return;
+    }
     if (r.layout == 2) {
         // layout 2 (the image layout is described with kHPageBytes): 8-byte s
         // entries, then 2 KiB h pages indexed by 8 state bits; page 0 is

@@ -72,8 +72,17 @@ bool params_ok(const bs_params* p) {
             set_error("layout 2 decodes with at most 256 lanes per word stream: set stream_lanes");
             return false;
         }
+    } else if (p->layout == 3) {
+        if (p->m_s < 11 || p->m_s > 12 || p->m_f != kMt) {
+            set_error("layout 3 needs m_s 11 or 12 and m_f = %u (the joint table's precision)", kMt);
+            return false;
+        }
+        if ((p->stream_lanes ? p->stream_lanes : K) > 256) {
+            set_error("layout 3 decodes with at most 256 lanes per word stream: set stream_lanes");
+            return false;
+        }
     } else {
-        set_error("layout must be 1 or 2 (got %u)", p->layout);
+        set_error("layout must be 1, 2 or 3 (got %u)", p->layout);
         return false;
     }
     return true;
@@ -95,10 +104,11 @@ bool quantise(const uint64_t* counts, uint32_t A, uint32_t M, uint32_t* q) {
         occupied += counts[i] != 0;
     }
     if (n == 0 || occupied > total) return false;
-    // (fixed-size working arrays: the model is built without heap memory)
+    // (fixed-size working arrays: the model is built without heap memory;
+    // the largest alphabet is layout 3's 512 x 8 joint symbols)
     struct Rem { uint64_t rem; uint32_t idx; };
-    if (A > 512) return false;
-    Rem rems[512];
+    if (A > 512 * 8) return false;
+    Rem rems[512 * 8];
     uint32_t n_rem = 0;
     int64_t have = 0;
     for (uint32_t i = 0; i < A; i++) {
@@ -223,8 +233,10 @@ uint32_t candidates(const uint64_t exp_counts[256], uint32_t* es) {
     return n;
 }
 
+// ct: the joint (sign, exponent, h) counts of layout 3 at 8 s + h (unused otherwise)
 bool finish_model(Model& md, const bs_params* p, const uint32_t* cand, uint32_t n_cand,
-                  const std::array<uint64_t, 128>* merged, const std::array<std::array<uint64_t, 8>, 256>& hc) {
+                  const std::array<uint64_t, 128>* merged, const std::array<std::array<uint64_t, 8>, 256>& hc,
+                  const uint64_t* ct) {
     md.m_s = p->m_s;
     md.m_f = p->m_f;
     md.layout = p->layout;
@@ -242,6 +254,13 @@ bool finish_model(Model& md, const bs_params* p, const uint32_t* cand, uint32_t 
         choose_htables(hc, md.m_f, p->max_tables, md);
         return true;
     }
+    if (md.layout == 3) {
+        if (!quantise(ct, 512 * 8, kMt, md.q_t.data())) {
+            set_error("cannot quantise the joint (sign, exponent, h) counts");
+            return false;
+        }
+        return true;
+    }
     uint64_t ec[256];
     for (uint32_t e = 0; e < 256; e++) ec[e] = md.counts_s[e] + md.counts_s[256 + e];
     choose_contexts(ec, cand, n_cand, merged, md.m_f, p->max_tables, md);
@@ -249,25 +268,35 @@ bool finish_model(Model& md, const bs_params* p, const uint32_t* cand, uint32_t 
 }
 
 // The model of n words from the device histogram's counters: cnt[e * 128 +
-// f] counts exponent e and fraction f over both signs, cnt[256 * 128 + e]
-// the negative words of exponent e.  md is overwritten; merged is working
-// memory for kCandidates fraction histograms.  Allocates nothing.
+// f] counts exponent e and fraction f over both signs, cnt[256 * 128 + 8 e +
+// h] the negative words of exponent e with high fraction bits h.  md is
+// overwritten; merged is working memory for kCandidates fraction histograms,
+// ct for the 4096 joint counts.  Allocates nothing.
 bs_status model_from_counts(Model& md, const bs_params* p, uint64_t n, const unsigned long long* cnt,
-                            std::array<uint64_t, 128>* merged) {
+                            std::array<uint64_t, 128>* merged, uint64_t* ct) {
     md = Model{};
     md.n = n;
     uint32_t cand[kCandidates];
     uint32_t n_cand = 0;
     std::array<std::array<uint64_t, 8>, 256> hc{};
+    for (uint32_t t = 0; t < 512 * 8; t++) ct[t] = 0;
     if (n) {
-        // the (sign, exponent) counts: negatives counted directly, positives
-        // as the exponent's total minus its negatives
+        // the (sign, exponent, h) counts: negatives counted directly,
+        // positives as the sign-merged count minus the negatives; the
+        // (sign, exponent) counts are their sums over h
         uint64_t ec[256], sum = 0;
         for (uint32_t x = 0; x < 256; x++) {
-            uint64_t tot = 0;
-            for (uint32_t f = 0; f < 128; f++) tot += cnt[x * 128 + f];
-            const uint64_t neg = cnt[256 * 128 + x];
-            if (neg > tot) { set_error("histogram counts are inconsistent"); return BS_E_HIP; }
+            uint64_t tot = 0, neg = 0;
+            for (uint32_t h = 0; h < 8; h++) {
+                uint64_t both = 0;
+                for (uint32_t f = 16 * h; f < 16 * h + 16; f++) both += cnt[x * 128 + f];
+                const uint64_t nh = cnt[256 * 128 + 8 * x + h];
+                if (nh > both) { set_error("histogram counts are inconsistent"); return BS_E_HIP; }
+                ct[8 * (256 + x) + h] = nh;
+                ct[8 * x + h] = both - nh;
+                tot += both;
+                neg += nh;
+            }
             md.counts_s[256 + x] = neg;
             md.counts_s[x] = tot - neg;
             ec[x] = tot;
@@ -280,7 +309,7 @@ bs_status model_from_counts(Model& md, const bs_params* p, uint64_t n, const uns
         for (uint32_t x = 0; x < 256; x++)
             for (uint32_t f = 0; f < 128; f++) hc[x][f >> 4] += cnt[x * 128 + f];
     }
-    return finish_model(md, p, cand, n_cand, merged, hc) ? BS_OK : BS_E_INVAL;
+    return finish_model(md, p, cand, n_cand, merged, hc, ct) ? BS_OK : BS_E_INVAL;
 }
 
 }  // namespace bs
@@ -326,7 +355,10 @@ bs_status bs_build_tables_host(const uint16_t* h, uint64_t n, const bs_params* p
     std::array<std::array<uint64_t, 8>, 256> hc{};
     for (uint32_t e = 0; e < 256; e++)
         for (uint32_t f = 0; f < 128; f++) hc[e][f >> 4] += cf[(e << 7) | f] + cf[((256 + e) << 7) | f];
-    if (!finish_model(*t, p, cand, n_cand, merged.data(), hc)) { delete t; return BS_E_INVAL; }
+    std::vector<uint64_t> ct(512 * 8, 0);   // joint (s, h) counts: fraction counts summed over the low four bits
+    for (uint32_t s = 0; s < 512; s++)
+        for (uint32_t f = 0; f < 128; f++) ct[8 * s + (f >> 4)] += cf[(s << 7) | f];
+    if (!finish_model(*t, p, cand, n_cand, merged.data(), hc, ct.data())) { delete t; return BS_E_INVAL; }
     *out = t;
     return BS_OK;
 }
@@ -342,6 +374,7 @@ bs_status bs_build_tables(const void* d_bf16, uint64_t n, const bs_params* p, vo
     unsigned long long* d_cnt = nullptr;   // kHistCounters: see model_from_counts
     std::vector<unsigned long long> cnt(kHistCounters, 0);
     std::vector<std::array<uint64_t, 128>> merged(kCandidates);
+    std::vector<uint64_t> ct(512 * 8);
     bs_status rc = BS_OK;
     hipError_t e = hipMalloc(&d_cnt, kHistCounters * sizeof(unsigned long long));
     if (e == hipSuccess && n) {
@@ -354,7 +387,7 @@ bs_status bs_build_tables(const void* d_bf16, uint64_t n, const bs_params* p, vo
         set_error("histogram: %s", hipGetErrorString(e));
         rc = BS_E_HIP;
     } else {
-        rc = model_from_counts(*t, p, n, cnt.data(), merged.data());
+        rc = model_from_counts(*t, p, n, cnt.data(), merged.data(), ct.data());
     }
     if (d_cnt) (void)hipFree(d_cnt);
     if (rc != BS_OK) { delete t; return rc; }
@@ -384,6 +417,12 @@ bs_status bs_tables_get_layout(const bs_tables* t, uint32_t* layout, uint32_t* q
     if (layout) *layout = t->layout;
     if (q_h)
         for (uint32_t k = 0; k < kMaxHTables; k++) memcpy(q_h + 8 * k, t->q_h[k].data(), 8 * 4);
+    return BS_OK;
+}
+
+bs_status bs_tables_get_joint(const bs_tables* t, uint32_t* q_t) {
+    if (!t || !q_t) { set_error("NULL argument"); return BS_E_INVAL; }
+    memcpy(q_t, t->q_t.data(), 512 * 8 * 4);
     return BS_OK;
 }
 

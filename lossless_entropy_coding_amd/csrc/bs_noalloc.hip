@@ -28,7 +28,7 @@ using namespace bs;
 
 namespace {
 
-constexpr uint64_t kScratchBytes = kHistCounters * sizeof(unsigned long long);   // 264,192 B
+constexpr uint64_t kScratchBytes = kHistCounters * sizeof(unsigned long long);   // 278,528 B
 static __device__ __align__(256) unsigned long long scratch[kHistCounters];
 
 constexpr int kMaxDevices = 64;
@@ -36,6 +36,7 @@ std::mutex g_lock;
 void* g_scratch[kMaxDevices];      // device address of `scratch` on each device (under g_lock)
 unsigned long long g_counts[kHistCounters];       // host copy of the counters (under g_lock)
 std::array<uint64_t, 128> g_merged[kCandidates];  // model working memory (under g_lock)
+uint64_t g_joint[512 * 8];                         // joint counts of layout 3 (under g_lock)
 
 // the address of this device's copy of `scratch`, looked up on first use
 bs_status scratch_of(int dev, void** out) {
@@ -84,7 +85,7 @@ bs_status bs_build_tables_noalloc(const void* d_bf16, uint64_t n, const bs_param
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) { set_error("histogram: %s", hipGetErrorString(e)); return BS_E_HIP; }
     }
-    return model_from_counts(*t, p, n, g_counts, g_merged);
+    return model_from_counts(*t, p, n, g_counts, g_merged, g_joint);
 }
 
 }  // extern "C"

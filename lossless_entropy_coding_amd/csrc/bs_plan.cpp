@@ -33,11 +33,14 @@ struct bs_plan {
     // thread share one kernel (16-wave workgroups), in the full or the compact
     // LDS layout; eight lanes per thread have their own (8-wave workgroups)
     // layout; records of layout 2 (one renormalisation per weight) form the
-    // fourth class, with their own kernel
-    static constexpr int kClasses = 4;
-    static constexpr uint32_t kMaxR[kClasses] = {4, 4, 8, 4};
-    static constexpr bool kCompact[kClasses] = {false, true, false, false};
+    // fourth class, with their own kernel, and records of layout 3 (the same
+    // with one joint symbol per weight) the fifth, with that kernel's
+    // joint-symbol instances
+    static constexpr int kClasses = 5;
+    static constexpr uint32_t kMaxR[kClasses] = {4, 4, 8, 4, 4};
+    static constexpr bool kCompact[kClasses] = {false, true, false, false, false};
     static constexpr int kLayout2 = 3;
+    static constexpr int kLayout3 = 4;
     int cus = 256;
     std::vector<uint32_t> dev_index;   // record -> index in d_recs (BF16) or d_raws (RAW)
     std::vector<uint32_t> rclass;      // record -> class (BF16)
@@ -128,13 +131,13 @@ void launch_shape(const bs_plan* p, int k, uint32_t e0, uint32_t e1, uint32_t& w
     }
     groups = (uint32_t)count(run);
     waves = std::min<uint32_t>(bsd::max_waves(bs_plan::kMaxR[k]), run);
-    if (k == bs_plan::kLayout2) {
-        // a layout-2 workgroup's rings follow its records' table image, whose
-        // size varies: take as many waves as fit after the largest
+    if (k == bs_plan::kLayout2 || k == bs_plan::kLayout3) {
+        // a layout-2 or -3 workgroup's rings follow its records' table image,
+        // whose size varies: take as many waves as fit after the largest
         uint32_t rb = 0;
         for (uint32_t e = e0; e < e1; e++) {
             const bsd::RecDev& d = p->h_recs[p->cls_recs[k][e]];
-            rb = std::max(rb, bsd::l2_ring_base(d.m_s, d.n_tables));
+            rb = std::max(rb, k == bs_plan::kLayout3 ? bsd::l3_ring_base(d.m_s) : bsd::l2_ring_base(d.m_s, d.n_tables));
         }
         waves = std::min(waves, bsd::l2_max_waves(rb));
     }
@@ -211,15 +214,16 @@ bs_status bs_plan_create(const void* h_container, uint64_t len, const void* d_co
         const uint32_t R = d.lanes_per_thread;
         d.layout = r.layout;
         uint32_t k;
-        if (r.layout == 2) {
+        if (r.layout >= 2) {
             if (R > 4) {
                 plan_free(p);
-                set_error("record %u: layout 2 decodes with at most 256 lanes per word stream (it has %u)", i, d.P);
+                set_error("record %u: layout %u decodes with at most 256 lanes per word stream (it has %u)", i, r.layout,
+                          d.P);
                 return BS_E_INVAL;
             }
             d.compact = 0;
-            lut_bytes += bsd::l2_ring_base(r.m_s, r.n_tables);
-            k = bs_plan::kLayout2;
+            lut_bytes += r.layout == 3 ? bsd::l3_ring_base(r.m_s) : bsd::l2_ring_base(r.m_s, r.n_tables);
+            k = r.layout == 3 ? bs_plan::kLayout3 : bs_plan::kLayout2;
         } else {
             d.compact = R <= 4 && r.m_s <= 11 && r.m_f <= 9;
             lut_bytes += (8ull << r.m_s) + (r.n_tables + 1ull) * bsd::fpage_bytes(d.compact);
@@ -342,8 +346,9 @@ bs_status bs_decode_async(const bs_plan* p, uint32_t first, uint32_t count, void
             rmax = std::max(rmax, R);
         }
         const uint32_t variant = rmin == rmax ? rmax : rmax <= 2 ? 0 : 3;
-        int e = k == bs_plan::kLayout2 ? bsk_decode2(&a, groups, variant, stream)
-                                       : bsk_decode(&a, groups, variant, bs_plan::kCompact[k], stream);
+        int e = k == bs_plan::kLayout2   ? bsk_decode2(&a, groups, variant, stream)
+                : k == bs_plan::kLayout3 ? bsk_decode3(&a, groups, variant, stream)
+                                         : bsk_decode(&a, groups, variant, bs_plan::kCompact[k], stream);
         if (e) return hip_err((hipError_t)e, "decode launch");
     }
     if (r1 > r0) {
@@ -391,8 +396,9 @@ bs_status bs_gemv_async(const bs_plan* p, uint32_t record, uint64_t rows, uint64
     uint32_t groups;
     launch_shape(p, k, e, e + 1, a.waves, a.run, groups);
     if (p->cls_start[k][e + 1] == p->cls_start[k][e]) groups = 0;
-    const int err = k == bs_plan::kLayout2 ? bsk_gemv2(&a, groups, p->cls_R[k][e], rows, stream)
-                                           : bsk_gemv(&a, groups, p->cls_R[k][e], rows, stream);
+    const int err = k == bs_plan::kLayout2   ? bsk_gemv2(&a, groups, p->cls_R[k][e], rows, stream)
+                    : k == bs_plan::kLayout3 ? bsk_gemv3(&a, groups, p->cls_R[k][e], rows, stream)
+                                             : bsk_gemv(&a, groups, p->cls_R[k][e], rows, stream);
     if (err) return hip_err((hipError_t)err, "fused product launch");
     return BS_OK;
 }

@@ -99,16 +99,22 @@ def _layout2(wl: synth.Workload, m_s: int = 11) -> synth.Workload:
     return wl
 
 
-# Layout 2 (one renormalisation per weight, the low fraction bits in a plane)
-# for every workload but the 4096x4096 matrix: its 1% exact zeros each pay
-# the four verbatim low bits, and it needs 2048 lanes per chunk to fill the
-# GPU, which together would exceed the 1% size budget in layout 2; it keeps
+def _layout3(wl: synth.Workload, m_s: int = 11) -> synth.Workload:
+    wl.layout, wl.m_s, wl.m_f = 3, m_s, codec.JOINT_BITS
+    return wl
+
+
+# Layout 3 (one joint (sign, exponent, high fraction bits) symbol and one
+# renormalisation per weight, the low fraction bits in a plane) for every
+# workload but the 4096x4096 matrix: its 1% exact zeros each pay the four
+# verbatim low bits, and it needs 2048 lanes per chunk to fill the GPU, which
+# together would exceed the 1% size budget in layouts 2 and 3; it keeps
 # layout 1 (a version-1 container).
 CONFIG_BUILDERS = {
-    "1": lambda device: _layout2(synth.cfg1(device)),
+    "1": lambda device: _layout3(synth.cfg1(device)),
     "2": lambda device: _with_streams(synth.cfg2(device, lanes=2048), 64),
-    "3": lambda device: _layout2(synth.cfg3(device, lanes=256)),
-    "4": lambda device: _layout2(synth.cfg4(device)),
+    "3": lambda device: _layout3(synth.cfg3(device, lanes=256)),
+    "4": lambda device: _layout3(synth.cfg4(device)),
 }
 
 
@@ -127,6 +133,8 @@ def encode_config(cfg: str, device: str = "cpu", lanes: int | None = None, chunk
         wl.layout = layout
         if layout == 2 and not m_s:
             wl.m_s, wl.m_f = 11, 5
+        elif layout == 3 and not m_s:
+            wl.m_s, wl.m_f = 11, codec.JOINT_BITS
         elif layout == 1 and not m_s:
             wl.m_s, wl.m_f = 12, 10
     if m_s:
@@ -159,8 +167,8 @@ class DecodeJob:
         self.m_s, self.m_f = enc.params["m_s"], enc.params["m_f"]
         self.layout = enc.params["layout"]
         # the decode kernel instance the workload's large records run on
-        if self.layout == 2:
-            self.kernel_name = "decode2_kernel<%d>" % self.lanes_per_thread
+        if self.layout >= 2:
+            self.kernel_name = "decode%d_kernel<%d>" % (self.layout, self.lanes_per_thread)
         else:
             compact = self.lanes_per_thread <= 4 and self.m_s <= 11 and self.m_f <= 9
             self.kernel_name = "decode_kernel<%d, %s>" % (self.lanes_per_thread, "true" if compact else "false")

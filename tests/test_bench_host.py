@@ -32,11 +32,18 @@ def _records():
         return json.load(f)
 
 
+def _kind(key):
+    """The kernel a traffic record measures, from its key."""
+    if key.startswith("fixed|"):
+        return "fixed"
+    return {"|L=2": "decode2_kernel", "|L=3": "decode3_kernel"}.get(key[-4:], "decode_kernel")
+
+
 def test_committed_traffic_records_match_the_kernel_sources():
     rec = _records()
     assert rec["workloads"], "no traffic records"
     for key, w in rec["workloads"].items():
-        kind = "fixed" if key.startswith("fixed|") else "decode2_kernel" if key.endswith("|L=2") else "decode_kernel"
+        kind = _kind(key)
         assert w["kernel_source_sha256"] == bench.kernel_source_sha256(kind), key
         assert bench.measured_traffic(key, kind) == w["traffic_bytes"]
         # counters close to the algorithmic bytes: nothing re-read
@@ -46,13 +53,13 @@ def test_committed_traffic_records_match_the_kernel_sources():
 
 def test_traffic_keys_name_the_layout():
     for key in _records()["workloads"]:
-        assert key.startswith("fixed|") or key.endswith(("|L=1", "|L=2")), key
+        assert key.startswith("fixed|") or key.endswith(("|L=1", "|L=2", "|L=3")), key
 
 
 def test_unknown_workload_or_changed_source_gives_null(monkeypatch):
     assert bench.measured_traffic("no such workload") is None
     key = next(iter(_records()["workloads"]))
-    kind = "fixed" if key.startswith("fixed|") else "decode2_kernel" if key.endswith("|L=2") else "decode_kernel"
+    kind = _kind(key)
     assert bench.measured_traffic(key, kind) is not None
     monkeypatch.setattr(bench, "kernel_source_sha256", lambda kind: "0" * 64)
     assert bench.measured_traffic(key, kind) is None
@@ -66,8 +73,8 @@ def test_copy_calibration_scales():
 
 
 def test_default_workload_has_a_traffic_record():
-    """The default bench line (the 84-layer checkpoint in layout 2, 256 lanes
+    """The default bench line (the 84-layer checkpoint in layout 3, 256 lanes
     per chunk in streams of 128) reports a measured traffic figure."""
     from lossless_entropy_coding_amd import synth
-    key = f"cfg5_checkpoint_84layers_{len(synth.cfg5_layout(layers=84))}tensors|W=65536|K=256|P=128|L=2"
-    assert bench.measured_traffic(key, "decode2_kernel") is not None, key
+    key = f"cfg5_checkpoint_84layers_{len(synth.cfg5_layout(layers=84))}tensors|W=65536|K=256|P=128|L=3"
+    assert bench.measured_traffic(key, "decode3_kernel") is not None, key

@@ -1,5 +1,5 @@
 """GPU: the fused decode and matrix-vector product against an fp64 product of
-the oracle's decode, on records of both layouts.
+the oracle's decode, on records of the three layouts.
 
 The weights are decoded in registers and multiplied into y without being
 written out [Qwen3.8-27B-BF16-NVLC-Lossless card, runtime paragraphs: the
@@ -49,7 +49,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("layout", [1, 2])
+@pytest.mark.parametrize("layout", [1, 2, 3])
 @pytest.mark.parametrize("name,rows,cols,W,K,P", CASES, ids=[c[0] for c in CASES])
 def test_gemv_matches_fp64_product_of_oracle_decode(name, rows, cols, W, K, P, layout):
     say("gemv case", name, rows, cols, W, K, P, "layout", layout)
@@ -59,7 +59,8 @@ def test_gemv_matches_fp64_product_of_oracle_decode(name, rows, cols, W, K, P, l
     w[rng.random(w.size) < 0.01] = 0.0
     words = _bf16_words(w)
     xw = _bf16_words(rng.standard_normal(cols))
-    p = (codec.params2(chunk_weights=W, lanes=K, stream_lanes=P) if layout == 2
+    p = (codec.params3(chunk_weights=W, lanes=K, stream_lanes=P) if layout == 3
+         else codec.params2(chunk_weights=W, lanes=K, stream_lanes=P) if layout == 2
          else codec.params(chunk_weights=W, lanes=K, stream_lanes=P))
     c = codec.encode([codec.bf16(words)], p)
     assert codec.record_info(c, 0).layout == layout
