@@ -33,6 +33,25 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def copy_ceiling(n: int = 1 << 30, reps: int = 20) -> float:
+    """GB/s (bytes read + written) of a plain device copy of n bytes."""
+    import torch
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * n / ms / 1e6
+
+
 def cold_flush(buf) -> None:
     """Leave the GPU caches cold and clean before a timed launch: write a
     1 GiB buffer (evicting what the launch would find cached), then read it
@@ -746,8 +765,24 @@ def main():
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
+
+        def timed(fn, reps=20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+        # the bandwidth plain streams reach on this GPU: a copy (as much read
+        # as written) and a fill (written only), HIP events around 20 of each
+        t_copy = timed(lambda: dst.copy_(src))
+        t_fill = timed(lambda: dst.fill_(3))
         print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
-                          "copies": 5}))
+                          "copies": 5, "copy_ms": round(t_copy, 4), "copy_GB_s": round(2 * n / t_copy / 1e6, 1),
+                          "fill_ms": round(t_fill, 4), "fill_GB_s": round(n / t_fill / 1e6, 1),
+                          "copy_frac_of_8TB_s": round(2 * n / t_copy / 1e6 / 8000, 4),
+                          "fill_frac_of_8TB_s": round(n / t_fill / 1e6 / 8000, 4)}))
         return
     L.lib()   # fails loudly if the HIP library is missing
     if a.gemv:
@@ -845,6 +880,12 @@ def main():
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "kernel": job.kernel_name if hasattr(job, "kernel_name") else "decode_kernel",
                 "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(avg_ms, 4)}
+    # context, measured after the timed region: what a plain 1 GiB device
+    # copy (as many bytes read as written) reaches on this GPU
+    copy_gbs = copy_ceiling()
+    roofline["copy_ceiling"] = {"GB_s": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+                                "decode_vs_copy": round(achieved / copy_gbs, 4),
+                                "what": "torch copy_ of 1 GiB, HIP events around 20 copies"}
 
     model = model_build_rate(job)
 
