@@ -503,6 +503,15 @@ uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count);
  * word stream of a chunk per wavefront at a time). */
 uint32_t bs_plan_waves_per_block(const bs_plan* plan);
 
+/* Workgroups of bs_decode_async(plan, first, count, ...) that decode packs of
+ * small records (0: none).  In a launch that also holds large records
+ * (layouts 2 and 3), records of at most one round of a workgroup's waves are
+ * decoded several to a workgroup, one after another, so that they do not
+ * each hold a CU for the whole launch; the pack size keeps a pack's decode
+ * well below a large run's.  For tests and tuning; 0 for a NULL plan or a
+ * range out of bounds. */
+uint32_t bs_plan_packs(const bs_plan* plan, uint32_t first, uint32_t count);
+
 /* ------------------------------------------------------- layer streaming
  *
  * Layers streamed on demand under a budget of device memory [Gemma 2 9B

@@ -47,15 +47,19 @@ def host_threads() -> int:
 class CheckpointJob:
     """One Plan per layer container; decode() decodes every layer in order."""
 
-    def __init__(self, layers: int = 84, chunk_weights: int = 65536, lanes: int | None = None, log=print,
+    def __init__(self, layers: int = 84, chunk_weights: int | None = None, lanes: int | None = None, log=print,
                  device: str = "cuda", m_s: int | None = None, m_f: int | None = None,
                  stream_lanes: int | None = None, layout: int = 3):
         tensors = synth.cfg5_layout(layers=layers)
-        # chunk shape: K = 256 lanes in streams of 128 for layouts 2 and 3 (as
-        # fast as 512 lanes here, at 0.2% less size); 512 in streams of 256 for
-        # layout 1
+        # chunk shape: layout 3 takes chunks of 32,768 weights with K = 128
+        # lanes in one stream (256 weights per lane, as K = 256 over 65,536
+        # weights, at twice the decode units: a layer's units then divide
+        # evenly over a workgroup's waves); layout 2 K = 256 in streams of 128
+        # over 65,536 weights; layout 1 512 lanes in streams of 256
+        if chunk_weights is None:
+            chunk_weights = 32768 if layout == 3 else 65536
         if lanes is None:
-            lanes = 256 if layout >= 2 else 512
+            lanes = 128 if layout == 3 else 256 if layout == 2 else 512
         if stream_lanes is None:
             stream_lanes = 128 if layout >= 2 else 256
         self.name = "cfg5_checkpoint_%dlayers_%dtensors" % (layers, len(tensors))

@@ -259,6 +259,13 @@ class Plan:
     def waves_per_block(self) -> int:
         return int(L.lib().bs_plan_waves_per_block(self.handle))
 
+    def packs(self, first: int = 0, count: int | None = None) -> int:
+        """Workgroups that decode packs of small records when records
+        [first, first + count) are decoded (0: none)."""
+        if count is None:
+            count = self.n_records - first
+        return int(L.lib().bs_plan_packs(self.handle, first, count))
+
     def new_output(self, first: int = 0, count: int | None = None) -> torch.Tensor:
         """A zero-filled output buffer for records [first, first+count) (gaps stay zero)."""
         n = self.out_bytes(first, count)

@@ -85,7 +85,7 @@ __device__ __forceinline__ uint32_t joint_step(uint32_t x, uint2 e) { return __u
 // high twelve bits, weight p at 16-bit half p of the four dwords.
 template <int R, uint32_t RW, bool J>
 __device__ __forceinline__ void group_pairs(uint32_t (&x)[R], uint32_t (&o)[R][4], const uint8_t* lds, const Model2& md,
-                                            Ring<RW>& g, uint32_t& pos, const bool (&all_on)[R]) {
+                                            Ring<RW>& g, uint32_t& pos, const bool (&on)[R]) {
 #pragma unroll
     for (int p = 0; p < 8; p++) {
         if (p % top_up_every(R, false) == 0) ring_top_up(g, pos);
@@ -115,7 +115,7 @@ __device__ __forceinline__ void group_pairs(uint32_t (&x)[R], uint32_t (&o)[R][4
                 w[q] = __builtin_amdgcn_alignbit(e[q].y, f[q].x, 25);
             }
         }
-        refill_all<R, RW>(x, all_on, g, pos);
+        refill_all<R, RW>(x, on, g, pos);
 #pragma unroll
         for (int q = 0; q < R; q++) {
             if (p & 1) o[q][p >> 1] = __builtin_amdgcn_perm(w[q], o[q][p >> 1], 0x05040100u);
@@ -173,15 +173,19 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
     const __amdgpu_buffer_rsrc_t plane = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(u.payload + code_bytes), (short)0, (int)((4 * groups + 15) & ~15u), 0x00020000);
     const uint32_t T = (groups + K - 1) / K;
+    // A stream narrower than the wave (P < 64, one lane per thread) takes the
+    // unrolled path too: lanes [P, 64) step on an idle state, never refill
+    // and store nothing, and are put back to the idle state after it.
+    const bool part = R == 1 && !V && P < 64;
+    bool on[R];
+#pragma unroll
+    for (int q = 0; q < R; q++) on[q] = !part || lane < P;
     // full macro-steps: every lane has 8 weights and none is in its last group
-    const uint32_t T_full = (P % 64 == 0) ? n_c / (8 * K) : 0;
+    const uint32_t T_full = (P % 64 == 0 || part) ? n_c / (8 * K) : 0;
     // a whole chunk: the last macro-step is every lane's last group, of 8 weights
     const bool whole = T_full != 0 && T_full == T;
     const uint32_t T_main = T_full ? T_full - 1 : 0;
 
-    bool all_on[R];
-#pragma unroll
-    for (int q = 0; q < R; q++) all_on[q] = true;
     const uint32_t prio0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
 
     uint32_t d[R];
@@ -194,11 +198,11 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
         for (int q = 0; q < R; q++)
             dn[q] = __builtin_amdgcn_raw_buffer_load_b32(plane, 4 * ((t + 1) * K + LB + 64 * q + lane), 0, 0);
         uint32_t o[R][4];
-        group_pairs<R, RW, J>(x, o, lds, md, g, pos, all_on);
+        group_pairs<R, RW, J>(x, o, lds, md, g, pos, on);
 #pragma unroll
         for (int q = 0; q < R; q++) {
             add_low_bits(o[q], d[q]);
-            if (!V) {
+            if (!V && on[q]) {
                 v4o* op = (v4o*)out + (uint64_t)t * K + LB + 64 * q + lane;
                 __builtin_nontemporal_store(v4o{o[q][0], o[q][1], o[q][2], o[q][3]}, op);
             }
@@ -222,7 +226,7 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
             for (int q = 0; q < R; q++) e[q] = s_entry(lds_s, x[q], md);
 #pragma unroll
             for (int q = 0; q < R; q++) x[q] = s_step(x[q], e[q], md);
-            refill_all<R, RW>(x, all_on, g, pos);
+            refill_all<R, RW>(x, on, g, pos);
 #pragma unroll
             for (int q = 0; q < R; q++) {
                 const uint32_t w = e[q].y << 7;   // low half s << 7
@@ -237,11 +241,11 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
             for (int k = 0; k < 4; k++)
                 o[q][k] |= ((x[q] >> (6 * k)) & 7u) << 4 | ((x[q] >> (6 * k + 3)) & 7u) << 20;
             add_low_bits(o[q], d[q]);
-            if (!V) {
+            if (!V && on[q]) {
                 v4o* op = (v4o*)out + (uint64_t)T_main * K + LB + 64 * q + lane;
                 __builtin_nontemporal_store(v4o{o[q][0], o[q][1], o[q][2], o[q][3]}, op);
             }
-            bad |= lane_bad(x[q], true, 8);
+            if (on[q]) bad |= lane_bad(x[q], true, 8);
         }
         if (V) gemv_step<R>(a, o, nullptr, mpos, lane);
         const uint64_t badm = __builtin_amdgcn_ballot_w64(bad);
@@ -250,9 +254,12 @@ __device__ __forceinline__ void unit_decode2(const DecodeArgs& a, const RecDev& 
     }
 
     // remaining macro-steps (partial chunks, lanes' last groups, fewer than
-    // 64 lanes): a lane takes part while it has weights; in its last group it
-    // decodes s alone.  One position per iteration; each lane's eight output
-    // words move through a 128-bit shift register.
+    // 64 lanes in the fused product): a lane takes part while it has weights;
+    // in its last group it decodes s alone.  One position per iteration; each
+    // lane's eight output words move through a 128-bit shift register.
+#pragma unroll
+    for (int q = 0; q < R; q++)
+        if (!on[q]) x[q] = kStateLow;
     bool has[R];
     uint32_t clast[R];
 #pragma unroll
@@ -405,11 +412,30 @@ __device__ __forceinline__ void run_record2(const DecodeArgs& a, const RecDev& r
     }
 }
 
+// A pack: the small records (1..small_units units) of the launch whose rank
+// among them is in [p * pack, p * pack + pack), each decoded with all its
+// units at once after its table image is staged; the workgroup waits for one
+// record's waves before it stages the next image over it.
+template <int G, bool V, bool J>
+__device__ __forceinline__ void run_pack(const DecodeArgs& a, uint32_t p, uint32_t wave, uint8_t* lds) {
+    const uint32_t first = p * a.pack, last = first + a.pack;
+    uint32_t rank = 0;
+    for (uint32_t e = a.i0; e < a.i1 && rank < last; e++) {
+        const uint32_t n_units = a.cls.start[e + 1] - a.cls.start[e];
+        if (n_units == 0 || n_units > a.small_units) continue;
+        if (rank++ < first) continue;
+        const RecDev r = a.recs[a.cls.recs[e]];
+        run_record2<G, V, J>(a, r, 0, wave, lds);
+        __syncthreads();
+    }
+}
+
 // Workgroup b decodes one run of units inside one record, as the layout-1
 // kernel does (record lookup by a prefix sum over the records' run counts
-// when the launch has several).  G: the lanes per thread of every record
-// (1, 2 or 4), 0 for a mix of 1 and 2, 3 for a mix that includes 4.  V:
-// the fused product (one record, G = 1, 2 or 4).  J: layout-3 records.
+// when the launch has several), or, past the runs, one pack of small records.
+// G: the lanes per thread of every record (1, 2 or 4), 0 for a mix of 1 and
+// 2, 3 for a mix that includes 4.  V: the fused product (one record, G = 1,
+// 2 or 4).  J: layout-3 records.
 template <int G, bool V, bool J>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     __shared__ __align__(16) uint8_t lds[kLds2];
@@ -422,13 +448,18 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         run_record2<G, V, J>(a, a.one, u0, wave, lds);
         return;
     }
+    constexpr uint32_t kPacked = UINT32_MAX - 1;
     if (wave == 0) {
         const uint32_t lane = threadIdx.x & 63;
         uint32_t carry = 0, e = UINT32_MAX, j = 0;
         for (uint32_t base = a.i0; base < a.i1; base += 64) {
             const uint32_t i = base + lane;
             uint32_t k = 0;
-            if (i < a.i1) k = (a.cls.start[i + 1] - a.cls.start[i] + a.run - 1) / a.run;
+            if (i < a.i1) {
+                const uint32_t n_units = a.cls.start[i + 1] - a.cls.start[i];
+                // small records are in packs, not runs
+                k = n_units <= a.small_units ? 0u : (n_units + a.run - 1) / a.run;
+            }
             const uint32_t incl = wave_scan(k);
             const uint32_t excl = carry + incl - k;
             const unsigned long long hit = __ballot(k != 0 && excl <= b && b < excl + k);
@@ -440,11 +471,17 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
             }
             carry += __shfl(incl, 63, 64);
         }
+        // past the runs: pack b - (run count)
+        if (e == UINT32_MAX && a.pack) { e = kPacked; j = b - carry; }
         if (lane == 0) { pick[0] = e; pick[1] = j; }
     }
     __syncthreads();
     const uint32_t e = __builtin_amdgcn_readfirstlane(pick[0]);
     if (e == UINT32_MAX) return;
+    if (e == kPacked) {
+        run_pack<G, V, J>(a, __builtin_amdgcn_readfirstlane(pick[1]), wave, lds);
+        return;
+    }
     const RecDev r = a.recs[a.cls.recs[e]];
     run_record2<G, V, J>(a, r, __builtin_amdgcn_readfirstlane(pick[1]) * a.run, wave, lds);
 }

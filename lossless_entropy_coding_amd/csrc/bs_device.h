@@ -140,6 +140,11 @@ struct DecodeArgs {
     uint32_t i0, i1;        // class entries of the decoded records
     uint32_t run;           // units per workgroup (a run inside one record)
     uint32_t waves;         // waves per workgroup (rings allocated)
+    // layouts 2 and 3: records of 1..small_units units are not cut into runs
+    // but decoded `pack` to a workgroup, one after another, by the workgroups
+    // after the runs' (small_units = 0: none)
+    uint32_t small_units;
+    uint32_t pack;
     RecDev one;             // the record itself when the launch has one (i1 = i0 + 1)
     // fused product with a vector (the kernel instances with V set): the
     // record is a row-major matrix of gcols columns; y[r] += sum over c of

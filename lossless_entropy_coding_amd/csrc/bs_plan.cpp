@@ -60,6 +60,9 @@ struct bs_plan {
 
 namespace {
 
+// a packed small record's start (table staging, unit opening) in lane steps
+constexpr uint32_t kPackStartSteps = 64;
+
 void plan_free(bs_plan* p) {
     if (!p) return;
     if (p->d_recs) (void)hipFree(p->d_recs);
@@ -103,43 +106,97 @@ void ranges(const bs_plan* p, uint32_t first, uint32_t count, uint32_t* e0, uint
 // rings fill a CU's LDS, or half of it in the compact layout).  `run` is the
 // smallest length whose run count fits the workgroups that run at once; when
 // the records alone outnumber those, runs are sized to the average share.
+//
+// Small records next to large ones (a layer's norm vectors beside its
+// matrices, layouts 2 and 3): a record of at most `waves` units decodes in
+// one round of a workgroup, far sooner than a run of a large record, and would
+// leave its CU idle for the rest of the launch.  Such records are packed
+// `pack` to a workgroup, which decodes them one after another (each with its
+// own table image), and the large records' runs spread over the other CUs.
+// A pack is sized so that its records, timed as lane steps of a lone wave,
+// take at most half as long as a large run's lane steps (a wave on a loaded
+// CU steps about three times slower than a lone one).  small = 0: no packing.
 void launch_shape(const bs_plan* p, int k, uint32_t e0, uint32_t e1, uint32_t& waves, uint32_t& run,
-                  uint32_t& groups) {
+                  uint32_t& groups, uint32_t& small, uint32_t& pack) {
     const std::vector<uint32_t>& st = p->cls_start[k];
-    const uint32_t total = st[e1] - st[e0];
-    uint32_t biggest = 0;
-    for (uint32_t e = e0; e < e1; e++) biggest = std::max(biggest, st[e + 1] - st[e]);
-    auto count = [&](uint32_t len) {
-        uint64_t g = 0;
-        for (uint32_t e = e0; e < e1; e++) g += (st[e + 1] - st[e] + len - 1) / len;
-        return g;
-    };
+    auto units = [&](uint32_t e) { return st[e + 1] - st[e]; };
     // workgroups that run at once: one per CU, or two in the compact layout
     // when their registers allow it (up to 2 lanes per thread)
     uint32_t rmax = 0;
     for (uint32_t e = e0; e < e1; e++) rmax = std::max(rmax, p->cls_R[k][e]);
     const uint32_t cus = (uint32_t)p->cus * (bs_plan::kCompact[k] && rmax <= 2 ? 2 : 1);
-    uint32_t lo = std::max<uint32_t>(1, (total + cus - 1) / cus), hi = std::max(lo, biggest);
-    if (count(hi) > cus) {
-        run = lo;
-    } else {
-        while (lo < hi) {
-            const uint32_t mid = lo + (hi - lo) / 2;
-            if (count(mid) <= cus) hi = mid; else lo = mid + 1;
+    // the shortest run whose workgroup count over the records with big(e)
+    // fits `slots`, and that count
+    auto fit = [&](uint32_t slots, auto big, uint32_t& len, uint32_t& count) {
+        uint64_t total = 0;
+        uint32_t biggest = 0;
+        for (uint32_t e = e0; e < e1; e++)
+            if (big(e)) { total += units(e); biggest = std::max(biggest, units(e)); }
+        auto cnt = [&](uint32_t l) {
+            uint64_t g = 0;
+            for (uint32_t e = e0; e < e1; e++)
+                if (big(e)) g += (units(e) + l - 1) / l;
+            return g;
+        };
+        uint32_t lo = (uint32_t)std::max<uint64_t>(1, (total + slots - 1) / slots), hi = std::max(lo, biggest);
+        if (cnt(hi) > slots) {
+            len = lo;
+        } else {
+            while (lo < hi) {
+                const uint32_t mid = lo + (hi - lo) / 2;
+                if (cnt(mid) <= slots) hi = mid; else lo = mid + 1;
+            }
+            len = lo;
         }
-        run = lo;
-    }
-    groups = (uint32_t)count(run);
-    waves = std::min<uint32_t>(bsd::max_waves(bs_plan::kMaxR[k]), run);
-    if (k == bs_plan::kLayout2 || k == bs_plan::kLayout3) {
-        // a layout-2 or -3 workgroup's rings follow its records' table image,
-        // whose size varies: take as many waves as fit after the largest
+        count = (uint32_t)cnt(len);
+    };
+    // waves per workgroup: a layout-2 or -3 workgroup's rings follow its
+    // records' table image, whose size varies: as many as fit after the largest
+    uint32_t wlim = bsd::max_waves(bs_plan::kMaxR[k]);
+    const bool l23 = k == bs_plan::kLayout2 || k == bs_plan::kLayout3;
+    if (l23) {
         uint32_t rb = 0;
         for (uint32_t e = e0; e < e1; e++) {
             const bsd::RecDev& d = p->h_recs[p->cls_recs[k][e]];
             rb = std::max(rb, k == bs_plan::kLayout3 ? bsd::l3_ring_base(d.m_s) : bsd::l2_ring_base(d.m_s, d.n_tables));
         }
-        waves = std::min(waves, bsd::l2_max_waves(rb));
+        wlim = std::min(wlim, bsd::l2_max_waves(rb));
+    }
+    fit(cus, [](uint32_t) { return true; }, run, groups);
+    waves = std::min(wlim, run);
+    small = pack = 0;
+    if (!l23 || e1 - e0 < 2) return;
+
+    // lane steps of a record's unit: the weights of a chunk's lane
+    auto steps = [&](uint32_t e) {
+        const bsd::RecDev& d = p->h_recs[p->cls_recs[k][e]];
+        return (uint32_t)((std::min<uint64_t>(d.n, d.W) + d.K - 1) / d.K);
+    };
+    auto is_small = [&](uint32_t e) { return units(e) != 0 && units(e) <= wlim; };
+    uint32_t n_small = 0, c_small = 0, s_big = 0;
+    for (uint32_t e = e0; e < e1; e++) {
+        if (is_small(e)) { n_small++; c_small = std::max(c_small, steps(e) + kPackStartSteps); }
+        else if (units(e)) s_big = std::max(s_big, steps(e));
+    }
+    if (n_small == 0 || s_big == 0) return;
+    auto big = [&](uint32_t e) { return units(e) > wlim; };
+    for (uint32_t np = 1; np < cus && np <= n_small;) {
+        uint32_t len, count;
+        fit(cus - np, big, len, count);
+        if (len < wlim) return;                                   // large runs of a single round: nothing to gain
+        const uint64_t budget = 3ull * ((len + wlim - 1) / wlim) * s_big / 2;
+        const uint32_t per = (uint32_t)std::min<uint64_t>(budget / c_small, n_small);
+        if (per < 2) return;
+        const uint32_t need = (n_small + per - 1) / per;
+        if (need <= np) {
+            run = len;
+            waves = wlim;
+            groups = count + need;
+            small = wlim;
+            pack = per;
+            return;
+        }
+        np = need;
     }
 }
 
@@ -291,11 +348,31 @@ uint32_t bs_plan_waves_per_block(const bs_plan* plan) {
     uint32_t w = 0;
     for (int k = 0; k < bs_plan::kClasses; k++) {
         if (!plan->cls_start[k].back()) continue;
-        uint32_t waves, run, groups;
-        launch_shape(plan, k, 0, (uint32_t)plan->cls_recs[k].size(), waves, run, groups);
+        uint32_t waves, run, groups, small, pack;
+        launch_shape(plan, k, 0, (uint32_t)plan->cls_recs[k].size(), waves, run, groups, small, pack);
         w = std::max(w, waves);
     }
     return w;
+}
+
+uint32_t bs_plan_packs(const bs_plan* plan, uint32_t first, uint32_t count) {
+    if (!plan || first > plan->c.n_records || count > plan->c.n_records - first || !count) return 0;
+    uint32_t e0[bs_plan::kClasses], e1[bs_plan::kClasses], r0, r1;
+    ranges(plan, first, count, e0, e1, r0, r1);
+    uint32_t n = 0;
+    for (int k = 0; k < bs_plan::kClasses; k++) {
+        if (e1[k] <= e0[k] || plan->cls_start[k][e1[k]] <= plan->cls_start[k][e0[k]]) continue;
+        uint32_t waves, run, groups, small, pack;
+        launch_shape(plan, k, e0[k], e1[k], waves, run, groups, small, pack);
+        if (!pack) continue;
+        uint32_t n_small = 0;
+        for (uint32_t e = e0[k]; e < e1[k]; e++) {
+            const uint32_t u = plan->cls_start[k][e + 1] - plan->cls_start[k][e];
+            n_small += u != 0 && u <= small;
+        }
+        n += (n_small + pack - 1) / pack;
+    }
+    return n;
 }
 
 uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count) {
@@ -336,7 +413,7 @@ bs_status bs_decode_async(const bs_plan* p, uint32_t first, uint32_t count, void
         a.i1 = e1[k];
         if (e1[k] - e0[k] == 1) a.one = p->h_recs[p->cls_recs[k][e0[k]]];
         uint32_t groups;
-        launch_shape(p, k, e0[k], e1[k], a.waves, a.run, groups);
+        launch_shape(p, k, e0[k], e1[k], a.waves, a.run, groups, a.small_units, a.pack);
         // the specialised kernel when every record of the launch has the same
         // lanes per thread, else the mixed one
         uint32_t rmin = 8, rmax = 0;
@@ -393,8 +470,8 @@ bs_status bs_gemv_async(const bs_plan* p, uint32_t record, uint64_t rows, uint64
     a.gx = (const uint16_t*)d_x;
     a.gy = d_y;
     a.gcols = cols;
-    uint32_t groups;
-    launch_shape(p, k, e, e + 1, a.waves, a.run, groups);
+    uint32_t groups, small, pack;
+    launch_shape(p, k, e, e + 1, a.waves, a.run, groups, small, pack);
     if (p->cls_start[k][e + 1] == p->cls_start[k][e]) groups = 0;
     const int err = k == bs_plan::kLayout2   ? bsk_gemv2(&a, groups, p->cls_R[k][e], rows, stream)
                     : k == bs_plan::kLayout3 ? bsk_gemv3(&a, groups, p->cls_R[k][e], rows, stream)

@@ -46,8 +46,12 @@ def test_committed_traffic_records_match_the_kernel_sources():
         kind = _kind(key)
         assert w["kernel_source_sha256"] == bench.kernel_source_sha256(kind), key
         assert bench.measured_traffic(key, kind) == w["traffic_bytes"]
-        # counters close to the algorithmic bytes: nothing re-read
-        assert 1.0 <= w["traffic_bytes"] / w["alg_bytes"] < 1.03, key
+        # counters close to the algorithmic bytes: nothing re-read.  A
+        # workload of a few MB (config 1, 3.5 MB) also fetches its record's
+        # table image once into each XCD's L2 (8 x 80 KiB in layout 3), which
+        # the algorithmic bytes do not count
+        bound = 1.03 if w["alg_bytes"] >= 64 << 20 else 1.3
+        assert 1.0 <= w["traffic_bytes"] / w["alg_bytes"] < bound, key
         assert w["traffic_bytes"] == w["fetch_bytes"] + w["write_bytes"]
 
 
@@ -73,8 +77,9 @@ def test_copy_calibration_scales():
 
 
 def test_default_workload_has_a_traffic_record():
-    """The default bench line (the 84-layer checkpoint in layout 3, 256 lanes
-    per chunk in streams of 128) reports a measured traffic figure."""
+    """The default bench line (the 84-layer checkpoint in layout 3, chunks of
+    32,768 weights over 128 lanes in one stream) reports a measured traffic
+    figure."""
     from lossless_entropy_coding_amd import synth
-    key = f"cfg5_checkpoint_84layers_{len(synth.cfg5_layout(layers=84))}tensors|W=65536|K=256|P=128|L=3"
+    key = f"cfg5_checkpoint_84layers_{len(synth.cfg5_layout(layers=84))}tensors|W=32768|K=128|P=128|L=3"
     assert bench.measured_traffic(key, "decode3_kernel") is not None, key
