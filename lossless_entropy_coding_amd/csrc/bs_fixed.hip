@@ -375,7 +375,18 @@ __global__ __launch_bounds__(64 * kGemmWaves) void fixed_gemm_kernel(FixedArgs a
             has[h] = r0 + mr[h] < a.rows;
             if (has[h]) in[h] = load_block(a, (r0 + mr[h]) * bpr, lane);
         }
+        // B operands: 16 B of X per lane and k step.  Rows past the batch read
+        // row 0; they only feed D columns that are never stored.  The loads go
+        // out kU at a time, each group while the one before it is multiplied,
+        // and a panel's first group is issued before its blocks are decoded.
+        const uint32_t n = nt * 16 + (lane & 15);
+        const uint16_t* xrow = a.gx + (uint64_t)(n < a.batch ? n : 0) * a.cols + ks * kSlice + 8 * (lane >> 4);
+        constexpr uint32_t kNs = kSlice / 32;               // k steps per wave and panel
+        constexpr uint32_t kU = kNs < 8 ? kNs : 8;
+        bf16x8 bv[kU];
         for (uint32_t p = 0; p < bpr; p++) {
+#pragma unroll
+            for (uint32_t u = 0; u < kU; u++) bv[u] = *(const bf16x8*)(xrow + (uint64_t)p * kFixBlockW + 32 * u);
             __syncthreads();          // the previous panel is consumed (and the table built)
 #pragma unroll
             for (uint32_t h = 0; h < kRpw; h++) {
@@ -395,18 +406,24 @@ __global__ __launch_bounds__(64 * kGemmWaves) void fixed_gemm_kernel(FixedArgs a
                 for (uint32_t h = 0; h < kRpw; h++)
                     if (has[h]) in[h] = load_block(a, (r0 + mr[h]) * bpr + p + 1, lane);
             }
-            const uint32_t n = nt * 16 + (lane & 15);
-            const bool n_ok = n < a.batch;
-            const uint16_t* xr = a.gx + (uint64_t)(n_ok ? n : 0) * a.cols + (uint64_t)p * kFixBlockW;
             const uint8_t* wr = wbuf[lane & 15];
-#pragma unroll 8
-            for (uint32_t s = 0; s < kSlice / 32; s++) {
-                const uint32_t e0 = ks * kSlice + 32 * s + 8 * (lane >> 4);
-                const uint32_t L = e0 >> 5, kp = (e0 >> 3) & 3u;
-                const bf16x8 av = *(const bf16x8*)(wr + 64 * L + 16 * ((kp + (L >> 1)) & 3u));
-                bf16x8 bv = {};
-                if (n_ok) bv = *(const bf16x8*)(xr + e0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+            const uint16_t* xr = xrow + (uint64_t)p * kFixBlockW;
+#pragma unroll
+            for (uint32_t s0 = 0; s0 < kNs; s0 += kU) {
+                bf16x8 cur[kU];
+#pragma unroll
+                for (uint32_t u = 0; u < kU; u++) cur[u] = bv[u];
+                if (s0 + kU < kNs) {
+#pragma unroll
+                    for (uint32_t u = 0; u < kU; u++) bv[u] = *(const bf16x8*)(xr + 32 * (s0 + kU + u));
+                }
+#pragma unroll
+                for (uint32_t u = 0; u < kU; u++) {
+                    const uint32_t e0 = ks * kSlice + 32 * (s0 + u) + 8 * (lane >> 4);
+                    const uint32_t L = e0 >> 5, kp = (e0 >> 3) & 3u;
+                    const bf16x8 av = *(const bf16x8*)(wr + 64 * L + 16 * ((kp + (L >> 1)) & 3u));
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, cur[u], acc, 0, 0, 0);
+                }
             }
         }
         red[wave][lane] = acc;
