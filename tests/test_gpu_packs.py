@@ -114,3 +114,34 @@ def test_damaged_small_record_in_a_pack_is_reported():
             continue
         got = codec.record_output(out, plan, i, 0).cpu().numpy().view(np.uint16)
         assert np.array_equal(got, w), i
+
+
+def test_packs_of_multi_unit_small_records_with_fifteen_waves():
+    """M_s 12 leaves room for 15 rings: small records are those of at most
+    15 units.  Chunks of 8192 weights over 128 lanes in 2 streams of 64:
+    small records of 1 to 7 chunks (2 to 14 units, several waves each) and
+    one of 300 weights (one unit) sit between three large records; on 256
+    CUs they take 4 packs of 2."""
+    say("packs, m_s 12, multi-unit small records")
+    rng = np.random.default_rng(123)
+    W2 = 8192
+    big = 1400 * W2
+    sizes = [5 * W2 + 17, big, 3 * W2, 2 * W2 + 1, big + 4000, 7 * W2, 300, W2, big - 77, 6 * W2 + 5]
+    words = [_words(rng, n, float(rng.choice([0.004, 0.02, 0.07]))) for n in sizes]
+    p = codec.params3(chunk_weights=W2, lanes=128, stream_lanes=64, m_s=12)
+    c = codec.encode([codec.bf16(w) for w in words], p)
+    plan = codec.Plan(c)
+    assert plan.waves_per_block == 15
+    n = plan.packs()
+    say("packs", n)
+    assert n >= 1
+    out = plan.decode()
+    rc, rep = plan.verify(out, flags=L.VERIFY_STATUS | L.VERIFY_SHA256)
+    assert rc == L.BS_OK, rep
+    for i, w in enumerate(words):
+        got = codec.record_output(out, plan, i, 0).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, w), i
+    for i in (0, 3, 5, 9):
+        ri = codec.record_info(c, i)
+        last = (ri.n - 1) // W2
+        assert np.array_equal(O.decode_chunk(c, i, last), words[i][last * W2:]), i
