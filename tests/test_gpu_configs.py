@@ -75,6 +75,11 @@ def test_config5_layers_into_one_buffer():
     say("config 5, two layers + tail")
     job = checkpoint.build_job(layers=2, log=say)
     assert len(job.plans) == 3 and job.n_tensors == 2 * 14 + 23
+    # a layer's 7 norm vectors are decoded in packs beside its matrices; the
+    # trailing vectors alone have no large record to share the CUs with
+    packs = [p.packs() for p in job.plans]
+    say("packs per launch", packs)
+    assert packs[0] >= 1 and packs[1] >= 1 and packs[2] == 0
     job.decode()
     torch.cuda.synchronize()
     ok, bad = job.verify()
