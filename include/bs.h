@@ -157,9 +157,11 @@ typedef struct {
     uint32_t layout;
 } bs_params;
 
-/* Fill *p with the defaults: W = 65536, K = 128, layout 2, m_s = 11,
- * m_f = 5, max_tables = 31, threads = 0, stream_lanes = 0 (one stream per
- * chunk). */
+/* Fill *p with the defaults: W = 65536, K = 128, layout 3 (the joint
+ * (s, h) symbol) with m_s = 11 and m_f = 13 (the joint table's precision),
+ * max_tables = 31 (layout 2's coded h tables; layout 3 has none), threads =
+ * 0, stream_lanes = 0 (one stream per chunk).  Switching to layout 2 also
+ * needs m_f = 16 - m_s; layout 1 takes m_f 8..10 and max_tables <= 6. */
 void bs_params_default(bs_params* p);
 
 /* ---------------------------------------------------------------- model */

@@ -44,7 +44,7 @@ def params(chunk_weights: int = 65536, lanes: int = 128, m_s: int = 12, m_f: int
 
 def params2(chunk_weights: int = 65536, lanes: int = 128, m_s: int = 11, threads: int = 0,
             stream_lanes: int = 0, max_tables: int = 31) -> L.Params:
-    """Layout-2 encoder parameters (the library's default layout)."""
+    """Layout-2 encoder parameters (two steps, one renormalisation per weight)."""
     return params(chunk_weights, lanes, m_s, 16 - m_s, max_tables, threads, stream_lanes, layout=2)
 
 
@@ -53,7 +53,8 @@ JOINT_BITS = 13   # precision of a layout-3 record's joint (s, h) table
 
 def params3(chunk_weights: int = 65536, lanes: int = 128, m_s: int = 11, threads: int = 0,
             stream_lanes: int = 0) -> L.Params:
-    """Layout-3 encoder parameters: s and h coded as one joint symbol."""
+    """Layout-3 encoder parameters (the library's default layout): s and h
+    coded as one joint symbol."""
     return params(chunk_weights, lanes, m_s, JOINT_BITS, 0, threads, stream_lanes, layout=3)
 
 

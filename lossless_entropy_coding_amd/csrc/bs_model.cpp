@@ -324,11 +324,11 @@ void bs_params_default(bs_params* p) {
     p->chunk_weights = 65536;
     p->lanes = 128;
     p->m_s = 11;
-    p->m_f = 5;
-    p->max_tables = 31;
+    p->m_f = kMt;          // the joint table's precision
+    p->max_tables = 31;    // layout 2's coded h tables (layout 3 has none)
     p->threads = 0;
     p->stream_lanes = 0;
-    p->layout = 2;
+    p->layout = 3;
 }
 
 bs_status bs_build_tables_host(const uint16_t* h, uint64_t n, const bs_params* p, bs_tables** out) {

@@ -390,11 +390,16 @@ def test_layout2_params_rejected():
         codec.encode([codec.bf16(_words(np.ones(64)), t)], codec.params2())
 
 
-def test_layout2_is_the_library_default():
+def test_layout3_is_the_library_default():
     import ctypes
     p = L.Params()
     L.lib().bs_params_default(ctypes.byref(p))
-    assert (p.layout, p.m_s, p.m_f, p.max_tables, p.lanes, p.chunk_weights) == (2, 11, 5, 31, 128, 65536)
+    assert (p.layout, p.m_s, p.m_f, p.max_tables, p.lanes, p.chunk_weights) == (3, 11, 13, 31, 128, 65536)
+    # the defaults encode as they are, and in layout 2 once m_f follows m_s
+    w = _words(np.random.default_rng(2).standard_normal(70000) * 0.02)
+    assert codec.container_info(codec.encode([codec.bf16(w)], p)).version == 3
+    p.layout, p.m_f = 2, 16 - p.m_s
+    assert codec.container_info(codec.encode([codec.bf16(w)], p)).version == 2
 
 
 def test_noalloc_tables_refuses_bad_arguments_on_the_host():
