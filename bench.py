@@ -467,21 +467,33 @@ def fixed_bench(a):
         # on the uncompressed matrix and decode-then-BLAS
         Wd = outs[0][: rows * cols].view(torch.bfloat16).reshape(rows, cols)
         gemm = {}
-        for batch in (16, 64):
+        for batch in (16, 32, 64):
             X = torch.randn(batch, cols, generator=g).to(torch.bfloat16).cuda()
             Y = torch.empty(batch, rows, dtype=torch.float32, device="cuda")
-            fg = plans[0].bound_gemm(Y, X.view(torch.int16), rows, cols, stream=stream)
-            _, t_fg = timed(fg)
+            R = (X.float() @ W.float().t())
+            # the library's choice (a workspace where bs_fixed_gemm_work_bytes asks for
+            # one), and both forms forced: 16 rows per workgroup, and the split product
+            # (32 rows, two workgroups per group of rows, then the sums' addition) with
+            # a workspace of its size
+            wsplit = torch.empty(4 * batch * rows, dtype=torch.uint8, device="cuda")
+            forms = {"fixed_fused_us": "auto", "fixed_fused_16row_us": None, "fixed_fused_split_us": wsplit}
+            rec, diffs = {}, {}
+            for key, work in forms.items():
+                fg = plans[0].bound_gemm(Y, X.view(torch.int16), rows, cols, stream=stream, work=work)
+                _, t_fg = timed(fg)
+                Y.fill_(float("nan"))
+                fg()
+                torch.cuda.synchronize()
+                rec[key] = round(t_fg * 1e6, 2)
+                diffs[key] = float((Y - R).abs().max() / R.abs().max())
             _, t_pg = timed(lambda: torch.matmul(X, W.t()))
             dec0 = steps[0]
             _, t_dg = timed(lambda: (dec0(), torch.matmul(X, Wd.t())))
-            fg()
-            torch.cuda.synchronize()
-            R = (X.float() @ W.float().t())
-            gemm[f"batch_{batch}"] = {"fixed_fused_us": round(t_fg * 1e6, 2), "plain_bf16_gemm_us": round(t_pg * 1e6, 2),
-                                      "decode_then_gemm_us": round(t_dg * 1e6, 2),
-                                      "fixed_fused_TFLOP_s": round(2 * batch * rows * cols / t_fg / 1e12, 2),
-                                      "max_rel_diff_vs_fp32_product": float((Y - R).abs().max() / R.abs().max())}
+            gemm[f"batch_{batch}"] = dict(rec, **{
+                "split_chosen": int(L.lib().bs_fixed_gemm_work_bytes(rows, cols, batch)) > 0,
+                "plain_bf16_gemm_us": round(t_pg * 1e6, 2), "decode_then_gemm_us": round(t_dg * 1e6, 2),
+                "fixed_fused_TFLOP_s": round(2 * batch * rows * cols / (rec["fixed_fused_us"] * 1e-6) / 1e12, 2),
+                "max_rel_diff_vs_fp32_product": max(diffs.values())})
         gemv["gemm"] = gemm
     line = {"metric": "fixed-width lane-stream decode: decoded BF16 GB/s on 1 MI355X (% HBM roofline) + bits/weight",
             "value": round(2 * n / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,

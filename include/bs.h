@@ -487,16 +487,33 @@ bs_status bs_fixed_gemv_async(const bs_fixed_info* info, const void* d_blob, uin
  * weights decoded where they are used]: Y[b, r] = sum over c of W[r, c] X[b, c]
  * for b < batch (1..64), with W the blob's n weights as a row-major rows x cols
  * matrix, cols a multiple of 2048 (so every row starts on a block) and below
- * 2^26.  Each workgroup decodes 16 rows a panel of 2048 columns at a time
- * into LDS and multiplies them with v_mfma_f32_16x16x32_bf16; the weights are
+ * 2^26, rows below 2^26.  A workgroup decodes its rows a panel of 2048 columns at a time into
+ * LDS and multiplies them with v_mfma_f32_16x16x32_bf16; the weights are
  * never written out.  d_x: batch x cols BF16 words, row-major, 16-B aligned;
- * d_y: batch x rows floats, row-major, overwritten.  Every entry is summed in
- * fp32 in one fixed order (the same result on every run; within the fp32
- * summation bound of the exact sum).  d_status as for bs_fixed_decode_async.
- * One kernel launch on `stream`; nothing is allocated.  Errors: BS_E_INVAL
- * (shape, batch, NULL, alignment), BS_E_HIP. */
+ * d_y: batch x rows floats, row-major, overwritten.  d_status as for
+ * bs_fixed_decode_async.
+ *
+ * Without a workspace (d_work NULL) a workgroup owns 16 rows and all their
+ * panels: one launch, nothing allocated.  With one (cols >= 4096), a
+ * workgroup takes 32 rows, so that each element of X it reads serves twice
+ * the rows, and half of their panels; the other half goes to a second
+ * workgroup, which leaves its partial sums in the workspace, and a second
+ * launch on `stream` adds them into Y.  d_work: 256-B aligned, work_bytes at
+ * least 4 * batch * rows (bs_fixed_gemm_work_bytes gives that size where a
+ * workspace helps); its contents need no initialisation and are overwritten.
+ * Calls that share a workspace must not overlap (enqueue them on one stream).
+ * Either way every entry is summed in fp32 in one fixed order: the same
+ * result on every run, within the fp32 summation bound of the exact sum.
+ * Errors: BS_E_INVAL (shape, batch, NULL, alignment, a workspace too small),
+ * BS_E_HIP. */
 bs_status bs_fixed_gemm_async(const bs_fixed_info* info, const void* d_blob, uint64_t rows, uint64_t cols,
-                              uint32_t batch, const void* d_x, float* d_y, uint32_t* d_status, void* stream);
+                              uint32_t batch, const void* d_x, float* d_y, uint32_t* d_status, void* d_work,
+                              uint64_t work_bytes, void* stream);
+
+/* The workspace that bs_fixed_gemm_async should be given for this shape, in
+ * bytes, or 0 where the product runs best without one (batch 16 or less, a
+ * single panel, or a shape it refuses). */
+uint64_t bs_fixed_gemm_work_bytes(uint64_t rows, uint64_t cols, uint32_t batch);
 
 /* Bytes needed to decode records [first, first + count). */
 uint64_t bs_plan_out_bytes(const bs_plan* plan, uint32_t first, uint32_t count);

@@ -476,25 +476,47 @@ class FixedPlan:
         self.gemv_into(y, x, rows, cols, stream=stream)
         return y
 
+    def gemm_work(self, rows: int, cols: int, batch: int, work="auto"):
+        """The workspace (tensor, bytes) a product of this shape is given:
+        work="auto" takes the size bs_fixed_gemm_work_bytes asks for (none
+        where it asks for 0), work=None none, and a device tensor is passed as
+        it is.  One buffer per plan, grown when a shape needs more; products
+        that share it must be enqueued on one stream."""
+        if work is None:
+            return None, 0
+        if isinstance(work, torch.Tensor):                # a caller's own workspace
+            return work, work.numel() * work.element_size()
+        need = int(L.lib().bs_fixed_gemm_work_bytes(rows, cols, batch))
+        if need == 0:
+            return None, 0
+        if getattr(self, "_work", None) is None or self._work.numel() < need:
+            self._work = torch.empty(need, dtype=torch.uint8, device=self.dev.device)
+        return self._work, need
+
     def gemm_into(self, y: torch.Tensor, x: torch.Tensor, rows: int, cols: int, status: bool = True,
-                  stream=None) -> None:
+                  stream=None, work="auto") -> None:
         """Enqueue Y = X W^T on the matrix cores (bs_fixed_gemm_async): x a
         (batch, cols) bfloat16 (or int16) tensor, y a (batch, rows) float32
-        tensor (overwritten), batch 1..64."""
+        tensor (overwritten), batch 1..64; work as for gemm_work."""
         assert x.dtype in (torch.bfloat16, torch.int16) and x.dim() == 2 and x.shape[1] == cols and x.is_contiguous()
         assert y.dtype == torch.float32 and tuple(y.shape) == (x.shape[0], rows) and y.is_contiguous()
+        wt, wb = self.gemm_work(rows, cols, x.shape[0], work)
         rc = L.lib().bs_fixed_gemm_async(C.byref(self.info), C.c_void_p(self.dev.data_ptr()), rows, cols, x.shape[0],
                                          C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()),
                                          C.c_void_p(self.status.data_ptr()) if status else None,
+                                         C.c_void_p(wt.data_ptr()) if wt is not None else None, C.c_uint64(wb),
                                          C.c_void_p(_stream_handle(stream)))
         L.check(rc, "bs_fixed_gemm_async")
 
-    def bound_gemm(self, y: torch.Tensor, x: torch.Tensor, rows: int, cols: int, stream=None):
+    def bound_gemm(self, y: torch.Tensor, x: torch.Tensor, rows: int, cols: int, stream=None, work="auto"):
+        """gemm_into with its ctypes arguments converted once."""
         f = L.lib().bs_fixed_gemm_async
+        wt, wb = self.gemm_work(rows, cols, x.shape[0], work)
         args = (C.byref(self.info), C.c_void_p(self.dev.data_ptr()), C.c_uint64(rows), C.c_uint64(cols),
                 C.c_uint32(x.shape[0]), C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()), None,
+                C.c_void_p(wt.data_ptr()) if wt is not None else None, C.c_uint64(wb),
                 C.c_void_p(_stream_handle(stream)))
-        keep = (x, y, self.dev)
+        keep = (x, y, self.dev, wt)
 
         def run():
             rc = f(*args)

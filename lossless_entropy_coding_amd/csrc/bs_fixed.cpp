@@ -366,8 +366,16 @@ bs_status bs_fixed_gemv_async(const bs_fixed_info* info, const void* d_blob, uin
     return BS_OK;
 }
 
+uint64_t bs_fixed_gemm_work_bytes(uint64_t rows, uint64_t cols, uint32_t batch) {
+    // the split product pays off where X's traffic bounds the product: more
+    // than one tile of 16 batch rows, and at least two panels to share out
+    if (rows == 0 || cols < 2 * bsd::kFixBlockW || cols % bsd::kFixBlockW || batch <= 16 || batch > 64) return 0;
+    return 4ull * batch * rows;
+}
+
 bs_status bs_fixed_gemm_async(const bs_fixed_info* info, const void* d_blob, uint64_t rows, uint64_t cols,
-                              uint32_t batch, const void* d_x, float* d_y, uint32_t* d_status, void* stream) {
+                              uint32_t batch, const void* d_x, float* d_y, uint32_t* d_status, void* d_work,
+                              uint64_t work_bytes, void* stream) {
     bsd::FixedArgs a;
     const bs_status rc = fixed_args(info, d_blob, a);
     if (rc != BS_OK) return rc;
@@ -378,6 +386,7 @@ bs_status bs_fixed_gemm_async(const bs_fixed_info* info, const void* d_blob, uin
         return BS_E_INVAL;
     }
     if (batch == 0 || batch > 64) { set_error("batch %u outside 1..64", batch); return BS_E_INVAL; }
+    if (rows >= (1ull << 26)) { set_error("%llu rows, at most 2^26 - 1", (unsigned long long)rows); return BS_E_INVAL; }
     if ((uintptr_t)d_x & 15) { set_error("X must be 16-B aligned"); return BS_E_INVAL; }
     a.status = d_status;
     a.gx = (const uint16_t*)d_x;
@@ -385,10 +394,27 @@ bs_status bs_fixed_gemm_async(const bs_fixed_info* info, const void* d_blob, uin
     a.rows = rows;
     a.cols = (uint32_t)cols;
     a.batch = batch;
+    a.ksplit = 1;
+    a.gpart = nullptr;
+    // the split product: 32 rows per work item, two items per group of rows
+    // (cols >= 4096), given a workspace for the second half's sums
+    const uint64_t groups32 = (rows + 31) / 32;
+    const bool split = d_work != nullptr && cols >= 2 * bsd::kFixBlockW;
+    if (split) {
+        if ((uintptr_t)d_work & 255) { set_error("the workspace must be 256-B aligned"); return BS_E_INVAL; }
+        if (work_bytes < 4ull * batch * rows) {
+            set_error("workspace of %llu B, %llu B needed", (unsigned long long)work_bytes,
+                      (unsigned long long)(4ull * batch * rows));
+            return BS_E_INVAL;
+        }
+        a.ksplit = 2;
+        a.gpart = (float*)d_work;
+    }
     int cus = 0;
     if (bsk_device_cus(&cus) != 0 || cus <= 0) cus = 256;
-    const uint32_t groups = (uint32_t)std::min<uint64_t>((rows + 15) / 16, 8ull * (uint64_t)cus);
-    const int e = bsk_fixed_gemm(&a, groups, stream);
+    const uint64_t items = split ? 2 * groups32 : (rows + 15) / 16;
+    const uint32_t groups = (uint32_t)std::min<uint64_t>(items, 8ull * (uint64_t)cus);
+    const int e = bsk_fixed_gemm(&a, groups, split ? 1 : 0, stream);
     if (e != 0) { set_error("fixed batched product launch: %s", hipGetErrorString((hipError_t)e)); return BS_E_HIP; }
     return BS_OK;
 }

@@ -330,26 +330,62 @@ __global__ __launch_bounds__(64 * kFixWaves) void fixed_gemv_kernel(FixedArgs a)
 }
 
 // The fused product with a batch of vectors, Y[n][r] = sum over c of W[r][c] X[n][c],
-// on the matrix cores.  Workgroup g owns rows 16 g .. 16 g + 15 (all their
-// columns, so it stores its part of Y and no atomics are needed).  Rows start
-// on a block (cols % 2048 == 0), so a panel of 2048 columns of the 16 rows is
-// 16 whole blocks: the kGemmWaves waves decode 16 / kGemmWaves each into LDS,
-// then multiply the panel with X with v_mfma_f32_16x16x32_bf16 (A: 16 rows x
-// 32 columns of the panel, a 16-B piece per lane read back through the
-// decode's piece rotation; B: 32 columns x 16 batch rows of X, 16 B per lane
-// from X in HBM or L2); the next panel's blocks are loaded while one is
-// multiplied.  The waves split the batch into NT tiles of 16 and each tile's
-// columns among kGemmWaves / NT waves; the K slices are added in wave order
-// at the end, so every Y entry is summed in one fixed order.
+// on the matrix cores.  A work item is a group of 16 MF rows and a share of
+// their panels of 2048 columns (rows start on a block, cols % 2048 == 0, so a
+// panel of a row is one whole block).  For each panel the kGemmWaves waves
+// decode the group's 16 MF blocks into LDS, 16 MF / kGemmWaves each, then
+// multiply the panel with X with v_mfma_f32_16x16x32_bf16 (A: 16 rows x 32
+// columns of the panel, a 16-B piece per lane read back through the decode's
+// piece rotation; B: 32 columns x 16 batch rows of X, 16 B per lane from X in
+// HBM or L2, one load serving MF row tiles); the next panel's blocks are
+// loaded while one is multiplied.  The waves split the batch into NT tiles of
+// 16 and each tile's columns among kGemmWaves / NT waves; the K slices are
+// added in wave order.
+//
+// MF 1: a workgroup takes all panels of its 16 rows and stores its part of Y.
+// MF 2 halves the X traffic per row (each X element feeds 32 rows); to keep
+// as many workgroups busy, ksplit 2 gives the first half of a group's panels
+// and the second half to two work items.  The first stores its partial sums
+// in Y, the second in the workspace, and combine_kernel, launched next on the
+// same stream, adds the second into the first: every Y entry is P0 + P1, one
+// value on every run.  (Combining in this kernel, by whichever work item
+// arrives second, needs an agent-scope acquire, which invalidates the XCD's
+// L2 and with it the X lines the other workgroups are reading; it measured
+// slower than the second launch.)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int NT>
+// Y += P: the split product's second half added into the first, n floats
+// (16 B per thread and step where both are 16-B aligned, then the tail)
+__global__ __launch_bounds__(256) void combine_kernel(float* __restrict__ y, const float* __restrict__ part, uint64_t n) {
+    const uint64_t t = (uint64_t)blockIdx.x * 256 + threadIdx.x, stride = (uint64_t)gridDim.x * 256;
+    uint64_t n4 = 0;
+    if ((((uintptr_t)y | (uintptr_t)part) & 15) == 0) {
+        n4 = n / 4;
+        for (uint64_t i = t; i < n4; i += stride) {
+            float4 a = ((float4*)y)[i];
+            const float4 b = ((const float4*)part)[i];
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+            ((float4*)y)[i] = a;
+        }
+    }
+    for (uint64_t i = 4 * n4 + t; i < n; i += stride) y[i] += part[i];
+}
+
+template <int NT, int MF>
 __global__ __launch_bounds__(64 * kGemmWaves) void fixed_gemm_kernel(FixedArgs a) {
+    constexpr uint32_t kRows = 16 * MF;               // rows of a work item
     __shared__ uint32_t lut[256];
-    __shared__ __attribute__((aligned(16))) uint8_t wbuf[16][kGemmRowBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t wbuf[kRows][kGemmRowBytes];
     __shared__ __attribute__((aligned(4))) uint16_t escl[kGemmWaves][kFixEscLds];
-    __shared__ f32x4 red[kGemmWaves][64];
+    // the waves' K slices: a table of their own at MF 1; at MF 2 they go over
+    // the decoded rows once the last panel is multiplied
+    __shared__ f32x4 red1[MF == 1 ? kGemmWaves : 1][64];
+    static_assert(MF == 1 || sizeof(wbuf) >= sizeof(f32x4) * kGemmWaves * MF * 64, "K-slice table over wbuf");
+    f32x4* red = MF == 1 ? &red1[0][0] : (f32x4*)&wbuf[0][0];
 
     const uint32_t t = threadIdx.x, lane = t & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -359,11 +395,20 @@ __global__ __launch_bounds__(64 * kGemmWaves) void fixed_gemm_kernel(FixedArgs a
     constexpr uint32_t kSlice = kFixBlockW / kWpt; // panel columns per wave
     const uint32_t nt = wave / kWpt, ks = wave % kWpt;
     const uint32_t bpr = a.cols / kFixBlockW;
-    const uint64_t groups = (a.rows + 15) / 16;
-    for (uint64_t g = blockIdx.x; g < groups; g += gridDim.x) {
-        const uint64_t r0 = 16 * g;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        constexpr uint32_t kRpw = 16 / kGemmWaves;      // rows (blocks of a panel) per wave
+    const uint32_t split = MF == 2 && a.ksplit == 2 && bpr >= 2 ? 2u : 1u;   // every share holds a panel
+    const uint32_t p_mid = (bpr + 1) / 2;          // the first share's panels: 0 .. p_mid - 1
+    const uint64_t groups = (a.rows + kRows - 1) / kRows;
+    const uint64_t items = groups * split;
+    for (uint64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const uint64_t g = item / split;
+        const uint32_t kh = (uint32_t)(item % split);
+        const uint32_t p0 = split == 1 ? 0u : (kh == 0 ? 0u : p_mid);
+        const uint32_t p1 = split == 1 ? bpr : (kh == 0 ? p_mid : bpr);
+        const uint64_t r0 = kRows * g;
+        f32x4 acc[MF];
+#pragma unroll
+        for (int m = 0; m < MF; m++) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        constexpr uint32_t kRpw = kRows / kGemmWaves;   // rows (blocks of a panel) per wave
         uint32_t mr[kRpw];
         bool has[kRpw];
         BlockIn in[kRpw];
@@ -373,21 +418,26 @@ __global__ __launch_bounds__(64 * kGemmWaves) void fixed_gemm_kernel(FixedArgs a
         for (uint32_t h = 0; h < kRpw; h++) {
             mr[h] = kRpw * wave + h;
             has[h] = r0 + mr[h] < a.rows;
-            if (has[h]) in[h] = load_block(a, (r0 + mr[h]) * bpr, lane);
+            if (has[h]) in[h] = load_block(a, (r0 + mr[h]) * bpr + p0, lane);
         }
         // B operands: 16 B of X per lane and k step.  Rows past the batch read
         // row 0; they only feed D columns that are never stored.  The loads go
         // out kU at a time, each group while the one before it is multiplied,
         // and a panel's first group is issued before its blocks are decoded.
+        // offsets in 32 bits (batch <= 64 and cols < 2^26; batch x rows < 2^32)
         const uint32_t n = nt * 16 + (lane & 15);
-        const uint16_t* xrow = a.gx + (uint64_t)(n < a.batch ? n : 0) * a.cols + ks * kSlice + 8 * (lane >> 4);
+        const uint16_t* xrow = a.gx + ((n < a.batch ? n : 0u) * a.cols + ks * kSlice + 8 * (lane >> 4));
         constexpr uint32_t kNs = kSlice / 32;               // k steps per wave and panel
-        constexpr uint32_t kU = kNs < 8 ? kNs : 8;
+        // X loads in flight per group: 8, or 2 where each feeds two row tiles
+        // (4 made the compiler spill 6 registers at NT 4 and ran 13% slower
+        // at batch 64)
+        constexpr uint32_t kUmax = MF == 2 ? 2 : 8;
+        constexpr uint32_t kU = kNs < kUmax ? kNs : kUmax;
         bf16x8 bv[kU];
-        for (uint32_t p = 0; p < bpr; p++) {
+        for (uint32_t p = p0; p < p1; p++) {
 #pragma unroll
             for (uint32_t u = 0; u < kU; u++) bv[u] = *(const bf16x8*)(xrow + (uint64_t)p * kFixBlockW + 32 * u);
-            __syncthreads();          // the previous panel is consumed (and the table built)
+            __syncthreads();          // the previous panel (or K-slice table) is consumed, the table built
 #pragma unroll
             for (uint32_t h = 0; h < kRpw; h++) {
                 uint32_t* st = (uint32_t*)wbuf[mr[h]];
@@ -401,12 +451,12 @@ __global__ __launch_bounds__(64 * kGemmWaves) void fixed_gemm_kernel(FixedArgs a
                 }
             }
             __syncthreads();
-            if (p + 1 < bpr) {
+            // the next panel's blocks load while this one is multiplied
+            if (p + 1 < p1) {
 #pragma unroll
                 for (uint32_t h = 0; h < kRpw; h++)
                     if (has[h]) in[h] = load_block(a, (r0 + mr[h]) * bpr + p + 1, lane);
             }
-            const uint8_t* wr = wbuf[lane & 15];
             const uint16_t* xr = xrow + (uint64_t)p * kFixBlockW;
 #pragma unroll
             for (uint32_t s0 = 0; s0 < kNs; s0 += kU) {
@@ -421,23 +471,41 @@ __global__ __launch_bounds__(64 * kGemmWaves) void fixed_gemm_kernel(FixedArgs a
                 for (uint32_t u = 0; u < kU; u++) {
                     const uint32_t e0 = ks * kSlice + 32 * (s0 + u) + 8 * (lane >> 4);
                     const uint32_t L = e0 >> 5, kp = (e0 >> 3) & 3u;
-                    const bf16x8 av = *(const bf16x8*)(wr + 64 * L + 16 * ((kp + (L >> 1)) & 3u));
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, cur[u], acc, 0, 0, 0);
+                    const uint32_t off = 64 * L + 16 * ((kp + (L >> 1)) & 3u);
+#pragma unroll
+                    for (int m = 0; m < MF; m++) {
+                        const bf16x8 av = *(const bf16x8*)(wbuf[16 * m + (lane & 15)] + off);
+                        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, cur[u], acc[m], 0, 0, 0);
+                    }
                 }
             }
         }
-        red[wave][lane] = acc;
+        if (MF == 2) __syncthreads();     // every wave is done with the decoded rows
+#pragma unroll
+        for (int m = 0; m < MF; m++) red[(wave * MF + m) * 64 + lane] = acc[m];
         __syncthreads();
+        f32x4 sum[MF];
+#pragma unroll
+        for (int m = 0; m < MF; m++) sum[m] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (ks == 0) {
-            f32x4 sum = red[wave][lane];
 #pragma unroll
-            for (uint32_t w2 = 1; w2 < kWpt; w2++) sum += red[wave + w2][lane];
-            const uint32_t n = nt * 16 + (lane & 15);
+            for (int m = 0; m < MF; m++) {
+                sum[m] = red[(wave * MF + m) * 64 + lane];
 #pragma unroll
-            for (uint32_t i = 0; i < 4; i++) {
-                const uint64_t r = r0 + 4 * (lane >> 4) + i;      // D row 4 (lane / 16) + i, column lane % 16
-                if (n < a.batch && r < a.rows) a.gy[(uint64_t)n * a.rows + r] = sum[i];
+                for (uint32_t w2 = 1; w2 < kWpt; w2++) sum[m] += red[((wave + w2) * MF + m) * 64 + lane];
             }
+        }
+        // D row 4 (lane / 16) + i of row tile m, column lane % 16
+        float* dst = split == 2 && kh == 1 ? a.gpart : a.gy;
+        if (ks == 0) {
+            const uint32_t rows = (uint32_t)a.rows, rg = (uint32_t)r0 + 4 * (lane >> 4);
+#pragma unroll
+            for (int m = 0; m < MF; m++)
+#pragma unroll
+                for (uint32_t i = 0; i < 4; i++) {
+                    const uint32_t r = rg + 16 * m + i;
+                    if (n < a.batch && r < rows) dst[n * rows + r] = sum[m][i];
+                }
         }
     }
 }
@@ -451,16 +519,33 @@ extern "C" int bsk_fixed_decode_many(const FixedMany* m, void* stream) {
     return (int)hipGetLastError();
 }
 
-extern "C" int bsk_fixed_gemm(const FixedArgs* args, uint32_t n_groups, void* stream) {
+extern "C" int bsk_fixed_gemm(const FixedArgs* args, uint32_t n_groups, int rows32, void* stream) {
     if (n_groups == 0 || args->rows == 0) return 0;
     const dim3 grid(n_groups), block(64 * kGemmWaves);
     hipStream_t st = (hipStream_t)stream;
     const uint32_t nt = (args->batch + 15) / 16;
+    if (rows32) {
+        if (args->ksplit != 1 && args->ksplit != 2) return (int)hipErrorInvalidValue;
+        if (args->ksplit == 2 && (!args->gpart || args->cols < 2 * kFixBlockW)) return (int)hipErrorInvalidValue;
+        switch (nt) {
+            case 1: hipLaunchKernelGGL((fixed_gemm_kernel<1, 2>), grid, block, 0, st, *args); break;
+            case 2: hipLaunchKernelGGL((fixed_gemm_kernel<2, 2>), grid, block, 0, st, *args); break;
+            case 3:
+            case 4: hipLaunchKernelGGL((fixed_gemm_kernel<4, 2>), grid, block, 0, st, *args); break;
+            default: return (int)hipErrorInvalidValue;
+        }
+        if (args->ksplit == 2) {
+            const uint64_t n = (uint64_t)args->batch * args->rows;
+            const uint32_t cgrid = (uint32_t)std::min<uint64_t>((n / 4 + 255) / 256 + 1, 2048);
+            hipLaunchKernelGGL(combine_kernel, dim3(cgrid), dim3(256), 0, st, args->gy, args->gpart, n);
+        }
+        return (int)hipGetLastError();
+    }
     switch (nt) {
-        case 1: hipLaunchKernelGGL(fixed_gemm_kernel<1>, grid, block, 0, st, *args); break;
-        case 2: hipLaunchKernelGGL(fixed_gemm_kernel<2>, grid, block, 0, st, *args); break;
+        case 1: hipLaunchKernelGGL((fixed_gemm_kernel<1, 1>), grid, block, 0, st, *args); break;
+        case 2: hipLaunchKernelGGL((fixed_gemm_kernel<2, 1>), grid, block, 0, st, *args); break;
         case 3:
-        case 4: hipLaunchKernelGGL(fixed_gemm_kernel<4>, grid, block, 0, st, *args); break;
+        case 4: hipLaunchKernelGGL((fixed_gemm_kernel<4, 1>), grid, block, 0, st, *args); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();

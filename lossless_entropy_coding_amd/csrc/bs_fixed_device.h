@@ -38,7 +38,10 @@ struct FixedArgs {
     // (row-major BF16), Y batch x rows in gy (row-major fp32), cols a
     // multiple of 2048 so that every row starts on a block
     uint32_t batch;
-    uint32_t reserved;
+    uint32_t ksplit;        // 1, or 2: two workgroups share a group of rows, one half of its panels each
+    // the split product's workspace: the second half's partial sums
+    // (batch x rows fp32, laid out as Y)
+    float* gpart;
 };
 
 // several tensors decoded in one launch: tensor i takes workgroups
@@ -66,8 +69,10 @@ int bsk_fixed_decode(const bsd::FixedArgs* args, uint32_t n_groups, void* stream
 // decode up to kFixManyMax blobs in one launch of wg_start[count] workgroups
 int bsk_fixed_decode_many(const bsd::FixedMany* m, void* stream);
 // the fused product of a fixed-width blob with a batch of vectors: one
-// workgroup of kGemmWaves waves per 16 rows (n_groups workgroups, striding)
-int bsk_fixed_gemm(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);
+// workgroup of kGemmWaves waves per 16 rows (rows32 0), or per 32 rows and
+// args->ksplit shares of the panels (rows32 1; with 2 shares a second launch
+// adds the workspace's sums into Y); n_groups workgroups, striding
+int bsk_fixed_gemm(const bsd::FixedArgs* args, uint32_t n_groups, int rows32, void* stream);
 // the fused product of a fixed-width blob with a vector: n_groups workgroups
 // of kFixWaves waves, each workgroup striding over the row groups
 int bsk_fixed_gemv(const bsd::FixedArgs* args, uint32_t n_groups, void* stream);

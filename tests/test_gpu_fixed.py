@@ -311,15 +311,36 @@ GEMM_CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,rows,cols,batch", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
-def test_fixed_gemm_matches_fp64_product_of_oracle_decode(name, rows, cols, batch):
+# the split product (a workspace given): every case with at least two panels,
+# and the bench's 4096x4096 shape at batch 64, 32-row groups with a ragged last
+# group (1000, 77 and 20 rows), an odd number of panels (3, 7)
+SPLIT_CASES = [c for c in GEMM_CASES if c[2] >= 4096] + [
+    ("4096x4096_b64", 4096, 4096, 64), ("20x8192_b40", 20, 8192, 40), ("96x4096_b17", 96, 4096, 17),
+]
+
+
+def _split_work(rows, batch):
+    """A workspace of the size bs.h gives for the split product, filled with
+    NaN bit patterns (its contents must not matter)."""
+    return torch.full((batch * rows,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
+
+
+CASES_BOTH = ([c + ("whole",) for c in GEMM_CASES] + [c + ("split",) for c in SPLIT_CASES]
+              + [("4096x4096_b64", 4096, 4096, 64, "auto")])     # the plan's own workspace, as the bench runs it
+
+
+@pytest.mark.parametrize("name,rows,cols,batch,form", CASES_BOTH, ids=[f"{c[0]}_{c[4]}" for c in CASES_BOTH])
+def test_fixed_gemm_matches_fp64_product_of_oracle_decode(name, rows, cols, batch, form):
     """Y = X W^T within the fp32 summation bound.  The matrix cores add the
     exact BF16 products of a 32-column step into an fp32 accumulator (at most
-    one rounding per addition: 32 per step, cols / 32 steps per wave) and the
-    waves' K slices are added in order (at most 15 more), so an entry's error
-    is at most (cols + 16) 2^-24 sum_c |W[r, c] X[b, c]|; the test allows twice
-    that.  Each entry is summed in one fixed order: two runs agree bit for bit."""
-    say("fixed gemm", name)
+    one rounding per addition: 32 per step, cols / 32 steps per wave), the
+    waves' K slices are added in order (at most 15 more) and, in the split
+    product, the two halves' sums once more, so an entry's error is at most
+    (cols + 17) 2^-24 sum_c |W[r, c] X[b, c]|; the test allows twice that.
+    Each entry is summed in one fixed order: two runs agree bit for bit (in
+    the split product the second run finds the first run's sums in the
+    workspace)."""
+    say("fixed gemm", name, form)
     rng = np.random.default_rng(rows + cols + batch)
     w = rng.standard_normal(rows * cols) * 0.02
     w[rng.random(w.size) < 0.002] *= 80.0
@@ -329,13 +350,14 @@ def test_fixed_gemm_matches_fp64_product_of_oracle_decode(name, rows, cols, batc
     xw = _bf16(rng.standard_normal(batch * cols)).reshape(batch, cols)
     X64 = _as_f64(xw)
     Y_ref = X64 @ W64.T
-    bound = 2 * (cols + 16) * 2.0 ** -24 * (np.abs(X64) @ np.abs(W64).T)
+    bound = 2 * (cols + 17) * 2.0 ** -24 * (np.abs(X64) @ np.abs(W64).T)
     plan = codec.FixedPlan(blob)
     x = torch.from_numpy(xw.view(np.int16).copy()).cuda()
+    work = {"split": lambda: _split_work(rows, batch), "whole": lambda: None, "auto": lambda: "auto"}[form]()
     ys = []
     for rep in range(2):
         y = torch.full((batch, rows), float("nan"), dtype=torch.float32, device="cuda")
-        plan.gemm_into(y, x, rows, cols)
+        plan.gemm_into(y, x, rows, cols, work=work)
         torch.cuda.synchronize()
         assert (plan.block_status() == 0).all()
         ys.append(y.cpu().numpy())
@@ -351,8 +373,9 @@ def test_fixed_gemm_argument_errors():
     y = torch.empty(4, 64, dtype=torch.float32, device="cuda")
     f = L.lib().bs_fixed_gemm_async
     import ctypes as C
-    args = lambda rows, cols, batch, xp: (C.byref(plan.info), C.c_void_p(plan.dev.data_ptr()), rows, cols, batch,
-                                          C.c_void_p(xp), C.c_void_p(y.data_ptr()), None, None)
+    args = lambda rows, cols, batch, xp, wp=None, wb=0: (C.byref(plan.info), C.c_void_p(plan.dev.data_ptr()), rows,
+                                                         cols, batch, C.c_void_p(xp), C.c_void_p(y.data_ptr()), None,
+                                                         C.c_void_p(wp) if wp else None, C.c_uint64(wb), None)
     assert f(*args(128, 1024, 4, x.data_ptr())) == L.BS_E_INVAL          # cols not a multiple of 2048
     assert f(*args(32, 2048, 4, x.data_ptr())) == L.BS_E_INVAL           # rows * cols != n
     assert f(*args(64, 2048, 0, x.data_ptr())) == L.BS_E_INVAL           # batch 0
@@ -361,6 +384,19 @@ def test_fixed_gemm_argument_errors():
     assert f(*args(64, 2048, 4, x.data_ptr())) == L.BS_OK
     torch.cuda.synchronize()
     assert float(y.abs().max()) == 0.0
+    # the split product's workspace: too small, misaligned; a blob of 32 x 4096
+    plan2 = codec.FixedPlan(codec.fixed_encode(_case_words("gauss", 32 * 4096, 13)))
+    x2 = torch.zeros(4, 4096, dtype=torch.int16, device="cuda")
+    y2 = torch.full((4, 32), float("nan"), dtype=torch.float32, device="cuda")
+    w2 = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    need = 4 * 4 * 32
+    a2 = lambda wp, wb: (C.byref(plan2.info), C.c_void_p(plan2.dev.data_ptr()), 32, 4096, 4, C.c_void_p(x2.data_ptr()),
+                         C.c_void_p(y2.data_ptr()), None, C.c_void_p(wp), C.c_uint64(wb), None)
+    assert f(*a2(w2.data_ptr(), need - 4)) == L.BS_E_INVAL               # too small
+    assert f(*a2(w2.data_ptr() + 16, need)) == L.BS_E_INVAL              # not 256-B aligned
+    assert f(*a2(w2.data_ptr(), need)) == L.BS_OK
+    torch.cuda.synchronize()
+    assert float(y2.abs().max()) == 0.0
 
 
 # --------------------------------------------------------------------------- built on the GPU

@@ -269,6 +269,30 @@ def test_fixed_decode_argument_checks_before_launch():
     assert f(C.byref(empty), C.c_void_p(4096), None, 0, None, None) == L.BS_OK     # nothing to do
 
 
+def test_fixed_gemm_workspace_size_and_checks_before_launch():
+    """The split product's workspace: the second half's partial sums (batch x
+    rows fp32), asked for only where the product has more than 16 batch rows
+    and two panels; a workspace too small or misaligned is refused before any
+    launch."""
+    import ctypes as C
+    ws = L.lib().bs_fixed_gemm_work_bytes
+    assert ws(4096, 4096, 64) == 4 * 64 * 4096
+    assert ws(1000, 14336, 17) == 4 * 17 * 1000
+    assert ws(20, 8192, 40) == 4 * 40 * 20
+    for rows, cols, batch in [(4096, 4096, 16), (4096, 2048, 64), (4096, 4096, 65), (0, 4096, 64), (64, 3000, 64)]:
+        assert ws(rows, cols, batch) == 0, (rows, cols, batch)
+    w = _words(np.random.default_rng(7).standard_normal(32 * 4096) * 0.02)
+    info = codec.fixed_info(codec.fixed_encode(w))
+    f = L.lib().bs_fixed_gemm_async
+    call = lambda wp, wb: f(C.byref(info), C.c_void_p(4096), 32, 4096, 40, C.c_void_p(4096), C.c_void_p(8192), None,
+                            C.c_void_p(wp), C.c_uint64(wb), None)
+    need = 4 * 40 * 32
+    assert call(1 << 20, need - 1) == L.BS_E_INVAL
+    assert b"needed" in L.lib().bs_last_error()
+    assert call((1 << 20) + 128, need) == L.BS_E_INVAL
+    assert b"aligned" in L.lib().bs_last_error()
+
+
 def test_fixed_decode_many_argument_checks_before_launch():
     import ctypes as C
     w = _words(np.random.default_rng(6).standard_normal(5000) * 0.02)
