@@ -924,7 +924,9 @@ def main():
                    "bits_per_weight": round(job.bits_per_weight, 5), "entropy_bits": round(job.entropy_bits, 5),
                    "bits_over_entropy_pct": round(100 * (job.bits_per_weight / job.entropy_bits - 1), 3),
                    "cold_cache": bool(a.cold), "parallelism": "single GPU",
-                   "tensors": getattr(job, "n_tensors", None), "container_bytes": job.container_bytes},
+                   "tensors": getattr(job, "n_tensors", None), "container_bytes": job.container_bytes,
+                   # bits per weight by part of the BF16 records (bs_container_sizes_get); they sum to bits_per_weight
+                   "bits_per_weight_parts": codec.size_breakdown_bits_per_weight(job.sizes)},
         "roofline": roofline,
         "model_build": model,
         "cpu_baseline": cpu,

@@ -311,10 +311,30 @@ typedef struct {
     uint32_t layout;        /* BF16 records: 1, 2 or 3 */
 } bs_record_info;
 
+/* Where a container's BF16 bits go [model cards' metrics tables: bits per
+ * weight counts every byte of the compressed checkpoint]: in bits, over all
+ * its BF16 records, summing exactly to 8 x bs_container_info.bf16_bytes (all
+ * zero when the container holds no BF16 weights). */
+typedef struct {
+    uint64_t weights;         /* BF16 weights */
+    uint64_t container_bits;  /* the BF16 side's share of the header, directory and gaps between records */
+    uint64_t fixed_bits;      /* record bodies' fixed parts (24 B each) */
+    uint64_t table_bits;      /* s-tables, routes, fraction / h / joint tables, their padding */
+    uint64_t index_bits;      /* chunk index and stream table, padded up to the first payload */
+    uint64_t code_bits;       /* the lanes' length codes, padded to 16 B per chunk */
+    uint64_t plane_bits;      /* layouts 2 and 3: the verbatim low fraction bits, padded to 16 B per chunk */
+    uint64_t state_bits;      /* final lane states: 16 + e bits each */
+    uint64_t word_bits;       /* the streams' 16-bit words */
+    uint64_t pad_bits;        /* the rest of the records: state bits padded to 16-bit units, payloads to 16 B */
+} bs_size_breakdown;
+
 /* Validate a host copy of a container and describe it.  Errors: BS_E_FORMAT,
  * BS_E_VERSION. */
 bs_status bs_container_info_get(const void* h_container, uint64_t len, bs_container_info* info);
 bs_status bs_record_info_get(const void* h_container, uint64_t len, uint32_t index, bs_record_info* info);
+/* The size breakdown of a host copy of a container (validated as above).
+ * Errors: BS_E_INVAL (NULL), BS_E_FORMAT, BS_E_VERSION. */
+bs_status bs_container_sizes_get(const void* h_container, uint64_t len, bs_size_breakdown* out);
 
 /* ---------------------------------------------------------------- decode */
 

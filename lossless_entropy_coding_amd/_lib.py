@@ -55,6 +55,11 @@ class ContainerInfo(C.Structure):
                 ("bf16_bytes", C.c_uint64), ("raw_bytes", C.c_uint64), ("n_streams", C.c_uint64)]
 
 
+class SizeBreakdown(C.Structure):
+    _fields_ = [(n, C.c_uint64) for n in ("weights", "container_bits", "fixed_bits", "table_bits", "index_bits",
+                                          "code_bits", "plane_bits", "state_bits", "word_bits", "pad_bits")]
+
+
 class RecordInfo(C.Structure):
     _fields_ = [("kind", C.c_uint32), ("chunk_weights", C.c_uint32), ("lanes", C.c_uint32),
                 ("n_chunks", C.c_uint32), ("m_s", C.c_uint32), ("m_f", C.c_uint32), ("n_tables", C.c_uint32),
@@ -103,6 +108,7 @@ SIGNATURES = {
     "bs_blob_free": (None, [C.c_void_p]),
     "bs_container_info_get": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(ContainerInfo)]),
     "bs_record_info_get": (C.c_int, [C.c_void_p, C.c_uint64, C.c_uint32, C.POINTER(RecordInfo)]),
+    "bs_container_sizes_get": (C.c_int, [C.c_void_p, C.c_uint64, C.POINTER(SizeBreakdown)]),
     "bs_plan_create": (C.c_int, [C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p, C.POINTER(C.c_void_p)]),
     "bs_plan_destroy": (None, [C.c_void_p]),
     "bs_plan_rebind": (C.c_int, [C.c_void_p, C.c_void_p]),

@@ -81,6 +81,7 @@ class CheckpointJob:
         self.plans, self.refs = [], []
         self.model_sample = None
         self.n_weights = self.raw_bytes = self.read_bytes = self.container_bytes = 0
+        self.sizes = {}
         self.n_tensors = 0
         bits = ent = 0.0
         if layout == 3:
@@ -116,6 +117,8 @@ class CheckpointJob:
             self.read_bytes += int(info.bf16_bytes) + int(info.raw_bytes)
             self.container_bytes += len(host)
             bits += 8.0 * info.bf16_bytes
+            for k, v in codec.container_sizes(host).items():       # where the BF16 bits go
+                self.sizes[k] = self.sizes.get(k, 0) + v
             out_max = max(out_max, plan.out_bytes())
             self.plans.append(plan)
             self.refs.append(ref)

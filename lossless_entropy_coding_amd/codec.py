@@ -218,6 +218,21 @@ def container_info(container) -> L.ContainerInfo:
     return info
 
 
+def container_sizes(container) -> dict:
+    """bs_container_sizes_get: where the container's BF16 bits go, as a dict
+    of bit counts (and the weight count)."""
+    sz = L.SizeBreakdown()
+    ptr, n = _host_bytes(container)
+    L.check(L.lib().bs_container_sizes_get(ptr, n, C.byref(sz)), "bs_container_sizes_get")
+    return {name: int(getattr(sz, name)) for name, _ in L.SizeBreakdown._fields_}
+
+
+def size_breakdown_bits_per_weight(sizes: dict) -> dict:
+    """A sum of container_sizes dicts as bits per weight by part."""
+    w = max(sizes["weights"], 1)
+    return {k[:-5] if k.endswith("_bits") else k: round(v / w, 5) for k, v in sizes.items() if k != "weights"}
+
+
 def record_info(container, i: int) -> L.RecordInfo:
     info = L.RecordInfo()
     ptr, n = _host_bytes(container)

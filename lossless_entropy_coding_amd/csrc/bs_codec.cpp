@@ -692,6 +692,62 @@ bs_status bs_record_info_get(const void* h, uint64_t len, uint32_t index, bs_rec
     return BS_OK;
 }
 
+bs_status bs_container_sizes_get(const void* hv, uint64_t len, bs_size_breakdown* out) {
+    if (!out) { set_error("NULL breakdown"); return BS_E_INVAL; }
+    Container c;
+    bs_status rc = parse_container((const uint8_t*)hv, len, c);
+    if (rc) return rc;
+    memset(out, 0, sizeof(*out));
+    const uint8_t* h = (const uint8_t*)hv;
+    uint64_t raw = 0, n_raw = 0, bf16_len = 0;
+    for (const Record& r : c.recs) {
+        if (r.kind != BS_KIND_BF16) {
+            raw += r.rec_len;
+            n_raw++;
+            continue;
+        }
+        out->weights += r.n;
+        bf16_len += r.rec_len;
+        const uint8_t* b = h + r.rec_offset;
+        out->fixed_bits += 8 * 24;
+        out->table_bits += 8 * (r.index_off - 24);
+        // the chunk index and stream table, with the padding up to the first payload
+        const uint64_t first = r.n_chunks ? rd64(b + r.index_off) : r.rec_len;
+        out->index_bits += 8 * (first - r.index_off);
+        const uint32_t P = r.K / r.S;
+        const uint8_t* stab = b + r.index_off + 16ull * r.n_chunks;
+        uint64_t used = 8 * first;
+        for (uint32_t ch = 0; ch < r.n_chunks; ch++) {
+            const uint8_t* e = b + r.index_off + 16ull * ch;
+            const uint64_t po = rd64(e), total = rd32(e + 8);
+            const uint64_t n_c = std::min<uint64_t>(r.W, r.n - (uint64_t)ch * r.W);
+            out->code_bits += 8 * code_bytes(r.K);
+            used += 8 * code_bytes(r.K);
+            if (r.layout >= 2) {
+                out->plane_bits += 8 * plane_bytes(n_c);
+                used += 8 * plane_bytes(n_c);
+            }
+            for (uint32_t st = 0; st < r.S; st++) {
+                const uint64_t from = st ? rd32(stab + 4ull * ((r.S - 1) * ch + st - 1)) : 0;
+                const uint64_t to = st + 1 < r.S ? rd32(stab + 4ull * ((r.S - 1) * ch + st)) : total;
+                uint64_t esum = 0;
+                for (uint32_t l = st * P; l < (st + 1) * P; l++) esum += (b[po + l / 2] >> (4 * (l % 2))) & 15u;
+                const uint64_t sbits = 16ull * P + esum;
+                out->state_bits += sbits;
+                out->word_bits += 16 * (to - from - state_units(P, esum));
+                used += sbits + 16 * (to - from - state_units(P, esum));
+            }
+        }
+        out->pad_bits += 8 * r.rec_len - used;
+    }
+    if (out->weights == 0) {      // nothing is charged to BF16 weights (bs_container_info's bf16_bytes is 0)
+        memset(out, 0, sizeof(*out));
+        return BS_OK;
+    }
+    out->container_bits = 8 * (len - raw - kDirEntryBytes * n_raw - bf16_len);
+    return BS_OK;
+}
+
 void bs_sha256(const void* h, uint64_t n, uint8_t out[32]) { sha256(h, n, out); }
 
 bs_status bs_write_file_new(const char* path, const void* h, uint64_t n) {
@@ -726,7 +782,7 @@ const char* bs_strerror(bs_status s) {
 }
 
 const char* bs_last_error(void) { return last_error(); }
-const char* bs_version(void) { return "bs 1.1 (container versions 1 and 2, gfx950)"; }
+const char* bs_version(void) { return "bs 1.2 (container versions 1, 2 and 3, gfx950)"; }
 
 }  // extern "C"
 

@@ -173,6 +173,7 @@ class DecodeJob:
             compact = self.lanes_per_thread <= 4 and self.m_s <= 11 and self.m_f <= 9
             self.kernel_name = "decode_kernel<%d, %s>" % (self.lanes_per_thread, "true" if compact else "false")
         self.container_bytes = len(enc.container)
+        self.sizes = codec.container_sizes(enc.container)     # where the BF16 bits go
         info = codec.container_info(enc.container)
         # bytes a decode reads: BF16 record bytes (tables, index, states, words) and verbatim spans
         self.read_bytes = int(info.bf16_bytes) + int(info.raw_bytes)

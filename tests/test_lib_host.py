@@ -269,6 +269,51 @@ def test_fixed_decode_argument_checks_before_launch():
     assert f(C.byref(empty), C.c_void_p(4096), None, 0, None, None) == L.BS_OK     # nothing to do
 
 
+@pytest.mark.parametrize("layout,n,W,K,P", [(1, 100000, 4096, 8, 2), (2, 70001, 65536, 128, 64), (3, 300000, 131072, 256, 64),
+                                             (3, 5000, 131072, 256, 0), (1, 0, 64, 8, 0), (3, 33333, 32768, 128, 128)])
+def test_size_breakdown_adds_up_and_matches_the_layout(layout, n, W, K, P):
+    """bs_container_sizes_get against a walk of the container written here
+    from the layout bs.h documents: the fixed parts, tables, index, length
+    codes and planes from the header fields, the state bits from the lanes'
+    length codes read out of each payload, the words from the index's unit
+    counts; the parts sum to 8 x the BF16 bytes."""
+    rng = np.random.default_rng(n + W + K + layout)
+    w = _words(rng.standard_normal(n) * 0.02)
+    mk = {1: codec.params, 2: codec.params2, 3: codec.params3}[layout]
+    p = mk(chunk_weights=W, lanes=K, stream_lanes=P)
+    blob = codec.encode([codec.bf16(w), codec.raw(np.arange(77, dtype=np.uint8))], p)
+    sz = codec.container_sizes(blob)
+    info = codec.container_info(blob)
+    parts = [v for k, v in sz.items() if k != "weights"]
+    assert sz["weights"] == n and sum(parts) == 8 * info.bf16_bytes
+    if n == 0:                                  # nothing is charged to BF16 weights
+        assert not any(parts)
+        return
+    ri = codec.record_info(blob, 0)
+    b = blob[ri.rec_offset: ri.rec_offset + ri.rec_len]
+    n_chunks, S = ri.n_chunks, ri.streams
+    K, W = ri.lanes, ri.chunk_weights          # a record smaller than a chunk gets fewer lanes
+    rd = lambda o, k: int.from_bytes(b[o: o + k], "little")
+    assert sz["fixed_bits"] == 8 * 24
+    first = rd(index_off := sz["fixed_bits"] // 8 + sz["table_bits"] // 8, 8) if n_chunks else ri.rec_len
+    assert sz["index_bits"] == 8 * (first - index_off) and first - index_off >= 16 * n_chunks + 4 * (S - 1) * n_chunks
+    codes = -(-((K + 1) // 2) // 16) * 16
+    assert sz["code_bits"] == 8 * codes * n_chunks
+    n_c = [min(W, n - c * W) for c in range(n_chunks)]
+    assert sz["plane_bits"] == (8 * sum(-(-(4 * -(-m // 8)) // 16) * 16 for m in n_c) if layout >= 2 else 0)
+    lanes_per = K // S
+    state = words = 0
+    for c in range(n_chunks):
+        po, total = rd(index_off + 16 * c, 8), rd(index_off + 16 * c + 8, 4)
+        starts = [0] + [rd(index_off + 16 * n_chunks + 4 * ((S - 1) * c + j), 4) for j in range(S - 1)] + [total]
+        for st in range(S):
+            e = sum((b[po + l // 2] >> (4 * (l % 2))) & 15 for l in range(st * lanes_per, (st + 1) * lanes_per))
+            state += 16 * lanes_per + e
+            words += 16 * (starts[st + 1] - starts[st] - -(-(16 * lanes_per + e) // 16))
+    assert sz["state_bits"] == state and sz["word_bits"] == words
+    assert 0 <= sz["pad_bits"] < 8 * 16 * (2 * n_chunks + 1) + 16 * S * n_chunks
+
+
 def test_fixed_gemm_workspace_size_and_checks_before_launch():
     """The split product's workspace: the second half's partial sums (batch x
     rows fp32), asked for only where the product has more than 16 batch rows
