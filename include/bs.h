@@ -531,7 +531,7 @@ bs_status bs_fixed_gemm_async(const bs_fixed_info* info, const void* d_blob, uin
                               uint64_t work_bytes, void* stream);
 
 /* The workspace that bs_fixed_gemm_async should be given for this shape, in
- * bytes, or 0 where the product runs best without one (batch 16 or less, a
+ * bytes, or 0 where the product runs best without one (batch below 8, a
  * single panel, or a shape it refuses). */
 uint64_t bs_fixed_gemm_work_bytes(uint64_t rows, uint64_t cols, uint32_t batch);
 

@@ -343,9 +343,9 @@ __global__ __launch_bounds__(64 * kFixWaves) void fixed_gemv_kernel(FixedArgs a)
 // added in wave order.
 //
 // MF 1: a workgroup takes all panels of its 16 rows and stores its part of Y.
-// MF 2 halves the X traffic per row (each X element feeds 32 rows); to keep
-// as many workgroups busy, ksplit 2 gives the first half of a group's panels
-// and the second half to two work items.  The first stores its partial sums
+// MF 2 halves the X traffic per row (each X element feeds 32 rows); so that
+// as many workgroups stay busy, ksplit 2 gives the first half of a group's
+// panels to one work item and the second half to another.  The first stores its partial sums
 // in Y, the second in the workspace, and combine_kernel, launched next on the
 // same stream, adds the second into the first: every Y entry is P0 + P1, one
 // value on every run.  (Combining in this kernel, by whichever work item

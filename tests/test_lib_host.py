@@ -316,7 +316,7 @@ def test_size_breakdown_adds_up_and_matches_the_layout(layout, n, W, K, P):
 
 def test_fixed_gemm_workspace_size_and_checks_before_launch():
     """The split product's workspace: the second half's partial sums (batch x
-    rows fp32), asked for only where the product has more than 16 batch rows
+    rows fp32), asked for only where the product has at least 8 batch rows
     and two panels; a workspace too small or misaligned is refused before any
     launch."""
     import ctypes as C
@@ -324,7 +324,8 @@ def test_fixed_gemm_workspace_size_and_checks_before_launch():
     assert ws(4096, 4096, 64) == 4 * 64 * 4096
     assert ws(1000, 14336, 17) == 4 * 17 * 1000
     assert ws(20, 8192, 40) == 4 * 40 * 20
-    for rows, cols, batch in [(4096, 4096, 16), (4096, 2048, 64), (4096, 4096, 65), (0, 4096, 64), (64, 3000, 64)]:
+    assert ws(4096, 4096, 8) == 4 * 8 * 4096
+    for rows, cols, batch in [(4096, 4096, 7), (4096, 2048, 64), (4096, 4096, 65), (0, 4096, 64), (64, 3000, 64)]:
         assert ws(rows, cols, batch) == 0, (rows, cols, batch)
     w = _words(np.random.default_rng(7).standard_normal(32 * 4096) * 0.02)
     info = codec.fixed_info(codec.fixed_encode(w))
