@@ -524,8 +524,8 @@ bs_status bs_fixed_gemv_async(const bs_fixed_info* info, const void* d_blob, uin
  * Calls that share a workspace must not overlap (enqueue them on one stream).
  * Either way every entry is summed in fp32 in one fixed order: the same
  * result on every run, within the fp32 summation bound of the exact sum.
- * Errors: BS_E_INVAL (shape, batch, NULL, alignment, a workspace too small),
- * BS_E_HIP. */
+ * Errors: BS_E_INVAL (shape, batch, NULL, alignment, a workspace too small
+ * or overlapping Y), BS_E_HIP. */
 bs_status bs_fixed_gemm_async(const bs_fixed_info* info, const void* d_blob, uint64_t rows, uint64_t cols,
                               uint32_t batch, const void* d_x, float* d_y, uint32_t* d_status, void* d_work,
                               uint64_t work_bytes, void* stream);

@@ -408,6 +408,8 @@ bs_status bs_fixed_gemm_async(const bs_fixed_info* info, const void* d_blob, uin
                       (unsigned long long)(4ull * batch * rows));
             return BS_E_INVAL;
         }
+        const uintptr_t w0 = (uintptr_t)d_work, y0 = (uintptr_t)d_y, sz = (uintptr_t)(4ull * batch * rows);
+        if (w0 < y0 + sz && y0 < w0 + sz) { set_error("the workspace overlaps Y"); return BS_E_INVAL; }
         a.ksplit = 2;
         a.gpart = (float*)d_work;
     }

@@ -337,6 +337,8 @@ def test_fixed_gemm_workspace_size_and_checks_before_launch():
     assert b"needed" in L.lib().bs_last_error()
     assert call((1 << 20) + 128, need) == L.BS_E_INVAL
     assert b"aligned" in L.lib().bs_last_error()
+    assert call(8192 - 256, need) == L.BS_E_INVAL            # Y is at 8192: the workspace would overlap it
+    assert b"overlaps" in L.lib().bs_last_error()
 
 
 def test_fixed_decode_many_argument_checks_before_launch():
