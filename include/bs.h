@@ -311,8 +311,9 @@ typedef struct {
     uint32_t layout;        /* BF16 records: 1, 2 or 3 */
 } bs_record_info;
 
-/* Where a container's BF16 bits go [model cards' metrics tables: bits per
- * weight counts every byte of the compressed checkpoint]: in bits, over all
+/* Where a container's BF16 bits go [Qwen3.8-27B-BF16-NVLC-Lossless card,
+ * metrics table: its bits per weight count every byte of the compressed
+ * checkpoint against the weights it holds]: in bits, over all
  * its BF16 records, summing exactly to 8 x bs_container_info.bf16_bytes (all
  * zero when the container holds no BF16 weights). */
 typedef struct {
@@ -532,7 +533,8 @@ bs_status bs_fixed_gemm_async(const bs_fixed_info* info, const void* d_blob, uin
 
 /* The workspace that bs_fixed_gemm_async should be given for this shape, in
  * bytes, or 0 where the product runs best without one (batch below 8, a
- * single panel, or a shape it refuses). */
+ * single panel, or a shape it refuses) [the product of the NVLC card's
+ * runtime paragraphs, as for bs_fixed_gemm_async]. */
 uint64_t bs_fixed_gemm_work_bytes(uint64_t rows, uint64_t cols, uint32_t batch);
 
 /* Bytes needed to decode records [first, first + count). */
